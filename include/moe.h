@@ -1,0 +1,227 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) grouped expert MLP library (libmoe.so).
+ *
+ * The library implements the hot path of a mixture-of-experts feed-forward
+ * layer on one GPU:
+ *   token permutation by expert with per-expert counts (split_sizes),
+ *   a grouped gate-up GEMM (H -> 2I) over all local experts in one launch,
+ *   ScaledSwiGLU with the routing probability folded in,
+ *   a grouped down GEMM (I -> H),
+ *   the top-k un-permute / combine,
+ * in BF16 and in MXFP8 (E4M3 elements with one E8M0 scale per 32 consecutive
+ * values along the GEMM's K), forward and backward.
+ *
+ * Source of the method: page "BioNeMo Uses Grouped Kernels and MXFP8" --
+ * Figure 1 (top-k router, outputs combined as a weighted sum), Grouping
+ * fragmented expert workloads (split_sizes, separate per-expert weights,
+ * gate-up out_features = 2 * intermediate_size, no bias), Reducing memory
+ * pressure with MXFP8 and Figure 3 (E4M3 + E8M0 per 32 values), Fusing
+ * precision conversion and expert computation and Figure 4 (quantize ->
+ * fused gate-up + ScaledSwiGLU -> down projection); page "How BioNeMo cuts
+ * overhead", How MXFP8 reduces memory use (16-bit master weights converted
+ * for each low-precision GEMM).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor argument is device memory owned by the caller, dense and
+ *     row-major.  Weight pointer tables (w1, w2, dw1, dw2) are HOST arrays of
+ *     E device pointers; the library copies them into kernel arguments.
+ *   - The library never allocates device memory and never synchronizes the
+ *     stream: all work is enqueued on `stream` (a hipStream_t; NULL = the
+ *     default stream).  split_sizes never leaves the device.
+ *   - Host-detectable argument errors return a status before anything is
+ *     enqueued.  An out-of-range expert id in topk_idx is detected on the
+ *     device: the (token, slot) pair is dropped (row_id_map = -1) and a flag
+ *     is raised in the first 4 bytes of the workspace; moe_read_device_error
+ *     reads it.
+ *   - Results are deterministic: identical inputs give identical bits (no
+ *     floating-point atomics anywhere).
+ *   - Calls are reentrant; concurrent calls must use distinct workspaces.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = 1,  /* null pointer, non-positive or inconsistent size */
+  MOE_ERR_UNSUPPORTED = 2,  /* valid but not implemented (shape alignment, dtype combination) */
+  MOE_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the size query returned */
+  MOE_ERR_HIP = 4           /* a HIP runtime call failed (launch error) */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_MXFP8_E4M3 = 2        /* E4M3FN bytes + E8M0 scale bytes, one per 32 values */
+} moe_dtype;
+
+/* Largest supported expert count and experts per token. */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 16
+
+/* Version of this ABI (bumped on any incompatible change). */
+int moe_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * mxfp8_quantize -- OCP MXFP8 block quantization (the standalone Quantize
+ * step of Figure 4's unfused flow).
+ *
+ * x        [rows, cols] in x_dtype (MOE_F32 or MOE_BF16).
+ * axis 0:  blocks of 32 consecutive values along cols (row-wise).
+ *          cols % 32 == 0.  q: [rows, cols] bytes; scales: [rows, cols/32].
+ * axis 1:  blocks of 32 consecutive values along rows (column-wise), the
+ *          rows being split into num_groups segments by the device array
+ *          group_offsets [num_groups+1] (exclusive prefix, group_offsets[0]
+ *          = 0, last = rows).  Blocks restart at every segment start and a
+ *          segment's last block is zero-padded.  The output is TRANSPOSED
+ *          so that the token axis is contiguous: segment g occupies columns
+ *          [P_g, P_g + ceil(M_g/32)*32) of q [cols, rows_pad] and columns
+ *          [P_g/32, ...) of scales [cols, rows_pad/32], where P_g is the
+ *          prefix sum of the padded segment sizes and rows_pad =
+ *          ceil(rows/32)*32 + 32*num_groups (an upper bound; the caller
+ *          allocates it).
+ *          Padding codes are 0x00.  cols % 32 == 0.
+ * Element rule: s = floor(log2(amax)) - 8 clamped to [-127, 127] (amax = 0
+ * gives s = -127), scale byte = s + 127, code = E4M3FN(v / 2^s) rounded to
+ * nearest even and saturated to +-448; the sign of a zero result is kept.
+ * ------------------------------------------------------------------------ */
+moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int axis,
+                          const int32_t* group_offsets, int num_groups,
+                          uint8_t* q, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute -- histogram, prefix sum and stable scatter of the (token,
+ * slot) pairs by expert (the gather of each expert's tokens before the
+ * grouped GEMM; split_sizes as in the grouped linear's interface).
+ *
+ * x          [T, H] in x_dtype (MOE_F32 or MOE_BF16).
+ * topk_idx   [T, k] int32 expert ids in [0, E).
+ * topk_prob  [T, k] float32 routing probabilities (may be NULL if prob_perm is NULL).
+ * perm_dtype MOE_BF16: x_perm is [T*k, H] bf16 (x rounded to nearest even);
+ *            MOE_MXFP8_E4M3: x_perm is [T*k, H] E4M3 bytes and x_perm_scales
+ *            [T*k, H/32] E8M0 bytes (H % 32 == 0); x_perm may be NULL to
+ *            produce only the index outputs.
+ * Outputs (device): split_sizes [E], offsets [E+1] (exclusive prefix sum),
+ *   row_id_map [T*k] ((t*k + j) -> permuted row), src_index [T*k] (row ->
+ *   t*k + j), prob_perm [T*k] (may be NULL).
+ * Row order inside an expert's group is ascending t*k + j (stable).
+ * workspace: at least moe_permute_workspace_size(T, k, E) bytes.
+ * ------------------------------------------------------------------------ */
+size_t moe_permute_workspace_size(int64_t T, int k, int E);
+moe_status moe_permute(const void* x, int x_dtype, int64_t T, int64_t H,
+                       const int32_t* topk_idx, const float* topk_prob, int k, int E,
+                       int perm_dtype, void* x_perm, uint8_t* x_perm_scales,
+                       int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                       int32_t* src_index, float* prob_perm,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_fwd -- the whole expert MLP forward:
+ *   permute -> [MXFP8: quantize W1, W2] -> FC1 grouped GEMM with the
+ *   ScaledSwiGLU * prob epilogue (writes h directly in the FC2 operand
+ *   format; the 2I-wide gate-up output is never written unless saved_gu is
+ *   given) -> FC2 grouped GEMM -> combine.
+ *
+ *   h[r, i]  = silu(g[r, i]) * u[r, i] * prob_perm[r],  silu(v) = v * sigmoid(v)
+ *   g, u     = columns [0, I) and [I, 2I) of x_perm[r] . W1_e^T
+ *   z[r]     = h[r] . W2_e^T            (rounded to io_dtype)
+ *   out[t]   = sum_j z[row_id_map[t*k + j]]   (fp32 sum, rounded to io_dtype)
+ *
+ * Shapes: x, out [T, H] io_dtype (MOE_F32 or MOE_BF16); w1[e] [2I, H] bf16
+ * (rows [0, I) gate, [I, 2I) up); w2[e] [H, I] bf16.
+ * compute: MOE_BF16 or MOE_MXFP8_E4M3 (both grouped GEMMs; weights are
+ * quantized from the bf16 masters on every call).
+ * Alignment: H % 64 == 0 and I % 64 == 0 (BF16); H % 128 == 0 and
+ * I % 128 == 0 (MXFP8).  Any token counts per expert, including zero.
+ * Permutation outputs are always written (caller buffers, device).
+ * saved_*: optional (all NULL for inference, all set for training): bf16
+ * copies kept for the backward -- x_perm [R, H], gu [R, 2I] (gate-up
+ * output), h [R, I] (before MXFP8 quantization).  R = T*k.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t T, H, I;
+  int32_t E, k;
+  int32_t compute;              /* moe_dtype: MOE_BF16 or MOE_MXFP8_E4M3 */
+  int32_t io_dtype;             /* moe_dtype: MOE_F32 or MOE_BF16 */
+  const void* x;                /* [T, H] */
+  const int32_t* topk_idx;      /* [T, k] */
+  const float* topk_prob;       /* [T, k] */
+  const void* const* w1;        /* host array of E device pointers, [2I, H] bf16 each */
+  const void* const* w2;        /* host array of E device pointers, [H, I] bf16 each */
+  void* out;                    /* [T, H] */
+  int32_t* split_sizes;         /* [E]   */
+  int32_t* offsets;             /* [E+1] */
+  int32_t* row_id_map;          /* [R]   */
+  int32_t* src_index;           /* [R]   */
+  float* prob_perm;             /* [R]   */
+  void* saved_x_perm;           /* [R, H]  bf16, or NULL */
+  void* saved_gu;               /* [R, 2I] bf16, or NULL */
+  void* saved_h;                /* [R, I]  bf16, or NULL */
+  void* workspace;
+  size_t workspace_bytes;
+} moe_mlp_fwd_args;
+
+size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a);
+moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_bwd -- gradients of sum(out * dy):
+ *   dz[r]     = dy[token of r]
+ *   dh        = dz . W2_e                              (FC2 dgrad)
+ *   a = silu(g) u;  dprob_perm[r] = sum_i dh[r,i] a[r,i]
+ *   du = dh p silu(g);  dg = dh p u silu'(g),  silu'(g) = s (1 + g (1 - s)), s = sigmoid(g)
+ *   dgu = [dg | du] rounded to bf16                    (FC2 dgrad epilogue)
+ *   dW2_e = dz_e^T . h_e ;  dW1_e = dgu_e^T . x_perm_e  (variable-K wgrad; zero-token experts get 0)
+ *   dx_perm = dgu . W1_e (rounded to io_dtype);  dx[t] = sum_j dx_perm[row_id_map[t*k+j]]
+ *   dprob[t, j] = dprob_perm[row_id_map[t*k+j]]
+ * Under MXFP8 every GEMM operand is quantized along that GEMM's own K
+ * (token-axis blocks restart per expert).  dw1/dw2 are overwritten.
+ * g, u, h and x_perm are the bf16 tensors saved by the forward.
+ * ------------------------------------------------------------------------ */
+typedef struct {
+  int64_t T, H, I;
+  int32_t E, k;
+  int32_t compute;              /* as in the forward */
+  int32_t io_dtype;             /* dtype of dy and dx */
+  int32_t dw_dtype;             /* MOE_F32 or MOE_BF16 */
+  const void* dy;               /* [T, H] */
+  const void* const* w1;        /* host array of E device pointers [2I, H] bf16 */
+  const void* const* w2;        /* host array of E device pointers [H, I] bf16 */
+  const int32_t* split_sizes;   /* from the forward */
+  const int32_t* offsets;
+  const int32_t* row_id_map;
+  const int32_t* src_index;
+  const float* prob_perm;
+  const void* saved_x_perm;     /* [R, H]  bf16 */
+  const void* saved_gu;         /* [R, 2I] bf16 */
+  const void* saved_h;          /* [R, I]  bf16 */
+  void* dx;                     /* [T, H] io_dtype */
+  float* dprob;                 /* [T, k] */
+  void* const* dw1;             /* host array of E device pointers [2I, H] dw_dtype */
+  void* const* dw2;             /* host array of E device pointers [H, I] dw_dtype */
+  void* workspace;
+  size_t workspace_bytes;
+} moe_mlp_bwd_args;
+
+size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a);
+moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream);
+
+/* Synchronizes `stream`, then returns the device error flag kept in the first
+ * 4 bytes of `workspace` by the last moe_permute / moe_grouped_mlp_fwd call
+ * that used it (0 = none, 1 = an expert id was out of range; every such call
+ * rewrites the flag).  Returns -1 if the HIP calls fail. */
+int moe_read_device_error(void* workspace, void* stream);
+
+/* Human-readable name of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

@@ -1,0 +1,332 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Every step of the layer runs in the library's HIP kernels; this module turns
+torch tensors into device pointers and the current HIP stream, allocates the
+caller-owned output and workspace buffers with torch, and raises on a non-OK
+status.  There is no fallback: if libmoe.so is missing or cannot be loaded,
+every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+MOE_F32, MOE_BF16, MOE_MXFP8_E4M3 = 0, 1, 2
+MAX_EXPERTS = 256
+
+# every symbol include/moe.h declares
+EXPORTS = (
+    "moe_abi_version", "moe_status_string", "mxfp8_quantize", "moe_permute_workspace_size", "moe_permute",
+    "moe_grouped_mlp_fwd_workspace", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd_workspace",
+    "moe_grouped_mlp_bwd", "moe_read_device_error",
+)
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("T", _i64), ("H", _i64), ("I", _i64),
+        ("E", _i32), ("k", _i32), ("compute", _i32), ("io_dtype", _i32),
+        ("x", _vp), ("topk_idx", _vp), ("topk_prob", _vp),
+        ("w1", ctypes.POINTER(_vp)), ("w2", ctypes.POINTER(_vp)),
+        ("out", _vp),
+        ("split_sizes", _vp), ("offsets", _vp), ("row_id_map", _vp), ("src_index", _vp), ("prob_perm", _vp),
+        ("saved_x_perm", _vp), ("saved_gu", _vp), ("saved_h", _vp),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("T", _i64), ("H", _i64), ("I", _i64),
+        ("E", _i32), ("k", _i32), ("compute", _i32), ("io_dtype", _i32), ("dw_dtype", _i32),
+        ("dy", _vp),
+        ("w1", ctypes.POINTER(_vp)), ("w2", ctypes.POINTER(_vp)),
+        ("split_sizes", _vp), ("offsets", _vp), ("row_id_map", _vp), ("src_index", _vp), ("prob_perm", _vp),
+        ("saved_x_perm", _vp), ("saved_gu", _vp), ("saved_h", _vp),
+        ("dx", _vp), ("dprob", _vp),
+        ("dw1", ctypes.POINTER(_vp)), ("dw2", ctypes.POINTER(_vp)),
+        ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def load(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} not found: build it with `python -m mixture_experts_grouped_permute_amd.build`")
+    lib = ctypes.CDLL(p)
+    lib.moe_abi_version.restype = ctypes.c_int
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.mxfp8_quantize.restype = ctypes.c_int
+    lib.mxfp8_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp]
+    lib.moe_permute_workspace_size.restype = ctypes.c_size_t
+    lib.moe_permute_workspace_size.argtypes = [_i64, ctypes.c_int, ctypes.c_int]
+    lib.moe_permute.restype = ctypes.c_int
+    lib.moe_permute.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_grouped_mlp_fwd_workspace.restype = ctypes.c_size_t
+    lib.moe_grouped_mlp_fwd_workspace.argtypes = [ctypes.POINTER(FwdArgs)]
+    lib.moe_grouped_mlp_fwd.restype = ctypes.c_int
+    lib.moe_grouped_mlp_fwd.argtypes = [ctypes.POINTER(FwdArgs), _vp]
+    lib.moe_grouped_mlp_bwd_workspace.restype = ctypes.c_size_t
+    lib.moe_grouped_mlp_bwd_workspace.argtypes = [ctypes.POINTER(BwdArgs)]
+    lib.moe_grouped_mlp_bwd.restype = ctypes.c_int
+    lib.moe_grouped_mlp_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+    lib.moe_read_device_error.restype = ctypes.c_int
+    lib.moe_read_device_error.argtypes = [_vp, _vp]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    try:
+        return load().moe_status_string(int(status)).decode()
+    except Exception:  # pragma: no cover - only while reporting another error
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != MOE_OK:
+        raise MoeError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _io(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _compute(c: str) -> int:
+    return {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3}[c]
+
+
+def _table(ws: Sequence[torch.Tensor] | torch.Tensor):
+    items = [ws[e] for e in range(ws.shape[0])] if isinstance(ws, torch.Tensor) else list(ws)
+    arr = (_vp * len(items))(*[_ptr(w.contiguous() if not w.is_contiguous() else w) for w in items])
+    return arr, items
+
+
+class _Workspace:
+    """A growable per-device scratch buffer owned by torch (the library never allocates)."""
+
+    def __init__(self):
+        self.buf = {}
+
+    def get(self, nbytes: int, device: torch.device) -> torch.Tensor:
+        key = (device.type, device.index)
+        b = self.buf.get(key)
+        if b is None or b.numel() < nbytes:
+            b = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+            self.buf[key] = b
+        return b
+
+
+_WS = _Workspace()
+
+
+# ----------------------------------------------------------------------------- entry points
+
+def mxfp8_quantize(x: torch.Tensor, axis: int = 0, group_offsets: Optional[torch.Tensor] = None):
+    """OCP MXFP8 of x [rows, cols] (bf16 or f32).
+
+    axis 0: returns (codes uint8 [rows, cols], scales uint8 [rows, cols/32]).
+    axis 1: blocks along rows restarted per segment of group_offsets (int32 device
+            [G+1]); returns (codes [cols, rows + 32G], scales [cols, (rows + 32G)/32]),
+            token axis contiguous, padded segments as documented in moe.h.
+    """
+    lib = load()
+    rows, cols = x.shape
+    dev = x.device
+    if axis == 0:
+        q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        s = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        st = lib.mxfp8_quantize(_ptr(x), _io(x), rows, cols, 0, None, 0, _ptr(q), _ptr(s), _stream(dev))
+    else:
+        G = group_offsets.numel() - 1
+        rp = (rows + 31) // 32 * 32 + 32 * G
+        q = torch.zeros((cols, rp), dtype=torch.uint8, device=dev)
+        s = torch.zeros((cols, rp // 32), dtype=torch.uint8, device=dev)
+        st = lib.mxfp8_quantize(_ptr(x), _io(x), rows, cols, 1, _ptr(group_offsets), G, _ptr(q), _ptr(s),
+                                _stream(dev))
+    _check(st, "mxfp8_quantize")
+    return q, s
+
+
+def moe_permute(x: Optional[torch.Tensor], topk_idx: torch.Tensor, topk_prob: Optional[torch.Tensor], E: int,
+                perm_dtype: str = "bf16"):
+    """Histogram / prefix sum / stable scatter.  Returns a dict of device tensors."""
+    lib = load()
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    R = T * k
+    out = {
+        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
+        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
+        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev) if topk_prob is not None else None,
+        "x_perm": None, "x_perm_scales": None,
+    }
+    H = 0
+    pd = _compute(perm_dtype)
+    if x is not None:
+        H = x.shape[1]
+        if pd == MOE_BF16:
+            out["x_perm"] = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        else:
+            out["x_perm"] = torch.empty((R, H), dtype=torch.uint8, device=dev)
+            out["x_perm_scales"] = torch.empty((R, H // 32), dtype=torch.uint8, device=dev)
+    need = lib.moe_permute_workspace_size(T, k, E)
+    ws = _WS.get(need, dev)
+    st = lib.moe_permute(_ptr(x), _io(x) if x is not None else MOE_BF16, T, H, _ptr(topk_idx), _ptr(topk_prob),
+                         k, E, pd, _ptr(out["x_perm"]), _ptr(out["x_perm_scales"]), _ptr(out["split_sizes"]),
+                         _ptr(out["offsets"]), _ptr(out["row_id_map"]), _ptr(out["src_index"]),
+                         _ptr(out["prob_perm"]), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check(st, "moe_permute")
+    out["workspace"] = ws
+    return out
+
+
+def _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved):
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    w1t, w1k = _table(w1)
+    w2t, w2k = _table(w2)
+    E = len(w1k)
+    I = w2k[0].shape[1]
+    a = FwdArgs()
+    a.T, a.H, a.I, a.E, a.k = T, H, I, E, k
+    a.compute = _compute(compute)
+    a.io_dtype = _io(x)
+    a.x, a.topk_idx, a.topk_prob = _ptr(x), _ptr(topk_idx), _ptr(topk_prob)
+    a.w1, a.w2 = w1t, w2t
+    a.out = _ptr(out)
+    a.split_sizes, a.offsets = _ptr(perm["split_sizes"]), _ptr(perm["offsets"])
+    a.row_id_map, a.src_index, a.prob_perm = _ptr(perm["row_id_map"]), _ptr(perm["src_index"]), _ptr(perm["prob_perm"])
+    if saved is not None:
+        a.saved_x_perm, a.saved_gu, a.saved_h = _ptr(saved["x_perm"]), _ptr(saved["gu"]), _ptr(saved["h"])
+    return a, (w1t, w2t, w1k, w2k), E, I
+
+
+def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor, w1, w2,
+                        compute: str = "bf16", save_for_backward: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Grouped expert MLP forward.  w1: [E,2I,H] tensor or E tensors [2I,H] (bf16);
+    w2: [E,H,I] or E tensors [H,I].  Returns (out, ctx) where ctx holds the
+    permutation and, with save_for_backward, the bf16 activations."""
+    lib = load()
+    dev = x.device
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    R = T * k
+    E = w1.shape[0] if isinstance(w1, torch.Tensor) else len(w1)
+    I = (w2.shape[2] if isinstance(w2, torch.Tensor) else w2[0].shape[1])
+    perm = {
+        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
+        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
+        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
+    }
+    saved = None
+    if save_for_backward:
+        saved = {
+            "x_perm": torch.empty((R, H), dtype=torch.bfloat16, device=dev),
+            "gu": torch.empty((R, 2 * I), dtype=torch.bfloat16, device=dev),
+            "h": torch.empty((R, I), dtype=torch.bfloat16, device=dev),
+        }
+    out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    a, keep, _, _ = _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved)
+    need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    if need == 0:
+        # the size query validates the arguments: surface the status of the call itself
+        _check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_fwd")
+    ws = workspace if workspace is not None else _WS.get(need, dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    _check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_fwd")
+    ctx = {"perm": perm, "saved": saved, "compute": compute, "E": E, "I": I, "workspace": ws, "_keep": keep}
+    return out, ctx
+
+
+def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32,
+                        workspace: Optional[torch.Tensor] = None):
+    """Backward of moe_grouped_mlp_fwd (needs save_for_backward=True).
+    Returns (dx [T,H], dprob [T,k] f32, dw1 [E,2I,H], dw2 [E,H,I])."""
+    lib = load()
+    dev = dy.device
+    T, H = dy.shape
+    perm, saved = ctx["perm"], ctx["saved"]
+    if saved is None:
+        raise ValueError("forward was run without save_for_backward")
+    E, I = ctx["E"], ctx["I"]
+    k = perm["row_id_map"].numel() // T
+    dx = torch.empty((T, H), dtype=dy.dtype, device=dev)
+    dprob = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dw1 = torch.empty((E, 2 * I, H), dtype=dw_dtype, device=dev)
+    dw2 = torch.empty((E, H, I), dtype=dw_dtype, device=dev)
+    w1t, w1k = _table(w1)
+    w2t, w2k = _table(w2)
+    dw1t, _ = _table(dw1)
+    dw2t, _ = _table(dw2)
+    a = BwdArgs()
+    a.T, a.H, a.I, a.E, a.k = T, H, I, E, k
+    a.compute = _compute(ctx["compute"])
+    a.io_dtype = _io(dy)
+    a.dw_dtype = _io(dw1)
+    a.dy = _ptr(dy)
+    a.w1, a.w2 = w1t, w2t
+    a.split_sizes, a.offsets = _ptr(perm["split_sizes"]), _ptr(perm["offsets"])
+    a.row_id_map, a.src_index, a.prob_perm = _ptr(perm["row_id_map"]), _ptr(perm["src_index"]), _ptr(perm["prob_perm"])
+    a.saved_x_perm, a.saved_gu, a.saved_h = _ptr(saved["x_perm"]), _ptr(saved["gu"]), _ptr(saved["h"])
+    a.dx, a.dprob = _ptr(dx), _ptr(dprob)
+    a.dw1, a.dw2 = dw1t, dw2t
+    need = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(a))
+    if need == 0:
+        _check(lib.moe_grouped_mlp_bwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_bwd")
+    ws = workspace if workspace is not None else _WS.get(need, dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    _check(lib.moe_grouped_mlp_bwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_bwd")
+    return dx, dprob, dw1, dw2
+
+
+def moe_read_device_error(workspace: torch.Tensor) -> int:
+    return load().moe_read_device_error(workspace.data_ptr(), _stream(workspace.device))

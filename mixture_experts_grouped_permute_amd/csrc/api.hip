@@ -1,0 +1,294 @@
+// C-ABI entry points of libmoe.so: argument validation, workspace carving and
+// launch sequencing.  Everything is enqueued on the caller's stream; nothing
+// here allocates device memory or synchronizes (except moe_read_device_error).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Sequential carve-out of a caller-provided workspace (or a dry run to size it).
+struct Carver {
+  uint8_t* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(reinterpret_cast<uint8_t*>(b)) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used = align_up(used + bytes);
+    return p;
+  }
+};
+
+inline bool io_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
+inline size_t io_size(int d) { return d == MOE_F32 ? 4 : 2; }
+
+int perm_blocks(int64_t R) { return (int)((R + kPermChunk - 1) / kPermChunk) + 0; }
+
+struct PermWs {
+  int32_t* err;
+  int32_t* block_counts;
+  int32_t* block_base;
+};
+
+PermWs carve_perm(Carver& c, int64_t R, int E) {
+  PermWs w;
+  const int nb = perm_blocks(R) < 1 ? 1 : perm_blocks(R);
+  w.err = reinterpret_cast<int32_t*>(c.take(kAlign));
+  w.block_counts = reinterpret_cast<int32_t*>(c.take(sizeof(int32_t) * (size_t)nb * (E + 1)));
+  w.block_base = reinterpret_cast<int32_t*>(c.take(sizeof(int32_t) * (size_t)nb * E));
+  return w;
+}
+
+#define MOE_CHECK(cond, code) \
+  do {                        \
+    if (!(cond)) return (code); \
+  } while (0)
+
+#define HIP_TRY(expr)                         \
+  do {                                        \
+    if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+moe_status check_common(int64_t T, int64_t H, int E, int k) {
+  if (T <= 0 || H <= 0 || E <= 0 || k <= 0) return MOE_ERR_INVALID_ARG;
+  if (E > MOE_MAX_EXPERTS || k > MOE_MAX_TOPK || k > E) return MOE_ERR_INVALID_ARG;
+  if (T * (int64_t)k > (int64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Forward workspace plan (pointers are null on a dry run).
+struct FwdPlan {
+  PermWs perm;
+  void* x_op;          // bf16 [R,H] or E4M3 [R,H]
+  uint8_t* x_sc;       // [R,H/32]
+  void* h_op;          // bf16 [R,I] or E4M3 [R,I]
+  uint8_t* h_sc;       // [R,I/32]
+  void* z;             // [R,H] io dtype
+  uint8_t* w1q; uint8_t* w1s; uint8_t* w2q; uint8_t* w2s;
+  size_t bytes;
+};
+
+FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
+  FwdPlan p{};
+  Carver c(ws);
+  const int64_t R = a->T * a->k, H = a->H, I = a->I;
+  const int E = a->E;
+  const bool mx = a->compute == MOE_MXFP8_E4M3;
+  p.perm = carve_perm(c, R, E);
+  if (mx) {
+    p.x_op = c.take((size_t)(R * H));
+    p.x_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * H / 32)));
+    p.h_op = c.take((size_t)(R * I));
+    p.h_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * I / 32)));
+    p.w1q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H)));
+    p.w1s = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H / 32)));
+    p.w2q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I)));
+    p.w2s = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I / 32)));
+  } else {
+    if (!a->saved_x_perm) p.x_op = c.take((size_t)(R * H * 2));
+    else p.x_op = a->saved_x_perm;
+    if (!a->saved_h) p.h_op = c.take((size_t)(R * I * 2));
+    else p.h_op = a->saved_h;
+  }
+  p.z = c.take((size_t)(R * H) * io_size(a->io_dtype));
+  p.bytes = c.used;
+  return p;
+}
+
+moe_status validate_fwd(const moe_mlp_fwd_args* a) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_common(a->T, a->H, a->E, a->k);
+  if (s != MOE_OK) return s;
+  if (a->I <= 0) return MOE_ERR_INVALID_ARG;
+  if (!io_ok(a->io_dtype)) return MOE_ERR_INVALID_ARG;
+  if (a->compute != MOE_BF16 && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const int64_t align = a->compute == MOE_BF16 ? 64 : 128;
+  if (a->H % align || a->I % align) return MOE_ERR_UNSUPPORTED;
+  if (!a->x || !a->topk_idx || !a->topk_prob || !a->w1 || !a->w2 || !a->out) return MOE_ERR_INVALID_ARG;
+  if (!a->split_sizes || !a->offsets || !a->row_id_map || !a->src_index || !a->prob_perm)
+    return MOE_ERR_INVALID_ARG;
+  for (int e = 0; e < a->E; ++e)
+    if (!a->w1[e] || !a->w2[e]) return MOE_ERR_INVALID_ARG;
+  const bool any_saved = a->saved_x_perm || a->saved_gu || a->saved_h;
+  const bool all_saved = a->saved_x_perm && a->saved_gu && a->saved_h;
+  if (any_saved && !all_saved) return MOE_ERR_INVALID_ARG;
+  // 32-bit buffer ranges inside the GEMMs
+  const int64_t R = a->T * a->k;
+  const int64_t widest = a->H > 2 * a->I ? a->H : 2 * a->I;
+  if (R * widest * 2 >= (int64_t)UINT32_MAX || 2 * a->I * a->H * 2 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return 1; }
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int axis,
+                          const int32_t* group_offsets, int num_groups, uint8_t* q, uint8_t* scales,
+                          void* stream) {
+  MOE_CHECK(x && q && scales, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(rows > 0 && cols > 0 && io_ok(x_dtype), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(cols % 32 == 0 || axis == 1, MOE_ERR_UNSUPPORTED);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (axis == 0) {
+    HIP_TRY(launch_mx_quant_rows(x, x_dtype == MOE_F32, rows, cols, q, scales, st));
+    return MOE_OK;
+  }
+  if (axis == 1) {
+    MOE_CHECK(group_offsets && num_groups >= 1 && num_groups <= MOE_MAX_EXPERTS, MOE_ERR_INVALID_ARG);
+    MOE_CHECK(cols % 32 == 0, MOE_ERR_UNSUPPORTED);
+    const int64_t rows_pad = (rows + 31) / 32 * 32 + 32 * (int64_t)num_groups;
+    HIP_TRY(launch_mx_quant_cols(x, x_dtype == MOE_F32, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                 st));
+    return MOE_OK;
+  }
+  return MOE_ERR_INVALID_ARG;
+}
+
+size_t moe_permute_workspace_size(int64_t T, int k, int E) {
+  if (T <= 0 || k <= 0 || E <= 0) return 0;
+  Carver c(nullptr);
+  carve_perm(c, T * k, E);
+  return c.used;
+}
+
+moe_status moe_permute(const void* x, int x_dtype, int64_t T, int64_t H, const int32_t* topk_idx,
+                       const float* topk_prob, int k, int E, int perm_dtype, void* x_perm,
+                       uint8_t* x_perm_scales, int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                       int32_t* src_index, float* prob_perm, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  moe_status s = check_common(T, x_perm ? H : 1, E, k);
+  if (s != MOE_OK) return s;
+  MOE_CHECK(topk_idx && split_sizes && offsets && row_id_map && src_index, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(!prob_perm || topk_prob, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(perm_dtype == MOE_BF16 || perm_dtype == MOE_MXFP8_E4M3, MOE_ERR_INVALID_ARG);
+  if (x_perm) {
+    MOE_CHECK(x && io_ok(x_dtype), MOE_ERR_INVALID_ARG);
+    MOE_CHECK(H % 32 == 0, MOE_ERR_UNSUPPORTED);
+    if (perm_dtype == MOE_MXFP8_E4M3) MOE_CHECK(x_perm_scales != nullptr, MOE_ERR_INVALID_ARG);
+  }
+  const size_t need = moe_permute_workspace_size(T, k, E);
+  MOE_CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Carver c(workspace);
+  PermWs w = carve_perm(c, T * k, E);
+  HIP_TRY(launch_permute_indices(topk_idx, topk_prob, T * k, E, split_sizes, offsets, row_id_map, src_index,
+                                 prob_perm, w.err, w.block_counts, w.block_base, st));
+  if (x_perm)
+    HIP_TRY(launch_permute_rows(x, x_dtype == MOE_F32, T, H, k, row_id_map, x_perm, x_perm_scales,
+                                perm_dtype == MOE_MXFP8_E4M3, st));
+  return MOE_OK;
+}
+
+size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a) {
+  if (validate_fwd(a) != MOE_OK) return 0;
+  return plan_fwd(a, nullptr).bytes;
+}
+
+moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream) {
+  moe_status s = validate_fwd(a);
+  if (s != MOE_OK) return s;
+  const size_t need = plan_fwd(a, nullptr).bytes;
+  MOE_CHECK(a->workspace && a->workspace_bytes >= need, MOE_ERR_WORKSPACE);
+  FwdPlan p = plan_fwd(a, a->workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t T = a->T, H = a->H, I = a->I, R = T * a->k;
+  const int E = a->E, k = a->k;
+  const bool mx = a->compute == MOE_MXFP8_E4M3;
+  const bool x_f32 = a->io_dtype == MOE_F32;
+
+  HIP_TRY(launch_permute_indices(a->topk_idx, a->topk_prob, R, E, a->split_sizes, a->offsets, a->row_id_map,
+                                 a->src_index, a->prob_perm, p.perm.err, p.perm.block_counts, p.perm.block_base,
+                                 st));
+  if (mx) {
+    HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, p.x_sc, true, st));
+    if (a->saved_x_perm)
+      HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, a->saved_x_perm, nullptr, false, st));
+    HIP_TRY(launch_mx_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.w1s, a->split_sizes, st));
+    HIP_TRY(launch_mx_quant_weights(a->w2, E, H, I, p.w2q, p.w2s, a->split_sizes, st));
+  } else {
+    HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, nullptr, false, st));
+  }
+
+  FwdGemm g1{};
+  g1.a = p.x_op;
+  g1.a_scales = p.x_sc;
+  g1.w_tab = a->w1;
+  g1.wq = p.w1q;
+  g1.wq_stride = 2 * I * H;
+  g1.ws = p.w1s;
+  g1.ws_stride = 2 * I * H / 32;
+  g1.K = H;
+  g1.N = I;
+  g1.E = E;
+  g1.split_sizes = a->split_sizes;
+  g1.prob_perm = a->prob_perm;
+  g1.out = p.h_op;
+  g1.out_scales = p.h_sc;
+  g1.save_gu = reinterpret_cast<uint16_t*>(a->saved_gu);
+  g1.save_h = mx ? reinterpret_cast<uint16_t*>(a->saved_h) : nullptr;
+  HIP_TRY(launch_fc1(g1, mx, st));
+
+  FwdGemm g2{};
+  g2.a = p.h_op;
+  g2.a_scales = p.h_sc;
+  g2.w_tab = a->w2;
+  g2.wq = p.w2q;
+  g2.wq_stride = H * I;
+  g2.ws = p.w2s;
+  g2.ws_stride = H * I / 32;
+  g2.K = I;
+  g2.N = H;
+  g2.E = E;
+  g2.split_sizes = a->split_sizes;
+  g2.out = p.z;
+  g2.out_f32 = x_f32;
+  HIP_TRY(launch_fc2(g2, mx, st));
+
+  HIP_TRY(launch_combine(p.z, x_f32, T, H, k, a->row_id_map, a->out, x_f32, st));
+  return MOE_OK;
+}
+
+size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a) {
+  (void)a;
+  return 0;
+}
+
+moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
+  (void)a;
+  (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+int moe_read_device_error(void* workspace, void* stream) {
+  if (!workspace) return -1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return -1;
+  int32_t flag = 0;
+  if (hipMemcpy(&flag, workspace, sizeof(flag), hipMemcpyDeviceToHost) != hipSuccess) return -1;
+  return flag;
+}
+
+}  // extern "C"

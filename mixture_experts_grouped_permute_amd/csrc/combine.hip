@@ -1,0 +1,125 @@
+// Un-permute / combine kernels for gfx950.
+//
+// Forward (page "BioNeMo Uses Grouped Kernels and MXFP8", Figure 1: the k
+// expert outputs of a token are combined as a weighted sum; the weights were
+// already applied to h by ScaledSwiGLU, so this is a plain sum):
+//   out[t] = sum_j z[row_id_map[t*k + j]]   (fp32, slot order, rounded once)
+// The same kernel sums dx_perm into dx in the backward.  A wave owns one token
+// and streams its k source rows with 16-byte loads.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+template <bool kInF32, bool kOutF32>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ z, int64_t T, int64_t H, int k,
+                                                        const int32_t* __restrict__ row_id_map,
+                                                        void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int rows[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) rows[j] = j < k ? row_id_map[t * k + j] : -1;
+  for (int64_t c = (int64_t)lane * 8; c < H; c += 512) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k || rows[j] < 0) continue;
+      const int64_t o = (int64_t)rows[j] * H + c;
+      if (kInF32) {
+        const float4* s = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + o);
+        float4 a = s[0], b = s[1];
+        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+      } else {
+        u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(z) + o);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
+          acc[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
+        }
+      }
+    }
+    const int64_t o = t * H + c;
+    if (kOutF32) {
+      float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o);
+      d[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      d[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    } else {
+      u32x4 w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + o) = w;
+    }
+  }
+}
+
+// dz[r] = dy[src_index[r] / k] for the rows of valid experts (rows past offsets[E] untouched).
+template <bool kF32>
+__global__ __launch_bounds__(256) void gather_kernel(const void* __restrict__ x, int64_t R, int64_t H, int k,
+                                                       const int32_t* __restrict__ src_index,
+                                                       const int32_t* __restrict__ offsets, int E,
+                                                       void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R || r >= offsets[E]) return;
+  const int64_t t = src_index[r] / k;
+  const int esz = kF32 ? 4 : 2;
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + t * H * esz;
+  uint8_t* dst = reinterpret_cast<uint8_t*>(out) + r * H * esz;
+  for (int64_t b = (int64_t)lane * 16; b < H * esz; b += 1024)
+    *reinterpret_cast<u32x4*>(dst + b) = *reinterpret_cast<const u32x4*>(src + b);
+}
+
+// dprob[t, j] = sum over parts of partial[row, part], row = row_id_map[t*k + j] (fixed order).
+__global__ __launch_bounds__(256) void dprob_kernel(const float* __restrict__ partial, int parts,
+                                                      const int32_t* __restrict__ row_id_map, int64_t Tk,
+                                                      float* __restrict__ dprob) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (p >= Tk) return;
+  const int r = row_id_map[p];
+  float s = 0.f;
+  if (r >= 0)
+    for (int q = 0; q < parts; ++q) s += partial[(int64_t)r * parts + q];
+  dprob[p] = s;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* z, bool z_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
+                          void* out, bool out_f32, hipStream_t st) {
+  dim3 grid((unsigned)((T + 3) / 4));
+  if (T == 0) return hipSuccess;
+  if (z_f32) {
+    if (out_f32) combine_kernel<true, true><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
+    else combine_kernel<true, false><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
+  } else {
+    if (out_f32) combine_kernel<false, true><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
+    else combine_kernel<false, false><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* x, bool f32, int64_t R, int64_t H, int k, const int32_t* src_index,
+                              const int32_t* offsets, int E, void* out, hipStream_t st) {
+  dim3 grid((unsigned)((R + 3) / 4));
+  if (R == 0) return hipSuccess;
+  if (f32) gather_kernel<true><<<grid, 256, 0, st>>>(x, R, H, k, src_index, offsets, E, out);
+  else gather_kernel<false><<<grid, 256, 0, st>>>(x, R, H, k, src_index, offsets, E, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_dprob_reduce(const float* partial, int64_t R, int parts, const int32_t* row_id_map, int64_t T,
+                               int k, float* dprob, hipStream_t st) {
+  (void)R;
+  const int64_t Tk = T * k;
+  if (Tk == 0) return hipSuccess;
+  dprob_kernel<<<(unsigned)((Tk + 255) / 256), 256, 0, st>>>(partial, parts, row_id_map, Tk, dprob);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,113 @@
+// Shared device helpers for the gfx950 kernels: vector types, bf16 rounding,
+// the OCP MXFP8 element/scale rule in integer arithmetic, wave reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxExperts = 256;
+
+__host__ __device__ inline float bf16_to_f32(uint16_t b) {
+  return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+// Round-to-nearest-even float32 -> bf16 bits (NaN kept quiet).
+__host__ __device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__host__ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// OCP MXFP8 (E4M3FN elements, E8M0 shared exponent) in integer arithmetic so
+// that the bytes do not depend on the float unit's denormal or rounding mode.
+//   shared exponent s = floor(log2(amax)) - 8, clamped to [-127, 127]
+//   code = E4M3FN(v / 2^s), round to nearest even, saturate to +-448,
+//   zero keeps its sign.
+// ---------------------------------------------------------------------------
+
+// Shared exponent from the bit pattern of |amax| (a non-negative float).
+__host__ __device__ inline int mx_shared_exp(float amax) {
+  uint32_t u = __builtin_bit_cast(uint32_t, amax);
+  int ef = (int)((u >> 23) & 0xFF);
+  if (ef == 0) return -127;          // zero or subnormal amax: floor(log2) <= -127
+  int s = ef - 127 - 8;
+  return s < -127 ? -127 : s;        // ef <= 254 keeps s <= 119
+}
+
+// E4M3FN code of v / 2^s.
+__host__ __device__ inline uint32_t mx_e4m3_code(float v, int s) {
+  uint32_t u = __builtin_bit_cast(uint32_t, v);
+  uint32_t sign = (u >> 24) & 0x80u;
+  int ef = (int)((u >> 23) & 0xFF);
+  uint32_t mant = u & 0x7FFFFFu;
+  int e;                             // unbiased exponent of bit 23 of `mant`
+  if (ef == 0) {
+    if (mant == 0) return sign;      // signed zero
+    int lz = __builtin_clz(mant) - 8; // shift the leading one to bit 23
+    mant <<= lz;
+    e = -126 - lz;
+  } else {
+    mant |= 0x800000u;
+    e = ef - 127;
+  }
+  int eq = e - s;                    // exponent of q = v / 2^s
+  uint32_t code;
+  if (eq >= -6) {
+    // normal E4M3: keep 4 significant bits (1.mmm), round at bit 20
+    uint32_t r = (mant + 0x7FFFFu + ((mant >> 20) & 1u)) >> 20;   // in [8, 16]
+    if (r == 16) { r = 8; ++eq; }
+    if (eq > 8 || (eq == 8 && r > 14)) return sign | 0x7Eu;      // saturate to 448
+    code = ((uint32_t)(eq + 7) << 3) | (r - 8);
+  } else {
+    // subnormal E4M3: n * 2^-9 with n = RNE(mant * 2^(eq - 14))
+    int sh = 14 - eq;                // >= 21
+    uint32_t n;
+    if (sh >= 32) {
+      n = 0;
+    } else {
+      n = (mant + (1u << (sh - 1)) - 1u + ((mant >> sh) & 1u)) >> sh;   // n in [0, 8]
+    }
+    code = n;                        // n == 8 is the smallest normal, code 0x08
+  }
+  return sign | code;
+}
+
+// 4-byte pack of the codes of v[0..3] with exponent s.
+__host__ __device__ inline uint32_t mx_pack4(float a, float b, float c, float d, int s) {
+  return mx_e4m3_code(a, s) | (mx_e4m3_code(b, s) << 8) | (mx_e4m3_code(c, s) << 16) |
+         (mx_e4m3_code(d, s) << 24);
+}
+
+// ---------------------------------------------------------------------------
+// wave64 helpers
+// ---------------------------------------------------------------------------
+__device__ inline float wave_xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+__device__ inline uint64_t lanemask_lt() {
+  int lane = __lane_id();
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+template <typename T>
+__device__ inline T* ptr_add_bytes(T* p, size_t bytes) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(p) + bytes);
+}
+
+}  // namespace moe

@@ -1,0 +1,447 @@
+// Persistent grouped GEMMs for gfx950: BF16 (v_mfma_f32_32x32x16_bf16) and
+// MXFP8 (v_mfma_scale_f32_32x32x64_f8f6f4 with E8M0 block scales).
+//
+// All local experts run in one launch (page "BioNeMo Uses Grouped Kernels and
+// MXFP8", Grouping fragmented expert workloads: the grouped linear submits
+// every expert's GEMM together, each expert keeping its own weights, with
+// split_sizes giving the uneven token counts).  The FC1 epilogue applies
+// ScaledSwiGLU with the routing probability and writes h straight in the FC2
+// operand format, so the 2I-wide gate-up result is never stored (Fusing
+// precision conversion and expert computation, Figure 4).
+//
+// Structure
+//   * 256 threads = 4 waves in a 2x2 grid; a workgroup owns a 256 x 256 output
+//     tile (FC1: 128 h columns = 128 gate + 128 up weight rows); each wave a
+//     128 x 128 block = 4 x 4 MFMA 32x32 fragments accumulated in fp32.
+//   * K is consumed in 128-byte steps (64 bf16 or 128 E4M3 values per row),
+//     double-buffered in LDS (2 x 64 KB) with the 16-byte chunks of each row
+//     XOR-swizzled by (row & 7) so both the row-wise stores and the MFMA
+//     fragment reads are bank-conflict free.
+//   * Global reads are buffer loads whose range is the expert's valid rows,
+//     so ragged tiles read zeros instead of neighbouring experts' data.
+//   * Scheduler: every workgroup recomputes the per-expert tile prefix sum
+//     from split_sizes in LDS (no host sync), then walks tiles in rounds of
+//     gridDim.x.  Tile order is expert, N-panel, M-block (M fastest) and a
+//     round hands each XCD (workgroup id mod 8) a contiguous slice, so the
+//     M-blocks that share one weight panel run together on one L2.
+#include "common.h"
+#include "kernels.h"
+#include <type_traits>
+#include <cstddef>
+
+namespace moe {
+namespace {
+
+constexpr int kBM = 256, kBN = 256;
+constexpr int kRowBytes = 128;
+constexpr int kTileBytes = 256 * kRowBytes;     // 32 KB per operand tile
+constexpr int kStageBytes = 2 * kTileBytes;     // A + B
+constexpr int kScaleBytes = 2 * 256 * 4;        // A + B scale words per stage (MXFP8)
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
+  return row * kRowBytes + ((chunk ^ (row & 7u)) << 4);
+}
+
+// Per-expert counts, row offsets and tile prefix (ceil(M_e / 256) * nN) in LDS.
+struct Sched {
+  int cnt[kMaxExperts];
+  int off[kMaxExperts + 1];
+  int tile[kMaxExperts + 1];
+};
+
+__device__ void build_sched(Sched& s, const int32_t* split_sizes, int E, int nN) {
+  __shared__ int wsum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int c = tid < E ? split_sizes[tid] : 0;
+  int t = (c + kBM - 1) / kBM * nN;
+  // inclusive wave scans of c and t
+  int ic = c, it = t;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int oc = __shfl_up(ic, d, 64), ot = __shfl_up(it, d, 64);
+    if (lane >= d) { ic += oc; it += ot; }
+  }
+  __shared__ int wsum_t[4];
+  if (lane == 63) { wsum[wave] = ic; wsum_t[wave] = it; }
+  __syncthreads();
+  int bc = 0, bt = 0;
+  for (int w = 0; w < wave; ++w) { bc += wsum[w]; bt += wsum_t[w]; }
+  if (tid < E) {
+    s.cnt[tid] = c;
+    s.off[tid] = bc + ic - c;
+    s.tile[tid] = bt + it - t;
+  }
+  if (tid == E - 1) { s.off[E] = bc + ic; s.tile[E] = bt + it; }
+  __syncthreads();
+}
+
+__device__ __forceinline__ int find_expert(const Sched& s, int E, int t) {
+  int lo = 0, hi = E - 1;   // largest e with tile[e] <= t (tile[] is non-decreasing)
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (s.tile[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+// ---------------------------------------------------------------------------
+// One K-pass of a 256x256 tile.  kFc1 selects the B row map (gate/up halves).
+// ---------------------------------------------------------------------------
+template <bool kMx, bool kFc1>
+struct TileCore {
+  f32x16 acc[4][4];
+
+  __device__ __forceinline__ void zero() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  }
+
+  // LDS row of B holding n-fragment j of wave column wn
+  static __device__ __forceinline__ int brow(int wn, int j) {
+    if (kFc1) return (j < 2) ? (wn * 64 + j * 32) : (128 + wn * 64 + (j - 2) * 32);
+    return wn * 128 + j * 32;
+  }
+
+  // Fragments of one MFMA K-substep: 4 A and 4 B operands (+ scales).
+  struct Frag {
+    typename std::conditional<kMx, i32x8, bf16x8>::type a[4], b[4];
+    int sa[4], sb[4];
+  };
+
+  static constexpr int kSub = kMx ? 2 : 4;   // MFMA K-substeps per 128-byte K step
+
+  __device__ __forceinline__ void load_frag(Frag& f, int kk, const uint8_t* sA, const uint8_t* sB,
+                                            const uint32_t* sAs, const uint32_t* sBs, int wm, int wn,
+                                            int lane) const {
+    const int r32 = lane & 31, g = lane >> 5;
+    if constexpr (!kMx) {
+      const uint32_t ch = (uint32_t)(kk * 2 + g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f.a[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + i * 32 + r32, ch));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        f.b[j] = *reinterpret_cast<const bf16x8*>(sB + swz(brow(wn, j) + r32, ch));
+    } else {
+      const uint32_t c0 = (uint32_t)(kk * 4 + g), c1 = (uint32_t)(kk * 4 + 2 + g);
+      const int sh = 8 * (2 * kk + g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = wm * 128 + i * 32 + r32;
+        u32x4 lo = *reinterpret_cast<const u32x4*>(sA + swz(row, c0));
+        u32x4 hi = *reinterpret_cast<const u32x4*>(sA + swz(row, c1));
+        f.a[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        f.sa[i] = (int)(sAs[row] >> sh);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = brow(wn, j) + r32;
+        u32x4 lo = *reinterpret_cast<const u32x4*>(sB + swz(row, c0));
+        u32x4 hi = *reinterpret_cast<const u32x4*>(sB + swz(row, c1));
+        f.b[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        f.sb[j] = (int)(sBs[row] >> sh);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void mma(const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (!kMx)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
+                                                                        f.sb[j]);
+      }
+  }
+
+  // All substeps of one LDS stage, fragments double-buffered in registers.
+  __device__ __forceinline__ void compute(const uint8_t* sA, const uint8_t* sB, const uint32_t* sAs,
+                                          const uint32_t* sBs, int wm, int wn, int lane) {
+    Frag f0, f1;
+    load_frag(f0, 0, sA, sB, sAs, sBs, wm, wn, lane);
+#pragma unroll
+    for (int kk = 0; kk < kSub; kk += 2) {
+      load_frag(f1, kk + 1, sA, sB, sAs, sBs, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 2 < kSub) load_frag(f0, kk + 2, sA, sB, sAs, sBs, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+};
+
+// Kernel arguments: scalars plus the per-expert weight pointer table inline.
+struct FwdKArgs {
+  const uint8_t* a;
+  const uint8_t* a_scales;
+  const uint8_t* wq;
+  const uint8_t* ws;
+  int64_t wq_stride, ws_stride;
+  int64_t K, N;
+  int E, nN;
+  const int32_t* split_sizes;
+  const float* prob_perm;
+  uint8_t* out;
+  uint8_t* out_scales;
+  uint16_t* save_gu;
+  uint16_t* save_h;
+  int out_f32;
+  const uint8_t* w[kMaxExperts];
+};
+
+// Reads w[e] straight from the kernel-argument segment (a uniform scalar load)
+// instead of letting the compiler copy the by-value table to private memory.
+__device__ __forceinline__ const uint8_t* kernarg_table(int e) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint8_t* const* tab = reinterpret_cast<const uint8_t* const*>(
+      reinterpret_cast<const char*>(__builtin_amdgcn_kernarg_segment_ptr()) + offsetof(FwdKArgs, w));
+  return tab[e];
+#else
+  (void)e;
+  return nullptr;
+#endif
+}
+
+template <bool kMx, bool kFc1>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_gemm_kernel(const FwdKArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * kScaleBytes : 16)];
+  __shared__ Sched sched;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int E = p.E;
+  build_sched(sched, p.split_sizes, E, p.nN);
+  const int total = sched.tile[E];
+  const int G = gridDim.x, per = G >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int64_t K = p.K, N = p.N;
+  const int esz = kMx ? 1 : 2;
+  const uint32_t rowb = (uint32_t)(K * esz);           // bytes per operand row
+  const int kT = (int)(rowb / kRowBytes);              // K steps
+  const int ldr = tid >> 3, ldc = tid & 7;             // loader: rows ldr + 32 i, chunk ldc
+  const uint32_t lds_ld = swz(ldr, ldc);
+  const uint32_t kscale_row = (uint32_t)(K / 32);      // scale bytes per row
+
+  for (int round = 0;; ++round) {
+    const int t = round * G + xcd * per + slot;
+    if (t >= total) break;
+    const int e = find_expert(sched, E, t);
+    const int Me = sched.cnt[e];
+    const int nM = (Me + kBM - 1) / kBM;
+    const int local = t - sched.tile[e];
+    const int mt = local % nM, nt = local / nM;
+    const int row0 = sched.off[e] + mt * kBM;           // first permuted row of the tile
+    const int mrows = min(kBM, Me - mt * kBM);
+    // ---- operand descriptors
+    rsrc_t ra = make_rsrc(p.a + (int64_t)row0 * rowb, (uint32_t)mrows * rowb);
+    const uint8_t* wbase = kMx ? (p.wq + (int64_t)e * p.wq_stride) : kernarg_table(e);
+    rsrc_t rb;
+    uint32_t bvo[8];
+    if (kFc1) {
+      // LDS rows [0,128): gate rows n0h + r; [128,256): up rows I + n0h + r.  Gate rows past I
+      // only feed masked columns; up rows past 2I fall outside the range and read zero.
+      const int64_t n0h = (int64_t)nt * 128;
+      rb = make_rsrc(wbase, (uint32_t)(2 * N * rowb));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int r = ldr + 32 * i;
+        int64_t wr = r < 128 ? (n0h + r) : (N + n0h + (r - 128));
+        bvo[i] = (uint32_t)(wr * rowb) + ldc * 16;
+      }
+    } else {
+      const int64_t n0 = (int64_t)nt * kBN;
+      const int64_t nrows = min((int64_t)kBN, N - n0);
+      rb = make_rsrc(wbase + n0 * rowb, (uint32_t)(nrows * rowb));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bvo[i] = (uint32_t)((ldr + 32 * i) * rowb) + ldc * 16;
+    }
+    rsrc_t ras, rbs;
+    uint32_t bso = 0;
+    if (kMx) {
+      ras = make_rsrc(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
+      const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
+      if (kFc1) {
+        const int64_t n0h = (int64_t)nt * 128;
+        rbs = make_rsrc(sbase, (uint32_t)(2 * N * kscale_row));
+        int64_t wr = tid < 128 ? (n0h + tid) : (N + n0h + (tid - 128));
+        bso = (uint32_t)(wr * kscale_row);
+      } else {
+        const int64_t n0 = (int64_t)nt * kBN;
+        const int64_t nrows = min((int64_t)kBN, N - n0);
+        rbs = make_rsrc(sbase + n0 * kscale_row, (uint32_t)(nrows * kscale_row));
+        bso = (uint32_t)(tid * kscale_row);
+      }
+    }
+    const uint32_t avo0 = (uint32_t)(ldr * rowb) + ldc * 16;
+    const uint32_t astride = 32u * rowb;
+
+    TileCore<kMx, kFc1> core;
+    core.zero();
+    u32x4 ra_reg[8], rb_reg[8];
+    uint32_t ras_reg = 0, rbs_reg = 0;
+
+    auto gload = [&](int kt) {
+      const uint32_t so = (uint32_t)kt * kRowBytes;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ra_reg[i] = bload16(ra, avo0 + i * astride, so);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rb_reg[i] = bload16(rb, bvo[i], so);
+      if (kMx) {
+        ras_reg = bload4(ras, (uint32_t)(tid * kscale_row), (uint32_t)kt * 4);
+        rbs_reg = bload4(rbs, bso, (uint32_t)kt * 4);
+      }
+    };
+    auto lstore = [&](int stage) {
+      uint8_t* sA = smem + stage * kStageBytes;
+      uint8_t* sB = sA + kTileBytes;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sA + lds_ld + i * 32 * kRowBytes) = ra_reg[i];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sB + lds_ld + i * 32 * kRowBytes) = rb_reg[i];
+      if (kMx) {
+        uint32_t* ss = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes + stage * kScaleBytes);
+        ss[tid] = ras_reg;
+        ss[256 + tid] = rbs_reg;
+      }
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < kT; ++kt) {
+      const int st = kt & 1;
+      if (kt + 1 < kT) gload(kt + 1);
+      const uint8_t* sA = smem + st * kStageBytes;
+      const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem + 2 * kStageBytes + st * kScaleBytes);
+      core.compute(sA, sA + kTileBytes, ss, ss + 256, wm, wn, lane);
+      if (kt + 1 < kT) lstore(st ^ 1);
+      __syncthreads();
+    }
+
+    // ---- epilogue
+    const int r32 = lane & 31, g4 = (lane >> 5) * 4;
+    if (kFc1) {
+      const int64_t I = N;
+      const int64_t n0h = (int64_t)nt * 128;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int64_t col = n0h + wn * 64 + jj * 32 + r32;
+          const bool cvalid = col < I;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = wm * 128 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
+            const bool valid = (m < mrows) && cvalid;
+            const int64_t grow = row0 + m;
+            const float gv = core.acc[i][jj][r], uv = core.acc[i][jj + 2][r];
+            const float pr = (m < mrows) ? p.prob_perm[grow] : 0.f;
+            const float h = silu_f(gv) * uv * pr;
+            if (p.save_gu && valid) {
+              p.save_gu[grow * 2 * I + col] = f32_to_bf16(gv);
+              p.save_gu[grow * 2 * I + I + col] = f32_to_bf16(uv);
+            }
+            if (!kMx) {
+              if (valid) reinterpret_cast<uint16_t*>(p.out)[grow * I + col] = f32_to_bf16(h);
+            } else {
+              if (p.save_h && valid) p.save_h[grow * I + col] = f32_to_bf16(h);
+              float am = fabsf(h);
+              am = wave_xor_max(am, 1);
+              am = wave_xor_max(am, 2);
+              am = wave_xor_max(am, 4);
+              am = wave_xor_max(am, 8);
+              am = wave_xor_max(am, 16);
+              const int s = mx_shared_exp(am);
+              if (valid) {
+                p.out[grow * I + col] = (uint8_t)mx_e4m3_code(h, s);
+                if (r32 == 0) p.out_scales[grow * (I / 32) + col / 32] = (uint8_t)(s + 127);
+              }
+            }
+          }
+        }
+      }
+    } else {
+      const int64_t n0 = (int64_t)nt * kBN;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t col = n0 + wn * 128 + j * 32 + r32;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int m = wm * 128 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
+            if (m < mrows && col < N) {
+              const int64_t o = (int64_t)(row0 + m) * N + col;
+              if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = core.acc[i][j][r];
+              else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(core.acc[i][j][r]);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
+  FwdKArgs k{};
+  k.a = reinterpret_cast<const uint8_t*>(g.a);
+  k.a_scales = g.a_scales;
+  k.wq = g.wq;
+  k.ws = g.ws;
+  k.wq_stride = g.wq_stride;
+  k.ws_stride = g.ws_stride;
+  k.K = g.K;
+  k.N = g.N;
+  k.E = g.E;
+  k.nN = (int)(fc1 ? (g.N + 127) / 128 : (g.N + kBN - 1) / kBN);
+  k.split_sizes = g.split_sizes;
+  k.prob_perm = g.prob_perm;
+  k.out = reinterpret_cast<uint8_t*>(g.out);
+  k.out_scales = g.out_scales;
+  k.save_gu = g.save_gu;
+  k.save_h = g.save_h;
+  k.out_f32 = g.out_f32 ? 1 : 0;
+  if (!mx)
+    for (int e = 0; e < g.E; ++e) k.w[e] = reinterpret_cast<const uint8_t*>(g.w_tab[e]);
+  return k;
+}
+
+}  // namespace
+
+hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
+  FwdKArgs k = make_fwd_args(g, mx, true);
+  if (mx) fwd_gemm_kernel<true, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else fwd_gemm_kernel<false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  return hipGetLastError();
+}
+
+hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
+  FwdKArgs k = make_fwd_args(g, mx, false);
+  if (mx) fwd_gemm_kernel<true, false><<<kGemmGrid, 256, 0, st>>>(k);
+  else fwd_gemm_kernel<false, false><<<kGemmGrid, 256, 0, st>>>(k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

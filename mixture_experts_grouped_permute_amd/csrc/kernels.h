@@ -1,0 +1,63 @@
+// Kernel launchers shared between the C-ABI layer and the .hip sources.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kPermChunk = 2048;   // (token, slot) ids per histogram / scatter block
+constexpr int kMaxTopK = 16;
+constexpr int kGemmGrid = 256;     // persistent GEMM workgroups: one per CU, a multiple of the 8 XCDs
+
+// ---- permutation (permute.hip)
+hipError_t launch_permute_indices(const int32_t* idx, const float* prob, int64_t R, int E, int32_t* split_sizes,
+                                  int32_t* offsets, int32_t* row_id_map, int32_t* src_index, float* prob_perm,
+                                  int32_t* err_flag, int32_t* block_counts, int32_t* block_base, hipStream_t st);
+hipError_t launch_permute_rows(const void* x, bool x_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
+                               void* out, uint8_t* out_scales, bool mx, hipStream_t st);
+
+// ---- quantization (quant.hip)
+hipError_t launch_mx_quant_rows(const void* x, bool x_f32, int64_t rows, int64_t cols, uint8_t* q,
+                                uint8_t* scales, hipStream_t st);
+// Row-wise MXFP8 of E bf16 weight matrices [rows, cols] given by a host pointer table; experts with
+// skip_if_empty != nullptr && skip_if_empty[e] == 0 are skipped (their codes are never read).
+hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
+                                   uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st);
+// Column-wise (blocks along rows, restarted per segment, transposed output); see mxfp8_quantize axis 1.
+hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t cols,
+                                const int32_t* group_offsets, int num_groups, int64_t rows_pad, uint8_t* q,
+                                uint8_t* scales, hipStream_t st);
+
+// ---- combine / gather (combine.hip)
+hipError_t launch_combine(const void* z, bool z_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
+                          void* out, bool out_f32, hipStream_t st);
+hipError_t launch_gather_rows(const void* x, bool f32, int64_t R, int64_t H, int k, const int32_t* src_index,
+                              const int32_t* offsets, int E, void* out, hipStream_t st);
+hipError_t launch_dprob_reduce(const float* partial, int64_t R, int parts, const int32_t* row_id_map,
+                               int64_t T, int k, float* dprob, hipStream_t st);
+
+// ---- grouped GEMMs (gemm.hip)
+struct FwdGemm {
+  // A operand: permuted rows [R, K] (bf16, or E4M3 codes + [R, K/32] scales)
+  const void* a;
+  const uint8_t* a_scales;
+  // B operand per expert: bf16 table (w_tab) or contiguous MXFP8 codes/scales with strides
+  const void* const* w_tab;          // host table of E device pointers (bf16 path)
+  const uint8_t* wq;                 // MXFP8 codes base, expert e at wq + e * wq_stride
+  int64_t wq_stride;
+  const uint8_t* ws;                 // MXFP8 scales base
+  int64_t ws_stride;
+  int64_t K, N;                      // FC1: K = H, N = I (h columns); FC2: K = I, N = H
+  int E;
+  const int32_t* split_sizes;
+  const float* prob_perm;            // FC1
+  void* out;                         // FC1: h (bf16 or E4M3 codes) [R, I]; FC2: z [R, H]
+  uint8_t* out_scales;               // FC1 MXFP8: [R, I/32]
+  uint16_t* save_gu;                 // FC1 training: [R, 2I] bf16
+  uint16_t* save_h;                  // FC1 MXFP8 training: [R, I] bf16 h
+  bool out_f32;                      // FC2
+};
+hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st);
+hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,222 @@
+// Token permutation by expert: histogram -> prefix sum -> stable scatter ->
+// row copy (bf16 cast or MXFP8 row quantization), for gfx950.
+//
+// The grouped linear of page "BioNeMo Uses Grouped Kernels and MXFP8"
+// (Grouping fragmented expert workloads) consumes each expert's tokens as one
+// contiguous group described by split_sizes; this file builds that grouping.
+// Rows inside a group are in ascending (token, slot) order, so every output
+// index is unique and the permutation is deterministic.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// K1: per-block expert histogram over kPermChunk consecutive (token, slot) ids.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ idx, int64_t R, int E,
+                                                          int32_t* __restrict__ block_counts,
+                                                          int32_t* __restrict__ block_bad) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int nbad;
+  if (threadIdx.x == 0) nbad = 0;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  __syncthreads();
+  int64_t base = (int64_t)blockIdx.x * kPermChunk;
+  int bad = 0;
+  for (int i = threadIdx.x; i < kPermChunk; i += blockDim.x) {
+    int64_t p = base + i;
+    if (p < R) {
+      int e = idx[p];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+      else bad = 1;
+    }
+  }
+  if (bad) atomicOr(&nbad, 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) block_counts[(int64_t)blockIdx.x * E + e] = cnt[e];
+  if (threadIdx.x == 0) block_bad[blockIdx.x] = nbad;
+}
+
+// ---------------------------------------------------------------------------
+// K2: split_sizes, offsets and the per-(block, expert) base rows.  One block.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restrict__ block_counts,
+                                                          const int32_t* __restrict__ block_bad, int nb, int E,
+                                                          int32_t* __restrict__ err_flag,
+                                                          int32_t* __restrict__ split_sizes,
+                                                          int32_t* __restrict__ offsets,
+                                                          int32_t* __restrict__ block_base) {
+  __shared__ int tot[kMaxExperts];
+  __shared__ int off[kMaxExperts + 1];
+  int e = threadIdx.x;
+  if (e < E) {
+    int s = 0;
+    for (int b = 0; b < nb; ++b) s += block_counts[(int64_t)b * E + e];
+    tot[e] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int i = 0; i < E; ++i) { off[i] = run; run += tot[i]; }
+    off[E] = run;
+  }
+  __syncthreads();
+  if (e < E) {
+    split_sizes[e] = tot[e];
+    offsets[e] = off[e];
+    int run = off[e];
+    for (int b = 0; b < nb; ++b) {
+      block_base[(int64_t)b * E + e] = run;
+      run += block_counts[(int64_t)b * E + e];
+    }
+  }
+  if (threadIdx.x == 0) {
+    offsets[E] = off[E];
+    int bad = 0;
+    for (int b = 0; b < nb; ++b) bad |= block_bad[b];
+    err_flag[0] = bad;   // the flag describes this call only
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K3: stable scatter of the indices.  Block b walks its chunk in rounds of 256
+// ids; inside a round a (token, slot) id's rank among equal experts is the
+// number of equal ids in lower lanes of its wave (ballot match on the 8 bits of
+// the expert id) plus the counts of earlier waves, on top of the running count.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ idx,
+                                                             const float* __restrict__ prob, int64_t R, int E,
+                                                             const int32_t* __restrict__ block_base,
+                                                             int32_t* __restrict__ row_id_map,
+                                                             int32_t* __restrict__ src_index,
+                                                             float* __restrict__ prob_perm) {
+  __shared__ int run[kMaxExperts];
+  __shared__ int wcnt[4][kMaxExperts];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  for (int e = tid; e < E; e += 256) run[e] = block_base[(int64_t)blockIdx.x * E + e];
+  int64_t base = (int64_t)blockIdx.x * kPermChunk;
+  for (int r = 0; r < kPermChunk / 256; ++r) {
+    for (int i = tid; i < 4 * kMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    int64_t p = base + r * 256 + tid;
+    int e = -1;
+    if (p < R) {
+      e = idx[p];
+      if ((unsigned)e >= (unsigned)E) e = -1;
+    }
+    uint64_t peers = __ballot(e >= 0);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      uint64_t b = __ballot(e >= 0 && ((e >> bit) & 1));
+      peers &= ((e >> bit) & 1) ? b : ~b;
+    }
+    int rank = __popcll(peers & lanemask_lt());
+    if (e >= 0 && rank == 0) wcnt[wave][e] = __popcll(peers);
+    __syncthreads();
+    if (e >= 0) {
+      int row = run[e] + rank;
+      for (int w = 0; w < wave; ++w) row += wcnt[w][e];
+      row_id_map[p] = row;
+      src_index[row] = (int32_t)p;
+      if (prob_perm) prob_perm[row] = prob[p];
+    } else if (p < R) {
+      row_id_map[p] = -1;
+    }
+    __syncthreads();
+    for (int x = tid; x < E; x += 256) run[x] += wcnt[0][x] + wcnt[1][x] + wcnt[2][x] + wcnt[3][x];
+    // the next round's clear of wcnt happens after this barrier
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K4: copy each token row once from X and write it to its k permuted rows,
+// rounding to bf16 or quantizing to MXFP8 on the way.  One wave per token;
+// a lane owns 8 consecutive values per step (4 lanes per MXFP8 block).
+// ---------------------------------------------------------------------------
+template <bool kInF32, bool kMx>
+__global__ __launch_bounds__(256) void perm_rows_kernel(const void* __restrict__ x, int64_t T, int64_t H, int k,
+                                                          const int32_t* __restrict__ row_id_map,
+                                                          void* __restrict__ out, uint8_t* __restrict__ out_scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int rows[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) rows[j] = j < k ? row_id_map[t * k + j] : -1;
+  for (int64_t c0 = 0; c0 < H; c0 += 512) {
+    int64_t c = c0 + lane * 8;
+    if (c >= H) break;   // H % 32 == 0 keeps every MXFP8 block's 4 lanes together
+    float v[8];
+    if (kInF32) {
+      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * H + c);
+      float4 a = src[0], b = src[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+      u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + t * H + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
+        v[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+      }
+    }
+    if (!kMx) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j >= k || rows[j] < 0) continue;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)rows[j] * H + c) = o;
+      }
+    } else {
+      float am = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+      am = wave_xor_max(am, 1);
+      am = wave_xor_max(am, 2);
+      int s = mx_shared_exp(am);
+      u32x2 o;
+      o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
+      o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j) {
+        if (j >= k || rows[j] < 0) continue;
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(out) + (int64_t)rows[j] * H + c) = o;
+        if ((lane & 3) == 0) out_scales[(int64_t)rows[j] * (H / 32) + c / 32] = (uint8_t)(s + 127);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_permute_indices(const int32_t* idx, const float* prob, int64_t R, int E, int32_t* split_sizes,
+                                  int32_t* offsets, int32_t* row_id_map, int32_t* src_index, float* prob_perm,
+                                  int32_t* err_flag, int32_t* block_counts, int32_t* block_base,
+                                  hipStream_t st) {
+  int nb = (int)((R + kPermChunk - 1) / kPermChunk);
+  if (nb < 1) nb = 1;
+  int32_t* block_bad = block_counts + (int64_t)nb * E;
+  perm_hist_kernel<<<nb, 256, 0, st>>>(idx, R, E, block_counts, block_bad);
+  perm_scan_kernel<<<1, 256, 0, st>>>(block_counts, block_bad, nb, E, err_flag, split_sizes, offsets, block_base);
+  perm_scatter_kernel<<<nb, 256, 0, st>>>(idx, prob, R, E, block_base, row_id_map, src_index, prob_perm);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_rows(const void* x, bool x_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
+                               void* out, uint8_t* out_scales, bool mx, hipStream_t st) {
+  dim3 grid((unsigned)((T + 3) / 4));
+  if (x_f32) {
+    if (mx) perm_rows_kernel<true, true><<<grid, 256, 0, st>>>(x, T, H, k, row_id_map, out, out_scales);
+    else perm_rows_kernel<true, false><<<grid, 256, 0, st>>>(x, T, H, k, row_id_map, out, out_scales);
+  } else {
+    if (mx) perm_rows_kernel<false, true><<<grid, 256, 0, st>>>(x, T, H, k, row_id_map, out, out_scales);
+    else perm_rows_kernel<false, false><<<grid, 256, 0, st>>>(x, T, H, k, row_id_map, out, out_scales);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

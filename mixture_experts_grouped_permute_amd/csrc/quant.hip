@@ -1,0 +1,211 @@
+// MXFP8 block quantization kernels for gfx950 (the Quantize step of Figure 4
+// on page "BioNeMo Uses Grouped Kernels and MXFP8"; format from Reducing
+// memory pressure with MXFP8, Figure 3: E4M3 values plus one E8M0 scale per
+// 32 consecutive values).  The element and scale rule (mx_shared_exp,
+// mx_e4m3_code in common.h) is integer arithmetic, so the bytes are exact.
+//
+// Row-wise kernels stream 16-byte loads: a lane owns 8 consecutive values, 4
+// lanes share one 32-value block and reduce its amax with two xor shuffles.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void load8(const void* x, bool f32, int64_t off, float v[8]) {
+  if (f32) {
+    const float4* s = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + off);
+    float4 a = s[0], b = s[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
+      v[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    }
+  }
+}
+
+// 8-value group g of a [rows, cols] matrix: row = g / (cols/8), col = 8 * (g % (cols/8)).
+// Every lane handles groups tid, tid + stride, ...  cols % 32 == 0, so the 4 lanes of
+// one 32-value block are always consecutive lanes of one wave and step together.
+template <bool kF32>
+__global__ __launch_bounds__(256) void mx_rows_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                        uint8_t* __restrict__ q, uint8_t* __restrict__ scales) {
+  const int64_t groups = rows * (cols / 8);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  // the loop bound is uniform per 4-lane block because groups % 4 == 0
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
+    const int64_t off = gi * 8;
+    float v[8];
+    load8(x, kF32, off, v);
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = wave_xor_max(am, 1);
+    am = wave_xor_max(am, 2);
+    const int s = mx_shared_exp(am);
+    u32x2 o;
+    o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
+    o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
+    *reinterpret_cast<u32x2*>(q + off) = o;
+    if ((threadIdx.x & 3) == 0) scales[off / 32] = (uint8_t)(s + 127);
+  }
+}
+
+// Weight tables: blockIdx.y = expert.  Skips experts with no tokens when asked.
+struct WTab {
+  const uint16_t* w[kMaxExperts];
+};
+
+__global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t rows, int64_t cols,
+                                                           uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+                                                           const int32_t* __restrict__ skip_if_empty) {
+  const int e = blockIdx.y;
+  if (skip_if_empty && skip_if_empty[e] == 0) return;
+  const uint16_t* x;
+#if defined(__HIP_DEVICE_COMPILE__)
+  {
+    const uint16_t* const* t = reinterpret_cast<const uint16_t* const*>(
+        reinterpret_cast<const char*>(__builtin_amdgcn_kernarg_segment_ptr()));
+    x = t[e];
+  }
+#else
+  x = tab.w[e];
+#endif
+  const int64_t n = rows * cols;
+  uint8_t* qe = q + (int64_t)e * n;
+  uint8_t* se = scales + (int64_t)e * (n / 32);
+  const int64_t groups = n / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
+    const int64_t off = gi * 8;
+    float v[8];
+    load8(x, false, off, v);
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = wave_xor_max(am, 1);
+    am = wave_xor_max(am, 2);
+    const int s = mx_shared_exp(am);
+    u32x2 o;
+    o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
+    o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
+    *reinterpret_cast<u32x2*>(qe + off) = o;
+    if ((threadIdx.x & 3) == 0) se[off / 32] = (uint8_t)(s + 127);
+  }
+}
+
+// Column-wise quantization with per-segment restart, transposed output.
+// A workgroup handles a 32-row block of one segment and 64 columns: it loads
+// the 32 x 64 tile (zero beyond the segment), one lane per column reduces the
+// block's amax down its column, and writes the column's 32 codes contiguously.
+template <bool kF32>
+__global__ __launch_bounds__(64) void mx_cols_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                       const int32_t* __restrict__ goff, int num_groups,
+                                                       int64_t rows_pad, uint8_t* __restrict__ q,
+                                                       uint8_t* __restrict__ scales) {
+  // blockIdx.x: global 32-row block index over the padded token axis; blockIdx.y: 64-column slab
+  __shared__ int s_pad[kMaxExperts + 1];
+  __shared__ int s_off[kMaxExperts + 1];
+  const int lane = threadIdx.x;
+  // padded segment starts: one wave scans the groups 64 at a time
+  int carry = 0;
+  for (int g0 = 0; g0 < num_groups; g0 += 64) {
+    const int g = g0 + lane;
+    int pad = 0;
+    if (g < num_groups) {
+      const int o = goff[g];
+      s_off[g] = o;
+      pad = (goff[g + 1] - o + 31) / 32 * 32;
+    }
+    int inc = pad;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      int t = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += t;
+    }
+    if (g < num_groups) s_pad[g] = carry + inc - pad;
+    carry += __shfl(inc, 63, 64);
+  }
+  if (lane == 0) {
+    s_off[num_groups] = goff[num_groups];
+    s_pad[num_groups] = carry;
+  }
+  __syncthreads();
+  const int64_t pblk = (int64_t)blockIdx.x * 32;       // padded row of this block
+  if (pblk >= s_pad[num_groups]) return;
+  int g = 0;
+  while (g + 1 < num_groups && s_pad[g + 1] <= pblk) ++g;
+  const int64_t src0 = s_off[g] + (pblk - s_pad[g]);   // first source row
+  const int64_t src_end = s_off[g + 1];
+  const int64_t c = (int64_t)blockIdx.y * 64 + lane;
+  if (c >= cols) return;
+  float v[32];
+  float am = 0.f;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const int64_t sr = src0 + r;
+    float val = 0.f;
+    if (sr < src_end) {
+      if (kF32) val = reinterpret_cast<const float*>(x)[sr * cols + c];
+      else val = bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[sr * cols + c]);
+    }
+    v[r] = val;
+    am = fmaxf(am, fabsf(val));
+  }
+  const int s = mx_shared_exp(am);
+  u32x4 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o0[i] = mx_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], s);
+    o1[i] = mx_pack4(v[16 + 4 * i], v[16 + 4 * i + 1], v[16 + 4 * i + 2], v[16 + 4 * i + 3], s);
+  }
+  uint8_t* dst = q + c * rows_pad + pblk;
+  *reinterpret_cast<u32x4*>(dst) = o0;
+  *reinterpret_cast<u32x4*>(dst + 16) = o1;
+  scales[c * (rows_pad / 32) + pblk / 32] = (uint8_t)(s + 127);
+}
+
+int grid_for(int64_t groups) {
+  int64_t b = (groups + 255) / 256;
+  return (int)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
+}
+
+}  // namespace
+
+hipError_t launch_mx_quant_rows(const void* x, bool x_f32, int64_t rows, int64_t cols, uint8_t* q,
+                                uint8_t* scales, hipStream_t st) {
+  const int64_t groups = rows * (cols / 8);
+  if (groups == 0) return hipSuccess;
+  if (x_f32) mx_rows_kernel<true><<<grid_for(groups), 256, 0, st>>>(x, rows, cols, q, scales);
+  else mx_rows_kernel<false><<<grid_for(groups), 256, 0, st>>>(x, rows, cols, q, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
+                                   uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st) {
+  WTab tab{};
+  for (int e = 0; e < E; ++e) tab.w[e] = reinterpret_cast<const uint16_t*>(w[e]);
+  const int64_t groups = rows * cols / 8;
+  int gx = grid_for(groups);
+  int per = (2048 + E - 1) / E;                 // about 2048 workgroups over all experts
+  if (gx > per) gx = per < 1 ? 1 : per;
+  mx_weights_kernel<<<dim3(gx, E), 256, 0, st>>>(tab, rows, cols, q, scales, skip_if_empty);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* group_offsets,
+                                int num_groups, int64_t rows_pad, uint8_t* q, uint8_t* scales, hipStream_t st) {
+  dim3 grid((unsigned)(rows_pad / 32), (unsigned)((cols + 63) / 64));
+  if (grid.x == 0) return hipSuccess;
+  if (x_f32)
+    mx_cols_kernel<true><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales);
+  else
+    mx_cols_kernel<false><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales);
+  return hipGetLastError();
+}
+
+}  // namespace moe

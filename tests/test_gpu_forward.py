@@ -1,0 +1,87 @@
+"""GPU parity: grouped MLP forward against the fp64 oracle (normwise relative error).
+
+BF16: 5e-3; MXFP8: 2e-2 (the tolerances fixed for this layer).  The cases span
+several 256-row tiles with ragged tails, zero-token experts in the first, middle
+and last positions, the edge sizes 1, 31, 33, 255, 257, one expert, every token
+on one expert, and the fine-grained 64-expert top-8 shape.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import BF16_TOL, MXFP8_TOL, cfg_small, gpu, log, need_gpu, to_np
+from moe_inputs import get_config, make_inputs
+from moe_inputs.generate import routing_with_counts
+from oracle import mlp
+
+CASES = [
+    # name, cfg, counts (None = the cfg's own routing)
+    ("cfg1-tiny-f32io", get_config(1), None),
+    ("ragged-bf16", cfg_small(T=700, H=256, I=384, E=4, k=2), None),
+    ("zeros-first-middle-last", cfg_small(T=400, H=128, I=256, E=8, k=2), [0, 400, 1, 31, 0, 33, 335, 0]),
+    ("edge-sizes", cfg_small(T=600, H=128, I=128, E=7, k=2), [255, 257, 1, 31, 33, 600, 23]),
+    ("one-expert", cfg_small(T=300, H=128, I=128, E=1, k=1), None),
+    ("all-to-one", cfg_small(T=520, H=128, I=256, E=4, k=1), [0, 0, 520, 0]),
+    ("finegrained-e64-k8", get_config(5).with_(T=512, H=256, I=256, precision="bf16"), None),
+    ("zipf-zero-expert", get_config(3).with_(T=1024, H=256, I=384, precision="bf16"), None),
+]
+
+
+def _inputs(cfg, counts):
+    if counts is None:
+        return make_inputs(cfg)
+    idx, pr = routing_with_counts(counts, cfg.T, cfg.k, 5)
+    return make_inputs(cfg, topk_idx=idx, topk_prob=pr)
+
+
+def _run(m, inp, compute):
+    d = inp.to("cuda")
+    out, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, compute)
+    torch.cuda.synchronize()
+    return out, ctx
+
+
+@gpu
+@pytest.mark.parametrize("name,cfg,counts", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("compute", ["bf16", "mxfp8"])
+def test_forward_matches_oracle(name, cfg, counts, compute):
+    m = need_gpu()
+    if compute == "mxfp8" and (cfg.H % 128 or cfg.I % 128):
+        pytest.skip("MXFP8 path needs H, I multiples of 128")
+    log(f"fwd {name} {compute} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
+    inp = _inputs(cfg, counts)
+    out, ctx = _run(m, inp, compute)
+    ref = mlp.forward(inp.x, inp.topk_idx.numpy(), inp.topk_prob, inp.w1, inp.w2, compute, cfg.x_dtype)
+    got = to_np(out)
+    assert np.all(np.isfinite(got))
+    err = mlp.normwise_rel_err(got, ref.out)
+    tol = BF16_TOL if compute == "bf16" else MXFP8_TOL
+    log(f"  normwise err {err:.3e} (tol {tol})")
+    assert err < tol
+    np.testing.assert_array_equal(ctx["perm"]["split_sizes"].cpu().numpy(), ref.perm.split_sizes)
+
+
+@gpu
+def test_forward_deterministic():
+    m = need_gpu()
+    log("fwd determinism")
+    cfg = cfg_small(T=700, H=256, I=384, E=4, k=2)
+    inp = make_inputs(cfg)
+    for compute in ("bf16", "mxfp8"):
+        if compute == "mxfp8":
+            cfg2 = cfg.with_(I=256)
+            inp = make_inputs(cfg2)
+        a, _ = _run(m, inp, compute)
+        b, _ = _run(m, inp, compute)
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@gpu
+def test_forward_rejects_bad_shapes():
+    m = need_gpu()
+    log("fwd error paths")
+    cfg = cfg_small(T=64, H=96, I=128, E=2, k=1)   # H % 64 != 0
+    inp = make_inputs(cfg).to("cuda")
+    with pytest.raises(m.MoeError) as ei:
+        m.moe_grouped_mlp_fwd(inp.x, inp.topk_idx, inp.topk_prob, inp.w1, inp.w2, "bf16")
+    assert ei.value.status == 2
