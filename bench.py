@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the grouped expert MLP forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-mxfp8] [--no-cpu-baseline]
+
+A step is one moe_grouped_mlp_fwd call over the Mixtral-8x7B-shaped layer
+(T=4096 tokens, H=4096, I=14336, 8 experts, top-2, bf16 with fp32
+accumulation): permutation, FC1 grouped GEMM with ScaledSwiGLU*prob, FC2
+grouped GEMM and combine.  Inputs are synthetic (seeded), resident in HBM
+before the timed region.  The same line also carries the MXFP8 layer
+(T=8192, Zipf(1.2) routing with one empty expert, weights quantized per call)
+and the fp64 CPU oracle timed on a bounded sample on the host cores.
+
+Prints one JSON line.
+"""
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE grouped-MLP fwd tokens/s + TFLOP/s (bf16, MXFP8), Mixtral 8x7B layer"
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}      # MI355X dense MFMA peaks
+PEAK_HBM_GBS = 8000.0
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _hip():
+    lib = ctypes.CDLL("libamdhip64.so.7")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+def _src_hash(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mixture_experts_grouped_permute_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source changed after the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel_key)
+    if not ent or ent.get("src_hash") != _src_hash(ent.get("sources", ["gemm.hip"])):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def run_gpu(cfg, steps, warmup):
+    import torch
+    import mixture_experts_grouped_permute_amd as m
+    from mixture_experts_grouped_permute_amd import _lib as L
+    from moe_inputs import make_inputs
+
+    lib = m.load()
+    hip = _hip()
+    _log(f"generating inputs for {cfg.name}")
+    inp = make_inputs(cfg)
+    d = inp.to("cuda:0")
+    _log("inputs resident on the GPU; warming up")
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    R = T * k
+    dev = d.x.device
+    perm = {
+        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
+        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
+        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
+    }
+    out = torch.empty((T, H), dtype=d.x.dtype, device=dev)
+    a, keep, _, _ = L._fwd_args(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision, out, perm, None)
+    need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    if need == 0:
+        raise RuntimeError("argument validation failed")
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    nph = lib.moe_fwd_phase_count()
+    names = [lib.moe_fwd_phase_name(i).decode() for i in range(nph)]
+    ev = []
+    for _ in range(steps * (nph + 1)):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        ev.append(e.value)
+    ev_arrays = [(ctypes.c_void_p * (nph + 1))(*ev[s * (nph + 1):(s + 1) * (nph + 1)]) for s in range(steps)]
+    for _ in range(warmup):
+        L._check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), stream), "fwd")
+    torch.cuda.synchronize()
+    _log(f"timing {steps} steps")
+    t0 = time.perf_counter()
+    for s in range(steps):
+        L._check(lib.moe_grouped_mlp_fwd_ex(ctypes.byref(a), stream, ev_arrays[s]), "fwd")
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ph = [[0.0] * nph for _ in range(steps)]
+    f = ctypes.c_float()
+    for s in range(steps):
+        for i in range(nph):
+            hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(ev_arrays[s][i]), ctypes.c_void_p(ev_arrays[s][i + 1]))
+            ph[s][i] = f.value
+    for e in ev:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    phase_ms = {names[i]: sum(ph[s][i] for s in range(steps)) / steps for i in range(nph)}
+    ms = (t1 - t0) * 1e3 / steps
+    split = perm["split_sizes"].cpu().tolist()
+    del keep
+    return {"ms_per_step": ms, "phase_ms": phase_ms, "split_sizes": split, "inputs": inp}
+
+
+def fc1_roofline(cfg, phase_ms):
+    flops = 4.0 * cfg.R * cfg.H * cfg.I          # gate-up GEMM: 2 * R * H * (2I)
+    t = phase_ms["fc1_gateup_swiglu"] * 1e-3
+    ach = flops / t / 1e12
+    peak = PEAK_TFLOPS[cfg.precision]
+    key = f"fc1_{cfg.precision}_{cfg.name}"
+    return {"kernel": "fwd_gemm_kernel (FC1 gate-up + ScaledSwiGLU*prob)", "bound": "mfma",
+            "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+            "traffic": _traffic(key), "flops_per_launch": flops}
+
+
+def cpu_baseline(inp, cfg, tokens):
+    """The fp64 oracle on the first `tokens` tokens of the workload (its full expert weights)."""
+    import numpy as np
+    from oracle import mlp
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    xs = inp.x[:tokens]
+    idx = inp.topk_idx[:tokens].numpy()
+    pr = inp.topk_prob[:tokens]
+    t0 = time.perf_counter()
+    mlp.forward(xs, idx, pr, inp.w1, inp.w2, cfg.precision, cfg.x_dtype)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {tokens} of {cfg.T} tokens of the same workload, all {cfg.E} experts' full weights "
+                      f"(fp64 numpy per-expert loop), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-mxfp8", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this layer runs unsharded on a single MI355X); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+    from moe_inputs import get_config
+
+    cfg = get_config(2)
+    r = run_gpu(cfg, args.steps, args.warmup)
+    ms = r["ms_per_step"]
+    tok_s = cfg.T / (ms * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} top-{cfg.k}, "
+                               f"bf16 operands, fp32 accumulation, N(0,1) router logits",
+                   "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.k, "parallelism": "none (1 GPU)"},
+        "tflops": round(cfg.fwd_flops() / (ms * 1e-3) / 1e12, 1),
+        "roofline": fc1_roofline(cfg, r["phase_ms"]),
+        "phase_ms": {k_: round(v, 4) for k_, v in r["phase_ms"].items()},
+        "split_sizes": r["split_sizes"],
+    }
+    if not args.no_cpu_baseline:
+        _log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
+        line["cpu_baseline"] = cpu_baseline(r["inputs"], cfg, args.cpu_tokens)
+    del r
+    if not args.no_mxfp8:
+        import torch
+        torch.cuda.empty_cache()
+        c3 = get_config(3)
+        r3 = run_gpu(c3, max(2, args.steps // 2), max(1, args.warmup // 2))
+        ms3 = r3["ms_per_step"]
+        line["mxfp8"] = {
+            "workload": f"{c3.name}: T={c3.T} H={c3.H} I={c3.I} E={c3.E} top-{c3.k}, MXFP8 both GEMMs, "
+                        f"Zipf(1.2) routing, expert {c3.zero_expert} empty, weights quantized per call",
+            "value": round(c3.T / (ms3 * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms3, 4),
+            "tflops": round(c3.fwd_flops() / (ms3 * 1e-3) / 1e12, 1),
+            "roofline": fc1_roofline(c3, r3["phase_ms"]),
+            "phase_ms": {k_: round(v, 4) for k_, v in r3["phase_ms"].items()},
+            "split_sizes": r3["split_sizes"],
+        }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -170,6 +170,16 @@ typedef struct {
 size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a);
 moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream);
 
+/* Same as moe_grouped_mlp_fwd, and additionally records events[i] (caller-
+ * created hipEvent_t handles, moe_fwd_phase_count() + 1 of them) on `stream`
+ * before phase i and after the last phase, without synchronizing, so a caller
+ * can time each phase with hipEventElapsedTime.  Phases that do not apply to
+ * the chosen precision are empty (their two events are adjacent).
+ * events == NULL behaves exactly like moe_grouped_mlp_fwd. */
+moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void* const* events);
+int moe_fwd_phase_count(void);
+const char* moe_fwd_phase_name(int i);   /* NULL when out of range */
+
 /* ------------------------------------------------------------------------
  * moe_grouped_mlp_bwd -- gradients of sum(out * dy):
  *   dz[r]     = dy[token of r]

@@ -25,7 +25,8 @@ MAX_EXPERTS = 256
 EXPORTS = (
     "moe_abi_version", "moe_status_string", "mxfp8_quantize", "moe_permute_workspace_size", "moe_permute",
     "moe_grouped_mlp_fwd_workspace", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd_workspace",
-    "moe_grouped_mlp_bwd", "moe_read_device_error",
+    "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
+    "moe_fwd_phase_name",
 )
 
 
@@ -97,6 +98,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_grouped_mlp_bwd_workspace.argtypes = [ctypes.POINTER(BwdArgs)]
     lib.moe_grouped_mlp_bwd.restype = ctypes.c_int
     lib.moe_grouped_mlp_bwd.argtypes = [ctypes.POINTER(BwdArgs), _vp]
+    lib.moe_grouped_mlp_fwd_ex.restype = ctypes.c_int
+    lib.moe_grouped_mlp_fwd_ex.argtypes = [ctypes.POINTER(FwdArgs), _vp, ctypes.POINTER(_vp)]
+    lib.moe_fwd_phase_count.restype = ctypes.c_int
+    lib.moe_fwd_phase_name.restype = ctypes.c_char_p
+    lib.moe_fwd_phase_name.argtypes = [ctypes.c_int]
     lib.moe_read_device_error.restype = ctypes.c_int
     lib.moe_read_device_error.argtypes = [_vp, _vp]
     if path is None:

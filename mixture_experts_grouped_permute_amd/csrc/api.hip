@@ -207,7 +207,18 @@ size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a) {
   return plan_fwd(a, nullptr).bytes;
 }
 
+static const char* const kFwdPhases[] = {"permute_index", "permute_rows", "quant_w1", "quant_w2",
+                                         "fc1_gateup_swiglu", "fc2_down", "combine"};
+constexpr int kNumFwdPhases = 7;
+
+int moe_fwd_phase_count(void) { return kNumFwdPhases; }
+const char* moe_fwd_phase_name(int i) { return (i >= 0 && i < kNumFwdPhases) ? kFwdPhases[i] : nullptr; }
+
 moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream) {
+  return moe_grouped_mlp_fwd_ex(a, stream, nullptr);
+}
+
+moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void* const* events) {
   moe_status s = validate_fwd(a);
   if (s != MOE_OK) return s;
   const size_t need = plan_fwd(a, nullptr).bytes;
@@ -218,19 +229,29 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream) {
   const int E = a->E, k = a->k;
   const bool mx = a->compute == MOE_MXFP8_E4M3;
   const bool x_f32 = a->io_dtype == MOE_F32;
+  auto mark = [&](int i) -> bool {
+    return !events || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) == hipSuccess;
+  };
 
+  MOE_CHECK(mark(0), MOE_ERR_HIP);
   HIP_TRY(launch_permute_indices(a->topk_idx, a->topk_prob, R, E, a->split_sizes, a->offsets, a->row_id_map,
                                  a->src_index, a->prob_perm, p.perm.err, p.perm.block_counts, p.perm.block_base,
                                  st));
+  MOE_CHECK(mark(1), MOE_ERR_HIP);
   if (mx) {
     HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, p.x_sc, true, st));
     if (a->saved_x_perm)
       HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, a->saved_x_perm, nullptr, false, st));
+    MOE_CHECK(mark(2), MOE_ERR_HIP);
     HIP_TRY(launch_mx_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.w1s, a->split_sizes, st));
+    MOE_CHECK(mark(3), MOE_ERR_HIP);
     HIP_TRY(launch_mx_quant_weights(a->w2, E, H, I, p.w2q, p.w2s, a->split_sizes, st));
   } else {
     HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, nullptr, false, st));
+    MOE_CHECK(mark(2), MOE_ERR_HIP);
+    MOE_CHECK(mark(3), MOE_ERR_HIP);
   }
+  MOE_CHECK(mark(4), MOE_ERR_HIP);
 
   FwdGemm g1{};
   g1.a = p.x_op;
@@ -250,6 +271,7 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream) {
   g1.save_gu = reinterpret_cast<uint16_t*>(a->saved_gu);
   g1.save_h = mx ? reinterpret_cast<uint16_t*>(a->saved_h) : nullptr;
   HIP_TRY(launch_fc1(g1, mx, st));
+  MOE_CHECK(mark(5), MOE_ERR_HIP);
 
   FwdGemm g2{};
   g2.a = p.h_op;
@@ -266,8 +288,10 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream) {
   g2.out = p.z;
   g2.out_f32 = x_f32;
   HIP_TRY(launch_fc2(g2, mx, st));
+  MOE_CHECK(mark(6), MOE_ERR_HIP);
 
   HIP_TRY(launch_combine(p.z, x_f32, T, H, k, a->row_id_map, a->out, x_f32, st));
+  MOE_CHECK(mark(7), MOE_ERR_HIP);
   return MOE_OK;
 }
 

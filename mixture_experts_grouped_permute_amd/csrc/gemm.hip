@@ -95,7 +95,22 @@ __device__ __forceinline__ int find_expert(const Sched& s, int E, int t) {
   return lo;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) { return g * __frcp_rn(1.0f + __expf(-g)); }
+
+// Same rotation for a 1024-byte-per-row tile (c16 in 0..63).
+__device__ __forceinline__ uint32_t epi_off_wide(int m, int c16) {
+  const int b = c16 >> 3, low = c16 & 7;
+  return (uint32_t)(m * 1024 + ((b << 3) + ((low + 2 * b + m) & 7)) * 16);
+}
+
+// Byte offset of 16-byte chunk c16 (0..31) of row m in a 512-byte-per-row LDS
+// staging tile.  Chunks are rotated within each group of 8 by (2 * group + m),
+// so both the column-wise writes from the MFMA layout and the row-wise reads
+// of whole groups touch 8 different bank groups per 8 lanes.
+__device__ __forceinline__ uint32_t epi_off(int m, int c16) {
+  const int b = c16 >> 3, low = c16 & 7;
+  return (uint32_t)(m * 512 + ((b << 3) + ((low + 2 * b + m) & 7)) * 16);
+}
 
 // ---------------------------------------------------------------------------
 // One K-pass of a 256x256 tile.  kFc1 selects the B row map (gate/up halves).
@@ -174,21 +189,32 @@ struct TileCore {
       }
   }
 
-  // All substeps of one LDS stage, fragments double-buffered in registers.
+  // All substeps of one LDS stage.  BF16 fragments are double-buffered in
+  // registers (2 x 32 VGPRs); the MXFP8 ones are twice as wide, so they are
+  // single-buffered and the compiler overlaps the reads with the MFMAs.
   __device__ __forceinline__ void compute(const uint8_t* sA, const uint8_t* sB, const uint32_t* sAs,
                                           const uint32_t* sBs, int wm, int wn, int lane) {
-    Frag f0, f1;
-    load_frag(f0, 0, sA, sB, sAs, sBs, wm, wn, lane);
+    if constexpr (kMx) {
 #pragma unroll
-    for (int kk = 0; kk < kSub; kk += 2) {
-      load_frag(f1, kk + 1, sA, sB, sAs, sBs, wm, wn, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk + 2 < kSub) load_frag(f0, kk + 2, sA, sB, sAs, sBs, wm, wn, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f1);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int kk = 0; kk < kSub; ++kk) {
+        Frag f;
+        load_frag(f, kk, sA, sB, sAs, sBs, wm, wn, lane);
+        mma(f);
+      }
+    } else {
+      Frag f0, f1;
+      load_frag(f0, 0, sA, sB, sAs, sBs, wm, wn, lane);
+#pragma unroll
+      for (int kk = 0; kk < kSub; kk += 2) {
+        load_frag(f1, kk + 1, sA, sB, sAs, sBs, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 2 < kSub) load_frag(f0, kk + 2, sA, sB, sAs, sBs, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(f1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   }
 };
@@ -225,7 +251,7 @@ __device__ __forceinline__ const uint8_t* kernarg_table(int e) {
 #endif
 }
 
-template <bool kMx, bool kFc1>
+template <bool kMx, bool kFc1, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * kScaleBytes : 16)];
@@ -234,7 +260,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int E = p.E;
   build_sched(sched, p.split_sizes, E, p.nN);
-  const int total = sched.tile[E];
+  const int total = __builtin_amdgcn_readfirstlane(sched.tile[E]);
   const int G = gridDim.x, per = G >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int64_t K = p.K, N = p.N;
   const int esz = kMx ? 1 : 2;
@@ -247,12 +273,14 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   for (int round = 0;; ++round) {
     const int t = round * G + xcd * per + slot;
     if (t >= total) break;
-    const int e = find_expert(sched, E, t);
-    const int Me = sched.cnt[e];
+    // the tile decode is uniform across the workgroup; readfirstlane makes it scalar so the
+    // buffer descriptors built from it live in SGPRs
+    const int e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, t));
+    const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
     const int nM = (Me + kBM - 1) / kBM;
-    const int local = t - sched.tile[e];
+    const int local = t - __builtin_amdgcn_readfirstlane(sched.tile[e]);
     const int mt = local % nM, nt = local / nM;
-    const int row0 = sched.off[e] + mt * kBM;           // first permuted row of the tile
+    const int row0 = __builtin_amdgcn_readfirstlane(sched.off[e]) + mt * kBM;   // first permuted row of the tile
     const int mrows = min(kBM, Me - mt * kBM);
     // ---- operand descriptors
     rsrc_t ra = make_rsrc(p.a + (int64_t)row0 * rowb, (uint32_t)mrows * rowb);
@@ -340,65 +368,147 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       __syncthreads();
     }
 
-    // ---- epilogue
-    const int r32 = lane & 31, g4 = (lane >> 5) * 4;
-    if (kFc1) {
+    // ---- epilogue, staged through LDS (the stage buffers are free after the last barrier).
+    // The lane id is laundered so the address arithmetic below is redone per tile instead of
+    // being hoisted above the main loop (where it would occupy ~100 VGPRs for the whole loop).
+    int elane = lane, etid = tid;
+    asm volatile("" : "+v"(elane), "+v"(etid));
+    const int r32 = elane & 31, g4 = (elane >> 5) * 4;
+    if constexpr (kFc1) {
       const int64_t I = N;
       const int64_t n0h = (int64_t)nt * 128;
+      // (A) silu(g) * u per element, fp32, into a rotated [256][128] LDS tile
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const int64_t col = n0h + wn * 64 + jj * 32 + r32;
-          const bool cvalid = col < I;
+          const int n = wn * 64 + jj * 32 + r32;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int m = wm * 128 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
-            const bool valid = (m < mrows) && cvalid;
-            const int64_t grow = row0 + m;
             const float gv = core.acc[i][jj][r], uv = core.acc[i][jj + 2][r];
-            const float pr = (m < mrows) ? p.prob_perm[grow] : 0.f;
-            const float h = silu_f(gv) * uv * pr;
-            if (p.save_gu && valid) {
-              p.save_gu[grow * 2 * I + col] = f32_to_bf16(gv);
-              p.save_gu[grow * 2 * I + I + col] = f32_to_bf16(uv);
+            if (p.save_gu && m < mrows && n0h + n < I) {
+              const int64_t grow = row0 + m;
+              p.save_gu[grow * 2 * I + n0h + n] = f32_to_bf16(gv);
+              p.save_gu[grow * 2 * I + I + n0h + n] = f32_to_bf16(uv);
             }
-            if (!kMx) {
-              if (valid) reinterpret_cast<uint16_t*>(p.out)[grow * I + col] = f32_to_bf16(h);
-            } else {
-              if (p.save_h && valid) p.save_h[grow * I + col] = f32_to_bf16(h);
-              float am = fabsf(h);
-              am = wave_xor_max(am, 1);
-              am = wave_xor_max(am, 2);
-              am = wave_xor_max(am, 4);
-              am = wave_xor_max(am, 8);
-              am = wave_xor_max(am, 16);
-              const int s = mx_shared_exp(am);
-              if (valid) {
-                p.out[grow * I + col] = (uint8_t)mx_e4m3_code(h, s);
-                if (r32 == 0) p.out_scales[grow * (I / 32) + col / 32] = (uint8_t)(s + 127);
-              }
+            // m & 7 and the chunk rotation depend only on (lane, r & 3); i and r >> 2 add constants
+            const int mb = wm * 128 + g4 + (r & 3);
+            const uint32_t off = epi_off(mb, n >> 2) + (n & 3) * 4 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);
+            *reinterpret_cast<float*>(smem + off) = silu_f(gv) * uv;
+          }
+          __builtin_amdgcn_sched_barrier(0);   // keep the accumulator reads of one fragment pair together
+        }
+      }
+      __syncthreads();
+      // (B) a thread owns whole 32-column blocks of a row: scale by prob, round or quantize
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int u = q * 256 + etid;
+        const int m = u >> 2, b = u & 3;
+        const int64_t col = n0h + b * 32;
+        if (m < mrows && col < I) {
+          const int64_t grow = row0 + m;
+          const float pr = p.prob_perm[grow];
+          float v[32];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(smem + epi_off(m, b * 8 + c));
+            v[4 * c] = w[0] * pr; v[4 * c + 1] = w[1] * pr; v[4 * c + 2] = w[2] * pr; v[4 * c + 3] = w[3] * pr;
+          }
+          if (!kMx || p.save_h) {
+            uint16_t* dst = kMx ? p.save_h : reinterpret_cast<uint16_t*>(p.out);
+            u32x4* d = reinterpret_cast<u32x4*>(dst + grow * I + col);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              d[c] = u32x4{pack_bf16x2(v[8 * c], v[8 * c + 1]), pack_bf16x2(v[8 * c + 2], v[8 * c + 3]),
+                           pack_bf16x2(v[8 * c + 4], v[8 * c + 5]), pack_bf16x2(v[8 * c + 6], v[8 * c + 7])};
+          }
+          if constexpr (kMx) {
+            float am = 0.f;
+#pragma unroll
+            for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(v[c]));
+            const int sx = mx_shared_exp(am);
+            u32x4 lo, hi;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              lo[c] = mx_pack4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3], sx);
+              hi[c] = mx_pack4(v[16 + 4 * c], v[16 + 4 * c + 1], v[16 + 4 * c + 2], v[16 + 4 * c + 3], sx);
             }
+            u32x4* d = reinterpret_cast<u32x4*>(p.out + grow * I + col);
+            d[0] = lo;
+            d[1] = hi;
+            p.out_scales[grow * (I / 32) + col / 32] = (uint8_t)(sx + 127);
           }
         }
       }
+      __syncthreads();
     } else {
       const int64_t n0 = (int64_t)nt * kBN;
+      if constexpr (kOutF32) {
+        // fp32 output: two passes of 128 rows (a [128][256] fp32 tile is 128 KB)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+        for (int half = 0; half < 2; ++half) {
+          if (wm == half) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t col = n0 + wn * 128 + j * 32 + r32;
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int m = wm * 128 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
+              for (int j = 0; j < 4; ++j) {
+                const int n = wn * 128 + j * 32 + r32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                  const int mb = g4 + (r & 3);
+                  const uint32_t off = epi_off_wide(mb, n >> 2) + (n & 3) * 4 + (uint32_t)((i * 32 + (r >> 2) * 8) * 1024);
+                  *reinterpret_cast<float*>(smem + off) = core.acc[i][j][r];
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+          }
+          __syncthreads();
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int u = q * 256 + etid;
+            const int ml = u >> 2, b = u & 3;     // 64-column block b of local row ml
+            const int m = half * 128 + ml;
+            const int64_t col = n0 + b * 64;
             if (m < mrows && col < N) {
-              const int64_t o = (int64_t)(row0 + m) * N + col;
-              if (p.out_f32) reinterpret_cast<float*>(p.out)[o] = core.acc[i][j][r];
-              else reinterpret_cast<uint16_t*>(p.out)[o] = f32_to_bf16(core.acc[i][j][r]);
+              u32x4* d = reinterpret_cast<u32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)(row0 + m) * N + col);
+#pragma unroll
+              for (int c = 0; c < 16; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off_wide(ml, b * 16 + c));
             }
           }
+          __syncthreads();
         }
+      } else {
+        // (A) bf16 into a rotated [256][256] LDS tile
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = wn * 128 + j * 32 + r32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int m = wm * 128 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
+              const int mb = wm * 128 + g4 + (r & 3);
+              const uint32_t off = epi_off(mb, n >> 3) + (n & 7) * 2 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);
+              *reinterpret_cast<uint16_t*>(smem + off) = f32_to_bf16(core.acc[i][j][r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        __syncthreads();
+        // (B) a thread copies 64-column (128-byte) row segments out with 16-byte stores
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = q * 256 + etid;
+          const int m = u >> 2, b = u & 3;
+          const int64_t col = n0 + b * 64;
+          if (m < mrows && col < N) {
+            u32x4* d = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)(row0 + m) * N + col);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off(m, b * 8 + c));
+          }
+        }
+        __syncthreads();
       }
     }
   }
@@ -432,15 +542,20 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
 
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
   FwdKArgs k = make_fwd_args(g, mx, true);
-  if (mx) fwd_gemm_kernel<true, true><<<kGemmGrid, 256, 0, st>>>(k);
-  else fwd_gemm_kernel<false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  if (mx) fwd_gemm_kernel<true, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+  else fwd_gemm_kernel<false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
   return hipGetLastError();
 }
 
 hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   FwdKArgs k = make_fwd_args(g, mx, false);
-  if (mx) fwd_gemm_kernel<true, false><<<kGemmGrid, 256, 0, st>>>(k);
-  else fwd_gemm_kernel<false, false><<<kGemmGrid, 256, 0, st>>>(k);
+  if (g.out_f32) {
+    if (mx) fwd_gemm_kernel<true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+    else fwd_gemm_kernel<false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  } else {
+    if (mx) fwd_gemm_kernel<true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+    else fwd_gemm_kernel<false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+  }
   return hipGetLastError();
 }
 
