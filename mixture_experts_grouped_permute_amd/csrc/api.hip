@@ -128,6 +128,68 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   return MOE_OK;
 }
 
+struct BwdPlan {
+  uint16_t* dz;         // [R, H] bf16
+  uint16_t* dgu;        // [R, 2I] bf16
+  float* dprob_part;    // [R, parts]
+  void* dx_perm;        // [R, H] io dtype
+  // MXFP8 operands, each quantized along its GEMM's K
+  uint8_t *dzq, *dzs, *w2tq, *w2ts, *dzT, *dzTs, *hT, *hTs;
+  uint8_t *dguq, *dgus, *w1tq, *w1ts, *dguT, *dguTs, *xT, *xTs;
+  int64_t rows_pad;
+  size_t bytes;
+};
+
+BwdPlan plan_bwd(const moe_mlp_bwd_args* a, void* ws) {
+  BwdPlan p{};
+  Carver c(ws);
+  const int64_t R = a->T * a->k, H = a->H, I = a->I;
+  const int E = a->E;
+  p.dz = reinterpret_cast<uint16_t*>(c.take((size_t)(R * H * 2)));
+  p.dgu = reinterpret_cast<uint16_t*>(c.take((size_t)(R * 2 * I * 2)));
+  p.dprob_part = reinterpret_cast<float*>(c.take((size_t)(R * bwd_dprob_parts(I) * 4)));
+  p.dx_perm = c.take((size_t)(R * H) * io_size(a->io_dtype));
+  if (a->compute == MOE_MXFP8_E4M3) {
+    const int64_t Rp = (R + 127) / 128 * 128 + 128 * (int64_t)E;
+    p.rows_pad = Rp;
+    auto take8 = [&](int64_t n) { return reinterpret_cast<uint8_t*>(c.take((size_t)n)); };
+    p.dzq = take8(R * H); p.dzs = take8(R * H / 32);
+    p.w2tq = take8((int64_t)E * I * H); p.w2ts = take8((int64_t)E * I * H / 32);
+    p.dzT = take8(H * Rp); p.dzTs = take8(H * Rp / 32);
+    p.hT = take8(I * Rp); p.hTs = take8(I * Rp / 32);
+    p.dguq = take8(R * 2 * I); p.dgus = take8(R * 2 * I / 32);
+    p.w1tq = take8((int64_t)E * H * 2 * I); p.w1ts = take8((int64_t)E * H * 2 * I / 32);
+    p.dguT = take8(2 * I * Rp); p.dguTs = take8(2 * I * Rp / 32);
+    p.xT = take8(H * Rp); p.xTs = take8(H * Rp / 32);
+  }
+  p.bytes = c.used;
+  return p;
+}
+
+moe_status validate_bwd(const moe_mlp_bwd_args* a) {
+  if (!a) return MOE_ERR_INVALID_ARG;
+  moe_status s = check_common(a->T, a->H, a->E, a->k);
+  if (s != MOE_OK) return s;
+  if (a->I <= 0) return MOE_ERR_INVALID_ARG;
+  if (!io_ok(a->io_dtype) || !io_ok(a->dw_dtype)) return MOE_ERR_INVALID_ARG;
+  if (a->compute != MOE_BF16 && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
+  const int64_t align = a->compute == MOE_BF16 ? 64 : 128;
+  if (a->H % align || a->I % align) return MOE_ERR_UNSUPPORTED;
+  if (!a->dy || !a->w1 || !a->w2 || !a->dx || !a->dprob || !a->dw1 || !a->dw2) return MOE_ERR_INVALID_ARG;
+  if (!a->split_sizes || !a->offsets || !a->row_id_map || !a->src_index || !a->prob_perm) return MOE_ERR_INVALID_ARG;
+  if (!a->saved_x_perm || !a->saved_gu || !a->saved_h) return MOE_ERR_INVALID_ARG;
+  for (int e = 0; e < a->E; ++e)
+    if (!a->w1[e] || !a->w2[e] || !a->dw1[e] || !a->dw2[e]) return MOE_ERR_INVALID_ARG;
+  const int64_t R = a->T * a->k;
+  const int64_t widest = a->H > 2 * a->I ? a->H : 2 * a->I;
+  if (R * widest * 2 >= (int64_t)UINT32_MAX || 2 * a->I * a->H * 4 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (a->compute == MOE_MXFP8_E4M3) {
+    const int64_t Rp = (R + 127) / 128 * 128 + 128 * (int64_t)a->E;
+    if (widest * Rp >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -296,14 +358,108 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
 }
 
 size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a) {
-  (void)a;
-  return 0;
+  if (validate_bwd(a) != MOE_OK) return 0;
+  return plan_bwd(a, nullptr).bytes;
 }
 
 moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
-  (void)a;
-  (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  moe_status s = validate_bwd(a);
+  if (s != MOE_OK) return s;
+  const size_t need = plan_bwd(a, nullptr).bytes;
+  MOE_CHECK(a->workspace && a->workspace_bytes >= need, MOE_ERR_WORKSPACE);
+  BwdPlan p = plan_bwd(a, a->workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t T = a->T, H = a->H, I = a->I, R = T * a->k;
+  const int E = a->E, k = a->k;
+  const bool mx = a->compute == MOE_MXFP8_E4M3;
+  const bool io_f32 = a->io_dtype == MOE_F32;
+  const bool dw_f32 = a->dw_dtype == MOE_F32;
+  const int parts = bwd_dprob_parts(I);
+
+  // dz = bf16(dy) gathered into expert order
+  HIP_TRY(launch_gather_rows(a->dy, io_f32, R, H, k, a->src_index, a->offsets, E, p.dz, st));
+
+  // ---- FC2 dgrad with the ScaledSwiGLU backward epilogue -> dgu, dprob partials
+  BwdGemm d2{};
+  d2.M = 0; d2.N = I; d2.K = H; d2.E = E;
+  d2.split_sizes = a->split_sizes;
+  d2.gu = reinterpret_cast<const uint16_t*>(a->saved_gu);
+  d2.prob_perm = a->prob_perm;
+  d2.dgu = reinterpret_cast<uint16_t*>(p.dgu);
+  d2.dprob_part = p.dprob_part;
+  d2.I = I;
+  if (mx) {
+    HIP_TRY(launch_mx_quant_rows(p.dz, false, R, H, p.dzq, p.dzs, st));
+    for (int e = 0; e < E; ++e)
+      HIP_TRY(launch_mx_quant_cols(a->w2[e], false, H, I, nullptr, 1, H, p.w2tq + (int64_t)e * I * H,
+                                   p.w2ts + (int64_t)e * I * (H / 32), st, 32));
+    d2.a = p.dzq; d2.lda = H; d2.a_scales = p.dzs; d2.ldas = H / 32;
+    d2.b = p.w2tq; d2.ldb = H; d2.b_stride = I * H; d2.b_scales = p.w2ts; d2.ldbs = H / 32;
+    d2.bs_stride = I * (H / 32);
+  } else {
+    d2.a = p.dz; d2.lda = H * 2;
+    d2.tab = a->w2; d2.ldb = I * 2;
+  }
+  HIP_TRY(launch_bwd_dgrad_fc2(d2, mx, st));
+
+  // ---- FC2 wgrad: dW2_e = dz_e^T h_e
+  BwdGemm w2{};
+  w2.M = H; w2.N = I; w2.E = E; w2.split_sizes = a->split_sizes;
+  w2.tab = reinterpret_cast<const void* const*>(a->dw2);
+  w2.out_f32 = dw_f32;
+  if (mx) {
+    const int64_t Rp = p.rows_pad;
+    HIP_TRY(launch_mx_quant_cols(p.dz, false, R, H, a->offsets, E, Rp, p.dzT, p.dzTs, st, 128));
+    HIP_TRY(launch_mx_quant_cols(a->saved_h, false, R, I, a->offsets, E, Rp, p.hT, p.hTs, st, 128));
+    w2.a = p.dzT; w2.lda = Rp; w2.a_scales = p.dzTs; w2.ldas = Rp / 32;
+    w2.b = p.hT; w2.ldb = Rp; w2.b_scales = p.hTs; w2.ldbs = Rp / 32;
+    w2.pad = 128;
+  } else {
+    w2.a = p.dz; w2.lda = H * 2;
+    w2.b = a->saved_h; w2.ldb = I * 2;
+  }
+  HIP_TRY(launch_bwd_wgrad(w2, mx, st));
+
+  // ---- FC1 dgrad: dx_perm = dgu . W1_e
+  BwdGemm d1{};
+  d1.N = H; d1.K = 2 * I; d1.E = E; d1.split_sizes = a->split_sizes;
+  d1.out = p.dx_perm; d1.out_f32 = io_f32;
+  if (mx) {
+    HIP_TRY(launch_mx_quant_rows(p.dgu, false, R, 2 * I, p.dguq, p.dgus, st));
+    for (int e = 0; e < E; ++e)
+      HIP_TRY(launch_mx_quant_cols(a->w1[e], false, 2 * I, H, nullptr, 1, 2 * I, p.w1tq + (int64_t)e * H * 2 * I,
+                                   p.w1ts + (int64_t)e * H * (2 * I / 32), st, 32));
+    d1.a = p.dguq; d1.lda = 2 * I; d1.a_scales = p.dgus; d1.ldas = 2 * I / 32;
+    d1.b = p.w1tq; d1.ldb = 2 * I; d1.b_stride = H * 2 * I; d1.b_scales = p.w1ts; d1.ldbs = 2 * I / 32;
+    d1.bs_stride = H * (2 * I / 32);
+  } else {
+    d1.a = p.dgu; d1.lda = 2 * I * 2;
+    d1.tab = a->w1; d1.ldb = H * 2;
+  }
+  HIP_TRY(launch_bwd_dgrad_fc1(d1, mx, st));
+
+  // ---- FC1 wgrad: dW1_e = dgu_e^T x_perm_e
+  BwdGemm w1{};
+  w1.M = 2 * I; w1.N = H; w1.E = E; w1.split_sizes = a->split_sizes;
+  w1.tab = reinterpret_cast<const void* const*>(a->dw1);
+  w1.out_f32 = dw_f32;
+  if (mx) {
+    const int64_t Rp = p.rows_pad;
+    HIP_TRY(launch_mx_quant_cols(p.dgu, false, R, 2 * I, a->offsets, E, Rp, p.dguT, p.dguTs, st, 128));
+    HIP_TRY(launch_mx_quant_cols(a->saved_x_perm, false, R, H, a->offsets, E, Rp, p.xT, p.xTs, st, 128));
+    w1.a = p.dguT; w1.lda = Rp; w1.a_scales = p.dguTs; w1.ldas = Rp / 32;
+    w1.b = p.xT; w1.ldb = Rp; w1.b_scales = p.xTs; w1.ldbs = Rp / 32;
+    w1.pad = 128;
+  } else {
+    w1.a = p.dgu; w1.lda = 2 * I * 2;
+    w1.b = a->saved_x_perm; w1.ldb = H * 2;
+  }
+  HIP_TRY(launch_bwd_wgrad(w1, mx, st));
+
+  // ---- un-permute: dx[t] = sum_j dx_perm[row(t, j)]; dprob[t, j] = sum of the row's partials
+  HIP_TRY(launch_combine(p.dx_perm, io_f32, T, H, k, a->row_id_map, a->dx, io_f32, st));
+  HIP_TRY(launch_dprob_reduce(p.dprob_part, R, parts, a->row_id_map, T, k, a->dprob, st));
+  return MOE_OK;
 }
 
 int moe_read_device_error(void* workspace, void* stream) {

@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ z
   }
 }
 
-// dz[r] = dy[src_index[r] / k] for the rows of valid experts (rows past offsets[E] untouched).
+// dz[r] = bf16(dy[src_index[r] / k]) for the rows of valid experts (rows past offsets[E] untouched).
 template <bool kF32>
 __global__ __launch_bounds__(256) void gather_kernel(const void* __restrict__ x, int64_t R, int64_t H, int k,
                                                        const int32_t* __restrict__ src_index,
@@ -68,11 +68,18 @@ __global__ __launch_bounds__(256) void gather_kernel(const void* __restrict__ x,
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R || r >= offsets[E]) return;
   const int64_t t = src_index[r] / k;
-  const int esz = kF32 ? 4 : 2;
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(x) + t * H * esz;
-  uint8_t* dst = reinterpret_cast<uint8_t*>(out) + r * H * esz;
-  for (int64_t b = (int64_t)lane * 16; b < H * esz; b += 1024)
-    *reinterpret_cast<u32x4*>(dst + b) = *reinterpret_cast<const u32x4*>(src + b);
+  uint16_t* dst = reinterpret_cast<uint16_t*>(out) + r * H;
+  for (int64_t c = (int64_t)lane * 8; c < H; c += 512) {
+    u32x4 w;
+    if (kF32) {
+      const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * H + c);
+      const float4 a = s4[0], b = s4[1];
+      w = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+    } else {
+      w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + t * H + c);
+    }
+    *reinterpret_cast<u32x4*>(dst + c) = w;
+  }
 }
 
 // dprob[t, j] = sum over parts of partial[row, part], row = row_id_map[t*k + j] (fixed order).

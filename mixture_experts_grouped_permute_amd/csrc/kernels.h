@@ -24,13 +24,16 @@ hipError_t launch_mx_quant_rows(const void* x, bool x_f32, int64_t rows, int64_t
 hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
                                    uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st);
 // Column-wise (blocks along rows, restarted per segment, transposed output); see mxfp8_quantize axis 1.
+// seg_align: segments are padded to a multiple of seg_align rows (32 for the C ABI; 128 when the
+// result feeds the variable-K wgrad GEMM, whose K steps are 128 values).
 hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t cols,
                                 const int32_t* group_offsets, int num_groups, int64_t rows_pad, uint8_t* q,
-                                uint8_t* scales, hipStream_t st);
+                                uint8_t* scales, hipStream_t st, int seg_align = 32);
 
 // ---- combine / gather (combine.hip)
 hipError_t launch_combine(const void* z, bool z_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
                           void* out, bool out_f32, hipStream_t st);
+// out[r] = bf16(x[src_index[r] / k]), r < offsets[E]
 hipError_t launch_gather_rows(const void* x, bool f32, int64_t R, int64_t H, int k, const int32_t* src_index,
                               const int32_t* offsets, int E, void* out, hipStream_t st);
 hipError_t launch_dprob_reduce(const float* partial, int64_t R, int parts, const int32_t* row_id_map,
@@ -59,5 +62,35 @@ struct FwdGemm {
 };
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st);
 hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st);
+
+// ---- backward grouped GEMMs (gemm_bwd.hip); byte strides throughout
+struct BwdGemm {
+  const void* a;            // dgrad: permuted rows (K-major); wgrad bf16: token-major rows; wgrad MXFP8: A^T [M][Rpad]
+  int64_t lda;
+  const uint8_t* a_scales;
+  int64_t ldas;
+  const void* b;            // wgrad bf16: token-major rows; MXFP8: transposed quantized operand
+  int64_t ldb;
+  int64_t b_stride;
+  const uint8_t* b_scales;
+  int64_t ldbs;
+  int64_t bs_stride;
+  const void* const* tab;   // bf16 dgrad: E weight pointers; wgrad: E dW output pointers
+  int64_t M, N, K;
+  int E;
+  int pad;                  // MXFP8 wgrad: token segments padded to this many rows
+  const int32_t* split_sizes;
+  const uint16_t* gu;
+  const float* prob_perm;
+  uint16_t* dgu;
+  float* dprob_part;
+  int64_t I;
+  void* out;
+  bool out_f32;
+};
+hipError_t launch_bwd_dgrad_fc2(const BwdGemm& g, bool mx, hipStream_t st);
+hipError_t launch_bwd_dgrad_fc1(const BwdGemm& g, bool mx, hipStream_t st);
+hipError_t launch_bwd_wgrad(const BwdGemm& g, bool mx, hipStream_t st);
+int bwd_dprob_parts(int64_t I);
 
 }  // namespace moe

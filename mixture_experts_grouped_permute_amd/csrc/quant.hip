@@ -106,20 +106,31 @@ template <bool kF32>
 __global__ __launch_bounds__(64) void mx_cols_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
                                                        const int32_t* __restrict__ goff, int num_groups,
                                                        int64_t rows_pad, uint8_t* __restrict__ q,
-                                                       uint8_t* __restrict__ scales) {
+                                                       uint8_t* __restrict__ scales, int seg_align) {
   // blockIdx.x: global 32-row block index over the padded token axis; blockIdx.y: 64-column slab
   __shared__ int s_pad[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
   const int lane = threadIdx.x;
+  if (!goff) {  // a single segment covering every row
+    if (lane == 0) {
+      s_off[0] = 0;
+      s_off[1] = (int)rows;
+      s_pad[0] = 0;
+      s_pad[1] = (int)((rows + seg_align - 1) / seg_align * seg_align);
+    }
+    num_groups = 1;
+  }
+  __syncthreads();
   // padded segment starts: one wave scans the groups 64 at a time
   int carry = 0;
+  if (goff) {
   for (int g0 = 0; g0 < num_groups; g0 += 64) {
     const int g = g0 + lane;
     int pad = 0;
     if (g < num_groups) {
       const int o = goff[g];
       s_off[g] = o;
-      pad = (goff[g + 1] - o + 31) / 32 * 32;
+      pad = (goff[g + 1] - o + seg_align - 1) / seg_align * seg_align;
     }
     int inc = pad;
 #pragma unroll
@@ -133,6 +144,7 @@ __global__ __launch_bounds__(64) void mx_cols_kernel(const void* __restrict__ x,
   if (lane == 0) {
     s_off[num_groups] = goff[num_groups];
     s_pad[num_groups] = carry;
+  }
   }
   __syncthreads();
   const int64_t pblk = (int64_t)blockIdx.x * 32;       // padded row of this block
@@ -198,13 +210,16 @@ hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, in
 }
 
 hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* group_offsets,
-                                int num_groups, int64_t rows_pad, uint8_t* q, uint8_t* scales, hipStream_t st) {
+                                int num_groups, int64_t rows_pad, uint8_t* q, uint8_t* scales, hipStream_t st,
+                                int seg_align) {
   dim3 grid((unsigned)(rows_pad / 32), (unsigned)((cols + 63) / 64));
   if (grid.x == 0) return hipSuccess;
   if (x_f32)
-    mx_cols_kernel<true><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales);
+    mx_cols_kernel<true><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                              seg_align);
   else
-    mx_cols_kernel<false><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales);
+    mx_cols_kernel<false><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                               seg_align);
   return hipGetLastError();
 }
 

@@ -205,7 +205,8 @@ def backward(fw: Forward, x, dy, w1, w2) -> Backward:
     MXFP8 operands are quantized along each GEMM's own K: dgrad FC2 (dz along
     H, W2 along H), wgrad FC2 (dz and h along tokens), dgrad FC1 (dGU along 2I,
     W1 along 2I), wgrad FC1 (dGU and X_perm along tokens).  dGU is rounded to
-    bf16 before it feeds FC1's GEMMs; saved GU and h are bf16.
+    bf16 before it feeds FC1's GEMMs; saved GU and h are bf16; dY enters the
+    GEMMs rounded to bf16.
     """
     prec, io = fw.precision, fw.io_dtype
     perm = fw.perm
@@ -216,12 +217,14 @@ def backward(fw: Forward, x, dy, w1, w2) -> Backward:
     H = int(w2.shape[1])
     dys = f64(dy)
     tok = perm.token_of_row
-    dz = dys[tok]
+    # dz is a GEMM operand: rounded to bf16 (a no-op for bf16 I/O), like X in the forward
+    dz = dys[tok] if prec == "exact" else nm.round_bf16(dys[tok])
     rnd = (lambda v: v) if prec == "exact" else nm.round_bf16
     gu_s = rnd(fw.gu)
     h_s = fw.h_op if prec != "mxfp8" else nm.round_bf16(fw.h)
     xs = f64(x)
-    x_s = fw.x_perm if prec != "mxfp8" else xs[tok]      # bf16 X_perm (X is bf16 under MXFP8)
+    # saved X_perm is bf16 (under MXFP8 it is re-quantized along tokens for the dW1 GEMM)
+    x_s = fw.x_perm if prec != "mxfp8" else nm.round_bf16(xs[tok])
     dgu = np.zeros((R, 2 * I))
     dx_perm = np.zeros((R, H))
     dprob_perm = np.zeros(R)
