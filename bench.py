@@ -64,7 +64,37 @@ def _traffic(kernel_key):
     return ent.get("bytes_per_launch")
 
 
-def run_gpu(cfg, steps, warmup):
+def _time_ex(lib, hip, call_ex, nph, steps, warmup):
+    """Run call_ex(events) warmup + steps times; returns (host ms/step, mean phase ms)."""
+    import torch
+    ev = []
+    for _ in range(steps * (nph + 1)):
+        e = ctypes.c_void_p()
+        if hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        ev.append(e.value)
+    arrays = [(ctypes.c_void_p * (nph + 1))(*ev[s * (nph + 1):(s + 1) * (nph + 1)]) for s in range(steps)]
+    for _ in range(warmup):
+        call_ex(None)
+    torch.cuda.synchronize()
+    _log(f"timing {steps} steps")
+    t0 = time.perf_counter()
+    for s in range(steps):
+        call_ex(arrays[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    f = ctypes.c_float()
+    sums = [0.0] * nph
+    for s in range(steps):
+        for i in range(nph):
+            hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(arrays[s][i]), ctypes.c_void_p(arrays[s][i + 1]))
+            sums[i] += f.value
+    for e in ev:
+        hip.hipEventDestroy(ctypes.c_void_p(e))
+    return (t1 - t0) * 1e3 / steps, [x / steps for x in sums]
+
+
+def run_gpu(cfg, steps, warmup, backward=False):
     import torch
     import mixture_experts_grouped_permute_amd as m
     from mixture_experts_grouped_permute_amd import _lib as L
@@ -73,69 +103,113 @@ def run_gpu(cfg, steps, warmup):
     lib = m.load()
     hip = _hip()
     _log(f"generating inputs for {cfg.name}")
-    inp = make_inputs(cfg)
+    inp = make_inputs(cfg, with_dy=backward)
     d = inp.to("cuda:0")
     _log("inputs resident on the GPU; warming up")
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     R = T * k
     dev = d.x.device
-    perm = {
-        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
-        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
-        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
-        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
-    }
-    out = torch.empty((T, H), dtype=d.x.dtype, device=dev)
-    a, keep, _, _ = L._fwd_args(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision, out, perm, None)
-    need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
-    if need == 0:
-        raise RuntimeError("argument validation failed")
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
-    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    nph = lib.moe_fwd_phase_count()
-    names = [lib.moe_fwd_phase_name(i).decode() for i in range(nph)]
-    ev = []
-    for _ in range(steps * (nph + 1)):
-        e = ctypes.c_void_p()
-        if hip.hipEventCreate(ctypes.byref(e)) != 0:
-            raise RuntimeError("hipEventCreate failed")
-        ev.append(e.value)
-    ev_arrays = [(ctypes.c_void_p * (nph + 1))(*ev[s * (nph + 1):(s + 1) * (nph + 1)]) for s in range(steps)]
-    for _ in range(warmup):
-        L._check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), stream), "fwd")
-    torch.cuda.synchronize()
-    _log(f"timing {steps} steps")
-    t0 = time.perf_counter()
-    for s in range(steps):
-        L._check(lib.moe_grouped_mlp_fwd_ex(ctypes.byref(a), stream, ev_arrays[s]), "fwd")
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ph = [[0.0] * nph for _ in range(steps)]
-    f = ctypes.c_float()
-    for s in range(steps):
-        for i in range(nph):
-            hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(ev_arrays[s][i]), ctypes.c_void_p(ev_arrays[s][i + 1]))
-            ph[s][i] = f.value
-    for e in ev:
-        hip.hipEventDestroy(ctypes.c_void_p(e))
-    phase_ms = {names[i]: sum(ph[s][i] for s in range(steps)) / steps for i in range(nph)}
-    ms = (t1 - t0) * 1e3 / steps
+    if not backward:
+        perm = {
+            "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+            "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+            "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
+            "src_index": torch.empty(R, dtype=torch.int32, device=dev),
+            "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
+        }
+        out = torch.empty((T, H), dtype=d.x.dtype, device=dev)
+        a, keep, _, _ = L._fwd_args(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision, out, perm, None)
+        need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+        if need == 0:
+            raise RuntimeError("argument validation failed")
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        nph = lib.moe_fwd_phase_count()
+        names = [lib.moe_fwd_phase_name(i).decode() for i in range(nph)]
+
+        def call(evs):
+            L._check(lib.moe_grouped_mlp_fwd_ex(ctypes.byref(a), stream, evs), "fwd")
+    else:
+        _, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision,
+                                       save_for_backward=True)
+        perm = ctx["perm"]
+        a, outs, keep = L._bwd_args(d.dy, ctx, d.w1, d.w2, torch.float32)
+        need = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(a))
+        if need == 0:
+            raise RuntimeError("argument validation failed")
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+        nph = lib.moe_bwd_phase_count()
+        names = [lib.moe_bwd_phase_name(i).decode() for i in range(nph)]
+
+        def call(evs):
+            L._check(lib.moe_grouped_mlp_bwd_ex(ctypes.byref(a), stream, evs), "bwd")
+    ms, ph = _time_ex(lib, hip, call, nph, steps, warmup)
     split = perm["split_sizes"].cpu().tolist()
     del keep
-    return {"ms_per_step": ms, "phase_ms": phase_ms, "split_sizes": split, "inputs": inp}
+    return {"ms_per_step": ms, "phase_ms": dict(zip(names, ph)), "split_sizes": split, "inputs": inp}
+
+
+def gemm_roofline(cfg, phase_ms, phase, flops, kernel):
+    t = phase_ms[phase] * 1e-3
+    ach = flops / t / 1e12
+    peak = PEAK_TFLOPS[cfg.precision]
+    key = f"{phase}_{cfg.precision}_{cfg.name}"
+    return {"kernel": kernel, "bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 4), "traffic": _traffic(key), "flops_per_launch": flops,
+            "avg_launch_ms": round(phase_ms[phase], 4)}
 
 
 def fc1_roofline(cfg, phase_ms):
-    flops = 4.0 * cfg.R * cfg.H * cfg.I          # gate-up GEMM: 2 * R * H * (2I)
-    t = phase_ms["fc1_gateup_swiglu"] * 1e-3
-    ach = flops / t / 1e12
-    peak = PEAK_TFLOPS[cfg.precision]
-    key = f"fc1_{cfg.precision}_{cfg.name}"
-    return {"kernel": "fwd_gemm_kernel (FC1 gate-up + ScaledSwiGLU*prob)", "bound": "mfma",
-            "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-            "traffic": _traffic(key), "flops_per_launch": flops}
+    # gate-up GEMM: 2 * R * H * (2I) flops
+    return gemm_roofline(cfg, phase_ms, "fc1_gateup_swiglu", 4.0 * cfg.R * cfg.H * cfg.I,
+                         "fwd_gemm_kernel (FC1 gate-up + ScaledSwiGLU*prob)")
+
+
+def fwd_leg(cfg, steps, warmup):
+    r = run_gpu(cfg, steps, warmup)
+    ms = r["ms_per_step"]
+    ph = r["phase_ms"]
+    hbm = {}
+    R, H, I, E = cfg.R, cfg.H, cfg.I, cfg.E
+    esz = 4 if cfg.x_dtype == "f32" else 2
+    op = 1 + 1 / 32 if cfg.precision == "mxfp8" else 2
+    # algorithmic bytes: read X once, write T*k permuted operand rows (+ index metadata)
+    hbm["permute_rows"] = (cfg.T * H * esz + R * H * op) / (ph["permute_rows"] * 1e-3) / 1e9
+    zsz = 2 if cfg.x_dtype == "bf16" else 4
+    hbm["combine"] = (R * H * zsz + cfg.T * H * esz + R * 4) / (ph["combine"] * 1e-3) / 1e9
+    if cfg.precision == "mxfp8":
+        nz = sum(1 for c in r["split_sizes"] if c > 0)
+        hbm["quant_w1"] = nz * 2 * I * H * (2 + 1 + 1 / 32) / (ph["quant_w1"] * 1e-3) / 1e9
+        hbm["quant_w2"] = nz * H * I * (2 + 1 + 1 / 32) / (ph["quant_w2"] * 1e-3) / 1e9
+    return r, {
+        "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "tflops": round(cfg.fwd_flops() / (ms * 1e-3) / 1e12, 1),
+        "roofline": fc1_roofline(cfg, ph),
+        "fc2_tflops": round(2.0 * R * H * I / (ph["fc2_down"] * 1e-3) / 1e12, 1),
+        "hbm_GBs": {k_: round(v, 1) for k_, v in hbm.items()},
+        "phase_ms": {k_: round(v, 4) for k_, v in ph.items()},
+        "split_sizes": r["split_sizes"],
+    }
+
+
+def bwd_leg(cfg, steps, warmup):
+    r = run_gpu(cfg, steps, warmup, backward=True)
+    ms = r["ms_per_step"]
+    ph = r["phase_ms"]
+    R, H, I = cfg.R, cfg.H, cfg.I
+    gem = {"dgrad_fc2_swiglu_bwd": 2.0 * R * H * I, "wgrad_fc2": 2.0 * R * H * I,
+           "dgrad_fc1": 4.0 * R * H * I, "wgrad_fc1": 4.0 * R * H * I}
+    dom = max(gem, key=lambda k_: ph[k_])
+    return {
+        "workload": f"{cfg.name}: T={cfg.T} H={H} I={I} E={cfg.E} top-{cfg.k}, bf16, dW in fp32",
+        "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
+        "tflops": round(cfg.bwd_flops() / (ms * 1e-3) / 1e12, 1),
+        "roofline": gemm_roofline(cfg, ph, dom, gem[dom], f"bwd_gemm_kernel ({dom})"),
+        "gemm_tflops": {k_: round(v / (ph[k_] * 1e-3) / 1e12, 1) for k_, v in gem.items()},
+        "phase_ms": {k_: round(v, 4) for k_, v in ph.items()},
+    }
 
 
 def cpu_baseline(inp, cfg, tokens):
@@ -165,6 +239,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-mxfp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -174,40 +249,37 @@ def main():
     from moe_inputs import get_config
 
     cfg = get_config(2)
-    r = run_gpu(cfg, args.steps, args.warmup)
-    ms = r["ms_per_step"]
-    tok_s = cfg.T / (ms * 1e-3)
+    r, leg = fwd_leg(cfg, args.steps, args.warmup)
+    ms = leg["ms_per_step"]
     line = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": leg["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} top-{cfg.k}, "
                                f"bf16 operands, fp32 accumulation, N(0,1) router logits",
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.k, "parallelism": "none (1 GPU)"},
-        "tflops": round(cfg.fwd_flops() / (ms * 1e-3) / 1e12, 1),
-        "roofline": fc1_roofline(cfg, r["phase_ms"]),
-        "phase_ms": {k_: round(v, 4) for k_, v in r["phase_ms"].items()},
-        "split_sizes": r["split_sizes"],
+        "tflops": leg["tflops"], "roofline": leg["roofline"],
+        "fc2_tflops": leg["fc2_tflops"], "hbm_GBs": leg["hbm_GBs"],
+        "phase_ms": leg["phase_ms"], "split_sizes": leg["split_sizes"],
     }
     if not args.no_cpu_baseline:
         _log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
         line["cpu_baseline"] = cpu_baseline(r["inputs"], cfg, args.cpu_tokens)
     del r
+    import torch
     if not args.no_mxfp8:
-        import torch
+        for key, ci in (("mxfp8", 3), ("mxfp8_finegrained", 5)):
+            torch.cuda.empty_cache()
+            c = get_config(ci)
+            rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2))
+            del rr
+            lg["workload"] = (f"{c.name}: T={c.T} H={c.H} I={c.I} E={c.E} top-{c.k}, MXFP8 both GEMMs, "
+                              f"Zipf({c.zipf_s}) routing" + (f", expert {c.zero_expert} empty" if c.zero_expert is not None else "")
+                              + ", weights quantized per call")
+            line[key] = lg
+    if not args.no_backward:
         torch.cuda.empty_cache()
-        c3 = get_config(3)
-        r3 = run_gpu(c3, max(2, args.steps // 2), max(1, args.warmup // 2))
-        ms3 = r3["ms_per_step"]
-        line["mxfp8"] = {
-            "workload": f"{c3.name}: T={c3.T} H={c3.H} I={c3.I} E={c3.E} top-{c3.k}, MXFP8 both GEMMs, "
-                        f"Zipf(1.2) routing, expert {c3.zero_expert} empty, weights quantized per call",
-            "value": round(c3.T / (ms3 * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms3, 4),
-            "tflops": round(c3.fwd_flops() / (ms3 * 1e-3) / 1e12, 1),
-            "roofline": fc1_roofline(c3, r3["phase_ms"]),
-            "phase_ms": {k_: round(v, 4) for k_, v in r3["phase_ms"].items()},
-            "split_sizes": r3["split_sizes"],
-        }
+        line["backward_bf16"] = bwd_leg(get_config(4), max(2, args.steps // 2), max(1, args.warmup // 2))
     print(json.dumps(line), flush=True)
 
 

@@ -222,6 +222,12 @@ typedef struct {
 size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a);
 moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream);
 
+/* Backward with per-phase events, as moe_grouped_mlp_fwd_ex (moe_bwd_phase_count() + 1
+ * caller-created hipEvent_t handles; NULL behaves like moe_grouped_mlp_bwd). */
+moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void* const* events);
+int moe_bwd_phase_count(void);
+const char* moe_bwd_phase_name(int i);   /* NULL when out of range */
+
 /* Synchronizes `stream`, then returns the device error flag kept in the first
  * 4 bytes of `workspace` by the last moe_permute / moe_grouped_mlp_fwd call
  * that used it (0 = none, 1 = an expert id was out of range; every such call

@@ -26,7 +26,7 @@ EXPORTS = (
     "moe_abi_version", "moe_status_string", "mxfp8_quantize", "moe_permute_workspace_size", "moe_permute",
     "moe_grouped_mlp_fwd_workspace", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd_workspace",
     "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
-    "moe_fwd_phase_name",
+    "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
 )
 
 
@@ -103,6 +103,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_fwd_phase_count.restype = ctypes.c_int
     lib.moe_fwd_phase_name.restype = ctypes.c_char_p
     lib.moe_fwd_phase_name.argtypes = [ctypes.c_int]
+    lib.moe_grouped_mlp_bwd_ex.restype = ctypes.c_int
+    lib.moe_grouped_mlp_bwd_ex.argtypes = [ctypes.POINTER(BwdArgs), _vp, ctypes.POINTER(_vp)]
+    lib.moe_bwd_phase_count.restype = ctypes.c_int
+    lib.moe_bwd_phase_name.restype = ctypes.c_char_p
+    lib.moe_bwd_phase_name.argtypes = [ctypes.c_int]
     lib.moe_read_device_error.restype = ctypes.c_int
     lib.moe_read_device_error.argtypes = [_vp, _vp]
     if path is None:
@@ -293,11 +298,8 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
     return out, ctx
 
 
-def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32,
-                        workspace: Optional[torch.Tensor] = None):
-    """Backward of moe_grouped_mlp_fwd (needs save_for_backward=True).
-    Returns (dx [T,H], dprob [T,k] f32, dw1 [E,2I,H], dw2 [E,H,I])."""
-    lib = load()
+def _bwd_args(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32):
+    """Output tensors and the argument struct of a backward call (no launch)."""
     dev = dy.device
     T, H = dy.shape
     perm, saved = ctx["perm"], ctx["saved"]
@@ -325,6 +327,17 @@ def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.floa
     a.saved_x_perm, a.saved_gu, a.saved_h = _ptr(saved["x_perm"]), _ptr(saved["gu"]), _ptr(saved["h"])
     a.dx, a.dprob = _ptr(dx), _ptr(dprob)
     a.dw1, a.dw2 = dw1t, dw2t
+    return a, (dx, dprob, dw1, dw2), (w1t, w2t, dw1t, dw2t, w1k, w2k)
+
+
+def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32,
+                        workspace: Optional[torch.Tensor] = None):
+    """Backward of moe_grouped_mlp_fwd (needs save_for_backward=True).
+    Returns (dx [T,H], dprob [T,k] f32, dw1 [E,2I,H], dw2 [E,H,I])."""
+    lib = load()
+    dev = dy.device
+    a, outs, keep = _bwd_args(dy, ctx, w1, w2, dw_dtype)
+    dx, dprob, dw1, dw2 = outs
     need = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(a))
     if need == 0:
         _check(lib.moe_grouped_mlp_bwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_bwd")

@@ -362,7 +362,19 @@ size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a) {
   return plan_bwd(a, nullptr).bytes;
 }
 
+static const char* const kBwdPhases[] = {"gather_dy", "quant_dgrad_fc2", "dgrad_fc2_swiglu_bwd",
+                                         "quant_wgrad_fc2", "wgrad_fc2", "quant_dgrad_fc1", "dgrad_fc1",
+                                         "quant_wgrad_fc1", "wgrad_fc1", "unpermute_dx_dprob"};
+constexpr int kNumBwdPhases = 10;
+
+int moe_bwd_phase_count(void) { return kNumBwdPhases; }
+const char* moe_bwd_phase_name(int i) { return (i >= 0 && i < kNumBwdPhases) ? kBwdPhases[i] : nullptr; }
+
 moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
+  return moe_grouped_mlp_bwd_ex(a, stream, nullptr);
+}
+
+moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void* const* events) {
   moe_status s = validate_bwd(a);
   if (s != MOE_OK) return s;
   const size_t need = plan_bwd(a, nullptr).bytes;
@@ -375,9 +387,14 @@ moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
   const bool io_f32 = a->io_dtype == MOE_F32;
   const bool dw_f32 = a->dw_dtype == MOE_F32;
   const int parts = bwd_dprob_parts(I);
+  auto mark = [&](int i) -> bool {
+    return !events || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) == hipSuccess;
+  };
 
   // dz = bf16(dy) gathered into expert order
+  MOE_CHECK(mark(0), MOE_ERR_HIP);
   HIP_TRY(launch_gather_rows(a->dy, io_f32, R, H, k, a->src_index, a->offsets, E, p.dz, st));
+  MOE_CHECK(mark(1), MOE_ERR_HIP);
 
   // ---- FC2 dgrad with the ScaledSwiGLU backward epilogue -> dgu, dprob partials
   BwdGemm d2{};
@@ -400,7 +417,9 @@ moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
     d2.a = p.dz; d2.lda = H * 2;
     d2.tab = a->w2; d2.ldb = I * 2;
   }
+  MOE_CHECK(mark(2), MOE_ERR_HIP);
   HIP_TRY(launch_bwd_dgrad_fc2(d2, mx, st));
+  MOE_CHECK(mark(3), MOE_ERR_HIP);
 
   // ---- FC2 wgrad: dW2_e = dz_e^T h_e
   BwdGemm w2{};
@@ -418,7 +437,9 @@ moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
     w2.a = p.dz; w2.lda = H * 2;
     w2.b = a->saved_h; w2.ldb = I * 2;
   }
+  MOE_CHECK(mark(4), MOE_ERR_HIP);
   HIP_TRY(launch_bwd_wgrad(w2, mx, st));
+  MOE_CHECK(mark(5), MOE_ERR_HIP);
 
   // ---- FC1 dgrad: dx_perm = dgu . W1_e
   BwdGemm d1{};
@@ -436,7 +457,9 @@ moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
     d1.a = p.dgu; d1.lda = 2 * I * 2;
     d1.tab = a->w1; d1.ldb = H * 2;
   }
+  MOE_CHECK(mark(6), MOE_ERR_HIP);
   HIP_TRY(launch_bwd_dgrad_fc1(d1, mx, st));
+  MOE_CHECK(mark(7), MOE_ERR_HIP);
 
   // ---- FC1 wgrad: dW1_e = dgu_e^T x_perm_e
   BwdGemm w1{};
@@ -454,11 +477,14 @@ moe_status moe_grouped_mlp_bwd(const moe_mlp_bwd_args* a, void* stream) {
     w1.a = p.dgu; w1.lda = 2 * I * 2;
     w1.b = a->saved_x_perm; w1.ldb = H * 2;
   }
+  MOE_CHECK(mark(8), MOE_ERR_HIP);
   HIP_TRY(launch_bwd_wgrad(w1, mx, st));
+  MOE_CHECK(mark(9), MOE_ERR_HIP);
 
   // ---- un-permute: dx[t] = sum_j dx_perm[row(t, j)]; dprob[t, j] = sum of the row's partials
   HIP_TRY(launch_combine(p.dx_perm, io_f32, T, H, k, a->row_id_map, a->dx, io_f32, st));
   HIP_TRY(launch_dprob_reduce(p.dprob_part, R, parts, a->row_id_map, T, k, a->dprob, st));
+  MOE_CHECK(mark(10), MOE_ERR_HIP);
   return MOE_OK;
 }
 
