@@ -241,7 +241,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,backward",
+                    help="comma list of bf16, mxfp8, mxfp8_finegrained, backward (bf16 always runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        src = torch.empty(args.copy_probe // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "launches": 5}), flush=True)
+        return
+    legs = set(x.strip() for x in args.legs.split(",") if x.strip())
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this layer runs unsharded on a single MI355X); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -269,6 +283,8 @@ def main():
     import torch
     if not args.no_mxfp8:
         for key, ci in (("mxfp8", 3), ("mxfp8_finegrained", 5)):
+            if key not in legs:
+                continue
             torch.cuda.empty_cache()
             c = get_config(ci)
             rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2))
@@ -277,7 +293,7 @@ def main():
                               f"Zipf({c.zipf_s}) routing" + (f", expert {c.zero_expert} empty" if c.zero_expert is not None else "")
                               + ", weights quantized per call")
             line[key] = lg
-    if not args.no_backward:
+    if not args.no_backward and "backward" in legs:
         torch.cuda.empty_cache()
         line["backward_bf16"] = bwd_leg(get_config(4), max(2, args.steps // 2), max(1, args.warmup // 2))
     print(json.dumps(line), flush=True)

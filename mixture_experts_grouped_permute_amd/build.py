@@ -23,7 +23,7 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
-    "-Wno-unused-result",
+    "-Wno-unused-result", "-Wno-inline-asm",
     # packed-fp32 instructions are never generated (they are not trusted on this hardware)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{os.path.join(ROOT, 'include')}",

@@ -65,6 +65,7 @@ __device__ __forceinline__ const uint8_t* kernarg_table(int e) {
 template <bool kMx, bool kFc1, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
+  static_assert(kPStages * kPStageBytes == 2 * kStageBytes, "the pipeline reuses the epilogue staging space");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * kScaleBytes : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -133,11 +134,70 @@ void fwd_gemm_kernel(const FwdKArgs p) {
         bso = (uint32_t)(tid * kscale_row);
       }
     }
-    const uint32_t avo0 = (uint32_t)(ldr * rowb) + ldc * 16;
-    const uint32_t astride = 32u * rowb;
-
     TileCore<kMx, kFc1> core;
     core.zero();
+    if constexpr (!kMx) {
+      // ---- BF16 main loop: 4-stage direct-to-LDS pipeline (64 bytes of K per stage).
+      // Thread (wave w, lane L) issues 4 DMA loads per operand per stage; load j fills the 1 KB
+      // block of rows (4w + j) * 16 + L / 4, physical chunk L % 4.
+      const int kTp = (int)(rowb / kPRowBytes);
+      uint32_t a_vo[4], b_vo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = (wave * 4 + j) * 16 + (lane >> 2);
+        const uint32_t c = (uint32_t)(lane & 3) ^ (((uint32_t)r >> 2) & 3u);
+        a_vo[j] = (uint32_t)r * rowb + c * 16;
+        int64_t wr = r;
+        if (kFc1) wr = r < 128 ? ((int64_t)nt * 128 + r) : (N + (int64_t)nt * 128 + (r - 128));
+        b_vo[j] = (uint32_t)(wr * rowb) + c * 16;
+      }
+      const i32x4 va = make_vsharp(p.a + (int64_t)row0 * rowb, (uint32_t)mrows * rowb);
+      const i32x4 vb = kFc1 ? make_vsharp(wbase, (uint32_t)(2 * N * rowb))
+                            : make_vsharp(wbase + (int64_t)nt * kBN * rowb,
+                                          (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * rowb));
+      const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 4) * 1024u;
+      auto issue = [&](int kt) {
+        const uint32_t sa = lds0 + (uint32_t)(kt & (kPStages - 1)) * kPStageBytes;
+        const uint32_t so = (uint32_t)kt * kPRowBytes;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(va, sa + j * 1024u, a_vo[j], so);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(vb, sa + kPTileBytes + j * 1024u, b_vo[j], so);
+      };
+      // wait until this thread's loads of stage s are in LDS, given the stages issued after it
+      auto wait_stage = [&](int after) {
+        if (after >= 2) wait_vmcnt<16>();
+        else if (after == 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+      };
+      typename TileCore<kMx, kFc1>::Frag f0, f1;
+#pragma unroll
+      for (int s = 0; s < 3; ++s)
+        if (s < kTp) issue(s);
+      wait_stage(min(2, kTp - 1));
+      __syncthreads();
+      if (3 < kTp) issue(3);
+      core.load_frag_p(f0, 0, smem, smem + kPTileBytes, wm, wn, lane);
+      for (int kt = 0; kt < kTp; ++kt) {
+        const uint8_t* sA = smem + (kt & (kPStages - 1)) * kPStageBytes;
+        core.load_frag_p(f1, 1, sA, sA + kPTileBytes, wm, wn, lane);
+        core.mma(f0);
+        core.mma_half(f1, 0);
+        if (kt + 1 < kTp) {
+          // stage kt+1: all its loads landed (own wait + barrier); stage kt's LDS reads are done
+          // in every wave, so its buffer can take stage kt+4
+          wait_stage(min(2, kTp - 2 - kt));
+          __syncthreads();
+          if (kt + 4 < kTp) issue(kt + 4);
+          const uint8_t* sN = smem + ((kt + 1) & (kPStages - 1)) * kPStageBytes;
+          core.load_frag_p(f0, 0, sN, sN + kPTileBytes, wm, wn, lane);
+        }
+        core.mma_half(f1, 2);
+      }
+      __syncthreads();
+    } else {
+    const uint32_t avo0 = (uint32_t)(ldr * rowb) + ldc * 16;
+    const uint32_t astride = 32u * rowb;
     u32x4 ra_reg[8], rb_reg[8];
     uint32_t ras_reg = 0, rbs_reg = 0;
 
@@ -177,6 +237,8 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       core.compute(sA, sA + kTileBytes, ss, ss + 256, wm, wn, lane);
       if (kt + 1 < kT) lstore(st ^ 1);
       __syncthreads();
+    }
+
     }
 
     // ---- epilogue, staged through LDS (the stage buffers are free after the last barrier).

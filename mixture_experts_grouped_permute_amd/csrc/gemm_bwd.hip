@@ -125,6 +125,12 @@ __device__ __forceinline__ void store_tile(const Core& core, uint8_t* smem, uint
   }
 }
 
+// Store the 8 transposed columns of one 8x8 block: column c goes to LDS row nb*8 + c, chunk kb.
+__device__ __forceinline__ void store_t8(uint8_t* s, const u32x4 w[8], int nb, int kb) {
+#pragma unroll
+  for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(s + swz(nb * 8 + c, kb)) = w[c];
+}
+
 template <int kRole, bool kMx, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_gemm_kernel(const BwdKArgs p) {
@@ -243,8 +249,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       if constexpr (kAMN) {
         u32x4 w[8];
         transpose8x8_b16(ra_reg, w);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(sA + swz(nb * 8 + c, kb)) = w[c];
+        store_t8(sA, w, nb, kb);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sA + lds_ld + i * 32 * kRowBytes) = ra_reg[i];
@@ -252,8 +257,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       if constexpr (kBMN) {
         u32x4 w[8];
         transpose8x8_b16(rb_reg, w);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(sB + swz(nb * 8 + c, kb)) = w[c];
+        store_t8(sB, w, nb, kb);
       } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sB + lds_ld + i * 32 * kRowBytes) = rb_reg[i];

@@ -29,8 +29,18 @@ __device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff)
 __device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
+// 128-byte rows, stored in pairs: rows 2j and 2j+1 share one 256-byte bank line (16 slots
+// of 16 bytes), and chunk c of row r sits in slot (((r & 1) << 3) | c) ^ hs(j),
+// hs(j) = (j & 7) | ((j & 4) << 1).  LDS serves a 16-byte-per-lane access 16 lanes (256 bytes,
+// 64 banks) at a time, and each of these 16-lane patterns lands in 16 distinct slots:
+//   * MFMA fragment reads: 16 consecutive rows at one chunk;
+//   * row-wise stores: two adjacent rows, all 8 chunks each;
+//   * transposed 8x8-block stores: rows R and R + 8 (same parity), all 8 chunks each --
+//     hs(j) and hs(j + 4) differ in bit 3, which moves the second row to the other half.
 __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
-  return row * kRowBytes + ((chunk ^ (row & 7u)) << 4);
+  const uint32_t j = row >> 1;
+  const uint32_t hs = (j & 7u) | ((j & 4u) << 1);
+  return j * 256u + (((((row & 1u) << 3) | chunk) ^ hs) << 4);
 }
 
 // Per-expert counts, row offsets and tile prefix (ceil(M_e / 256) * nN) in LDS.
@@ -97,6 +107,57 @@ __device__ __forceinline__ uint32_t epi_off(int m, int c16) {
 // ---------------------------------------------------------------------------
 // One K-pass of a 256x256 tile.  kFc1 selects the B row map (gate/up halves).
 // ---------------------------------------------------------------------------
+// ---- BF16 4-stage direct-to-LDS pipeline: each stage holds 64 bytes (32 values) of K per
+// row for the 256 A rows and 256 B rows.  The LDS-DMA loads place lane L's 16 bytes at
+// slot L of a 1 KB block (16 rows x 4 chunks), so the chunk swizzle is chosen on the global
+// side: physical chunk p of row r holds logical chunk p ^ ((r >> 2) & 3).  Four rows share a
+// 256-byte bank line, so 16 consecutive rows read at one logical chunk cover all sixteen
+// 16-byte bank groups.
+constexpr int kPStages = 4;
+constexpr int kPRowBytes = 64;
+constexpr int kPTileBytes = 256 * kPRowBytes;     // 16 KB
+constexpr int kPStageBytes = 2 * kPTileBytes;     // 32 KB: A + B
+
+__device__ __forceinline__ uint32_t pswz(uint32_t row, uint32_t chunk) {
+  return row * kPRowBytes + ((chunk ^ ((row >> 2) & 3u)) << 4);
+}
+
+// s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Buffer descriptor as four SGPR words, for the inline-asm LDS-DMA loads below.
+__device__ __forceinline__ i32x4 make_vsharp(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  i32x4 v;
+  v[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  v[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));   // stride 0
+  v[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  v[3] = 0x00020000;
+  return v;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(lds_ptr_t)p);
+}
+
+// 16-byte buffer load straight into LDS: lane L's bytes land at lds + 16 L.  Issued as inline
+// asm so the compiler does not treat it as an LDS write that every later LDS read must wait
+// for; the kernel orders it explicitly with wait_vmcnt and barriers.  Offsets past `bytes`
+// of the descriptor read zero.
+__device__ __forceinline__ void dma16(const i32x4& vs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);   // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(l), "v"(voff), "s"(vs), "s"(soff)
+               : "memory", "m0");
+}
+
 // Transpose an 8x8 block of bf16: v[r] holds 8 consecutive values of row r,
 // w[c] receives column c (8 values, one per row) -- v_perm_b32 picks the low or
 // high halves of two words at a time.
@@ -168,6 +229,33 @@ struct TileCore {
         f.sb[j] = (int)(sBs[row] >> sh);
       }
     }
+  }
+
+  // BF16 fragments of MFMA K-substep kk (0..1) from a pipelined 64-byte-row stage
+  __device__ __forceinline__ void load_frag_p(Frag& f, int kk, const uint8_t* sA, const uint8_t* sB, int wm, int wn,
+                                              int lane) const {
+    const int r32 = lane & 31, g = lane >> 5;
+    const uint32_t ch = (uint32_t)(kk * 2 + g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = *reinterpret_cast<const bf16x8*>(sA + pswz(wm * 128 + i * 32 + r32, ch));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      f.b[j] = *reinterpret_cast<const bf16x8*>(sB + pswz(brow(wn, j) + r32, ch));
+  }
+
+  // MFMAs of fragment rows i in [i0, i0 + 2)
+  __device__ __forceinline__ void mma_half(const Frag& f, int i0) {
+#pragma unroll
+    for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (!kMx)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
+                                                                        f.sb[j]);
+      }
   }
 
   __device__ __forceinline__ void mma(const Frag& f) {
