@@ -110,8 +110,13 @@ class Forward:
     extra: dict = field(default_factory=dict)
 
 
-def forward(x, topk_idx, topk_prob, w1, w2, precision: str = "bf16", io_dtype: str = "bf16") -> Forward:
-    """Whole layer.  x [T,H]; topk_idx/prob [T,k]; w1 [E,2I,H]; w2 [E,H,I]."""
+def forward(x, topk_idx, topk_prob, w1, w2, precision: str = "bf16", io_dtype: str = "bf16",
+            experts=None) -> Forward:
+    """Whole layer.  x [T,H]; topk_idx/prob [T,k]; w1 [E,2I,H]; w2 [E,H,I].
+
+    experts: optional subset of expert ids; only their rows are computed (the
+    same arithmetic), and out[t] is NaN for tokens routed to any other expert.
+    """
     xs = f64(x)
     idx = np.asarray(topk_idx)
     prob = f64(topk_prob)
@@ -129,9 +134,13 @@ def forward(x, topk_idx, topk_prob, w1, w2, precision: str = "bf16", io_dtype: s
     hq = np.zeros((R, I))
     z = np.zeros((R, H))
     off = perm.offsets
+    todo = set(range(E)) if experts is None else set(int(e) for e in experts)
     for e in range(E):
         lo, hi = int(off[e]), int(off[e + 1])
         if hi == lo:
+            continue
+        if e not in todo:
+            z[lo:hi] = np.nan
             continue
         g_, h_, hq_, z_ = expert_forward(x_perm[lo:hi], p_perm[lo:hi],
                                          weight_operand(f64(w1[e]), precision),
@@ -193,7 +202,7 @@ def _col_operand(a, precision):
     return nm.fake_quant_mxfp8(pad, axis=0)[:M]
 
 
-def backward(fw: Forward, x, dy, w1, w2) -> Backward:
+def backward(fw: Forward, x, dy, w1, w2, experts=None) -> Backward:
     """Gradients of sum(out * dy) w.r.t. X, topk_prob, W1 and W2.
 
         dz = dY[token of row];  dh = dz . W2_e          (FC2 dgrad)
@@ -207,6 +216,9 @@ def backward(fw: Forward, x, dy, w1, w2) -> Backward:
     W1 along 2I), wgrad FC1 (dGU and X_perm along tokens).  dGU is rounded to
     bf16 before it feeds FC1's GEMMs; saved GU and h are bf16; dY enters the
     GEMMs rounded to bf16.
+
+    experts: optional subset (as in `forward`); gradients that depend on any
+    other expert are NaN.
     """
     prec, io = fw.precision, fw.io_dtype
     perm = fw.perm
@@ -231,8 +243,15 @@ def backward(fw: Forward, x, dy, w1, w2) -> Backward:
     dw1 = np.zeros((E, 2 * I, H))
     dw2 = np.zeros((E, H, I))
     off = perm.offsets
+    todo = set(range(E)) if experts is None else set(int(e) for e in experts)
     for e in range(E):
         lo, hi = int(off[e]), int(off[e + 1])
+        if e not in todo:
+            dx_perm[lo:hi] = np.nan
+            dprob_perm[lo:hi] = np.nan
+            dw1[e] = np.nan
+            dw2[e] = np.nan
+            continue
         if hi == lo:
             continue
         w1e, w2e = f64(w1[e]), f64(w2[e])
