@@ -66,7 +66,8 @@ template <bool kMx, bool kFc1, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
   static_assert(kPStages * kPStageBytes == 2 * kStageBytes, "the pipeline reuses the epilogue staging space");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * kScaleBytes : 16)];
+  // 4 pipeline stages (the epilogue reuses them), plus the MXFP8 scale ring (4 x 2 KB)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPStages * kPStageBytes + (kMx ? kPStages * 2048 : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -77,9 +78,6 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   const int64_t K = p.K, N = p.N;
   const int esz = kMx ? 1 : 2;
   const uint32_t rowb = (uint32_t)(K * esz);           // bytes per operand row
-  const int kT = (int)(rowb / kRowBytes);              // K steps
-  const int ldr = tid >> 3, ldc = tid & 7;             // loader: rows ldr + 32 i, chunk ldc
-  const uint32_t lds_ld = swz(ldr, ldc);
   const uint32_t kscale_row = (uint32_t)(K / 32);      // scale bytes per row
 
   for (int round = 0;; ++round) {
@@ -94,52 +92,17 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     const int mt = local % nM, nt = local / nM;
     const int row0 = __builtin_amdgcn_readfirstlane(sched.off[e]) + mt * kBM;   // first permuted row of the tile
     const int mrows = min(kBM, Me - mt * kBM);
-    // ---- operand descriptors
-    rsrc_t ra = make_rsrc(p.a + (int64_t)row0 * rowb, (uint32_t)mrows * rowb);
     const uint8_t* wbase = kMx ? (p.wq + (int64_t)e * p.wq_stride) : kernarg_table(e);
-    rsrc_t rb;
-    uint32_t bvo[8];
-    if (kFc1) {
-      // LDS rows [0,128): gate rows n0h + r; [128,256): up rows I + n0h + r.  Gate rows past I
-      // only feed masked columns; up rows past 2I fall outside the range and read zero.
-      const int64_t n0h = (int64_t)nt * 128;
-      rb = make_rsrc(wbase, (uint32_t)(2 * N * rowb));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int r = ldr + 32 * i;
-        int64_t wr = r < 128 ? (n0h + r) : (N + n0h + (r - 128));
-        bvo[i] = (uint32_t)(wr * rowb) + ldc * 16;
-      }
-    } else {
-      const int64_t n0 = (int64_t)nt * kBN;
-      const int64_t nrows = min((int64_t)kBN, N - n0);
-      rb = make_rsrc(wbase + n0 * rowb, (uint32_t)(nrows * rowb));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) bvo[i] = (uint32_t)((ldr + 32 * i) * rowb) + ldc * 16;
-    }
-    rsrc_t ras, rbs;
-    uint32_t bso = 0;
-    if (kMx) {
-      ras = make_rsrc(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
-      const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
-      if (kFc1) {
-        const int64_t n0h = (int64_t)nt * 128;
-        rbs = make_rsrc(sbase, (uint32_t)(2 * N * kscale_row));
-        int64_t wr = tid < 128 ? (n0h + tid) : (N + n0h + (tid - 128));
-        bso = (uint32_t)(wr * kscale_row);
-      } else {
-        const int64_t n0 = (int64_t)nt * kBN;
-        const int64_t nrows = min((int64_t)kBN, N - n0);
-        rbs = make_rsrc(sbase + n0 * kscale_row, (uint32_t)(nrows * kscale_row));
-        bso = (uint32_t)(tid * kscale_row);
-      }
-    }
     TileCore<kMx, kFc1> core;
     core.zero();
-    if constexpr (!kMx) {
-      // ---- BF16 main loop: 4-stage direct-to-LDS pipeline (64 bytes of K per stage).
-      // Thread (wave w, lane L) issues 4 DMA loads per operand per stage; load j fills the 1 KB
-      // block of rows (4w + j) * 16 + L / 4, physical chunk L % 4.
+    {
+      // ---- main loop: 4-stage direct-to-LDS pipeline, 64 bytes of K per stage (32 bf16 or
+      // 64 E4M3 values).  Thread (wave w, lane L) issues 4 DMA loads per operand per stage;
+      // load j fills the 1 KB block of rows (4w + j) * 16 + L / 4, physical chunk L % 4.
+      // MXFP8 adds one 4-byte scale load per operand per stage: lane L of wave w loads the
+      // scale word of row 64w + L covering the stage's 128-value pair of stages.
+      // FC1 B rows [0,128) are gate rows n0h + r, rows [128,256) up rows I + n0h + r: gate rows
+      // past I only feed masked columns, up rows past 2I fall outside the range and read zero.
       const int kTp = (int)(rowb / kPRowBytes);
       uint32_t a_vo[4], b_vo[4];
 #pragma unroll
@@ -156,6 +119,26 @@ void fwd_gemm_kernel(const FwdKArgs p) {
                             : make_vsharp(wbase + (int64_t)nt * kBN * rowb,
                                           (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * rowb));
       const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 4) * 1024u;
+      // MXFP8 scale descriptors and per-lane offsets
+      i32x4 vas = va, vbs = vb;
+      uint32_t as_vo = 0, bs_vo = 0;
+      const uint32_t lds_sc = lds_addr(smem + kPStages * kPStageBytes) + (uint32_t)wave * 256u;
+      if constexpr (kMx) {
+        const int r = wave * 64 + lane;
+        vas = make_vsharp(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
+        as_vo = (uint32_t)r * kscale_row;
+        const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
+        if (kFc1) {
+          const int64_t n0h = (int64_t)nt * 128;
+          vbs = make_vsharp(sbase, (uint32_t)(2 * N * kscale_row));
+          const int64_t wr = r < 128 ? (n0h + r) : (N + n0h + (r - 128));
+          bs_vo = (uint32_t)(wr * kscale_row);
+        } else {
+          const int64_t n0 = (int64_t)nt * kBN;
+          vbs = make_vsharp(sbase + n0 * kscale_row, (uint32_t)(min((int64_t)kBN, N - n0) * kscale_row));
+          bs_vo = (uint32_t)r * kscale_row;
+        }
+      }
       auto issue = [&](int kt) {
         const uint32_t sa = lds0 + (uint32_t)(kt & (kPStages - 1)) * kPStageBytes;
         const uint32_t so = (uint32_t)kt * kPRowBytes;
@@ -163,12 +146,23 @@ void fwd_gemm_kernel(const FwdKArgs p) {
         for (int j = 0; j < 4; ++j) dma16(va, sa + j * 1024u, a_vo[j], so);
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma16(vb, sa + kPTileBytes + j * 1024u, b_vo[j], so);
+        if constexpr (kMx) {
+          const uint32_t ss = lds_sc + (uint32_t)(kt & (kPStages - 1)) * 2048u;
+          const uint32_t sso = (uint32_t)(kt >> 1) * 4u;
+          dma4(vas, ss, as_vo, sso);
+          dma4(vbs, ss + 1024u, bs_vo, sso);
+        }
       };
-      // wait until this thread's loads of stage s are in LDS, given the stages issued after it
+      // wait until this thread's loads of a stage are in LDS, given the stages issued after it
+      constexpr int kPer = kMx ? 10 : 8;   // loads per stage per thread
       auto wait_stage = [&](int after) {
-        if (after >= 2) wait_vmcnt<16>();
-        else if (after == 1) wait_vmcnt<8>();
+        if (after >= 2) wait_vmcnt<2 * kPer>();
+        else if (after == 1) wait_vmcnt<kPer>();
         else wait_vmcnt<0>();
+      };
+      auto stage_ptr = [&](int kt) { return smem + (kt & (kPStages - 1)) * kPStageBytes; };
+      auto scale_ptr = [&](int kt) {
+        return reinterpret_cast<const uint32_t*>(smem + kPStages * kPStageBytes + (kt & (kPStages - 1)) * 2048);
       };
       typename TileCore<kMx, kFc1>::Frag f0, f1;
 #pragma unroll
@@ -177,68 +171,47 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       wait_stage(min(2, kTp - 1));
       __syncthreads();
       if (3 < kTp) issue(3);
-      core.load_frag_p(f0, 0, smem, smem + kPTileBytes, wm, wn, lane);
-      for (int kt = 0; kt < kTp; ++kt) {
-        const uint8_t* sA = smem + (kt & (kPStages - 1)) * kPStageBytes;
-        core.load_frag_p(f1, 1, sA, sA + kPTileBytes, wm, wn, lane);
-        core.mma(f0);
-        core.mma_half(f1, 0);
-        if (kt + 1 < kTp) {
-          // stage kt+1: all its loads landed (own wait + barrier); stage kt's LDS reads are done
-          // in every wave, so its buffer can take stage kt+4
-          wait_stage(min(2, kTp - 2 - kt));
-          __syncthreads();
-          if (kt + 4 < kTp) issue(kt + 4);
-          const uint8_t* sN = smem + ((kt + 1) & (kPStages - 1)) * kPStageBytes;
-          core.load_frag_p(f0, 0, sN, sN + kPTileBytes, wm, wn, lane);
+      if constexpr (!kMx) {
+        core.load_frag_p(f0, 0, smem, smem + kPTileBytes, wm, wn, lane);
+        for (int kt = 0; kt < kTp; ++kt) {
+          const uint8_t* sA = stage_ptr(kt);
+          core.load_frag_p(f1, 1, sA, sA + kPTileBytes, wm, wn, lane);
+          core.mma(f0);
+          core.mma_half(f1, 0);
+          if (kt + 1 < kTp) {
+            // stage kt+1: all its loads landed (own wait + barrier); stage kt's LDS reads are done
+            // in every wave, so its buffer can take stage kt+4
+            wait_stage(min(2, kTp - 2 - kt));
+            __syncthreads();
+            if (kt + 4 < kTp) issue(kt + 4);
+            const uint8_t* sN = stage_ptr(kt + 1);
+            core.load_frag_p(f0, 0, sN, sN + kPTileBytes, wm, wn, lane);
+          }
+          core.mma_half(f1, 2);
         }
-        core.mma_half(f1, 2);
+      } else {
+        // one MFMA K step per stage: finish the first half of stage kt from registers, load stage
+        // kt+1 behind the barrier, then the second half
+        auto step = [&](int kt, typename TileCore<kMx, kFc1>::Frag& cur, typename TileCore<kMx, kFc1>::Frag& nxt) {
+          core.mma_half(cur, 0);
+          if (kt + 1 < kTp) {
+            wait_stage(min(2, kTp - 2 - kt));
+            __syncthreads();
+            if (kt + 4 < kTp) issue(kt + 4);
+            const uint8_t* sN = stage_ptr(kt + 1);
+            const uint32_t* cN = scale_ptr(kt + 1);
+            core.load_frag_pm(nxt, kt + 1, sN, sN + kPTileBytes, cN, cN + 256, wm, wn, lane);
+          }
+          core.mma_half(cur, 2);
+        };
+        core.load_frag_pm(f0, 0, smem, smem + kPTileBytes, scale_ptr(0), scale_ptr(0) + 256, wm, wn, lane);
+        // K is a multiple of 128 on this path, so the stage count is even
+        for (int kt = 0; kt < kTp; kt += 2) {
+          step(kt, f0, f1);
+          step(kt + 1, f1, f0);
+        }
       }
       __syncthreads();
-    } else {
-    const uint32_t avo0 = (uint32_t)(ldr * rowb) + ldc * 16;
-    const uint32_t astride = 32u * rowb;
-    u32x4 ra_reg[8], rb_reg[8];
-    uint32_t ras_reg = 0, rbs_reg = 0;
-
-    auto gload = [&](int kt) {
-      const uint32_t so = (uint32_t)kt * kRowBytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ra_reg[i] = bload16(ra, avo0 + i * astride, so);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rb_reg[i] = bload16(rb, bvo[i], so);
-      if (kMx) {
-        ras_reg = bload4(ras, (uint32_t)(tid * kscale_row), (uint32_t)kt * 4);
-        rbs_reg = bload4(rbs, bso, (uint32_t)kt * 4);
-      }
-    };
-    auto lstore = [&](int stage) {
-      uint8_t* sA = smem + stage * kStageBytes;
-      uint8_t* sB = sA + kTileBytes;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sA + lds_ld + i * 32 * kRowBytes) = ra_reg[i];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sB + lds_ld + i * 32 * kRowBytes) = rb_reg[i];
-      if (kMx) {
-        uint32_t* ss = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes + stage * kScaleBytes);
-        ss[tid] = ras_reg;
-        ss[256 + tid] = rbs_reg;
-      }
-    };
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < kT; ++kt) {
-      const int st = kt & 1;
-      if (kt + 1 < kT) gload(kt + 1);
-      const uint8_t* sA = smem + st * kStageBytes;
-      const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem + 2 * kStageBytes + st * kScaleBytes);
-      core.compute(sA, sA + kTileBytes, ss, ss + 256, wm, wn, lane);
-      if (kt + 1 < kT) lstore(st ^ 1);
-      __syncthreads();
-    }
-
     }
 
     // ---- epilogue, staged through LDS (the stage buffers are free after the last barrier).

@@ -158,6 +158,15 @@ __device__ __forceinline__ void dma16(const i32x4& vs, uint32_t lds, uint32_t vo
                : "memory", "m0");
 }
 
+// 4-byte variant: lane L's word lands at lds + 4 L.
+__device__ __forceinline__ void dma4(const i32x4& vs, uint32_t lds, uint32_t voff, uint32_t soff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(l), "v"(voff), "s"(vs), "s"(soff)
+               : "memory", "m0");
+}
+
 // Transpose an 8x8 block of bf16: v[r] holds 8 consecutive values of row r,
 // w[c] receives column c (8 values, one per row) -- v_perm_b32 picks the low or
 // high halves of two words at a time.
@@ -242,6 +251,36 @@ struct TileCore {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       f.b[j] = *reinterpret_cast<const bf16x8*>(sB + pswz(brow(wn, j) + r32, ch));
+  }
+
+  // MXFP8 fragments of pipelined stage s (one 64-value K step): bytes 0-15 of a lane are logical
+  // chunk g, bytes 16-31 chunk 2 + g; the scale word of each row holds the E8M0 bytes of the
+  // four 32-value blocks of stages 2*(s/2) and 2*(s/2)+1.
+  __device__ __forceinline__ void load_frag_pm(Frag& f, int s, const uint8_t* sA, const uint8_t* sB,
+                                               const uint32_t* sAs, const uint32_t* sBs, int wm, int wn,
+                                               int lane) const {
+    const int r32 = lane & 31, g = lane >> 5;
+    const int sh = 8 * (2 * (s & 1) + g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wm * 128 + i * 32 + r32;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(sA + pswz(row, g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(sA + pswz(row, 2 + g));
+      if constexpr (kMx) {
+        f.a[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        f.sa[i] = (int)(sAs[row] >> sh);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = brow(wn, j) + r32;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(sB + pswz(row, g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(sB + pswz(row, 2 + g));
+      if constexpr (kMx) {
+        f.b[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        f.sb[j] = (int)(sBs[row] >> sh);
+      }
+    }
   }
 
   // MFMAs of fragment rows i in [i0, i0 + 2)
