@@ -212,9 +212,9 @@ def bwd_leg(cfg, steps, warmup):
     }
 
 
-def cpu_baseline(inp, cfg, tokens):
-    """The fp64 oracle on the first `tokens` tokens of the workload (its full expert weights)."""
-    import numpy as np
+def cpu_baseline(inp, cfg, tokens, min_seconds=12.0, max_passes=8):
+    """The fp64 oracle on the first `tokens` tokens of the workload (its full expert weights),
+    repeated until about min_seconds of CPU work have run."""
     from oracle import mlp
     try:
         from threadpoolctl import threadpool_info
@@ -224,12 +224,16 @@ def cpu_baseline(inp, cfg, tokens):
     xs = inp.x[:tokens]
     idx = inp.topk_idx[:tokens].numpy()
     pr = inp.topk_prob[:tokens]
-    t0 = time.perf_counter()
-    mlp.forward(xs, idx, pr, inp.w1, inp.w2, cfg.precision, cfg.x_dtype)
-    dt = time.perf_counter() - t0
-    return {"value": round(tokens / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {tokens} of {cfg.T} tokens of the same workload, all {cfg.E} experts' full weights "
-                      f"(fp64 numpy per-expert loop), {dt:.1f} s"}
+    passes, dt = 0, 0.0
+    while passes < max_passes and (passes == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        mlp.forward(xs, idx, pr, inp.w1, inp.w2, cfg.precision, cfg.x_dtype)
+        dt += time.perf_counter() - t0
+        passes += 1
+    return {"value": round(passes * tokens / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} passes over the first {tokens} of {cfg.T} tokens of the same workload, all "
+                      f"{cfg.E} experts' full weights (fp64 numpy per-expert loop, {threads} BLAS threads), "
+                      f"{dt:.1f} s in total"}
 
 
 def main():

@@ -1,0 +1,130 @@
+"""The C ABI on the host: libmoe.so loads, exports every function include/moe.h
+declares, and its host-side logic (size queries, argument validation, status
+strings, phase names) answers without touching a GPU.
+
+No call here enqueues GPU work: every compute entry point is only called with
+arguments that its validation rejects before anything is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "mixture_experts_grouped_permute_amd", "libmoe.so")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n.startswith(("moe_", "mxfp8_"))))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libmoe.so is not built (run __graft_entry__.build())")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_four_operations():
+    names = _declared()
+    for n in ("moe_permute", "mxfp8_quantize", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        getattr(lib, n)
+
+
+def test_binding_lists_every_declared_symbol():
+    from mixture_experts_grouped_permute_amd import _lib
+    assert sorted(_lib.EXPORTS) == _declared()
+
+
+def test_version_status_and_phase_names(lib):
+    assert lib.moe_abi_version() == 1
+    lib.moe_status_string.restype = ctypes.c_char_p
+    for s in range(5):
+        assert lib.moe_status_string(s)
+    lib.moe_fwd_phase_name.restype = ctypes.c_char_p
+    lib.moe_bwd_phase_name.restype = ctypes.c_char_p
+    fwd = [lib.moe_fwd_phase_name(i).decode() for i in range(lib.moe_fwd_phase_count())]
+    bwd = [lib.moe_bwd_phase_name(i).decode() for i in range(lib.moe_bwd_phase_count())]
+    assert "fc1_gateup_swiglu" in fwd and "fc2_down" in fwd and "combine" in fwd
+    assert "wgrad_fc1" in bwd and "dgrad_fc2_swiglu_bwd" in bwd
+    assert lib.moe_fwd_phase_name(len(fwd)) is None and lib.moe_fwd_phase_name(-1) is None
+
+
+def test_permute_workspace_grows_with_rows(lib):
+    f = lib.moe_permute_workspace_size
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    a, b = f(4096, 2, 8), f(1 << 20, 2, 8)
+    assert 0 < a < b
+
+
+def _fwd_args(**kw):
+    from mixture_experts_grouped_permute_amd._lib import FwdArgs
+    E = kw.pop("E", 8)
+    tab = (ctypes.c_void_p * E)(*([0x1000] * E))
+    a = FwdArgs(T=4096, H=4096, I=14336, E=E, k=2, compute=1, io_dtype=1, x=0x1000, topk_idx=0x1000,
+                topk_prob=0x1000, w1=tab, w2=tab, out=0x1000, split_sizes=0x1000, offsets=0x1000,
+                row_id_map=0x1000, src_index=0x1000, prob_perm=0x1000)
+    for k_, v in kw.items():
+        setattr(a, k_, v)
+    return a, tab
+
+
+def test_fwd_workspace_query_and_validation(lib):
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE
+    lib.moe_grouped_mlp_fwd_workspace.restype = ctypes.c_size_t
+    a, tab = _fwd_args()
+    bf16 = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    a.compute = 2
+    mx = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    # MXFP8 additionally holds the E4M3 weights (1 byte per weight + scales)
+    assert mx > bf16 > 0 and mx - bf16 >= 8 * 3 * 4096 * 14336 // 2
+    # no workspace: rejected on the host before any launch
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(a), None) == MOE_ERR_WORKSPACE
+    bad = [dict(T=0), dict(k=9), dict(E=0), dict(E=300), dict(x=0), dict(compute=7), dict(io_dtype=2),
+           dict(row_id_map=0), dict(saved_gu=0x1000)]
+    for kw in bad:
+        b, tb = _fwd_args(**kw)
+        assert lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(b)) == 0, kw
+        assert lib.moe_grouped_mlp_fwd(ctypes.byref(b), None) == MOE_ERR_INVALID_ARG, kw
+    # H not a multiple of the MXFP8 GEMM step: valid, but not implemented
+    b, tb = _fwd_args(H=4096 + 64, compute=2)
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(b), None) == MOE_ERR_UNSUPPORTED
+    # a null weight pointer in the host table
+    b, tb = _fwd_args()
+    tb[3] = None
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(b), None) == MOE_ERR_INVALID_ARG
+
+
+def test_quantize_and_permute_validation(lib):
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED
+    q = lib.mxfp8_quantize
+    q.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    p = 0x1000
+    assert q(None, 1, 64, 64, 0, None, 0, p, p, None) == MOE_ERR_INVALID_ARG
+    assert q(p, 1, 64, 48, 0, None, 0, p, p, None) == MOE_ERR_UNSUPPORTED   # cols % 32 != 0
+    assert q(p, 1, 64, 64, 2, None, 0, p, p, None) == MOE_ERR_INVALID_ARG   # no such axis
+    assert q(p, 2, 64, 64, 0, None, 0, p, p, None) == MOE_ERR_INVALID_ARG   # input already MXFP8
+    pm = lib.moe_permute
+    pm.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                   ctypes.c_size_t, ctypes.c_void_p]
+    # k > E
+    assert pm(p, 1, 16, 64, p, p, 5, 4, 1, p, None, p, p, p, p, p, p, 1 << 20, None) == MOE_ERR_INVALID_ARG
