@@ -5,7 +5,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "common.h"
 #include "kernels.h"
 

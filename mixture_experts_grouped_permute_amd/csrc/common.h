@@ -20,16 +20,29 @@ __host__ __device__ inline float bf16_to_f32(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-// Round-to-nearest-even float32 -> bf16 bits (NaN kept quiet).
+// Round-to-nearest-even float32 -> bf16 bits (NaN kept quiet).  On the device this is
+// gfx950's v_cvt_pk_bf16_f32 (round to nearest even under the default rounding mode);
+// the host keeps the integer form.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 __host__ __device__ inline uint16_t f32_to_bf16(float f) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+#else
   uint32_t u = __builtin_bit_cast(uint32_t, f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+#endif
 }
 
 __host__ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+#else
   return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+#endif
 }
 
 // ---------------------------------------------------------------------------

@@ -96,102 +96,110 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     TileCore<kMx, kFc1> core;
     core.zero();
     {
-      // ---- main loop: 4-stage direct-to-LDS pipeline, 64 bytes of K per stage (32 bf16 or
-      // 64 E4M3 values).  Thread (wave w, lane L) issues 4 DMA loads per operand per stage;
-      // load j fills the 1 KB block of rows (4w + j) * 16 + L / 4, physical chunk L % 4.
-      // MXFP8 adds one 4-byte scale load per operand per stage: lane L of wave w loads the
-      // scale word of row 64w + L covering the stage's 128-value pair of stages.
+      // ---- main loop: direct-to-LDS loads (buffer_load_dwordx4 ... lds), one 16-byte chunk per
+      // lane, each load filling a contiguous 1 KB of LDS.
       // FC1 B rows [0,128) are gate rows n0h + r, rows [128,256) up rows I + n0h + r: gate rows
       // past I only feed masked columns, up rows past 2I fall outside the range and read zero.
-      const int kTp = (int)(rowb / kPRowBytes);
-      uint32_t a_vo[4], b_vo[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = (wave * 4 + j) * 16 + (lane >> 2);
-        const uint32_t c = (uint32_t)(lane & 3) ^ (((uint32_t)r >> 2) & 3u);
-        a_vo[j] = (uint32_t)r * rowb + c * 16;
-        int64_t wr = r;
-        if (kFc1) wr = r < 128 ? ((int64_t)nt * 128 + r) : (N + (int64_t)nt * 128 + (r - 128));
-        b_vo[j] = (uint32_t)(wr * rowb) + c * 16;
-      }
+      auto b_row = [&](int r) -> int64_t {
+        return kFc1 ? (r < 128 ? ((int64_t)nt * 128 + r) : (N + (int64_t)nt * 128 + (r - 128))) : (int64_t)r;
+      };
       const i32x4 va = make_vsharp(p.a + (int64_t)row0 * rowb, (uint32_t)mrows * rowb);
       const i32x4 vb = kFc1 ? make_vsharp(wbase, (uint32_t)(2 * N * rowb))
                             : make_vsharp(wbase + (int64_t)nt * kBN * rowb,
                                           (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * rowb));
-      const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 4) * 1024u;
-      // MXFP8 scale descriptors and per-lane offsets
-      i32x4 vas = va, vbs = vb;
-      uint32_t as_vo = 0, bs_vo = 0;
-      const uint32_t lds_sc = lds_addr(smem + kPStages * kPStageBytes) + (uint32_t)wave * 256u;
-      if constexpr (kMx) {
-        const int r = wave * 64 + lane;
-        vas = make_vsharp(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
-        as_vo = (uint32_t)r * kscale_row;
-        const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
-        if (kFc1) {
-          const int64_t n0h = (int64_t)nt * 128;
-          vbs = make_vsharp(sbase, (uint32_t)(2 * N * kscale_row));
-          const int64_t wr = r < 128 ? (n0h + r) : (N + n0h + (r - 128));
-          bs_vo = (uint32_t)(wr * kscale_row);
-        } else {
-          const int64_t n0 = (int64_t)nt * kBN;
-          vbs = make_vsharp(sbase + n0 * kscale_row, (uint32_t)(min((int64_t)kBN, N - n0) * kscale_row));
-          bs_vo = (uint32_t)r * kscale_row;
+      if constexpr (!kMx) {
+        // BF16: two 64 KB stages of 128 bytes of K per row (64 values, 4 MFMA K steps), in the
+        // 128-byte-row swizzle (swz) the MFMA core reads.  Whole 128-byte rows per load keep every
+        // L2 request a full line.  Load q of wave w fills row pairs j = 4 (8w + q) + L / 16; lane
+        // L's 16-byte LDS slot s = L % 16 holds (row parity, chunk) = s ^ hs(j).
+        const int kT = (int)(rowb / kRowBytes);
+        uint32_t a_vo[8], b_vo[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int j = (wave * 8 + q) * 4 + (lane >> 4);
+          const uint32_t hs = (uint32_t)((j & 7) | ((j & 4) << 1));
+          const uint32_t sl = (uint32_t)(lane & 15) ^ hs;
+          const int r = 2 * j + (int)(sl >> 3);
+          const uint32_t c = sl & 7u;
+          a_vo[q] = (uint32_t)r * rowb + c * 16;
+          b_vo[q] = (uint32_t)(b_row(r) * rowb) + c * 16;
         }
-      }
-      auto issue = [&](int kt) {
-        const uint32_t sa = lds0 + (uint32_t)(kt & (kPStages - 1)) * kPStageBytes;
-        const uint32_t so = (uint32_t)kt * kPRowBytes;
+        const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 8) * 1024u;
+        auto issue = [&](int kt) {
+          const uint32_t sa = lds0 + (uint32_t)(kt & 1) * (uint32_t)kStageBytes;
+          const uint32_t so = (uint32_t)kt * kRowBytes;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(va, sa + j * 1024u, a_vo[j], so);
+          for (int q = 0; q < 8; ++q) dma16(va, sa + q * 1024u, a_vo[q], so);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(vb, sa + kPTileBytes + j * 1024u, b_vo[j], so);
-        if constexpr (kMx) {
+          for (int q = 0; q < 8; ++q) dma16(vb, sa + kTileBytes + q * 1024u, b_vo[q], so);
+        };
+        issue(0);
+        for (int kt = 0; kt < kT; ++kt) {
+          // stage kt landed (own loads + barrier); every wave finished reading stage kt-1, whose
+          // buffer takes stage kt+1 while stage kt is multiplied
+          wait_vmcnt<0>();
+          __syncthreads();
+          if (kt + 1 < kT) issue(kt + 1);
+          const uint8_t* sA = smem + (kt & 1) * kStageBytes;
+          core.compute(sA, sA + kTileBytes, nullptr, nullptr, wm, wn, lane);
+        }
+      } else {
+        // MXFP8: a 4-stage pipeline of 64 bytes of K per row (64 E4M3 values, one MFMA K step).
+        // Load j of wave w fills rows (4w + j) * 16 + L / 4, physical chunk L % 4 (pswz layout);
+        // one 4-byte scale load per operand per stage: lane L of wave w loads the scale word of
+        // row 64w + L covering the stage's 128-value pair of stages.
+        const int kTp = (int)(rowb / kPRowBytes);
+        uint32_t a_vo[4], b_vo[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = (wave * 4 + j) * 16 + (lane >> 2);
+          const uint32_t c = (uint32_t)(lane & 3) ^ (((uint32_t)r >> 2) & 3u);
+          a_vo[j] = (uint32_t)r * rowb + c * 16;
+          b_vo[j] = (uint32_t)(b_row(r) * rowb) + c * 16;
+        }
+        const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 4) * 1024u;
+        const uint32_t lds_sc = lds_addr(smem + kPStages * kPStageBytes) + (uint32_t)wave * 256u;
+        const int r = wave * 64 + lane;
+        const i32x4 vas = make_vsharp(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
+        const uint32_t as_vo = (uint32_t)r * kscale_row;
+        const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
+        const i32x4 vbs = kFc1 ? make_vsharp(sbase, (uint32_t)(2 * N * kscale_row))
+                               : make_vsharp(sbase + (int64_t)nt * kBN * kscale_row,
+                                             (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * kscale_row));
+        const uint32_t bs_vo = (uint32_t)(b_row(r) * kscale_row);
+        auto issue = [&](int kt) {
+          const uint32_t sa = lds0 + (uint32_t)(kt & (kPStages - 1)) * kPStageBytes;
+          const uint32_t so = (uint32_t)kt * kPRowBytes;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dma16(va, sa + j * 1024u, a_vo[j], so);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dma16(vb, sa + kPTileBytes + j * 1024u, b_vo[j], so);
           const uint32_t ss = lds_sc + (uint32_t)(kt & (kPStages - 1)) * 2048u;
           const uint32_t sso = (uint32_t)(kt >> 1) * 4u;
           dma4(vas, ss, as_vo, sso);
           dma4(vbs, ss + 1024u, bs_vo, sso);
-        }
-      };
-      // wait until this thread's loads of a stage are in LDS, given the stages issued after it
-      constexpr int kPer = kMx ? 10 : 8;   // loads per stage per thread
-      auto wait_stage = [&](int after) {
-        if (after >= 2) wait_vmcnt<2 * kPer>();
-        else if (after == 1) wait_vmcnt<kPer>();
-        else wait_vmcnt<0>();
-      };
-      auto stage_ptr = [&](int kt) { return smem + (kt & (kPStages - 1)) * kPStageBytes; };
-      auto scale_ptr = [&](int kt) {
-        return reinterpret_cast<const uint32_t*>(smem + kPStages * kPStageBytes + (kt & (kPStages - 1)) * 2048);
-      };
-      typename TileCore<kMx, kFc1>::Frag f0, f1;
+        };
+        // wait until this thread's loads of a stage are in LDS, given the stages issued after it
+        constexpr int kPer = 10;   // loads per stage per thread
+        auto wait_stage = [&](int after) {
+          if (after >= 2) wait_vmcnt<2 * kPer>();
+          else if (after == 1) wait_vmcnt<kPer>();
+          else wait_vmcnt<0>();
+        };
+        auto stage_ptr = [&](int kt) { return smem + (kt & (kPStages - 1)) * kPStageBytes; };
+        auto scale_ptr = [&](int kt) {
+          return reinterpret_cast<const uint32_t*>(smem + kPStages * kPStageBytes + (kt & (kPStages - 1)) * 2048);
+        };
+        typename TileCore<kMx, kFc1>::Frag f0, f1;
 #pragma unroll
-      for (int s = 0; s < 3; ++s)
-        if (s < kTp) issue(s);
-      wait_stage(min(2, kTp - 1));
-      __syncthreads();
-      if (3 < kTp) issue(3);
-      if constexpr (!kMx) {
-        core.load_frag_p(f0, 0, smem, smem + kPTileBytes, wm, wn, lane);
-        for (int kt = 0; kt < kTp; ++kt) {
-          const uint8_t* sA = stage_ptr(kt);
-          core.load_frag_p(f1, 1, sA, sA + kPTileBytes, wm, wn, lane);
-          core.mma(f0);
-          core.mma_half(f1, 0);
-          if (kt + 1 < kTp) {
-            // stage kt+1: all its loads landed (own wait + barrier); stage kt's LDS reads are done
-            // in every wave, so its buffer can take stage kt+4
-            wait_stage(min(2, kTp - 2 - kt));
-            __syncthreads();
-            if (kt + 4 < kTp) issue(kt + 4);
-            const uint8_t* sN = stage_ptr(kt + 1);
-            core.load_frag_p(f0, 0, sN, sN + kPTileBytes, wm, wn, lane);
-          }
-          core.mma_half(f1, 2);
-        }
-      } else {
+        for (int s = 0; s < 3; ++s)
+          if (s < kTp) issue(s);
+        wait_stage(min(2, kTp - 1));
+        __syncthreads();
+        if (3 < kTp) issue(3);
         // one MFMA K step per stage: finish the first half of stage kt from registers, load stage
-        // kt+1 behind the barrier, then the second half
+        // kt+1 behind the barrier (its loads landed; stage kt's buffer is free in every wave and
+        // takes stage kt+4), then the second half
         auto step = [&](int kt, typename TileCore<kMx, kFc1>::Frag& cur, typename TileCore<kMx, kFc1>::Frag& nxt) {
           core.mma_half(cur, 0);
           if (kt + 1 < kTp) {
@@ -223,6 +231,37 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     if constexpr (kFc1) {
       const int64_t I = N;
       const int64_t n0h = (int64_t)nt * 128;
+      if (p.save_gu) {
+        // training: the gate-up output as bf16, staged as a [256][256] tile (gate columns
+        // [0,128), up columns [128,256)) and stored as 128-byte row segments
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + r32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int mb = wm * 128 + g4 + (r & 3);
+              const uint32_t off = epi_off(mb, n >> 3) + (n & 7) * 2 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);
+              *reinterpret_cast<uint16_t*>(smem + off) = f32_to_bf16(core.acc[i][j][r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = q * 256 + etid;
+          const int m = u >> 2, b = u & 3;
+          const int64_t col = n0h + (b & 1) * 64;
+          if (m < mrows && col < I) {
+            uint16_t* dst = p.save_gu + (int64_t)(row0 + m) * 2 * I + (b >> 1) * I + col;
+            u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off(m, b * 8 + c));
+          }
+        }
+        __syncthreads();
+      }
       // (A) silu(g) * u per element, fp32, into a rotated [256][128] LDS tile
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -231,13 +270,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           const int n = wn * 64 + jj * 32 + r32;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int m = wm * 128 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
             const float gv = core.acc[i][jj][r], uv = core.acc[i][jj + 2][r];
-            if (p.save_gu && m < mrows && n0h + n < I) {
-              const int64_t grow = row0 + m;
-              p.save_gu[grow * 2 * I + n0h + n] = f32_to_bf16(gv);
-              p.save_gu[grow * 2 * I + I + n0h + n] = f32_to_bf16(uv);
-            }
             // m & 7 and the chunk rotation depend only on (lane, r & 3); i and r >> 2 add constants
             const int mb = wm * 128 + g4 + (r & 3);
             const uint32_t off = epi_off(mb, n >> 2) + (n & 3) * 4 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);

@@ -334,7 +334,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
                 const uint32_t gwd = gw[x >> 1], uwd = uw[x >> 1];
                 const float g = bf16_to_f32((uint16_t)((x & 1) ? (gwd >> 16) : (gwd & 0xFFFF)));
                 const float uu = bf16_to_f32((uint16_t)((x & 1) ? (uwd >> 16) : (uwd & 0xFFFF)));
-                const float s = __frcp_rn(1.0f + __expf(-g));
+                const float s = sigmoid_f(g);
                 const float sl = g * s;
                 part += dh * (sl * uu);
                 const float da = dh * pr;

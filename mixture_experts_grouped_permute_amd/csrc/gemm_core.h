@@ -87,7 +87,9 @@ __device__ __forceinline__ int find_expert(const Sched& s, int E, int t) {
   return lo;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g * __frcp_rn(1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g) with the hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32, ~1 ulp each)
+__device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
+__device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
 // Same rotation for a 1024-byte-per-row tile (c16 in 0..63).
 __device__ __forceinline__ uint32_t epi_off_wide(int m, int c16) {
