@@ -101,9 +101,21 @@ __host__ __device__ inline uint32_t mx_e4m3_code(float v, int s) {
 }
 
 // 4-byte pack of the codes of v[0..3] with exponent s.
+// Device: q = v * 2^-s is exact (|q| < 2^9; anything that underflows fp32 rounds to a signed
+// zero in E4M3 anyway), clamping q to +-448 is exactly the saturation rule, and gfx950's
+// v_cvt_pk_fp8_f32 then rounds to the nearest E4M3FN value, ties to even, keeping the sign of
+// zero -- the same code as mx_e4m3_code, at two values per instruction.
 __host__ __device__ inline uint32_t mx_pack4(float a, float b, float c, float d, int s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const float m = __builtin_bit_cast(float, (uint32_t)(127 - s) << 23);   // 2^-s, s in [-127, 119]
+  auto q = [m](float v) { return __builtin_amdgcn_fmed3f(v * m, -448.0f, 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(a), q(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(q(c), q(d), w, true);
+  return (uint32_t)w;
+#else
   return mx_e4m3_code(a, s) | (mx_e4m3_code(b, s) << 8) | (mx_e4m3_code(c, s) << 16) |
          (mx_e4m3_code(d, s) << 24);
+#endif
 }
 
 // ---------------------------------------------------------------------------
