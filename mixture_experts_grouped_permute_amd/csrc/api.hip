@@ -73,6 +73,7 @@ struct FwdPlan {
   void* h_op;          // bf16 [R,I] or E4M3 [R,I]
   uint8_t* h_sc;       // [R,I/32]
   void* z;             // [R,H] io dtype
+  float* part;         // FC2 split-tile partials
   uint8_t* w1q; uint8_t* w1s; uint8_t* w2q; uint8_t* w2s;
   size_t bytes;
 };
@@ -100,6 +101,7 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
     else p.h_op = a->saved_h;
   }
   p.z = c.take((size_t)(R * H) * io_size(a->io_dtype));
+  p.part = reinterpret_cast<float*>(c.take(kFc2PartBytes));
   p.bytes = c.used;
   return p;
 }
@@ -348,6 +350,7 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
   g2.E = E;
   g2.split_sizes = a->split_sizes;
   g2.out = p.z;
+  g2.part = p.part;
   g2.out_f32 = x_f32;
   HIP_TRY(launch_fc2(g2, mx, st));
   MOE_CHECK(mark(6), MOE_ERR_HIP);

@@ -46,6 +46,8 @@ struct FwdKArgs {
   uint16_t* save_gu;
   uint16_t* save_h;
   int out_f32;
+  float* part;               // split tiles' fp32 partial accumulators, kGemmGrid x 64K floats
+  int split;                 // 0: every tile; 1: tiles before the split ones; 2: the split parts
   const uint8_t* w[kMaxExperts];
 };
 
@@ -60,6 +62,20 @@ __device__ __forceinline__ const uint8_t* kernarg_table(int e) {
   (void)e;
   return nullptr;
 #endif
+}
+
+// Split of the last round: tiles [full, total) are split into S parts along K (S = 1: none).
+__device__ __forceinline__ void split_policy(int total, int G, int kU, int& full, int& S) {
+  const int rem = total % G;
+  full = total;
+  S = 1;
+  if (rem > 0) {
+    const int sk = min(G / rem, kU / kMinSplitUnits);
+    if (sk >= 2) {
+      S = sk;
+      full = total - rem;
+    }
+  }
 }
 
 template <bool kMx, bool kFc1, bool kOutF32>
@@ -79,16 +95,33 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   const int esz = kMx ? 1 : 2;
   const uint32_t rowb = (uint32_t)(K * esz);           // bytes per operand row
   const uint32_t kscale_row = (uint32_t)(K / 32);      // scale bytes per row
+  const int kU = (int)(rowb / 128);                    // K units of 128 bytes
+
+  // Load balance of the last round: with `total` tiles over G workgroups, the last round holds
+  // rem = total % G tiles and would leave G - rem workgroups idle for a whole tile.  FC2 splits
+  // each of those rem tiles into S parts along K (S = G / rem, at least kMinSplitUnits K units
+  // per part): pass 1 runs tiles [0, full), pass 2 (the fp32-output instance) runs the rem * S
+  // parts and writes their fp32 tiles to p.part, and fc2_fixup_kernel sums the S partials of
+  // each tile in part order -- deterministic -- into the output.  split = 0: all tiles, one pass.
+  int full = total, S = 1;
+  if (p.split) split_policy(total, G, kU, full, S);
+  const int lo = p.split == 2 ? full : 0;
+  const int hi = p.split == 0 ? total : (p.split == 1 ? full : (S > 1 ? full + (total - full) * S : full));
 
   for (int round = 0;; ++round) {
-    const int t = round * G + xcd * per + slot;
-    if (t >= total) break;
+    const int t = lo + round * G + xcd * per + slot;
+    if (t >= hi) break;
+    int tile = t, part = -1;
+    if (kOutF32 && p.split == 2) {
+      tile = full + (t - full) / S;
+      part = (t - full) % S;
+    }
     // the tile decode is uniform across the workgroup; readfirstlane makes it scalar so the
     // buffer descriptors built from it live in SGPRs
-    const int e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, t));
+    const int e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, tile));
     const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
     const int nM = (Me + kBM - 1) / kBM;
-    const int local = t - __builtin_amdgcn_readfirstlane(sched.tile[e]);
+    const int local = tile - __builtin_amdgcn_readfirstlane(sched.tile[e]);
     const int mt = local % nM, nt = local / nM;
     const int row0 = __builtin_amdgcn_readfirstlane(sched.off[e]) + mt * kBM;   // first permuted row of the tile
     const int mrows = min(kBM, Me - mt * kBM);
@@ -96,6 +129,9 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     TileCore<kMx, kFc1> core;
     core.zero();
     {
+      // K units [u0, u1) of this work item (all of K unless the tile is split)
+      const int u0 = part < 0 ? 0 : part * kU / S;
+      const int u1 = part < 0 ? kU : (part + 1) * kU / S;
       // ---- main loop: direct-to-LDS loads (buffer_load_dwordx4 ... lds), one 16-byte chunk per
       // lane, each load filling a contiguous 1 KB of LDS.
       // FC1 B rows [0,128) are gate rows n0h + r, rows [128,256) up rows I + n0h + r: gate rows
@@ -112,7 +148,6 @@ void fwd_gemm_kernel(const FwdKArgs p) {
         // 128-byte-row swizzle (swz) the MFMA core reads.  Whole 128-byte rows per load keep every
         // L2 request a full line.  Load q of wave w fills row pairs j = 4 (8w + q) + L / 16; lane
         // L's 16-byte LDS slot s = L % 16 holds (row parity, chunk) = s ^ hs(j).
-        const int kT = (int)(rowb / kRowBytes);
         uint32_t a_vo[8], b_vo[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -133,13 +168,13 @@ void fwd_gemm_kernel(const FwdKArgs p) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) dma16(vb, sa + kTileBytes + q * 1024u, b_vo[q], so);
         };
-        issue(0);
-        for (int kt = 0; kt < kT; ++kt) {
+        issue(u0);
+        for (int kt = u0; kt < u1; ++kt) {
           // stage kt landed (own loads + barrier); every wave finished reading stage kt-1, whose
           // buffer takes stage kt+1 while stage kt is multiplied
           wait_vmcnt<0>();
           __syncthreads();
-          if (kt + 1 < kT) issue(kt + 1);
+          if (kt + 1 < u1) issue(kt + 1);
           const uint8_t* sA = smem + (kt & 1) * kStageBytes;
           core.compute(sA, sA + kTileBytes, nullptr, nullptr, wm, wn, lane);
         }
@@ -148,7 +183,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
         // Load j of wave w fills rows (4w + j) * 16 + L / 4, physical chunk L % 4 (pswz layout);
         // one 4-byte scale load per operand per stage: lane L of wave w loads the scale word of
         // row 64w + L covering the stage's 128-value pair of stages.
-        const int kTp = (int)(rowb / kPRowBytes);
+        const int s0 = 2 * u0, s1 = 2 * u1;   // stages [s0, s1); s0 is even
         uint32_t a_vo[4], b_vo[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -193,28 +228,29 @@ void fwd_gemm_kernel(const FwdKArgs p) {
         typename TileCore<kMx, kFc1>::Frag f0, f1;
 #pragma unroll
         for (int s = 0; s < 3; ++s)
-          if (s < kTp) issue(s);
-        wait_stage(min(2, kTp - 1));
+          if (s0 + s < s1) issue(s0 + s);
+        wait_stage(min(2, s1 - s0 - 1));
         __syncthreads();
-        if (3 < kTp) issue(3);
+        if (s0 + 3 < s1) issue(s0 + 3);
         // one MFMA K step per stage: finish the first half of stage kt from registers, load stage
         // kt+1 behind the barrier (its loads landed; stage kt's buffer is free in every wave and
         // takes stage kt+4), then the second half
         auto step = [&](int kt, typename TileCore<kMx, kFc1>::Frag& cur, typename TileCore<kMx, kFc1>::Frag& nxt) {
           core.mma_half(cur, 0);
-          if (kt + 1 < kTp) {
-            wait_stage(min(2, kTp - 2 - kt));
+          if (kt + 1 < s1) {
+            wait_stage(min(2, s1 - 2 - kt));
             __syncthreads();
-            if (kt + 4 < kTp) issue(kt + 4);
+            if (kt + 4 < s1) issue(kt + 4);
             const uint8_t* sN = stage_ptr(kt + 1);
             const uint32_t* cN = scale_ptr(kt + 1);
             core.load_frag_pm(nxt, kt + 1, sN, sN + kPTileBytes, cN, cN + 256, wm, wn, lane);
           }
           core.mma_half(cur, 2);
         };
-        core.load_frag_pm(f0, 0, smem, smem + kPTileBytes, scale_ptr(0), scale_ptr(0) + 256, wm, wn, lane);
-        // K is a multiple of 128 on this path, so the stage count is even
-        for (int kt = 0; kt < kTp; kt += 2) {
+        core.load_frag_pm(f0, s0, stage_ptr(s0), stage_ptr(s0) + kPTileBytes, scale_ptr(s0), scale_ptr(s0) + 256,
+                          wm, wn, lane);
+        // K units are 128 values, so the stage count is even
+        for (int kt = s0; kt < s1; kt += 2) {
           step(kt, f0, f1);
           step(kt + 1, f1, f0);
         }
@@ -324,7 +360,15 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       __syncthreads();
     } else {
       const int64_t n0 = (int64_t)nt * kBN;
+      // a split part stores its whole fp32 tile, row-major [256][256], to its slot of p.part;
+      // fc2_fixup_kernel sums the parts
       if constexpr (kOutF32) {
+        const bool sp = part >= 0;
+        float* const fdst = sp ? p.part + (size_t)(t - full) * 65536 : reinterpret_cast<float*>(p.out);
+        const int64_t fld = sp ? 256 : N;
+        const int64_t frow0 = sp ? 0 : row0, fcol0 = sp ? 0 : n0;
+        const int fmrows = sp ? kBM : mrows;
+        const int64_t fN = sp ? 256 : N;
         // fp32 output: two passes of 128 rows (a [128][256] fp32 tile is 128 KB)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -349,9 +393,9 @@ void fwd_gemm_kernel(const FwdKArgs p) {
             const int u = q * 256 + etid;
             const int ml = u >> 2, b = u & 3;     // 64-column block b of local row ml
             const int m = half * 128 + ml;
-            const int64_t col = n0 + b * 64;
-            if (m < mrows && col < N) {
-              u32x4* d = reinterpret_cast<u32x4*>(reinterpret_cast<float*>(p.out) + (int64_t)(row0 + m) * N + col);
+            const int64_t col = fcol0 + b * 64;
+            if (m < fmrows && col < fN) {
+              u32x4* d = reinterpret_cast<u32x4*>(fdst + (frow0 + m) * fld + col);
 #pragma unroll
               for (int c = 0; c < 16; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off_wide(ml, b * 16 + c));
             }
@@ -393,6 +437,57 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   }
 }
 
+// Finishes the split tiles of an FC2 launch: the S row-major [256][256] fp32 partials of tile
+// full + blockIdx.x are summed in part order and stored to z (bf16 or fp32).  Thread tid owns
+// 8 consecutive columns of rows 32 blockIdx.y + tid / 32 + 8 q.
+template <bool kOutF32>
+__global__ __launch_bounds__(256) void fc2_fixup_kernel(const FwdKArgs p, int kU) {
+  __shared__ Sched sched;
+  const int E = p.E;
+  build_sched(sched, p.split_sizes, E, p.nN);
+  const int total = sched.tile[E];
+  int full, S;
+  split_policy(total, gridDim.x, kU, full, S);
+  const int b = blockIdx.x;
+  if (S < 2 || full + b >= total) return;
+  const int tile = full + b;
+  const int e = find_expert(sched, E, tile);
+  const int Me = sched.cnt[e];
+  const int nM = (Me + kBM - 1) / kBM;
+  const int local = tile - sched.tile[e];
+  const int mt = local % nM, nt = local / nM;
+  const int row0 = sched.off[e] + mt * kBM;
+  const int mrows = min(kBM, Me - mt * kBM);
+  const int64_t N = p.N, n0 = (int64_t)nt * kBN;
+  const int c = (threadIdx.x & 31) * 8;
+  const float* src = p.part + (size_t)b * S * 65536;
+  // blockIdx.y takes rows [32 y, 32 y + 32) of the tile
+  const int mend = min(mrows, (int)(blockIdx.y + 1) * 32);
+  for (int m = blockIdx.y * 32 + (threadIdx.x >> 5); m < mend; m += 8) {
+    if (n0 + c >= N) continue;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < S; ++q) {
+      const f32x4* s4 = reinterpret_cast<const f32x4*>(src + (size_t)q * 65536 + m * 256 + c);
+      const f32x4 x0 = s4[0], x1 = s4[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += x0[i];
+        acc[4 + i] += x1[i];
+      }
+    }
+    const int64_t o = (int64_t)(row0 + m) * N + n0 + c;
+    if (kOutF32) {
+      f32x4* d = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + o);
+      d[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      d[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    } else {
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + o) =
+          u32x4{pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]), pack_bf16x2(acc[4], acc[5]),
+                pack_bf16x2(acc[6], acc[7])};
+    }
+  }
+}
+
 FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
   FwdKArgs k{};
   k.a = reinterpret_cast<const uint8_t*>(g.a);
@@ -428,6 +523,12 @@ hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
 
 hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   FwdKArgs k = make_fwd_args(g, mx, false);
+  k.part = g.part;
+  // a split needs at least 2 parts of kMinSplitUnits K units each
+  const int kU = (int)(g.K * (mx ? 1 : 2) / 128);
+  const bool split = g.part != nullptr && kU / kMinSplitUnits >= 2;
+  // pass 1 (or the only pass): the output-dtype instance
+  k.split = split ? 1 : 0;
   if (g.out_f32) {
     if (mx) fwd_gemm_kernel<true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
     else fwd_gemm_kernel<false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
@@ -435,6 +536,17 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
     if (mx) fwd_gemm_kernel<true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
     else fwd_gemm_kernel<false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
   }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || !split) return err;
+  // pass 2: the split parts (whether there are any is decided on the device), then the fixup
+  k.split = 2;
+  if (mx) fwd_gemm_kernel<true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else fwd_gemm_kernel<false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const dim3 fgrid(kGemmGrid, kBM / 32);
+  if (g.out_f32) fc2_fixup_kernel<true><<<fgrid, 256, 0, st>>>(k, kU);
+  else fc2_fixup_kernel<false><<<fgrid, 256, 0, st>>>(k, kU);
   return hipGetLastError();
 }
 

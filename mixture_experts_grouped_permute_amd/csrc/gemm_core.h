@@ -115,6 +115,9 @@ __device__ __forceinline__ uint32_t epi_off(int m, int c16) {
 // side: physical chunk p of row r holds logical chunk p ^ ((r >> 2) & 3).  Four rows share a
 // 256-byte bank line, so 16 consecutive rows read at one logical chunk cover all sixteen
 // 16-byte bank groups.
+// K units of 128 bytes per part of a split tile, at least: a split costs two short extra launches,
+// so it only pays for long tiles
+constexpr int kMinSplitUnits = 16;
 constexpr int kPStages = 4;
 constexpr int kPRowBytes = 64;
 constexpr int kPTileBytes = 256 * kPRowBytes;     // 16 KB

@@ -59,7 +59,10 @@ struct FwdGemm {
   uint16_t* save_gu;                 // FC1 training: [R, 2I] bf16
   uint16_t* save_h;                  // FC1 MXFP8 training: [R, I] bf16 h
   bool out_f32;                      // FC2
+  float* part;                       // FC2: kGemmGrid x 65536 fp32 for split tiles (nullptr: no split)
 };
+// Workspace of the FC2 split-tile partials (bytes).
+constexpr size_t kFc2PartBytes = (size_t)kGemmGrid * 65536 * sizeof(float);
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st);
 hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st);
 

@@ -62,6 +62,30 @@ def test_forward_matches_oracle(name, cfg, counts, compute):
 
 
 @gpu
+@pytest.mark.parametrize("compute", ["bf16", "mxfp8"])
+def test_forward_split_last_round(compute):
+    """Down-projection tiles of the last, partly filled round are split along K and summed by
+    the fixup pass: 24 M-blocks x 12 N-tiles = 288 tiles over 256 workgroups, the 32 tiles of
+    that round all belong to the last expert.  The oracle runs experts 3 and 7 (tokens routed
+    to both are compared) -- every expert's arithmetic is the same."""
+    m = need_gpu()
+    counts = [600, 700, 768, 514, 640, 520, 700, 600]     # 3 M-blocks of 256 rows each
+    cfg = cfg_small(T=sum(counts) // 2, H=3072, I=4096, E=8, k=2)
+    log(f"fwd split-tail {compute} T={cfg.T} H={cfg.H} I={cfg.I}")
+    inp = _inputs(cfg, counts)
+    out, ctx = _run(m, inp, compute)
+    idx = inp.topk_idx.numpy()
+    experts = (3, 7)
+    rows = np.all(np.isin(idx, experts), axis=1)
+    assert rows.sum() >= 16
+    ref = mlp.forward(inp.x, idx, inp.topk_prob, inp.w1, inp.w2, compute, cfg.x_dtype, experts=experts)
+    err = mlp.normwise_rel_err(to_np(out)[rows], ref.out[rows])
+    tol = BF16_TOL if compute == "bf16" else MXFP8_TOL
+    log(f"  {rows.sum()} tokens, normwise err {err:.3e} (tol {tol})")
+    assert err < tol
+
+
+@gpu
 def test_forward_deterministic():
     m = need_gpu()
     log("fwd determinism")
