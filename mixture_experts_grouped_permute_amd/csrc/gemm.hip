@@ -81,9 +81,8 @@ __device__ __forceinline__ void split_policy(int total, int G, int kU, int& full
 template <bool kMx, bool kFc1, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
-  static_assert(kPStages * kPStageBytes == 2 * kStageBytes, "the pipeline reuses the epilogue staging space");
-  // 4 pipeline stages (the epilogue reuses them), plus the MXFP8 scale ring (4 x 2 KB)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kPStages * kPStageBytes + (kMx ? kPStages * 2048 : 16)];
+  // 2 pipeline stages (the epilogue reuses them), plus the MXFP8 scale words (2 x 2 KB)
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * 2048 : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -143,11 +142,13 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const i32x4 vb = kFc1 ? make_vsharp(wbase, (uint32_t)(2 * N * rowb))
                             : make_vsharp(wbase + (int64_t)nt * kBN * rowb,
                                           (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * rowb));
-      if constexpr (!kMx) {
-        // BF16: two 64 KB stages of 128 bytes of K per row (64 values, 4 MFMA K steps), in the
-        // 128-byte-row swizzle (swz) the MFMA core reads.  Whole 128-byte rows per load keep every
-        // L2 request a full line.  Load q of wave w fills row pairs j = 4 (8w + q) + L / 16; lane
-        // L's 16-byte LDS slot s = L % 16 holds (row parity, chunk) = s ^ hs(j).
+      {
+        // Two 64 KB stages of 128 bytes of K per row (64 bf16 = 4 MFMA K steps, or 128 E4M3 = 2
+        // MX MFMA K steps), in the 128-byte-row swizzle (swz) the MFMA core reads.  Whole
+        // 128-byte rows per load keep every L2 request a full line.  Load q of wave w fills row
+        // pairs j = 4 (8w + q) + L / 16; lane L's 16-byte LDS slot s = L % 16 holds (row parity,
+        // chunk) = s ^ hs(j).  MXFP8 adds one 4-byte load per operand per stage: the E8M0 scales
+        // of the stage's four 32-value blocks of row 64w + L.
         uint32_t a_vo[8], b_vo[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -160,6 +161,19 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           b_vo[q] = (uint32_t)(b_row(r) * rowb) + c * 16;
         }
         const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 8) * 1024u;
+        const uint32_t lds_sc = lds_addr(smem + 2 * kStageBytes) + (uint32_t)wave * 256u;
+        i32x4 vas = va, vbs = vb;
+        uint32_t as_vo = 0, bs_vo = 0;
+        if constexpr (kMx) {
+          const int r = wave * 64 + lane;
+          vas = make_vsharp(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
+          as_vo = (uint32_t)r * kscale_row;
+          const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
+          vbs = kFc1 ? make_vsharp(sbase, (uint32_t)(2 * N * kscale_row))
+                     : make_vsharp(sbase + (int64_t)nt * kBN * kscale_row,
+                                   (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * kscale_row));
+          bs_vo = (uint32_t)(b_row(r) * kscale_row);
+        }
         auto issue = [&](int kt) {
           const uint32_t sa = lds0 + (uint32_t)(kt & 1) * (uint32_t)kStageBytes;
           const uint32_t so = (uint32_t)kt * kRowBytes;
@@ -167,6 +181,11 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           for (int q = 0; q < 8; ++q) dma16(va, sa + q * 1024u, a_vo[q], so);
 #pragma unroll
           for (int q = 0; q < 8; ++q) dma16(vb, sa + kTileBytes + q * 1024u, b_vo[q], so);
+          if constexpr (kMx) {
+            const uint32_t ss = lds_sc + (uint32_t)(kt & 1) * 2048u;
+            dma4(vas, ss, as_vo, (uint32_t)kt * 4u);
+            dma4(vbs, ss + 1024u, bs_vo, (uint32_t)kt * 4u);
+          }
         };
         issue(u0);
         for (int kt = u0; kt < u1; ++kt) {
@@ -176,83 +195,8 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           __syncthreads();
           if (kt + 1 < u1) issue(kt + 1);
           const uint8_t* sA = smem + (kt & 1) * kStageBytes;
-          core.compute(sA, sA + kTileBytes, nullptr, nullptr, wm, wn, lane);
-        }
-      } else {
-        // MXFP8: a 4-stage pipeline of 64 bytes of K per row (64 E4M3 values, one MFMA K step).
-        // Load j of wave w fills rows (4w + j) * 16 + L / 4, physical chunk L % 4 (pswz layout);
-        // one 4-byte scale load per operand per stage: lane L of wave w loads the scale word of
-        // row 64w + L covering the stage's 128-value pair of stages.
-        const int s0 = 2 * u0, s1 = 2 * u1;   // stages [s0, s1); s0 is even
-        uint32_t a_vo[4], b_vo[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = (wave * 4 + j) * 16 + (lane >> 2);
-          const uint32_t c = (uint32_t)(lane & 3) ^ (((uint32_t)r >> 2) & 3u);
-          a_vo[j] = (uint32_t)r * rowb + c * 16;
-          b_vo[j] = (uint32_t)(b_row(r) * rowb) + c * 16;
-        }
-        const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 4) * 1024u;
-        const uint32_t lds_sc = lds_addr(smem + kPStages * kPStageBytes) + (uint32_t)wave * 256u;
-        const int r = wave * 64 + lane;
-        const i32x4 vas = make_vsharp(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
-        const uint32_t as_vo = (uint32_t)r * kscale_row;
-        const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
-        const i32x4 vbs = kFc1 ? make_vsharp(sbase, (uint32_t)(2 * N * kscale_row))
-                               : make_vsharp(sbase + (int64_t)nt * kBN * kscale_row,
-                                             (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * kscale_row));
-        const uint32_t bs_vo = (uint32_t)(b_row(r) * kscale_row);
-        auto issue = [&](int kt) {
-          const uint32_t sa = lds0 + (uint32_t)(kt & (kPStages - 1)) * kPStageBytes;
-          const uint32_t so = (uint32_t)kt * kPRowBytes;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dma16(va, sa + j * 1024u, a_vo[j], so);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) dma16(vb, sa + kPTileBytes + j * 1024u, b_vo[j], so);
-          const uint32_t ss = lds_sc + (uint32_t)(kt & (kPStages - 1)) * 2048u;
-          const uint32_t sso = (uint32_t)(kt >> 1) * 4u;
-          dma4(vas, ss, as_vo, sso);
-          dma4(vbs, ss + 1024u, bs_vo, sso);
-        };
-        // wait until this thread's loads of a stage are in LDS, given the stages issued after it
-        constexpr int kPer = 10;   // loads per stage per thread
-        auto wait_stage = [&](int after) {
-          if (after >= 2) wait_vmcnt<2 * kPer>();
-          else if (after == 1) wait_vmcnt<kPer>();
-          else wait_vmcnt<0>();
-        };
-        auto stage_ptr = [&](int kt) { return smem + (kt & (kPStages - 1)) * kPStageBytes; };
-        auto scale_ptr = [&](int kt) {
-          return reinterpret_cast<const uint32_t*>(smem + kPStages * kPStageBytes + (kt & (kPStages - 1)) * 2048);
-        };
-        typename TileCore<kMx, kFc1>::Frag f0, f1;
-#pragma unroll
-        for (int s = 0; s < 3; ++s)
-          if (s0 + s < s1) issue(s0 + s);
-        wait_stage(min(2, s1 - s0 - 1));
-        __syncthreads();
-        if (s0 + 3 < s1) issue(s0 + 3);
-        // one MFMA K step per stage: finish the first half of stage kt from registers, load stage
-        // kt+1 behind the barrier (its loads landed; stage kt's buffer is free in every wave and
-        // takes stage kt+4), then the second half
-        auto step = [&](int kt, typename TileCore<kMx, kFc1>::Frag& cur, typename TileCore<kMx, kFc1>::Frag& nxt) {
-          core.mma_half(cur, 0);
-          if (kt + 1 < s1) {
-            wait_stage(min(2, s1 - 2 - kt));
-            __syncthreads();
-            if (kt + 4 < s1) issue(kt + 4);
-            const uint8_t* sN = stage_ptr(kt + 1);
-            const uint32_t* cN = scale_ptr(kt + 1);
-            core.load_frag_pm(nxt, kt + 1, sN, sN + kPTileBytes, cN, cN + 256, wm, wn, lane);
-          }
-          core.mma_half(cur, 2);
-        };
-        core.load_frag_pm(f0, s0, stage_ptr(s0), stage_ptr(s0) + kPTileBytes, scale_ptr(s0), scale_ptr(s0) + 256,
-                          wm, wn, lane);
-        // K units are 128 values, so the stage count is even
-        for (int kt = s0; kt < s1; kt += 2) {
-          step(kt, f0, f1);
-          step(kt + 1, f1, f0);
+          const uint32_t* sS = reinterpret_cast<const uint32_t*>(smem + 2 * kStageBytes + (kt & 1) * 2048);
+          core.compute(sA, sA + kTileBytes, sS, sS + 256, wm, wn, lane);
         }
       }
       __syncthreads();

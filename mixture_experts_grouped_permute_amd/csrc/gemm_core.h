@@ -109,24 +109,12 @@ __device__ __forceinline__ uint32_t epi_off(int m, int c16) {
 // ---------------------------------------------------------------------------
 // One K-pass of a 256x256 tile.  kFc1 selects the B row map (gate/up halves).
 // ---------------------------------------------------------------------------
-// ---- BF16 4-stage direct-to-LDS pipeline: each stage holds 64 bytes (32 values) of K per
-// row for the 256 A rows and 256 B rows.  The LDS-DMA loads place lane L's 16 bytes at
-// slot L of a 1 KB block (16 rows x 4 chunks), so the chunk swizzle is chosen on the global
-// side: physical chunk p of row r holds logical chunk p ^ ((r >> 2) & 3).  Four rows share a
-// 256-byte bank line, so 16 consecutive rows read at one logical chunk cover all sixteen
-// 16-byte bank groups.
+// ---- direct-to-LDS loads: the LDS-DMA form of buffer_load places lane L's 16 bytes at
+// slot L of a contiguous 1 KB block, so the swizzle of the LDS tile (swz) is applied on the
+// global side, by choosing which row and chunk each lane fetches.
 // K units of 128 bytes per part of a split tile, at least: a split costs two short extra launches,
 // so it only pays for long tiles
 constexpr int kMinSplitUnits = 16;
-constexpr int kPStages = 4;
-constexpr int kPRowBytes = 64;
-constexpr int kPTileBytes = 256 * kPRowBytes;     // 16 KB
-constexpr int kPStageBytes = 2 * kPTileBytes;     // 32 KB: A + B
-
-__device__ __forceinline__ uint32_t pswz(uint32_t row, uint32_t chunk) {
-  return row * kPRowBytes + ((chunk ^ ((row >> 2) & 3u)) << 4);
-}
-
 // s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -239,49 +227,6 @@ struct TileCore {
         const int row = brow(wn, j) + r32;
         u32x4 lo = *reinterpret_cast<const u32x4*>(sB + swz(row, c0));
         u32x4 hi = *reinterpret_cast<const u32x4*>(sB + swz(row, c1));
-        f.b[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        f.sb[j] = (int)(sBs[row] >> sh);
-      }
-    }
-  }
-
-  // BF16 fragments of MFMA K-substep kk (0..1) from a pipelined 64-byte-row stage
-  __device__ __forceinline__ void load_frag_p(Frag& f, int kk, const uint8_t* sA, const uint8_t* sB, int wm, int wn,
-                                              int lane) const {
-    const int r32 = lane & 31, g = lane >> 5;
-    const uint32_t ch = (uint32_t)(kk * 2 + g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f.a[i] = *reinterpret_cast<const bf16x8*>(sA + pswz(wm * 128 + i * 32 + r32, ch));
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      f.b[j] = *reinterpret_cast<const bf16x8*>(sB + pswz(brow(wn, j) + r32, ch));
-  }
-
-  // MXFP8 fragments of pipelined stage s (one 64-value K step): bytes 0-15 of a lane are logical
-  // chunk g, bytes 16-31 chunk 2 + g; the scale word of each row holds the E8M0 bytes of the
-  // four 32-value blocks of stages 2*(s/2) and 2*(s/2)+1.
-  __device__ __forceinline__ void load_frag_pm(Frag& f, int s, const uint8_t* sA, const uint8_t* sB,
-                                               const uint32_t* sAs, const uint32_t* sBs, int wm, int wn,
-                                               int lane) const {
-    const int r32 = lane & 31, g = lane >> 5;
-    const int sh = 8 * (2 * (s & 1) + g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + i * 32 + r32;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(sA + pswz(row, g));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(sA + pswz(row, 2 + g));
-      if constexpr (kMx) {
-        f.a[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        f.sa[i] = (int)(sAs[row] >> sh);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = brow(wn, j) + r32;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(sB + pswz(row, g));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(sB + pswz(row, 2 + g));
-      if constexpr (kMx) {
         f.b[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         f.sb[j] = (int)(sBs[row] >> sh);
       }
