@@ -137,7 +137,8 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   constexpr bool kWg = kRole == kRoleWgrad;
   constexpr bool kAMN = kWg && !kMx;   // bf16 wgrad: A is token-major
   constexpr bool kBMN = !kMx;          // bf16: B is N-contiguous (weights in dgrad, activations in wgrad)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * kScaleBytes : 16)];
+  // two stages of A + B (64 KB each; the epilogue reuses them) plus the MXFP8 scale words
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * 2048 : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -145,9 +146,6 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   build_sched(sched, p.split_sizes, E, p.nN, kWg ? (kMx ? p.pad : 1) : 0);
   const int total = kWg ? E * p.nM * p.nN : __builtin_amdgcn_readfirstlane(sched.tile[E]);
   const int G = gridDim.x, per = G >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int ldr = tid >> 3, ldc = tid & 7;                // K-major loader: rows ldr + 32 i, chunk ldc
-  const int kb = tid & 7, nb = tid >> 3;                  // MN-major loader: k-rows kb*8.., mn nb*8..
-  const uint32_t lds_ld = swz(ldr, ldc);
   constexpr int kKStep = kMx ? 128 : 64;                  // K values per LDS stage
 
   for (int round = 0;; ++round) {
@@ -182,106 +180,108 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     const int64_t n0 = (int64_t)nt * kBN;
     const int64_t m0w = (int64_t)mt * kBM;                // wgrad output row origin
 
-    // ---- operand descriptors
-    rsrc_t ra, rb, ras, rbs;
-    uint32_t av0, bv0;
-    if constexpr (kAMN) {
-      const int Me = sched.cnt[e];
-      ra = make_rsrc(p.a + koff * p.lda, (uint32_t)(Me * p.lda));
-      av0 = (uint32_t)((kb * 8) * p.lda + (m0w + nb * 8) * 2);
-    } else if constexpr (kWg) {   // MXFP8 wgrad: A^T quantized [M][Rpad], segment at koff
-      ra = make_rsrc(p.a + m0w * p.lda + koff, (uint32_t)(mrows * p.lda));
-      ras = make_rsrc(p.as + m0w * p.ldas + koff / 32, (uint32_t)(mrows * p.ldas));
-      av0 = (uint32_t)(ldr * p.lda) + ldc * 16;
+    // ---- operands: two LDS stages of A and B (32 KB each) filled by direct-to-LDS loads
+    // (buffer_load_dwordx4 ... lds, lane L's 16 bytes to slot L of a contiguous 1 KB block).
+    //   K-major operand: 256 rows x 128 bytes of K in the swz layout; load q of wave w fills row
+    //     pairs j = 4 (8w + q) + L / 16, slot s = L % 16 holding (row parity, chunk) = s ^ hs(j).
+    //   MN-major operand (bf16, K rows of 256 contiguous columns): 64 K rows x 512 bytes in the
+    //     mnswz layout; load q of wave w fills rows 2 (8w + q) + L / 32, physical chunk L % 32.
+    //     The K row advance is carried in the per-lane offset so that rows past the end of the
+    //     operand (a ragged token segment in wgrad) fall outside the descriptor and read zero.
+    //   MXFP8 operands are K-major, with one 4-byte E8M0 word per row per stage.
+    int64_t a_base_off, b_base_off;
+    uint32_t a_range, b_range;
+    const uint8_t* abase;
+    const uint8_t* bbase;
+    if constexpr (kAMN) {            // bf16 wgrad: A^T = token-major rows [tok][M]
+      const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
+      abase = p.a; a_base_off = koff * p.lda + m0w * 2; a_range = (uint32_t)max((int64_t)0, Me * p.lda - m0w * 2);
+    } else if constexpr (kWg) {      // MXFP8 wgrad: A^T quantized [M][Rpad], segment at koff
+      abase = p.a; a_base_off = m0w * p.lda + koff; a_range = (uint32_t)(mrows * p.lda);
     } else {
-      ra = make_rsrc(p.a + (int64_t)row0 * p.lda, (uint32_t)(mrows * p.lda));
-      if (kMx) ras = make_rsrc(p.as + (int64_t)row0 * p.ldas, (uint32_t)(mrows * p.ldas));
-      av0 = (uint32_t)(ldr * p.lda) + ldc * 16;
+      abase = p.a; a_base_off = (int64_t)row0 * p.lda; a_range = (uint32_t)(mrows * p.lda);
     }
     if constexpr (kBMN) {
-      if constexpr (kWg) {
-        const int Me = sched.cnt[e];
-        rb = make_rsrc(p.b + koff * p.ldb, (uint32_t)(Me * p.ldb));
-      } else {
-        rb = make_rsrc(bwd_table(e), (uint32_t)(p.K * p.ldb));
+      if constexpr (kWg) {           // bf16 wgrad: token-major rows [tok][N]
+        const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
+        bbase = p.b; b_base_off = koff * p.ldb + n0 * 2; b_range = (uint32_t)max((int64_t)0, Me * p.ldb - n0 * 2);
+      } else {                       // bf16 dgrad: W_e [K][N]
+        bbase = bwd_table(e); b_base_off = n0 * 2; b_range = (uint32_t)(p.K * p.ldb - n0 * 2);
       }
-      bv0 = (uint32_t)((kb * 8) * p.ldb + (n0 + nb * 8) * 2);
-    } else if constexpr (kWg) {   // MXFP8 wgrad: B^T quantized [N][Rpad]
-      rb = make_rsrc(p.b + n0 * p.ldb + koff, (uint32_t)(ncols * p.ldb));
-      rbs = make_rsrc(p.bs + n0 * p.ldbs + koff / 32, (uint32_t)(ncols * p.ldbs));
-      bv0 = (uint32_t)(ldr * p.ldb) + ldc * 16;
-    } else {                      // MXFP8 dgrad: W^T quantized [N][K] per expert
-      rb = make_rsrc(p.b + (int64_t)e * p.b_stride + n0 * p.ldb, (uint32_t)(ncols * p.ldb));
-      rbs = make_rsrc(p.bs + (int64_t)e * p.bs_stride + n0 * p.ldbs, (uint32_t)(ncols * p.ldbs));
-      bv0 = (uint32_t)(ldr * p.ldb) + ldc * 16;
+    } else if constexpr (kWg) {      // MXFP8 wgrad: B^T quantized [N][Rpad]
+      bbase = p.b; b_base_off = n0 * p.ldb + koff; b_range = (uint32_t)(ncols * p.ldb);
+    } else {                         // MXFP8 dgrad: W^T quantized [N][K] per expert
+      bbase = p.b + (int64_t)e * p.b_stride; b_base_off = n0 * p.ldb; b_range = (uint32_t)(ncols * p.ldb);
     }
+    const i32x4 va = make_vsharp(abase + a_base_off, a_range);
+    const i32x4 vb = make_vsharp(bbase + b_base_off, b_range);
+    uint32_t a_vo[8], b_vo[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      // K-major slot mapping
+      const int j = (wave * 8 + q) * 4 + (lane >> 4);
+      const uint32_t hs = (uint32_t)((j & 7) | ((j & 4) << 1));
+      const uint32_t sl = (uint32_t)(lane & 15) ^ hs;
+      const int rk = 2 * j + (int)(sl >> 3);
+      const uint32_t ck = sl & 7u;
+      // MN-major slot mapping
+      const int rm = 2 * (wave * 8 + q) + (lane >> 5);
+      const uint32_t cm = (uint32_t)(lane & 31) ^ (((uint32_t)rm & 3u) << 2);
+      a_vo[q] = kAMN ? (uint32_t)(rm * p.lda) + cm * 16 : (uint32_t)(rk * p.lda) + ck * 16;
+      b_vo[q] = kBMN ? (uint32_t)(rm * p.ldb) + cm * 16 : (uint32_t)(rk * p.ldb) + ck * 16;
+    }
+    // per-stage advance of the offsets: K-major along the row (128 bytes), MN-major 64 rows down
+    const uint32_t a_step = kAMN ? (uint32_t)(64 * p.lda) : (uint32_t)kRowBytes;
+    const uint32_t b_step = kBMN ? (uint32_t)(64 * p.ldb) : (uint32_t)kRowBytes;
+    const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 8) * 1024u;
+    i32x4 vas = va, vbs = vb;
+    uint32_t as_vo = 0, bs_vo = 0;
+    if constexpr (kMx) {
+      const int r = wave * 64 + lane;
+      if constexpr (kWg) {
+        vas = make_vsharp(p.as + m0w * p.ldas + koff / 32, (uint32_t)(mrows * p.ldas));
+        vbs = make_vsharp(p.bs + n0 * p.ldbs + koff / 32, (uint32_t)(ncols * p.ldbs));
+      } else {
+        vas = make_vsharp(p.as + (int64_t)row0 * p.ldas, (uint32_t)(mrows * p.ldas));
+        vbs = make_vsharp(p.bs + (int64_t)e * p.bs_stride + n0 * p.ldbs, (uint32_t)(ncols * p.ldbs));
+      }
+      as_vo = (uint32_t)(r * p.ldas);
+      bs_vo = (uint32_t)(r * p.ldbs);
+    }
+    const uint32_t lds_sc = lds_addr(smem + 2 * kStageBytes) + (uint32_t)wave * 256u;
 
     TileCore<kMx, false> core;
     core.zero();
-    u32x4 ra_reg[8], rb_reg[8];
-    uint32_t ras_reg = 0, rbs_reg = 0;
-
-    auto gload = [&](int kt) {
-      if constexpr (kAMN) {
-        const uint32_t base = av0 + (uint32_t)(kt * 64) * (uint32_t)p.lda;
+    auto issue = [&](int kt) {
+      const uint32_t sa = lds0 + (uint32_t)(kt & 1) * (uint32_t)kStageBytes;
+      const uint32_t ao = (uint32_t)kt * a_step, bo = (uint32_t)kt * b_step;
 #pragma unroll
-        for (int rr = 0; rr < 8; ++rr) ra_reg[rr] = bload16(ra, base + rr * (uint32_t)p.lda, 0);
-      } else {
+      for (int q = 0; q < 8; ++q) dma16(va, sa + q * 1024u, a_vo[q] + ao, 0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ra_reg[i] = bload16(ra, av0 + i * 32u * (uint32_t)p.lda, (uint32_t)kt * kRowBytes);
-      }
-      if constexpr (kBMN) {
-        const uint32_t base = bv0 + (uint32_t)(kt * 64) * (uint32_t)p.ldb;
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) rb_reg[rr] = bload16(rb, base + rr * (uint32_t)p.ldb, 0);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rb_reg[i] = bload16(rb, bv0 + i * 32u * (uint32_t)p.ldb, (uint32_t)kt * kRowBytes);
-      }
+      for (int q = 0; q < 8; ++q) dma16(vb, sa + kTileBytes + q * 1024u, b_vo[q] + bo, 0);
       if constexpr (kMx) {
-        ras_reg = bload4(ras, (uint32_t)(tid * p.ldas), (uint32_t)kt * 4);
-        rbs_reg = bload4(rbs, (uint32_t)(tid * p.ldbs), (uint32_t)kt * 4);
+        const uint32_t ss = lds_sc + (uint32_t)(kt & 1) * 2048u;
+        dma4(vas, ss, as_vo + (uint32_t)kt * 4u, 0);
+        dma4(vbs, ss + 1024u, bs_vo + (uint32_t)kt * 4u, 0);
       }
     };
-    auto lstore = [&](int stage) {
-      uint8_t* sA = smem + stage * kStageBytes;
-      uint8_t* sB = sA + kTileBytes;
-      if constexpr (kAMN) {
-        u32x4 w[8];
-        transpose8x8_b16(ra_reg, w);
-        store_t8(sA, w, nb, kb);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sA + lds_ld + i * 32 * kRowBytes) = ra_reg[i];
-      }
-      if constexpr (kBMN) {
-        u32x4 w[8];
-        transpose8x8_b16(rb_reg, w);
-        store_t8(sB, w, nb, kb);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(sB + lds_ld + i * 32 * kRowBytes) = rb_reg[i];
-      }
-      if constexpr (kMx) {
-        uint32_t* ss = reinterpret_cast<uint32_t*>(smem + 2 * kStageBytes + stage * kScaleBytes);
-        ss[tid] = ras_reg;
-        ss[256 + tid] = rbs_reg;
-      }
-    };
-
     if (kT > 0) {
-      gload(0);
-      lstore(0);
-      __syncthreads();
+      issue(0);
       for (int kt = 0; kt < kT; ++kt) {
-        const int st = kt & 1;
-        if (kt + 1 < kT) gload(kt + 1);
-        const uint8_t* sA = smem + st * kStageBytes;
-        const uint32_t* ss = reinterpret_cast<const uint32_t*>(smem + 2 * kStageBytes + st * kScaleBytes);
-        core.compute(sA, sA + kTileBytes, ss, ss + 256, wm, wn, lane);
-        if (kt + 1 < kT) lstore(st ^ 1);
+        // stage kt landed (own loads + barrier); every wave finished stage kt-1, whose buffer
+        // takes stage kt+1 while stage kt is multiplied
+        wait_vmcnt<0>();
         __syncthreads();
+        if (kt + 1 < kT) issue(kt + 1);
+        const uint8_t* sA = smem + (kt & 1) * kStageBytes;
+        if constexpr (kMx) {
+          const uint32_t* sS = reinterpret_cast<const uint32_t*>(smem + 2 * kStageBytes + (kt & 1) * 2048);
+          core.compute(sA, sA + kTileBytes, sS, sS + 256, wm, wn, lane);
+        } else {
+          core.template compute_x<kAMN, kBMN>(sA, sA + kTileBytes, wm, wn, lane);
+        }
       }
+      __syncthreads();
     }
 
     // ---- epilogue

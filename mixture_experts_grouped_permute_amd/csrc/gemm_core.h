@@ -109,6 +109,31 @@ __device__ __forceinline__ uint32_t epi_off(int m, int c16) {
 // ---------------------------------------------------------------------------
 // One K-pass of a 256x256 tile.  kFc1 selects the B row map (gate/up halves).
 // ---------------------------------------------------------------------------
+// ---- MN-major (N-contiguous) bf16 tiles: a stage of 64 K rows x 256 columns (512 bytes per row).
+// Row k's 16-byte chunk c is stored at chunk c ^ ((k & 3) << 2) of the row.  A transposing read
+// (ds_read_b64_tr_b16) by 16 lanes covers 4 K rows x 16 columns: source lane 4 j + q reads the
+// 8 bytes of row k0 + j at columns c0 + 4q..4q+3, and lane i of the group receives column c0 + i at
+// rows k0..k0+3.  The swizzle puts those 4 rows x 32 bytes (and the neighbouring group's) in 16
+// distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t mnswz(uint32_t k, uint32_t col) {
+  return k * 512u + ((((col >> 3) ^ ((k & 3u) << 2))) << 4) + (col & 7u) * 2u;
+}
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+// The MFMA bf16 operand of rows (M or N) rb + 0..31, K step kk (16 values) of an MN-major stage:
+// lane l holds row rb + l % 32 at K values 16 kk + 8 (l / 32) + 0..7.
+__device__ __forceinline__ bf16x8 load_mn_frag(const uint8_t* s, int rb, int kk, int lane) {
+  const int G = lane >> 4, sl = lane & 15;
+  const int col = rb + 16 * (G & 1) + 4 * (sl & 3);
+  const int k = kk * 16 + 8 * (G >> 1) + (sl >> 2);
+  typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
+  const auto base = (__attribute__((address_space(3))) uint8_t*)(s);
+  const bf16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + mnswz(k, col)));
+  const bf16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + mnswz(k + 4, col)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // ---- direct-to-LDS loads: the LDS-DMA form of buffer_load places lane L's 16 bytes at
 // slot L of a contiguous 1 KB block, so the swizzle of the LDS tile (swz) is applied on the
 // global side, by choosing which row and chunk each lane fetches.
@@ -258,6 +283,43 @@ struct TileCore {
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
                                                                         f.sb[j]);
       }
+  }
+
+  // BF16 fragments of K step kk with either operand stored MN-major (transposing reads) or
+  // K-major (swz layout).
+  template <bool kAMN, bool kBMN>
+  __device__ __forceinline__ void load_frag_x(Frag& f, int kk, const uint8_t* sA, const uint8_t* sB, int wm,
+                                              int wn, int lane) const {
+    const int r32 = lane & 31, g = lane >> 5;
+    const uint32_t ch = (uint32_t)(kk * 2 + g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (kAMN) f.a[i] = load_mn_frag(sA, wm * 128 + i * 32, kk, lane);
+      else f.a[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + i * 32 + r32, ch));
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (kBMN) f.b[j] = load_mn_frag(sB, brow(wn, j), kk, lane);
+      else f.b[j] = *reinterpret_cast<const bf16x8*>(sB + swz(brow(wn, j) + r32, ch));
+    }
+  }
+
+  template <bool kAMN, bool kBMN>
+  __device__ __forceinline__ void compute_x(const uint8_t* sA, const uint8_t* sB, int wm, int wn, int lane) {
+    static_assert(!kMx, "MN-major operands are bf16 only");
+    Frag f0, f1;
+    load_frag_x<kAMN, kBMN>(f0, 0, sA, sB, wm, wn, lane);
+#pragma unroll
+    for (int kk = 0; kk < kSub; kk += 2) {
+      load_frag_x<kAMN, kBMN>(f1, kk + 1, sA, sB, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk + 2 < kSub) load_frag_x<kAMN, kBMN>(f0, kk + 2, sA, sB, wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      mma(f1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 
   // All substeps of one LDS stage.  BF16 fragments are double-buffered in
