@@ -28,6 +28,29 @@ __device__ __forceinline__ void load8(const void* x, bool f32, int64_t off, floa
   }
 }
 
+// Quantize the 8 bf16 values of w (elements off .. off+7 of a row-major matrix whose 32-value
+// blocks are spread over 4 consecutive lanes) into q, and the block's scale byte into scales.
+__device__ __forceinline__ void quant8_bf16(const u32x4 w, uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
+                                            int64_t off) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
+    v[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+  }
+  float am = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
+  am = wave_xor_max(am, 1);
+  am = wave_xor_max(am, 2);
+  const int s = mx_shared_exp(am);
+  u32x2 o;
+  o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
+  o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
+  *reinterpret_cast<u32x2*>(q + off) = o;
+  if ((threadIdx.x & 3) == 0) scales[off / 32] = (uint8_t)(s + 127);
+}
+
 // 8-value group g of a [rows, cols] matrix: row = g / (cols/8), col = 8 * (g % (cols/8)).
 // Every lane handles groups tid, tid + stride, ...  cols % 32 == 0, so the 4 lanes of
 // one 32-value block are always consecutive lanes of one wave and step together.
@@ -80,22 +103,17 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
   uint8_t* se = scales + (int64_t)e * (n / 32);
   const int64_t groups = n / 8;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
-    const int64_t off = gi * 8;
-    float v[8];
-    load8(x, false, off, v);
-    float am = 0.f;
+  int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // four groups per lane per iteration, their loads issued together (the 4 lanes of a block
+  // take the same branch: groups and every gi of a block's first lane are multiples of 4)
+  for (; gi + 3 * stride < groups; gi += 4 * stride) {
+    u32x4 w[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-    am = wave_xor_max(am, 1);
-    am = wave_xor_max(am, 2);
-    const int s = mx_shared_exp(am);
-    u32x2 o;
-    o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
-    o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
-    *reinterpret_cast<u32x2*>(qe + off) = o;
-    if ((threadIdx.x & 3) == 0) se[off / 32] = (uint8_t)(s + 127);
+    for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4*>(x + (gi + u * stride) * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) quant8_bf16(w[u], qe, se, (gi + u * stride) * 8);
   }
+  for (; gi < groups; gi += stride) quant8_bf16(*reinterpret_cast<const u32x4*>(x + gi * 8), qe, se, gi * 8);
 }
 
 // Column-wise quantization with per-segment restart, transposed output.
