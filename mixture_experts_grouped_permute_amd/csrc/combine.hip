@@ -22,38 +22,52 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ z
   int rows[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) rows[j] = j < k ? row_id_map[t * k + j] : -1;
-  for (int64_t c = (int64_t)lane * 8; c < H; c += 512) {
-    float acc[8];
+  // bf16 input: two 512-column passes at a time, so a lane has 2 k loads in flight
+  constexpr int kU = kInF32 ? 1 : 2;
+  for (int64_t c0 = (int64_t)lane * 8; c0 < H; c0 += 512 * kU) {
+    float acc[kU][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
 #pragma unroll
     for (int j = 0; j < kMaxTopK; ++j) {
       if (j >= k || rows[j] < 0) continue;
-      const int64_t o = (int64_t)rows[j] * H + c;
-      if (kInF32) {
-        const float4* s = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + o);
-        float4 a = s[0], b = s[1];
-        acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
-        acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
-      } else {
-        u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(z) + o);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
-          acc[2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = c0 + 512 * u;
+        if (c >= H) continue;
+        const int64_t o = (int64_t)rows[j] * H + c;
+        if (kInF32) {
+          const float4* s = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(z) + o);
+          float4 a = s[0], b = s[1];
+          acc[u][0] += a.x; acc[u][1] += a.y; acc[u][2] += a.z; acc[u][3] += a.w;
+          acc[u][4] += b.x; acc[u][5] += b.y; acc[u][6] += b.z; acc[u][7] += b.w;
+        } else {
+          u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(z) + o);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[u][2 * i] += bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
+            acc[u][2 * i + 1] += bf16_to_f32((uint16_t)(w[i] >> 16));
+          }
         }
       }
     }
-    const int64_t o = t * H + c;
-    if (kOutF32) {
-      float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o);
-      d[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      d[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    } else {
-      u32x4 w;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i], acc[2 * i + 1]);
-      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + o) = w;
+    for (int u = 0; u < kU; ++u) {
+      const int64_t c = c0 + 512 * u;
+      if (c >= H) continue;
+      const int64_t o = t * H + c;
+      if (kOutF32) {
+        float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o);
+        d[0] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+        d[1] = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+      } else {
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[u][2 * i], acc[u][2 * i + 1]);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + o) = w;
+      }
     }
   }
 }

@@ -28,29 +28,6 @@ __device__ __forceinline__ void load8(const void* x, bool f32, int64_t off, floa
   }
 }
 
-// Quantize the 8 bf16 values of w (elements off .. off+7 of a row-major matrix whose 32-value
-// blocks are spread over 4 consecutive lanes) into q, and the block's scale byte into scales.
-__device__ __forceinline__ void quant8_bf16(const u32x4 w, uint8_t* __restrict__ q, uint8_t* __restrict__ scales,
-                                            int64_t off) {
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
-    v[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
-  }
-  float am = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-  am = wave_xor_max(am, 1);
-  am = wave_xor_max(am, 2);
-  const int s = mx_shared_exp(am);
-  u32x2 o;
-  o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
-  o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
-  *reinterpret_cast<u32x2*>(q + off) = o;
-  if ((threadIdx.x & 3) == 0) scales[off / 32] = (uint8_t)(s + 127);
-}
-
 // 8-value group g of a [rows, cols] matrix: row = g / (cols/8), col = 8 * (g % (cols/8)).
 // Every lane handles groups tid, tid + stride, ...  cols % 32 == 0, so the 4 lanes of
 // one 32-value block are always consecutive lanes of one wave and step together.
@@ -101,19 +78,33 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
   const int64_t n = rows * cols;
   uint8_t* qe = q + (int64_t)e * n;
   uint8_t* se = scales + (int64_t)e * (n / 32);
-  const int64_t groups = n / 8;
+  // a lane quantizes 16 consecutive values (two 16-byte loads, one 16-byte store of codes); the
+  // 2 lanes of a 32-value block are neighbours and reduce its amax with one xor shuffle
+  const int64_t groups = n / 16;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // four groups per lane per iteration, their loads issued together (the 4 lanes of a block
-  // take the same branch: groups and every gi of a block's first lane are multiples of 4)
-  for (; gi + 3 * stride < groups; gi += 4 * stride) {
-    u32x4 w[4];
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < groups; gi += stride) {
+    const int64_t off = gi * 16;
+    const u32x4 w0 = *reinterpret_cast<const u32x4*>(x + off);
+    const u32x4 w1 = *reinterpret_cast<const u32x4*>(x + off + 8);
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = *reinterpret_cast<const u32x4*>(x + (gi + u * stride) * 8);
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((uint16_t)(w0[i] & 0xFFFF));
+      v[2 * i + 1] = bf16_to_f32((uint16_t)(w0[i] >> 16));
+      v[8 + 2 * i] = bf16_to_f32((uint16_t)(w1[i] & 0xFFFF));
+      v[8 + 2 * i + 1] = bf16_to_f32((uint16_t)(w1[i] >> 16));
+    }
+    float am = 0.f;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) quant8_bf16(w[u], qe, se, (gi + u * stride) * 8);
+    for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(v[i]));
+    am = wave_xor_max(am, 1);
+    const int sx = mx_shared_exp(am);
+    u32x4 o;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) o[c] = mx_pack4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3], sx);
+    *reinterpret_cast<u32x4*>(qe + off) = o;
+    if ((threadIdx.x & 1) == 0) se[off / 32] = (uint8_t)(sx + 127);
   }
-  for (; gi < groups; gi += stride) quant8_bf16(*reinterpret_cast<const u32x4*>(x + gi * 8), qe, se, gi * 8);
 }
 
 // Column-wise quantization with per-segment restart, transposed output.
@@ -219,7 +210,7 @@ hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, in
                                    uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st) {
   WTab tab{};
   for (int e = 0; e < E; ++e) tab.w[e] = reinterpret_cast<const uint16_t*>(w[e]);
-  const int64_t groups = rows * cols / 8;
+  const int64_t groups = rows * cols / 16;
   int gx = grid_for(groups);
   int per = (2048 + E - 1) / E;                 // about 2048 workgroups over all experts
   if (gx > per) gx = per < 1 ? 1 : per;
