@@ -11,6 +11,7 @@ Modules
             per-expert-segment column-wise)
   permute   stable counting-sort permutation of (token, slot) pairs by expert
   mlp       grouped expert MLP forward and backward, per-expert loop, fp64
+  router    softmax -> top-k -> renormalise router (the fused router's oracle)
 
 Parity status: every function here is pinned by a CPU test (brute force,
 library cross-checks, closed forms or invariants); none is "parity unpinned".
