@@ -122,6 +122,36 @@ moe_status moe_permute(const void* x, int x_dtype, int64_t T, int64_t H,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_route_topk -- the top-k router ahead of the permutation (page "BioNeMo
+ * Uses Grouped Kernels and MXFP8", Figure 1: each token goes to k experts
+ * whose outputs are combined with the routing weights).
+ *
+ * logits     [T, E] in logits_dtype (MOE_F32 or MOE_BF16), device.
+ * topk_idx   [T, k] int32 out: the k largest logits of each token in
+ *            descending order, equal logits -> lower expert id first.
+ * topk_prob  [T, k] float32 out: softmax over all E experts renormalised over
+ *            the k selected (= softmax of the k selected logits), fp32.
+ * 1 <= k <= min(E, 16), E <= 256.  A token whose logits are all -inf (or
+ * NaN) is outside the contract.
+ * ------------------------------------------------------------------------ */
+moe_status moe_route_topk(const void* logits, int logits_dtype, int64_t T, int E, int k,
+                          int32_t* topk_idx, float* topk_prob, void* stream);
+
+/* ------------------------------------------------------------------------
+ * moe_route_permute -- moe_route_topk fused with moe_permute: the router
+ * kernel also writes the expert histogram the permutation's prefix sum reads,
+ * so the permutation's histogram pass over topk_idx is skipped.  Arguments as
+ * the two calls; topk_idx / topk_prob are outputs here.  workspace: at least
+ * moe_permute_workspace_size(T, k, E) bytes.
+ * ------------------------------------------------------------------------ */
+moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x, int x_dtype,
+                             int64_t T, int64_t H, int E, int k, int perm_dtype,
+                             int32_t* topk_idx, float* topk_prob, void* x_perm, uint8_t* x_perm_scales,
+                             int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                             int32_t* src_index, float* prob_perm,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_grouped_mlp_fwd -- the whole expert MLP forward:
  *   permute -> [MXFP8: quantize W1, W2] -> FC1 grouped GEMM with the
  *   ScaledSwiGLU * prob epilogue (writes h directly in the FC2 operand

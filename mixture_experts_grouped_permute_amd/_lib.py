@@ -27,6 +27,7 @@ EXPORTS = (
     "moe_grouped_mlp_fwd_workspace", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd_workspace",
     "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
+    "moe_route_topk", "moe_route_permute",
 )
 
 
@@ -110,6 +111,12 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_bwd_phase_name.argtypes = [ctypes.c_int]
     lib.moe_read_device_error.restype = ctypes.c_int
     lib.moe_read_device_error.argtypes = [_vp, _vp]
+    lib.moe_route_topk.restype = ctypes.c_int
+    lib.moe_route_topk.argtypes = [_vp, ctypes.c_int, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]
+    lib.moe_route_permute.restype = ctypes.c_int
+    lib.moe_route_permute.argtypes = [_vp, ctypes.c_int, _vp, ctypes.c_int, _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_size_t, _vp]
     if path is None:
         _lib = lib
     return lib
@@ -234,6 +241,55 @@ def moe_permute(x: Optional[torch.Tensor], topk_idx: torch.Tensor, topk_prob: Op
                          _ptr(out["offsets"]), _ptr(out["row_id_map"]), _ptr(out["src_index"]),
                          _ptr(out["prob_perm"]), ws.data_ptr(), ws.numel(), _stream(dev))
     _check(st, "moe_permute")
+    out["workspace"] = ws
+    return out
+
+
+def moe_route_topk(logits: torch.Tensor, k: int):
+    """Top-k router: returns (topk_idx int32 [T,k], topk_prob float32 [T,k])."""
+    lib = load()
+    T, E = logits.shape
+    dev = logits.device
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    prob = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _check(lib.moe_route_topk(_ptr(logits), _io(logits), T, E, k, _ptr(idx), _ptr(prob), _stream(dev)),
+           "moe_route_topk")
+    return idx, prob
+
+
+def moe_route_permute(logits: torch.Tensor, x: Optional[torch.Tensor], k: int, perm_dtype: str = "bf16"):
+    """Router fused with the permutation.  Returns moe_permute's dict plus topk_idx / topk_prob."""
+    lib = load()
+    T, E = logits.shape
+    dev = logits.device
+    R = T * k
+    out = {
+        "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+        "topk_prob": torch.empty((T, k), dtype=torch.float32, device=dev),
+        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
+        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
+        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
+        "x_perm": None, "x_perm_scales": None,
+    }
+    H = 0
+    pd = _compute(perm_dtype)
+    if x is not None:
+        H = x.shape[1]
+        if pd == MOE_BF16:
+            out["x_perm"] = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
+        else:
+            out["x_perm"] = torch.empty((R, H), dtype=torch.uint8, device=dev)
+            out["x_perm_scales"] = torch.empty((R, H // 32), dtype=torch.uint8, device=dev)
+    need = lib.moe_permute_workspace_size(T, k, E)
+    ws = _WS.get(need, dev)
+    st = lib.moe_route_permute(_ptr(logits), _io(logits), _ptr(x), _io(x) if x is not None else MOE_BF16, T, H, E, k,
+                               pd, _ptr(out["topk_idx"]), _ptr(out["topk_prob"]), _ptr(out["x_perm"]),
+                               _ptr(out["x_perm_scales"]), _ptr(out["split_sizes"]), _ptr(out["offsets"]),
+                               _ptr(out["row_id_map"]), _ptr(out["src_index"]), _ptr(out["prob_perm"]),
+                               ws.data_ptr(), ws.numel(), _stream(dev))
+    _check(st, "moe_route_permute")
     out["workspace"] = ws
     return out
 

@@ -31,17 +31,15 @@ struct Carver {
 inline bool io_ok(int d) { return d == MOE_F32 || d == MOE_BF16; }
 inline size_t io_size(int d) { return d == MOE_F32 ? 4 : 2; }
 
-int perm_blocks(int64_t R) { return (int)((R + kPermChunk - 1) / kPermChunk) + 0; }
-
 struct PermWs {
   int32_t* err;
   int32_t* block_counts;
   int32_t* block_base;
 };
 
-PermWs carve_perm(Carver& c, int64_t R, int E) {
+PermWs carve_perm(Carver& c, int64_t T, int E) {
   PermWs w;
-  const int nb = perm_blocks(R) < 1 ? 1 : perm_blocks(R);
+  const int nb = perm_blocks(T);
   w.err = reinterpret_cast<int32_t*>(c.take(kAlign));
   w.block_counts = reinterpret_cast<int32_t*>(c.take(sizeof(int32_t) * (size_t)nb * (E + 1)));
   w.block_base = reinterpret_cast<int32_t*>(c.take(sizeof(int32_t) * (size_t)nb * E));
@@ -84,7 +82,7 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
   const int64_t R = a->T * a->k, H = a->H, I = a->I;
   const int E = a->E;
   const bool mx = a->compute == MOE_MXFP8_E4M3;
-  p.perm = carve_perm(c, R, E);
+  p.perm = carve_perm(c, a->T, E);
   if (mx) {
     p.x_op = c.take((size_t)(R * H));
     p.x_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * H / 32)));
@@ -234,7 +232,7 @@ moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols
 size_t moe_permute_workspace_size(int64_t T, int k, int E) {
   if (T <= 0 || k <= 0 || E <= 0) return 0;
   Carver c(nullptr);
-  carve_perm(c, T * k, E);
+  carve_perm(c, T, E);
   return c.used;
 }
 
@@ -257,9 +255,48 @@ moe_status moe_permute(const void* x, int x_dtype, int64_t T, int64_t H, const i
   MOE_CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   Carver c(workspace);
-  PermWs w = carve_perm(c, T * k, E);
-  HIP_TRY(launch_permute_indices(topk_idx, topk_prob, T * k, E, split_sizes, offsets, row_id_map, src_index,
+  PermWs w = carve_perm(c, T, E);
+  HIP_TRY(launch_permute_indices(topk_idx, topk_prob, T, k, E, split_sizes, offsets, row_id_map, src_index,
                                  prob_perm, w.err, w.block_counts, w.block_base, st));
+  if (x_perm)
+    HIP_TRY(launch_permute_rows(x, x_dtype == MOE_F32, T, H, k, row_id_map, x_perm, x_perm_scales,
+                                perm_dtype == MOE_MXFP8_E4M3, st));
+  return MOE_OK;
+}
+
+moe_status moe_route_topk(const void* logits, int logits_dtype, int64_t T, int E, int k, int32_t* topk_idx,
+                          float* topk_prob, void* stream) {
+  moe_status s = check_common(T, 1, E, k);
+  if (s != MOE_OK) return s;
+  MOE_CHECK(logits && io_ok(logits_dtype) && topk_idx && topk_prob, MOE_ERR_INVALID_ARG);
+  HIP_TRY(launch_router(logits, logits_dtype == MOE_F32, T, E, k, topk_idx, topk_prob, nullptr,
+                        reinterpret_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x, int x_dtype, int64_t T,
+                             int64_t H, int E, int k, int perm_dtype, int32_t* topk_idx, float* topk_prob,
+                             void* x_perm, uint8_t* x_perm_scales, int32_t* split_sizes, int32_t* offsets,
+                             int32_t* row_id_map, int32_t* src_index, float* prob_perm, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  moe_status s = check_common(T, x_perm ? H : 1, E, k);
+  if (s != MOE_OK) return s;
+  MOE_CHECK(logits && io_ok(logits_dtype) && topk_idx && topk_prob, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(split_sizes && offsets && row_id_map && src_index, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(perm_dtype == MOE_BF16 || perm_dtype == MOE_MXFP8_E4M3, MOE_ERR_INVALID_ARG);
+  if (x_perm) {
+    MOE_CHECK(x && io_ok(x_dtype), MOE_ERR_INVALID_ARG);
+    MOE_CHECK(H % 32 == 0, MOE_ERR_UNSUPPORTED);
+    if (perm_dtype == MOE_MXFP8_E4M3) MOE_CHECK(x_perm_scales != nullptr, MOE_ERR_INVALID_ARG);
+  }
+  const size_t need = moe_permute_workspace_size(T, k, E);
+  MOE_CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  Carver c(workspace);
+  PermWs w = carve_perm(c, T, E);
+  HIP_TRY(launch_router(logits, logits_dtype == MOE_F32, T, E, k, topk_idx, topk_prob, w.block_counts, st));
+  HIP_TRY(launch_permute_indices(topk_idx, topk_prob, T, k, E, split_sizes, offsets, row_id_map, src_index,
+                                 prob_perm, w.err, w.block_counts, w.block_base, st, /*counts_ready=*/true));
   if (x_perm)
     HIP_TRY(launch_permute_rows(x, x_dtype == MOE_F32, T, H, k, row_id_map, x_perm, x_perm_scales,
                                 perm_dtype == MOE_MXFP8_E4M3, st));
@@ -298,7 +335,7 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
   };
 
   MOE_CHECK(mark(0), MOE_ERR_HIP);
-  HIP_TRY(launch_permute_indices(a->topk_idx, a->topk_prob, R, E, a->split_sizes, a->offsets, a->row_id_map,
+  HIP_TRY(launch_permute_indices(a->topk_idx, a->topk_prob, T, k, a->E, a->split_sizes, a->offsets, a->row_id_map,
                                  a->src_index, a->prob_perm, p.perm.err, p.perm.block_counts, p.perm.block_base,
                                  st));
   MOE_CHECK(mark(1), MOE_ERR_HIP);

@@ -5,14 +5,26 @@
 
 namespace moe {
 
-constexpr int kPermChunk = 2048;   // (token, slot) ids per histogram / scatter block
+constexpr int kPermTokens = 256;   // tokens (k (token, slot) ids each) per histogram / scatter block
 constexpr int kMaxTopK = 16;
 constexpr int kGemmGrid = 256;     // persistent GEMM workgroups: one per CU, a multiple of the 8 XCDs
 
 // ---- permutation (permute.hip)
-hipError_t launch_permute_indices(const int32_t* idx, const float* prob, int64_t R, int E, int32_t* split_sizes,
-                                  int32_t* offsets, int32_t* row_id_map, int32_t* src_index, float* prob_perm,
-                                  int32_t* err_flag, int32_t* block_counts, int32_t* block_base, hipStream_t st);
+// Number of permutation blocks (histogram chunks) for T tokens.
+inline int perm_blocks(int64_t T) {
+  const int64_t nb = (T + kPermTokens - 1) / kPermTokens;
+  return nb < 1 ? 1 : (int)nb;
+}
+// block_counts: [nb][E] per-block expert counts followed by nb "bad id" flags.  With
+// counts_ready the histogram pass is skipped (the router already wrote block_counts).
+hipError_t launch_permute_indices(const int32_t* idx, const float* prob, int64_t T, int k, int E,
+                                  int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                                  int32_t* src_index, float* prob_perm, int32_t* err_flag, int32_t* block_counts,
+                                  int32_t* block_base, hipStream_t st, bool counts_ready = false);
+// ---- fused router (router.hip): top-k of the logits [T, E] (f32 or bf16), renormalised
+// softmax weights, and (block_counts != nullptr) the permutation's per-block histogram.
+hipError_t launch_router(const void* logits, bool f32, int64_t T, int E, int k, int32_t* idx, float* prob,
+                         int32_t* block_counts, hipStream_t st);
 hipError_t launch_permute_rows(const void* x, bool x_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
                                void* out, uint8_t* out_scales, bool mx, hipStream_t st);
 

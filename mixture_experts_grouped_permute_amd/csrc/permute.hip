@@ -12,9 +12,10 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// K1: per-block expert histogram over kPermChunk consecutive (token, slot) ids.
+// K1: per-block expert histogram over the chunk of kPermTokens tokens = kPermTokens * k
+// consecutive (token, slot) ids.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ idx, int64_t R, int E,
+__global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restrict__ idx, int64_t R, int k, int E,
                                                           int32_t* __restrict__ block_counts,
                                                           int32_t* __restrict__ block_bad) {
   __shared__ int cnt[kMaxExperts];
@@ -22,9 +23,10 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
   if (threadIdx.x == 0) nbad = 0;
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
-  int64_t base = (int64_t)blockIdx.x * kPermChunk;
+  const int chunk = kPermTokens * k;
+  int64_t base = (int64_t)blockIdx.x * chunk;
   int bad = 0;
-  for (int i = threadIdx.x; i < kPermChunk; i += blockDim.x) {
+  for (int i = threadIdx.x; i < chunk; i += blockDim.x) {
     int64_t p = base + i;
     if (p < R) {
       int e = idx[p];
@@ -39,42 +41,61 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// K2: split_sizes, offsets and the per-(block, expert) base rows.  One block.
+// K2: split_sizes, offsets and the per-(block, expert) base rows.  One workgroup of 1024
+// threads: expert e's column of block counts is cut into S = 1024 / E slices, thread (e, s)
+// sums its slice, an exclusive prefix over the slices gives each slice's base, and the thread
+// then writes the running base of every block in its slice.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restrict__ block_counts,
-                                                          const int32_t* __restrict__ block_bad, int nb, int E,
-                                                          int32_t* __restrict__ err_flag,
-                                                          int32_t* __restrict__ split_sizes,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ block_base) {
+__global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ block_counts,
+                                                           const int32_t* __restrict__ block_bad, int nb, int E,
+                                                           int32_t* __restrict__ err_flag,
+                                                           int32_t* __restrict__ split_sizes,
+                                                           int32_t* __restrict__ offsets,
+                                                           int32_t* __restrict__ block_base) {
+  __shared__ int slice_sum[1024];
   __shared__ int tot[kMaxExperts];
   __shared__ int off[kMaxExperts + 1];
-  int e = threadIdx.x;
-  if (e < E) {
-    int s = 0;
-    for (int b = 0; b < nb; ++b) s += block_counts[(int64_t)b * E + e];
-    tot[e] = s;
+  __shared__ int bad;
+  const int tid = threadIdx.x;
+  const int S = 1024 / E;                 // >= 4 slices per expert (E <= 256)
+  const int e = tid / S, sl = tid % S;
+  const bool act = e < E;
+  const int per = (nb + S - 1) / S;
+  const int b0 = min(nb, sl * per), b1 = min(nb, b0 + per);
+  if (tid == 0) bad = 0;
+  int s = 0;
+  if (act)
+    for (int b = b0; b < b1; ++b) s += block_counts[(int64_t)b * E + e];
+  slice_sum[tid] = s;
+  int bd = 0;
+  for (int b = tid; b < nb; b += 1024) bd |= block_bad[b];
+  __syncthreads();
+  if (bd) atomicOr(&bad, 1);
+  int pre = 0;
+  if (act) {
+    for (int q = 0; q < sl; ++q) pre += slice_sum[e * S + q];
+    if (sl == S - 1) tot[e] = pre + s;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     int run = 0;
     for (int i = 0; i < E; ++i) { off[i] = run; run += tot[i]; }
     off[E] = run;
   }
   __syncthreads();
-  if (e < E) {
-    split_sizes[e] = tot[e];
-    offsets[e] = off[e];
-    int run = off[e];
-    for (int b = 0; b < nb; ++b) {
+  if (act) {
+    if (sl == 0) {
+      split_sizes[e] = tot[e];
+      offsets[e] = off[e];
+    }
+    int run = off[e] + pre;
+    for (int b = b0; b < b1; ++b) {
       block_base[(int64_t)b * E + e] = run;
       run += block_counts[(int64_t)b * E + e];
     }
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     offsets[E] = off[E];
-    int bad = 0;
-    for (int b = 0; b < nb; ++b) bad |= block_bad[b];
     err_flag[0] = bad;   // the flag describes this call only
   }
 }
@@ -86,7 +107,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t* __restric
 // the expert id) plus the counts of earlier waves, on top of the running count.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __restrict__ idx,
-                                                             const float* __restrict__ prob, int64_t R, int E,
+                                                             const float* __restrict__ prob, int64_t R, int k, int E,
                                                              const int32_t* __restrict__ block_base,
                                                              int32_t* __restrict__ row_id_map,
                                                              int32_t* __restrict__ src_index,
@@ -95,8 +116,8 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   __shared__ int wcnt[4][kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int e = tid; e < E; e += 256) run[e] = block_base[(int64_t)blockIdx.x * E + e];
-  int64_t base = (int64_t)blockIdx.x * kPermChunk;
-  for (int r = 0; r < kPermChunk / 256; ++r) {
+  int64_t base = (int64_t)blockIdx.x * kPermTokens * k;
+  for (int r = 0; r < k; ++r) {   // the chunk's kPermTokens * k ids in rounds of 256
     for (int i = tid; i < 4 * kMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     int64_t p = base + r * 256 + tid;
@@ -193,16 +214,16 @@ __global__ __launch_bounds__(256) void perm_rows_kernel(const void* __restrict__
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_permute_indices(const int32_t* idx, const float* prob, int64_t R, int E, int32_t* split_sizes,
-                                  int32_t* offsets, int32_t* row_id_map, int32_t* src_index, float* prob_perm,
-                                  int32_t* err_flag, int32_t* block_counts, int32_t* block_base,
-                                  hipStream_t st) {
-  int nb = (int)((R + kPermChunk - 1) / kPermChunk);
-  if (nb < 1) nb = 1;
+hipError_t launch_permute_indices(const int32_t* idx, const float* prob, int64_t T, int k, int E,
+                                  int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                                  int32_t* src_index, float* prob_perm, int32_t* err_flag, int32_t* block_counts,
+                                  int32_t* block_base, hipStream_t st, bool counts_ready) {
+  const int64_t R = T * k;
+  const int nb = perm_blocks(T);
   int32_t* block_bad = block_counts + (int64_t)nb * E;
-  perm_hist_kernel<<<nb, 256, 0, st>>>(idx, R, E, block_counts, block_bad);
-  perm_scan_kernel<<<1, 256, 0, st>>>(block_counts, block_bad, nb, E, err_flag, split_sizes, offsets, block_base);
-  perm_scatter_kernel<<<nb, 256, 0, st>>>(idx, prob, R, E, block_base, row_id_map, src_index, prob_perm);
+  if (!counts_ready) perm_hist_kernel<<<nb, 256, 0, st>>>(idx, R, k, E, block_counts, block_bad);
+  perm_scan_kernel<<<1, 1024, 0, st>>>(block_counts, block_bad, nb, E, err_flag, split_sizes, offsets, block_base);
+  perm_scatter_kernel<<<nb, 256, 0, st>>>(idx, prob, R, k, E, block_base, row_id_map, src_index, prob_perm);
   return hipGetLastError();
 }
 

@@ -6,6 +6,6 @@ weights, upstream gradients).  It holds none of the layer's arithmetic: no
 permutation, no quantization, no GEMM, no activation function.
 """
 from .configs import CONFIGS, MoEConfig, get_config
-from .generate import MoEInputs, make_inputs, route_topk
+from .generate import MoEInputs, make_inputs, make_logits, route_topk
 
-__all__ = ["CONFIGS", "MoEConfig", "get_config", "MoEInputs", "make_inputs", "route_topk"]
+__all__ = ["CONFIGS", "MoEConfig", "get_config", "MoEInputs", "make_inputs", "make_logits", "route_topk"]

@@ -122,8 +122,10 @@ def _bf16(a: np.ndarray, scale: float = 1.0) -> torch.Tensor:
     return t.to(torch.bfloat16)
 
 
-def make_routing(cfg: MoEConfig, seed: int):
-    T, E, k = cfg.T, cfg.E, cfg.k
+def make_logits(cfg: MoEConfig, seed: Optional[int] = None) -> np.ndarray:
+    """The router logits [T, E] (float64) of a workload's routing recipe."""
+    seed = cfg.seed if seed is None else seed
+    T, E = cfg.T, cfg.E
     logits = _fill(seed, "logits", T * E).reshape(T, E).astype(np.float64)
     if cfg.routing == "zipf":
         gum = _fill(seed, "gumbel", T * E, kind="gumbel").reshape(T, E).astype(np.float64)
@@ -133,7 +135,11 @@ def make_routing(cfg: MoEConfig, seed: int):
         raise ValueError(cfg.routing)
     if cfg.zero_expert is not None:
         logits[:, cfg.zero_expert] = -np.inf
-    return route_topk(logits, k)
+    return logits
+
+
+def make_routing(cfg: MoEConfig, seed: int):
+    return route_topk(make_logits(cfg, seed), cfg.k)
 
 
 def make_inputs(cfg: MoEConfig, seed: Optional[int] = None, *, topk_idx=None, topk_prob=None,
