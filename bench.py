@@ -212,6 +212,65 @@ def bwd_leg(cfg, steps, warmup):
     }
 
 
+def router_leg(cfg, steps=20, warmup=5):
+    """The fused router alone and fused with the permutation, on the workload's own logits
+    (outputs and workspace allocated once; HIP-event timing on the current stream)."""
+    import numpy as np
+    import torch
+    import mixture_experts_grouped_permute_amd as m
+    from mixture_experts_grouped_permute_amd import _lib as L
+    from moe_inputs import make_logits
+    lib = m.load()
+    dev = torch.device("cuda:0")
+    T, E, k, H = cfg.T, cfg.E, cfg.k, cfg.H
+    R = T * k
+    lg = torch.from_numpy(make_logits(cfg).astype(np.float32)).to(dev)
+    g = np.random.Generator(np.random.PCG64(cfg.seed))
+    x = torch.from_numpy(g.standard_normal((T, H), dtype=np.float32)).to(torch.bfloat16).to(dev)
+    i32 = lambda n: torch.empty(n, dtype=torch.int32, device=dev)
+    idx, prob = i32(R), torch.empty(R, dtype=torch.float32, device=dev)
+    split, offs, rid, src = i32(E), i32(E + 1), i32(R), i32(R)
+    pperm = torch.empty(R, dtype=torch.float32, device=dev)
+    mx = cfg.precision == "mxfp8"
+    xp = torch.empty((R, H), dtype=torch.uint8 if mx else torch.bfloat16, device=dev)
+    xs = torch.empty((R, H // 32), dtype=torch.uint8, device=dev) if mx else None
+    ws = torch.empty(lib.moe_permute_workspace_size(T, k, E), dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    pd = L.MOE_MXFP8_E4M3 if mx else L.MOE_BF16
+
+    def route():
+        L._check(lib.moe_route_topk(lg.data_ptr(), L.MOE_F32, T, E, k, idx.data_ptr(), prob.data_ptr(), st), "route")
+
+    def route_permute():
+        L._check(lib.moe_route_permute(lg.data_ptr(), L.MOE_F32, x.data_ptr(), L.MOE_BF16, T, H, E, k, pd,
+                                       idx.data_ptr(), prob.data_ptr(), xp.data_ptr(), L._ptr(xs), split.data_ptr(),
+                                       offs.data_ptr(), rid.data_ptr(), src.data_ptr(), pperm.data_ptr(),
+                                       ws.data_ptr(), ws.numel(), st), "route_permute")
+
+    def permute_only():
+        L._check(lib.moe_permute(x.data_ptr(), L.MOE_BF16, T, H, idx.data_ptr(), prob.data_ptr(), k, E, pd,
+                                 xp.data_ptr(), L._ptr(xs), split.data_ptr(), offs.data_ptr(), rid.data_ptr(),
+                                 src.data_ptr(), pperm.data_ptr(), ws.data_ptr(), ws.numel(), st), "permute")
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            f()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+    ms_route, ms_rp, ms_perm = timed(route), timed(route_permute), timed(permute_only)
+    route_bytes = T * E * 4 + R * 8
+    return {"route_us": round(ms_route * 1e3, 1), "route_hbm_GBs": round(route_bytes / (ms_route * 1e-3) / 1e9, 1),
+            "route_permute_us": round(ms_rp * 1e3, 1),
+            "route_then_permute_us": round((ms_route + ms_perm) * 1e3, 1)}
+
+
 def cpu_baseline(inp, cfg, tokens, min_seconds=12.0, max_passes=8):
     """The fp64 oracle on the first `tokens` tokens of the workload (its full expert weights),
     repeated until about min_seconds of CPU work have run."""
@@ -245,8 +304,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,backward",
-                    help="comma list of bf16, mxfp8, mxfp8_finegrained, backward (bf16 always runs)")
+    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,backward,router",
+                    help="comma list of bf16, mxfp8, mxfp8_finegrained, backward, router (bf16 always runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -297,6 +356,8 @@ def main():
                               f"Zipf({c.zipf_s}) routing" + (f", expert {c.zero_expert} empty" if c.zero_expert is not None else "")
                               + ", weights quantized per call")
             line[key] = lg
+    if "router" in legs:
+        line["router"] = {c.name: router_leg(c) for c in (get_config(2), get_config(5))}
     if not args.no_backward and "backward" in legs:
         torch.cuda.empty_cache()
         line["backward_bf16"] = bwd_leg(get_config(4), max(2, args.steps // 2), max(1, args.warmup // 2))

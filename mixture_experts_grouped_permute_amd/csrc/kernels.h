@@ -5,7 +5,7 @@
 
 namespace moe {
 
-constexpr int kPermTokens = 256;   // tokens (k (token, slot) ids each) per histogram / scatter block
+constexpr int kPermTokens = 64;    // tokens (k (token, slot) ids each) per histogram / scatter block
 constexpr int kMaxTopK = 16;
 constexpr int kGemmGrid = 256;     // persistent GEMM workgroups: one per CU, a multiple of the 8 XCDs
 

@@ -116,13 +116,15 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
   __shared__ int wcnt[4][kMaxExperts];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   for (int e = tid; e < E; e += 256) run[e] = block_base[(int64_t)blockIdx.x * E + e];
-  int64_t base = (int64_t)blockIdx.x * kPermTokens * k;
-  for (int r = 0; r < k; ++r) {   // the chunk's kPermTokens * k ids in rounds of 256
+  const int chunk = kPermTokens * k;
+  int64_t base = (int64_t)blockIdx.x * chunk;
+  for (int r = 0; r * 256 < chunk; ++r) {   // the chunk's ids in rounds of 256
     for (int i = tid; i < 4 * kMaxExperts; i += 256) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     int64_t p = base + r * 256 + tid;
     int e = -1;
-    if (p < R) {
+    const bool in_chunk = r * 256 + tid < chunk;
+    if (in_chunk && p < R) {
       e = idx[p];
       if ((unsigned)e >= (unsigned)E) e = -1;
     }
@@ -141,7 +143,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
       row_id_map[p] = row;
       src_index[row] = (int32_t)p;
       if (prob_perm) prob_perm[row] = prob[p];
-    } else if (p < R) {
+    } else if (in_chunk && p < R) {
       row_id_map[p] = -1;
     }
     __syncthreads();
