@@ -271,6 +271,49 @@ def router_leg(cfg, steps=20, warmup=5):
             "route_then_permute_us": round((ms_route + ms_perm) * 1e3, 1)}
 
 
+def loop_leg(cfg, steps=10, warmup=3):
+    """Grouped forward against the per-expert loop of launches (host-side counts given), same
+    inputs and workspace, HIP-event timing on the current stream."""
+    import numpy as np
+    import torch
+    import mixture_experts_grouped_permute_amd as m
+    from mixture_experts_grouped_permute_amd import _lib as L
+    from moe_inputs import make_inputs
+    lib = m.load()
+    inp = make_inputs(cfg)
+    d = inp.to("cuda:0")
+    dev = d.x.device
+    T, E, k, R = cfg.T, cfg.E, cfg.k, cfg.R
+    perm = {n: torch.empty(sz, dtype=dt, device=dev) for n, sz, dt in
+            (("split_sizes", E, torch.int32), ("offsets", E + 1, torch.int32), ("row_id_map", R, torch.int32),
+             ("src_index", R, torch.int32), ("prob_perm", R, torch.float32))}
+    out = torch.empty((T, cfg.H), dtype=d.x.dtype, device=dev)
+    a, keep, _, _ = L._fwd_args(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision, out, perm, None)
+    ws = torch.empty(lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a)), dtype=torch.uint8, device=dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    counts = np.bincount(inp.topk_idx.numpy().ravel(), minlength=E)
+    hc = (ctypes.c_int32 * E)(*[int(c) for c in counts])
+    st = torch.cuda.current_stream(dev).cuda_stream
+
+    def timed(f):
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            f()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / steps
+
+    ms_g = timed(lambda: L._check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), st), "grouped"))
+    ms_l = timed(lambda: L._check(lib.moe_grouped_mlp_fwd_loop(ctypes.byref(a), hc, st), "loop"))
+    del keep
+    return {"grouped_ms": round(ms_g, 4), "loop_ms": round(ms_l, 4), "loop_over_grouped": round(ms_l / ms_g, 3),
+            "experts_with_tokens": int((counts > 0).sum())}
+
+
 def cpu_baseline(inp, cfg, tokens, min_seconds=12.0, max_passes=8):
     """The fp64 oracle on the first `tokens` tokens of the workload (its full expert weights),
     repeated until about min_seconds of CPU work have run."""
@@ -304,8 +347,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,backward,router",
-                    help="comma list of bf16, mxfp8, mxfp8_finegrained, backward, router (bf16 always runs)")
+    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,backward,router,loop",
+                    help="comma list of bf16, mxfp8, mxfp8_finegrained, backward, router, loop (bf16 always runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -356,6 +399,9 @@ def main():
                               f"Zipf({c.zipf_s}) routing" + (f", expert {c.zero_expert} empty" if c.zero_expert is not None else "")
                               + ", weights quantized per call")
             line[key] = lg
+    if "loop" in legs:
+        torch.cuda.empty_cache()
+        line["loop_vs_grouped"] = {c.name: loop_leg(c) for c in (get_config(2), get_config(5))}
     if "router" in legs:
         line["router"] = {c.name: router_leg(c) for c in (get_config(2), get_config(5))}
     if not args.no_backward and "backward" in legs:

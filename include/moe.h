@@ -258,6 +258,23 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
 int moe_bwd_phase_count(void);
 const char* moe_bwd_phase_name(int i);   /* NULL when out of range */
 
+/* ------------------------------------------------------------------------
+ * moe_grouped_mlp_fwd_loop -- the same layer as moe_grouped_mlp_fwd, but as a
+ * per-expert loop: the permutation, then for each expert with tokens its own
+ * launches (MXFP8: quantize W1_e, W2_e; FC1_e with the ScaledSwiGLU*prob
+ * epilogue; FC2_e), then the combine.  This is the execution the pages
+ * contrast with grouping (page "BioNeMo Uses Grouped Kernels and MXFP8",
+ * Grouping fragmented expert workloads, Figure 2), kept as a baseline.
+ *
+ * Arguments as moe_grouped_mlp_fwd (same workspace size), plus
+ * split_sizes_host: HOST array [E] of the per-expert token counts of topk_idx
+ * (the caller obtains them, e.g. from a previous permutation; they must equal
+ * the counts the device computes, which is the caller's responsibility; their
+ * sum must be T*k).  Results equal moe_grouped_mlp_fwd's up to fp32
+ * accumulation order.
+ * ------------------------------------------------------------------------ */
+moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* split_sizes_host, void* stream);
+
 /* Synchronizes `stream`, then returns the device error flag kept in the first
  * 4 bytes of `workspace` by the last moe_permute / moe_grouped_mlp_fwd call
  * that used it (0 = none, 1 = an expert id was out of range; every such call

@@ -27,7 +27,7 @@ EXPORTS = (
     "moe_grouped_mlp_fwd_workspace", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd_workspace",
     "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
-    "moe_route_topk", "moe_route_permute",
+    "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop",
 )
 
 
@@ -111,6 +111,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_bwd_phase_name.argtypes = [ctypes.c_int]
     lib.moe_read_device_error.restype = ctypes.c_int
     lib.moe_read_device_error.argtypes = [_vp, _vp]
+    lib.moe_grouped_mlp_fwd_loop.restype = ctypes.c_int
+    lib.moe_grouped_mlp_fwd_loop.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(_i32), _vp]
     lib.moe_route_topk.restype = ctypes.c_int
     lib.moe_route_topk.argtypes = [_vp, ctypes.c_int, _i64, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]
     lib.moe_route_permute.restype = ctypes.c_int
@@ -352,6 +354,35 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
     _check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_fwd")
     ctx = {"perm": perm, "saved": saved, "compute": compute, "E": E, "I": I, "workspace": ws, "_keep": keep}
     return out, ctx
+
+
+def moe_grouped_mlp_fwd_loop(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor, w1, w2,
+                             split_sizes_host: Sequence[int], compute: str = "bf16"):
+    """The same forward as a per-expert loop of launches (the baseline grouping replaces).
+    split_sizes_host: the per-expert token counts of topk_idx, on the host."""
+    lib = load()
+    dev = x.device
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    R = T * k
+    E = w1.shape[0] if isinstance(w1, torch.Tensor) else len(w1)
+    perm = {
+        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
+        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
+        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
+        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
+        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
+    }
+    out = torch.empty((T, H), dtype=x.dtype, device=dev)
+    a, keep, _, _ = _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, None)
+    need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    if need == 0:
+        _check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_fwd_loop")
+    ws = _WS.get(need, dev)
+    a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
+    counts = (_i32 * E)(*[int(c) for c in split_sizes_host])
+    _check(lib.moe_grouped_mlp_fwd_loop(ctypes.byref(a), counts, _stream(dev)), "moe_grouped_mlp_fwd_loop")
+    return out, {"perm": perm, "workspace": ws, "_keep": keep}
 
 
 def _bwd_args(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32):

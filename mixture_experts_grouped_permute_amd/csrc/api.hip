@@ -397,6 +397,78 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
   return MOE_OK;
 }
 
+moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* split_sizes_host, void* stream) {
+  moe_status s = validate_fwd(a);
+  if (s != MOE_OK) return s;
+  MOE_CHECK(split_sizes_host != nullptr, MOE_ERR_INVALID_ARG);
+  int64_t sum = 0;
+  for (int e = 0; e < a->E; ++e) {
+    MOE_CHECK(split_sizes_host[e] >= 0, MOE_ERR_INVALID_ARG);
+    sum += split_sizes_host[e];
+  }
+  MOE_CHECK(sum == a->T * a->k, MOE_ERR_INVALID_ARG);
+  const size_t need = plan_fwd(a, nullptr).bytes;
+  MOE_CHECK(a->workspace && a->workspace_bytes >= need, MOE_ERR_WORKSPACE);
+  FwdPlan p = plan_fwd(a, a->workspace);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const int64_t T = a->T, H = a->H, I = a->I;
+  const int E = a->E, k = a->k;
+  const bool mx = a->compute == MOE_MXFP8_E4M3;
+  const bool x_f32 = a->io_dtype == MOE_F32;
+  const int64_t esz = mx ? 1 : 2;
+
+  HIP_TRY(launch_permute_indices(a->topk_idx, a->topk_prob, T, k, E, a->split_sizes, a->offsets, a->row_id_map,
+                                 a->src_index, a->prob_perm, p.perm.err, p.perm.block_counts, p.perm.block_base,
+                                 st));
+  HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, p.x_sc, mx, st));
+  if (mx && a->saved_x_perm)
+    HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, a->saved_x_perm, nullptr, false, st));
+  int64_t row0 = 0;
+  for (int e = 0; e < E; ++e) {
+    const int64_t Me = split_sizes_host[e];
+    if (Me == 0) continue;
+    uint8_t* xo = reinterpret_cast<uint8_t*>(p.x_op) + row0 * H * esz;
+    uint8_t* ho = reinterpret_cast<uint8_t*>(p.h_op) + row0 * I * esz;
+    if (mx) {
+      HIP_TRY(launch_mx_quant_weights(a->w1 + e, 1, 2 * I, H, p.w1q, p.w1s, nullptr, st));
+      HIP_TRY(launch_mx_quant_weights(a->w2 + e, 1, H, I, p.w2q, p.w2s, nullptr, st));
+    }
+    FwdGemm g1{};
+    g1.a = xo;
+    g1.a_scales = mx ? p.x_sc + row0 * (H / 32) : nullptr;
+    g1.w_tab = a->w1 + e;
+    g1.wq = p.w1q;
+    g1.ws = p.w1s;
+    g1.K = H;
+    g1.N = I;
+    g1.E = 1;
+    g1.split_sizes = a->split_sizes + e;   // the expert's own count, on the device
+    g1.prob_perm = a->prob_perm + row0;
+    g1.out = ho;
+    g1.out_scales = mx ? p.h_sc + row0 * (I / 32) : nullptr;
+    g1.save_gu = a->saved_gu ? reinterpret_cast<uint16_t*>(a->saved_gu) + row0 * 2 * I : nullptr;
+    g1.save_h = (mx && a->saved_h) ? reinterpret_cast<uint16_t*>(a->saved_h) + row0 * I : nullptr;
+    HIP_TRY(launch_fc1(g1, mx, st));
+    FwdGemm g2{};
+    g2.a = ho;
+    g2.a_scales = g1.out_scales;
+    g2.w_tab = a->w2 + e;
+    g2.wq = p.w2q;
+    g2.ws = p.w2s;
+    g2.K = I;
+    g2.N = H;
+    g2.E = 1;
+    g2.split_sizes = a->split_sizes + e;
+    g2.out = reinterpret_cast<uint8_t*>(p.z) + row0 * H * io_size(a->io_dtype);
+    g2.part = nullptr;
+    g2.out_f32 = x_f32;
+    HIP_TRY(launch_fc2(g2, mx, st));
+    row0 += Me;
+  }
+  HIP_TRY(launch_combine(p.z, x_f32, T, H, k, a->row_id_map, a->out, x_f32, st));
+  return MOE_OK;
+}
+
 size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a) {
   if (validate_bwd(a) != MOE_OK) return 0;
   return plan_bwd(a, nullptr).bytes;
