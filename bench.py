@@ -94,7 +94,7 @@ def _time_ex(lib, hip, call_ex, nph, steps, warmup):
     return (t1 - t0) * 1e3 / steps, [x / steps for x in sums]
 
 
-def run_gpu(cfg, steps, warmup, backward=False):
+def run_gpu(cfg, steps, warmup, backward=False, cached=False):
     import torch
     import mixture_experts_grouped_permute_amd as m
     from mixture_experts_grouped_permute_amd import _lib as L
@@ -120,6 +120,10 @@ def run_gpu(cfg, steps, warmup, backward=False):
         }
         out = torch.empty((T, H), dtype=d.x.dtype, device=dev)
         a, keep, _, _ = L._fwd_args(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision, out, perm, None)
+        if cached:   # MXFP8 weights quantized once, outside the timed region
+            wq = m.quantize_weights(d.w1, d.w2)
+            a.w1q, a.w1s, a.w2q, a.w2s = (t.data_ptr() for t in wq)
+            keep = (keep, wq)
         need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
         if need == 0:
             raise RuntimeError("argument validation failed")
@@ -395,6 +399,12 @@ def main():
             c = get_config(ci)
             rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2))
             del rr
+            torch.cuda.empty_cache()
+            rc = run_gpu(c, max(2, args.steps // 2), max(1, args.warmup // 2), cached=True)
+            lg["cached_weights"] = {"ms_per_step": round(rc["ms_per_step"], 4),
+                                    "value": round(c.T / (rc["ms_per_step"] * 1e-3), 1), "unit": "tokens/s",
+                                    "note": "MXFP8 weights quantized once and passed in (not per call)"}
+            del rc
             lg["workload"] = (f"{c.name}: T={c.T} H={c.H} I={c.I} E={c.E} top-{c.k}, MXFP8 both GEMMs, "
                               f"Zipf({c.zipf_s}) routing" + (f", expert {c.zero_expert} empty" if c.zero_expert is not None else "")
                               + ", weights quantized per call")

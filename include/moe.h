@@ -173,6 +173,12 @@ moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x
  * saved_*: optional (all NULL for inference, all set for training): bf16
  * copies kept for the backward -- x_perm [R, H], gu [R, 2I] (gate-up
  * output), h [R, I] (before MXFP8 quantization).  R = T*k.
+ * w1q, w1s, w2q, w2s: optional pre-quantized MXFP8 weights (MXFP8 compute
+ * only; all four or none): the row-wise mxfp8_quantize (axis 0) of every
+ * W1_e and W2_e, stacked -- w1q [E, 2I, H] and w1s [E, 2I, H/32], w2q [E, H,
+ * I] and w2s [E, H, I/32], device.  When given, the per-call weight
+ * quantization is skipped (weights quantized once and cached by the caller)
+ * and the workspace is smaller; w1 / w2 are then not read.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t T, H, I;
@@ -195,6 +201,10 @@ typedef struct {
   void* saved_h;                /* [R, I]  bf16, or NULL */
   void* workspace;
   size_t workspace_bytes;
+  const uint8_t* w1q;           /* [E, 2I, H]    E4M3, or NULL (ABI version 2) */
+  const uint8_t* w1s;           /* [E, 2I, H/32] E8M0 */
+  const uint8_t* w2q;           /* [E, H, I]     E4M3 */
+  const uint8_t* w2s;           /* [E, H, I/32]  E8M0 */
 } moe_mlp_fwd_args;
 
 size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a);

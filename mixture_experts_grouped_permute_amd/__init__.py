@@ -6,10 +6,10 @@ library's HIP kernels for gfx950.
 """
 from ._lib import (MOE_BF16, MOE_F32, MOE_MXFP8_E4M3, EXPORTS, MoeError, load, moe_grouped_mlp_bwd,
                    moe_grouped_mlp_fwd, moe_grouped_mlp_fwd_loop, moe_permute, moe_read_device_error, moe_route_permute, moe_route_topk,
-                   mxfp8_quantize, LIB_PATH)
+                   mxfp8_quantize, quantize_weights, LIB_PATH)
 
 __all__ = [
     "MOE_BF16", "MOE_F32", "MOE_MXFP8_E4M3", "EXPORTS", "MoeError", "load", "moe_grouped_mlp_bwd",
     "moe_grouped_mlp_fwd", "moe_grouped_mlp_fwd_loop", "moe_permute", "moe_read_device_error", "moe_route_permute", "moe_route_topk",
-    "mxfp8_quantize", "LIB_PATH",
+    "mxfp8_quantize", "quantize_weights", "LIB_PATH",
 ]

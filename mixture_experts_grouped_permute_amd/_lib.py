@@ -52,6 +52,7 @@ class FwdArgs(ctypes.Structure):
         ("split_sizes", _vp), ("offsets", _vp), ("row_id_map", _vp), ("src_index", _vp), ("prob_perm", _vp),
         ("saved_x_perm", _vp), ("saved_gu", _vp), ("saved_h", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("w1q", _vp), ("w1s", _vp), ("w2q", _vp), ("w2s", _vp),
     ]
 
 
@@ -317,11 +318,25 @@ def _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved):
     return a, (w1t, w2t, w1k, w2k), E, I
 
 
+def quantize_weights(w1, w2):
+    """MXFP8 weights for reuse across calls: (w1q [E,2I,H], w1s [E,2I,H/32], w2q [E,H,I],
+    w2s [E,H,I/32]), each expert quantized row-wise by mxfp8_quantize."""
+    e1 = [w1[e] for e in range(len(w1))]
+    e2 = [w2[e] for e in range(len(w2))]
+    q1 = [mxfp8_quantize(w, axis=0) for w in e1]
+    q2 = [mxfp8_quantize(w, axis=0) for w in e2]
+    return (torch.stack([q for q, _ in q1]), torch.stack([s for _, s in q1]),
+            torch.stack([q for q, _ in q2]), torch.stack([s for _, s in q2]))
+
+
 def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor, w1, w2,
-                        compute: str = "bf16", save_for_backward: bool = False, workspace: Optional[torch.Tensor] = None):
+                        compute: str = "bf16", save_for_backward: bool = False, workspace: Optional[torch.Tensor] = None,
+                        w_quant=None):
     """Grouped expert MLP forward.  w1: [E,2I,H] tensor or E tensors [2I,H] (bf16);
-    w2: [E,H,I] or E tensors [H,I].  Returns (out, ctx) where ctx holds the
-    permutation and, with save_for_backward, the bf16 activations."""
+    w2: [E,H,I] or E tensors [H,I].  w_quant: optional (w1q, w1s, w2q, w2s) from
+    quantize_weights (MXFP8 only): the per-call weight quantization is skipped.
+    Returns (out, ctx) where ctx holds the permutation and, with save_for_backward,
+    the bf16 activations."""
     lib = load()
     dev = x.device
     T, H = x.shape
@@ -345,6 +360,9 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
         }
     out = torch.empty((T, H), dtype=x.dtype, device=dev)
     a, keep, _, _ = _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved)
+    if w_quant is not None:
+        a.w1q, a.w1s, a.w2q, a.w2s = (_ptr(t) for t in w_quant)
+        keep = (keep, w_quant)
     need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
     if need == 0:
         # the size query validates the arguments: surface the status of the call itself

@@ -88,10 +88,17 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
     p.x_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * H / 32)));
     p.h_op = c.take((size_t)(R * I));
     p.h_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * I / 32)));
-    p.w1q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H)));
-    p.w1s = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H / 32)));
-    p.w2q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I)));
-    p.w2s = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I / 32)));
+    if (a->w1q) {   // quantized weights cached by the caller
+      p.w1q = const_cast<uint8_t*>(a->w1q);
+      p.w1s = const_cast<uint8_t*>(a->w1s);
+      p.w2q = const_cast<uint8_t*>(a->w2q);
+      p.w2s = const_cast<uint8_t*>(a->w2s);
+    } else {
+      p.w1q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H)));
+      p.w1s = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H / 32)));
+      p.w2q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I)));
+      p.w2s = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I / 32)));
+    }
   } else {
     if (!a->saved_x_perm) p.x_op = c.take((size_t)(R * H * 2));
     else p.x_op = a->saved_x_perm;
@@ -113,11 +120,16 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   if (a->compute != MOE_BF16 && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
   const int64_t align = a->compute == MOE_BF16 ? 64 : 128;
   if (a->H % align || a->I % align) return MOE_ERR_UNSUPPORTED;
-  if (!a->x || !a->topk_idx || !a->topk_prob || !a->w1 || !a->w2 || !a->out) return MOE_ERR_INVALID_ARG;
+  if (!a->x || !a->topk_idx || !a->topk_prob || !a->out) return MOE_ERR_INVALID_ARG;
+  if (!a->w1q && (!a->w1 || !a->w2)) return MOE_ERR_INVALID_ARG;
   if (!a->split_sizes || !a->offsets || !a->row_id_map || !a->src_index || !a->prob_perm)
     return MOE_ERR_INVALID_ARG;
-  for (int e = 0; e < a->E; ++e)
-    if (!a->w1[e] || !a->w2[e]) return MOE_ERR_INVALID_ARG;
+  if (!a->w1q)
+    for (int e = 0; e < a->E; ++e)
+      if (!a->w1[e] || !a->w2[e]) return MOE_ERR_INVALID_ARG;
+  const bool any_q = a->w1q || a->w1s || a->w2q || a->w2s;
+  const bool all_q = a->w1q && a->w1s && a->w2q && a->w2s;
+  if (any_q && (!all_q || a->compute != MOE_MXFP8_E4M3)) return MOE_ERR_INVALID_ARG;
   const bool any_saved = a->saved_x_perm || a->saved_gu || a->saved_h;
   const bool all_saved = a->saved_x_perm && a->saved_gu && a->saved_h;
   if (any_saved && !all_saved) return MOE_ERR_INVALID_ARG;
@@ -194,7 +206,7 @@ moe_status validate_bwd(const moe_mlp_bwd_args* a) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 1; }
+int moe_abi_version(void) { return 2; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -344,9 +356,9 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
     if (a->saved_x_perm)
       HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, a->saved_x_perm, nullptr, false, st));
     MOE_CHECK(mark(2), MOE_ERR_HIP);
-    HIP_TRY(launch_mx_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.w1s, a->split_sizes, st));
+    if (!a->w1q) HIP_TRY(launch_mx_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.w1s, a->split_sizes, st));
     MOE_CHECK(mark(3), MOE_ERR_HIP);
-    HIP_TRY(launch_mx_quant_weights(a->w2, E, H, I, p.w2q, p.w2s, a->split_sizes, st));
+    if (!a->w1q) HIP_TRY(launch_mx_quant_weights(a->w2, E, H, I, p.w2q, p.w2s, a->split_sizes, st));
   } else {
     HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, nullptr, false, st));
     MOE_CHECK(mark(2), MOE_ERR_HIP);
@@ -429,16 +441,21 @@ moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* sp
     if (Me == 0) continue;
     uint8_t* xo = reinterpret_cast<uint8_t*>(p.x_op) + row0 * H * esz;
     uint8_t* ho = reinterpret_cast<uint8_t*>(p.h_op) + row0 * I * esz;
-    if (mx) {
+    // MXFP8 weights of expert e: cached by the caller, or quantized here into slot 0
+    const uint8_t* w1q_e = a->w1q ? a->w1q + e * 2 * I * H : p.w1q;
+    const uint8_t* w1s_e = a->w1q ? a->w1s + e * 2 * I * H / 32 : p.w1s;
+    const uint8_t* w2q_e = a->w1q ? a->w2q + e * H * I : p.w2q;
+    const uint8_t* w2s_e = a->w1q ? a->w2s + e * H * I / 32 : p.w2s;
+    if (mx && !a->w1q) {
       HIP_TRY(launch_mx_quant_weights(a->w1 + e, 1, 2 * I, H, p.w1q, p.w1s, nullptr, st));
       HIP_TRY(launch_mx_quant_weights(a->w2 + e, 1, H, I, p.w2q, p.w2s, nullptr, st));
     }
     FwdGemm g1{};
     g1.a = xo;
     g1.a_scales = mx ? p.x_sc + row0 * (H / 32) : nullptr;
-    g1.w_tab = a->w1 + e;
-    g1.wq = p.w1q;
-    g1.ws = p.w1s;
+    g1.w_tab = a->w1 ? a->w1 + e : nullptr;
+    g1.wq = w1q_e;
+    g1.ws = w1s_e;
     g1.K = H;
     g1.N = I;
     g1.E = 1;
@@ -452,9 +469,9 @@ moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* sp
     FwdGemm g2{};
     g2.a = ho;
     g2.a_scales = g1.out_scales;
-    g2.w_tab = a->w2 + e;
-    g2.wq = p.w2q;
-    g2.ws = p.w2s;
+    g2.w_tab = a->w2 ? a->w2 + e : nullptr;
+    g2.wq = w2q_e;
+    g2.ws = w2s_e;
     g2.K = I;
     g2.N = H;
     g2.E = 1;

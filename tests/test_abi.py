@@ -52,7 +52,7 @@ def test_binding_lists_every_declared_symbol():
 
 
 def test_version_status_and_phase_names(lib):
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     lib.moe_status_string.restype = ctypes.c_char_p
     for s in range(5):
         assert lib.moe_status_string(s)
@@ -128,3 +128,20 @@ def test_quantize_and_permute_validation(lib):
                    ctypes.c_size_t, ctypes.c_void_p]
     # k > E
     assert pm(p, 1, 16, 64, p, p, 5, 4, 1, p, None, p, p, p, p, p, p, 1 << 20, None) == MOE_ERR_INVALID_ARG
+
+
+def test_fwd_cached_weight_validation(lib):
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG
+    lib.moe_grouped_mlp_fwd_workspace.restype = ctypes.c_size_t
+    a, tab = _fwd_args(compute=2)
+    per_call = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    a.w1q = a.w1s = a.w2q = a.w2s = 0x2000
+    cached = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    # the cached weights are not copied into the workspace
+    assert 0 < cached < per_call and per_call - cached >= 8 * 3 * 4096 * 14336
+    b, tb = _fwd_args(compute=1)           # BF16 compute: no MXFP8 weights accepted
+    b.w1q = b.w1s = b.w2q = b.w2s = 0x2000
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(b), None) == MOE_ERR_INVALID_ARG
+    c, tc = _fwd_args(compute=2)           # all four or none
+    c.w1q = 0x2000
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(c), None) == MOE_ERR_INVALID_ARG

@@ -13,6 +13,7 @@ from gpu_util import BF16_TOL, MXFP8_TOL, cfg_small, gpu, log, need_gpu, to_np
 from moe_inputs import get_config, make_inputs
 from moe_inputs.generate import routing_with_counts
 from oracle import mlp
+from oracle import numerics as nm
 
 CASES = [
     # name, cfg, counts (None = the cfg's own routing)
@@ -83,6 +84,26 @@ def test_forward_split_last_round(compute):
     tol = BF16_TOL if compute == "bf16" else MXFP8_TOL
     log(f"  {rows.sum()} tokens, normwise err {err:.3e} (tol {tol})")
     assert err < tol
+
+
+@gpu
+def test_forward_cached_mxfp8_weights_equal_per_call_quantization():
+    """Weights quantized once (quantize_weights) give bit-identical outputs to the per-call
+    quantization, in the grouped and the per-expert-loop forward."""
+    m = need_gpu()
+    cfg = cfg_small(T=600, H=256, I=256, E=8, k=2)
+    log("fwd cached MXFP8 weights")
+    inp = make_inputs(cfg)
+    d = inp.to("cuda")
+    wq = m.quantize_weights(d.w1, d.w2)
+    a, _ = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8")
+    b, _ = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", w_quant=wq)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # the oracle's weight bytes are the cached ones
+    c1, s1 = nm.quantize_mxfp8(inp.w1[3].to(torch.float64).numpy(), axis=1)
+    np.testing.assert_array_equal(wq[0][3].cpu().numpy(), c1)
+    np.testing.assert_array_equal(wq[1][3].cpu().numpy(), s1)
 
 
 @gpu
