@@ -12,13 +12,20 @@
 // Structure
 //   * 256 threads = 4 waves in a 2x2 grid; a workgroup owns a 256 x 256 output
 //     tile (FC1: 128 h columns = 128 gate + 128 up weight rows); each wave a
-//     128 x 128 block = 4 x 4 MFMA 32x32 fragments accumulated in fp32.
+//     128 x 128 block = 4 x 4 MFMA 32x32 blocks accumulated in fp32.  The weight
+//     block is the MFMA's first operand, so a lane ends up holding one token row
+//     and runs of 4 consecutive output columns, and the epilogues store straight
+//     from the accumulators (no LDS staging).
 //   * K is consumed in 128-byte steps (64 bf16 or 128 E4M3 values per row),
-//     double-buffered in LDS (2 x 64 KB) with the 16-byte chunks of each row
-//     XOR-swizzled by (row & 7) so both the row-wise stores and the MFMA
-//     fragment reads are bank-conflict free.
+//     double-buffered in LDS (2 x 64 KB) in the swz layout, filled by
+//     direct-to-LDS buffer loads.  Inside a stage the next stage's loads and the
+//     next substep's fragment reads are interleaved one by one between the MFMAs,
+//     so the wave's in-order issue never stalls behind a burst of memory
+//     instructions; the last stage of a tile loads the first stage of the
+//     workgroup's next tile, which lands while the epilogue runs.
 //   * Global reads are buffer loads whose range is the expert's valid rows,
-//     so ragged tiles read zeros instead of neighbouring experts' data.
+//     so ragged tiles read zeros instead of neighbouring experts' data; the
+//     epilogue's buffer stores end at the tile's last valid row the same way.
 //   * Scheduler: every workgroup recomputes the per-expert tile prefix sum
 //     from split_sizes in LDS (no host sync), then walks tiles in rounds of
 //     gridDim.x.  Tile order is expert, N-panel, M-block (M fastest) and a
@@ -78,11 +85,71 @@ __device__ __forceinline__ void split_policy(int total, int G, int kU, int& full
   }
 }
 
+// Fragments of one MFMA K substep of a wave: 4 token blocks (a) and 4 weight blocks (b) of 32
+// rows, plus the E8M0 scale bytes of the lane's rows (MXFP8).
+template <bool kMx>
+struct FwdFrag {
+  typename std::conditional<kMx, i32x8, bf16x8>::type a[4], b[4];
+  int sa[4], sb[4];
+};
+
+// Element e of the fragments of substep kk, in the order the 16 MFMAs of a substep consume them:
+// a0, b0, b1, b2, b3, a1, a2, a3 (the MFMAs run token block i outer, weight block j inner).
+template <bool kMx, bool kFc1>
+__device__ __forceinline__ void read_elem(FwdFrag<kMx>& f, const uint8_t* sA, const uint32_t* sS, int kk, int e,
+                                          int wm, int wn, int lane) {
+  const int r32 = lane & 31, g = lane >> 5;
+  const bool isA = e == 0 || e >= 5;
+  const int idx = e == 0 ? 0 : (e >= 5 ? e - 4 : e - 1);
+  const int row = isA ? wm * 128 + idx * 32 + r32 : TileCore<kMx, kFc1>::brow(wn, idx) + r32;
+  const uint8_t* base = isA ? sA : sA + kTileBytes;
+  if constexpr (!kMx) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(base + swz(row, (uint32_t)(kk * 2 + g)));
+    if (isA) f.a[idx] = v; else f.b[idx] = v;
+  } else {
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + g)));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + 2 + g)));
+    const i32x8 v{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    // the scale byte of this lane's 32-value block, read on its own: a shift of the whole word
+    // would make the read wait for LDS on the spot
+    const int sc = reinterpret_cast<const uint8_t*>(sS)[((isA ? 0 : 256) + row) * 4 + 2 * kk + g];
+    if (isA) { f.a[idx] = v; f.sa[idx] = sc; } else { f.b[idx] = v; f.sb[idx] = sc; }
+  }
+}
+
+// Order of the reads of the next substep's elements while the current substep's MFMAs run:
+// b0 b1 a0 b2 a1 b3 a2 a3 -- each a block is read only after the MFMAs that use the current one
+// are issued, so the two fragment sets share the a registers.
+__device__ __forceinline__ constexpr int next_elem(int s) {
+  return s == 0 ? 1 : s == 1 ? 2 : s == 2 ? 0 : s == 3 ? 3 : s == 4 ? 5 : s == 5 ? 4 : s;
+}
+
+// Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
+// allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
+// and spills.
+__device__ __forceinline__ float agpr_read(float x) {
+  float y;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+  return y;
+}
+__device__ __forceinline__ void agpr_read16(const f32x16& a, float (&o)[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = agpr_read(a[r]);
+}
+
+// One work item: a 256 x 256 output tile, or one K part of a split tile.
+struct FwdItem {
+  int t, tile, part, e, mt, nt, row0, mrows, u0, u1;
+};
+
 template <bool kMx, bool kFc1, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
-  // 2 pipeline stages (the epilogue reuses them), plus the MXFP8 scale words (2 x 2 KB)
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * 2048 : 16)];
+  // 2 pipeline stages, then the MXFP8 scale words (2 x 2 KB), then the routing probabilities of the
+  // tile's rows (FC1, double-buffered by work item)
+  constexpr int kScOff = 2 * kStageBytes;
+  constexpr int kPrOff = kScOff + (kMx ? 2 * 2048 : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPrOff + (kFc1 ? 2 * 1024 : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -107,278 +174,311 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   const int lo = p.split == 2 ? full : 0;
   const int hi = p.split == 0 ? total : (p.split == 1 ? full : (S > 1 ? full + (total - full) * S : full));
 
-  for (int round = 0;; ++round) {
-    const int t = lo + round * G + xcd * per + slot;
-    if (t >= hi) break;
-    int tile = t, part = -1;
+  // Work item of round r of this workgroup (uniform; valid iff it.t < hi).
+  auto decode = [&](int round, FwdItem& it) {
+    it.t = lo + round * G + xcd * per + slot;
+    it.u0 = 0;
+    if (it.t >= hi) return;
+    it.tile = it.t;
+    it.part = -1;
     if (kOutF32 && p.split == 2) {
-      tile = full + (t - full) / S;
-      part = (t - full) % S;
+      it.tile = full + (it.t - full) / S;
+      it.part = (it.t - full) % S;
     }
-    // the tile decode is uniform across the workgroup; readfirstlane makes it scalar so the
-    // buffer descriptors built from it live in SGPRs
-    const int e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, tile));
-    const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
+    it.e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, it.tile));
+    const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
     const int nM = (Me + kBM - 1) / kBM;
-    const int local = tile - __builtin_amdgcn_readfirstlane(sched.tile[e]);
-    const int mt = local % nM, nt = local / nM;
-    const int row0 = __builtin_amdgcn_readfirstlane(sched.off[e]) + mt * kBM;   // first permuted row of the tile
-    const int mrows = min(kBM, Me - mt * kBM);
-    const uint8_t* wbase = kMx ? (p.wq + (int64_t)e * p.wq_stride) : kernarg_table(e);
+    const int local = it.tile - __builtin_amdgcn_readfirstlane(sched.tile[it.e]);
+    it.mt = local % nM;
+    it.nt = local / nM;
+    it.row0 = __builtin_amdgcn_readfirstlane(sched.off[it.e]) + it.mt * kBM;
+    it.mrows = min(kBM, Me - it.mt * kBM);
+    it.u0 = it.part < 0 ? 0 : it.part * kU / S;
+    it.u1 = it.part < 0 ? kU : (it.part + 1) * kU / S;
+  };
+  // Buffer descriptors of an item's operands: the A rows of its tile (zero past the expert's
+  // rows), and the weight rows from the tile's first one.  FC1 B rows [0,128) of a tile are gate
+  // rows n0h + r, rows [128,256) the up rows I + n0h + r; gate rows past I only feed masked
+  // columns, up rows past 2I fall outside the range and read zero.  An invalid item gets
+  // zero-range descriptors: its loads touch no memory.
+  struct Desc { i32x4 va, vb, vas, vbs; };
+  auto descs = [&](const FwdItem& it, Desc& d) {
+    if (it.t >= hi) {
+      d.va = make_vsharp(p.a, 0); d.vb = d.va; d.vas = d.va; d.vbs = d.va;
+      return;
+    }
+    const int64_t b0 = kFc1 ? (int64_t)it.nt * 128 : (int64_t)it.nt * kBN;        // first weight row
+    const int64_t brows = kFc1 ? 2 * N - b0 : min((int64_t)kBN, N - b0);
+    const uint8_t* wbase = kMx ? (p.wq + (int64_t)it.e * p.wq_stride) : kernarg_table(it.e);
+    d.va = make_vsharp(p.a + (int64_t)it.row0 * rowb, (uint32_t)it.mrows * rowb);
+    d.vb = make_vsharp(wbase + b0 * rowb, (uint32_t)(brows * rowb));
+    if constexpr (kMx) {
+      const uint8_t* sbase = p.ws + (int64_t)it.e * p.ws_stride;
+      d.vas = make_vsharp(p.a_scales + (int64_t)it.row0 * kscale_row, (uint32_t)it.mrows * kscale_row);
+      d.vbs = make_vsharp(sbase + b0 * kscale_row, (uint32_t)(brows * kscale_row));
+    } else {
+      d.vas = d.va;
+      d.vbs = d.vb;
+    }
+  };
+
+  // Direct-to-LDS loads (buffer_load_dwordx4 ... lds), one 16-byte chunk per lane, each load
+  // filling a contiguous 1 KB of LDS: load q of wave w fills row pairs j = 4 (8w + q) + L / 16,
+  // lane L's 16-byte LDS slot s = L % 16 holding (row parity, chunk) = s ^ hs(j), so the
+  // stage lands in the swz layout.  Whole 128-byte rows per load keep every L2 request a full
+  // line.  MXFP8 adds one 4-byte load per operand per stage: the E8M0 scales of the stage's four
+  // 32-value blocks of row 64 w + L.  The voffsets are the same for every tile.
+  uint32_t a_vo[8], b_vo[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int j = (wave * 8 + q) * 4 + (lane >> 4);
+    const uint32_t hs = (uint32_t)((j & 7) | ((j & 4) << 1));
+    const uint32_t sl = (uint32_t)(lane & 15) ^ hs;
+    const int r = 2 * j + (int)(sl >> 3);
+    const uint32_t c = sl & 7u;
+    const int64_t br = kFc1 ? (r < 128 ? (int64_t)r : N + (r - 128)) : (int64_t)r;
+    a_vo[q] = (uint32_t)r * rowb + c * 16;
+    b_vo[q] = (uint32_t)(br * rowb) + c * 16;
+  }
+  uint32_t as_vo = 0, bs_vo = 0;
+  if constexpr (kMx) {
+    const int r = wave * 64 + lane;
+    const int64_t br = kFc1 ? (r < 128 ? (int64_t)r : N + (r - 128)) : (int64_t)r;
+    as_vo = (uint32_t)r * kscale_row;
+    bs_vo = (uint32_t)(br * kscale_row);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
+  const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * 256u);
+  // stage kt of the item described by d into buffer b
+  auto dma_a = [&](const Desc& d, int b, int kt, int q) {
+    dma16(d.va, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q], (uint32_t)kt * kRowBytes);
+  };
+  auto dma_b = [&](const Desc& d, int b, int kt, int q) {
+    dma16(d.vb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q], (uint32_t)kt * kRowBytes);
+  };
+  auto dma_s = [&](const Desc& d, int b, int kt) {
+    if constexpr (kMx) {
+      const uint32_t ss = lds_sc + (uint32_t)b * 2048u;
+      dma4(d.vas, ss, as_vo, (uint32_t)kt * 4u);
+      dma4(d.vbs, ss + 1024u, bs_vo, (uint32_t)kt * 4u);
+    }
+  };
+
+  FwdItem cur, nxt;
+  Desc dc, dn;
+  decode(0, cur);
+  descs(cur, dc);
+  int par = 0;    // buffer of the current item's first stage
+  if (cur.t < hi) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) { dma_a(dc, 0, cur.u0, q); dma_b(dc, 0, cur.u0, q); }
+    dma_s(dc, 0, cur.u0);
+  }
+
+  for (int round = 0; cur.t < hi; ++round) {
+    decode(round + 1, nxt);
+    descs(nxt, dn);
+    const int ipar = round & 1;                          // probability buffer of this item
+    if constexpr (kFc1) {
+      const float pr = tid < cur.mrows ? p.prob_perm[cur.row0 + tid] : 0.f;
+      reinterpret_cast<float*>(smem + kPrOff)[ipar * 256 + tid] = pr;
+    }
     TileCore<kMx, kFc1> core;
     core.zero();
-    {
-      // K units [u0, u1) of this work item (all of K unless the tile is split)
-      const int u0 = part < 0 ? 0 : part * kU / S;
-      const int u1 = part < 0 ? kU : (part + 1) * kU / S;
-      // ---- main loop: direct-to-LDS loads (buffer_load_dwordx4 ... lds), one 16-byte chunk per
-      // lane, each load filling a contiguous 1 KB of LDS.
-      // FC1 B rows [0,128) are gate rows n0h + r, rows [128,256) up rows I + n0h + r: gate rows
-      // past I only feed masked columns, up rows past 2I fall outside the range and read zero.
-      auto b_row = [&](int r) -> int64_t {
-        return kFc1 ? (r < 128 ? ((int64_t)nt * 128 + r) : (N + (int64_t)nt * 128 + (r - 128))) : (int64_t)r;
-      };
-      const i32x4 va = make_vsharp(p.a + (int64_t)row0 * rowb, (uint32_t)mrows * rowb);
-      const i32x4 vb = kFc1 ? make_vsharp(wbase, (uint32_t)(2 * N * rowb))
-                            : make_vsharp(wbase + (int64_t)nt * kBN * rowb,
-                                          (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * rowb));
-      {
-        // Two 64 KB stages of 128 bytes of K per row (64 bf16 = 4 MFMA K steps, or 128 E4M3 = 2
-        // MX MFMA K steps), in the 128-byte-row swizzle (swz) the MFMA core reads.  Whole
-        // 128-byte rows per load keep every L2 request a full line.  Load q of wave w fills row
-        // pairs j = 4 (8w + q) + L / 16; lane L's 16-byte LDS slot s = L % 16 holds (row parity,
-        // chunk) = s ^ hs(j).  MXFP8 adds one 4-byte load per operand per stage: the E8M0 scales
-        // of the stage's four 32-value blocks of row 64w + L.
-        uint32_t a_vo[8], b_vo[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int j = (wave * 8 + q) * 4 + (lane >> 4);
-          const uint32_t hs = (uint32_t)((j & 7) | ((j & 4) << 1));
-          const uint32_t sl = (uint32_t)(lane & 15) ^ hs;
-          const int r = 2 * j + (int)(sl >> 3);
-          const uint32_t c = sl & 7u;
-          a_vo[q] = (uint32_t)r * rowb + c * 16;
-          b_vo[q] = (uint32_t)(b_row(r) * rowb) + c * 16;
-        }
-        const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 8) * 1024u;
-        const uint32_t lds_sc = lds_addr(smem + 2 * kStageBytes) + (uint32_t)wave * 256u;
-        i32x4 vas = va, vbs = vb;
-        uint32_t as_vo = 0, bs_vo = 0;
-        if constexpr (kMx) {
-          const int r = wave * 64 + lane;
-          vas = make_vsharp(p.a_scales + (int64_t)row0 * kscale_row, (uint32_t)mrows * kscale_row);
-          as_vo = (uint32_t)r * kscale_row;
-          const uint8_t* sbase = p.ws + (int64_t)e * p.ws_stride;
-          vbs = kFc1 ? make_vsharp(sbase, (uint32_t)(2 * N * kscale_row))
-                     : make_vsharp(sbase + (int64_t)nt * kBN * kscale_row,
-                                   (uint32_t)(min((int64_t)kBN, N - (int64_t)nt * kBN) * kscale_row));
-          bs_vo = (uint32_t)(b_row(r) * kscale_row);
-        }
-        auto issue = [&](int kt) {
-          const uint32_t sa = lds0 + (uint32_t)(kt & 1) * (uint32_t)kStageBytes;
-          const uint32_t so = (uint32_t)kt * kRowBytes;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) dma16(va, sa + q * 1024u, a_vo[q], so);
-#pragma unroll
-          for (int q = 0; q < 8; ++q) dma16(vb, sa + kTileBytes + q * 1024u, b_vo[q], so);
-          if constexpr (kMx) {
-            const uint32_t ss = lds_sc + (uint32_t)(kt & 1) * 2048u;
-            dma4(vas, ss, as_vo, (uint32_t)kt * 4u);
-            dma4(vbs, ss + 1024u, bs_vo, (uint32_t)kt * 4u);
-          }
-        };
-        issue(u0);
-        for (int kt = u0; kt < u1; ++kt) {
-          // stage kt landed (own loads + barrier); every wave finished reading stage kt-1, whose
-          // buffer takes stage kt+1 while stage kt is multiplied
-          wait_vmcnt<0>();
-          __syncthreads();
-          if (kt + 1 < u1) issue(kt + 1);
-          const uint8_t* sA = smem + (kt & 1) * kStageBytes;
-          const uint32_t* sS = reinterpret_cast<const uint32_t*>(smem + 2 * kStageBytes + (kt & 1) * 2048);
-          core.compute(sA, sA + kTileBytes, sS, sS + 256, wm, wn, lane);
-        }
-      }
+    typedef FwdFrag<kMx> Fr;
+    auto mm = [&](const Fr& f, int q) {
+      const int i = q >> 2, j = q & 3;
+      // weight block as the MFMA's A operand: each lane ends up with one token row and 16 output
+      // columns, in 4 runs of 4 consecutive columns
+      if constexpr (!kMx)
+        core.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], core.acc[i][j], 0, 0, 0);
+      else
+        core.acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], core.acc[i][j], 0, 0, 0,
+                                                                           f.sb[j], 0, f.sa[i]);
+    };
+    const int n = cur.u1 - cur.u0;
+#pragma unroll 1
+    for (int s = 0; s < n; ++s) {
+      const int kt = cur.u0 + s, b = (par + s) & 1;
+      // stage kt landed (own loads + barrier); every wave finished reading the other buffer, which
+      // takes the next stage -- of this item, or the first of the next item -- while this one is
+      // multiplied
+      wait_vmcnt<0>();
       __syncthreads();
-    }
-
-    // ---- epilogue, staged through LDS (the stage buffers are free after the last barrier).
-    // The lane id is laundered so the address arithmetic below is redone per tile instead of
-    // being hoisted above the main loop (where it would occupy ~100 VGPRs for the whole loop).
-    int elane = lane, etid = tid;
-    asm volatile("" : "+v"(elane), "+v"(etid));
-    const int r32 = elane & 31, g4 = (elane >> 5) * 4;
-    if constexpr (kFc1) {
-      const int64_t I = N;
-      const int64_t n0h = (int64_t)nt * 128;
-      if (p.save_gu) {
-        // training: the gate-up output as bf16, staged as a [256][256] tile (gate columns
-        // [0,128), up columns [128,256)) and stored as 128-byte row segments
+      const bool last = s + 1 == n;
+      const Desc& dd = last ? dn : dc;
+      const int kn = last ? nxt.u0 : kt + 1;
+      const int bn = b ^ 1;
+      const uint8_t* sA = smem + b * kStageBytes;
+      const uint32_t* sS = reinterpret_cast<const uint32_t*>(smem + kScOff + b * 2048);
+      Fr f0, f1;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = (j >> 1) * 128 + wn * 64 + (j & 1) * 32 + r32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int mb = wm * 128 + g4 + (r & 3);
-              const uint32_t off = epi_off(mb, n >> 3) + (n & 7) * 2 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);
-              *reinterpret_cast<uint16_t*>(smem + off) = f32_to_bf16(core.acc[i][j][r]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int u = q * 256 + etid;
-          const int m = u >> 2, b = u & 3;
-          const int64_t col = n0h + (b & 1) * 64;
-          if (m < mrows && col < I) {
-            uint16_t* dst = p.save_gu + (int64_t)(row0 + m) * 2 * I + (b >> 1) * I + col;
-            u32x4* d = reinterpret_cast<u32x4*>(dst);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off(m, b * 8 + c));
-          }
-        }
-        __syncthreads();
+      for (int e = 0; e < 8; ++e) {
+        read_elem<kMx, kFc1>(f0, sA, sS, 0, e, wm, wn, lane);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // (A) silu(g) * u per element, fp32, into a rotated [256][128] LDS tile
+      if constexpr (!kMx) {
+        // 4 substeps: the A loads of the next stage and the substep-1 reads between the MFMAs of
+        // substep 0, the B loads and the substep-2 reads in substep 1, the substep-3 reads in
+        // substep 2 -- at most one memory instruction per MFMA, so neither the texture unit nor
+        // the LDS queue backs up and stalls the wave's MFMA issue
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int n = wn * 64 + jj * 32 + r32;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float gv = core.acc[i][jj][r], uv = core.acc[i][jj + 2][r];
-            // m & 7 and the chunk rotation depend only on (lane, r & 3); i and r >> 2 add constants
-            const int mb = wm * 128 + g4 + (r & 3);
-            const uint32_t off = epi_off(mb, n >> 2) + (n & 3) * 4 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);
-            *reinterpret_cast<float*>(smem + off) = silu_f(gv) * uv;
-          }
-          __builtin_amdgcn_sched_barrier(0);   // keep the accumulator reads of one fragment pair together
+        for (int q = 0; q < 16; ++q) {
+          mm(f0, q);
+          if (q & 1) read_elem<kMx, kFc1>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
+          else dma_a(dd, bn, kn, q >> 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      __syncthreads();
-      // (B) a thread owns whole 32-column blocks of a row: scale by prob, round or quantize
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int u = q * 256 + etid;
-        const int m = u >> 2, b = u & 3;
-        const int64_t col = n0h + b * 32;
-        if (m < mrows && col < I) {
-          const int64_t grow = row0 + m;
-          const float pr = p.prob_perm[grow];
-          float v[32];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const f32x4 w = *reinterpret_cast<const f32x4*>(smem + epi_off(m, b * 8 + c));
-            v[4 * c] = w[0] * pr; v[4 * c + 1] = w[1] * pr; v[4 * c + 2] = w[2] * pr; v[4 * c + 3] = w[3] * pr;
-          }
-          if (!kMx || p.save_h) {
-            uint16_t* dst = kMx ? p.save_h : reinterpret_cast<uint16_t*>(p.out);
-            u32x4* d = reinterpret_cast<u32x4*>(dst + grow * I + col);
-#pragma unroll
-            for (int c = 0; c < 4; ++c)
-              d[c] = u32x4{pack_bf16x2(v[8 * c], v[8 * c + 1]), pack_bf16x2(v[8 * c + 2], v[8 * c + 3]),
-                           pack_bf16x2(v[8 * c + 4], v[8 * c + 5]), pack_bf16x2(v[8 * c + 6], v[8 * c + 7])};
-          }
-          if constexpr (kMx) {
-            float am = 0.f;
-#pragma unroll
-            for (int c = 0; c < 32; ++c) am = fmaxf(am, fabsf(v[c]));
-            const int sx = mx_shared_exp(am);
-            u32x4 lo, hi;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              lo[c] = mx_pack4(v[4 * c], v[4 * c + 1], v[4 * c + 2], v[4 * c + 3], sx);
-              hi[c] = mx_pack4(v[16 + 4 * c], v[16 + 4 * c + 1], v[16 + 4 * c + 2], v[16 + 4 * c + 3], sx);
-            }
-            u32x4* d = reinterpret_cast<u32x4*>(p.out + grow * I + col);
-            d[0] = lo;
-            d[1] = hi;
-            p.out_scales[grow * (I / 32) + col / 32] = (uint8_t)(sx + 127);
-          }
+        for (int q = 0; q < 16; ++q) {
+          mm(f1, q);
+          if (q & 1) read_elem<kMx, kFc1>(f0, sA, sS, 2, next_elem(q >> 1), wm, wn, lane);
+          else dma_b(dd, bn, kn, q >> 1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      __syncthreads();
-    } else {
-      const int64_t n0 = (int64_t)nt * kBN;
-      // a split part stores its whole fp32 tile, row-major [256][256], to its slot of p.part;
-      // fc2_fixup_kernel sums the parts
-      if constexpr (kOutF32) {
-        const bool sp = part >= 0;
-        float* const fdst = sp ? p.part + (size_t)(t - full) * 65536 : reinterpret_cast<float*>(p.out);
-        const int64_t fld = sp ? 256 : N;
-        const int64_t frow0 = sp ? 0 : row0, fcol0 = sp ? 0 : n0;
-        const int fmrows = sp ? kBM : mrows;
-        const int64_t fN = sp ? 256 : N;
-        // fp32 output: two passes of 128 rows (a [128][256] fp32 tile is 128 KB)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          if (wm == half) {
+        for (int q = 0; q < 16; ++q) {
+          mm(f0, q);
+          if (q & 1) read_elem<kMx, kFc1>(f1, sA, sS, 3, next_elem(q >> 1), wm, wn, lane);
+          __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int n = wn * 128 + j * 32 + r32;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                  const int mb = g4 + (r & 3);
-                  const uint32_t off = epi_off_wide(mb, n >> 2) + (n & 3) * 4 + (uint32_t)((i * 32 + (r >> 2) * 8) * 1024);
-                  *reinterpret_cast<float*>(smem + off) = core.acc[i][j][r];
-                }
-                __builtin_amdgcn_sched_barrier(0);
-              }
-          }
-          __syncthreads();
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int u = q * 256 + etid;
-            const int ml = u >> 2, b = u & 3;     // 64-column block b of local row ml
-            const int m = half * 128 + ml;
-            const int64_t col = fcol0 + b * 64;
-            if (m < fmrows && col < fN) {
-              u32x4* d = reinterpret_cast<u32x4*>(fdst + (frow0 + m) * fld + col);
-#pragma unroll
-              for (int c = 0; c < 16; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off_wide(ml, b * 16 + c));
-            }
-          }
-          __syncthreads();
+        for (int q = 0; q < 16; ++q) {
+          mm(f1, q);
+          __builtin_amdgcn_sched_barrier(0);
         }
       } else {
-        // (A) bf16 into a rotated [256][256] LDS tile
+        // 2 substeps of MX MFMAs (twice as long as the BF16 ones): the next stage's 18 loads and the
+        // substep-1 reads between the MFMAs of substep 0
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = wn * 128 + j * 32 + r32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int m = wm * 128 + i * 32 + (r >> 2) * 8 + g4 + (r & 3);
-              const int mb = wm * 128 + g4 + (r & 3);
-              const uint32_t off = epi_off(mb, n >> 3) + (n & 7) * 2 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);
-              *reinterpret_cast<uint16_t*>(smem + off) = f32_to_bf16(core.acc[i][j][r]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 16; ++q) {
+          mm(f0, q);
+          if (q & 1) {
+            read_elem<kMx, kFc1>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
+            dma_b(dd, bn, kn, q >> 1);
+          } else {
+            dma_a(dd, bn, kn, q >> 1);
           }
-        __syncthreads();
-        // (B) a thread copies 64-column (128-byte) row segments out with 16-byte stores
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int u = q * 256 + etid;
-          const int m = u >> 2, b = u & 3;
-          const int64_t col = n0 + b * 64;
-          if (m < mrows && col < N) {
-            u32x4* d = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.out) + (int64_t)(row0 + m) * N + col);
-#pragma unroll
-            for (int c = 0; c < 8; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off(m, b * 8 + c));
-          }
+          if (q == 15) dma_s(dd, bn, kn);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          mm(f1, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
+    par = (par + n) & 1;
+
+    // ---- epilogue straight from the accumulators.  acc[i][j][4 q + c] of lane l is token row
+    // wm*128 + 32 i + l % 32 of the tile and output column (weight block j) + 8 q + 4 (l / 32) + c.
+    // Stores go through buffer descriptors that end at the tile's last row, so the rows of a
+    // ragged tile past the expert's tokens are dropped by the range check instead of by a branch.
+    // The lane id is laundered so the address arithmetic is redone per tile instead of being
+    // hoisted above the main loop, and each 32 x 32 block is finished before the next one is
+    // started, so only its accumulators are copied out of the AGPRs at a time.
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const int r32 = elane & 31, ch = (elane >> 5) * 4;
+    if constexpr (kFc1) {
+      const int64_t I = N;
+      const uint32_t I32 = (uint32_t)I;
+      const float* prs = reinterpret_cast<const float*>(smem + kPrOff) + ipar * 256;
+      const uint32_t mr = (uint32_t)cur.mrows;
+      const int64_t r0 = cur.row0;
+      const rsrc_t ro = kMx ? make_rsrc(p.out + r0 * I, mr * I32) : make_rsrc(p.out + r0 * I * 2, mr * I32 * 2);
+      const rsrc_t rsc = make_rsrc(kMx ? p.out_scales + r0 * (I / 32) : p.out, kMx ? mr * (I32 / 32) : 0);
+      const rsrc_t rh = make_rsrc(p.save_h ? p.save_h + r0 * I : nullptr, p.save_h ? mr * I32 * 2 : 0);
+      const rsrc_t rg = make_rsrc(p.save_gu ? p.save_gu + r0 * 2 * I : nullptr, p.save_gu ? mr * I32 * 4 : 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 128 + i * 32 + r32;
+        const float pr = prs[m];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const uint32_t col = (uint32_t)cur.nt * 128u + (uint32_t)(wn * 64 + jj * 32);   // h column of the block
+          if (col >= I32) continue;                                                         // wave-uniform
+          float g[16], u[16];
+          agpr_read16(core.acc[i][jj], g);
+          agpr_read16(core.acc[i][jj + 2], u);
+          const uint32_t e0 = (uint32_t)m * I32 + col + (uint32_t)ch;                       // element of h
+          if (p.save_gu) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const uint32_t o = (2 * (uint32_t)m * I32 + col + (uint32_t)(ch + 8 * q)) * 2u;
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(g[4 * q], g[4 * q + 1]), pack_bf16x2(g[4 * q + 2], g[4 * q + 3])}, rg, o, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(u[4 * q], u[4 * q + 1]), pack_bf16x2(u[4 * q + 2], u[4 * q + 3])}, rg, o + I32 * 2u, 0, 0);
+            }
+          }
+          float v[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = (silu_f(g[r]) * u[r]) * pr;
+          if (!kMx || p.save_h) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3])},
+                                                    kMx ? rh : ro, (e0 + 8u * q) * 2u, 0, 0);
+          }
+          if constexpr (kMx) {
+            // the 32-column block of this row is split between lanes l and l ^ 32
+            float am = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
+            am = fmaxf(am, __shfl_xor(am, 32, 64));
+            const int sx = mx_shared_exp(am);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              __builtin_amdgcn_raw_buffer_store_b32(mx_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], sx), ro, e0 + 8u * q, 0, 0);
+            // one scale byte per row and block, from the lane holding its first columns
+            const uint32_t so = ch == 0 ? (uint32_t)m * (I32 / 32) + col / 32 : 0xFFFFFFF0u;
+            __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sx + 127), rsc, so, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      const uint32_t N32 = (uint32_t)N;
+      const uint32_t esz_o = kOutF32 ? 4u : 2u;
+      rsrc_t ro;
+      uint32_t ld;                                   // row pitch in elements
+      if (kOutF32 && cur.part >= 0) {
+        // a split part stores its whole fp32 tile, row-major [256][256], to its slot of p.part;
+        // fc2_fixup_kernel sums the parts
+        ro = make_rsrc(p.part + (size_t)(cur.t - full) * 65536, 65536u * 4u);
+        ld = 256;
+      } else {
+        ro = make_rsrc(p.out + (int64_t)cur.row0 * N * esz_o, (uint32_t)cur.mrows * N32 * esz_o);
+        ld = N32;
+      }
+      // first column of the tile in the destination (0 for a part slot)
+      const uint32_t c0 = (kOutF32 && cur.part >= 0) ? 0u : (uint32_t)cur.nt * kBN;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = wm * 128 + i * 32 + r32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t tc = (uint32_t)(wn * 128 + j * 32);           // column of the block within the tile
+          if ((uint32_t)cur.nt * kBN + tc >= N32) continue;            // wave-uniform
+          float a[16];
+          agpr_read16(core.acc[i][j], a);
+          const uint32_t e0 = (uint32_t)m * ld + c0 + tc + (uint32_t)ch;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (kOutF32)
+              __builtin_amdgcn_raw_buffer_store_b128(f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, ro, (e0 + 8u * q) * 4u, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])},
+                                                    ro, (e0 + 8u * q) * 2u, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    cur = nxt;
+    dc = dn;
   }
+  wait_vmcnt<0>();
 }
 
 // Finishes the split tiles of an FC2 launch: the S row-major [256][256] fp32 partials of tile
