@@ -85,58 +85,6 @@ __device__ __forceinline__ void split_policy(int total, int G, int kU, int& full
   }
 }
 
-// Fragments of one MFMA K substep of a wave: 4 token blocks (a) and 4 weight blocks (b) of 32
-// rows, plus the E8M0 scale bytes of the lane's rows (MXFP8).
-template <bool kMx>
-struct FwdFrag {
-  typename std::conditional<kMx, i32x8, bf16x8>::type a[4], b[4];
-  int sa[4], sb[4];
-};
-
-// Element e of the fragments of substep kk, in the order the 16 MFMAs of a substep consume them:
-// a0, b0, b1, b2, b3, a1, a2, a3 (the MFMAs run token block i outer, weight block j inner).
-template <bool kMx, bool kFc1>
-__device__ __forceinline__ void read_elem(FwdFrag<kMx>& f, const uint8_t* sA, const uint32_t* sS, int kk, int e,
-                                          int wm, int wn, int lane) {
-  const int r32 = lane & 31, g = lane >> 5;
-  const bool isA = e == 0 || e >= 5;
-  const int idx = e == 0 ? 0 : (e >= 5 ? e - 4 : e - 1);
-  const int row = isA ? wm * 128 + idx * 32 + r32 : TileCore<kMx, kFc1>::brow(wn, idx) + r32;
-  const uint8_t* base = isA ? sA : sA + kTileBytes;
-  if constexpr (!kMx) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(base + swz(row, (uint32_t)(kk * 2 + g)));
-    if (isA) f.a[idx] = v; else f.b[idx] = v;
-  } else {
-    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + g)));
-    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + 2 + g)));
-    const i32x8 v{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    // the scale byte of this lane's 32-value block, read on its own: a shift of the whole word
-    // would make the read wait for LDS on the spot
-    const int sc = reinterpret_cast<const uint8_t*>(sS)[((isA ? 0 : 256) + row) * 4 + 2 * kk + g];
-    if (isA) { f.a[idx] = v; f.sa[idx] = sc; } else { f.b[idx] = v; f.sb[idx] = sc; }
-  }
-}
-
-// Order of the reads of the next substep's elements while the current substep's MFMAs run:
-// b0 b1 a0 b2 a1 b3 a2 a3 -- each a block is read only after the MFMAs that use the current one
-// are issued, so the two fragment sets share the a registers.
-__device__ __forceinline__ constexpr int next_elem(int s) {
-  return s == 0 ? 1 : s == 1 ? 2 : s == 2 ? 0 : s == 3 ? 3 : s == 4 ? 5 : s == 5 ? 4 : s;
-}
-
-// Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
-// allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
-// and spills.
-__device__ __forceinline__ float agpr_read(float x) {
-  float y;
-  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
-  return y;
-}
-__device__ __forceinline__ void agpr_read16(const f32x16& a, float (&o)[16]) {
-#pragma unroll
-  for (int r = 0; r < 16; ++r) o[r] = agpr_read(a[r]);
-}
-
 // One work item: a 256 x 256 output tile, or one K part of a split tile.
 struct FwdItem {
   int t, tile, part, e, mt, nt, row0, mrows, u0, u1;
@@ -285,17 +233,6 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     }
     TileCore<kMx, kFc1> core;
     core.zero();
-    typedef FwdFrag<kMx> Fr;
-    auto mm = [&](const Fr& f, int q) {
-      const int i = q >> 2, j = q & 3;
-      // weight block as the MFMA's A operand: each lane ends up with one token row and 16 output
-      // columns, in 4 runs of 4 consecutive columns
-      if constexpr (!kMx)
-        core.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], core.acc[i][j], 0, 0, 0);
-      else
-        core.acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], core.acc[i][j], 0, 0, 0,
-                                                                           f.sb[j], 0, f.sa[i]);
-    };
     const int n = cur.u1 - cur.u0;
 #pragma unroll 1
     for (int s = 0; s < n; ++s) {
@@ -310,64 +247,10 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const int kn = last ? nxt.u0 : kt + 1;
       const int bn = b ^ 1;
       const uint8_t* sA = smem + b * kStageBytes;
-      const uint32_t* sS = reinterpret_cast<const uint32_t*>(smem + kScOff + b * 2048);
-      Fr f0, f1;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        read_elem<kMx, kFc1>(f0, sA, sS, 0, e, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (!kMx) {
-        // 4 substeps: the A loads of the next stage and the substep-1 reads between the MFMAs of
-        // substep 0, the B loads and the substep-2 reads in substep 1, the substep-3 reads in
-        // substep 2 -- at most one memory instruction per MFMA, so neither the texture unit nor
-        // the LDS queue backs up and stalls the wave's MFMA issue
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          mm(f0, q);
-          if (q & 1) read_elem<kMx, kFc1>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
-          else dma_a(dd, bn, kn, q >> 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          mm(f1, q);
-          if (q & 1) read_elem<kMx, kFc1>(f0, sA, sS, 2, next_elem(q >> 1), wm, wn, lane);
-          else dma_b(dd, bn, kn, q >> 1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          mm(f0, q);
-          if (q & 1) read_elem<kMx, kFc1>(f1, sA, sS, 3, next_elem(q >> 1), wm, wn, lane);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          mm(f1, q);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        // 2 substeps of MX MFMAs (twice as long as the BF16 ones): the next stage's 18 loads and the
-        // substep-1 reads between the MFMAs of substep 0
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          mm(f0, q);
-          if (q & 1) {
-            read_elem<kMx, kFc1>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
-            dma_b(dd, bn, kn, q >> 1);
-          } else {
-            dma_a(dd, bn, kn, q >> 1);
-          }
-          if (q == 15) dma_s(dd, bn, kn);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          mm(f1, q);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+      const uint8_t* sS = smem + kScOff + b * 2048;
+      mma_stage<kMx, kFc1, false, false>(
+          core, sA, sS, wm, wn, lane, [&](int q) { dma_a(dd, bn, kn, q); }, [&](int q) { dma_b(dd, bn, kn, q); },
+          [&]() { dma_s(dd, bn, kn); });
     }
     par = (par + n) & 1;
 

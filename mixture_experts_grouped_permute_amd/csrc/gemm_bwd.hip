@@ -11,10 +11,13 @@
 //              with no tokens gets an all-zero dW_e)
 //
 // BF16 operands whose contiguous dimension is M or N (the weights in dgrad,
-// both token-major activations in wgrad) are loaded as 8 x 8 bf16 blocks and
-// transposed in registers (v_perm_b32) into the same K-major, XOR-swizzled LDS
-// layout the MFMA core reads.  MXFP8 operands arrive already quantized along
-// each GEMM's K in K-major layout, so they use the plain row loader.
+// both token-major activations in wgrad) are staged in LDS as they are stored
+// (mnswz layout) and read with gfx950's transposing LDS load
+// (ds_read_b64_tr_b16), which delivers the MFMA's K-major operand layout.
+// MXFP8 operands arrive already quantized along each GEMM's K in K-major
+// layout.  The main loop is the forward's interleaved stage schedule, the last
+// stage of a tile loads the first stage of the next one, and the epilogues
+// store straight from the accumulators.
 #include "gemm_core.h"
 
 namespace moe {
@@ -57,79 +60,11 @@ __device__ __forceinline__ const uint8_t* bwd_table(int e) {
 #endif
 }
 
-// Write a 256 x 256 fp32 accumulator tile to dst (row stride ld elements), rows < mrows and
-// columns < ncols (a multiple of 64) only, through LDS: bf16 in one pass, fp32 in two halves.
-template <bool kF32, class Core>
-__device__ __forceinline__ void store_tile(const Core& core, uint8_t* smem, uint8_t* dst, int64_t ld, int mrows,
-                                           int ncols, int wm, int wn, int elane, int etid) {
-  const int r32 = elane & 31, g4 = (elane >> 5) * 4;
-  if constexpr (!kF32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = wn * 128 + j * 32 + r32;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int mb = wm * 128 + g4 + (r & 3);
-          const uint32_t off = epi_off(mb, n >> 3) + (n & 7) * 2 + (uint32_t)((i * 32 + (r >> 2) * 8) * 512);
-          *reinterpret_cast<uint16_t*>(smem + off) = f32_to_bf16(core.acc[i][j][r]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int u = q * 256 + etid;
-      const int m = u >> 2, b = u & 3;
-      if (m < mrows && b * 64 < ncols) {
-        u32x4* d = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(dst) + (int64_t)m * ld + b * 64);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off(m, b * 8 + c));
-      }
-    }
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      if (wm == half) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int n = wn * 128 + j * 32 + r32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int mb = g4 + (r & 3);
-              const uint32_t off =
-                  epi_off_wide(mb, n >> 2) + (n & 3) * 4 + (uint32_t)((i * 32 + (r >> 2) * 8) * 1024);
-              *reinterpret_cast<float*>(smem + off) = core.acc[i][j][r];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int u = q * 256 + etid;
-        const int ml = u >> 2, b = u & 3;
-        const int m = half * 128 + ml;
-        if (m < mrows && b * 64 < ncols) {
-          u32x4* d = reinterpret_cast<u32x4*>(reinterpret_cast<float*>(dst) + (int64_t)m * ld + b * 64);
-#pragma unroll
-          for (int c = 0; c < 16; ++c) d[c] = *reinterpret_cast<const u32x4*>(smem + epi_off_wide(ml, b * 16 + c));
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// Store the 8 transposed columns of one 8x8 block: column c goes to LDS row nb*8 + c, chunk kb.
-__device__ __forceinline__ void store_t8(uint8_t* s, const u32x4 w[8], int nb, int kb) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(s + swz(nb * 8 + c, kb)) = w[c];
-}
+// One work item of the backward kernel: a 256 x 256 output tile and its K extent.
+struct BwdItem {
+  int t, e, mt, nt, row0, mrows, ncols, kT, Me;
+  int64_t koff;
+};
 
 template <int kRole, bool kMx, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -137,8 +72,13 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   constexpr bool kWg = kRole == kRoleWgrad;
   constexpr bool kAMN = kWg && !kMx;   // bf16 wgrad: A is token-major
   constexpr bool kBMN = !kMx;          // bf16: B is N-contiguous (weights in dgrad, activations in wgrad)
-  // two stages of A + B (64 KB each; the epilogue reuses them) plus the MXFP8 scale words
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes + (kMx ? 2 * 2048 : 16)];
+  constexpr bool kD2 = kRole == kRoleDgradFc2;
+  // two stages of A + B (64 KB each), the MXFP8 scale words (2 x 2 KB), and for the FC2 dgrad the
+  // routing probabilities of the tile's rows (2 x 1 KB, by work item) and the per-row dprob
+  // partials of the two wave columns (2 x 1 KB)
+  constexpr int kScOff = 2 * kStageBytes;
+  constexpr int kXOff = kScOff + (kMx ? 2 * 2048 : 0);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXOff + (kD2 ? 4096 : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -148,222 +88,285 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   const int G = gridDim.x, per = G >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   constexpr int kKStep = kMx ? 128 : 64;                  // K values per LDS stage
 
-  for (int round = 0;; ++round) {
-    const int t = round * G + xcd * per + slot;
-    if (t >= total) break;
-    int e, mt, nt, row0, mrows, ncols, kT;
-    int64_t koff = 0;
+  auto decode = [&](int round, BwdItem& it) {
+    it.t = round * G + xcd * per + slot;
+    it.kT = 0;
+    if (it.t >= total) return;
     if constexpr (kWg) {
       const int pe = p.nM * p.nN;
-      e = t / pe;
-      const int local = t - e * pe;
-      mt = local % p.nM;
-      nt = local / p.nM;
-      const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
-      koff = kMx ? __builtin_amdgcn_readfirstlane(sched.tile[e]) : __builtin_amdgcn_readfirstlane(sched.off[e]);
-      kT = (Me + kKStep - 1) / kKStep;
-      row0 = mt * kBM;
-      mrows = (int)min((int64_t)kBM, p.M - row0);
-      ncols = (int)min((int64_t)kBN, p.N - (int64_t)nt * kBN);
+      it.e = it.t / pe;
+      const int local = it.t - it.e * pe;
+      it.mt = local % p.nM;
+      it.nt = local / p.nM;
+      it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
+      it.koff = kMx ? __builtin_amdgcn_readfirstlane(sched.tile[it.e]) : __builtin_amdgcn_readfirstlane(sched.off[it.e]);
+      it.kT = (it.Me + kKStep - 1) / kKStep;
+      it.row0 = it.mt * kBM;
+      it.mrows = (int)min((int64_t)kBM, p.M - it.row0);
     } else {
-      e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, t));
-      const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
-      const int nMe = (Me + kBM - 1) / kBM;
-      const int local = t - __builtin_amdgcn_readfirstlane(sched.tile[e]);
-      mt = local % nMe;
-      nt = local / nMe;
-      row0 = __builtin_amdgcn_readfirstlane(sched.off[e]) + mt * kBM;
-      mrows = min(kBM, Me - mt * kBM);
-      ncols = (int)min((int64_t)kBN, p.N - (int64_t)nt * kBN);
-      kT = (int)(p.K * (kMx ? 1 : 2) / kRowBytes);
+      it.e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, it.t));
+      it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
+      const int nMe = (it.Me + kBM - 1) / kBM;
+      const int local = it.t - __builtin_amdgcn_readfirstlane(sched.tile[it.e]);
+      it.mt = local % nMe;
+      it.nt = local / nMe;
+      it.row0 = __builtin_amdgcn_readfirstlane(sched.off[it.e]) + it.mt * kBM;
+      it.mrows = min(kBM, it.Me - it.mt * kBM);
+      it.koff = 0;
+      it.kT = (int)(p.K * (kMx ? 1 : 2) / kRowBytes);
     }
-    const int64_t n0 = (int64_t)nt * kBN;
-    const int64_t m0w = (int64_t)mt * kBM;                // wgrad output row origin
+    it.ncols = (int)min((int64_t)kBN, p.N - (int64_t)it.nt * kBN);
+  };
 
-    // ---- operands: two LDS stages of A and B (32 KB each) filled by direct-to-LDS loads
-    // (buffer_load_dwordx4 ... lds, lane L's 16 bytes to slot L of a contiguous 1 KB block).
-    //   K-major operand: 256 rows x 128 bytes of K in the swz layout; load q of wave w fills row
-    //     pairs j = 4 (8w + q) + L / 16, slot s = L % 16 holding (row parity, chunk) = s ^ hs(j).
-    //   MN-major operand (bf16, K rows of 256 contiguous columns): 64 K rows x 512 bytes in the
-    //     mnswz layout; load q of wave w fills rows 2 (8w + q) + L / 32, physical chunk L % 32.
-    //     The K row advance is carried in the per-lane offset so that rows past the end of the
-    //     operand (a ragged token segment in wgrad) fall outside the descriptor and read zero.
-    //   MXFP8 operands are K-major, with one 4-byte E8M0 word per row per stage.
+  // ---- operands: two LDS stages of A and B (32 KB each) filled by direct-to-LDS loads
+  // (buffer_load_dwordx4 ... lds, lane L's 16 bytes to slot L of a contiguous 1 KB block).
+  //   K-major operand: 256 rows x 128 bytes of K in the swz layout; load q of wave w fills row
+  //     pairs j = 4 (8w + q) + L / 16, slot s = L % 16 holding (row parity, chunk) = s ^ hs(j).
+  //   MN-major operand (bf16, K rows of 256 contiguous columns): 64 K rows x 512 bytes in the
+  //     mnswz layout; load q of wave w fills rows 2 (8w + q) + L / 32, physical chunk L % 32.
+  //     The K row advance is carried in the per-lane offset so that rows past the end of the
+  //     operand (a ragged token segment in wgrad) fall outside the descriptor and read zero.
+  //   MXFP8 operands are K-major, with one 4-byte E8M0 word per row per stage.
+  // Invalid items and items without K stages get zero-range descriptors: their loads touch no
+  // memory.
+  struct Desc { i32x4 va, vb, vas, vbs; };
+  auto descs = [&](const BwdItem& it, Desc& d) {
+    if (it.t >= total || it.kT == 0) {
+      d.va = make_vsharp(p.a, 0); d.vb = d.va; d.vas = d.va; d.vbs = d.va;
+      return;
+    }
+    const int64_t n0 = (int64_t)it.nt * kBN;
+    const int64_t m0w = (int64_t)it.mt * kBM;
     int64_t a_base_off, b_base_off;
     uint32_t a_range, b_range;
-    const uint8_t* abase;
     const uint8_t* bbase;
     if constexpr (kAMN) {            // bf16 wgrad: A^T = token-major rows [tok][M]
-      const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
-      abase = p.a; a_base_off = koff * p.lda + m0w * 2; a_range = (uint32_t)max((int64_t)0, Me * p.lda - m0w * 2);
+      a_base_off = it.koff * p.lda + m0w * 2; a_range = (uint32_t)max((int64_t)0, it.Me * p.lda - m0w * 2);
     } else if constexpr (kWg) {      // MXFP8 wgrad: A^T quantized [M][Rpad], segment at koff
-      abase = p.a; a_base_off = m0w * p.lda + koff; a_range = (uint32_t)(mrows * p.lda);
+      a_base_off = m0w * p.lda + it.koff; a_range = (uint32_t)(it.mrows * p.lda);
     } else {
-      abase = p.a; a_base_off = (int64_t)row0 * p.lda; a_range = (uint32_t)(mrows * p.lda);
+      a_base_off = (int64_t)it.row0 * p.lda; a_range = (uint32_t)(it.mrows * p.lda);
     }
     if constexpr (kBMN) {
       if constexpr (kWg) {           // bf16 wgrad: token-major rows [tok][N]
-        const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[e]);
-        bbase = p.b; b_base_off = koff * p.ldb + n0 * 2; b_range = (uint32_t)max((int64_t)0, Me * p.ldb - n0 * 2);
+        bbase = p.b; b_base_off = it.koff * p.ldb + n0 * 2; b_range = (uint32_t)max((int64_t)0, it.Me * p.ldb - n0 * 2);
       } else {                       // bf16 dgrad: W_e [K][N]
-        bbase = bwd_table(e); b_base_off = n0 * 2; b_range = (uint32_t)(p.K * p.ldb - n0 * 2);
+        bbase = bwd_table(it.e); b_base_off = n0 * 2; b_range = (uint32_t)(p.K * p.ldb - n0 * 2);
       }
     } else if constexpr (kWg) {      // MXFP8 wgrad: B^T quantized [N][Rpad]
-      bbase = p.b; b_base_off = n0 * p.ldb + koff; b_range = (uint32_t)(ncols * p.ldb);
+      bbase = p.b; b_base_off = n0 * p.ldb + it.koff; b_range = (uint32_t)(it.ncols * p.ldb);
     } else {                         // MXFP8 dgrad: W^T quantized [N][K] per expert
-      bbase = p.b + (int64_t)e * p.b_stride; b_base_off = n0 * p.ldb; b_range = (uint32_t)(ncols * p.ldb);
+      bbase = p.b + (int64_t)it.e * p.b_stride; b_base_off = n0 * p.ldb; b_range = (uint32_t)(it.ncols * p.ldb);
     }
-    const i32x4 va = make_vsharp(abase + a_base_off, a_range);
-    const i32x4 vb = make_vsharp(bbase + b_base_off, b_range);
-    uint32_t a_vo[8], b_vo[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      // K-major slot mapping
-      const int j = (wave * 8 + q) * 4 + (lane >> 4);
-      const uint32_t hs = (uint32_t)((j & 7) | ((j & 4) << 1));
-      const uint32_t sl = (uint32_t)(lane & 15) ^ hs;
-      const int rk = 2 * j + (int)(sl >> 3);
-      const uint32_t ck = sl & 7u;
-      // MN-major slot mapping
-      const int rm = 2 * (wave * 8 + q) + (lane >> 5);
-      const uint32_t cm = (uint32_t)(lane & 31) ^ (((uint32_t)rm & 3u) << 2);
-      a_vo[q] = kAMN ? (uint32_t)(rm * p.lda) + cm * 16 : (uint32_t)(rk * p.lda) + ck * 16;
-      b_vo[q] = kBMN ? (uint32_t)(rm * p.ldb) + cm * 16 : (uint32_t)(rk * p.ldb) + ck * 16;
-    }
-    // per-stage advance of the offsets: K-major along the row (128 bytes), MN-major 64 rows down
-    const uint32_t a_step = kAMN ? (uint32_t)(64 * p.lda) : (uint32_t)kRowBytes;
-    const uint32_t b_step = kBMN ? (uint32_t)(64 * p.ldb) : (uint32_t)kRowBytes;
-    const uint32_t lds0 = lds_addr(smem) + (uint32_t)(wave * 8) * 1024u;
-    i32x4 vas = va, vbs = vb;
-    uint32_t as_vo = 0, bs_vo = 0;
+    d.va = make_vsharp(p.a + a_base_off, a_range);
+    d.vb = make_vsharp(bbase + b_base_off, b_range);
     if constexpr (kMx) {
-      const int r = wave * 64 + lane;
       if constexpr (kWg) {
-        vas = make_vsharp(p.as + m0w * p.ldas + koff / 32, (uint32_t)(mrows * p.ldas));
-        vbs = make_vsharp(p.bs + n0 * p.ldbs + koff / 32, (uint32_t)(ncols * p.ldbs));
+        d.vas = make_vsharp(p.as + m0w * p.ldas + it.koff / 32, (uint32_t)(it.mrows * p.ldas));
+        d.vbs = make_vsharp(p.bs + n0 * p.ldbs + it.koff / 32, (uint32_t)(it.ncols * p.ldbs));
       } else {
-        vas = make_vsharp(p.as + (int64_t)row0 * p.ldas, (uint32_t)(mrows * p.ldas));
-        vbs = make_vsharp(p.bs + (int64_t)e * p.bs_stride + n0 * p.ldbs, (uint32_t)(ncols * p.ldbs));
+        d.vas = make_vsharp(p.as + (int64_t)it.row0 * p.ldas, (uint32_t)(it.mrows * p.ldas));
+        d.vbs = make_vsharp(p.bs + (int64_t)it.e * p.bs_stride + n0 * p.ldbs, (uint32_t)(it.ncols * p.ldbs));
       }
-      as_vo = (uint32_t)(r * p.ldas);
-      bs_vo = (uint32_t)(r * p.ldbs);
+    } else {
+      d.vas = d.va;
+      d.vbs = d.vb;
     }
-    const uint32_t lds_sc = lds_addr(smem + 2 * kStageBytes) + (uint32_t)wave * 256u;
+  };
 
+  uint32_t a_vo[8], b_vo[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    // K-major slot mapping
+    const int j = (wave * 8 + q) * 4 + (lane >> 4);
+    const uint32_t hs = (uint32_t)((j & 7) | ((j & 4) << 1));
+    const uint32_t sl = (uint32_t)(lane & 15) ^ hs;
+    const int rk = 2 * j + (int)(sl >> 3);
+    const uint32_t ck = sl & 7u;
+    // MN-major slot mapping
+    const int rm = 2 * (wave * 8 + q) + (lane >> 5);
+    const uint32_t cm = (uint32_t)(lane & 31) ^ (((uint32_t)rm & 3u) << 2);
+    a_vo[q] = kAMN ? (uint32_t)(rm * p.lda) + cm * 16 : (uint32_t)(rk * p.lda) + ck * 16;
+    b_vo[q] = kBMN ? (uint32_t)(rm * p.ldb) + cm * 16 : (uint32_t)(rk * p.ldb) + ck * 16;
+  }
+  // per-stage advance of the offsets: K-major along the row (128 bytes), MN-major 64 rows down
+  const uint32_t a_step = kAMN ? (uint32_t)(64 * p.lda) : (uint32_t)kRowBytes;
+  const uint32_t b_step = kBMN ? (uint32_t)(64 * p.ldb) : (uint32_t)kRowBytes;
+  uint32_t as_vo = 0, bs_vo = 0;
+  if constexpr (kMx) {
+    const int r = wave * 64 + lane;
+    as_vo = (uint32_t)(r * p.ldas);
+    bs_vo = (uint32_t)(r * p.ldbs);
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
+  const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * 256u);
+  auto dma_a = [&](const Desc& d, int b, int kt, int q) {
+    dma16(d.va, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q] + (uint32_t)kt * a_step, 0);
+  };
+  auto dma_b = [&](const Desc& d, int b, int kt, int q) {
+    dma16(d.vb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q] + (uint32_t)kt * b_step, 0);
+  };
+  auto dma_s = [&](const Desc& d, int b, int kt) {
+    if constexpr (kMx) {
+      const uint32_t ss = lds_sc + (uint32_t)b * 2048u;
+      dma4(d.vas, ss, as_vo + (uint32_t)kt * 4u, 0);
+      dma4(d.vbs, ss + 1024u, bs_vo + (uint32_t)kt * 4u, 0);
+    }
+  };
+
+  BwdItem cur, nxt;
+  Desc dc, dn;
+  decode(0, cur);
+  descs(cur, dc);
+  int par = 0;             // buffer of the current item's first stage
+  bool issued = false;     // the current item's first stage was loaded by the previous item
+  for (int round = 0; cur.t < total; ++round) {
+    decode(round + 1, nxt);
+    descs(nxt, dn);
+    const int ipar = round & 1;
+    if constexpr (kD2) {
+      const float pr = tid < cur.mrows ? p.prob_perm[cur.row0 + tid] : 0.f;
+      reinterpret_cast<float*>(smem + kXOff)[ipar * 256 + tid] = pr;
+    }
+    if (!issued && cur.kT > 0) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { dma_a(dc, par, 0, q); dma_b(dc, par, 0, q); }
+      dma_s(dc, par, 0);
+    }
+    // the last stage loads the next item's first one, if it has any stage
+    const bool chain = nxt.t < total && nxt.kT > 0;
     TileCore<kMx, false> core;
     core.zero();
-    auto issue = [&](int kt) {
-      const uint32_t sa = lds0 + (uint32_t)(kt & 1) * (uint32_t)kStageBytes;
-      const uint32_t ao = (uint32_t)kt * a_step, bo = (uint32_t)kt * b_step;
+#pragma unroll 1
+    for (int s = 0; s < cur.kT; ++s) {
+      const int b = (par + s) & 1;
+      // stage s landed (own loads + barrier); every wave finished reading the other buffer, which
+      // takes the next stage while this one is multiplied
+      wait_vmcnt<0>();
+      __syncthreads();
+      const bool last = s + 1 == cur.kT;
+      const Desc& dd = last ? dn : dc;
+      const int kn = last ? 0 : s + 1;
+      const int bn = b ^ 1;
+      const uint8_t* sA = smem + b * kStageBytes;
+      const uint8_t* sS = smem + kScOff + b * 2048;
+      mma_stage<kMx, false, kAMN, kBMN>(
+          core, sA, sS, wm, wn, lane, [&](int q) { dma_a(dd, bn, kn, q); }, [&](int q) { dma_b(dd, bn, kn, q); },
+          [&]() { dma_s(dd, bn, kn); });
+    }
+    issued = cur.kT > 0 && chain;
+    par = (par + cur.kT) & 1;
+
+    // ---- epilogue straight from the accumulators: acc[i][j][4 q + c] of lane l is output row
+    // wm*128 + 32 i + l % 32 of the tile and column wn*128 + 32 j + 8 q + 4 (l / 32) + c.  Loads and
+    // stores go through buffer descriptors that end at the tile's last valid row.
+    int elane = lane;
+    asm volatile("" : "+v"(elane));
+    const int r32 = elane & 31, ch = (elane >> 5) * 4;
+    const int64_t n0 = (int64_t)cur.nt * kBN;
+    if constexpr (kD2) {
+      // ScaledSwiGLU backward per element (dh = this tile, g / u = the saved gate-up output,
+      // p = the routing probability of the row):
+      //   dG = dh p u s (1 + g (1 - s)), dU = dh p g s, s = sigmoid(g); dprob partial = sum dh g s u.
+      // The saved g / u of the next 32 x 32 block are loaded while this one is computed.
+      const int64_t I = p.I;
+      const uint32_t I32 = (uint32_t)I;
+      const float* prs = reinterpret_cast<const float*>(smem + kXOff) + ipar * 256;
+      float* red = reinterpret_cast<float*>(smem + kXOff + 2048);
+      const uint32_t mr = (uint32_t)cur.mrows;
+      const rsrc_t rgu = make_rsrc(p.gu + (int64_t)cur.row0 * 2 * I, mr * I32 * 4);
+      const rsrc_t rdg = make_rsrc(p.dgu + (int64_t)cur.row0 * 2 * I, mr * I32 * 4);
+      u32x2 gl[2][4], ul[2][4];
+      auto boff = [&](int blk, int q) -> uint32_t {   // byte offset of run q of block blk (gate half)
+        const int i = blk >> 2, j = blk & 3;
+        const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
+        return (2 * m * I32 + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32 + ch + 8 * q)) * 2u;
+      };
+      auto load = [&](int blk, int bf) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) dma16(va, sa + q * 1024u, a_vo[q] + ao, 0);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) dma16(vb, sa + kTileBytes + q * 1024u, b_vo[q] + bo, 0);
-      if constexpr (kMx) {
-        const uint32_t ss = lds_sc + (uint32_t)(kt & 1) * 2048u;
-        dma4(vas, ss, as_vo + (uint32_t)kt * 4u, 0);
-        dma4(vbs, ss + 1024u, bs_vo + (uint32_t)kt * 4u, 0);
-      }
-    };
-    if (kT > 0) {
-      issue(0);
-      for (int kt = 0; kt < kT; ++kt) {
-        // stage kt landed (own loads + barrier); every wave finished stage kt-1, whose buffer
-        // takes stage kt+1 while stage kt is multiplied
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (kt + 1 < kT) issue(kt + 1);
-        const uint8_t* sA = smem + (kt & 1) * kStageBytes;
-        if constexpr (kMx) {
-          const uint32_t* sS = reinterpret_cast<const uint32_t*>(smem + 2 * kStageBytes + (kt & 1) * 2048);
-          core.compute(sA, sA + kTileBytes, sS, sS + 256, wm, wn, lane);
-        } else {
-          core.template compute_x<kAMN, kBMN>(sA, sA + kTileBytes, wm, wn, lane);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t o = boff(blk, q);
+          gl[bf][q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rgu, o, 0, 0));
+          ul[bf][q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rgu, o + I32 * 2u, 0, 0));
         }
+      };
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+      load(0, 0);
+#pragma unroll
+      for (int blk = 0; blk < 16; ++blk) {
+        const int i = blk >> 2, j = blk & 3, bf = blk & 1;
+        if (blk + 1 < 16) load(blk + 1, bf ^ 1);
+        const bool cv = n0 + wn * 128 + j * 32 < I;                 // wave-uniform
+        if (cv) {
+          const float pr = prs[wm * 128 + i * 32 + r32];
+          float dh[16];
+          agpr_read16(core.acc[i][j], dh);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float dgv[4], duv[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+              const uint32_t gw = gl[bf][q][x >> 1], uw = ul[bf][q][x >> 1];
+              const float g = bf16_to_f32((uint16_t)((x & 1) ? (gw >> 16) : (gw & 0xFFFF)));
+              const float uu = bf16_to_f32((uint16_t)((x & 1) ? (uw >> 16) : (uw & 0xFFFF)));
+              const float d = dh[4 * q + x];
+              const float sg = sigmoid_f(g);
+              const float sl = g * sg;
+              part[i] += d * (sl * uu);
+              const float da = d * pr;
+              duv[x] = da * sl;
+              dgv[x] = da * uu * (sg * (1.0f + g * (1.0f - sg)));
+            }
+            const uint32_t o = boff(blk, q);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3])}, rdg, o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3])}, rdg,
+                                                  o + I32 * 2u, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // per-row partial over the tile's 256 columns: the lane pair (l, l ^ 32) holds a row's 128
+      // columns of this wave, the two waves of a row block the two halves -- fixed-order sums
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = part[i] + __shfl_xor(part[i], 32, 64);
+        if (ch == 0) red[wn * 256 + wm * 128 + i * 32 + r32] = s;
       }
       __syncthreads();
-    }
-
-    // ---- epilogue
-    int elane = lane, etid = tid;
-    asm volatile("" : "+v"(elane), "+v"(etid));
-    if constexpr (kRole == kRoleDgradFc2) {
-      const int r32 = elane & 31, g4 = (elane >> 5) * 4;
-      const int64_t I = p.I;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        if (wm == half) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const int n = wn * 128 + j * 32 + r32;
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int mb = g4 + (r & 3);
-                const uint32_t off =
-                    epi_off_wide(mb, n >> 2) + (n & 3) * 4 + (uint32_t)((i * 32 + (r >> 2) * 8) * 1024);
-                *reinterpret_cast<float*>(smem + off) = core.acc[i][j][r];
-              }
-              __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int u = q * 256 + etid;
-          const int ml = u >> 2, b = u & 3;
-          const int m = half * 128 + ml;
-          const int64_t col = n0 + b * 64;
-          float part = 0.f;
-          if (m < mrows && col < I) {
-            const int64_t grow = row0 + m;
-            const float pr = p.prob_perm[grow];
-            const uint16_t* gp = p.gu + grow * 2 * I + col;
-            uint16_t* dgp = p.dgu + grow * 2 * I + col;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              const f32x4 d0 = *reinterpret_cast<const f32x4*>(smem + epi_off_wide(ml, b * 16 + 2 * c));
-              const f32x4 d1 = *reinterpret_cast<const f32x4*>(smem + epi_off_wide(ml, b * 16 + 2 * c + 1));
-              const u32x4 gw = *reinterpret_cast<const u32x4*>(gp + 8 * c);
-              const u32x4 uw = *reinterpret_cast<const u32x4*>(gp + I + 8 * c);
-              float dgv[8], duv[8];
-#pragma unroll
-              for (int x = 0; x < 8; ++x) {
-                const float dh = x < 4 ? d0[x] : d1[x - 4];
-                const uint32_t gwd = gw[x >> 1], uwd = uw[x >> 1];
-                const float g = bf16_to_f32((uint16_t)((x & 1) ? (gwd >> 16) : (gwd & 0xFFFF)));
-                const float uu = bf16_to_f32((uint16_t)((x & 1) ? (uwd >> 16) : (uwd & 0xFFFF)));
-                const float s = sigmoid_f(g);
-                const float sl = g * s;
-                part += dh * (sl * uu);
-                const float da = dh * pr;
-                duv[x] = da * sl;
-                dgv[x] = da * uu * (s * (1.0f + g * (1.0f - s)));
-              }
-              *reinterpret_cast<u32x4*>(dgp + 8 * c) =
-                  u32x4{pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3]), pack_bf16x2(dgv[4], dgv[5]),
-                        pack_bf16x2(dgv[6], dgv[7])};
-              *reinterpret_cast<u32x4*>(dgp + I + 8 * c) =
-                  u32x4{pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3]), pack_bf16x2(duv[4], duv[5]),
-                        pack_bf16x2(duv[6], duv[7])};
-            }
-          }
-          // the 4 column blocks of a row sit in 4 consecutive lanes: fixed-order pairwise sum
-          part += __shfl_xor(part, 1, 64);
-          part += __shfl_xor(part, 2, 64);
-          if (b == 0 && m < mrows) p.dprob_part[(int64_t)(row0 + m) * p.nN + nt] = part;
-        }
-        __syncthreads();
-      }
-    } else if constexpr (kRole == kRoleDgradFc1) {
-      uint8_t* dst = p.out + ((int64_t)row0 * p.N + n0) * (kOutF32 ? 4 : 2);
-      store_tile<kOutF32>(core, smem, dst, p.N, mrows, ncols, wm, wn, elane, etid);
+      if (tid < cur.mrows) p.dprob_part[(int64_t)(cur.row0 + tid) * p.nN + cur.nt] = red[tid] + red[256 + tid];
     } else {
-      uint8_t* dst = const_cast<uint8_t*>(bwd_table(e)) + (m0w * p.N + n0) * (kOutF32 ? 4 : 2);
-      store_tile<kOutF32>(core, smem, dst, p.N, mrows, ncols, wm, wn, elane, etid);
+      // FC1 dgrad: dx_perm rows of the tile; wgrad: rows m0w.. of dW_e
+      const uint32_t N32 = (uint32_t)p.N;
+      const uint32_t es = kOutF32 ? 4u : 2u;
+      const int64_t r0 = kWg ? (int64_t)cur.mt * kBM : (int64_t)cur.row0;
+      uint8_t* obase = kWg ? const_cast<uint8_t*>(bwd_table(cur.e)) : p.out;
+      const rsrc_t ro = make_rsrc(obase + r0 * p.N * es, (uint32_t)cur.mrows * N32 * es);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t col = (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);
+          if (col >= N32) continue;                                  // wave-uniform
+          float a[16];
+          agpr_read16(core.acc[i][j], a);
+          const uint32_t e0 = m * N32 + col + (uint32_t)ch;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if constexpr (kOutF32)
+              __builtin_amdgcn_raw_buffer_store_b128(f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, ro, (e0 + 8u * q) * 4u, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])},
+                                                    ro, (e0 + 8u * q) * 2u, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
+    cur = nxt;
+    dc = dn;
   }
+  wait_vmcnt<0>();
 }
 
 template <int kRole, bool kMx>

@@ -1,7 +1,7 @@
-// Shared pieces of the grouped GEMMs for gfx950: buffer-resource loads, the
-// swizzled LDS layout, the in-kernel per-expert tile scheduler, the 256x256
-// MFMA tile core (BF16 32x32x16 and MX-scaled FP8 32x32x64) and the rotated
-// LDS staging layout of the epilogues.
+// Shared pieces of the grouped GEMMs for gfx950: buffer descriptors and
+// direct-to-LDS loads, the swizzled LDS layouts, the in-kernel per-expert tile
+// scheduler, the 256x256 tile's accumulators and the interleaved stage schedule
+// of its MFMAs (BF16 32x32x16 and MX-scaled FP8 32x32x64).
 #pragma once
 #include <cstddef>
 #include <type_traits>
@@ -16,18 +16,11 @@ constexpr int kBM = 256, kBN = 256;
 constexpr int kRowBytes = 128;
 constexpr int kTileBytes = 256 * kRowBytes;     // 32 KB per operand tile
 constexpr int kStageBytes = 2 * kTileBytes;     // A + B
-constexpr int kScaleBytes = 2 * 256 * 4;        // A + B scale words per stage (MXFP8)
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bload16(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ uint32_t bload4(rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 // 128-byte rows, stored in pairs: rows 2j and 2j+1 share one 256-byte bank line (16 slots
 // of 16 bytes), and chunk c of row r sits in slot (((r & 1) << 3) | c) ^ hs(j),
@@ -91,24 +84,6 @@ __device__ __forceinline__ int find_expert(const Sched& s, int E, int t) {
 __device__ __forceinline__ float sigmoid_f(float g) { return __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 __device__ __forceinline__ float silu_f(float g) { return g * sigmoid_f(g); }
 
-// Same rotation for a 1024-byte-per-row tile (c16 in 0..63).
-__device__ __forceinline__ uint32_t epi_off_wide(int m, int c16) {
-  const int b = c16 >> 3, low = c16 & 7;
-  return (uint32_t)(m * 1024 + ((b << 3) + ((low + 2 * b + m) & 7)) * 16);
-}
-
-// Byte offset of 16-byte chunk c16 (0..31) of row m in a 512-byte-per-row LDS
-// staging tile.  Chunks are rotated within each group of 8 by (2 * group + m),
-// so both the column-wise writes from the MFMA layout and the row-wise reads
-// of whole groups touch 8 different bank groups per 8 lanes.
-__device__ __forceinline__ uint32_t epi_off(int m, int c16) {
-  const int b = c16 >> 3, low = c16 & 7;
-  return (uint32_t)(m * 512 + ((b << 3) + ((low + 2 * b + m) & 7)) * 16);
-}
-
-// ---------------------------------------------------------------------------
-// One K-pass of a 256x256 tile.  kFc1 selects the B row map (gate/up halves).
-// ---------------------------------------------------------------------------
 // ---- MN-major (N-contiguous) bf16 tiles: a stage of 64 K rows x 256 columns (512 bytes per row).
 // Row k's 16-byte chunk c is stored at chunk c ^ ((k & 3) << 2) of the row.  A transposing read
 // (ds_read_b64_tr_b16) by 16 lanes covers 4 K rows x 16 columns: source lane 4 j + q reads the
@@ -185,18 +160,9 @@ __device__ __forceinline__ void dma4(const i32x4& vs, uint32_t lds, uint32_t vof
                : "memory", "m0");
 }
 
-// Transpose an 8x8 block of bf16: v[r] holds 8 consecutive values of row r,
-// w[c] receives column c (8 values, one per row) -- v_perm_b32 picks the low or
-// high halves of two words at a time.
-__device__ __forceinline__ void transpose8x8_b16(const u32x4 v[8], u32x4 w[8]) {
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w[c][q] = __builtin_amdgcn_perm(v[2 * q + 1][c >> 1], v[2 * q][c >> 1], sel);
-  }
-}
-
+// The 256 x 256 tile's accumulators: wave (wm, wn) owns A rows wm*128 + [0, 128) and B rows
+// brow(wn, j) + [0, 32), j < 4, as 4 x 4 blocks of 32 x 32 fp32.  kFc1 selects the B row map of
+// the gate-up projection (gate rows [0, 128), the matching up rows [128, 256)).
 template <bool kMx, bool kFc1>
 struct TileCore {
   f32x16 acc[4][4];
@@ -215,142 +181,143 @@ struct TileCore {
     if (kFc1) return (j < 2) ? (wn * 64 + j * 32) : (128 + wn * 64 + (j - 2) * 32);
     return wn * 128 + j * 32;
   }
-
-  // Fragments of one MFMA K-substep: 4 A and 4 B operands (+ scales).
-  struct Frag {
-    typename std::conditional<kMx, i32x8, bf16x8>::type a[4], b[4];
-    int sa[4], sb[4];
-  };
-
-  static constexpr int kSub = kMx ? 2 : 4;   // MFMA K-substeps per 128-byte K step
-
-  __device__ __forceinline__ void load_frag(Frag& f, int kk, const uint8_t* sA, const uint8_t* sB,
-                                            const uint32_t* sAs, const uint32_t* sBs, int wm, int wn,
-                                            int lane) const {
-    const int r32 = lane & 31, g = lane >> 5;
-    if constexpr (!kMx) {
-      const uint32_t ch = (uint32_t)(kk * 2 + g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        f.a[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + i * 32 + r32, ch));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        f.b[j] = *reinterpret_cast<const bf16x8*>(sB + swz(brow(wn, j) + r32, ch));
-    } else {
-      const uint32_t c0 = (uint32_t)(kk * 4 + g), c1 = (uint32_t)(kk * 4 + 2 + g);
-      const int sh = 8 * (2 * kk + g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + r32;
-        u32x4 lo = *reinterpret_cast<const u32x4*>(sA + swz(row, c0));
-        u32x4 hi = *reinterpret_cast<const u32x4*>(sA + swz(row, c1));
-        f.a[i] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        f.sa[i] = (int)(sAs[row] >> sh);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = brow(wn, j) + r32;
-        u32x4 lo = *reinterpret_cast<const u32x4*>(sB + swz(row, c0));
-        u32x4 hi = *reinterpret_cast<const u32x4*>(sB + swz(row, c1));
-        f.b[j] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        f.sb[j] = (int)(sBs[row] >> sh);
-      }
-    }
-  }
-
-  // MFMAs of fragment rows i in [i0, i0 + 2)
-  __device__ __forceinline__ void mma_half(const Frag& f, int i0) {
-#pragma unroll
-    for (int i = i0; i < i0 + 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (!kMx)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
-                                                                        f.sb[j]);
-      }
-  }
-
-  __device__ __forceinline__ void mma(const Frag& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if constexpr (!kMx)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
-        else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[j], acc[i][j], 0, 0, 0, f.sa[i], 0,
-                                                                        f.sb[j]);
-      }
-  }
-
-  // BF16 fragments of K step kk with either operand stored MN-major (transposing reads) or
-  // K-major (swz layout).
-  template <bool kAMN, bool kBMN>
-  __device__ __forceinline__ void load_frag_x(Frag& f, int kk, const uint8_t* sA, const uint8_t* sB, int wm,
-                                              int wn, int lane) const {
-    const int r32 = lane & 31, g = lane >> 5;
-    const uint32_t ch = (uint32_t)(kk * 2 + g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (kAMN) f.a[i] = load_mn_frag(sA, wm * 128 + i * 32, kk, lane);
-      else f.a[i] = *reinterpret_cast<const bf16x8*>(sA + swz(wm * 128 + i * 32 + r32, ch));
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (kBMN) f.b[j] = load_mn_frag(sB, brow(wn, j), kk, lane);
-      else f.b[j] = *reinterpret_cast<const bf16x8*>(sB + swz(brow(wn, j) + r32, ch));
-    }
-  }
-
-  template <bool kAMN, bool kBMN>
-  __device__ __forceinline__ void compute_x(const uint8_t* sA, const uint8_t* sB, int wm, int wn, int lane) {
-    static_assert(!kMx, "MN-major operands are bf16 only");
-    Frag f0, f1;
-    load_frag_x<kAMN, kBMN>(f0, 0, sA, sB, wm, wn, lane);
-#pragma unroll
-    for (int kk = 0; kk < kSub; kk += 2) {
-      load_frag_x<kAMN, kBMN>(f1, kk + 1, sA, sB, wm, wn, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (kk + 2 < kSub) load_frag_x<kAMN, kBMN>(f0, kk + 2, sA, sB, wm, wn, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      mma(f1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-  // All substeps of one LDS stage.  BF16 fragments are double-buffered in
-  // registers (2 x 32 VGPRs); the MXFP8 ones are twice as wide, so they are
-  // single-buffered and the compiler overlaps the reads with the MFMAs.
-  __device__ __forceinline__ void compute(const uint8_t* sA, const uint8_t* sB, const uint32_t* sAs,
-                                          const uint32_t* sBs, int wm, int wn, int lane) {
-    if constexpr (kMx) {
-#pragma unroll
-      for (int kk = 0; kk < kSub; ++kk) {
-        Frag f;
-        load_frag(f, kk, sA, sB, sAs, sBs, wm, wn, lane);
-        mma(f);
-      }
-    } else {
-      Frag f0, f1;
-      load_frag(f0, 0, sA, sB, sAs, sBs, wm, wn, lane);
-#pragma unroll
-      for (int kk = 0; kk < kSub; kk += 2) {
-        load_frag(f1, kk + 1, sA, sB, sAs, sBs, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(f0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kk + 2 < kSub) load_frag(f0, kk + 2, sA, sB, sAs, sBs, wm, wn, lane);
-        __builtin_amdgcn_sched_barrier(0);
-        mma(f1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
 };
+
+// ---------------------------------------------------------------------------
+// The interleaved stage schedule shared by the forward and backward GEMMs.
+// ---------------------------------------------------------------------------
+// Fragments of one MFMA K substep of a wave: 4 A blocks (token rows in dgrad and the forward, M
+// rows in wgrad) and 4 B blocks of 32 rows, plus the E8M0 scale bytes of the lane's rows (MXFP8).
+template <bool kMx>
+struct StepFrag {
+  typename std::conditional<kMx, i32x8, bf16x8>::type a[4], b[4];
+  int sa[4], sb[4];
+};
+
+// Element e of the fragments of substep kk, e in the order the 16 MFMAs of a substep consume them
+// (A block i outer, B block j inner): a0, b0, b1, b2, b3, a1, a2, a3.  BF16 operands are K-major
+// (swz layout, one 16-byte read) or MN-major (mnswz layout, two transposing reads); MXFP8 ones are
+// K-major, two 16-byte reads plus the scale byte of the lane's 32-value block, read on its own (a
+// shift of the whole scale word would make the read wait for LDS on the spot).
+template <bool kMx, bool kFc1, bool kAMN, bool kBMN>
+__device__ __forceinline__ void read_elem(StepFrag<kMx>& f, const uint8_t* sA, const uint8_t* sS, int kk, int e,
+                                          int wm, int wn, int lane) {
+  const int r32 = lane & 31, g = lane >> 5;
+  const bool isA = e == 0 || e >= 5;
+  const int idx = e == 0 ? 0 : (e >= 5 ? e - 4 : e - 1);
+  const int rb = isA ? wm * 128 + idx * 32 : TileCore<kMx, kFc1>::brow(wn, idx);
+  const uint8_t* base = isA ? sA : sA + kTileBytes;
+  if constexpr (!kMx) {
+    const bool mn = isA ? kAMN : kBMN;
+    const bf16x8 v = mn ? load_mn_frag(base, rb, kk, lane)
+                        : *reinterpret_cast<const bf16x8*>(base + swz(rb + r32, (uint32_t)(kk * 2 + g)));
+    if (isA) f.a[idx] = v; else f.b[idx] = v;
+  } else {
+    const int row = rb + r32;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + g)));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + 2 + g)));
+    const i32x8 v{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    const int sc = sS[((isA ? 0 : 256) + row) * 4 + 2 * kk + g];
+    if (isA) { f.a[idx] = v; f.sa[idx] = sc; } else { f.b[idx] = v; f.sb[idx] = sc; }
+  }
+}
+
+// Order of the reads of the next substep's elements while the current substep's MFMAs run:
+// b0 b1 a0 b2 a1 b3 a2 a3 -- each a block is read only after the MFMAs that use the current one
+// are issued, so the two fragment sets share the a registers.
+__device__ __forceinline__ constexpr int next_elem(int s) {
+  return s == 0 ? 1 : s == 1 ? 2 : s == 2 ? 0 : s == 3 ? 3 : s == 4 ? 5 : s == 5 ? 4 : s;
+}
+
+// MFMA of A block i and B block j with the B block as the instruction's first operand: lane l
+// accumulates A row 32 i + l % 32 of the wave's block at B rows (output columns) 32 j + 8 q +
+// 4 (l / 32) + c in acc[i][j][4 q + c] -- one output row and runs of 4 consecutive columns, which
+// the epilogues store straight from the accumulators.
+template <bool kMx, bool kFc1>
+__device__ __forceinline__ void mma_ij(TileCore<kMx, kFc1>& core, const StepFrag<kMx>& f, int q) {
+  const int i = q >> 2, j = q & 3;
+  if constexpr (!kMx)
+    core.acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], core.acc[i][j], 0, 0, 0);
+  else
+    core.acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.b[j], f.a[i], core.acc[i][j], 0, 0, 0, f.sb[j],
+                                                                       0, f.sa[i]);
+}
+
+// The MFMAs of one LDS stage (sA: A tile, then B tile; sS: MXFP8 scale words), with the loads of
+// the next stage and the next substep's fragment reads interleaved one by one between them, so the
+// wave's in-order issue never stalls behind a burst of memory instructions.  dma_a(q) / dma_b(q)
+// (q < 8) issue the next stage's A / B loads, dma_s() its MXFP8 scale loads.
+//   BF16 (4 substeps): A loads and the substep-1 reads between the MFMAs of substep 0, B loads and
+//     the substep-2 reads in substep 1, the substep-3 reads in substep 2.
+//   MXFP8 (2 substeps of MFMAs twice as long): all loads and the substep-1 reads in substep 0.
+template <bool kMx, bool kFc1, bool kAMN, bool kBMN, class DA, class DB, class DS>
+__device__ __forceinline__ void mma_stage(TileCore<kMx, kFc1>& core, const uint8_t* sA, const uint8_t* sS, int wm,
+                                          int wn, int lane, DA&& dma_a, DB&& dma_b, DS&& dma_s) {
+  StepFrag<kMx> f0, f1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    read_elem<kMx, kFc1, kAMN, kBMN>(f0, sA, sS, 0, e, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (!kMx) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma_ij(core, f0, q);
+      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
+      else dma_a(q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma_ij(core, f1, q);
+      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN>(f0, sA, sS, 2, next_elem(q >> 1), wm, wn, lane);
+      else dma_b(q >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma_ij(core, f0, q);
+      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN>(f1, sA, sS, 3, next_elem(q >> 1), wm, wn, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma_ij(core, f1, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma_ij(core, f0, q);
+      if (q & 1) {
+        read_elem<kMx, kFc1, kAMN, kBMN>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
+        dma_b(q >> 1);
+      } else {
+        dma_a(q >> 1);
+      }
+      if (q == 15) dma_s();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      mma_ij(core, f1, q);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
+// allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
+// and spills.
+__device__ __forceinline__ float agpr_read(float x) {
+  float y;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+  return y;
+}
+__device__ __forceinline__ void agpr_read16(const f32x16& a, float (&o)[16]) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) o[r] = agpr_read(a[r]);
+}
 
 }  // namespace gemm
 }  // namespace moe
