@@ -145,6 +145,7 @@ struct BwdPlan {
   uint16_t* dgu;        // [R, 2I] bf16
   float* dprob_part;    // [R, parts]
   void* dx_perm;        // [R, H] io dtype
+  float* part;          // FC1 dgrad split-tile partials
   // MXFP8 operands, each quantized along its GEMM's K
   uint8_t *dzq, *dzs, *w2tq, *w2ts, *dzT, *dzTs, *hT, *hTs;
   uint8_t *dguq, *dgus, *w1tq, *w1ts, *dguT, *dguTs, *xT, *xTs;
@@ -161,6 +162,7 @@ BwdPlan plan_bwd(const moe_mlp_bwd_args* a, void* ws) {
   p.dgu = reinterpret_cast<uint16_t*>(c.take((size_t)(R * 2 * I * 2)));
   p.dprob_part = reinterpret_cast<float*>(c.take((size_t)(R * bwd_dprob_parts(I) * 4)));
   p.dx_perm = c.take((size_t)(R * H) * io_size(a->io_dtype));
+  p.part = reinterpret_cast<float*>(c.take(kFc2PartBytes));
   if (a->compute == MOE_MXFP8_E4M3) {
     const int64_t Rp = (R + 127) / 128 * 128 + 128 * (int64_t)E;
     p.rows_pad = Rp;
@@ -573,7 +575,7 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   // ---- FC1 dgrad: dx_perm = dgu . W1_e
   BwdGemm d1{};
   d1.N = H; d1.K = 2 * I; d1.E = E; d1.split_sizes = a->split_sizes;
-  d1.out = p.dx_perm; d1.out_f32 = io_f32;
+  d1.out = p.dx_perm; d1.out_f32 = io_f32; d1.part = p.part;
   if (mx) {
     HIP_TRY(launch_mx_quant_rows(p.dgu, false, R, 2 * I, p.dguq, p.dgus, st));
     for (int e = 0; e < E; ++e)

@@ -71,20 +71,6 @@ __device__ __forceinline__ const uint8_t* kernarg_table(int e) {
 #endif
 }
 
-// Split of the last round: tiles [full, total) are split into S parts along K (S = 1: none).
-__device__ __forceinline__ void split_policy(int total, int G, int kU, int& full, int& S) {
-  const int rem = total % G;
-  full = total;
-  S = 1;
-  if (rem > 0) {
-    const int sk = min(G / rem, kU / kMinSplitUnits);
-    if (sk >= 2) {
-      S = sk;
-      full = total - rem;
-    }
-  }
-}
-
 // One work item: a 256 x 256 output tile, or one K part of a split tile.
 struct FwdItem {
   int t, tile, part, e, mt, nt, row0, mrows, u0, u1;
@@ -473,6 +459,21 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   if (err != hipSuccess) return err;
   const dim3 fgrid(kGemmGrid, kBM / 32);
   if (g.out_f32) fc2_fixup_kernel<true><<<fgrid, 256, 0, st>>>(k, kU);
+  else fc2_fixup_kernel<false><<<fgrid, 256, 0, st>>>(k, kU);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_fixup(const int32_t* split_sizes, int E, int64_t N, float* part, void* out, bool out_f32,
+                              int kU, hipStream_t st) {
+  FwdKArgs k{};
+  k.split_sizes = split_sizes;
+  k.E = E;
+  k.N = N;
+  k.nN = (int)((N + kBN - 1) / kBN);
+  k.part = part;
+  k.out = reinterpret_cast<uint8_t*>(out);
+  const dim3 fgrid(kGemmGrid, kBM / 32);
+  if (out_f32) fc2_fixup_kernel<true><<<fgrid, 256, 0, st>>>(k, kU);
   else fc2_fixup_kernel<false><<<fgrid, 256, 0, st>>>(k, kU);
   return hipGetLastError();
 }

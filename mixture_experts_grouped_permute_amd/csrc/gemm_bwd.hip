@@ -46,6 +46,8 @@ struct BwdKArgs {
   float* dprob_part;        // FC2 dgrad: [R, nN]
   int64_t I;
   uint8_t* out;             // FC1 dgrad: dx_perm [R, N]
+  float* part;              // FC1 dgrad split parts: kGemmGrid x 64K floats
+  int split;                // FC1 dgrad: 0 every tile; 1 tiles before the split ones; 2 the split parts
   const uint8_t* tab[kMaxExperts];   // BF16 dgrad: W_e; wgrad: dW_e
 };
 
@@ -63,6 +65,7 @@ __device__ __forceinline__ const uint8_t* bwd_table(int e) {
 // One work item of the backward kernel: a 256 x 256 output tile and its K extent.
 struct BwdItem {
   int t, e, mt, nt, row0, mrows, ncols, kT, Me;
+  int part, u0;             // K part of a split tile (-1: whole K) and its first stage
   int64_t koff;
 };
 
@@ -87,11 +90,22 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   const int total = kWg ? E * p.nM * p.nN : __builtin_amdgcn_readfirstlane(sched.tile[E]);
   const int G = gridDim.x, per = G >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   constexpr int kKStep = kMx ? 128 : 64;                  // K values per LDS stage
+  const int kU = kWg ? 0 : (int)(p.K * (kMx ? 1 : 2) / kRowBytes);   // dgrad K units of 128 bytes
+
+  // FC1 dgrad balances its last round like the forward down projection: the rem = total % G tiles
+  // of the last round are split into S parts along K; pass 1 runs tiles [0, full), pass 2 (the
+  // fp32 instance) the parts, which store fp32 tiles to p.part for the fixup kernel to sum.
+  int full = total, S = 1;
+  if (kRole == kRoleDgradFc1 && p.split) split_policy(total, G, kU, full, S);
+  const int lo = p.split == 2 ? full : 0;
+  const int hi = p.split == 0 ? total : (p.split == 1 ? full : (S > 1 ? full + (total - full) * S : full));
 
   auto decode = [&](int round, BwdItem& it) {
-    it.t = round * G + xcd * per + slot;
+    it.t = lo + round * G + xcd * per + slot;
     it.kT = 0;
-    if (it.t >= total) return;
+    it.u0 = 0;
+    it.part = -1;
+    if (it.t >= hi) return;
     if constexpr (kWg) {
       const int pe = p.nM * p.nN;
       it.e = it.t / pe;
@@ -104,16 +118,22 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       it.row0 = it.mt * kBM;
       it.mrows = (int)min((int64_t)kBM, p.M - it.row0);
     } else {
-      it.e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, it.t));
+      int tile = it.t;
+      if (kOutF32 && p.split == 2) {
+        tile = full + (it.t - full) / S;
+        it.part = (it.t - full) % S;
+      }
+      it.e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, tile));
       it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
       const int nMe = (it.Me + kBM - 1) / kBM;
-      const int local = it.t - __builtin_amdgcn_readfirstlane(sched.tile[it.e]);
+      const int local = tile - __builtin_amdgcn_readfirstlane(sched.tile[it.e]);
       it.mt = local % nMe;
       it.nt = local / nMe;
       it.row0 = __builtin_amdgcn_readfirstlane(sched.off[it.e]) + it.mt * kBM;
       it.mrows = min(kBM, it.Me - it.mt * kBM);
       it.koff = 0;
-      it.kT = (int)(p.K * (kMx ? 1 : 2) / kRowBytes);
+      it.u0 = it.part < 0 ? 0 : it.part * kU / S;
+      it.kT = (it.part < 0 ? kU : (it.part + 1) * kU / S) - it.u0;
     }
     it.ncols = (int)min((int64_t)kBN, p.N - (int64_t)it.nt * kBN);
   };
@@ -131,7 +151,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   // memory.
   struct Desc { i32x4 va, vb, vas, vbs; };
   auto descs = [&](const BwdItem& it, Desc& d) {
-    if (it.t >= total || it.kT == 0) {
+    if (it.t >= hi || it.kT == 0) {
       d.va = make_vsharp(p.a, 0); d.vb = d.va; d.vas = d.va; d.vbs = d.va;
       return;
     }
@@ -220,7 +240,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   descs(cur, dc);
   int par = 0;             // buffer of the current item's first stage
   bool issued = false;     // the current item's first stage was loaded by the previous item
-  for (int round = 0; cur.t < total; ++round) {
+  for (int round = 0; cur.t < hi; ++round) {
     decode(round + 1, nxt);
     descs(nxt, dn);
     const int ipar = round & 1;
@@ -230,11 +250,11 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     }
     if (!issued && cur.kT > 0) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) { dma_a(dc, par, 0, q); dma_b(dc, par, 0, q); }
-      dma_s(dc, par, 0);
+      for (int q = 0; q < 8; ++q) { dma_a(dc, par, cur.u0, q); dma_b(dc, par, cur.u0, q); }
+      dma_s(dc, par, cur.u0);
     }
     // the last stage loads the next item's first one, if it has any stage
-    const bool chain = nxt.t < total && nxt.kT > 0;
+    const bool chain = nxt.t < hi && nxt.kT > 0;
     TileCore<kMx, false> core;
     core.zero();
 #pragma unroll 1
@@ -246,7 +266,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       __syncthreads();
       const bool last = s + 1 == cur.kT;
       const Desc& dd = last ? dn : dc;
-      const int kn = last ? 0 : s + 1;
+      const int kn = last ? nxt.u0 : cur.u0 + s + 1;
       const int bn = b ^ 1;
       const uint8_t* sA = smem + b * kStageBytes;
       const uint8_t* sS = smem + kScOff + b * 2048;
@@ -335,19 +355,23 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       __syncthreads();
       if (tid < cur.mrows) p.dprob_part[(int64_t)(cur.row0 + tid) * p.nN + cur.nt] = red[tid] + red[256 + tid];
     } else {
-      // FC1 dgrad: dx_perm rows of the tile; wgrad: rows m0w.. of dW_e
-      const uint32_t N32 = (uint32_t)p.N;
+      // FC1 dgrad: dx_perm rows of the tile (a split part: its whole fp32 tile, row-major
+      // [256][256], to its slot of p.part); wgrad: rows m0w.. of dW_e
+      const bool sp = kOutF32 && cur.part >= 0;
+      const uint32_t N32 = sp ? 256u : (uint32_t)p.N;
       const uint32_t es = kOutF32 ? 4u : 2u;
       const int64_t r0 = kWg ? (int64_t)cur.mt * kBM : (int64_t)cur.row0;
       uint8_t* obase = kWg ? const_cast<uint8_t*>(bwd_table(cur.e)) : p.out;
-      const rsrc_t ro = make_rsrc(obase + r0 * p.N * es, (uint32_t)cur.mrows * N32 * es);
+      const rsrc_t ro = sp ? make_rsrc(p.part + (size_t)(cur.t - full) * 65536, 65536u * 4u)
+                           : make_rsrc(obase + r0 * p.N * es, (uint32_t)cur.mrows * N32 * es);
+      const int64_t cbase = sp ? 0 : n0;                             // tile's first column in the destination
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t col = (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);
-          if (col >= N32) continue;                                  // wave-uniform
+          if ((uint32_t)n0 + (uint32_t)(wn * 128 + j * 32) >= (uint32_t)p.N) continue;   // wave-uniform
+          const uint32_t col = (uint32_t)cbase + (uint32_t)(wn * 128 + j * 32);          // in the destination
           float a[16];
           agpr_read16(core.acc[i][j], a);
           const uint32_t e0 = m * N32 + col + (uint32_t)ch;
@@ -416,7 +440,18 @@ hipError_t launch_bwd_dgrad_fc2(const BwdGemm& g, bool mx, hipStream_t st) {
 
 hipError_t launch_bwd_dgrad_fc1(const BwdGemm& g, bool mx, hipStream_t st) {
   BwdKArgs k = base_args(g);
-  return mx ? launch_role<kRoleDgradFc1, true>(k, g.out_f32, st) : launch_role<kRoleDgradFc1, false>(k, g.out_f32, st);
+  // a split needs at least 2 parts of kMinSplitUnits K units each
+  const int kU = (int)(g.K * (mx ? 1 : 2) / kRowBytes);
+  const bool split = g.part != nullptr && kU / kMinSplitUnits >= 2;
+  k.part = g.part;
+  k.split = split ? 1 : 0;
+  hipError_t err = mx ? launch_role<kRoleDgradFc1, true>(k, g.out_f32, st) : launch_role<kRoleDgradFc1, false>(k, g.out_f32, st);
+  if (err != hipSuccess || !split) return err;
+  // pass 2: the split parts (whether there are any is decided on the device), then the fixup
+  k.split = 2;
+  err = mx ? launch_role<kRoleDgradFc1, true>(k, true, st) : launch_role<kRoleDgradFc1, false>(k, true, st);
+  if (err != hipSuccess) return err;
+  return launch_split_fixup(g.split_sizes, g.E, g.N, g.part, g.out, g.out_f32, kU, st);
 }
 
 hipError_t launch_bwd_wgrad(const BwdGemm& g, bool mx, hipStream_t st) {

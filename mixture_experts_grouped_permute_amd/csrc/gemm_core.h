@@ -115,6 +115,20 @@ __device__ __forceinline__ bf16x8 load_mn_frag(const uint8_t* s, int rb, int kk,
 // K units of 128 bytes per part of a split tile, at least: a split costs two short extra launches,
 // so it only pays for long tiles
 constexpr int kMinSplitUnits = 16;
+
+// Split of the last round: tiles [full, total) are split into S parts along K (S = 1: none).
+__device__ __forceinline__ void split_policy(int total, int G, int kU, int& full, int& S) {
+  const int rem = total % G;
+  full = total;
+  S = 1;
+  if (rem > 0) {
+    const int sk = min(G / rem, kU / kMinSplitUnits);
+    if (sk >= 2) {
+      S = sk;
+      full = total - rem;
+    }
+  }
+}
 // s_waitcnt vmcnt(n) with the other counters left unconstrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {

@@ -77,6 +77,11 @@ struct FwdGemm {
 constexpr size_t kFc2PartBytes = (size_t)kGemmGrid * 65536 * sizeof(float);
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st);
 hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st);
+// Sums the S fp32 K-part tiles of the split 256-row tiles of the last round (tile list of
+// ceil(M_e / 256) x ceil(N / 256) tiles per expert, parts as written by a split GEMM pass) into
+// out ([rows, N], bf16 or fp32).  kU: K units of 128 bytes of the GEMM.
+hipError_t launch_split_fixup(const int32_t* split_sizes, int E, int64_t N, float* part, void* out, bool out_f32,
+                              int kU, hipStream_t st);
 
 // ---- backward grouped GEMMs (gemm_bwd.hip); byte strides throughout
 struct BwdGemm {
@@ -102,6 +107,7 @@ struct BwdGemm {
   int64_t I;
   void* out;
   bool out_f32;
+  float* part;              // FC1 dgrad: split-tile partials (kFc2PartBytes), or null for no split
 };
 hipError_t launch_bwd_dgrad_fc2(const BwdGemm& g, bool mx, hipStream_t st);
 hipError_t launch_bwd_dgrad_fc1(const BwdGemm& g, bool mx, hipStream_t st);

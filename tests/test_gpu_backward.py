@@ -18,6 +18,9 @@ CASES = [
     ("zeros-first-middle-last", cfg_small(T=400, H=128, I=256, E=8, k=2), [0, 400, 1, 31, 0, 33, 335, 0]),
     ("edge-sizes", cfg_small(T=600, H=128, I=128, E=7, k=2), [255, 257, 1, 31, 33, 600, 23]),
     ("one-expert", cfg_small(T=300, H=128, I=128, E=1, k=1), None),
+    # 8 FC1-dgrad tiles with a long K: the last (only) round is split into K parts (4 for BF16,
+    # 2 for MXFP8) that a fixup kernel sums
+    ("split-k-dgrad", cfg_small(T=600, H=256, I=2048, E=4, k=2), None),
     ("finegrained-e64-k8", get_config(5).with_(T=512, H=256, I=256, precision="bf16"), None),
     ("zipf-zero-expert", get_config(3).with_(T=1024, H=256, I=384, precision="bf16"), None),
 ]

@@ -62,6 +62,32 @@ def test_forward_matches_oracle(name, cfg, counts, compute):
     np.testing.assert_array_equal(ctx["perm"]["split_sizes"].cpu().numpy(), ref.perm.split_sizes)
 
 
+# experts whose last 256-row tile holds 0, 44, 64, 65, 128, 129, 192 and 1 rows
+TAIL_COUNTS = [256, 300, 64, 65, 128, 129, 192, 513]
+
+
+@gpu
+@pytest.mark.parametrize("compute", ["bf16", "mxfp8"])
+def test_forward_ragged_tails_per_expert(compute):
+    """Each expert's tokens (top-1, so an output row belongs to one expert) match the oracle on
+    their own, so a wrong ragged tile cannot hide inside the layer-wide error."""
+    m = need_gpu()
+    cfg = cfg_small(T=sum(TAIL_COUNTS), H=256, I=384 if compute == "bf16" else 256, E=8, k=1)
+    log(f"fwd ragged tails {compute} counts={TAIL_COUNTS}")
+    inp = _inputs(cfg, TAIL_COUNTS)
+    out, _ = _run(m, inp, compute)
+    idx = inp.topk_idx.numpy()
+    ref = mlp.forward(inp.x, idx, inp.topk_prob, inp.w1, inp.w2, compute, cfg.x_dtype)
+    got = to_np(out)
+    tol = BF16_TOL if compute == "bf16" else MXFP8_TOL
+    for e in range(cfg.E):
+        rows = np.nonzero(idx[:, 0] == e)[0]
+        assert len(rows) == TAIL_COUNTS[e]
+        err = mlp.normwise_rel_err(got[rows], ref.out[rows])
+        log(f"  expert {e} ({len(rows)} rows) err {err:.3e}")
+        assert err < tol
+
+
 @gpu
 @pytest.mark.parametrize("compute", ["bf16", "mxfp8"])
 def test_forward_split_last_round(compute):
