@@ -79,10 +79,11 @@ struct FwdItem {
 template <bool kMx, bool kFc1, bool kOutF32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
-  // 2 pipeline stages, then the MXFP8 scale words (2 x 2 KB), then the routing probabilities of the
-  // tile's rows (FC1, double-buffered by work item)
+  // 2 pipeline stages, then the MXFP8 scales of groups of 4 stages (2 x 8 KB), then the routing
+  // probabilities of the tile's rows (FC1, double-buffered by work item)
   constexpr int kScOff = 2 * kStageBytes;
-  constexpr int kPrOff = kScOff + (kMx ? 2 * 2048 : 0);
+  constexpr int kScBuf = 8192;
+  constexpr int kPrOff = kScOff + (kMx ? 2 * kScBuf : 0);
   __shared__ __attribute__((aligned(16))) uint8_t smem[kPrOff + (kFc1 ? 2 * 1024 : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -123,8 +124,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     const int Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
     const int nM = (Me + kBM - 1) / kBM;
     const int local = it.tile - __builtin_amdgcn_readfirstlane(sched.tile[it.e]);
-    it.mt = local % nM;
-    it.nt = local / nM;
+    tile_coords(local, nM, p.nN, it.mt, it.nt);
     it.row0 = __builtin_amdgcn_readfirstlane(sched.off[it.e]) + it.mt * kBM;
     it.mrows = min(kBM, Me - it.mt * kBM);
     it.u0 = it.part < 0 ? 0 : it.part * kU / S;
@@ -174,15 +174,24 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     a_vo[q] = (uint32_t)r * rowb + c * 16;
     b_vo[q] = (uint32_t)(br * rowb) + c * 16;
   }
-  uint32_t as_vo = 0, bs_vo = 0;
+  // MXFP8 scales, loaded a group of 4 stages at a time: 16 bytes of E8M0 per row (stage kt's 4
+  // bytes at (kt & 3) * 4), four lanes per row reading its consecutive words, which the load merges
+  // into one request per row (per-stage loads of 4 bytes cost a request per row per stage).  Load
+  // j < 4 of wave w covers rows 64 w + 16 j + L / 4; lane L's word lands at slot L of a 256-byte
+  // block, so row r's 16 bytes sit at r * 16 (A rows, then B rows at 4096).  Only 4-byte alignment
+  // is needed: the scale rows of K = 1408 are 44 bytes.
+  uint32_t as_vo[4] = {0, 0, 0, 0}, bs_vo[4] = {0, 0, 0, 0};
   if constexpr (kMx) {
-    const int r = wave * 64 + lane;
-    const int64_t br = kFc1 ? (r < 128 ? (int64_t)r : N + (r - 128)) : (int64_t)r;
-    as_vo = (uint32_t)r * kscale_row;
-    bs_vo = (uint32_t)(br * kscale_row);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = wave * 64 + j * 16 + (lane >> 2);
+      const int64_t br = kFc1 ? (r < 128 ? (int64_t)r : N + (r - 128)) : (int64_t)r;
+      as_vo[j] = (uint32_t)r * kscale_row + (uint32_t)(lane & 3) * 4u;
+      bs_vo[j] = (uint32_t)(br * kscale_row) + (uint32_t)(lane & 3) * 4u;
+    }
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
-  const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * 256u);
+  const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * 1024u);
   // stage kt of the item described by d into buffer b
   auto dma_a = [&](const Desc& d, int b, int kt, int q) {
     dma16(d.va, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q], (uint32_t)kt * kRowBytes);
@@ -190,11 +199,15 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   auto dma_b = [&](const Desc& d, int b, int kt, int q) {
     dma16(d.vb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q], (uint32_t)kt * kRowBytes);
   };
-  auto dma_s = [&](const Desc& d, int b, int kt) {
+  // the scales of stage group g (stages 4 g .. 4 g + 3) of the item described by d into buffer sb
+  auto dma_s = [&](const Desc& d, int sb, int g) {
     if constexpr (kMx) {
-      const uint32_t ss = lds_sc + (uint32_t)b * 2048u;
-      dma4(d.vas, ss, as_vo, (uint32_t)kt * 4u);
-      dma4(d.vbs, ss + 1024u, bs_vo, (uint32_t)kt * 4u);
+      const uint32_t ss = lds_sc + (uint32_t)sb * (uint32_t)kScBuf;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dma4(d.vas, ss + (uint32_t)j * 256u, as_vo[j], (uint32_t)g * 16u);
+        dma4(d.vbs, ss + 4096u + (uint32_t)j * 256u, bs_vo[j], (uint32_t)g * 16u);
+      }
     }
   };
 
@@ -203,10 +216,11 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   decode(0, cur);
   descs(cur, dc);
   int par = 0;    // buffer of the current item's first stage
+  int spar = 0;   // scale buffer of the current item's first stage group
   if (cur.t < hi) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) { dma_a(dc, 0, cur.u0, q); dma_b(dc, 0, cur.u0, q); }
-    dma_s(dc, 0, cur.u0);
+    dma_s(dc, 0, cur.u0 >> 2);
   }
 
   for (int round = 0; cur.t < hi; ++round) {
@@ -220,9 +234,15 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     TileCore<kMx, kFc1> core;
     core.zero();
     const int n = cur.u1 - cur.u0;
+    // scale groups: the item's are g0 .. glast, group g in buffer (spar + g - g0) & 1.  The first
+    // stage of the item and the first stage of each later group load the next group -- after the
+    // last group, the next item's first one -- into the buffer of the group before the current one,
+    // which every wave finished reading before this stage's barrier.
+    const int g0 = cur.u0 >> 2, glast = (cur.u1 - 1) >> 2;
 #pragma unroll 1
     for (int s = 0; s < n; ++s) {
       const int kt = cur.u0 + s, b = (par + s) & 1;
+      const int g = kt >> 2;
       // stage kt landed (own loads + barrier); every wave finished reading the other buffer, which
       // takes the next stage -- of this item, or the first of the next item -- while this one is
       // multiplied
@@ -233,12 +253,20 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const int kn = last ? nxt.u0 : kt + 1;
       const int bn = b ^ 1;
       const uint8_t* sA = smem + b * kStageBytes;
-      const uint8_t* sS = smem + kScOff + b * 2048;
-      mma_stage<kMx, kFc1, false, false>(
+      const uint8_t* sS = smem + kScOff + ((spar + g - g0) & 1) * kScBuf + (kt & 3) * 4;
+      const bool sload = s == 0 || (kt & 3) == 0;
+      const bool snext = g == glast;                     // the next item's first group
+      const Desc& ds = snext ? dn : dc;
+      const int sg = snext ? nxt.u0 >> 2 : g + 1;
+      const int sb = (spar + g - g0 + 1) & 1;
+      mma_stage<kMx, kFc1, false, false, 16>(
           core, sA, sS, wm, wn, lane, [&](int q) { dma_a(dd, bn, kn, q); }, [&](int q) { dma_b(dd, bn, kn, q); },
-          [&]() { dma_s(dd, bn, kn); });
+          [&]() {
+            if (sload) dma_s(ds, sb, sg);
+          });
     }
     par = (par + n) & 1;
+    spar = (spar + glast - g0 + 1) & 1;
 
     // ---- epilogue straight from the accumulators.  acc[i][j][4 q + c] of lane l is token row
     // wm*128 + 32 i + l % 32 of the tile and output column (weight block j) + 8 q + 4 (l / 32) + c.
@@ -368,7 +396,8 @@ __global__ __launch_bounds__(256) void fc2_fixup_kernel(const FwdKArgs p, int kU
   const int Me = sched.cnt[e];
   const int nM = (Me + kBM - 1) / kBM;
   const int local = tile - sched.tile[e];
-  const int mt = local % nM, nt = local / nM;
+  int mt, nt;
+  tile_coords(local, nM, p.nN, mt, nt);
   const int row0 = sched.off[e] + mt * kBM;
   const int mrows = min(kBM, Me - mt * kBM);
   const int64_t N = p.N, n0 = (int64_t)nt * kBN;

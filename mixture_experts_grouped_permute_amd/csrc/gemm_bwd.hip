@@ -110,8 +110,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const int pe = p.nM * p.nN;
       it.e = it.t / pe;
       const int local = it.t - it.e * pe;
-      it.mt = local % p.nM;
-      it.nt = local / p.nM;
+      tile_coords(local, p.nM, p.nN, it.mt, it.nt);
       it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
       it.koff = kMx ? __builtin_amdgcn_readfirstlane(sched.tile[it.e]) : __builtin_amdgcn_readfirstlane(sched.off[it.e]);
       it.kT = (it.Me + kKStep - 1) / kKStep;
@@ -127,8 +126,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
       const int nMe = (it.Me + kBM - 1) / kBM;
       const int local = tile - __builtin_amdgcn_readfirstlane(sched.tile[it.e]);
-      it.mt = local % nMe;
-      it.nt = local / nMe;
+      tile_coords(local, nMe, p.nN, it.mt, it.nt);
       it.row0 = __builtin_amdgcn_readfirstlane(sched.off[it.e]) + it.mt * kBM;
       it.mrows = min(kBM, it.Me - it.mt * kBM);
       it.koff = 0;
@@ -270,7 +268,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const int bn = b ^ 1;
       const uint8_t* sA = smem + b * kStageBytes;
       const uint8_t* sS = smem + kScOff + b * 2048;
-      mma_stage<kMx, false, kAMN, kBMN>(
+      mma_stage<kMx, false, kAMN, kBMN, 4>(
           core, sA, sS, wm, wn, lane, [&](int q) { dma_a(dd, bn, kn, q); }, [&](int q) { dma_b(dd, bn, kn, q); },
           [&]() { dma_s(dd, bn, kn); });
     }

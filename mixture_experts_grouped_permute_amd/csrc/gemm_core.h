@@ -71,6 +71,33 @@ __device__ void build_sched(Sched& s, const int32_t* split_sizes, int E, int nN,
   __syncthreads();
 }
 
+// Coordinates (mt, nt) of tile `local` of one expert's nM x nN tile grid.  The M-tiles are split
+// into ng = ceil(nM / kGroupM) groups of balanced size (the first nM % ng groups one larger), and
+// each group is walked panel by panel with its M-tiles fastest.  The 32 consecutive tiles an XCD
+// takes in a round then span at most kGroupM M-tiles and several panels, whose operand slices the
+// XCD's L2 shares, instead of up to 32 M-tiles of one panel.  With nM <= kGroupM this is the plain
+// M-fastest order.
+constexpr int kGroupM = 8;
+__device__ __forceinline__ void tile_coords(int local, int nM, int nN, int& mt, int& nt) {
+  const int ng = (nM + kGroupM - 1) / kGroupM;
+  const int base = nM / ng, r = nM - base * ng;      // r groups of base + 1 M-tiles, then base
+  const int big = r * (base + 1) * nN;               // tiles of the larger groups
+  int gm, m0, l;
+  if (local < big) {
+    const int g = local / ((base + 1) * nN);
+    gm = base + 1;
+    m0 = g * gm;
+    l = local - g * gm * nN;
+  } else {
+    const int g = (local - big) / (base * nN);
+    gm = base;
+    m0 = r * (base + 1) + g * base;
+    l = local - big - g * base * nN;
+  }
+  mt = m0 + l % gm;
+  nt = l / gm;
+}
+
 __device__ __forceinline__ int find_expert(const Sched& s, int E, int t) {
   int lo = 0, hi = E - 1;   // largest e with tile[e] <= t (tile[] is non-decreasing)
   while (lo < hi) {
@@ -209,11 +236,12 @@ struct StepFrag {
 };
 
 // Element e of the fragments of substep kk, e in the order the 16 MFMAs of a substep consume them
-// (A block i outer, B block j inner): a0, b0, b1, b2, b3, a1, a2, a3.  BF16 operands are K-major
+// (A block i outer, B block j inner): a0, b0, b1, b2, b3, a1, a2, a3.  MXFP8 scales: the stage's
+// four E8M0 bytes of row r (A rows 0..255, then B rows) at sS + r * kScRow.  BF16 operands are K-major
 // (swz layout, one 16-byte read) or MN-major (mnswz layout, two transposing reads); MXFP8 ones are
 // K-major, two 16-byte reads plus the scale byte of the lane's 32-value block, read on its own (a
 // shift of the whole scale word would make the read wait for LDS on the spot).
-template <bool kMx, bool kFc1, bool kAMN, bool kBMN>
+template <bool kMx, bool kFc1, bool kAMN, bool kBMN, int kScRow>
 __device__ __forceinline__ void read_elem(StepFrag<kMx>& f, const uint8_t* sA, const uint8_t* sS, int kk, int e,
                                           int wm, int wn, int lane) {
   const int r32 = lane & 31, g = lane >> 5;
@@ -231,7 +259,7 @@ __device__ __forceinline__ void read_elem(StepFrag<kMx>& f, const uint8_t* sA, c
     const u32x4 lo = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + g)));
     const u32x4 hi = *reinterpret_cast<const u32x4*>(base + swz(row, (uint32_t)(kk * 4 + 2 + g)));
     const i32x8 v{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-    const int sc = sS[((isA ? 0 : 256) + row) * 4 + 2 * kk + g];
+    const int sc = sS[((isA ? 0 : 256) + row) * kScRow + 2 * kk + g];
     if (isA) { f.a[idx] = v; f.sa[idx] = sc; } else { f.b[idx] = v; f.sb[idx] = sc; }
   }
 }
@@ -263,35 +291,36 @@ __device__ __forceinline__ void mma_ij(TileCore<kMx, kFc1>& core, const StepFrag
 // (q < 8) issue the next stage's A / B loads, dma_s() its MXFP8 scale loads.
 //   BF16 (4 substeps): A loads and the substep-1 reads between the MFMAs of substep 0, B loads and
 //     the substep-2 reads in substep 1, the substep-3 reads in substep 2.
-//   MXFP8 (2 substeps of MFMAs twice as long): all loads and the substep-1 reads in substep 0.
-template <bool kMx, bool kFc1, bool kAMN, bool kBMN, class DA, class DB, class DS>
+//   MXFP8 (2 substeps of MFMAs twice as long): all loads and the substep-1 reads in substep 0, the
+//     scale loads (dma_s) right after the first MFMA.
+template <bool kMx, bool kFc1, bool kAMN, bool kBMN, int kScRow, class DA, class DB, class DS>
 __device__ __forceinline__ void mma_stage(TileCore<kMx, kFc1>& core, const uint8_t* sA, const uint8_t* sS, int wm,
                                           int wn, int lane, DA&& dma_a, DB&& dma_b, DS&& dma_s) {
   StepFrag<kMx> f0, f1;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    read_elem<kMx, kFc1, kAMN, kBMN>(f0, sA, sS, 0, e, wm, wn, lane);
+    read_elem<kMx, kFc1, kAMN, kBMN, kScRow>(f0, sA, sS, 0, e, wm, wn, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (!kMx) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mma_ij(core, f0, q);
-      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
+      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN, kScRow>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
       else dma_a(q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mma_ij(core, f1, q);
-      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN>(f0, sA, sS, 2, next_elem(q >> 1), wm, wn, lane);
+      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN, kScRow>(f0, sA, sS, 2, next_elem(q >> 1), wm, wn, lane);
       else dma_b(q >> 1);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       mma_ij(core, f0, q);
-      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN>(f1, sA, sS, 3, next_elem(q >> 1), wm, wn, lane);
+      if (q & 1) read_elem<kMx, kFc1, kAMN, kBMN, kScRow>(f1, sA, sS, 3, next_elem(q >> 1), wm, wn, lane);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -304,12 +333,12 @@ __device__ __forceinline__ void mma_stage(TileCore<kMx, kFc1>& core, const uint8
     for (int q = 0; q < 16; ++q) {
       mma_ij(core, f0, q);
       if (q & 1) {
-        read_elem<kMx, kFc1, kAMN, kBMN>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
+        read_elem<kMx, kFc1, kAMN, kBMN, kScRow>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
         dma_b(q >> 1);
       } else {
         dma_a(q >> 1);
       }
-      if (q == 15) dma_s();
+      if (q == 0) dma_s();
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
