@@ -254,16 +254,16 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const int bn = b ^ 1;
       const uint8_t* sA = smem + b * kStageBytes;
       const uint8_t* sS = smem + kScOff + ((spar + g - g0) & 1) * kScBuf + (kt & 3) * 4;
-      const bool sload = s == 0 || (kt & 3) == 0;
-      const bool snext = g == glast;                     // the next item's first group
-      const Desc& ds = snext ? dn : dc;
-      const int sg = snext ? nxt.u0 >> 2 : g + 1;
-      const int sb = (spar + g - g0 + 1) & 1;
+      // the scale group load is issued here, ahead of the stage's fragment reads: a branch among
+      // the MFMAs would split the block and make the compiler re-extend every scale byte read
+      // before it, waiting for all of them at once
+      if (kMx && (s == 0 || (kt & 3) == 0)) {
+        const bool snext = g == glast;                   // the next item's first group
+        dma_s(snext ? dn : dc, (spar + g - g0 + 1) & 1, snext ? nxt.u0 >> 2 : g + 1);
+      }
       mma_stage<kMx, kFc1, false, false, 16>(
           core, sA, sS, wm, wn, lane, [&](int q) { dma_a(dd, bn, kn, q); }, [&](int q) { dma_b(dd, bn, kn, q); },
-          [&]() {
-            if (sload) dma_s(ds, sb, sg);
-          });
+          []() {});
     }
     par = (par + n) & 1;
     spar = (spar + glast - g0 + 1) & 1;
