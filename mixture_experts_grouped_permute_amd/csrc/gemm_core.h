@@ -293,6 +293,8 @@ __device__ __forceinline__ void mma_ij(TileCore<kMx, kFc1>& core, const StepFrag
 //     the substep-2 reads in substep 1, the substep-3 reads in substep 2.
 //   MXFP8 (2 substeps of MFMAs twice as long): all loads and the substep-1 reads in substep 0, the
 //     scale loads (dma_s) right after the first MFMA.
+// No branch may sit among the MFMAs: the scale bytes read before it would be re-extended after it,
+// each behind a wait for its LDS read.
 template <bool kMx, bool kFc1, bool kAMN, bool kBMN, int kScRow, class DA, class DB, class DS>
 __device__ __forceinline__ void mma_stage(TileCore<kMx, kFc1>& core, const uint8_t* sA, const uint8_t* sS, int wm,
                                           int wn, int lane, DA&& dma_a, DB&& dma_b, DS&& dma_s) {
