@@ -76,9 +76,13 @@ struct FwdItem {
   int t, tile, part, e, mt, nt, row0, mrows, u0, u1;
 };
 
-template <bool kMx, bool kFc1, bool kOutF32>
+// kDeep (MXFP8 with K of at least two stages and a multiple of 512, so 16-byte scale rows): the
+// stage barrier sits between the two substeps and stage loads are issued two stages ahead
+// (mma_stage_mx_deep).
+template <bool kMx, bool kFc1, bool kOutF32, bool kDeep>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
+  static_assert(!kDeep || kMx, "the deep pipeline is the MXFP8 one");
   // 2 pipeline stages, then the MXFP8 scales of groups of 4 stages (2 x 8 KB), then the routing
   // probabilities of the tile's rows (FC1, double-buffered by work item)
   constexpr int kScOff = 2 * kStageBytes;
@@ -175,19 +179,22 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     b_vo[q] = (uint32_t)(br * rowb) + c * 16;
   }
   // MXFP8 scales, loaded a group of 4 stages at a time: 16 bytes of E8M0 per row (stage kt's 4
-  // bytes at (kt & 3) * 4), four lanes per row reading its consecutive words, which the load merges
-  // into one request per row (per-stage loads of 4 bytes cost a request per row per stage).  Load
-  // j < 4 of wave w covers rows 64 w + 16 j + L / 4; lane L's word lands at slot L of a 256-byte
-  // block, so row r's 16 bytes sit at r * 16 (A rows, then B rows at 4096).  Only 4-byte alignment
-  // is needed: the scale rows of K = 1408 are 44 bytes.
+  // bytes at (kt & 3) * 4), row r's 16 bytes at r * 16 of the buffer (A rows, then B rows at 4096).
+  //   * 16-byte scale rows (K % 512 == 0): one 16-byte load per row, lane L of wave w fetching row
+  //     64 w + L (direct-to-LDS loads of 4 bytes cost about as much issue time each as one of 16).
+  //   * otherwise (the scale rows of K = 1408 are 44 bytes): four lanes per row, reading its
+  //     consecutive words, which the load merges into one request; load j < 4 of wave w covers
+  //     rows 64 w + 16 j + L / 4, lane L's word landing at slot L of a 256-byte block.
+  const bool sc16 = kDeep || (kscale_row & 15u) == 0;
   uint32_t as_vo[4] = {0, 0, 0, 0}, bs_vo[4] = {0, 0, 0, 0};
   if constexpr (kMx) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = wave * 64 + j * 16 + (lane >> 2);
+      const int r = sc16 ? wave * 64 + lane : wave * 64 + j * 16 + (lane >> 2);
       const int64_t br = kFc1 ? (r < 128 ? (int64_t)r : N + (r - 128)) : (int64_t)r;
-      as_vo[j] = (uint32_t)r * kscale_row + (uint32_t)(lane & 3) * 4u;
-      bs_vo[j] = (uint32_t)(br * kscale_row) + (uint32_t)(lane & 3) * 4u;
+      const uint32_t w4 = sc16 ? 0u : (uint32_t)(lane & 3) * 4u;
+      as_vo[j] = (uint32_t)r * kscale_row + w4;
+      bs_vo[j] = (uint32_t)(br * kscale_row) + w4;
     }
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
@@ -200,14 +207,34 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     dma16(d.vb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q], (uint32_t)kt * kRowBytes);
   };
   // the scales of stage group g (stages 4 g .. 4 g + 3) of the item described by d into buffer sb
+  // (called at a stage's top, outside its MFMAs, except in the deep pipeline, which takes the
+  // 16-byte form only: no branch may sit among the MFMAs)
   auto dma_s = [&](const Desc& d, int sb, int g) {
     if constexpr (kMx) {
       const uint32_t ss = lds_sc + (uint32_t)sb * (uint32_t)kScBuf;
+      if (sc16) {
+        dma16(d.vas, ss, as_vo[0], (uint32_t)g * 16u);
+        dma16(d.vbs, ss + 4096u, bs_vo[0], (uint32_t)g * 16u);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dma4(d.vas, ss + (uint32_t)j * 256u, as_vo[j], (uint32_t)g * 16u);
-        dma4(d.vbs, ss + 4096u + (uint32_t)j * 256u, bs_vo[j], (uint32_t)g * 16u);
+        for (int j = 0; j < 4; ++j) {
+          dma4(d.vas, ss + (uint32_t)j * 256u, as_vo[j], (uint32_t)g * 16u);
+          dma4(d.vbs, ss + 4096u + (uint32_t)j * 256u, bs_vo[j], (uint32_t)g * 16u);
+        }
       }
+    }
+  };
+
+  // the scale group load of the deep pipeline, predicated by its descriptor: off, it reads no memory
+  // but still writes (zeros) to its LDS buffer, so it always targets the buffer that no pending
+  // stage uses
+  auto dma_s_pred = [&](const Desc& d, bool on, int sb, int g) {
+    if constexpr (kMx) {
+      const i32x4 z = make_vsharp(p.a, 0);
+      Desc e;
+      e.vas = on ? d.vas : z;
+      e.vbs = on ? d.vbs : z;
+      dma_s(e, sb, g);
     }
   };
 
@@ -217,10 +244,21 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   descs(cur, dc);
   int par = 0;    // buffer of the current item's first stage
   int spar = 0;   // scale buffer of the current item's first stage group
+  int sbc = 0, sbn = 0;   // deep pipeline: scale buffers of the current and the next stage
   if (cur.t < hi) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) { dma_a(dc, 0, cur.u0, q); dma_b(dc, 0, cur.u0, q); }
     dma_s(dc, 0, cur.u0 >> 2);
+    if constexpr (kDeep) {
+      // the first stage landed before the loop; the second (every item has at least two) follows
+      wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { dma_a(dc, 1, cur.u0 + 1, q); dma_b(dc, 1, cur.u0 + 1, q); }
+      const bool ng = ((cur.u0 + 1) & 3) == 0;
+      sbn = ng ? 1 : 0;
+      dma_s_pred(dc, ng, 1, (cur.u0 + 1) >> 2);
+    }
   }
 
   for (int round = 0; cur.t < hi; ++round) {
@@ -239,6 +277,34 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     // last group, the next item's first one -- into the buffer of the group before the current one,
     // which every wave finished reading before this stage's barrier.
     const int g0 = cur.u0 >> 2, glast = (cur.u1 - 1) >> 2;
+    if constexpr (kDeep) {
+      // the item's first stage landed before the barrier of the previous stage (or the prologue's)
+      StepFrag<true> f0;
+      read_first<true, kFc1, false, false, 16>(f0, smem + par * kStageBytes,
+                                               smem + kScOff + sbc * kScBuf + (cur.u0 & 3) * 4, wm, wn, lane);
+#pragma unroll 1
+      for (int s = 0; s < n; ++s) {
+        const int kt = cur.u0 + s, b = (par + s) & 1, bn = b ^ 1;
+        const int kn = s + 1 < n ? kt + 1 : nxt.u0;           // the next stage
+        const bool in2 = s + 2 < n;                           // the stage after next: this item's or the next's
+        const Desc& dt = in2 ? dc : dn;
+        const int k2 = in2 ? kt + 2 : nxt.u0 + (s + 2 - n);
+        // a new scale group goes to the buffer the next stage does not use: it holds this stage's
+        // group (read before the barrier) or an older one
+        const bool ng = (!in2 && s + 2 == n) || (k2 & 3) == 0;  // it starts a scale group
+        const int sbd = ng ? (sbn ^ 1) : sbn;
+        mma_stage_mx_deep<kFc1>(
+            core, f0, smem + b * kStageBytes, smem + kScOff + sbc * kScBuf + (kt & 3) * 4, smem + bn * kStageBytes,
+            smem + kScOff + sbn * kScBuf + (kn & 3) * 4, wm, wn, lane, [&](int q) { dma_a(dt, b, k2, q); },
+            [&](int q) { dma_b(dt, b, k2, q); }, [&]() { dma_s_pred(dt, ng, sbn ^ 1, k2 >> 2); },
+            [&]() {
+              wait_vmcnt<0>();
+              __syncthreads();
+            });
+        sbc = sbn;
+        sbn = sbd;
+      }
+    } else {
 #pragma unroll 1
     for (int s = 0; s < n; ++s) {
       const int kt = cur.u0 + s, b = (par + s) & 1;
@@ -264,6 +330,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       mma_stage<kMx, kFc1, false, false, 16>(
           core, sA, sS, wm, wn, lane, [&](int q) { dma_a(dd, bn, kn, q); }, [&](int q) { dma_b(dd, bn, kn, q); },
           []() {});
+    }
     }
     par = (par + n) & 1;
     spar = (spar + glast - g0 + 1) & 1;
@@ -458,8 +525,9 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
 
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
   FwdKArgs k = make_fwd_args(g, mx, true);
-  if (mx) fwd_gemm_kernel<true, true, false><<<kGemmGrid, 256, 0, st>>>(k);
-  else fwd_gemm_kernel<false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+  if (mx && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (mx) fwd_gemm_kernel<true, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+  else fwd_gemm_kernel<false, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
   return hipGetLastError();
 }
 
@@ -471,19 +539,25 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   const bool split = g.part != nullptr && kU / kMinSplitUnits >= 2;
   // pass 1 (or the only pass): the output-dtype instance
   k.split = split ? 1 : 0;
+  // MXFP8 with K of at least two 128-byte stages and 16-byte scale rows takes the deep pipeline
+  // (split parts have at least kMinSplitUnits stages)
+  const bool deep = mx && g.K >= 256 && g.K % 512 == 0;
   if (g.out_f32) {
-    if (mx) fwd_gemm_kernel<true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else fwd_gemm_kernel<false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+    if (deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+    else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+    else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
   } else {
-    if (mx) fwd_gemm_kernel<true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
-    else fwd_gemm_kernel<false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+    if (deep) fwd_gemm_kernel<true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+    else if (mx) fwd_gemm_kernel<true, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+    else fwd_gemm_kernel<false, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !split) return err;
   // pass 2: the split parts (whether there are any is decided on the device), then the fixup
   k.split = 2;
-  if (mx) fwd_gemm_kernel<true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
-  else fwd_gemm_kernel<false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  if (deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+  else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const dim3 fgrid(kGemmGrid, kBM / 32);

@@ -351,6 +351,53 @@ __device__ __forceinline__ void mma_stage(TileCore<kMx, kFc1>& core, const uint8
   }
 }
 
+// The substep-0 fragments of the stage in sA / sS.
+template <bool kMx, bool kFc1, bool kAMN, bool kBMN, int kScRow>
+__device__ __forceinline__ void read_first(StepFrag<kMx>& f0, const uint8_t* sA, const uint8_t* sS, int wm, int wn,
+                                           int lane) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    read_elem<kMx, kFc1, kAMN, kBMN, kScRow>(f0, sA, sS, 0, e, wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// MXFP8 stage with its barrier between the two substeps (the forward GEMM with K of at least two
+// stages).  On entry f0 holds this stage's substep-0 fragments, read during the previous stage's
+// substep 1 (or by read_first).  Substep 0 reads the substep-1 fragments of this stage (sA, sS).
+// sync() then waits for the next stage's loads and for every wave, after which this stage's buffer
+// is free: substep 1 reads the next stage's substep-0 fragments (sAn, sSn) into f0, and issues the
+// loads of the stage after next into this stage's buffer (dma_a / dma_b, q < 8; dma_s its scale
+// group, predicated by its descriptor, since no branch may sit among the MFMAs).  The fragment
+// reads of both halves overlap MFMAs, instead of every wave reading its first fragments at once
+// after a barrier, and the loads have a whole stage to land.
+template <bool kFc1, class DA, class DB, class DS, class SY>
+__device__ __forceinline__ void mma_stage_mx_deep(TileCore<true, kFc1>& core, StepFrag<true>& f0, const uint8_t* sA,
+                                                  const uint8_t* sS, const uint8_t* sAn, const uint8_t* sSn, int wm,
+                                                  int wn, int lane, DA&& dma_a, DB&& dma_b, DS&& dma_s, SY&& sync) {
+  StepFrag<true> f1;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    mma_ij(core, f0, q);
+    if (q & 1) read_elem<true, kFc1, false, false, 16>(f1, sA, sS, 1, next_elem(q >> 1), wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sync();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    mma_ij(core, f1, q);
+    if (q & 1) {
+      read_elem<true, kFc1, false, false, 16>(f0, sAn, sSn, 0, next_elem(q >> 1), wm, wn, lane);
+      dma_b(q >> 1);
+    } else {
+      dma_a(q >> 1);
+    }
+    if (q == 0) dma_s();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
 // allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
 // and spills.
