@@ -76,13 +76,12 @@ struct FwdItem {
   int t, tile, part, e, mt, nt, row0, mrows, u0, u1;
 };
 
-// kDeep (MXFP8 with K of at least two stages and a multiple of 512, so 16-byte scale rows): the
-// stage barrier sits between the two substeps and stage loads are issued two stages ahead
-// (mma_stage_mx_deep).
+// kDeep (K of at least two stages; MXFP8 also needs K % 512 == 0, so 16-byte scale rows): the stage
+// barrier sits inside the stage and stage loads are issued two stages ahead (mma_stage_mx_deep,
+// mma_stage_bf16_deep).
 template <bool kMx, bool kFc1, bool kOutF32, bool kDeep>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
-  static_assert(!kDeep || kMx, "the deep pipeline is the MXFP8 one");
   // 2 pipeline stages, then the MXFP8 scales of groups of 4 stages (2 x 8 KB), then the routing
   // probabilities of the tile's rows (FC1, double-buffered by work item)
   constexpr int kScOff = 2 * kStageBytes;
@@ -279,9 +278,9 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     const int g0 = cur.u0 >> 2, glast = (cur.u1 - 1) >> 2;
     if constexpr (kDeep) {
       // the item's first stage landed before the barrier of the previous stage (or the prologue's)
-      StepFrag<true> f0;
-      read_first<true, kFc1, false, false, 16>(f0, smem + par * kStageBytes,
-                                               smem + kScOff + sbc * kScBuf + (cur.u0 & 3) * 4, wm, wn, lane);
+      StepFrag<kMx> f0;
+      read_first<kMx, kFc1, false, false, 16>(f0, smem + par * kStageBytes,
+                                              smem + kScOff + sbc * kScBuf + (cur.u0 & 3) * 4, wm, wn, lane);
 #pragma unroll 1
       for (int s = 0; s < n; ++s) {
         const int kt = cur.u0 + s, b = (par + s) & 1, bn = b ^ 1;
@@ -293,14 +292,18 @@ void fwd_gemm_kernel(const FwdKArgs p) {
         // group (read before the barrier) or an older one
         const bool ng = (!in2 && s + 2 == n) || (k2 & 3) == 0;  // it starts a scale group
         const int sbd = ng ? (sbn ^ 1) : sbn;
-        mma_stage_mx_deep<kFc1>(
-            core, f0, smem + b * kStageBytes, smem + kScOff + sbc * kScBuf + (kt & 3) * 4, smem + bn * kStageBytes,
-            smem + kScOff + sbn * kScBuf + (kn & 3) * 4, wm, wn, lane, [&](int q) { dma_a(dt, b, k2, q); },
-            [&](int q) { dma_b(dt, b, k2, q); }, [&]() { dma_s_pred(dt, ng, sbn ^ 1, k2 >> 2); },
-            [&]() {
-              wait_vmcnt<0>();
-              __syncthreads();
-            });
+        auto sync = [&]() {
+          wait_vmcnt<0>();
+          __syncthreads();
+        };
+        if constexpr (kMx)
+          mma_stage_mx_deep<kFc1>(
+              core, f0, smem + b * kStageBytes, smem + kScOff + sbc * kScBuf + (kt & 3) * 4, smem + bn * kStageBytes,
+              smem + kScOff + sbn * kScBuf + (kn & 3) * 4, wm, wn, lane, [&](int q) { dma_a(dt, b, k2, q); },
+              [&](int q) { dma_b(dt, b, k2, q); }, [&]() { dma_s_pred(dt, ng, sbn ^ 1, k2 >> 2); }, sync);
+        else
+          mma_stage_bf16_deep<kFc1>(core, f0, smem + b * kStageBytes, smem + bn * kStageBytes, wm, wn, lane,
+                                    [&](int q) { dma_a(dt, b, k2, q); }, [&](int q) { dma_b(dt, b, k2, q); }, sync);
         sbc = sbn;
         sbn = sbd;
       }
@@ -527,6 +530,7 @@ hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
   FwdKArgs k = make_fwd_args(g, mx, true);
   if (mx && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (mx) fwd_gemm_kernel<true, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (g.K >= 128) fwd_gemm_kernel<false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else fwd_gemm_kernel<false, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
   return hipGetLastError();
 }
@@ -539,24 +543,27 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   const bool split = g.part != nullptr && kU / kMinSplitUnits >= 2;
   // pass 1 (or the only pass): the output-dtype instance
   k.split = split ? 1 : 0;
-  // MXFP8 with K of at least two 128-byte stages and 16-byte scale rows takes the deep pipeline
+  // K of at least two 128-byte stages (and 16-byte scale rows for MXFP8) takes the deep pipeline
   // (split parts have at least kMinSplitUnits stages)
-  const bool deep = mx && g.K >= 256 && g.K % 512 == 0;
+  const bool deep = mx ? (g.K >= 256 && g.K % 512 == 0) : g.K >= 128;
   if (g.out_f32) {
-    if (deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+    if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
     else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+    else if (deep) fwd_gemm_kernel<false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
     else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
   } else {
-    if (deep) fwd_gemm_kernel<true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+    if (mx && deep) fwd_gemm_kernel<true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
     else if (mx) fwd_gemm_kernel<true, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+    else if (deep) fwd_gemm_kernel<false, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
     else fwd_gemm_kernel<false, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || !split) return err;
   // pass 2: the split parts (whether there are any is decided on the device), then the fixup
   k.split = 2;
-  if (deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+  if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (deep) fwd_gemm_kernel<false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
   else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
   err = hipGetLastError();
   if (err != hipSuccess) return err;

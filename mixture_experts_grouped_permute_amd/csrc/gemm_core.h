@@ -398,6 +398,47 @@ __device__ __forceinline__ void mma_stage_mx_deep(TileCore<true, kFc1>& core, St
   }
 }
 
+// BF16 stage with its barrier after the second of its four substeps (the forward GEMM with K of at
+// least two stages).  On entry f0 holds this stage's substep-0 fragments.  Substeps 0 and 1 read
+// the fragments of substeps 1, 2 and 3 (this stage's buffer is then fully read); sync() waits for
+// the next stage's loads and for every wave; substep 2 reads the next stage's substep-0 fragments
+// (sAn) into f0 and, with substep 3, issues the loads of the stage after next into this stage's
+// buffer.  Memory instructions per substep: 16, 8, 16, 8; three fragment sets live at most.
+template <bool kFc1, class DA, class DB, class SY>
+__device__ __forceinline__ void mma_stage_bf16_deep(TileCore<false, kFc1>& core, StepFrag<false>& f0,
+                                                    const uint8_t* sA, const uint8_t* sAn, int wm, int wn, int lane,
+                                                    DA&& dma_a, DB&& dma_b, SY&& sync) {
+  StepFrag<false> f1, f2, f3;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    mma_ij(core, f0, q);
+    if (q & 1) read_elem<false, kFc1, false, false, 4>(f1, sA, sA, 1, next_elem(q >> 1), wm, wn, lane);
+    else read_elem<false, kFc1, false, false, 4>(f2, sA, sA, 2, next_elem(q >> 1), wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    mma_ij(core, f1, q);
+    if (q & 1) read_elem<false, kFc1, false, false, 4>(f3, sA, sA, 3, next_elem(q >> 1), wm, wn, lane);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  sync();
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    mma_ij(core, f2, q);
+    if (q & 1) read_elem<false, kFc1, false, false, 4>(f0, sAn, sAn, 0, next_elem(q >> 1), wm, wn, lane);
+    else dma_a(q >> 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    mma_ij(core, f3, q);
+    if (!(q & 1)) dma_b(q >> 1);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
 // allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
 // and spills.
