@@ -25,6 +25,12 @@ CASES = [
     ("all-to-one", cfg_small(T=520, H=128, I=256, E=4, k=1), [0, 0, 520, 0]),
     ("finegrained-e64-k8", get_config(5).with_(T=512, H=256, I=256, precision="bf16"), None),
     ("zipf-zero-expert", get_config(3).with_(T=1024, H=256, I=384, precision="bf16"), None),
+    # K of a single 128-byte stage in both GEMMs (BF16: the K loop without the two-ahead loads)
+    ("one-stage-k", cfg_small(T=300, H=64, I=64, E=4, k=2), None),
+    # FC1 with a single-stage K, FC2 with two stages
+    ("mixed-depth", cfg_small(T=300, H=64, I=128, E=4, k=2), None),
+    # MXFP8 FC1 with K = 384: three stages but 12-byte scale rows (scale words read per lane)
+    ("mx-row-scales", cfg_small(T=300, H=384, I=256, E=4, k=2), None),
 ]
 
 
