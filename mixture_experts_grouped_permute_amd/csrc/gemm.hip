@@ -369,23 +369,29 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           float g[16], u[16];
           agpr_read16(core.acc[i][jj], g);
           agpr_read16(core.acc[i][jj + 2], u);
-          const uint32_t e0 = (uint32_t)m * I32 + col + (uint32_t)ch;                       // element of h
+          // stores go out in the lane-paired layout (pack_bf16_runs8 / swap_runs8): the lane's 8
+          // consecutive columns 16 pp + 8 hh + [0, 8) of the block
+          const uint32_t e8 = (uint32_t)m * I32 + col + 2u * (uint32_t)ch;                  // element of h
           if (p.save_gu) {
+            u32x4 og[2], ou[2];
+            pack_bf16_runs8(g, og);
+            pack_bf16_runs8(u, ou);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const uint32_t o = (2 * (uint32_t)m * I32 + col + (uint32_t)(ch + 8 * q)) * 2u;
-              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(g[4 * q], g[4 * q + 1]), pack_bf16x2(g[4 * q + 2], g[4 * q + 3])}, rg, o, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(u[4 * q], u[4 * q + 1]), pack_bf16x2(u[4 * q + 2], u[4 * q + 3])}, rg, o + I32 * 2u, 0, 0);
+            for (int pp = 0; pp < 2; ++pp) {
+              const uint32_t o = (2 * (uint32_t)m * I32 + col + 2u * (uint32_t)ch + 16u * pp) * 2u;
+              __builtin_amdgcn_raw_buffer_store_b128(og[pp], rg, o, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(ou[pp], rg, o + I32 * 2u, 0, 0);
             }
           }
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = (silu_f(g[r]) * u[r]) * pr;
           if (!kMx || p.save_h) {
+            u32x4 oh[2];
+            pack_bf16_runs8(v, oh);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(v[4 * q], v[4 * q + 1]), pack_bf16x2(v[4 * q + 2], v[4 * q + 3])},
-                                                    kMx ? rh : ro, (e0 + 8u * q) * 2u, 0, 0);
+            for (int pp = 0; pp < 2; ++pp)
+              __builtin_amdgcn_raw_buffer_store_b128(oh[pp], kMx ? rh : ro, (e8 + 16u * pp) * 2u, 0, 0);
           }
           if constexpr (kMx) {
             // the 32-column block of this row is split between lanes l and l ^ 32
@@ -394,9 +400,13 @@ void fwd_gemm_kernel(const FwdKArgs p) {
             for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
             am = fmaxf(am, __shfl_xor(am, 32, 64));
             const int sx = mx_shared_exp(am);
+            uint32_t cq[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              __builtin_amdgcn_raw_buffer_store_b32(mx_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], sx), ro, e0 + 8u * q, 0, 0);
+            for (int q = 0; q < 4; ++q) cq[q] = mx_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], sx);
+            u32x2 oc[2];
+            swap_runs8(cq, oc);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) __builtin_amdgcn_raw_buffer_store_b64(oc[pp], ro, e8 + 16u * pp, 0, 0);
             // one scale byte per row and block, from the lane holding its first columns
             const uint32_t so = ch == 0 ? (uint32_t)m * (I32 / 32) + col / 32 : 0xFFFFFFF0u;
             __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(sx + 127), rsc, so, 0, 0);
@@ -430,13 +440,18 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           float a[16];
           agpr_read16(core.acc[i][j], a);
           const uint32_t e0 = (uint32_t)m * ld + c0 + tc + (uint32_t)ch;
+          if constexpr (kOutF32) {
+            // fp32 runs already give 32 contiguous bytes per row (lanes l and l ^ 32)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if constexpr (kOutF32)
+            for (int q = 0; q < 4; ++q)
               __builtin_amdgcn_raw_buffer_store_b128(f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, ro, (e0 + 8u * q) * 4u, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])},
-                                                    ro, (e0 + 8u * q) * 2u, 0, 0);
+          } else {
+            // bf16 in the lane-paired layout: 8 consecutive columns 16 pp + 8 hh + [0, 8) per lane
+            const uint32_t e8 = (uint32_t)m * ld + c0 + tc + 2u * (uint32_t)ch;
+            u32x4 oa[2];
+            pack_bf16_runs8(a, oa);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) __builtin_amdgcn_raw_buffer_store_b128(oa[pp], ro, (e8 + 16u * pp) * 2u, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }

@@ -286,7 +286,11 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       // ScaledSwiGLU backward per element (dh = this tile, g / u = the saved gate-up output,
       // p = the routing probability of the row):
       //   dG = dh p u s (1 + g (1 - s)), dU = dh p g s, s = sigmoid(g); dprob partial = sum dh g s u.
-      // The saved g / u of the next 32 x 32 block are loaded while this one is computed.
+      // The saved g / u of the next 32 x 32 block are loaded while this one is computed.  Each lane
+      // first trades half of its accumulator runs with lane l ^ 32 (v_permlane32_swap), so that it
+      // holds 8 consecutive columns 16 pp + 8 hh + [0, 8) (pp < 2, hh = l / 32) of its row: g / u are
+      // then read and dG / dU written 16 bytes per lane, half the accesses of the accumulators'
+      // 8-byte runs, with 32 contiguous bytes per row per access.
       const int64_t I = p.I;
       const uint32_t I32 = (uint32_t)I;
       const float* prs = reinterpret_cast<const float*>(smem + kXOff) + ipar * 256;
@@ -294,18 +298,19 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const uint32_t mr = (uint32_t)cur.mrows;
       const rsrc_t rgu = make_rsrc(p.gu + (int64_t)cur.row0 * 2 * I, mr * I32 * 4);
       const rsrc_t rdg = make_rsrc(p.dgu + (int64_t)cur.row0 * 2 * I, mr * I32 * 4);
-      u32x2 gl[2][4], ul[2][4];
-      auto boff = [&](int blk, int q) -> uint32_t {   // byte offset of run q of block blk (gate half)
+      const int hh = elane >> 5;
+      u32x4 gl[2][2], ul[2][2];                      // [buffer][pp]: 8 bf16 each
+      auto boff = [&](int blk, int pp) -> uint32_t {  // byte offset of the lane's 8 gate columns
         const int i = blk >> 2, j = blk & 3;
         const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
-        return (2 * m * I32 + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32 + ch + 8 * q)) * 2u;
+        return (2 * m * I32 + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32 + 16 * pp + 8 * hh)) * 2u;
       };
       auto load = [&](int blk, int bf) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t o = boff(blk, q);
-          gl[bf][q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rgu, o, 0, 0));
-          ul[bf][q] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rgu, o + I32 * 2u, 0, 0));
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint32_t o = boff(blk, pp);
+          gl[bf][pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rgu, o, 0, 0));
+          ul[bf][pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rgu, o + I32 * 2u, 0, 0));
         }
       };
       float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -319,15 +324,25 @@ void bwd_gemm_kernel(const BwdKArgs p) {
           const float pr = prs[wm * 128 + i * 32 + r32];
           float dh[16];
           agpr_read16(core.acc[i][j], dh);
+          // dh[4 q + c] is column 8 q + 4 hh + c; after the swaps dh[8 pp + x] is column 16 pp + 8 hh + x
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float dgv[4], duv[4];
+          for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-              const uint32_t gw = gl[bf][q][x >> 1], uw = ul[bf][q][x >> 1];
+            for (int c = 0; c < 4; ++c) {
+              const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, dh[8 * pp + c]),
+                                                              __builtin_bit_cast(uint32_t, dh[8 * pp + 4 + c]), false, false);
+              dh[8 * pp + c] = __builtin_bit_cast(float, (uint32_t)r[0]);
+              dh[8 * pp + 4 + c] = __builtin_bit_cast(float, (uint32_t)r[1]);
+            }
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            float dgv[8], duv[8];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+              const uint32_t gw = gl[bf][pp][x >> 1], uw = ul[bf][pp][x >> 1];
               const float g = bf16_to_f32((uint16_t)((x & 1) ? (gw >> 16) : (gw & 0xFFFF)));
               const float uu = bf16_to_f32((uint16_t)((x & 1) ? (uw >> 16) : (uw & 0xFFFF)));
-              const float d = dh[4 * q + x];
+              const float d = dh[8 * pp + x];
               const float sg = sigmoid_f(g);
               const float sl = g * sg;
               part[i] += d * (sl * uu);
@@ -335,10 +350,13 @@ void bwd_gemm_kernel(const BwdKArgs p) {
               duv[x] = da * sl;
               dgv[x] = da * uu * (sg * (1.0f + g * (1.0f - sg)));
             }
-            const uint32_t o = boff(blk, q);
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3])}, rdg, o, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3])}, rdg,
-                                                  o + I32 * 2u, 0, 0);
+            const uint32_t o = boff(blk, pp);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3]),
+                                                         pack_bf16x2(dgv[4], dgv[5]), pack_bf16x2(dgv[6], dgv[7])},
+                                                   rdg, o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3]),
+                                                         pack_bf16x2(duv[4], duv[5]), pack_bf16x2(duv[6], duv[7])},
+                                                   rdg, o + I32 * 2u, 0, 0);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -372,14 +390,18 @@ void bwd_gemm_kernel(const BwdKArgs p) {
           const uint32_t col = (uint32_t)cbase + (uint32_t)(wn * 128 + j * 32);          // in the destination
           float a[16];
           agpr_read16(core.acc[i][j], a);
-          const uint32_t e0 = m * N32 + col + (uint32_t)ch;
+          if constexpr (kOutF32) {
+            const uint32_t e0 = m * N32 + col + (uint32_t)ch;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if constexpr (kOutF32)
+            for (int q = 0; q < 4; ++q)
               __builtin_amdgcn_raw_buffer_store_b128(f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, ro, (e0 + 8u * q) * 4u, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack_bf16x2(a[4 * q], a[4 * q + 1]), pack_bf16x2(a[4 * q + 2], a[4 * q + 3])},
-                                                    ro, (e0 + 8u * q) * 2u, 0, 0);
+          } else {
+            // bf16 in the lane-paired layout: 8 consecutive columns 16 pp + 8 hh + [0, 8) per lane
+            const uint32_t e8 = m * N32 + col + 2u * (uint32_t)ch;
+            u32x4 oa[2];
+            pack_bf16_runs8(a, oa);
+#pragma unroll
+            for (int pp = 0; pp < 2; ++pp) __builtin_amdgcn_raw_buffer_store_b128(oa[pp], ro, (e8 + 16u * pp) * 2u, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
         }

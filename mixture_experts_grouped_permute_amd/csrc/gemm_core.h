@@ -439,6 +439,35 @@ __device__ __forceinline__ void mma_stage_bf16_deep(TileCore<false, kFc1>& core,
   }
 }
 
+// Lane pairing for epilogue stores.  A lane holds its row's columns 8 q + 4 hh + c (q, c < 4,
+// hh = lane / 32) of a 32 x 32 accumulator block; v_permlane32_swap of runs 2 pp and 2 pp + 1 with
+// lane l ^ 32 leaves it 8 consecutive columns 16 pp + 8 hh + [0, 8) instead, so that stores move 16
+// (bf16) or 8 (E4M3) bytes per lane and 32 or 16 contiguous bytes per row.
+//   pack_bf16_runs8: the 16 values to bf16, o[pp] = columns 16 pp + 8 hh + [0, 8);
+//   swap_runs8: 4 words of 4 E4M3 codes (run q each), o[pp] = columns 16 pp + 8 hh + [0, 8).
+__device__ __forceinline__ void pack_bf16_runs8(const float (&v)[16], u32x4 (&o)[2]) {
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    uint32_t w0[2], w1[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      w0[k] = pack_bf16x2(v[8 * pp + 2 * k], v[8 * pp + 2 * k + 1]);
+      w1[k] = pack_bf16x2(v[8 * pp + 4 + 2 * k], v[8 * pp + 4 + 2 * k + 1]);
+      const auto r = __builtin_amdgcn_permlane32_swap(w0[k], w1[k], false, false);
+      w0[k] = (uint32_t)r[0];
+      w1[k] = (uint32_t)r[1];
+    }
+    o[pp] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+  }
+}
+__device__ __forceinline__ void swap_runs8(const uint32_t (&c)[4], u32x2 (&o)[2]) {
+#pragma unroll
+  for (int pp = 0; pp < 2; ++pp) {
+    const auto r = __builtin_amdgcn_permlane32_swap(c[2 * pp], c[2 * pp + 1], false, false);
+    o[pp] = u32x2{(uint32_t)r[0], (uint32_t)r[1]};
+  }
+}
+
 // Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
 // allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
 // and spills.
