@@ -23,7 +23,11 @@ Readings where the pages are silent (all listed with the design notes):
     the combine is an unweighted sum of the k expert outputs.
   * Operand formats: "bf16" rounds X to bf16 and h to bf16; "mxfp8" quantizes
     X and h along H / I and W1, W2 along their K (H / I) with the OCP MXFP8
-    rule; "exact" applies no rounding at all (used by the derivative checks).
+    rule; "fp8" (forward only) quantizes each GEMM operand tensor with one
+    scale: every W1_e and W2_e, and each expert's rows of X_perm and of h --
+    the operands of that expert's GEMM -- with h rounded to bf16 first (the
+    scale needs the amax of the whole tensor, so h exists in bf16 before it is
+    quantized); "exact" applies no rounding at all (the derivative checks).
   * Each grouped GEMM writes its output in the layer's I/O dtype (bf16, or f32
     for f32 I/O) -- the down projection's z before the combine, the FC1 dgrad
     output before the un-permute sum; the combine sums in high precision and
@@ -73,6 +77,8 @@ def activation_operand(x, precision: str):
         return nm.round_bf16(x)
     if precision == "mxfp8":
         return nm.fake_quant_mxfp8(x, axis=1)
+    if precision == "fp8":          # x: the rows of one expert (one tensor)
+        return nm.fake_quant_fp8_tensor(nm.round_bf16(x))
     raise ValueError(precision)
 
 
@@ -80,6 +86,8 @@ def weight_operand(w_e, precision: str, k_axis: int = 1):
     """A bf16 master weight as the GEMM sees it (MXFP8: blocks along the GEMM's K)."""
     if precision in ("exact", "bf16"):
         return w_e
+    if precision == "fp8":
+        return nm.fake_quant_fp8_tensor(w_e)
     return nm.fake_quant_mxfp8(w_e, axis=k_axis)
 
 
@@ -126,7 +134,10 @@ def forward(x, topk_idx, topk_prob, w1, w2, precision: str = "bf16", io_dtype: s
     I = int(w2.shape[2])
     perm = permute(idx, E)
     tok = perm.token_of_row
-    x_perm = activation_operand(xs, precision)[tok]
+    if precision == "fp8":
+        x_perm = nm.round_bf16(xs)[tok]     # quantized per expert segment below
+    else:
+        x_perm = activation_operand(xs, precision)[tok]
     p_perm = prob.reshape(-1)[perm.src_index]
     R = T * k
     gu = np.zeros((R, 2 * I))
@@ -142,6 +153,8 @@ def forward(x, topk_idx, topk_prob, w1, w2, precision: str = "bf16", io_dtype: s
         if e not in todo:
             z[lo:hi] = np.nan
             continue
+        if precision == "fp8":
+            x_perm[lo:hi] = activation_operand(x_perm[lo:hi], precision)
         g_, h_, hq_, z_ = expert_forward(x_perm[lo:hi], p_perm[lo:hi],
                                          weight_operand(f64(w1[e]), precision),
                                          weight_operand(f64(w2[e]), precision), precision, io_dtype)
@@ -159,7 +172,11 @@ def forward_tokens(x, topk_idx, topk_prob, w1, w2, tokens, precision="bf16", io_
 
     Every rounding step of the layer acts within one row of X or h, or within
     one row of a weight, so a token's output does not depend on other tokens.
+    That is not so for per-tensor FP8 (the scale of an expert's rows depends on
+    all of them), which `forward` computes instead.
     """
+    if precision == "fp8":
+        raise ValueError("per-tensor FP8 couples the rows of an expert; use forward")
     idx = np.asarray(topk_idx)
     prob = f64(topk_prob)
     cache = {} if weight_cache is None else weight_cache
@@ -221,6 +238,8 @@ def backward(fw: Forward, x, dy, w1, w2, experts=None) -> Backward:
     other expert are NaN.
     """
     prec, io = fw.precision, fw.io_dtype
+    if prec == "fp8":
+        raise ValueError("the per-tensor FP8 variant is forward only")
     perm = fw.perm
     T, k = perm.row_id_map.size // perm.k, perm.k
     R = T * k

@@ -5,14 +5,23 @@ pressure with MXFP8, Figure 3; page "How BioNeMo cuts overhead", How MXFP8
 reduces memory use):
   * BF16: 1 sign, 8 exponent, 7 mantissa bits.
   * MXFP8: E4M3 elements plus one shared E8M0 scale per 32 consecutive values.
+  * FP8 (same sections): 8-bit values whose scaling is coarser than MXFP8's
+    per-32-value blocks -- read as one scale per tensor (below).
 The pages do not spell out the scale rule or the rounding; the readings taken
-are the OCP Microscaling (MX) v1.0 ones:
+for MXFP8 are the OCP Microscaling (MX) v1.0 ones:
   * shared exponent s = floor(log2(amax)) - 8, where 8 is the exponent of the
     largest normal E4M3 value (448 = 1.75 * 2^8); s is clamped to [-127, 127],
     so an all-zero block gets s = -127 (E8M0 byte 0x00); E8M0 byte = s + 127;
   * element = v / 2^s rounded to E4M3FN (OCP variant: bias 7, no infinities,
     max 448, subnormals n * 2^-9) with round-to-nearest, ties to even, and
     saturated to +-448; the sign of a value that rounds to zero is kept.
+For per-tensor FP8 the readings are current scaling of each tensor as a whole:
+  * s = 448 / amax as an fp32 division (correctly rounded), amax = max |v|
+    over the tensor; amax == 0 gives s = 1, and an s that overflows fp32 is
+    clamped to the largest finite fp32 value;
+  * element = E4M3FN(fp32(v * s)): the product rounded once to fp32, then to
+    E4M3FN as above (nearest, ties to even, saturated to +-448, zero keeps its
+    sign); the value the code stands for is decode(code) / s.
 """
 from __future__ import annotations
 
@@ -194,3 +203,59 @@ def fake_quant_mxfp8_segments(x, offsets) -> np.ndarray:
         lo, hi = int(offsets[g]), int(offsets[g + 1])
         out[lo:hi] = deq[:, pad[g]:pad[g] + (hi - lo)].T
     return out
+
+
+# ----------------------------------------------------------------------------- per-tensor FP8
+
+FLT_MAX = float(np.finfo(np.float32).max)
+
+
+def fp8_tensor_scale(amax) -> np.float32:
+    """s = 448 / amax in fp32; 1 for amax == 0; clamped to the largest finite fp32 value."""
+    a = np.float32(amax)
+    if a == 0:
+        return np.float32(1.0)
+    with np.errstate(over="ignore"):
+        s = np.float32(E4M3_MAX) / a                 # one IEEE fp32 division
+    return np.float32(FLT_MAX) if np.isinf(s) else np.float32(s)
+
+
+def quantize_fp8_tensor(x):
+    """Per-tensor-scaled E4M3 of x (values exactly representable in fp32, e.g. bf16).
+
+    Returns (codes uint8 with x's shape, s as np.float32).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    x32 = x64.astype(np.float32)
+    if not np.array_equal(x32.astype(np.float64), x64, equal_nan=True):
+        raise ValueError("per-tensor FP8 input must be exactly representable in fp32")
+    amax = float(np.max(np.abs(x64))) if x64.size else 0.0
+    s = fp8_tensor_scale(amax)
+    q = (x32 * s).astype(np.float64)                 # fp32 product, then E4M3
+    return encode_e4m3(round_e4m3(q)), s
+
+
+def dequantize_fp8_tensor(codes, s) -> np.ndarray:
+    return decode_e4m3(codes) / np.float64(s)
+
+
+def fake_quant_fp8_tensor(x) -> np.ndarray:
+    """dequantize(quantize(x)) with one scale for all of x."""
+    c, s = quantize_fp8_tensor(x)
+    return dequantize_fp8_tensor(c, s)
+
+
+def quantize_fp8_segments(x, offsets):
+    """Per-tensor FP8 of each row segment [offsets[g], offsets[g+1]) of x [R, C] on its own.
+
+    Returns (codes [R, C] uint8, scales [G] float32); an empty segment gets s = 1.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    off = np.asarray(offsets, dtype=np.int64)
+    codes = np.zeros(x.shape, dtype=np.uint8)
+    scales = np.ones(len(off) - 1, dtype=np.float32)
+    for g in range(len(off) - 1):
+        lo, hi = int(off[g]), int(off[g + 1])
+        if hi > lo:
+            codes[lo:hi], scales[g] = quantize_fp8_tensor(x[lo:hi])
+    return codes, scales
