@@ -25,7 +25,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE grouped-MLP fwd tokens/s + TFLOP/s (bf16, MXFP8), Mixtral 8x7B layer"
-PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0}      # MI355X dense MFMA peaks
+PEAK_TFLOPS = {"bf16": 2500.0, "mxfp8": 5000.0, "fp8": 5000.0}      # MI355X dense MFMA peaks
 PEAK_HBM_GBS = 8000.0
 
 
@@ -179,6 +179,9 @@ def fwd_leg(cfg, steps, warmup):
     R, H, I, E = cfg.R, cfg.H, cfg.I, cfg.E
     esz = 4 if cfg.x_dtype == "f32" else 2
     op = 1 + 1 / 32 if cfg.precision == "mxfp8" else 2
+    if cfg.precision == "fp8":
+        # bf16 rows written, then read by the amax and the quantize pass, codes written
+        op = 2 + 2 + 2 + 1
     # algorithmic bytes: read X once, write T*k permuted operand rows (+ index metadata)
     hbm["permute_rows"] = (cfg.T * H * esz + R * H * op) / (ph["permute_rows"] * 1e-3) / 1e9
     zsz = 2 if cfg.x_dtype == "bf16" else 4
@@ -187,6 +190,10 @@ def fwd_leg(cfg, steps, warmup):
         nz = sum(1 for c in r["split_sizes"] if c > 0)
         hbm["quant_w1"] = nz * 2 * I * H * (2 + 1 + 1 / 32) / (ph["quant_w1"] * 1e-3) / 1e9
         hbm["quant_w2"] = nz * H * I * (2 + 1 + 1 / 32) / (ph["quant_w2"] * 1e-3) / 1e9
+    if cfg.precision == "fp8":
+        # two passes over every bf16 weight (amax, then quantize) and the codes written
+        hbm["quant_w1"] = E * 2 * I * H * (2 + 2 + 1) / (ph["quant_w1"] * 1e-3) / 1e9
+        hbm["quant_w2"] = E * H * I * (2 + 2 + 1) / (ph["quant_w2"] * 1e-3) / 1e9
     return r, {
         "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
         "tflops": round(cfg.fwd_flops() / (ms * 1e-3) / 1e12, 1),
@@ -351,8 +358,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,backward,router,loop",
-                    help="comma list of bf16, mxfp8, mxfp8_finegrained, backward, router, loop (bf16 always runs)")
+    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,fp8,backward,router,loop",
+                    help="comma list of bf16, mxfp8, mxfp8_finegrained, fp8, backward, router, loop "
+                         "(bf16 always runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -409,6 +417,16 @@ def main():
                               f"Zipf({c.zipf_s}) routing" + (f", expert {c.zero_expert} empty" if c.zero_expert is not None else "")
                               + ", weights quantized per call")
             line[key] = lg
+        if "fp8" in legs:
+            torch.cuda.empty_cache()
+            c = get_config(3).with_(precision="fp8")
+            rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2))
+            del rr
+            lg["workload"] = (f"{c.name} shape and routing: T={c.T} H={c.H} I={c.I} E={c.E} top-{c.k}, "
+                              f"per-tensor-scaled FP8 (E4M3, one fp32 scale per operand tensor) both GEMMs, "
+                              f"weights quantized per call; fc1_gateup_swiglu includes h's amax and quantize "
+                              f"passes, permute_rows those of X_perm")
+            line["fp8_tensor"] = lg
     if "loop" in legs:
         torch.cuda.empty_cache()
         line["loop_vs_grouped"] = {c.name: loop_leg(c) for c in (get_config(2), get_config(5))}

@@ -9,7 +9,8 @@
  *   a grouped down GEMM (I -> H),
  *   the top-k un-permute / combine,
  * in BF16 and in MXFP8 (E4M3 elements with one E8M0 scale per 32 consecutive
- * values along the GEMM's K), forward and backward.
+ * values along the GEMM's K), forward and backward, and a forward in
+ * per-tensor-scaled FP8 (E4M3 with one fp32 scale per operand tensor).
  *
  * Source of the method: page "BioNeMo Uses Grouped Kernels and MXFP8" --
  * Figure 1 (top-k router, outputs combined as a weighted sum), Grouping
@@ -58,7 +59,8 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,
   MOE_BF16 = 1,
-  MOE_MXFP8_E4M3 = 2        /* E4M3FN bytes + E8M0 scale bytes, one per 32 values */
+  MOE_MXFP8_E4M3 = 2,       /* E4M3FN bytes + E8M0 scale bytes, one per 32 values */
+  MOE_FP8_E4M3 = 3          /* E4M3FN bytes + one fp32 scale per tensor (forward only) */
 } moe_dtype;
 
 /* Largest supported expert count and experts per token. */
@@ -94,6 +96,33 @@ int moe_abi_version(void);
 moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, int axis,
                           const int32_t* group_offsets, int num_groups,
                           uint8_t* q, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fp8_tensor_quantize -- per-tensor-scaled FP8 (page "BioNeMo Uses Grouped
+ * Kernels and MXFP8", Reducing memory pressure with MXFP8: FP8 and MXFP8 use
+ * 8-bit values and differ in the granularity of their scaling; FP8 here has
+ * one scale per tensor), current scaling.
+ *
+ * x        [rows, cols] in x_dtype (MOE_F32 or MOE_BF16), device.
+ * Tensors: the row segments [group_offsets[g], group_offsets[g+1]) of x for
+ *          g < num_groups (device int32 [num_groups+1], an exclusive prefix,
+ *          last = rows; empty segments allowed), or, with group_offsets NULL
+ *          and num_groups == 1, all of x.
+ * Per tensor: amax = max |v|; s = 448 / amax as an fp32 division rounded to
+ *          nearest (s = 1 when amax == 0; the largest finite float when the
+ *          quotient overflows); code = E4M3FN(fp32(v * s)) rounded to nearest
+ *          even, saturated to +-448, the sign of a zero result kept.  The
+ *          value a code stands for is decode(code) / s.
+ * q        [rows, cols] code bytes; scales [num_groups] fp32 s (s = 1 for an
+ *          empty segment), device.
+ * workspace: fp8_tensor_quantize_workspace(num_groups) bytes of device
+ *          memory (amax partials), caller-owned.
+ * cols % 8 == 0, else MOE_ERR_UNSUPPORTED; 1 <= num_groups <= 256.
+ * ------------------------------------------------------------------------ */
+size_t fp8_tensor_quantize_workspace(int num_groups);
+moe_status fp8_tensor_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols,
+                               const int32_t* group_offsets, int num_groups, uint8_t* q, float* scales,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * moe_permute -- histogram, prefix sum and stable scatter of the (token,
@@ -165,10 +194,15 @@ moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x
  *
  * Shapes: x, out [T, H] io_dtype (MOE_F32 or MOE_BF16); w1[e] [2I, H] bf16
  * (rows [0, I) gate, [I, 2I) up); w2[e] [H, I] bf16.
- * compute: MOE_BF16 or MOE_MXFP8_E4M3 (both grouped GEMMs; weights are
- * quantized from the bf16 masters on every call).
+ * compute: MOE_BF16, MOE_MXFP8_E4M3 or MOE_FP8_E4M3 (both grouped GEMMs;
+ * weights are quantized from the bf16 masters on every call).  MOE_FP8_E4M3
+ * quantizes each GEMM operand tensor as fp8_tensor_quantize does: every W1_e
+ * and W2_e, and each expert's rows of X_perm (bf16) and of h (rounded to bf16
+ * first, since its scale needs the amax of the expert's whole h); it is
+ * forward only (saved_* must be NULL, else MOE_ERR_UNSUPPORTED), takes no
+ * cached weights, and is not offered by moe_grouped_mlp_fwd_loop.
  * Alignment: H % 64 == 0 and I % 64 == 0 (BF16); H % 128 == 0 and
- * I % 128 == 0 (MXFP8).  Any token counts per expert, including zero.
+ * I % 128 == 0 (MXFP8, FP8).  Any token counts per expert, including zero.
  * Permutation outputs are always written (caller buffers, device).
  * saved_*: optional (all NULL for inference, all set for training): bf16
  * copies kept for the backward -- x_perm [R, H], gu [R, 2I] (gate-up
@@ -214,7 +248,9 @@ moe_status moe_grouped_mlp_fwd(const moe_mlp_fwd_args* a, void* stream);
  * created hipEvent_t handles, moe_fwd_phase_count() + 1 of them) on `stream`
  * before phase i and after the last phase, without synchronizing, so a caller
  * can time each phase with hipEventElapsedTime.  Phases that do not apply to
- * the chosen precision are empty (their two events are adjacent).
+ * the chosen precision are empty (their two events are adjacent).  Under
+ * MOE_FP8_E4M3, permute_rows includes the quantization of X_perm and
+ * fc1_gateup_swiglu that of h.
  * events == NULL behaves exactly like moe_grouped_mlp_fwd. */
 moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void* const* events);
 int moe_fwd_phase_count(void);

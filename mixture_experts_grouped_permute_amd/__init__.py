@@ -1,15 +1,17 @@
 """MI355X-native grouped expert MLP (permute -> grouped GEMM -> ScaledSwiGLU*prob
--> grouped GEMM -> combine) in BF16 and MXFP8, behind the C ABI of libmoe.so.
+-> grouped GEMM -> combine) in BF16 and MXFP8 (forward and backward) and in
+per-tensor-scaled FP8 (forward), behind the C ABI of libmoe.so.
 
 The functions below are thin ctypes wrappers; all computation happens in the
 library's HIP kernels for gfx950.
 """
-from ._lib import (MOE_BF16, MOE_F32, MOE_MXFP8_E4M3, EXPORTS, MoeError, load, moe_grouped_mlp_bwd,
-                   moe_grouped_mlp_fwd, moe_grouped_mlp_fwd_loop, moe_permute, moe_read_device_error, moe_route_permute, moe_route_topk,
-                   mxfp8_quantize, quantize_weights, LIB_PATH)
+from ._lib import (MOE_BF16, MOE_F32, MOE_FP8_E4M3, MOE_MXFP8_E4M3, EXPORTS, MoeError, load, fp8_tensor_quantize,
+                   moe_grouped_mlp_bwd, moe_grouped_mlp_fwd, moe_grouped_mlp_fwd_loop, moe_permute,
+                   moe_read_device_error, moe_route_permute, moe_route_topk, mxfp8_quantize, quantize_weights,
+                   LIB_PATH)
 
 __all__ = [
-    "MOE_BF16", "MOE_F32", "MOE_MXFP8_E4M3", "EXPORTS", "MoeError", "load", "moe_grouped_mlp_bwd",
-    "moe_grouped_mlp_fwd", "moe_grouped_mlp_fwd_loop", "moe_permute", "moe_read_device_error", "moe_route_permute", "moe_route_topk",
-    "mxfp8_quantize", "quantize_weights", "LIB_PATH",
+    "MOE_BF16", "MOE_F32", "MOE_FP8_E4M3", "MOE_MXFP8_E4M3", "EXPORTS", "MoeError", "load",
+    "fp8_tensor_quantize", "moe_grouped_mlp_bwd", "moe_grouped_mlp_fwd", "moe_grouped_mlp_fwd_loop", "moe_permute",
+    "moe_read_device_error", "moe_route_permute", "moe_route_topk", "mxfp8_quantize", "quantize_weights", "LIB_PATH",
 ]

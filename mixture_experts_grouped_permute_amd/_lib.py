@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
-MOE_F32, MOE_BF16, MOE_MXFP8_E4M3 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP8_E4M3, MOE_FP8_E4M3 = 0, 1, 2, 3
 MAX_EXPERTS = 256
 
 # every symbol include/moe.h declares
@@ -27,7 +27,8 @@ EXPORTS = (
     "moe_grouped_mlp_fwd_workspace", "moe_grouped_mlp_fwd", "moe_grouped_mlp_bwd_workspace",
     "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
-    "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop",
+    "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop", "fp8_tensor_quantize_workspace",
+    "fp8_tensor_quantize",
 )
 
 
@@ -87,6 +88,11 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.mxfp8_quantize.restype = ctypes.c_int
     lib.mxfp8_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp]
+    lib.fp8_tensor_quantize_workspace.restype = ctypes.c_size_t
+    lib.fp8_tensor_quantize_workspace.argtypes = [ctypes.c_int]
+    lib.fp8_tensor_quantize.restype = ctypes.c_int
+    lib.fp8_tensor_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, ctypes.c_int, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]
     lib.moe_permute_workspace_size.restype = ctypes.c_size_t
     lib.moe_permute_workspace_size.argtypes = [_i64, ctypes.c_int, ctypes.c_int]
     lib.moe_permute.restype = ctypes.c_int
@@ -158,7 +164,7 @@ def _io(t: torch.Tensor) -> int:
 
 
 def _compute(c: str) -> int:
-    return {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3}[c]
+    return {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3, "fp8": MOE_FP8_E4M3}[c]
 
 
 def _table(ws: Sequence[torch.Tensor] | torch.Tensor):
@@ -210,6 +216,24 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 0, group_offsets: Optional[torch
         st = lib.mxfp8_quantize(_ptr(x), _io(x), rows, cols, 1, _ptr(group_offsets), G, _ptr(q), _ptr(s),
                                 _stream(dev))
     _check(st, "mxfp8_quantize")
+    return q, s
+
+
+def fp8_tensor_quantize(x: torch.Tensor, group_offsets: Optional[torch.Tensor] = None):
+    """Per-tensor-scaled E4M3 of x [rows, cols] (bf16 or f32): one fp32 scale per row segment of
+    group_offsets (int32 device [G+1]), or one for all of x.  Returns (codes uint8 [rows, cols],
+    scales float32 [G]); a code stands for decode(code) / scale."""
+    lib = load()
+    rows, cols = x.shape
+    dev = x.device
+    G = 1 if group_offsets is None else group_offsets.numel() - 1
+    q = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    s = torch.empty(G, dtype=torch.float32, device=dev)
+    need = lib.fp8_tensor_quantize_workspace(G)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    st = lib.fp8_tensor_quantize(_ptr(x), _io(x), rows, cols, _ptr(group_offsets), G, _ptr(q), _ptr(s),
+                                 _ptr(ws), ws.numel(), _stream(dev))
+    _check(st, "fp8_tensor_quantize")
     return q, s
 
 
@@ -333,8 +357,9 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
                         compute: str = "bf16", save_for_backward: bool = False, workspace: Optional[torch.Tensor] = None,
                         w_quant=None):
     """Grouped expert MLP forward.  w1: [E,2I,H] tensor or E tensors [2I,H] (bf16);
-    w2: [E,H,I] or E tensors [H,I].  w_quant: optional (w1q, w1s, w2q, w2s) from
-    quantize_weights (MXFP8 only): the per-call weight quantization is skipped.
+    w2: [E,H,I] or E tensors [H,I].  compute: "bf16", "mxfp8" or "fp8" (per-tensor scales,
+    forward only).  w_quant: optional (w1q, w1s, w2q, w2s) from quantize_weights (MXFP8
+    only): the per-call weight quantization is skipped.
     Returns (out, ctx) where ctx holds the permutation and, with save_for_backward,
     the bf16 activations."""
     lib = load()

@@ -73,6 +73,13 @@ struct FwdPlan {
   void* z;             // [R,H] io dtype
   float* part;         // FC2 split-tile partials
   uint8_t* w1q; uint8_t* w1s; uint8_t* w2q; uint8_t* w2s;
+  // per-tensor FP8: bf16 X_perm and h ahead of their quantization, per-expert scales s and 1 / s
+  // (X_perm rows, W1, h rows, W2), amax partials, and the 0x7F block scales the GEMMs read
+  void* x_bf; void* h_bf;
+  float *sx, *ix, *sw1, *iw1, *sh, *ih, *sw2, *iw2;
+  float* pt_part;
+  uint8_t* unit;
+  int64_t unit_bytes;
   size_t bytes;
 };
 
@@ -83,7 +90,23 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
   const int E = a->E;
   const bool mx = a->compute == MOE_MXFP8_E4M3;
   p.perm = carve_perm(c, a->T, E);
-  if (mx) {
+  if (a->compute == MOE_FP8_E4M3) {
+    auto f = [&](size_t n) { return reinterpret_cast<float*>(c.take(n * sizeof(float))); };
+    p.x_bf = c.take((size_t)(R * H * 2));
+    p.x_op = c.take((size_t)(R * H));
+    p.h_bf = c.take((size_t)(R * I * 2));
+    p.h_op = c.take((size_t)(R * I));
+    p.w1q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H)));
+    p.w2q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I)));
+    p.sx = f(E); p.ix = f(E); p.sw1 = f(E); p.iw1 = f(E);
+    p.sh = f(E); p.ih = f(E); p.sw2 = f(E); p.iw2 = f(E);
+    p.pt_part = f(pt_part_floats(E));
+    // unit block scales: the FC1 GEMM reads rows [0, max(R, 2I)) of H/32 bytes, FC2 rows
+    // [0, max(R, H)) of I/32 bytes (the weight scales with expert stride 0)
+    const int64_t u1 = (R > 2 * I ? R : 2 * I) * (H / 32), u2 = (R > H ? R : H) * (I / 32);
+    p.unit_bytes = ((u1 > u2 ? u1 : u2) + 3) / 4 * 4;
+    p.unit = reinterpret_cast<uint8_t*>(c.take((size_t)p.unit_bytes));
+  } else if (mx) {
     p.x_op = c.take((size_t)(R * H));
     p.x_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * H / 32)));
     p.h_op = c.take((size_t)(R * I));
@@ -117,7 +140,8 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   if (s != MOE_OK) return s;
   if (a->I <= 0) return MOE_ERR_INVALID_ARG;
   if (!io_ok(a->io_dtype)) return MOE_ERR_INVALID_ARG;
-  if (a->compute != MOE_BF16 && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
+  if (a->compute != MOE_BF16 && a->compute != MOE_MXFP8_E4M3 && a->compute != MOE_FP8_E4M3)
+    return MOE_ERR_INVALID_ARG;
   const int64_t align = a->compute == MOE_BF16 ? 64 : 128;
   if (a->H % align || a->I % align) return MOE_ERR_UNSUPPORTED;
   if (!a->x || !a->topk_idx || !a->topk_prob || !a->out) return MOE_ERR_INVALID_ARG;
@@ -133,6 +157,7 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   const bool any_saved = a->saved_x_perm || a->saved_gu || a->saved_h;
   const bool all_saved = a->saved_x_perm && a->saved_gu && a->saved_h;
   if (any_saved && !all_saved) return MOE_ERR_INVALID_ARG;
+  if (any_saved && a->compute == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;   // forward only
   // 32-bit buffer ranges inside the GEMMs
   const int64_t R = a->T * a->k;
   const int64_t widest = a->H > 2 * a->I ? a->H : 2 * a->I;
@@ -186,6 +211,7 @@ moe_status validate_bwd(const moe_mlp_bwd_args* a) {
   if (s != MOE_OK) return s;
   if (a->I <= 0) return MOE_ERR_INVALID_ARG;
   if (!io_ok(a->io_dtype) || !io_ok(a->dw_dtype)) return MOE_ERR_INVALID_ARG;
+  if (a->compute == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;   // the per-tensor FP8 variant is forward only
   if (a->compute != MOE_BF16 && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
   const int64_t align = a->compute == MOE_BF16 ? 64 : 128;
   if (a->H % align || a->I % align) return MOE_ERR_UNSUPPORTED;
@@ -201,6 +227,69 @@ moe_status validate_bwd(const moe_mlp_bwd_args* a) {
     const int64_t Rp = (R + 127) / 128 * 128 + 128 * (int64_t)a->E;
     if (widest * Rp >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   }
+  return MOE_OK;
+}
+
+// Per-tensor FP8 forward after the index pass: X_perm (bf16, then quantized per expert
+// segment), the weights (per expert tensor), FC1 on unit-scaled codes writing bf16 h, h
+// quantized per expert segment, FC2, combine.  Every tensor's scale comes from its own amax.
+template <typename Mark>
+moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t st, Mark& mark) {
+  const int64_t T = a->T, H = a->H, I = a->I, R = T * a->k;
+  const int E = a->E, k = a->k;
+  const bool x_f32 = a->io_dtype == MOE_F32;
+  HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_bf, nullptr, false, st));
+  HIP_TRY(launch_pt_quant(p.x_bf, false, R, H, a->offsets, E, reinterpret_cast<uint8_t*>(p.x_op), p.sx, p.ix,
+                          p.pt_part, st));
+  MOE_CHECK(mark(2), MOE_ERR_HIP);
+  HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(p.unit), p.unit_bytes / 4, 0x7F7F7F7Fu, st));
+  HIP_TRY(launch_pt_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.sw1, p.iw1, p.pt_part, st));
+  MOE_CHECK(mark(3), MOE_ERR_HIP);
+  HIP_TRY(launch_pt_quant_weights(a->w2, E, H, I, p.w2q, p.sw2, p.iw2, p.pt_part, st));
+  MOE_CHECK(mark(4), MOE_ERR_HIP);
+
+  FwdGemm g1{};
+  g1.a = p.x_op;
+  g1.a_scales = p.unit;
+  g1.wq = p.w1q;
+  g1.wq_stride = 2 * I * H;
+  g1.ws = p.unit;
+  g1.ws_stride = 0;
+  g1.K = H;
+  g1.N = I;
+  g1.E = E;
+  g1.split_sizes = a->split_sizes;
+  g1.prob_perm = a->prob_perm;
+  g1.out = p.h_bf;
+  g1.save_h = reinterpret_cast<uint16_t*>(p.h_bf);
+  g1.pt_inv_a = p.ix;
+  g1.pt_inv_b = p.iw1;
+  HIP_TRY(launch_fc1(g1, true, st));
+  HIP_TRY(launch_pt_quant(p.h_bf, false, R, I, a->offsets, E, reinterpret_cast<uint8_t*>(p.h_op), p.sh, p.ih,
+                          p.pt_part, st));
+  MOE_CHECK(mark(5), MOE_ERR_HIP);
+
+  FwdGemm g2{};
+  g2.a = p.h_op;
+  g2.a_scales = p.unit;
+  g2.wq = p.w2q;
+  g2.wq_stride = H * I;
+  g2.ws = p.unit;
+  g2.ws_stride = 0;
+  g2.K = I;
+  g2.N = H;
+  g2.E = E;
+  g2.split_sizes = a->split_sizes;
+  g2.out = p.z;
+  g2.part = p.part;
+  g2.out_f32 = x_f32;
+  g2.pt_inv_a = p.ih;
+  g2.pt_inv_b = p.iw2;
+  HIP_TRY(launch_fc2(g2, true, st));
+  MOE_CHECK(mark(6), MOE_ERR_HIP);
+
+  HIP_TRY(launch_combine(p.z, x_f32, T, H, k, a->row_id_map, a->out, x_f32, st));
+  MOE_CHECK(mark(7), MOE_ERR_HIP);
   return MOE_OK;
 }
 
@@ -241,6 +330,26 @@ moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols
     return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;
+}
+
+size_t fp8_tensor_quantize_workspace(int num_groups) {
+  if (num_groups < 1 || num_groups > MOE_MAX_EXPERTS) return 0;
+  return align_up(pt_part_floats(num_groups) * sizeof(float));
+}
+
+moe_status fp8_tensor_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols, const int32_t* group_offsets,
+                               int num_groups, uint8_t* q, float* scales, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  MOE_CHECK(x && q && scales, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(rows > 0 && cols > 0 && io_ok(x_dtype), MOE_ERR_INVALID_ARG);
+  MOE_CHECK(num_groups >= 1 && num_groups <= MOE_MAX_EXPERTS, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(group_offsets || num_groups == 1, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(cols % 8 == 0, MOE_ERR_UNSUPPORTED);
+  const size_t need = fp8_tensor_quantize_workspace(num_groups);
+  MOE_CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE);
+  HIP_TRY(launch_pt_quant(x, x_dtype == MOE_F32, rows, cols, group_offsets, num_groups, q, scales, nullptr,
+                          reinterpret_cast<float*>(workspace), reinterpret_cast<hipStream_t>(stream)));
+  return MOE_OK;
 }
 
 size_t moe_permute_workspace_size(int64_t T, int k, int E) {
@@ -353,6 +462,7 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
                                  a->src_index, a->prob_perm, p.perm.err, p.perm.block_counts, p.perm.block_base,
                                  st));
   MOE_CHECK(mark(1), MOE_ERR_HIP);
+  if (a->compute == MOE_FP8_E4M3) return fwd_fp8_tail(a, p, st, mark);
   if (mx) {
     HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, p.x_sc, true, st));
     if (a->saved_x_perm)
@@ -415,6 +525,7 @@ moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* sp
   moe_status s = validate_fwd(a);
   if (s != MOE_OK) return s;
   MOE_CHECK(split_sizes_host != nullptr, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(a->compute != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
   int64_t sum = 0;
   for (int e = 0; e < a->E; ++e) {
     MOE_CHECK(split_sizes_host[e] >= 0, MOE_ERR_INVALID_ARG);

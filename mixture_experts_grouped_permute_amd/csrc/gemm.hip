@@ -55,6 +55,8 @@ struct FwdKArgs {
   int out_f32;
   float* part;               // split tiles' fp32 partial accumulators, kGemmGrid x 64K floats
   int split;                 // 0: every tile; 1: tiles before the split ones; 2: the split parts
+  const float* pt_inv_a;     // per-tensor FP8: per expert 1 / s of the A rows and of the weight
+  const float* pt_inv_b;
   const uint8_t* w[kMaxExperts];
 };
 
@@ -358,6 +360,10 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const rsrc_t rsc = make_rsrc(kMx ? p.out_scales + r0 * (I / 32) : p.out, kMx ? mr * (I32 / 32) : 0);
       const rsrc_t rh = make_rsrc(p.save_h ? p.save_h + r0 * I : nullptr, p.save_h ? mr * I32 * 2 : 0);
       const rsrc_t rg = make_rsrc(p.save_gu ? p.save_gu + r0 * 2 * I : nullptr, p.save_gu ? mr * I32 * 4 : 0);
+      // per-tensor FP8: the products of unit-scaled codes times 1 / (s_a s_b) of the tile's
+      // expert, and h leaves as bf16 (its scale needs the amax of the expert's whole h)
+      const bool pt = kMx && p.pt_inv_a != nullptr;
+      const float dq = pt ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wm * 128 + i * 32 + r32;
@@ -369,6 +375,10 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           float g[16], u[16];
           agpr_read16(core.acc[i][jj], g);
           agpr_read16(core.acc[i][jj + 2], u);
+          if constexpr (kMx) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) { g[r] *= dq; u[r] *= dq; }
+          }
           // stores go out in the lane-paired layout (pack_bf16_runs8 / swap_runs8): the lane's 8
           // consecutive columns 16 pp + 8 hh + [0, 8) of the block
           const uint32_t e8 = (uint32_t)m * I32 + col + 2u * (uint32_t)ch;                  // element of h
@@ -386,14 +396,14 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = (silu_f(g[r]) * u[r]) * pr;
-          if (!kMx || p.save_h) {
+          if (!kMx || pt || p.save_h) {
             u32x4 oh[2];
             pack_bf16_runs8(v, oh);
 #pragma unroll
             for (int pp = 0; pp < 2; ++pp)
               __builtin_amdgcn_raw_buffer_store_b128(oh[pp], kMx ? rh : ro, (e8 + 16u * pp) * 2u, 0, 0);
           }
-          if constexpr (kMx) {
+          if (kMx && !pt) {
             // the 32-column block of this row is split between lanes l and l ^ 32
             float am = 0.f;
 #pragma unroll
@@ -430,6 +440,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       }
       // first column of the tile in the destination (0 for a part slot)
       const uint32_t c0 = (kOutF32 && cur.part >= 0) ? 0u : (uint32_t)cur.nt * kBN;
+      const float dq = (kMx && p.pt_inv_a != nullptr) ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wm * 128 + i * 32 + r32;
@@ -439,6 +450,10 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           if ((uint32_t)cur.nt * kBN + tc >= N32) continue;            // wave-uniform
           float a[16];
           agpr_read16(core.acc[i][j], a);
+          if constexpr (kMx) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) a[r] *= dq;
+          }
           const uint32_t e0 = (uint32_t)m * ld + c0 + tc + (uint32_t)ch;
           if constexpr (kOutF32) {
             // fp32 runs already give 32 contiguous bytes per row (lanes l and l ^ 32)
@@ -534,6 +549,8 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
   k.save_gu = g.save_gu;
   k.save_h = g.save_h;
   k.out_f32 = g.out_f32 ? 1 : 0;
+  k.pt_inv_a = g.pt_inv_a;
+  k.pt_inv_b = g.pt_inv_b;
   if (!mx)
     for (int e = 0; e < g.E; ++e) k.w[e] = reinterpret_cast<const uint8_t*>(g.w_tab[e]);
   return k;

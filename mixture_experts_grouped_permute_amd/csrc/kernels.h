@@ -42,6 +42,19 @@ hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t
                                 const int32_t* group_offsets, int num_groups, int64_t rows_pad, uint8_t* q,
                                 uint8_t* scales, hipStream_t st, int seg_align = 32);
 
+// Per-tensor FP8 (one fp32 scale per tensor): the row segments [offsets[g], offsets[g+1]) of x
+// [rows, cols] (offsets == nullptr: one segment of all rows), or each of E bf16 weight matrices
+// [rows, cols] of a host pointer table (codes stacked [E, rows, cols]).  scales[g] = s,
+// inv[g] = 1 / s (inv may be nullptr); part: pt_part_floats(G) floats of amax partials.
+// cols % 8 == 0.
+int pt_blocks(int G);
+size_t pt_part_floats(int G);
+hipError_t launch_pt_quant(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* offsets, int G,
+                           uint8_t* q, float* scales, float* inv, float* part, hipStream_t st);
+hipError_t launch_pt_quant_weights(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
+                                   float* scales, float* inv, float* part, hipStream_t st);
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
+
 // ---- combine / gather (combine.hip)
 hipError_t launch_combine(const void* z, bool z_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
                           void* out, bool out_f32, hipStream_t st);
@@ -72,6 +85,11 @@ struct FwdGemm {
   uint16_t* save_h;                  // FC1 MXFP8 training: [R, I] bf16 h
   bool out_f32;                      // FC2
   float* part;                       // FC2: kGemmGrid x 65536 fp32 for split tiles (nullptr: no split)
+  // per-tensor FP8 (MXFP8 instance with every block scale 1, i.e. a_scales / ws point at 0x7F
+  // bytes and ws_stride = 0): per expert 1 / s of its A rows and of its weight; the products are
+  // multiplied by both, and FC1 writes bf16 h to save_h instead of E4M3 codes.  nullptr: MXFP8.
+  const float* pt_inv_a;
+  const float* pt_inv_b;
 };
 // Workspace of the FC2 split-tile partials (bytes).
 constexpr size_t kFc2PartBytes = (size_t)kGemmGrid * 65536 * sizeof(float);

@@ -190,6 +190,115 @@ __global__ __launch_bounds__(64) void mx_cols_kernel(const void* __restrict__ x,
   scales[c * (rows_pad / 32) + pblk / 32] = (uint8_t)(s + 127);
 }
 
+// ---------------------------------------------------------------------------
+// Per-tensor-scaled FP8 (FP8 beside MXFP8 on page "BioNeMo Uses Grouped Kernels
+// and MXFP8", Reducing memory pressure with MXFP8: the same E4M3 elements with a
+// coarser scale -- here one fp32 scale per tensor).  A tensor is a row segment
+// [offsets[g], offsets[g+1]) of a contiguous [rows, cols] matrix, or one matrix
+// of a weight table.  Two passes: amax partials over each tensor (grid nb x G,
+// part[g * nb + b]), then each block reduces its tensor's nb partials, forms
+//   s = 448 / amax (fp32 division, correctly rounded; 1 for amax == 0; the
+//       largest finite float if the quotient overflows)
+// and stores E4M3FN(fp32(v * s)): the product clamped to +-448 (the saturation
+// rule) and rounded by v_cvt_pk_fp8_f32 (nearest, ties to even, zero keeps its
+// sign).  Max is order-free, so the result does not depend on the grid.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float pt_scale(float amax) {
+  if (!(amax > 0.f)) return 1.f;
+  const float s = 448.0f / amax;
+  return s > 3.402823466e38f ? 3.402823466e38f : s;
+}
+
+// the tensor of block row g: its first element and element count
+template <bool kTab>
+__device__ __forceinline__ void pt_range(const WTab& tab, const void* x, bool f32, const int32_t* offsets,
+                                         int64_t rows, int64_t cols, int g, const void*& base, int64_t& first,
+                                         int64_t& n) {
+  if constexpr (kTab) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint16_t* const* t = reinterpret_cast<const uint16_t* const*>(
+        reinterpret_cast<const char*>(__builtin_amdgcn_kernarg_segment_ptr()));
+    base = t[g];
+#else
+    base = tab.w[g];
+#endif
+    first = 0;
+    n = rows * cols;
+  } else {
+    (void)tab;
+    (void)f32;
+    const int64_t lo = offsets ? offsets[g] : 0, hi = offsets ? offsets[g + 1] : rows;
+    base = x;
+    first = lo * cols;
+    n = (hi - lo) * cols;
+  }
+}
+
+__device__ __forceinline__ float block_max(float v, float* red) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = wave_xor_max(v, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  v = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  return v;
+}
+
+template <bool kF32, bool kTab>
+__global__ __launch_bounds__(256) void pt_amax_kernel(const WTab tab, const void* x, const int32_t* offsets,
+                                                       int64_t rows, int64_t cols, float* part) {
+  __shared__ float red[4];
+  const int g = blockIdx.y, nb = gridDim.x;
+  const void* base;
+  int64_t first, n;
+  pt_range<kTab>(tab, x, kF32, offsets, rows, cols, g, base, first, n);
+  float am = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n / 8; i += (int64_t)nb * 256) {
+    float v[8];
+    load8(base, kF32, first + i * 8, v);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(v[c]));
+  }
+  am = block_max(am, red);
+  if (threadIdx.x == 0) part[g * nb + blockIdx.x] = am;
+}
+
+template <bool kF32, bool kTab>
+__global__ __launch_bounds__(256) void pt_quant_kernel(const WTab tab, const void* x, const int32_t* offsets,
+                                                        int64_t rows, int64_t cols, const float* part,
+                                                        uint8_t* __restrict__ q, float* scales, float* inv) {
+  __shared__ float red[4];
+  const int g = blockIdx.y, nb = gridDim.x;
+  const void* base;
+  int64_t first, n;
+  pt_range<kTab>(tab, x, kF32, offsets, rows, cols, g, base, first, n);
+  float am = 0.f;
+  for (int i = threadIdx.x; i < nb; i += 256) am = fmaxf(am, part[g * nb + i]);
+  am = block_max(am, red);
+  const float s = pt_scale(am);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    scales[g] = s;
+    if (inv) inv[g] = 1.0f / s;
+  }
+  uint8_t* qg = q + (kTab ? (int64_t)g * n : first);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n / 8; i += (int64_t)nb * 256) {
+    float v[8];
+    load8(base, kF32, first + i * 8, v);
+    auto c = [s](float a) { return __builtin_amdgcn_fmed3f(a * s, -448.0f, 448.0f); };
+    u32x2 o;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(c(v[0]), c(v[1]), 0, false);
+    o[0] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c(v[2]), c(v[3]), w, true);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c(v[4]), c(v[5]), 0, false);
+    o[1] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c(v[6]), c(v[7]), w, true);
+    *reinterpret_cast<u32x2*>(qg + i * 8) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = v;
+}
+
 int grid_for(int64_t groups) {
   int64_t b = (groups + 255) / 256;
   return (int)(b < 1 ? 1 : (b > 8192 ? 8192 : b));
@@ -229,6 +338,44 @@ hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t
   else
     mx_cols_kernel<false><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
                                                seg_align);
+  return hipGetLastError();
+}
+
+int pt_blocks(int G) {
+  const int nb = 2048 / (G < 1 ? 1 : G);
+  return nb < 1 ? 1 : (nb > 256 ? 256 : nb);
+}
+
+size_t pt_part_floats(int G) { return (size_t)G * (size_t)pt_blocks(G); }
+
+hipError_t launch_pt_quant(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* offsets, int G,
+                           uint8_t* q, float* scales, float* inv, float* part, hipStream_t st) {
+  if (G <= 0) return hipSuccess;
+  const dim3 grid((unsigned)pt_blocks(G), (unsigned)G);
+  WTab tab{};
+  if (x_f32) {
+    pt_amax_kernel<true, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part);
+    pt_quant_kernel<true, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part, q, scales, inv);
+  } else {
+    pt_amax_kernel<false, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part);
+    pt_quant_kernel<false, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part, q, scales, inv);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pt_quant_weights(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
+                                   float* scales, float* inv, float* part, hipStream_t st) {
+  WTab tab{};
+  for (int e = 0; e < E; ++e) tab.w[e] = reinterpret_cast<const uint16_t*>(w[e]);
+  const dim3 grid((unsigned)pt_blocks(E), (unsigned)E);
+  pt_amax_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, nullptr, rows, cols, part);
+  pt_quant_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, nullptr, rows, cols, part, q, scales, inv);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill_u32_kernel<<<grid_for(n), 256, 0, st>>>(p, n, v);
   return hipGetLastError();
 }
 

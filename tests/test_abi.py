@@ -21,7 +21,7 @@ def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", src, flags=re.M)
-    return sorted(set(n for n in names if n.startswith(("moe_", "mxfp8_"))))
+    return sorted(set(n for n in names if n.startswith(("moe_", "mxfp8_", "fp8_"))))
 
 
 @pytest.fixture(scope="module")
@@ -145,3 +145,36 @@ def test_fwd_cached_weight_validation(lib):
     c, tc = _fwd_args(compute=2)           # all four or none
     c.w1q = 0x2000
     assert lib.moe_grouped_mlp_fwd(ctypes.byref(c), None) == MOE_ERR_INVALID_ARG
+
+
+def test_fp8_forward_and_quantizer_validation(lib):
+    from mixture_experts_grouped_permute_amd._lib import (MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED,
+                                                          MOE_ERR_WORKSPACE, MOE_FP8_E4M3)
+    lib.moe_grouped_mlp_fwd_workspace.restype = ctypes.c_size_t
+    a, tab = _fwd_args(compute=2)
+    mx = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    b, tb = _fwd_args(compute=MOE_FP8_E4M3)
+    f8 = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(b))
+    # FP8 holds the bf16 X_perm and h ahead of their quantization, but no E8M0 scales
+    assert f8 > 0 and f8 > mx - 8 * 3 * 4096 * 14336 // 32
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(b), None) == MOE_ERR_WORKSPACE
+    c, tc = _fwd_args(compute=MOE_FP8_E4M3, H=4096 + 64)          # not a multiple of 128
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(c), None) == MOE_ERR_UNSUPPORTED
+    d, td = _fwd_args(compute=MOE_FP8_E4M3)                       # forward only
+    d.saved_x_perm = d.saved_gu = d.saved_h = 0x3000
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(d), None) == MOE_ERR_UNSUPPORTED
+    e, te = _fwd_args(compute=MOE_FP8_E4M3)                       # cached weights are MXFP8 only
+    e.w1q = e.w1s = e.w2q = e.w2s = 0x2000
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(e), None) == MOE_ERR_INVALID_ARG
+    lib.fp8_tensor_quantize_workspace.restype = ctypes.c_size_t
+    lib.fp8_tensor_quantize_workspace.argtypes = [ctypes.c_int]
+    assert lib.fp8_tensor_quantize_workspace(8) >= 8 * 4 and lib.fp8_tensor_quantize_workspace(0) == 0
+    q = lib.fp8_tensor_quantize
+    q.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    p = 0x1000
+    assert q(None, 1, 64, 64, None, 1, p, p, p, 1 << 20, None) == MOE_ERR_INVALID_ARG
+    assert q(p, 1, 64, 60, None, 1, p, p, p, 1 << 20, None) == MOE_ERR_UNSUPPORTED   # cols % 8 != 0
+    assert q(p, 1, 64, 64, None, 2, p, p, p, 1 << 20, None) == MOE_ERR_INVALID_ARG   # 2 groups, no offsets
+    assert q(p, 2, 64, 64, None, 1, p, p, p, 1 << 20, None) == MOE_ERR_INVALID_ARG   # input already E4M3
+    assert q(p, 1, 64, 64, None, 1, p, p, p, 4, None) == MOE_ERR_WORKSPACE
