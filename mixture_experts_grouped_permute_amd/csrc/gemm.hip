@@ -81,7 +81,10 @@ struct FwdItem {
 // kDeep (K of at least two stages; MXFP8 also needs K % 512 == 0, so 16-byte scale rows): the stage
 // barrier sits inside the stage and stage loads are issued two stages ahead (mma_stage_mx_deep,
 // mma_stage_bf16_deep).
-template <bool kMx, bool kFc1, bool kOutF32, bool kDeep>
+// kPt (with kMx): per-tensor-scaled FP8 -- unit block scales, the per-expert dequantization in
+// the epilogue, and FC1's h written as bf16 (a separate instance, so the MXFP8 epilogue keeps
+// its own code)
+template <bool kMx, bool kFc1, bool kOutF32, bool kDeep, bool kPt = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
   // 2 pipeline stages, then the MXFP8 scales of groups of 4 stages (2 x 8 KB), then the routing
@@ -362,7 +365,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const rsrc_t rg = make_rsrc(p.save_gu ? p.save_gu + r0 * 2 * I : nullptr, p.save_gu ? mr * I32 * 4 : 0);
       // per-tensor FP8: the products of unit-scaled codes times 1 / (s_a s_b) of the tile's
       // expert, and h leaves as bf16 (its scale needs the amax of the expert's whole h)
-      const bool pt = kMx && p.pt_inv_a != nullptr;
+      constexpr bool pt = kMx && kPt;
       const float dq = pt ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -375,7 +378,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           float g[16], u[16];
           agpr_read16(core.acc[i][jj], g);
           agpr_read16(core.acc[i][jj + 2], u);
-          if constexpr (kMx) {
+          if constexpr (pt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) { g[r] *= dq; u[r] *= dq; }
           }
@@ -403,7 +406,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
             for (int pp = 0; pp < 2; ++pp)
               __builtin_amdgcn_raw_buffer_store_b128(oh[pp], kMx ? rh : ro, (e8 + 16u * pp) * 2u, 0, 0);
           }
-          if (kMx && !pt) {
+          if constexpr (kMx && !pt) {
             // the 32-column block of this row is split between lanes l and l ^ 32
             float am = 0.f;
 #pragma unroll
@@ -440,7 +443,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       }
       // first column of the tile in the destination (0 for a part slot)
       const uint32_t c0 = (kOutF32 && cur.part >= 0) ? 0u : (uint32_t)cur.nt * kBN;
-      const float dq = (kMx && p.pt_inv_a != nullptr) ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
+      const float dq = (kMx && kPt) ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wm * 128 + i * 32 + r32;
@@ -450,7 +453,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           if ((uint32_t)cur.nt * kBN + tc >= N32) continue;            // wave-uniform
           float a[16];
           agpr_read16(core.acc[i][j], a);
-          if constexpr (kMx) {
+          if constexpr (kMx && kPt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) a[r] *= dq;
           }
@@ -560,7 +563,10 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
 
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
   FwdKArgs k = make_fwd_args(g, mx, true);
-  if (mx && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  const bool pt = mx && g.pt_inv_a != nullptr;
+  if (pt && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (pt) fwd_gemm_kernel<true, true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (mx && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (mx) fwd_gemm_kernel<true, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
   else if (g.K >= 128) fwd_gemm_kernel<false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else fwd_gemm_kernel<false, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
@@ -578,7 +584,13 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   // K of at least two 128-byte stages (and 16-byte scale rows for MXFP8) takes the deep pipeline
   // (split parts have at least kMinSplitUnits stages)
   const bool deep = mx ? (g.K >= 256 && g.K % 512 == 0) : g.K >= 128;
-  if (g.out_f32) {
+  const bool pt = mx && g.pt_inv_a != nullptr;
+  if (pt) {
+    if (g.out_f32 && deep) fwd_gemm_kernel<true, false, true, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+    else if (g.out_f32) fwd_gemm_kernel<true, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+    else if (deep) fwd_gemm_kernel<true, false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+    else fwd_gemm_kernel<true, false, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  } else if (g.out_f32) {
     if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
     else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
     else if (deep) fwd_gemm_kernel<false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
@@ -593,7 +605,9 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   if (err != hipSuccess || !split) return err;
   // pass 2: the split parts (whether there are any is decided on the device), then the fixup
   k.split = 2;
-  if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+  if (pt && deep) fwd_gemm_kernel<true, false, true, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (pt) fwd_gemm_kernel<true, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
   else if (deep) fwd_gemm_kernel<false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
   else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
