@@ -30,10 +30,14 @@ def _covered(idx, experts):
 @pytest.mark.timeout(900)
 # The last expert's down-projection tiles fill the GEMM's last, partly occupied round, where
 # they are split along K and finished by the fixup pass: each subset includes that expert.
-@pytest.mark.parametrize("ci,experts", [(2, (0, 7)), (3, (4, 5, 6, 7))], ids=["mixtral-bf16", "mixtral-mxfp8-zipf"])
-def test_fullsize_forward(ci, experts):
+# The per-tensor FP8 case runs the MXFP8 workload's inputs with one scale per operand tensor.
+@pytest.mark.parametrize("ci,experts,prec", [(2, (0, 7), None), (3, (4, 5, 6, 7), None), (3, (4, 5, 6, 7), "fp8")],
+                         ids=["mixtral-bf16", "mixtral-mxfp8-zipf", "mixtral-fp8-tensor-zipf"])
+def test_fullsize_forward(ci, experts, prec):
     m = need_gpu()
     cfg = get_config(ci)
+    if prec is not None:
+        cfg = cfg.with_(precision=prec)
     log(f"full-size fwd {cfg.name}: generating inputs")
     inp = make_inputs(cfg)
     d = inp.to("cuda")
@@ -51,7 +55,7 @@ def test_fullsize_forward(ci, experts):
     assert rows.sum() >= 16, rows.sum()
     err = mlp.normwise_rel_err(to_np(out)[rows], fw.out[rows])
     tol = BF16_TOL if cfg.precision == "bf16" else MXFP8_TOL
-    log(f"  {rows.sum()} tokens compared, normwise err {err:.3e} (tol {tol})")
+    log(f"  {cfg.precision}: {rows.sum()} tokens compared, normwise err {err:.3e} (tol {tol})")
     assert err < tol
 
 
@@ -99,6 +103,27 @@ def test_fullsize_mxfp8_bytes():
     rc, rs = nm.quantize_mxfp8(inp.w1[e].to(torch.float64).numpy(), axis=1)
     np.testing.assert_array_equal(q1.cpu().numpy(), rc)
     np.testing.assert_array_equal(s1.cpu().numpy(), rs)
+
+
+@gpu
+@slow
+@pytest.mark.timeout(900)
+def test_fullsize_fp8_tensor_bytes():
+    """The per-tensor FP8 quantizer over the bf16 permuted rows of the MXFP8 workload, one
+    tensor per expert segment (the empty expert included): codes and scales byte for byte."""
+    m = need_gpu()
+    cfg = get_config(3)
+    log("full-size per-tensor FP8 bytes: generating inputs")
+    inp = make_inputs(cfg)
+    d = inp.to("cuda")
+    res = m.moe_permute(d.x, d.topk_idx, d.topk_prob, cfg.E, "bf16")
+    q, s = m.fp8_tensor_quantize(res["x_perm"], res["offsets"])
+    torch.cuda.synchronize()
+    ref = oracle_permute(inp.topk_idx.numpy(), cfg.E)
+    xp = inp.x.to(torch.float64).numpy()[ref.token_of_row]
+    rc, rs = nm.quantize_fp8_segments(xp, ref.offsets)
+    np.testing.assert_array_equal(s.cpu().numpy(), rs)
+    np.testing.assert_array_equal(q.cpu().numpy(), rc)
 
 
 @gpu
