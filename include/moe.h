@@ -88,7 +88,9 @@ int moe_abi_version(void);
  *          prefix sum of the padded segment sizes and rows_pad =
  *          ceil(rows/32)*32 + 32*num_groups (an upper bound; the caller
  *          allocates it).
- *          Padding codes are 0x00.  cols % 32 == 0.
+ *          Padding codes are 0x00.  cols % 32 == 0.  Offsets outside [0, rows]
+ *          or decreasing are clamped on the device (the result is then not
+ *          meaningful, but no access leaves the buffers described here).
  * Element rule: s = floor(log2(amax)) - 8 clamped to [-127, 127] (amax = 0
  * gives s = -127), scale byte = s + 127, code = E4M3FN(v / 2^s) rounded to
  * nearest even and saturated to +-448; the sign of a zero result is kept.
@@ -107,7 +109,8 @@ moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols
  * Tensors: the row segments [group_offsets[g], group_offsets[g+1]) of x for
  *          g < num_groups (device int32 [num_groups+1], an exclusive prefix,
  *          last = rows; empty segments allowed), or, with group_offsets NULL
- *          and num_groups == 1, all of x.
+ *          and num_groups == 1, all of x.  Offsets outside [0, rows] or
+ *          decreasing are clamped on the device (no access leaves the buffers).
  * Per tensor: amax = max |v|; s = 448 / amax as an fp32 division rounded to
  *          nearest (s = 1 when amax == 0; the largest finite float when the
  *          quotient overflows); code = E4M3FN(fp32(v * s)) rounded to nearest

@@ -78,6 +78,7 @@ struct FwdPlan {
   void* x_bf; void* h_bf;
   float *sx, *ix, *sw1, *iw1, *sh, *ih, *sw2, *iw2;
   float* pt_part;
+  uint32_t* h_amax;    // per expert max |bf16 h| (float bits), raised by FC1's epilogue
   uint8_t* unit;
   int64_t unit_bytes;
   size_t bytes;
@@ -101,6 +102,7 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
     p.sx = f(E); p.ix = f(E); p.sw1 = f(E); p.iw1 = f(E);
     p.sh = f(E); p.ih = f(E); p.sw2 = f(E); p.iw2 = f(E);
     p.pt_part = f(pt_part_floats(E));
+    p.h_amax = reinterpret_cast<uint32_t*>(c.take((size_t)E * sizeof(uint32_t)));
     // unit block scales: the FC1 GEMM reads rows [0, max(R, 2I)) of H/32 bytes, FC2 rows
     // [0, max(R, H)) of I/32 bytes (the weight scales with expert stride 0)
     const int64_t u1 = (R > 2 * I ? R : 2 * I) * (H / 32), u2 = (R > H ? R : H) * (I / 32);
@@ -231,8 +233,9 @@ moe_status validate_bwd(const moe_mlp_bwd_args* a) {
 }
 
 // Per-tensor FP8 forward after the index pass: X_perm (bf16, then quantized per expert
-// segment), the weights (per expert tensor), FC1 on unit-scaled codes writing bf16 h, h
-// quantized per expert segment, FC2, combine.  Every tensor's scale comes from its own amax.
+// segment), the weights (per expert tensor), FC1 on unit-scaled codes writing bf16 h and each
+// expert's amax of it, h quantized per expert segment, FC2, combine.  Every tensor's scale
+// comes from its own amax.
 template <typename Mark>
 moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t st, Mark& mark) {
   const int64_t T = a->T, H = a->H, I = a->I, R = T * a->k;
@@ -243,6 +246,7 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
                           p.pt_part, st));
   MOE_CHECK(mark(2), MOE_ERR_HIP);
   HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(p.unit), p.unit_bytes / 4, 0x7F7F7F7Fu, st));
+  HIP_TRY(launch_fill_u32(p.h_amax, E, 0u, st));
   HIP_TRY(launch_pt_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.sw1, p.iw1, p.pt_part, st));
   MOE_CHECK(mark(3), MOE_ERR_HIP);
   HIP_TRY(launch_pt_quant_weights(a->w2, E, H, I, p.w2q, p.sw2, p.iw2, p.pt_part, st));
@@ -264,9 +268,10 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   g1.save_h = reinterpret_cast<uint16_t*>(p.h_bf);
   g1.pt_inv_a = p.ix;
   g1.pt_inv_b = p.iw1;
+  g1.pt_amax_out = p.h_amax;
   HIP_TRY(launch_fc1(g1, true, st));
   HIP_TRY(launch_pt_quant(p.h_bf, false, R, I, a->offsets, E, reinterpret_cast<uint8_t*>(p.h_op), p.sh, p.ih,
-                          p.pt_part, st));
+                          p.pt_part, st, p.h_amax));
   MOE_CHECK(mark(5), MOE_ERR_HIP);
 
   FwdGemm g2{};

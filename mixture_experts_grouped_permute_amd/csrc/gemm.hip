@@ -57,6 +57,7 @@ struct FwdKArgs {
   int split;                 // 0: every tile; 1: tiles before the split ones; 2: the split parts
   const float* pt_inv_a;     // per-tensor FP8: per expert 1 / s of the A rows and of the weight
   const float* pt_inv_b;
+  uint32_t* pt_amax_out;     // per-tensor FP8, FC1: per expert max |bf16 h| (float bits, atomic max)
   const uint8_t* w[kMaxExperts];
 };
 
@@ -367,6 +368,8 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       // expert, and h leaves as bf16 (its scale needs the amax of the expert's whole h)
       constexpr bool pt = kMx && kPt;
       const float dq = pt ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
+      float hmax = 0.f;   // per-tensor FP8: the largest |h| of the wave's blocks (rows past the tile's
+                          // end are zero: zero A rows and probability)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wm * 128 + i * 32 + r32;
@@ -399,6 +402,10 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = (silu_f(g[r]) * u[r]) * pr;
+          if constexpr (pt) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) hmax = fmaxf(hmax, fabsf(v[r]));
+          }
           if (!kMx || pt || p.save_h) {
             u32x4 oh[2];
             pack_bf16_runs8(v, oh);
@@ -426,6 +433,15 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+      if constexpr (pt) {
+        // the wave's largest |h| rounded to bf16 (rounding is monotone, so this is the largest
+        // stored value) raises the expert's amax for the quantization of h
+        float hm = hmax;
+#pragma unroll
+        for (int mk = 32; mk >= 1; mk >>= 1) hm = fmaxf(hm, __shfl_xor(hm, mk, 64));
+        hm = bf16_to_f32(f32_to_bf16(hm));
+        if (lane == 0) atomicMax(p.pt_amax_out + cur.e, __builtin_bit_cast(uint32_t, hm));
       }
     } else {
       const uint32_t N32 = (uint32_t)N;
@@ -554,6 +570,7 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
   k.out_f32 = g.out_f32 ? 1 : 0;
   k.pt_inv_a = g.pt_inv_a;
   k.pt_inv_b = g.pt_inv_b;
+  k.pt_amax_out = g.pt_amax_out;
   if (!mx)
     for (int e = 0; e < g.E; ++e) k.w[e] = reinterpret_cast<const uint8_t*>(g.w_tab[e]);
   return k;

@@ -49,8 +49,11 @@ hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t
 // cols % 8 == 0.
 int pt_blocks(int G);
 size_t pt_part_floats(int G);
+// amax_in: per-tensor amax as float bits, already known (the amax pass is skipped); nullptr:
+// computed here into part.
 hipError_t launch_pt_quant(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* offsets, int G,
-                           uint8_t* q, float* scales, float* inv, float* part, hipStream_t st);
+                           uint8_t* q, float* scales, float* inv, float* part, hipStream_t st,
+                           const uint32_t* amax_in = nullptr);
 hipError_t launch_pt_quant_weights(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
                                    float* scales, float* inv, float* part, hipStream_t st);
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t v, hipStream_t st);
@@ -90,6 +93,9 @@ struct FwdGemm {
   // multiplied by both, and FC1 writes bf16 h to save_h instead of E4M3 codes.  nullptr: MXFP8.
   const float* pt_inv_a;
   const float* pt_inv_b;
+  // per-tensor FP8, FC1: per expert max |bf16 h| as float bits, raised with an integer atomic max
+  // (order-free, so deterministic); zeroed by the caller before the launch
+  uint32_t* pt_amax_out;
 };
 // Workspace of the FC2 split-tile partials (bytes).
 constexpr size_t kFc2PartBytes = (size_t)kGemmGrid * 65536 * sizeof(float);

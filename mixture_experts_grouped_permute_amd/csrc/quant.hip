@@ -137,9 +137,12 @@ __global__ __launch_bounds__(64) void mx_cols_kernel(const void* __restrict__ x,
     const int g = g0 + lane;
     int pad = 0;
     if (g < num_groups) {
-      const int o = goff[g];
+      // offsets are the caller's device data: clamped into [0, rows] and non-decreasing, so
+      // that a bad array cannot take the kernel outside its buffers
+      const int o = min(max(goff[g], 0), (int)rows);
+      const int o1 = min(max(goff[g + 1], o), (int)rows);
       s_off[g] = o;
-      pad = (goff[g + 1] - o + seg_align - 1) / seg_align * seg_align;
+      pad = (o1 - o + seg_align - 1) / seg_align * seg_align;
     }
     int inc = pad;
 #pragma unroll
@@ -151,7 +154,7 @@ __global__ __launch_bounds__(64) void mx_cols_kernel(const void* __restrict__ x,
     carry += __shfl(inc, 63, 64);
   }
   if (lane == 0) {
-    s_off[num_groups] = goff[num_groups];
+    s_off[num_groups] = min(max(goff[num_groups], 0), (int)rows);
     s_pad[num_groups] = carry;
   }
   }
@@ -228,7 +231,10 @@ __device__ __forceinline__ void pt_range(const WTab& tab, const void* x, bool f3
   } else {
     (void)tab;
     (void)f32;
-    const int64_t lo = offsets ? offsets[g] : 0, hi = offsets ? offsets[g + 1] : rows;
+    // offsets are device data: clamped into [0, rows] and non-decreasing (memory-safe for any array)
+    int64_t lo = offsets ? (int64_t)offsets[g] : 0, hi = offsets ? (int64_t)offsets[g + 1] : rows;
+    lo = lo < 0 ? 0 : (lo > rows ? rows : lo);
+    hi = hi < lo ? lo : (hi > rows ? rows : hi);
     base = x;
     first = lo * cols;
     n = (hi - lo) * cols;
@@ -267,15 +273,20 @@ __global__ __launch_bounds__(256) void pt_amax_kernel(const WTab tab, const void
 template <bool kF32, bool kTab>
 __global__ __launch_bounds__(256) void pt_quant_kernel(const WTab tab, const void* x, const int32_t* offsets,
                                                         int64_t rows, int64_t cols, const float* part,
-                                                        uint8_t* __restrict__ q, float* scales, float* inv) {
+                                                        uint8_t* __restrict__ q, float* scales, float* inv,
+                                                        const uint32_t* amax_in) {
   __shared__ float red[4];
   const int g = blockIdx.y, nb = gridDim.x;
   const void* base;
   int64_t first, n;
   pt_range<kTab>(tab, x, kF32, offsets, rows, cols, g, base, first, n);
   float am = 0.f;
-  for (int i = threadIdx.x; i < nb; i += 256) am = fmaxf(am, part[g * nb + i]);
-  am = block_max(am, red);
+  if (amax_in) {
+    am = __builtin_bit_cast(float, amax_in[g]);
+  } else {
+    for (int i = threadIdx.x; i < nb; i += 256) am = fmaxf(am, part[g * nb + i]);
+    am = block_max(am, red);
+  }
   const float s = pt_scale(am);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     scales[g] = s;
@@ -349,16 +360,17 @@ int pt_blocks(int G) {
 size_t pt_part_floats(int G) { return (size_t)G * (size_t)pt_blocks(G); }
 
 hipError_t launch_pt_quant(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* offsets, int G,
-                           uint8_t* q, float* scales, float* inv, float* part, hipStream_t st) {
+                           uint8_t* q, float* scales, float* inv, float* part, hipStream_t st,
+                           const uint32_t* amax_in) {
   if (G <= 0) return hipSuccess;
   const dim3 grid((unsigned)pt_blocks(G), (unsigned)G);
   WTab tab{};
   if (x_f32) {
-    pt_amax_kernel<true, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part);
-    pt_quant_kernel<true, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part, q, scales, inv);
+    if (!amax_in) pt_amax_kernel<true, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part);
+    pt_quant_kernel<true, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part, q, scales, inv, amax_in);
   } else {
-    pt_amax_kernel<false, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part);
-    pt_quant_kernel<false, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part, q, scales, inv);
+    if (!amax_in) pt_amax_kernel<false, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part);
+    pt_quant_kernel<false, false><<<grid, 256, 0, st>>>(tab, x, offsets, rows, cols, part, q, scales, inv, amax_in);
   }
   return hipGetLastError();
 }
@@ -369,7 +381,7 @@ hipError_t launch_pt_quant_weights(const void* const* w, int E, int64_t rows, in
   for (int e = 0; e < E; ++e) tab.w[e] = reinterpret_cast<const uint16_t*>(w[e]);
   const dim3 grid((unsigned)pt_blocks(E), (unsigned)E);
   pt_amax_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, nullptr, rows, cols, part);
-  pt_quant_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, nullptr, rows, cols, part, q, scales, inv);
+  pt_quant_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, nullptr, rows, cols, part, q, scales, inv, nullptr);
   return hipGetLastError();
 }
 
