@@ -214,7 +214,8 @@ def bwd_leg(cfg, steps, warmup):
            "dgrad_fc1": 4.0 * R * H * I, "wgrad_fc1": 4.0 * R * H * I}
     dom = max(gem, key=lambda k_: ph[k_])
     return {
-        "workload": f"{cfg.name}: T={cfg.T} H={H} I={I} E={cfg.E} top-{cfg.k}, bf16, dW in fp32",
+        "workload": f"{cfg.name}: T={cfg.T} H={H} I={I} E={cfg.E} top-{cfg.k}, {cfg.precision} GEMM operands"
+                    + (" (each quantized along its GEMM's K)" if cfg.precision == "mxfp8" else "") + ", dW in fp32",
         "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
         "tflops": round(cfg.bwd_flops() / (ms * 1e-3) / 1e12, 1),
         "roofline": gemm_roofline(cfg, ph, dom, gem[dom], f"bwd_gemm_kernel ({dom})"),
@@ -358,9 +359,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,fp8,backward,router,loop",
-                    help="comma list of bf16, mxfp8, mxfp8_finegrained, fp8, backward, router, loop "
-                         "(bf16 always runs)")
+    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,fp8,backward,backward_mxfp8,router,loop",
+                    help="comma list of bf16, mxfp8, mxfp8_finegrained, fp8, backward, backward_mxfp8, router, "
+                         "loop (bf16 always runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
     args = ap.parse_args()
@@ -435,6 +436,11 @@ def main():
     if not args.no_backward and "backward" in legs:
         torch.cuda.empty_cache()
         line["backward_bf16"] = bwd_leg(get_config(4), max(2, args.steps // 2), max(1, args.warmup // 2))
+    if not args.no_backward and "backward_mxfp8" in legs:
+        # the MXFP8 backward on the same workload (its forward run with MXFP8 too)
+        torch.cuda.empty_cache()
+        line["backward_mxfp8"] = bwd_leg(get_config(4).with_(precision="mxfp8"), max(2, args.steps // 2),
+                                         max(1, args.warmup // 2))
     print(json.dumps(line), flush=True)
 
 

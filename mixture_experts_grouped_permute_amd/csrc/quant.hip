@@ -108,77 +108,107 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
 }
 
 // Column-wise quantization with per-segment restart, transposed output.
-// A workgroup handles a 32-row block of one segment and 64 columns: it loads
-// the 32 x 64 tile (zero beyond the segment), one lane per column reduces the
-// block's amax down its column, and writes the column's 32 codes contiguously.
+// The padded token axis (each segment padded to a multiple of seg_align rows) is cut into
+// 32-row blocks.  A workgroup of 256 lanes takes 4 consecutive blocks (128 padded rows) of 64
+// columns:
+//   * the source row of each padded row (or none: padding, or past the last segment) goes to LDS;
+//   * the 128 x 64 tile is loaded with 16-byte row-contiguous loads (zero for rows with no
+//     source) and kept in LDS as fp32;
+//   * lane (c, b) = (t % 64, t / 64) reduces block b of column c down its 32 rows, and writes its
+//     32 codes (two 16-byte stores) and its scale byte; the 4 blocks of a column fill one 128-byte
+//     stretch of the transposed output row.
+constexpr int kColRows = 128;   // padded rows per workgroup
 template <bool kF32>
-__global__ __launch_bounds__(64) void mx_cols_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                       const int32_t* __restrict__ goff, int num_groups,
-                                                       int64_t rows_pad, uint8_t* __restrict__ q,
-                                                       uint8_t* __restrict__ scales, int seg_align) {
-  // blockIdx.x: global 32-row block index over the padded token axis; blockIdx.y: 64-column slab
+__global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                        const int32_t* __restrict__ goff, int num_groups,
+                                                        int64_t rows_pad, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ scales, int seg_align) {
   __shared__ int s_pad[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
-  const int lane = threadIdx.x;
+  __shared__ int s_src[kColRows];
+  __shared__ float tile[kColRows][64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   if (!goff) {  // a single segment covering every row
-    if (lane == 0) {
+    if (t == 0) {
       s_off[0] = 0;
       s_off[1] = (int)rows;
       s_pad[0] = 0;
       s_pad[1] = (int)((rows + seg_align - 1) / seg_align * seg_align);
     }
     num_groups = 1;
-  }
-  __syncthreads();
-  // padded segment starts: one wave scans the groups 64 at a time
-  int carry = 0;
-  if (goff) {
-  for (int g0 = 0; g0 < num_groups; g0 += 64) {
-    const int g = g0 + lane;
-    int pad = 0;
-    if (g < num_groups) {
-      // offsets are the caller's device data: clamped into [0, rows] and non-decreasing, so
-      // that a bad array cannot take the kernel outside its buffers
-      const int o = min(max(goff[g], 0), (int)rows);
-      const int o1 = min(max(goff[g + 1], o), (int)rows);
-      s_off[g] = o;
-      pad = (o1 - o + seg_align - 1) / seg_align * seg_align;
-    }
-    int inc = pad;
+  } else if (wave == 0) {
+    // padded segment starts: one wave scans the groups 64 at a time
+    int carry = 0;
+    for (int g0 = 0; g0 < num_groups; g0 += 64) {
+      const int g = g0 + lane;
+      int pad = 0;
+      if (g < num_groups) {
+        // offsets are the caller's device data: clamped into [0, rows] and non-decreasing, so
+        // that a bad array cannot take the kernel outside its buffers
+        const int o = min(max(goff[g], 0), (int)rows);
+        const int o1 = min(max(goff[g + 1], o), (int)rows);
+        s_off[g] = o;
+        pad = (o1 - o + seg_align - 1) / seg_align * seg_align;
+      }
+      int inc = pad;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      int t = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += t;
+      for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += v;
+      }
+      if (g < num_groups) s_pad[g] = carry + inc - pad;
+      carry += __shfl(inc, 63, 64);
     }
-    if (g < num_groups) s_pad[g] = carry + inc - pad;
-    carry += __shfl(inc, 63, 64);
-  }
-  if (lane == 0) {
-    s_off[num_groups] = min(max(goff[num_groups], 0), (int)rows);
-    s_pad[num_groups] = carry;
-  }
+    if (lane == 0) {
+      s_off[num_groups] = min(max(goff[num_groups], 0), (int)rows);
+      s_pad[num_groups] = carry;
+    }
   }
   __syncthreads();
-  const int64_t pblk = (int64_t)blockIdx.x * 32;       // padded row of this block
-  if (pblk >= s_pad[num_groups]) return;
-  int g = 0;
-  while (g + 1 < num_groups && s_pad[g + 1] <= pblk) ++g;
-  const int64_t src0 = s_off[g] + (pblk - s_pad[g]);   // first source row
-  const int64_t src_end = s_off[g + 1];
-  const int64_t c = (int64_t)blockIdx.y * 64 + lane;
-  if (c >= cols) return;
+  const int64_t p0 = (int64_t)blockIdx.x * kColRows;   // first padded row of this workgroup
+  const int64_t ptotal = s_pad[num_groups];
+  if (p0 >= ptotal) return;                             // uniform: nothing of this slab is written
+  if (t < kColRows) {
+    const int64_t pr = p0 + t;
+    int src = -1;
+    if (pr < ptotal) {
+      int lo = 0, hi = num_groups - 1;                  // largest g with s_pad[g] <= pr
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pad[mid] <= pr) lo = mid; else hi = mid - 1;
+      }
+      const int64_t sr = s_off[lo] + (pr - s_pad[lo]);
+      const int64_t end = lo + 1 < num_groups ? min(s_off[lo + 1], (int)rows) : s_off[num_groups];
+      if (sr < end && sr < rows) src = (int)sr;
+    }
+    s_src[t] = src;
+  }
+  __syncthreads();
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  // the tile: chunk j of 8 values (kF32: 16 chunks of 4 per row would be finer; 8 keeps one loop)
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int id = t + 256 * it;                        // 1024 chunks: 128 rows x 8 chunks of 8 columns
+    const int rr = id >> 3, ck = id & 7;
+    const int64_t col = c0 + 8 * ck;
+    const int src = s_src[rr];
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    if (src >= 0 && col < cols) load8(x, kF32, (int64_t)src * cols + col, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[rr][8 * ck + e] = v[e];
+  }
+  __syncthreads();
+  const int64_t c = c0 + lane;
+  const int64_t pblk = p0 + 32 * wave;                  // padded row of this lane's block
+  if (c >= cols || pblk >= ptotal || pblk + 32 > rows_pad) return;
   float v[32];
   float am = 0.f;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    const int64_t sr = src0 + r;
-    float val = 0.f;
-    if (sr < src_end) {
-      if (kF32) val = reinterpret_cast<const float*>(x)[sr * cols + c];
-      else val = bf16_to_f32(reinterpret_cast<const uint16_t*>(x)[sr * cols + c]);
-    }
-    v[r] = val;
-    am = fmaxf(am, fabsf(val));
+    v[r] = tile[32 * wave + r][lane];
+    am = fmaxf(am, fabsf(v[r]));
   }
   const int s = mx_shared_exp(am);
   u32x4 o0, o1;
@@ -341,14 +371,14 @@ hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, in
 hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* group_offsets,
                                 int num_groups, int64_t rows_pad, uint8_t* q, uint8_t* scales, hipStream_t st,
                                 int seg_align) {
-  dim3 grid((unsigned)(rows_pad / 32), (unsigned)((cols + 63) / 64));
+  dim3 grid((unsigned)((rows_pad + kColRows - 1) / kColRows), (unsigned)((cols + 63) / 64));
   if (grid.x == 0) return hipSuccess;
   if (x_f32)
-    mx_cols_kernel<true><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
-                                              seg_align);
-  else
-    mx_cols_kernel<false><<<grid, 64, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+    mx_cols_kernel<true><<<grid, 256, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
                                                seg_align);
+  else
+    mx_cols_kernel<false><<<grid, 256, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                                seg_align);
   return hipGetLastError();
 }
 
