@@ -6,6 +6,8 @@
 //
 // Row-wise kernels stream 16-byte loads: a lane owns 8 consecutive values, 4
 // lanes share one 32-value block and reduce its amax with two xor shuffles.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -113,7 +115,8 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
 // columns:
 //   * the source row of each padded row (or none: padding, or past the last segment) goes to LDS;
 //   * the 128 x 64 tile is loaded with 16-byte row-contiguous loads (zero for rows with no
-//     source) and kept in LDS as fp32;
+//     source) and kept in LDS as loaded (bf16 input: its raw 16 KB, which leaves room for more
+//     workgroups per CU than an fp32 copy; f32 input: fp32);
 //   * lane (c, b) = (t % 64, t / 64) reduces block b of column c down its 32 rows, and writes its
 //     32 codes (two 16-byte stores) and its scale byte; the 4 blocks of a column fill one 128-byte
 //     stretch of the transposed output row.
@@ -125,8 +128,9 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x
                                                         uint8_t* __restrict__ scales, int seg_align) {
   __shared__ int s_pad[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
+  using TT = typename std::conditional<kF32, float, uint16_t>::type;
   __shared__ int s_src[kColRows];
-  __shared__ float tile[kColRows][64];
+  __shared__ __attribute__((aligned(16))) TT tile[kColRows][64];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   if (!goff) {  // a single segment covering every row
     if (t == 0) {
@@ -185,19 +189,26 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x
   }
   __syncthreads();
   const int64_t c0 = (int64_t)blockIdx.y * 64;
-  // the tile: chunk j of 8 values (kF32: 16 chunks of 4 per row would be finer; 8 keeps one loop)
+  // the tile, in chunks of 8 values
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int id = t + 256 * it;                        // 1024 chunks: 128 rows x 8 chunks of 8 columns
     const int rr = id >> 3, ck = id & 7;
     const int64_t col = c0 + 8 * ck;
     const int src = s_src[rr];
-    float v[8];
+    if constexpr (kF32) {
+      float v[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    if (src >= 0 && col < cols) load8(x, kF32, (int64_t)src * cols + col, v);
+      for (int e = 0; e < 8; ++e) v[e] = 0.f;
+      if (src >= 0 && col < cols) load8(x, true, (int64_t)src * cols + col, v);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) tile[rr][8 * ck + e] = v[e];
+      for (int e = 0; e < 8; ++e) tile[rr][8 * ck + e] = v[e];
+    } else {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (src >= 0 && col < cols)
+        w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + (int64_t)src * cols + col);
+      *reinterpret_cast<u32x4*>(&tile[rr][8 * ck]) = w;
+    }
   }
   __syncthreads();
   const int64_t c = c0 + lane;
@@ -207,7 +218,8 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x
   float am = 0.f;
 #pragma unroll
   for (int r = 0; r < 32; ++r) {
-    v[r] = tile[32 * wave + r][lane];
+    if constexpr (kF32) v[r] = tile[32 * wave + r][lane];
+    else v[r] = bf16_to_f32(tile[32 * wave + r][lane]);
     am = fmaxf(am, fabsf(v[r]));
   }
   const int s = mx_shared_exp(am);

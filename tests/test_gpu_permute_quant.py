@@ -116,13 +116,17 @@ def test_mxfp8_quantize_exhaustive_bf16():
 
 
 @gpu
-@pytest.mark.parametrize("sizes", [[0, 5, 32, 33, 0, 70], [257], [1, 0, 0, 64, 31]])
-def test_mxfp8_quantize_colwise_segments_bit_exact(sizes):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+# the last case spans several 128-row workgroup tiles of the padded token axis
+@pytest.mark.parametrize("sizes", [[0, 5, 32, 33, 0, 70], [257], [1, 0, 0, 64, 31], [130, 0, 400, 7, 129, 1]])
+def test_mxfp8_quantize_colwise_segments_bit_exact(sizes, dtype):
     m = need_gpu()
-    log(f"mxfp8_quantize axis1 segments {sizes}")
+    log(f"mxfp8_quantize axis1 segments {sizes} {dtype}")
     g = np.random.default_rng(len(sizes))
     off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
     x = torch.from_numpy(g.standard_normal((int(off[-1]), 96))).to(torch.bfloat16)
+    if dtype == "f32":
+        x = x.to(torch.float32) * (1 + torch.from_numpy(g.uniform(0, 1e-3, tuple(x.shape))).to(torch.float32))
     q, s = m.mxfp8_quantize(x.cuda(), axis=1, group_offsets=torch.from_numpy(off).cuda())
     rc, rs = nm.quantize_mxfp8_segments_t(x.to(torch.float64).numpy(), off)
     rp = rc.shape[1]
