@@ -117,9 +117,10 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
 //   * the 128 x 64 tile is loaded with 16-byte row-contiguous loads (zero for rows with no
 //     source) and kept in LDS as loaded (bf16 input: its raw 16 KB, which leaves room for more
 //     workgroups per CU than an fp32 copy; f32 input: fp32);
-//   * lane (c, b) = (t % 64, t / 64) reduces block b of column c down its 32 rows, and writes its
-//     32 codes (two 16-byte stores) and its scale byte; the 4 blocks of a column fill one 128-byte
-//     stretch of the transposed output row.
+//   * lane (c, b) = (t % 64, t / 64) reduces block b of column c down its 32 rows, stores its
+//     scale byte, and puts its 32 codes in an LDS staging area [column][padded row];
+//   * the staged codes go out as 16-byte pieces with consecutive lanes along one output row, so
+//     a store instruction writes 8 whole 128-byte stretches of the transposed output.
 constexpr int kColRows = 128;   // padded rows per workgroup
 template <bool kF32>
 __global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
@@ -211,9 +212,11 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x
     }
   }
   __syncthreads();
+  // codes staged [column][padded row], padded by 16 bytes per column against bank conflicts
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[64][kColRows + 16];
   const int64_t c = c0 + lane;
   const int64_t pblk = p0 + 32 * wave;                  // padded row of this lane's block
-  if (c >= cols || pblk >= ptotal || pblk + 32 > rows_pad) return;
+  const bool valid = c < cols && pblk < ptotal && pblk + 32 <= rows_pad;
   float v[32];
   float am = 0.f;
 #pragma unroll
@@ -229,10 +232,21 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x
     o0[i] = mx_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], s);
     o1[i] = mx_pack4(v[16 + 4 * i], v[16 + 4 * i + 1], v[16 + 4 * i + 2], v[16 + 4 * i + 3], s);
   }
-  uint8_t* dst = q + c * rows_pad + pblk;
-  *reinterpret_cast<u32x4*>(dst) = o0;
-  *reinterpret_cast<u32x4*>(dst + 16) = o1;
-  scales[c * (rows_pad / 32) + pblk / 32] = (uint8_t)(s + 127);
+  *reinterpret_cast<u32x4*>(&ostage[lane][32 * wave]) = o0;
+  *reinterpret_cast<u32x4*>(&ostage[lane][32 * wave + 16]) = o1;
+  if (valid) scales[c * (rows_pad / 32) + pblk / 32] = (uint8_t)(s + 127);
+  __syncthreads();
+  // piece pc (16 padded rows) of column lc; 8 pieces per column, 2 per 32-row block
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int id = t + 256 * it;
+    const int lc = id >> 3, pc = id & 7;
+    const int64_t cc = c0 + lc;
+    const int64_t pb = p0 + 32 * (pc >> 1);
+    if (cc < cols && pb < ptotal && pb + 32 <= rows_pad)
+      *reinterpret_cast<u32x4*>(q + cc * rows_pad + p0 + 16 * pc) =
+          *reinterpret_cast<const u32x4*>(&ostage[lc][16 * pc]);
+  }
 }
 
 // ---------------------------------------------------------------------------
