@@ -202,8 +202,8 @@ moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x
  * quantizes each GEMM operand tensor as fp8_tensor_quantize does: every W1_e
  * and W2_e, and each expert's rows of X_perm (bf16) and of h (rounded to bf16
  * first, since its scale needs the amax of the expert's whole h); it is
- * forward only (saved_* must be NULL, else MOE_ERR_UNSUPPORTED), takes no
- * cached weights, and is not offered by moe_grouped_mlp_fwd_loop.
+ * forward only (saved_* must be NULL, else MOE_ERR_UNSUPPORTED) and is not
+ * offered by moe_grouped_mlp_fwd_loop.
  * Alignment: H % 64 == 0 and I % 64 == 0 (BF16); H % 128 == 0 and
  * I % 128 == 0 (MXFP8, FP8).  Any token counts per expert, including zero.
  * Permutation outputs are always written (caller buffers, device).
@@ -216,11 +216,16 @@ moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x
  * I] and w2s [E, H, I/32], device.  When given, the per-call weight
  * quantization is skipped (weights quantized once and cached by the caller)
  * and the workspace is smaller; w1 / w2 are then not read.
+ * w1q, w1_scale, w2q, w2_scale: the same for MOE_FP8_E4M3 (all four or none;
+ * w1s / w2s then NULL): fp8_tensor_quantize of every W1_e and W2_e as one
+ * tensor each, stacked -- w1q [E, 2I, H] and w2q [E, H, I] codes, w1_scale
+ * and w2_scale [E] fp32 scales s, device (ABI version 3).  Any other mix of
+ * the six cached-weight fields is MOE_ERR_INVALID_ARG.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t T, H, I;
   int32_t E, k;
-  int32_t compute;              /* moe_dtype: MOE_BF16 or MOE_MXFP8_E4M3 */
+  int32_t compute;              /* moe_dtype: MOE_BF16, MOE_MXFP8_E4M3 or MOE_FP8_E4M3 */
   int32_t io_dtype;             /* moe_dtype: MOE_F32 or MOE_BF16 */
   const void* x;                /* [T, H] */
   const int32_t* topk_idx;      /* [T, k] */
@@ -242,6 +247,8 @@ typedef struct {
   const uint8_t* w1s;           /* [E, 2I, H/32] E8M0 */
   const uint8_t* w2q;           /* [E, H, I]     E4M3 */
   const uint8_t* w2s;           /* [E, H, I/32]  E8M0 */
+  const float* w1_scale;        /* [E] fp32 per-tensor FP8 scales, or NULL (ABI version 3) */
+  const float* w2_scale;        /* [E] */
 } moe_mlp_fwd_args;
 
 size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a);

@@ -54,6 +54,7 @@ class FwdArgs(ctypes.Structure):
         ("saved_x_perm", _vp), ("saved_gu", _vp), ("saved_h", _vp),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("w1q", _vp), ("w1s", _vp), ("w2q", _vp), ("w2s", _vp),
+        ("w1_scale", _vp), ("w2_scale", _vp),
     ]
 
 
@@ -342,11 +343,20 @@ def _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved):
     return a, (w1t, w2t, w1k, w2k), E, I
 
 
-def quantize_weights(w1, w2):
-    """MXFP8 weights for reuse across calls: (w1q [E,2I,H], w1s [E,2I,H/32], w2q [E,H,I],
-    w2s [E,H,I/32]), each expert quantized row-wise by mxfp8_quantize."""
+def quantize_weights(w1, w2, compute: str = "mxfp8"):
+    """Quantized weights for reuse across calls.
+    "mxfp8": (w1q [E,2I,H], w1s [E,2I,H/32], w2q [E,H,I], w2s [E,H,I/32]), each expert quantized
+    row-wise by mxfp8_quantize.  "fp8": (w1q [E,2I,H], w1_scale [E], w2q [E,H,I], w2_scale [E]),
+    each expert's matrix one tensor of fp8_tensor_quantize."""
     e1 = [w1[e] for e in range(len(w1))]
     e2 = [w2[e] for e in range(len(w2))]
+    if compute == "fp8":
+        q1 = [fp8_tensor_quantize(w) for w in e1]
+        q2 = [fp8_tensor_quantize(w) for w in e2]
+        return (torch.stack([q for q, _ in q1]), torch.cat([s for _, s in q1]),
+                torch.stack([q for q, _ in q2]), torch.cat([s for _, s in q2]))
+    if compute != "mxfp8":
+        raise ValueError(f"no cached weights for compute {compute!r}")
     q1 = [mxfp8_quantize(w, axis=0) for w in e1]
     q2 = [mxfp8_quantize(w, axis=0) for w in e2]
     return (torch.stack([q for q, _ in q1]), torch.stack([s for _, s in q1]),
@@ -358,8 +368,8 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
                         w_quant=None):
     """Grouped expert MLP forward.  w1: [E,2I,H] tensor or E tensors [2I,H] (bf16);
     w2: [E,H,I] or E tensors [H,I].  compute: "bf16", "mxfp8" or "fp8" (per-tensor scales,
-    forward only).  w_quant: optional (w1q, w1s, w2q, w2s) from quantize_weights (MXFP8
-    only): the per-call weight quantization is skipped.
+    forward only).  w_quant: optional quantize_weights(w1, w2, compute) output ("mxfp8" or
+    "fp8"): the per-call weight quantization is skipped.
     Returns (out, ctx) where ctx holds the permutation and, with save_for_backward,
     the bf16 activations."""
     lib = load()
@@ -386,7 +396,10 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
     out = torch.empty((T, H), dtype=x.dtype, device=dev)
     a, keep, _, _ = _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved)
     if w_quant is not None:
-        a.w1q, a.w1s, a.w2q, a.w2s = (_ptr(t) for t in w_quant)
+        if compute == "fp8":
+            a.w1q, a.w1_scale, a.w2q, a.w2_scale = (_ptr(t) for t in w_quant)
+        else:
+            a.w1q, a.w1s, a.w2q, a.w2s = (_ptr(t) for t in w_quant)
         keep = (keep, w_quant)
     need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
     if need == 0:

@@ -76,7 +76,7 @@ struct FwdPlan {
   // per-tensor FP8: bf16 X_perm and h ahead of their quantization, per-expert scales s and 1 / s
   // (X_perm rows, W1, h rows, W2), amax partials, and the 0x7F block scales the GEMMs read
   void* x_bf; void* h_bf;
-  float *sx, *ix, *sw1, *iw1, *sh, *ih, *sw2, *iw2;
+  float *sx, *sw1, *sh, *sw2;
   float* pt_part;
   uint32_t* h_amax;    // per expert max |bf16 h| (float bits), raised by FC1's epilogue
   uint8_t* unit;
@@ -97,10 +97,19 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
     p.x_op = c.take((size_t)(R * H));
     p.h_bf = c.take((size_t)(R * I * 2));
     p.h_op = c.take((size_t)(R * I));
-    p.w1q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H)));
-    p.w2q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I)));
-    p.sx = f(E); p.ix = f(E); p.sw1 = f(E); p.iw1 = f(E);
-    p.sh = f(E); p.ih = f(E); p.sw2 = f(E); p.iw2 = f(E);
+    if (a->w1q) {   // per-tensor FP8 weights cached by the caller: codes and fp32 scales
+      p.w1q = const_cast<uint8_t*>(a->w1q);
+      p.w2q = const_cast<uint8_t*>(a->w2q);
+      p.sw1 = const_cast<float*>(a->w1_scale);
+      p.sw2 = const_cast<float*>(a->w2_scale);
+    } else {
+      p.w1q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * 2 * I * H)));
+      p.w2q = reinterpret_cast<uint8_t*>(c.take((size_t)(E * H * I)));
+      p.sw1 = f(E);
+      p.sw2 = f(E);
+    }
+    p.sx = f(E);
+    p.sh = f(E);
     p.pt_part = f(pt_part_floats(E));
     p.h_amax = reinterpret_cast<uint32_t*>(c.take((size_t)E * sizeof(uint32_t)));
     // unit block scales: the FC1 GEMM reads rows [0, max(R, 2I)) of H/32 bytes, FC2 rows
@@ -153,9 +162,13 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   if (!a->w1q)
     for (int e = 0; e < a->E; ++e)
       if (!a->w1[e] || !a->w2[e]) return MOE_ERR_INVALID_ARG;
-  const bool any_q = a->w1q || a->w1s || a->w2q || a->w2s;
-  const bool all_q = a->w1q && a->w1s && a->w2q && a->w2s;
-  if (any_q && (!all_q || a->compute != MOE_MXFP8_E4M3)) return MOE_ERR_INVALID_ARG;
+  // cached weights: MXFP8 codes with E8M0 scales (w1s, w2s), or per-tensor FP8 codes with fp32
+  // scales (w1_scale, w2_scale) -- all four of the precision's fields, or none of the six
+  const bool any_q = a->w1q || a->w1s || a->w2q || a->w2s || a->w1_scale || a->w2_scale;
+  const bool mx_q = a->w1q && a->w1s && a->w2q && a->w2s && !a->w1_scale && !a->w2_scale;
+  const bool f8_q = a->w1q && a->w2q && a->w1_scale && a->w2_scale && !a->w1s && !a->w2s;
+  if (any_q && !((mx_q && a->compute == MOE_MXFP8_E4M3) || (f8_q && a->compute == MOE_FP8_E4M3)))
+    return MOE_ERR_INVALID_ARG;
   const bool any_saved = a->saved_x_perm || a->saved_gu || a->saved_h;
   const bool all_saved = a->saved_x_perm && a->saved_gu && a->saved_h;
   if (any_saved && !all_saved) return MOE_ERR_INVALID_ARG;
@@ -242,14 +255,14 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   const int E = a->E, k = a->k;
   const bool x_f32 = a->io_dtype == MOE_F32;
   HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_bf, nullptr, false, st));
-  HIP_TRY(launch_pt_quant(p.x_bf, false, R, H, a->offsets, E, reinterpret_cast<uint8_t*>(p.x_op), p.sx, p.ix,
+  HIP_TRY(launch_pt_quant(p.x_bf, false, R, H, a->offsets, E, reinterpret_cast<uint8_t*>(p.x_op), p.sx, nullptr,
                           p.pt_part, st));
   MOE_CHECK(mark(2), MOE_ERR_HIP);
   HIP_TRY(launch_fill_u32(reinterpret_cast<uint32_t*>(p.unit), p.unit_bytes / 4, 0x7F7F7F7Fu, st));
   HIP_TRY(launch_fill_u32(p.h_amax, E, 0u, st));
-  HIP_TRY(launch_pt_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.sw1, p.iw1, p.pt_part, st));
+  if (!a->w1q) HIP_TRY(launch_pt_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.sw1, nullptr, p.pt_part, st));
   MOE_CHECK(mark(3), MOE_ERR_HIP);
-  HIP_TRY(launch_pt_quant_weights(a->w2, E, H, I, p.w2q, p.sw2, p.iw2, p.pt_part, st));
+  if (!a->w1q) HIP_TRY(launch_pt_quant_weights(a->w2, E, H, I, p.w2q, p.sw2, nullptr, p.pt_part, st));
   MOE_CHECK(mark(4), MOE_ERR_HIP);
 
   FwdGemm g1{};
@@ -266,11 +279,11 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   g1.prob_perm = a->prob_perm;
   g1.out = p.h_bf;
   g1.save_h = reinterpret_cast<uint16_t*>(p.h_bf);
-  g1.pt_inv_a = p.ix;
-  g1.pt_inv_b = p.iw1;
+  g1.pt_s_a = p.sx;
+  g1.pt_s_b = p.sw1;
   g1.pt_amax_out = p.h_amax;
   HIP_TRY(launch_fc1(g1, true, st));
-  HIP_TRY(launch_pt_quant(p.h_bf, false, R, I, a->offsets, E, reinterpret_cast<uint8_t*>(p.h_op), p.sh, p.ih,
+  HIP_TRY(launch_pt_quant(p.h_bf, false, R, I, a->offsets, E, reinterpret_cast<uint8_t*>(p.h_op), p.sh, nullptr,
                           p.pt_part, st, p.h_amax));
   MOE_CHECK(mark(5), MOE_ERR_HIP);
 
@@ -288,8 +301,8 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   g2.out = p.z;
   g2.part = p.part;
   g2.out_f32 = x_f32;
-  g2.pt_inv_a = p.ih;
-  g2.pt_inv_b = p.iw2;
+  g2.pt_s_a = p.sh;
+  g2.pt_s_b = p.sw2;
   HIP_TRY(launch_fc2(g2, true, st));
   MOE_CHECK(mark(6), MOE_ERR_HIP);
 
@@ -302,7 +315,7 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
 
 extern "C" {
 
-int moe_abi_version(void) { return 2; }
+int moe_abi_version(void) { return 3; }
 
 const char* moe_status_string(int status) {
   switch (status) {

@@ -55,8 +55,8 @@ struct FwdKArgs {
   int out_f32;
   float* part;               // split tiles' fp32 partial accumulators, kGemmGrid x 64K floats
   int split;                 // 0: every tile; 1: tiles before the split ones; 2: the split parts
-  const float* pt_inv_a;     // per-tensor FP8: per expert 1 / s of the A rows and of the weight
-  const float* pt_inv_b;
+  const float* pt_s_a;       // per-tensor FP8: per expert scale s of the A rows and of the weight
+  const float* pt_s_b;
   uint32_t* pt_amax_out;     // per-tensor FP8, FC1: per expert max |bf16 h| (float bits, atomic max)
   const uint8_t* w[kMaxExperts];
 };
@@ -367,7 +367,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       // per-tensor FP8: the products of unit-scaled codes times 1 / (s_a s_b) of the tile's
       // expert, and h leaves as bf16 (its scale needs the amax of the expert's whole h)
       constexpr bool pt = kMx && kPt;
-      const float dq = pt ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
+      const float dq = pt ? (1.0f / p.pt_s_a[cur.e]) * (1.0f / p.pt_s_b[cur.e]) : 1.0f;
       float hmax = 0.f;   // per-tensor FP8: the largest |h| of the wave's blocks (rows past the tile's
                           // end are zero: zero A rows and probability)
 #pragma unroll
@@ -459,7 +459,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       }
       // first column of the tile in the destination (0 for a part slot)
       const uint32_t c0 = (kOutF32 && cur.part >= 0) ? 0u : (uint32_t)cur.nt * kBN;
-      const float dq = (kMx && kPt) ? p.pt_inv_a[cur.e] * p.pt_inv_b[cur.e] : 1.0f;
+      const float dq = (kMx && kPt) ? (1.0f / p.pt_s_a[cur.e]) * (1.0f / p.pt_s_b[cur.e]) : 1.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wm * 128 + i * 32 + r32;
@@ -568,8 +568,8 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
   k.save_gu = g.save_gu;
   k.save_h = g.save_h;
   k.out_f32 = g.out_f32 ? 1 : 0;
-  k.pt_inv_a = g.pt_inv_a;
-  k.pt_inv_b = g.pt_inv_b;
+  k.pt_s_a = g.pt_s_a;
+  k.pt_s_b = g.pt_s_b;
   k.pt_amax_out = g.pt_amax_out;
   if (!mx)
     for (int e = 0; e < g.E; ++e) k.w[e] = reinterpret_cast<const uint8_t*>(g.w_tab[e]);
@@ -580,7 +580,7 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
 
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
   FwdKArgs k = make_fwd_args(g, mx, true);
-  const bool pt = mx && g.pt_inv_a != nullptr;
+  const bool pt = mx && g.pt_s_a != nullptr;
   if (pt && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (pt) fwd_gemm_kernel<true, true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (mx && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
@@ -601,7 +601,7 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   // K of at least two 128-byte stages (and 16-byte scale rows for MXFP8) takes the deep pipeline
   // (split parts have at least kMinSplitUnits stages)
   const bool deep = mx ? (g.K >= 256 && g.K % 512 == 0) : g.K >= 128;
-  const bool pt = mx && g.pt_inv_a != nullptr;
+  const bool pt = mx && g.pt_s_a != nullptr;
   if (pt) {
     if (g.out_f32 && deep) fwd_gemm_kernel<true, false, true, true, true><<<kGemmGrid, 256, 0, st>>>(k);
     else if (g.out_f32) fwd_gemm_kernel<true, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);

@@ -89,10 +89,11 @@ struct FwdGemm {
   bool out_f32;                      // FC2
   float* part;                       // FC2: kGemmGrid x 65536 fp32 for split tiles (nullptr: no split)
   // per-tensor FP8 (MXFP8 instance with every block scale 1, i.e. a_scales / ws point at 0x7F
-  // bytes and ws_stride = 0): per expert 1 / s of its A rows and of its weight; the products are
-  // multiplied by both, and FC1 writes bf16 h to save_h instead of E4M3 codes.  nullptr: MXFP8.
-  const float* pt_inv_a;
-  const float* pt_inv_b;
+  // bytes and ws_stride = 0): per expert the scale s of its A rows and of its weight; the products
+  // are multiplied by (1 / s_a)(1 / s_b), and FC1 writes bf16 h to save_h instead of E4M3 codes.
+  // nullptr: MXFP8.
+  const float* pt_s_a;
+  const float* pt_s_b;
   // per-tensor FP8, FC1: per expert max |bf16 h| as float bits, raised with an integer atomic max
   // (order-free, so deterministic); zeroed by the caller before the launch
   uint32_t* pt_amax_out;

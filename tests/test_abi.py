@@ -52,7 +52,7 @@ def test_binding_lists_every_declared_symbol():
 
 
 def test_version_status_and_phase_names(lib):
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     lib.moe_status_string.restype = ctypes.c_char_p
     for s in range(5):
         assert lib.moe_status_string(s)
@@ -163,9 +163,18 @@ def test_fp8_forward_and_quantizer_validation(lib):
     d, td = _fwd_args(compute=MOE_FP8_E4M3)                       # forward only
     d.saved_x_perm = d.saved_gu = d.saved_h = 0x3000
     assert lib.moe_grouped_mlp_fwd(ctypes.byref(d), None) == MOE_ERR_UNSUPPORTED
-    e, te = _fwd_args(compute=MOE_FP8_E4M3)                       # cached weights are MXFP8 only
+    e, te = _fwd_args(compute=MOE_FP8_E4M3)                       # E8M0 scales are MXFP8's
     e.w1q = e.w1s = e.w2q = e.w2s = 0x2000
     assert lib.moe_grouped_mlp_fwd(ctypes.byref(e), None) == MOE_ERR_INVALID_ARG
+    f, tf = _fwd_args(compute=MOE_FP8_E4M3)                       # cached FP8 codes + fp32 scales
+    f.w1q = f.w2q = f.w1_scale = f.w2_scale = 0x2000
+    cached = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(f))
+    assert 0 < cached < f8 and f8 - cached >= 8 * 3 * 4096 * 14336
+    f.w1s = 0x2000                                                # mixed with E8M0 scales
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(f), None) == MOE_ERR_INVALID_ARG
+    g_, tg = _fwd_args(compute=2)                                 # MXFP8 takes no fp32 scales
+    g_.w1q = g_.w1s = g_.w2q = g_.w2s = g_.w1_scale = 0x2000
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(g_), None) == MOE_ERR_INVALID_ARG
     lib.fp8_tensor_quantize_workspace.restype = ctypes.c_size_t
     lib.fp8_tensor_quantize_workspace.argtypes = [ctypes.c_int]
     assert lib.fp8_tensor_quantize_workspace(8) >= 8 * 4 and lib.fp8_tensor_quantize_workspace(0) == 0

@@ -137,3 +137,25 @@ def test_forward_fp8_deterministic_and_rejections():
     with pytest.raises(m.MoeError) as ei:
         m.moe_grouped_mlp_fwd(e.x, e.topk_idx, e.topk_prob, e.w1, e.w2, "fp8")
     assert ei.value.status == 2
+
+
+@gpu
+def test_forward_fp8_cached_weights_equal_per_call_quantization():
+    """Weights quantized once (quantize_weights(..., "fp8")) give bit-identical outputs to the
+    per-call quantization; the cached codes and scales are the oracle's."""
+    m = need_gpu()
+    cfg = cfg_small(T=600, H=256, I=384, E=8, k=2)
+    log("fwd fp8 cached weights")
+    inp = make_inputs(cfg)
+    d = inp.to("cuda")
+    wq = m.quantize_weights(d.w1, d.w2, "fp8")
+    a, _ = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "fp8")
+    b, _ = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "fp8", w_quant=wq)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    c1, s1 = nm.quantize_fp8_tensor(inp.w1[5].to(torch.float64).numpy())
+    np.testing.assert_array_equal(wq[0][5].cpu().numpy(), c1)
+    assert wq[1][5].item() == float(s1)
+    c2, s2 = nm.quantize_fp8_tensor(inp.w2[2].to(torch.float64).numpy())
+    np.testing.assert_array_equal(wq[2][2].cpu().numpy(), c2)
+    assert wq[3][2].item() == float(s2)
