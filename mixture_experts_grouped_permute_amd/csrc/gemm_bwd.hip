@@ -110,7 +110,9 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const int pe = p.nM * p.nN;
       it.e = it.t / pe;
       const int local = it.t - it.e * pe;
-      tile_coords(local, p.nM, p.nN, it.mt, it.nt);
+      // groups of 4 M-tiles when an expert's dW has few of them (FC2's H / 256 = 16): measured
+      // 10 % faster for that wgrad than groups of 8, the same for FC1's 2I / 256 = 112
+      tile_coords(local, p.nM, p.nN, it.mt, it.nt, p.nM <= 16 ? 4 : kGroupM);
       it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
       it.koff = kMx ? __builtin_amdgcn_readfirstlane(sched.tile[it.e]) : __builtin_amdgcn_readfirstlane(sched.off[it.e]);
       it.kT = (it.Me + kKStep - 1) / kKStep;

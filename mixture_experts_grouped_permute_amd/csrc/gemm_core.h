@@ -72,14 +72,14 @@ __device__ void build_sched(Sched& s, const int32_t* split_sizes, int E, int nN,
 }
 
 // Coordinates (mt, nt) of tile `local` of one expert's nM x nN tile grid.  The M-tiles are split
-// into ng = ceil(nM / kGroupM) groups of balanced size (the first nM % ng groups one larger), and
+// into ng = ceil(nM / group_m) groups of balanced size (group_m: kGroupM unless the caller picks one) (the first nM % ng groups one larger), and
 // each group is walked panel by panel with its M-tiles fastest.  The 32 consecutive tiles an XCD
 // takes in a round then span at most kGroupM M-tiles and several panels, whose operand slices the
 // XCD's L2 shares, instead of up to 32 M-tiles of one panel.  With nM <= kGroupM this is the plain
 // M-fastest order.
 constexpr int kGroupM = 8;
-__device__ __forceinline__ void tile_coords(int local, int nM, int nN, int& mt, int& nt) {
-  const int ng = (nM + kGroupM - 1) / kGroupM;
+__device__ __forceinline__ void tile_coords(int local, int nM, int nN, int& mt, int& nt, int group_m = kGroupM) {
+  const int ng = (nM + group_m - 1) / group_m;
   const int base = nM / ng, r = nM - base * ng;      // r groups of base + 1 M-tiles, then base
   const int big = r * (base + 1) * nN;               // tiles of the larger groups
   int gm, m0, l;
