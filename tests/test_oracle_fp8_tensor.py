@@ -276,3 +276,35 @@ def test_fp8_rejected_where_rows_are_coupled():
     fw = mlp.forward(inp.x, idx, inp.topk_prob, inp.w1, inp.w2, "fp8")
     with pytest.raises(ValueError):
         mlp.backward(fw, inp.x, inp.dy, inp.w1, inp.w2)
+
+
+# ---------------------------------------------------------------------------- hand-derived cases
+
+import os                                                      # noqa: E402
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "fp8_tensor_cases.txt")
+
+
+def _golden():
+    out = []
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line.startswith("tensor "):
+            continue
+        parts = [p.strip() for p in line.split("|")]
+        name = parts[0].split()[1]
+        s = Fraction(parts[1].split("=")[1])
+        vals, codes = [], []
+        for tok in parts[2].split():
+            v, c = tok.split("=")
+            vals.append(float(v))
+            codes.append(int(c, 16))
+        out.append((name, s, vals, codes))
+    return out
+
+
+@pytest.mark.parametrize("name,s,vals,codes", _golden(), ids=[g[0] for g in _golden()])
+def test_golden_fp8_tensor_cases(name, s, vals, codes):
+    c, got_s = nm.quantize_fp8_tensor(np.array(vals))
+    assert Fraction(float(got_s)) == s
+    np.testing.assert_array_equal(c, np.array(codes, dtype=np.uint8))
