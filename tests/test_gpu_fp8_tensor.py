@@ -159,3 +159,23 @@ def test_forward_fp8_cached_weights_equal_per_call_quantization():
     c2, s2 = nm.quantize_fp8_tensor(inp.w2[2].to(torch.float64).numpy())
     np.testing.assert_array_equal(wq[2][2].cpu().numpy(), c2)
     assert wq[3][2].item() == float(s2)
+
+
+@gpu
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fp8_tensor_quantize_hand_derived_cases(dtype):
+    """The hand-derived tensors of tests/golden/fp8_tensor_cases.txt through the GPU quantizer
+    (each padded with zeros to a multiple of 8 columns, which changes neither amax nor codes)."""
+    from test_oracle_fp8_tensor import _golden
+    from fractions import Fraction
+    m = need_gpu()
+    log(f"fp8_tensor_quantize hand-derived cases {dtype}")
+    for name, s, vals, codes in _golden():
+        n = (len(vals) + 7) // 8 * 8
+        x = torch.zeros((1, n), dtype=torch.float64)
+        x[0, :len(vals)] = torch.tensor(vals, dtype=torch.float64)
+        x = x.to(torch.bfloat16 if dtype == "bf16" else torch.float32)
+        q, sc = m.fp8_tensor_quantize(x.cuda())
+        torch.cuda.synchronize()
+        assert Fraction(sc.item()) == s, name
+        assert q.cpu().numpy()[0, :len(vals)].tolist() == codes, name
