@@ -100,6 +100,32 @@ moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols
                           uint8_t* q, uint8_t* scales, void* stream);
 
 /* ------------------------------------------------------------------------
+ * mxfp8_quantize_weights -- OCP MXFP8 of a table of E bf16 weight matrices in
+ * one launch, the conversion of the 16-bit master weights for each
+ * low-precision GEMM (page "How BioNeMo cuts overhead", How MXFP8 reduces
+ * memory use; blocks of 32 values with one E8M0 scale as in page "BioNeMo
+ * Uses Grouped Kernels and MXFP8", Reducing memory pressure with MXFP8).
+ * moe_grouped_mlp_fwd (axis 0) and moe_grouped_mlp_bwd (axis 1) run the same
+ * kernels on every call unless their cached-weight arguments are given; this
+ * entry point produces those cached arguments.
+ *
+ * w        HOST array of E device pointers, each a bf16 matrix [rows, cols].
+ * axis 0:  row-wise, blocks along cols (cols % 32 == 0): q [E, rows, cols],
+ *          scales [E, rows, cols/32] -- the forward GEMMs' B operands (W1_e
+ *          along H, W2_e along I).
+ * axis 1:  column-wise, blocks along rows (rows % 32 == 0), output transposed:
+ *          q [E, cols, rows], scales [E, cols, rows/32] -- the backward dgrad
+ *          GEMMs' B operands (W2_e^T along H, W1_e^T along 2I).  cols % 32 == 0.
+ * skip     optional device int32 [E] (e.g. split_sizes): matrices with
+ *          skip[e] == 0 are not quantized and their q / scales slots are left
+ *          untouched.  NULL quantizes every matrix.
+ * q, scales device, caller-owned.  1 <= E <= 256.  Element and scale rule as
+ * mxfp8_quantize.
+ * ------------------------------------------------------------------------ */
+moe_status mxfp8_quantize_weights(const void* const* w, int E, int64_t rows, int64_t cols, int axis,
+                                  const int32_t* skip, uint8_t* q, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------
  * fp8_tensor_quantize -- per-tensor-scaled FP8 (page "BioNeMo Uses Grouped
  * Kernels and MXFP8", Reducing memory pressure with MXFP8: FP8 and MXFP8 use
  * 8-bit values and differ in the granularity of their scaling; FP8 here has
@@ -131,6 +157,11 @@ moe_status fp8_tensor_quantize(const void* x, int x_dtype, int64_t rows, int64_t
  * moe_permute -- histogram, prefix sum and stable scatter of the (token,
  * slot) pairs by expert (the gather of each expert's tokens before the
  * grouped GEMM; split_sizes as in the grouped linear's interface).
+ *
+ * Source: page "BioNeMo Uses Grouped Kernels and MXFP8", Grouping fragmented
+ * expert workloads -- the grouped linear takes one contiguous group of tokens
+ * per expert plus split_sizes, the per-expert token counts, which absorb
+ * uneven routing; Figure 1 -- the top-k router sends each token to k experts.
  *
  * x          [T, H] in x_dtype (MOE_F32 or MOE_BF16).
  * topk_idx   [T, k] int32 expert ids in [0, E).
@@ -184,7 +215,17 @@ moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * moe_grouped_mlp_fwd -- the whole expert MLP forward:
+ * moe_grouped_mlp_fwd -- the whole expert MLP forward.
+ *
+ * Source: page "BioNeMo Uses Grouped Kernels and MXFP8", Grouping fragmented
+ * expert workloads and Figure 2 (all local experts' GEMMs of a projection in
+ * one grouped submission instead of a loop of per-expert launches, gate-up
+ * out_features = 2 * intermediate_size, no bias); Fusing precision
+ * conversion and expert computation and Figure 4 (quantize, then one fused
+ * kernel for gate-up + ScaledSwiGLU with the routing probabilities, then the
+ * down projection); page "How BioNeMo cuts overhead", Why fused operations
+ * matter (intermediates not materialized).
+ *
  *   permute -> [MXFP8: quantize W1, W2] -> FC1 grouped GEMM with the
  *   ScaledSwiGLU * prob epilogue (writes h directly in the FC2 operand
  *   format; the 2I-wide gate-up output is never written unless saved_gu is
@@ -221,6 +262,19 @@ moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x
  * tensor each, stacked -- w1q [E, 2I, H] and w2q [E, H, I] codes, w1_scale
  * and w2_scale [E] fp32 scales s, device (ABI version 3).  Any other mix of
  * the six cached-weight fields is MOE_ERR_INVALID_ARG.
+ * error_flag: optional device int32 that receives the permutation's flag for
+ * out-of-range expert ids (0 or 1) instead of the first 4 bytes of the
+ * workspace, so that it stays readable after later calls reuse the workspace
+ * (moe_read_device_error accepts either address).
+ * h_codes, h_scales: optional (MXFP8 compute only; both or neither, else
+ * MOE_ERR_INVALID_ARG): caller buffers [R, I] and [R, I/32] that receive the
+ * E4M3 codes and E8M0 scales of h which the FC1 epilogue's fused quantizer
+ * writes and FC2 reads, in place of workspace buffers (the workspace is then
+ * smaller).  Rows are in permuted order, quantized along I.
+ * h_f32: optional [R, I] fp32, any compute: the epilogue also stores h =
+ * silu(g) * u * p in fp32 exactly as it computed it, before rounding it to
+ * bf16 or quantizing it -- the input of the fused quantizer, so that its
+ * bytes can be checked against mxfp8_quantize's rule.  NULL in production.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t T, H, I;
@@ -249,6 +303,10 @@ typedef struct {
   const uint8_t* w2s;           /* [E, H, I/32]  E8M0 */
   const float* w1_scale;        /* [E] fp32 per-tensor FP8 scales, or NULL (ABI version 3) */
   const float* w2_scale;        /* [E] */
+  int32_t* error_flag;          /* device int32, or NULL (ABI version 4) */
+  uint8_t* h_codes;             /* [R, I]    E4M3, or NULL (ABI version 4) */
+  uint8_t* h_scales;            /* [R, I/32] E8M0 */
+  float* h_f32;                 /* [R, I]    fp32, or NULL (ABI version 4) */
 } moe_mlp_fwd_args;
 
 size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a);
@@ -267,7 +325,18 @@ int moe_fwd_phase_count(void);
 const char* moe_fwd_phase_name(int i);   /* NULL when out of range */
 
 /* ------------------------------------------------------------------------
- * moe_grouped_mlp_bwd -- gradients of sum(out * dy):
+ * moe_grouped_mlp_bwd -- the matching fused backward.
+ *
+ * Source: page "BioNeMo Uses Grouped Kernels and MXFP8", Fusing precision
+ * conversion and expert computation (MXFP8 enabled for forward and backward;
+ * the fused forward has a corresponding fused backward operation); page "How
+ * BioNeMo cuts overhead", Why fused operations matter (a fused operation for
+ * the forward pass and a matching one for the backward pass).  The gradients
+ * are those of the forward above; the grouped wgrad with K = split_sizes[e]
+ * and the ScaledSwiGLU backward fused into the FC2 dgrad epilogue are this
+ * library's design.
+ *
+ * Gradients of sum(out * dy):
  *   dz[r]     = dy[token of r]
  *   dh        = dz . W2_e                              (FC2 dgrad)
  *   a = silu(g) u;  dprob_perm[r] = sum_i dh[r,i] a[r,i]
@@ -279,6 +348,12 @@ const char* moe_fwd_phase_name(int i);   /* NULL when out of range */
  * Under MXFP8 every GEMM operand is quantized along that GEMM's own K
  * (token-axis blocks restart per expert).  dw1/dw2 are overwritten.
  * g, u, h and x_perm are the bf16 tensors saved by the forward.
+ * w1tq, w1ts, w2tq, w2ts: optional (MXFP8 only; all four or none, else
+ * MOE_ERR_INVALID_ARG): the transposed weights of the dgrad GEMMs quantized
+ * once by the caller -- mxfp8_quantize_weights(w1, E, 2I, H, axis 1) and
+ * mxfp8_quantize_weights(w2, E, H, I, axis 1).  Without them the backward
+ * quantizes them itself on every call (one launch per weight table, experts
+ * without tokens skipped).
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t T, H, I;
@@ -303,6 +378,10 @@ typedef struct {
   void* const* dw2;             /* host array of E device pointers [H, I] dw_dtype */
   void* workspace;
   size_t workspace_bytes;
+  const uint8_t* w1tq;          /* [E, H, 2I]    E4M3, or NULL (ABI version 4) */
+  const uint8_t* w1ts;          /* [E, H, 2I/32] E8M0 */
+  const uint8_t* w2tq;          /* [E, I, H]     E4M3 */
+  const uint8_t* w2ts;          /* [E, I, H/32]  E8M0 */
 } moe_mlp_bwd_args;
 
 size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a);

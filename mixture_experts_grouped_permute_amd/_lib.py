@@ -28,7 +28,7 @@ EXPORTS = (
     "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
     "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop", "fp8_tensor_quantize_workspace",
-    "fp8_tensor_quantize",
+    "fp8_tensor_quantize", "mxfp8_quantize_weights",
 )
 
 
@@ -55,6 +55,7 @@ class FwdArgs(ctypes.Structure):
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("w1q", _vp), ("w1s", _vp), ("w2q", _vp), ("w2s", _vp),
         ("w1_scale", _vp), ("w2_scale", _vp),
+        ("error_flag", _vp), ("h_codes", _vp), ("h_scales", _vp), ("h_f32", _vp),
     ]
 
 
@@ -69,6 +70,7 @@ class BwdArgs(ctypes.Structure):
         ("dx", _vp), ("dprob", _vp),
         ("dw1", ctypes.POINTER(_vp)), ("dw2", ctypes.POINTER(_vp)),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
+        ("w1tq", _vp), ("w1ts", _vp), ("w2tq", _vp), ("w2ts", _vp),
     ]
 
 
@@ -89,6 +91,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.mxfp8_quantize.restype = ctypes.c_int
     lib.mxfp8_quantize.argtypes = [_vp, ctypes.c_int, _i64, _i64, ctypes.c_int, _vp, ctypes.c_int, _vp, _vp, _vp]
+    lib.mxfp8_quantize_weights.restype = ctypes.c_int
+    lib.mxfp8_quantize_weights.argtypes = [ctypes.POINTER(_vp), ctypes.c_int, _i64, _i64, ctypes.c_int, _vp, _vp,
+                                           _vp, _vp]
     lib.fp8_tensor_quantize_workspace.restype = ctypes.c_size_t
     lib.fp8_tensor_quantize_workspace.argtypes = [ctypes.c_int]
     lib.fp8_tensor_quantize.restype = ctypes.c_int
@@ -168,20 +173,43 @@ def _compute(c: str) -> int:
     return {"bf16": MOE_BF16, "mxfp8": MOE_MXFP8_E4M3, "fp8": MOE_FP8_E4M3}[c]
 
 
-def _table(ws: Sequence[torch.Tensor] | torch.Tensor):
+def _need(t: Optional[torch.Tensor], dtype: torch.dtype, device: torch.device, what: str) -> None:
+    """Raise TypeError unless t is a tensor of `dtype` on `device` (the library reads raw bytes)."""
+    if t is None:
+        return
+    if t.dtype != dtype:
+        raise TypeError(f"{what} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise TypeError(f"{what} must be on {device}, got {t.device}")
+
+
+def _table(ws: Sequence[torch.Tensor] | torch.Tensor, dtype: Optional[torch.dtype] = None,
+           device: Optional[torch.device] = None, what: str = "weight"):
+    """Host array of the device pointers of ws[e] (a stacked tensor or a list), and the tensors
+    behind them: non-contiguous entries are copied, and the copies are returned so that the caller
+    keeps them alive until the launch has been enqueued."""
     items = [ws[e] for e in range(ws.shape[0])] if isinstance(ws, torch.Tensor) else list(ws)
-    arr = (_vp * len(items))(*[_ptr(w.contiguous() if not w.is_contiguous() else w) for w in items])
+    if dtype is not None:
+        for w in items:
+            _need(w, dtype, device if device is not None else w.device, what)
+    items = [w if w.is_contiguous() else w.contiguous() for w in items]
+    arr = (_vp * len(items))(*[w.data_ptr() for w in items])
     return arr, items
 
 
 class _Workspace:
-    """A growable per-device scratch buffer owned by torch (the library never allocates)."""
+    """A growable scratch buffer per (device, stream), owned by torch (the library never
+    allocates).  Calls on one stream run in order, so they can share its buffer; calls on
+    different streams get different buffers.  A grown buffer replaces the old one, which stays
+    valid for the kernels already enqueued: it was allocated on that same stream, so torch's
+    allocator reuses its memory only in that stream's order."""
 
     def __init__(self):
         self.buf = {}
 
     def get(self, nbytes: int, device: torch.device) -> torch.Tensor:
-        key = (device.type, device.index)
+        stream = torch.cuda.current_stream(device)
+        key = (device.type, device.index, stream.cuda_stream)
         b = self.buf.get(key)
         if b is None or b.numel() < nbytes:
             b = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -238,32 +266,47 @@ def fp8_tensor_quantize(x: torch.Tensor, group_offsets: Optional[torch.Tensor] =
     return q, s
 
 
-def moe_permute(x: Optional[torch.Tensor], topk_idx: torch.Tensor, topk_prob: Optional[torch.Tensor], E: int,
-                perm_dtype: str = "bf16"):
-    """Histogram / prefix sum / stable scatter.  Returns a dict of device tensors."""
-    lib = load()
-    T, k = topk_idx.shape
-    dev = topk_idx.device
+def _check_routing(topk_idx: torch.Tensor, topk_prob: Optional[torch.Tensor], device: torch.device) -> None:
+    _need(topk_idx, torch.int32, device, "topk_idx")
+    _need(topk_prob, torch.float32, device, "topk_prob")
+
+
+def _perm_outputs(T: int, k: int, E: int, dev: torch.device, prob: bool = True) -> dict:
     R = T * k
-    out = {
+    return {
         "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
         "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
         "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
         "src_index": torch.empty(R, dtype=torch.int32, device=dev),
-        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev) if topk_prob is not None else None,
-        "x_perm": None, "x_perm_scales": None,
+        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev) if prob else None,
     }
+
+
+def moe_permute(x: Optional[torch.Tensor], topk_idx: torch.Tensor, topk_prob: Optional[torch.Tensor], E: int,
+                perm_dtype: str = "bf16"):
+    """Histogram / prefix sum / stable scatter.  Returns a dict of device tensors; its
+    "workspace" entry (this call's own) holds the bad-expert-id flag in its first 4 bytes."""
+    lib = load()
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    _check_routing(topk_idx, topk_prob, dev)
+    R = T * k
+    out = _perm_outputs(T, k, E, dev, topk_prob is not None)
+    out["x_perm"], out["x_perm_scales"] = None, None
     H = 0
     pd = _compute(perm_dtype)
     if x is not None:
+        if x.device != dev:
+            raise TypeError(f"x must be on {dev}")
         H = x.shape[1]
         if pd == MOE_BF16:
             out["x_perm"] = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
         else:
             out["x_perm"] = torch.empty((R, H), dtype=torch.uint8, device=dev)
             out["x_perm_scales"] = torch.empty((R, H // 32), dtype=torch.uint8, device=dev)
+    # the index workspace is small: one per call, so the flag it holds stays this call's
     need = lib.moe_permute_workspace_size(T, k, E)
-    ws = _WS.get(need, dev)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     st = lib.moe_permute(_ptr(x), _io(x) if x is not None else MOE_BF16, T, H, _ptr(topk_idx), _ptr(topk_prob),
                          k, E, pd, _ptr(out["x_perm"]), _ptr(out["x_perm_scales"]), _ptr(out["split_sizes"]),
                          _ptr(out["offsets"]), _ptr(out["row_id_map"]), _ptr(out["src_index"]),
@@ -294,16 +337,14 @@ def moe_route_permute(logits: torch.Tensor, x: Optional[torch.Tensor], k: int, p
     out = {
         "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
         "topk_prob": torch.empty((T, k), dtype=torch.float32, device=dev),
-        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
-        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
-        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
-        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
+        **_perm_outputs(T, k, E, dev),
         "x_perm": None, "x_perm_scales": None,
     }
     H = 0
     pd = _compute(perm_dtype)
     if x is not None:
+        if x.device != dev:
+            raise TypeError(f"x must be on {dev}")
         H = x.shape[1]
         if pd == MOE_BF16:
             out["x_perm"] = torch.empty((R, H), dtype=torch.bfloat16, device=dev)
@@ -311,7 +352,7 @@ def moe_route_permute(logits: torch.Tensor, x: Optional[torch.Tensor], k: int, p
             out["x_perm"] = torch.empty((R, H), dtype=torch.uint8, device=dev)
             out["x_perm_scales"] = torch.empty((R, H // 32), dtype=torch.uint8, device=dev)
     need = lib.moe_permute_workspace_size(T, k, E)
-    ws = _WS.get(need, dev)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     st = lib.moe_route_permute(_ptr(logits), _io(logits), _ptr(x), _io(x) if x is not None else MOE_BF16, T, H, E, k,
                                pd, _ptr(out["topk_idx"]), _ptr(out["topk_prob"]), _ptr(out["x_perm"]),
                                _ptr(out["x_perm_scales"]), _ptr(out["split_sizes"]), _ptr(out["offsets"]),
@@ -323,11 +364,17 @@ def moe_route_permute(logits: torch.Tensor, x: Optional[torch.Tensor], k: int, p
 
 
 def _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved):
+    """Argument struct of a forward call (no launch) and the tensors it points into."""
     T, H = x.shape
     k = topk_idx.shape[1]
-    w1t, w1k = _table(w1)
-    w2t, w2k = _table(w2)
+    dev = x.device
+    _io(x)
+    _check_routing(topk_idx, topk_prob, dev)
+    w1t, w1k = _table(w1, torch.bfloat16, dev, "w1")
+    w2t, w2k = _table(w2, torch.bfloat16, dev, "w2")
     E = len(w1k)
+    if len(w2k) != E:
+        raise ValueError("w1 and w2 must hold the same number of experts")
     I = w2k[0].shape[1]
     a = FwdArgs()
     a.T, a.H, a.I, a.E, a.k = T, H, I, E, k
@@ -343,35 +390,66 @@ def _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved):
     return a, (w1t, w2t, w1k, w2k), E, I
 
 
-def quantize_weights(w1, w2, compute: str = "mxfp8"):
+def mxfp8_quantize_weights(w, axis: int = 0, skip: Optional[torch.Tensor] = None):
+    """OCP MXFP8 of E bf16 matrices [rows, cols] (a stacked tensor or a list) in one launch.
+    axis 0: (codes [E, rows, cols], scales [E, rows, cols/32]);
+    axis 1: transposed, (codes [E, cols, rows], scales [E, cols, rows/32]).
+    skip: optional int32 device [E]; matrices with skip[e] == 0 are left as zeros."""
+    lib = load()
+    tab, items = _table(w, torch.bfloat16, None, "w")
+    E = len(items)
+    rows, cols = items[0].shape
+    dev = items[0].device
+    for t in items:
+        if t.shape != (rows, cols) or t.device != dev:
+            raise ValueError("every matrix must have the same shape and device")
+    _need(skip, torch.int32, dev, "skip")
+    shape = (E, rows, cols) if axis == 0 else (E, cols, rows)
+    make = torch.zeros if skip is not None else torch.empty
+    q = make(shape, dtype=torch.uint8, device=dev)
+    s = make((shape[0], shape[1], shape[2] // 32), dtype=torch.uint8, device=dev)
+    _check(lib.mxfp8_quantize_weights(tab, E, rows, cols, axis, _ptr(skip), _ptr(q), _ptr(s), _stream(dev)),
+           "mxfp8_quantize_weights")
+    return q, s
+
+
+def quantize_weights(w1, w2, compute: str = "mxfp8", transposed: bool = False):
     """Quantized weights for reuse across calls.
-    "mxfp8": (w1q [E,2I,H], w1s [E,2I,H/32], w2q [E,H,I], w2s [E,H,I/32]), each expert quantized
-    row-wise by mxfp8_quantize.  "fp8": (w1q [E,2I,H], w1_scale [E], w2q [E,H,I], w2_scale [E]),
-    each expert's matrix one tensor of fp8_tensor_quantize."""
-    e1 = [w1[e] for e in range(len(w1))]
-    e2 = [w2[e] for e in range(len(w2))]
+    "mxfp8": (w1q [E,2I,H], w1s [E,2I,H/32], w2q [E,H,I], w2s [E,H,I/32]), every expert quantized
+    row-wise by the kernel the forward runs per call (mxfp8_quantize_weights, axis 0).
+    "mxfp8", transposed=True: the backward's dgrad operands, (w1tq [E,H,2I], w1ts [E,H,2I/32],
+    w2tq [E,I,H], w2ts [E,I,H/32]) (axis 1).
+    "fp8": (w1q [E,2I,H], w1_scale [E], w2q [E,H,I], w2_scale [E]), each expert's matrix one
+    tensor of fp8_tensor_quantize."""
     if compute == "fp8":
+        if transposed:
+            raise ValueError("the per-tensor FP8 variant is forward only")
+        e1 = [w1[e] for e in range(len(w1))]
+        e2 = [w2[e] for e in range(len(w2))]
         q1 = [fp8_tensor_quantize(w) for w in e1]
         q2 = [fp8_tensor_quantize(w) for w in e2]
         return (torch.stack([q for q, _ in q1]), torch.cat([s for _, s in q1]),
                 torch.stack([q for q, _ in q2]), torch.cat([s for _, s in q2]))
     if compute != "mxfp8":
         raise ValueError(f"no cached weights for compute {compute!r}")
-    q1 = [mxfp8_quantize(w, axis=0) for w in e1]
-    q2 = [mxfp8_quantize(w, axis=0) for w in e2]
-    return (torch.stack([q for q, _ in q1]), torch.stack([s for _, s in q1]),
-            torch.stack([q for q, _ in q2]), torch.stack([s for _, s in q2]))
+    axis = 1 if transposed else 0
+    w1q, w1s = mxfp8_quantize_weights(w1, axis)
+    w2q, w2s = mxfp8_quantize_weights(w2, axis)
+    return w1q, w1s, w2q, w2s
 
 
 def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor, w1, w2,
                         compute: str = "bf16", save_for_backward: bool = False, workspace: Optional[torch.Tensor] = None,
-                        w_quant=None):
+                        w_quant=None, debug_h: bool = False):
     """Grouped expert MLP forward.  w1: [E,2I,H] tensor or E tensors [2I,H] (bf16);
     w2: [E,H,I] or E tensors [H,I].  compute: "bf16", "mxfp8" or "fp8" (per-tensor scales,
     forward only).  w_quant: optional quantize_weights(w1, w2, compute) output ("mxfp8" or
     "fp8"): the per-call weight quantization is skipped.
-    Returns (out, ctx) where ctx holds the permutation and, with save_for_backward,
-    the bf16 activations."""
+    debug_h: also return, in ctx["debug"], h in fp32 as FC1's epilogue computed it ("h_f32",
+    [R, I], permuted rows) and, under MXFP8, the E4M3 codes and E8M0 scales its fused quantizer
+    wrote ("h_codes" [R, I], "h_scales" [R, I/32]).
+    Returns (out, ctx) where ctx holds the permutation, the bad-expert-id flag ("error_flag")
+    and, with save_for_backward, the bf16 activations."""
     lib = load()
     dev = x.device
     T, H = x.shape
@@ -379,13 +457,7 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
     R = T * k
     E = w1.shape[0] if isinstance(w1, torch.Tensor) else len(w1)
     I = (w2.shape[2] if isinstance(w2, torch.Tensor) else w2[0].shape[1])
-    perm = {
-        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
-        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
-        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
-        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
-    }
+    perm = _perm_outputs(T, k, E, dev)
     saved = None
     if save_for_backward:
         saved = {
@@ -395,7 +467,20 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
         }
     out = torch.empty((T, H), dtype=x.dtype, device=dev)
     a, keep, _, _ = _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, saved)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    a.error_flag = flag.data_ptr()
+    debug = None
+    if debug_h:
+        debug = {"h_f32": torch.empty((R, I), dtype=torch.float32, device=dev)}
+        a.h_f32 = debug["h_f32"].data_ptr()
+        if compute == "mxfp8":
+            debug["h_codes"] = torch.empty((R, I), dtype=torch.uint8, device=dev)
+            debug["h_scales"] = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
+            a.h_codes, a.h_scales = debug["h_codes"].data_ptr(), debug["h_scales"].data_ptr()
     if w_quant is not None:
+        for t in w_quant:
+            if t.device != dev:
+                raise TypeError(f"cached weights must be on {dev}")
         if compute == "fp8":
             a.w1q, a.w1_scale, a.w2q, a.w2_scale = (_ptr(t) for t in w_quant)
         else:
@@ -408,7 +493,10 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
     ws = workspace if workspace is not None else _WS.get(need, dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_fwd")
-    ctx = {"perm": perm, "saved": saved, "compute": compute, "E": E, "I": I, "workspace": ws, "_keep": keep}
+    ctx = {"perm": perm, "saved": saved, "compute": compute, "E": E, "I": I, "error_flag": flag,
+           "workspace": ws, "_keep": keep}
+    if debug is not None:
+        ctx["debug"] = debug
     return out, ctx
 
 
@@ -420,17 +508,12 @@ def moe_grouped_mlp_fwd_loop(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob:
     dev = x.device
     T, H = x.shape
     k = topk_idx.shape[1]
-    R = T * k
     E = w1.shape[0] if isinstance(w1, torch.Tensor) else len(w1)
-    perm = {
-        "split_sizes": torch.empty(E, dtype=torch.int32, device=dev),
-        "offsets": torch.empty(E + 1, dtype=torch.int32, device=dev),
-        "row_id_map": torch.empty(R, dtype=torch.int32, device=dev),
-        "src_index": torch.empty(R, dtype=torch.int32, device=dev),
-        "prob_perm": torch.empty(R, dtype=torch.float32, device=dev),
-    }
+    perm = _perm_outputs(T, k, E, dev)
     out = torch.empty((T, H), dtype=x.dtype, device=dev)
     a, keep, _, _ = _fwd_args(x, topk_idx, topk_prob, w1, w2, compute, out, perm, None)
+    flag = torch.zeros(1, dtype=torch.int32, device=dev)
+    a.error_flag = flag.data_ptr()
     need = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
     if need == 0:
         _check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_fwd_loop")
@@ -438,24 +521,25 @@ def moe_grouped_mlp_fwd_loop(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob:
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     counts = (_i32 * E)(*[int(c) for c in split_sizes_host])
     _check(lib.moe_grouped_mlp_fwd_loop(ctypes.byref(a), counts, _stream(dev)), "moe_grouped_mlp_fwd_loop")
-    return out, {"perm": perm, "workspace": ws, "_keep": keep}
+    return out, {"perm": perm, "error_flag": flag, "workspace": ws, "_keep": keep}
 
 
-def _bwd_args(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32):
+def _bwd_args(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32, w_quant_t=None):
     """Output tensors and the argument struct of a backward call (no launch)."""
     dev = dy.device
     T, H = dy.shape
     perm, saved = ctx["perm"], ctx["saved"]
     if saved is None:
         raise ValueError("forward was run without save_for_backward")
+    _io(dy)
     E, I = ctx["E"], ctx["I"]
     k = perm["row_id_map"].numel() // T
     dx = torch.empty((T, H), dtype=dy.dtype, device=dev)
     dprob = torch.empty((T, k), dtype=torch.float32, device=dev)
     dw1 = torch.empty((E, 2 * I, H), dtype=dw_dtype, device=dev)
     dw2 = torch.empty((E, H, I), dtype=dw_dtype, device=dev)
-    w1t, w1k = _table(w1)
-    w2t, w2k = _table(w2)
+    w1t, w1k = _table(w1, torch.bfloat16, dev, "w1")
+    w2t, w2k = _table(w2, torch.bfloat16, dev, "w2")
     dw1t, _ = _table(dw1)
     dw2t, _ = _table(dw2)
     a = BwdArgs()
@@ -470,16 +554,22 @@ def _bwd_args(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32):
     a.saved_x_perm, a.saved_gu, a.saved_h = _ptr(saved["x_perm"]), _ptr(saved["gu"]), _ptr(saved["h"])
     a.dx, a.dprob = _ptr(dx), _ptr(dprob)
     a.dw1, a.dw2 = dw1t, dw2t
-    return a, (dx, dprob, dw1, dw2), (w1t, w2t, dw1t, dw2t, w1k, w2k)
+    if w_quant_t is not None:
+        for t in w_quant_t:
+            _need(t, torch.uint8, dev, "cached transposed weights")
+        a.w1tq, a.w1ts, a.w2tq, a.w2ts = (_ptr(t) for t in w_quant_t)
+    return a, (dx, dprob, dw1, dw2), (w1t, w2t, dw1t, dw2t, w1k, w2k, w_quant_t)
 
 
 def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32,
-                        workspace: Optional[torch.Tensor] = None):
+                        workspace: Optional[torch.Tensor] = None, w_quant_t=None):
     """Backward of moe_grouped_mlp_fwd (needs save_for_backward=True).
+    w_quant_t: optional quantize_weights(w1, w2, "mxfp8", transposed=True) output (MXFP8): the
+    per-call quantization of the transposed weights is skipped.
     Returns (dx [T,H], dprob [T,k] f32, dw1 [E,2I,H], dw2 [E,H,I])."""
     lib = load()
     dev = dy.device
-    a, outs, keep = _bwd_args(dy, ctx, w1, w2, dw_dtype)
+    a, outs, keep = _bwd_args(dy, ctx, w1, w2, dw_dtype, w_quant_t)
     dx, dprob, dw1, dw2 = outs
     need = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(a))
     if need == 0:
@@ -487,8 +577,11 @@ def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.floa
     ws = workspace if workspace is not None else _WS.get(need, dev)
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(lib.moe_grouped_mlp_bwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_bwd")
+    del keep
     return dx, dprob, dw1, dw2
 
 
-def moe_read_device_error(workspace: torch.Tensor) -> int:
-    return load().moe_read_device_error(workspace.data_ptr(), _stream(workspace.device))
+def moe_read_device_error(flag: torch.Tensor) -> int:
+    """The bad-expert-id flag of a call: ctx["error_flag"] of a forward, or the "workspace" of a
+    moe_permute / moe_route_permute result (synchronizes the current stream)."""
+    return load().moe_read_device_error(flag.data_ptr(), _stream(flag.device))

@@ -120,8 +120,13 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
   } else if (mx) {
     p.x_op = c.take((size_t)(R * H));
     p.x_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * H / 32)));
-    p.h_op = c.take((size_t)(R * I));
-    p.h_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * I / 32)));
+    if (a->h_codes) {   // h's codes and scales go to the caller's buffers
+      p.h_op = a->h_codes;
+      p.h_sc = a->h_scales;
+    } else {
+      p.h_op = c.take((size_t)(R * I));
+      p.h_sc = reinterpret_cast<uint8_t*>(c.take((size_t)(R * I / 32)));
+    }
     if (a->w1q) {   // quantized weights cached by the caller
       p.w1q = const_cast<uint8_t*>(a->w1q);
       p.w1s = const_cast<uint8_t*>(a->w1s);
@@ -142,6 +147,7 @@ FwdPlan plan_fwd(const moe_mlp_fwd_args* a, void* ws) {
   p.z = c.take((size_t)(R * H) * io_size(a->io_dtype));
   p.part = reinterpret_cast<float*>(c.take(kFc2PartBytes));
   p.bytes = c.used;
+  if (a->error_flag) p.perm.err = a->error_flag;
   return p;
 }
 
@@ -173,6 +179,8 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   const bool all_saved = a->saved_x_perm && a->saved_gu && a->saved_h;
   if (any_saved && !all_saved) return MOE_ERR_INVALID_ARG;
   if (any_saved && a->compute == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;   // forward only
+  if ((a->h_codes != nullptr) != (a->h_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+  if (a->h_codes && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
   // 32-bit buffer ranges inside the GEMMs
   const int64_t R = a->T * a->k;
   const int64_t widest = a->H > 2 * a->I ? a->H : 2 * a->I;
@@ -208,11 +216,19 @@ BwdPlan plan_bwd(const moe_mlp_bwd_args* a, void* ws) {
     p.rows_pad = Rp;
     auto take8 = [&](int64_t n) { return reinterpret_cast<uint8_t*>(c.take((size_t)n)); };
     p.dzq = take8(R * H); p.dzs = take8(R * H / 32);
-    p.w2tq = take8((int64_t)E * I * H); p.w2ts = take8((int64_t)E * I * H / 32);
+    if (a->w2tq) {
+      p.w2tq = const_cast<uint8_t*>(a->w2tq); p.w2ts = const_cast<uint8_t*>(a->w2ts);
+    } else {
+      p.w2tq = take8((int64_t)E * I * H); p.w2ts = take8((int64_t)E * I * H / 32);
+    }
     p.dzT = take8(H * Rp); p.dzTs = take8(H * Rp / 32);
     p.hT = take8(I * Rp); p.hTs = take8(I * Rp / 32);
     p.dguq = take8(R * 2 * I); p.dgus = take8(R * 2 * I / 32);
-    p.w1tq = take8((int64_t)E * H * 2 * I); p.w1ts = take8((int64_t)E * H * 2 * I / 32);
+    if (a->w1tq) {
+      p.w1tq = const_cast<uint8_t*>(a->w1tq); p.w1ts = const_cast<uint8_t*>(a->w1ts);
+    } else {
+      p.w1tq = take8((int64_t)E * H * 2 * I); p.w1ts = take8((int64_t)E * H * 2 * I / 32);
+    }
     p.dguT = take8(2 * I * Rp); p.dguTs = take8(2 * I * Rp / 32);
     p.xT = take8(H * Rp); p.xTs = take8(H * Rp / 32);
   }
@@ -233,6 +249,9 @@ moe_status validate_bwd(const moe_mlp_bwd_args* a) {
   if (!a->dy || !a->w1 || !a->w2 || !a->dx || !a->dprob || !a->dw1 || !a->dw2) return MOE_ERR_INVALID_ARG;
   if (!a->split_sizes || !a->offsets || !a->row_id_map || !a->src_index || !a->prob_perm) return MOE_ERR_INVALID_ARG;
   if (!a->saved_x_perm || !a->saved_gu || !a->saved_h) return MOE_ERR_INVALID_ARG;
+  const bool any_wt = a->w1tq || a->w1ts || a->w2tq || a->w2ts;
+  const bool all_wt = a->w1tq && a->w1ts && a->w2tq && a->w2ts;
+  if (any_wt && (!all_wt || a->compute != MOE_MXFP8_E4M3)) return MOE_ERR_INVALID_ARG;
   for (int e = 0; e < a->E; ++e)
     if (!a->w1[e] || !a->w2[e] || !a->dw1[e] || !a->dw2[e]) return MOE_ERR_INVALID_ARG;
   const int64_t R = a->T * a->k;
@@ -282,6 +301,7 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   g1.pt_s_a = p.sx;
   g1.pt_s_b = p.sw1;
   g1.pt_amax_out = p.h_amax;
+  g1.h_f32 = a->h_f32;
   HIP_TRY(launch_fc1(g1, true, st));
   HIP_TRY(launch_pt_quant(p.h_bf, false, R, I, a->offsets, E, reinterpret_cast<uint8_t*>(p.h_op), p.sh, nullptr,
                           p.pt_part, st, p.h_amax));
@@ -315,7 +335,7 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
 
 extern "C" {
 
-int moe_abi_version(void) { return 3; }
+int moe_abi_version(void) { return 4; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -348,6 +368,20 @@ moe_status mxfp8_quantize(const void* x, int x_dtype, int64_t rows, int64_t cols
     return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;
+}
+
+moe_status mxfp8_quantize_weights(const void* const* w, int E, int64_t rows, int64_t cols, int axis,
+                                  const int32_t* skip, uint8_t* q, uint8_t* scales, void* stream) {
+  MOE_CHECK(w && q && scales, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(E >= 1 && E <= MOE_MAX_EXPERTS && rows > 0 && cols > 0, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(axis == 0 || axis == 1, MOE_ERR_INVALID_ARG);
+  for (int e = 0; e < E; ++e) MOE_CHECK(w[e] != nullptr, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(cols % 32 == 0 && (axis == 0 || rows % 32 == 0), MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(rows < (int64_t)INT32_MAX && cols < (int64_t)INT32_MAX, MOE_ERR_UNSUPPORTED);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (axis == 0) HIP_TRY(launch_mx_quant_weights(w, E, rows, cols, q, scales, skip, st));
+  else HIP_TRY(launch_mx_quant_weights_t(w, E, rows, cols, q, scales, skip, st));
+  return MOE_OK;
 }
 
 size_t fp8_tensor_quantize_workspace(int num_groups) {
@@ -513,6 +547,7 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
   g1.out_scales = p.h_sc;
   g1.save_gu = reinterpret_cast<uint16_t*>(a->saved_gu);
   g1.save_h = mx ? reinterpret_cast<uint16_t*>(a->saved_h) : nullptr;
+  g1.h_f32 = a->h_f32;
   HIP_TRY(launch_fc1(g1, mx, st));
   MOE_CHECK(mark(5), MOE_ERR_HIP);
 
@@ -596,6 +631,7 @@ moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* sp
     g1.out_scales = mx ? p.h_sc + row0 * (I / 32) : nullptr;
     g1.save_gu = a->saved_gu ? reinterpret_cast<uint16_t*>(a->saved_gu) + row0 * 2 * I : nullptr;
     g1.save_h = (mx && a->saved_h) ? reinterpret_cast<uint16_t*>(a->saved_h) + row0 * I : nullptr;
+    g1.h_f32 = a->h_f32 ? a->h_f32 + row0 * I : nullptr;
     HIP_TRY(launch_fc1(g1, mx, st));
     FwdGemm g2{};
     g2.a = ho;
@@ -667,9 +703,8 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   d2.I = I;
   if (mx) {
     HIP_TRY(launch_mx_quant_rows(p.dz, false, R, H, p.dzq, p.dzs, st));
-    for (int e = 0; e < E; ++e)
-      HIP_TRY(launch_mx_quant_cols(a->w2[e], false, H, I, nullptr, 1, H, p.w2tq + (int64_t)e * I * H,
-                                   p.w2ts + (int64_t)e * I * (H / 32), st, 32));
+    // W2_e^T along H for every expert with tokens, one launch (unless cached by the caller)
+    if (!a->w2tq) HIP_TRY(launch_mx_quant_weights_t(a->w2, E, H, I, p.w2tq, p.w2ts, a->split_sizes, st));
     d2.a = p.dzq; d2.lda = H; d2.a_scales = p.dzs; d2.ldas = H / 32;
     d2.b = p.w2tq; d2.ldb = H; d2.b_stride = I * H; d2.b_scales = p.w2ts; d2.ldbs = H / 32;
     d2.bs_stride = I * (H / 32);
@@ -707,9 +742,8 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   d1.out = p.dx_perm; d1.out_f32 = io_f32; d1.part = p.part;
   if (mx) {
     HIP_TRY(launch_mx_quant_rows(p.dgu, false, R, 2 * I, p.dguq, p.dgus, st));
-    for (int e = 0; e < E; ++e)
-      HIP_TRY(launch_mx_quant_cols(a->w1[e], false, 2 * I, H, nullptr, 1, 2 * I, p.w1tq + (int64_t)e * H * 2 * I,
-                                   p.w1ts + (int64_t)e * H * (2 * I / 32), st, 32));
+    // W1_e^T along 2I for every expert with tokens, one launch (unless cached by the caller)
+    if (!a->w1tq) HIP_TRY(launch_mx_quant_weights_t(a->w1, E, 2 * I, H, p.w1tq, p.w1ts, a->split_sizes, st));
     d1.a = p.dguq; d1.lda = 2 * I; d1.a_scales = p.dgus; d1.ldas = 2 * I / 32;
     d1.b = p.w1tq; d1.ldb = 2 * I; d1.b_stride = H * 2 * I; d1.b_scales = p.w1ts; d1.ldbs = 2 * I / 32;
     d1.bs_stride = H * (2 * I / 32);

@@ -58,6 +58,7 @@ struct FwdKArgs {
   const float* pt_s_a;       // per-tensor FP8: per expert scale s of the A rows and of the weight
   const float* pt_s_b;
   uint32_t* pt_amax_out;     // per-tensor FP8, FC1: per expert max |bf16 h| (float bits, atomic max)
+  float* h_f32;              // FC1: h in fp32 as the epilogue computes it, before rounding, or null
   const uint8_t* w[kMaxExperts];
 };
 
@@ -364,6 +365,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const rsrc_t rsc = make_rsrc(kMx ? p.out_scales + r0 * (I / 32) : p.out, kMx ? mr * (I32 / 32) : 0);
       const rsrc_t rh = make_rsrc(p.save_h ? p.save_h + r0 * I : nullptr, p.save_h ? mr * I32 * 2 : 0);
       const rsrc_t rg = make_rsrc(p.save_gu ? p.save_gu + r0 * 2 * I : nullptr, p.save_gu ? mr * I32 * 4 : 0);
+      const rsrc_t rf = make_rsrc(p.h_f32 ? p.h_f32 + r0 * I : nullptr, p.h_f32 ? mr * I32 * 4 : 0);
       // per-tensor FP8: the products of unit-scaled codes times 1 / (s_a s_b) of the tile's
       // expert, and h leaves as bf16 (its scale needs the amax of the expert's whole h)
       constexpr bool pt = kMx && kPt;
@@ -402,6 +404,14 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           float v[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] = (silu_f(g[r]) * u[r]) * pr;
+          if (p.h_f32) {
+            // the fp32 h ahead of its rounding: runs of 4 columns 8 q + ch of the block
+            const uint32_t e4 = (uint32_t)m * I32 + col + (uint32_t)ch;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              __builtin_amdgcn_raw_buffer_store_b128(f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]}, rf,
+                                                     (e4 + 8u * q) * 4u, 0, 0);
+          }
           if constexpr (pt) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) hmax = fmaxf(hmax, fabsf(v[r]));
@@ -571,6 +581,7 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
   k.pt_s_a = g.pt_s_a;
   k.pt_s_b = g.pt_s_b;
   k.pt_amax_out = g.pt_amax_out;
+  k.h_f32 = g.h_f32;
   if (!mx)
     for (int e = 0; e < g.E; ++e) k.w[e] = reinterpret_cast<const uint8_t*>(g.w_tab[e]);
   return k;

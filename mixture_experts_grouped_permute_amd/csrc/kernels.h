@@ -35,6 +35,11 @@ hipError_t launch_mx_quant_rows(const void* x, bool x_f32, int64_t rows, int64_t
 // skip_if_empty != nullptr && skip_if_empty[e] == 0 are skipped (their codes are never read).
 hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
                                    uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st);
+// Column-wise MXFP8 of E bf16 weight matrices [rows, cols] (rows % 32 == 0) of a host pointer table
+// in one launch, transposed: matrix e's codes [cols, rows] at q + e * cols * rows, its scales
+// [cols, rows / 32] at scales + e * cols * rows / 32; skip_if_empty as launch_mx_quant_weights.
+hipError_t launch_mx_quant_weights_t(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
+                                     uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st);
 // Column-wise (blocks along rows, restarted per segment, transposed output); see mxfp8_quantize axis 1.
 // seg_align: segments are padded to a multiple of seg_align rows (32 for the C ABI; 128 when the
 // result feeds the variable-K wgrad GEMM, whose K steps are 128 values).
@@ -97,6 +102,9 @@ struct FwdGemm {
   // per-tensor FP8, FC1: per expert max |bf16 h| as float bits, raised with an integer atomic max
   // (order-free, so deterministic); zeroed by the caller before the launch
   uint32_t* pt_amax_out;
+  // FC1: optional fp32 copy of h = silu(g) u p [R, I] as the epilogue computes it, before it is
+  // rounded to bf16 or quantized (the input of the fused quantizer); nullptr: not written
+  float* h_f32;
 };
 // Workspace of the FC2 split-tile partials (bytes).
 constexpr size_t kFc2PartBytes = (size_t)kGemmGrid * 65536 * sizeof(float);

@@ -121,12 +121,32 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
 //     scale byte, and puts its 32 codes in an LDS staging area [column][padded row];
 //   * the staged codes go out as 16-byte pieces with consecutive lanes along one output row, so
 //     a store instruction writes 8 whole 128-byte stretches of the transposed output.
+//
+// kTab: a table of E weight matrices instead of one x (blockIdx.z = matrix e, read from the
+// kernel-argument table; matrices with skip[e] == 0 are left alone), each a single segment with
+// rows % 32 == 0, matrix e's output at q + e * cols * rows_pad and scales + e * cols * rows_pad / 32.
 constexpr int kColRows = 128;   // padded rows per workgroup
-template <bool kF32>
-__global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
-                                                        const int32_t* __restrict__ goff, int num_groups,
-                                                        int64_t rows_pad, uint8_t* __restrict__ q,
-                                                        uint8_t* __restrict__ scales, int seg_align) {
+template <bool kF32, bool kTab = false>
+__global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void* __restrict__ x, int64_t rows,
+                                                        int64_t cols, const int32_t* __restrict__ goff,
+                                                        int num_groups, int64_t rows_pad, uint8_t* __restrict__ q,
+                                                        uint8_t* __restrict__ scales, int seg_align,
+                                                        const int32_t* __restrict__ skip) {
+  if constexpr (kTab) {
+    const int e = blockIdx.z;
+    if (skip && skip[e] == 0) return;
+#if defined(__HIP_DEVICE_COMPILE__)
+    x = reinterpret_cast<const uint16_t* const*>(
+        reinterpret_cast<const char*>(__builtin_amdgcn_kernarg_segment_ptr()))[e];
+#else
+    x = tab.w[e];
+#endif
+    q += (int64_t)e * cols * rows_pad;
+    scales += (int64_t)e * cols * (rows_pad / 32);
+  } else {
+    (void)tab;
+    (void)skip;
+  }
   __shared__ int s_pad[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
   using TT = typename std::conditional<kF32, float, uint16_t>::type;
@@ -399,12 +419,24 @@ hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t
                                 int seg_align) {
   dim3 grid((unsigned)((rows_pad + kColRows - 1) / kColRows), (unsigned)((cols + 63) / 64));
   if (grid.x == 0) return hipSuccess;
+  WTab tab{};
   if (x_f32)
-    mx_cols_kernel<true><<<grid, 256, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
-                                               seg_align);
+    mx_cols_kernel<true><<<grid, 256, 0, st>>>(tab, x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                               seg_align, nullptr);
   else
-    mx_cols_kernel<false><<<grid, 256, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
-                                                seg_align);
+    mx_cols_kernel<false><<<grid, 256, 0, st>>>(tab, x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                                seg_align, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quant_weights_t(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
+                                     uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st) {
+  WTab tab{};
+  for (int e = 0; e < E; ++e) tab.w[e] = reinterpret_cast<const uint16_t*>(w[e]);
+  dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + 63) / 64), (unsigned)E);
+  if (grid.x == 0) return hipSuccess;
+  mx_cols_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, rows, cols, nullptr, 1, rows, q, scales, 32,
+                                                    skip_if_empty);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ def test_binding_lists_every_declared_symbol():
 
 
 def test_version_status_and_phase_names(lib):
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
     lib.moe_status_string.restype = ctypes.c_char_p
     for s in range(5):
         assert lib.moe_status_string(s)
@@ -187,3 +187,64 @@ def test_fp8_forward_and_quantizer_validation(lib):
     assert q(p, 1, 64, 64, None, 2, p, p, p, 1 << 20, None) == MOE_ERR_INVALID_ARG   # 2 groups, no offsets
     assert q(p, 2, 64, 64, None, 1, p, p, p, 1 << 20, None) == MOE_ERR_INVALID_ARG   # input already E4M3
     assert q(p, 1, 64, 64, None, 1, p, p, p, 4, None) == MOE_ERR_WORKSPACE
+
+
+def test_abi4_debug_outputs_and_error_flag_validation(lib):
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG
+    lib.moe_grouped_mlp_fwd_workspace.restype = ctypes.c_size_t
+    a, tab = _fwd_args(compute=2)
+    per_call = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    a.h_codes, a.h_scales = 0x2000, 0x3000
+    # h's codes and scales go to the caller's buffers: R * I * (1 + 1/32) bytes fewer
+    own = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a))
+    assert per_call - own >= 8192 * 14336 * 33 // 32
+    a.h_f32 = 0x4000
+    a.error_flag = 0x5000
+    assert lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(a)) == own
+    b, tb = _fwd_args(compute=2)           # both or neither
+    b.h_codes = 0x2000
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(b), None) == MOE_ERR_INVALID_ARG
+    c, tc = _fwd_args(compute=1)           # MXFP8 only
+    c.h_codes, c.h_scales = 0x2000, 0x3000
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(c), None) == MOE_ERR_INVALID_ARG
+    d, td = _fwd_args(compute=1)           # fp32 h is accepted for any compute
+    d.h_f32 = 0x4000
+    assert lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(d)) > 0
+
+
+def test_weight_quantizer_validation(lib):
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED
+    f = lib.mxfp8_quantize_weights
+    f.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    p = 0x1000
+    tab = (ctypes.c_void_p * 4)(*([p] * 4))
+    assert f(tab, 0, 64, 64, 0, None, p, p, None) == MOE_ERR_INVALID_ARG       # no matrices
+    assert f(tab, 4, 64, 64, 2, None, p, p, None) == MOE_ERR_INVALID_ARG       # no such axis
+    assert f(tab, 4, 64, 48, 0, None, p, p, None) == MOE_ERR_UNSUPPORTED       # cols % 32
+    assert f(tab, 4, 48, 64, 1, None, p, p, None) == MOE_ERR_UNSUPPORTED       # rows % 32 along rows
+    assert f(tab, 4, 64, 64, 0, None, None, p, None) == MOE_ERR_INVALID_ARG    # no output
+    tab[2] = None
+    assert f(tab, 4, 64, 64, 0, None, p, p, None) == MOE_ERR_INVALID_ARG       # a null matrix
+
+
+def test_bwd_cached_transposed_weight_validation(lib):
+    from mixture_experts_grouped_permute_amd._lib import BwdArgs, MOE_ERR_INVALID_ARG
+    E = 8
+    tab = (ctypes.c_void_p * E)(*([0x1000] * E))
+
+    def args(**kw):
+        a = BwdArgs(T=4096, H=4096, I=14336, E=E, k=2, compute=2, io_dtype=1, dw_dtype=0, dy=0x1000, w1=tab, w2=tab,
+                    split_sizes=0x1000, offsets=0x1000, row_id_map=0x1000, src_index=0x1000, prob_perm=0x1000,
+                    saved_x_perm=0x1000, saved_gu=0x1000, saved_h=0x1000, dx=0x1000, dprob=0x1000, dw1=tab, dw2=tab)
+        for k_, v in kw.items():
+            setattr(a, k_, v)
+        return a
+
+    lib.moe_grouped_mlp_bwd_workspace.restype = ctypes.c_size_t
+    per_call = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(args()))
+    cached = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(args(w1tq=0x2000, w1ts=0x2000, w2tq=0x2000, w2ts=0x2000)))
+    assert 0 < cached < per_call and per_call - cached >= E * 3 * 4096 * 14336
+    assert lib.moe_grouped_mlp_bwd(ctypes.byref(args(w1tq=0x2000)), None) == MOE_ERR_INVALID_ARG
+    bf = args(compute=1, w1tq=0x2000, w1ts=0x2000, w2tq=0x2000, w2ts=0x2000)
+    assert lib.moe_grouped_mlp_bwd(ctypes.byref(bf), None) == MOE_ERR_INVALID_ARG

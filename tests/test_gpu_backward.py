@@ -76,3 +76,39 @@ def test_backward_deterministic():
         res.append(m.moe_grouped_mlp_bwd(d.dy, ctx, d.w1, d.w2))
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+@gpu
+def test_backward_cached_transposed_weights():
+    """MXFP8 backward with the dgrad weights quantized once (quantize_weights(..., transposed=True))
+    gives the same bits as the per-call quantization, which skips experts without tokens."""
+    m = need_gpu()
+    log("bwd cached transposed MXFP8 weights")
+    cfg = cfg_small(T=400, H=128, I=256, E=8, k=2)
+    inp = _inputs(cfg, [0, 400, 1, 31, 0, 33, 335, 0])
+    d = inp.to("cuda")
+    out, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", save_for_backward=True)
+    a = m.moe_grouped_mlp_bwd(d.dy, ctx, d.w1, d.w2)
+    wt = m.quantize_weights(d.w1, d.w2, "mxfp8", transposed=True)
+    b = m.moe_grouped_mlp_bwd(d.dy, ctx, d.w1, d.w2, w_quant_t=wt)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@gpu
+def test_forward_flag_survives_backward():
+    """A forward's bad-expert-id flag lives in its own tensor: a backward that reuses the shared
+    workspace afterwards does not change what it reads."""
+    m = need_gpu()
+    log("fwd flag after bwd")
+    cfg = cfg_small(T=64, H=128, I=128, E=4, k=2)
+    inp = make_inputs(cfg, with_dy=True)
+    d = inp.to("cuda")
+    bad = d.topk_idx.clone()
+    bad[5, 1] = 9
+    _, ctx_bad = m.moe_grouped_mlp_fwd(d.x, bad, d.topk_prob, d.w1, d.w2, "bf16")
+    _, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "bf16", save_for_backward=True)
+    m.moe_grouped_mlp_bwd(d.dy, ctx, d.w1, d.w2)
+    assert m.moe_read_device_error(ctx_bad["error_flag"]) == 1
+    assert m.moe_read_device_error(ctx["error_flag"]) == 0

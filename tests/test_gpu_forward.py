@@ -118,6 +118,49 @@ def test_forward_split_last_round(compute):
     assert err < tol
 
 
+def _fused_h_check(m, inp):
+    """Forward with the FC1 epilogue's debug outputs: the E4M3 codes and E8M0 scales its fused
+    quantizer wrote must be the oracle quantizer's bytes for the kernel's own fp32 h (one
+    result exists for a given input).  Returns (the kernel's fp32 h, its codes)."""
+    d = inp.to("cuda")
+    out, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", debug_h=True)
+    plain, _ = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8")
+    torch.cuda.synchronize()
+    # FC2 read the caller's code buffers: the output is the production call's, bit for bit
+    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out.view(torch.int32),
+                       plain.view(torch.int16) if plain.dtype == torch.bfloat16 else plain.view(torch.int32))
+    dbg = ctx["debug"]
+    h32 = dbg["h_f32"].cpu().numpy().astype(np.float64)
+    codes = dbg["h_codes"].cpu().numpy()
+    scales = dbg["h_scales"].cpu().numpy()
+    rc, rs = nm.quantize_mxfp8(h32, axis=1)
+    np.testing.assert_array_equal(scales, rs)
+    np.testing.assert_array_equal(codes, rc)
+    return h32, codes
+
+
+@gpu
+@pytest.mark.parametrize("name,cfg,counts", CASES, ids=[c[0] for c in CASES])
+def test_fused_h_quantizer_bytes(name, cfg, counts):
+    """The fused MXFP8 quantizer of h in the FC1 epilogue, byte for byte against the oracle's
+    quantizer applied to the epilogue's own fp32 h."""
+    m = need_gpu()
+    if cfg.H % 128 or cfg.I % 128:
+        pytest.skip("MXFP8 path needs H, I multiples of 128")
+    log(f"fused h quantizer {name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
+    inp = _inputs(cfg, counts)
+    h32, codes = _fused_h_check(m, inp)
+    ref = mlp.forward(inp.x, inp.topk_idx.numpy(), inp.topk_prob, inp.w1, inp.w2, "mxfp8", cfg.x_dtype)
+    # the kernel's fp32 h against the oracle's fp64 h (same operands; fp32 vs fp64 arithmetic).
+    # Codes of the oracle's fp64 h are only counted, not compared: the last bits of h differ, so
+    # a value at a rounding tie may land on either side.
+    err = mlp.normwise_rel_err(h32, ref.h)
+    oc, _ = nm.quantize_mxfp8(ref.h, axis=1)
+    flips = int(np.count_nonzero(oc != codes))
+    log(f"  bytes equal; h fp32 vs fp64 err {err:.2e}; codes differing from Q(fp64 h): {flips} of {codes.size}")
+    assert err < 1e-5
+
+
 @gpu
 def test_forward_cached_mxfp8_weights_equal_per_call_quantization():
     """Weights quantized once (quantize_weights) give bit-identical outputs to the per-call
@@ -132,10 +175,47 @@ def test_forward_cached_mxfp8_weights_equal_per_call_quantization():
     b, _ = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", w_quant=wq)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
-    # the oracle's weight bytes are the cached ones
-    c1, s1 = nm.quantize_mxfp8(inp.w1[3].to(torch.float64).numpy(), axis=1)
-    np.testing.assert_array_equal(wq[0][3].cpu().numpy(), c1)
-    np.testing.assert_array_equal(wq[1][3].cpu().numpy(), s1)
+    # the oracle's weight bytes are the cached ones, for every expert and both projections
+    for e in range(cfg.E):
+        c1, s1 = nm.quantize_mxfp8(inp.w1[e].to(torch.float64).numpy(), axis=1)
+        c2, s2 = nm.quantize_mxfp8(inp.w2[e].to(torch.float64).numpy(), axis=1)
+        np.testing.assert_array_equal(wq[0][e].cpu().numpy(), c1)
+        np.testing.assert_array_equal(wq[1][e].cpu().numpy(), s1)
+        np.testing.assert_array_equal(wq[2][e].cpu().numpy(), c2)
+        np.testing.assert_array_equal(wq[3][e].cpu().numpy(), s2)
+
+
+@gpu
+def test_weight_quantizer_tables():
+    """mxfp8_quantize_weights (the kernels the forward and backward run per call on their weight
+    tables): row-wise and transposed column-wise bytes of every matrix against the oracle, and
+    matrices whose skip entry is 0 left untouched."""
+    m = need_gpu()
+    log("weight quantizer tables")
+    g = np.random.default_rng(31)
+    E, rows, cols = 5, 320, 192
+    w = torch.from_numpy(g.standard_normal((E, rows, cols)).astype(np.float32) * 0.02).to(torch.bfloat16)
+    w[2, 5:37] = 0.0          # all-zero blocks along both axes
+    w[3] *= 1e-30             # subnormal-range values (bf16 keeps the fp32 exponent range)
+    dw = w.to("cuda")
+    skip = torch.tensor([1, 0, 3, 1, 0], dtype=torch.int32, device="cuda")
+    q0, s0 = m.mxfp8_quantize_weights(dw, axis=0)
+    q1, s1 = m.mxfp8_quantize_weights(dw, axis=1)
+    q2, s2 = m.mxfp8_quantize_weights([dw[e] for e in range(E)], axis=1, skip=skip)
+    torch.cuda.synchronize()
+    for e in range(E):
+        we = w[e].to(torch.float64).numpy()
+        rc, rs = nm.quantize_mxfp8(we, axis=1)
+        np.testing.assert_array_equal(q0[e].cpu().numpy(), rc)
+        np.testing.assert_array_equal(s0[e].cpu().numpy(), rs)
+        cc, cs = nm.quantize_mxfp8(we, axis=0)             # blocks along rows, [rows, cols/..]
+        np.testing.assert_array_equal(q1[e].cpu().numpy(), cc.T)
+        np.testing.assert_array_equal(s1[e].cpu().numpy(), cs.T)
+        if skip[e].item() == 0:
+            assert int(q2[e].count_nonzero()) == 0 and int(s2[e].count_nonzero()) == 0
+        else:
+            np.testing.assert_array_equal(q2[e].cpu().numpy(), cc.T)
+            np.testing.assert_array_equal(s2[e].cpu().numpy(), cs.T)
 
 
 @gpu

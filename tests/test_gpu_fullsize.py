@@ -59,10 +59,33 @@ def test_fullsize_forward(ci, experts, prec):
     assert err < tol
 
 
+def _finegrained_sample(idx, E, T, extra=320, seed=0):
+    """Tokens whose outputs are compared for the 64-expert layer: for every expert, the tokens of
+    the first row of its segment, of the first row of its last 256-row tile and of its last row
+    (rows in a segment ascend with the token index), plus `extra` random tokens."""
+    ref = oracle_permute(idx, E)
+    toks = set()
+    for e in range(E):
+        lo, hi = int(ref.offsets[e]), int(ref.offsets[e + 1])
+        if hi == lo:
+            continue
+        last_tile = lo + (hi - lo - 1) // 256 * 256
+        for r in (lo, last_tile, hi - 1):
+            toks.add(int(ref.token_of_row[r]))
+    g = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.array(sorted(toks)))
+    toks.update(int(t) for t in g.choice(rest, size=extra, replace=False))
+    return sorted(toks)
+
+
 @gpu
 @slow
 @pytest.mark.timeout(900)
 def test_fullsize_finegrained_forward_sampled_tokens():
+    """The 64-expert top-8 MXFP8 layer at full size: at least 512 tokens, covering the first and
+    last row of every expert and the first row of its last tile, against the oracle token by
+    token (every rounding step of that layer acts within one row, so a token's output needs
+    only its own row)."""
     m = need_gpu()
     cfg = get_config(5)
     log(f"full-size fwd {cfg.name}: generating inputs")
@@ -72,11 +95,16 @@ def test_fullsize_finegrained_forward_sampled_tokens():
     torch.cuda.synchronize()
     idx = inp.topk_idx.numpy()
     np.testing.assert_array_equal(ctx["perm"]["split_sizes"].cpu().numpy(), np.bincount(idx.ravel(), minlength=cfg.E))
-    tokens = [0, 1, 2, cfg.T // 2, cfg.T - 1]
-    log(f"  oracle on tokens {tokens}")
+    tokens = _finegrained_sample(idx, cfg.E, cfg.T)
+    assert len(tokens) >= 512
+    covered = np.unique(idx[tokens])
+    assert len(covered) == int((np.bincount(idx.ravel(), minlength=cfg.E) > 0).sum())
+    log(f"  oracle on {len(tokens)} tokens covering {len(covered)} experts")
     ref = mlp.forward_tokens(inp.x, idx, inp.topk_prob, inp.w1, inp.w2, tokens, cfg.precision, cfg.x_dtype)
-    err = mlp.normwise_rel_err(to_np(out)[tokens], ref)
-    log(f"  normwise err {err:.3e} (tol {MXFP8_TOL})")
+    got = to_np(out)[tokens]
+    err = mlp.normwise_rel_err(got, ref)
+    worst = max(mlp.normwise_rel_err(got[i], ref[i]) for i in range(len(tokens)))
+    log(f"  normwise err {err:.3e}, worst single token {worst:.3e} (tol {MXFP8_TOL})")
     assert err < MXFP8_TOL
 
 
@@ -84,7 +112,8 @@ def test_fullsize_finegrained_forward_sampled_tokens():
 @slow
 @pytest.mark.timeout(900)
 def test_fullsize_mxfp8_bytes():
-    """Permuted X rows and one expert's weights quantized by the kernels the MXFP8 layer runs."""
+    """Every permuted X row of the MXFP8 workload, byte for byte (the permutation's fused row
+    quantizer)."""
     m = need_gpu()
     cfg = get_config(3)
     log("full-size MXFP8 bytes: generating inputs")
@@ -97,12 +126,81 @@ def test_fullsize_mxfp8_bytes():
     tok = ref.token_of_row
     np.testing.assert_array_equal(res["x_perm"].cpu().numpy(), c[tok])
     np.testing.assert_array_equal(res["x_perm_scales"].cpu().numpy(), s[tok])
+
+
+def _oracle_rows(w, axis, chunk=2048):
+    """The oracle's MXFP8 of a bf16 matrix (axis 1: blocks along each row; axis 0: along each
+    column), a band of rows (axis 1) or columns (axis 0) at a time to bound host memory."""
+    w64 = w.to(torch.float64).numpy() if hasattr(w, "numpy") else w
+    if axis == 1:
+        parts = [nm.quantize_mxfp8(w64[r:r + chunk], axis=1) for r in range(0, w64.shape[0], chunk)]
+        return np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts])
+    parts = [nm.quantize_mxfp8(w64[:, c:c + chunk], axis=0) for c in range(0, w64.shape[1], chunk)]
+    return np.concatenate([p[0] for p in parts], axis=1), np.concatenate([p[1] for p in parts], axis=1)
+
+
+@gpu
+@slow
+@pytest.mark.timeout(900)
+def test_fullsize_weight_quantizer_bytes():
+    """The weight quantizer the MXFP8 layer runs on every call (mxfp8_quantize_weights, which the
+    forward's per-call path and quantize_weights share): every expert's W1 and W2 at the Mixtral
+    shape row-wise, as the forward GEMMs read them; and the backward's transposed, column-wise
+    W1^T / W2^T of two experts."""
+    m = need_gpu()
+    cfg = get_config(3)
+    log("full-size weight quantizer bytes: generating inputs")
+    inp = make_inputs(cfg)
+    d = inp.to("cuda")
+    w1q, w1s, w2q, w2s = m.quantize_weights(d.w1, d.w2, "mxfp8")
+    torch.cuda.synchronize()
+    for e in range(cfg.E):
+        log(f"  expert {e}: W1 [{2 * cfg.I}, {cfg.H}] and W2 [{cfg.H}, {cfg.I}] row-wise")
+        for got_q, got_s, w in ((w1q[e], w1s[e], inp.w1[e]), (w2q[e], w2s[e], inp.w2[e])):
+            rc, rs = _oracle_rows(w, axis=1)
+            np.testing.assert_array_equal(got_s.cpu().numpy(), rs)
+            np.testing.assert_array_equal(got_q.cpu().numpy(), rc)
+    del w1q, w1s, w2q, w2s
+    t1q, t1s, t2q, t2s = m.quantize_weights(d.w1, d.w2, "mxfp8", transposed=True)
+    torch.cuda.synchronize()
+    for e in (0, 5):
+        log(f"  expert {e}: W1^T and W2^T column-wise (backward operands)")
+        for got_q, got_s, w in ((t1q[e], t1s[e], inp.w1[e]), (t2q[e], t2s[e], inp.w2[e])):
+            rc, rs = _oracle_rows(w, axis=0)
+            np.testing.assert_array_equal(got_s.cpu().numpy(), rs.T)
+            np.testing.assert_array_equal(got_q.cpu().numpy(), rc.T)
+
+
+@gpu
+@slow
+@pytest.mark.timeout(900)
+def test_fullsize_fused_h_quantizer_bytes():
+    """The FC1 epilogue's fused MXFP8 quantizer of h at the full Mixtral MXFP8 workload (T=8192,
+    Zipf routing), byte for byte against the oracle's quantizer on the kernel's fp32 h, for the
+    rows of expert 6 (and the row count of every expert's h)."""
+    m = need_gpu()
+    cfg = get_config(3)
+    log("full-size fused h quantizer: generating inputs")
+    inp = make_inputs(cfg)
+    d = inp.to("cuda")
+    out, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", debug_h=True)
+    torch.cuda.synchronize()
+    off = ctx["perm"]["offsets"].cpu().numpy()
     e = 6
-    log(f"  weights of expert {e}")
-    q1, s1 = m.mxfp8_quantize(d.w1[e], axis=0)
-    rc, rs = nm.quantize_mxfp8(inp.w1[e].to(torch.float64).numpy(), axis=1)
-    np.testing.assert_array_equal(q1.cpu().numpy(), rc)
-    np.testing.assert_array_equal(s1.cpu().numpy(), rs)
+    lo, hi = int(off[e]), int(off[e + 1])
+    dbg = ctx["debug"]
+    h32 = dbg["h_f32"][lo:hi].cpu().numpy().astype(np.float64)
+    rc, rs = nm.quantize_mxfp8(h32, axis=1)
+    log(f"  expert {e}: {hi - lo} rows x {cfg.I}")
+    np.testing.assert_array_equal(dbg["h_scales"][lo:hi].cpu().numpy(), rs)
+    np.testing.assert_array_equal(dbg["h_codes"][lo:hi].cpu().numpy(), rc)
+    # the kernel's h against the oracle's for the same expert
+    fw = mlp.forward(inp.x, inp.topk_idx.numpy(), inp.topk_prob, inp.w1, inp.w2, "mxfp8", cfg.x_dtype,
+                     experts=(e,))
+    err = mlp.normwise_rel_err(h32, fw.h[lo:hi])
+    flips = int(np.count_nonzero(nm.quantize_mxfp8(fw.h[lo:hi], axis=1)[0] != rc))
+    log(f"  h fp32 vs fp64 err {err:.2e}; codes differing from Q(fp64 h): {flips} of {rc.size}")
+    assert err < 1e-5
 
 
 @gpu

@@ -302,3 +302,76 @@ def test_backward_matches_scalar_loop(precision):
     np.testing.assert_allclose(bw.dprob, dprob, rtol=1e-6)
     np.testing.assert_allclose(bw.dw1, dw1, rtol=1e-9, atol=1e-15)
     np.testing.assert_allclose(bw.dw2, dw2, rtol=1e-9, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- the tolerance metric
+
+@pytest.mark.parametrize("got,ref,want", [
+    # 3-4-5 triangle: the difference has norm 5, the reference norm 5 / 10 / 5
+    ([0.0, 0.0], [3.0, 4.0], 1.0),
+    ([9.0, 4.0], [6.0, 8.0], 0.5),
+    ([3.0, 4.0], [3.0, 4.0], 0.0),
+    # the denominator is the reference's norm, not the result's
+    ([6.0, 8.0], [3.0, 4.0], 1.0),
+    # 2-D: one Frobenius norm over all entries -- a row with a zero reference row must not give
+    # inf, and the result is not the largest per-row error (5 / 10 = 0.5 in the second row)
+    ([[3.0, 4.0], [0.0, 1.0]], [[3.0, 4.0], [0.0, 0.0]], 0.2),
+    ([[3.0, 4.0], [6.0, 13.0]], [[3.0, 4.0], [6.0, 8.0]], 5.0 / math.sqrt(125.0)),
+    # both zero gives 0, a nonzero result against a zero reference gives inf
+    ([0.0, 0.0, 0.0], [0.0, 0.0, 0.0], 0.0),
+    ([0.0, -2.0], [0.0, 0.0], math.inf),
+])
+def test_normwise_rel_err_hand_values(got, ref, want):
+    """||got - ref||_F / ||ref||_F on values worked out by hand."""
+    v = mlp.normwise_rel_err(np.array(got), np.array(ref))
+    if math.isinf(want):
+        assert math.isinf(v)
+    else:
+        assert v == pytest.approx(want, rel=1e-15, abs=0.0)
+
+
+def test_normwise_rel_err_mixed_precision_inputs():
+    # bf16 values widened to fp32 against an fp64 array: the one entry that differs is off by
+    # 0.5, and the reference's squares sum to 1 + 1 + 4 = 6
+    got = torch.tensor([[1.0, 1.5], [2.0, 0.0]], dtype=torch.bfloat16).float().numpy()
+    ref = np.array([[1.0, 1.0], [2.0, 0.0]])
+    assert mlp.normwise_rel_err(got, ref) == pytest.approx(0.5 / math.sqrt(6.0), rel=1e-15)
+
+
+# ----------------------------------------------------------------------------- token-axis MXFP8 operand
+
+@pytest.mark.parametrize("M", [1, 31, 32, 45, 96])
+def test_col_operand_matches_segment_quantizer(M):
+    """The wgrad operand quantized along the token axis equals the brute-force-pinned
+    column-wise segment quantizer (one segment, its last block zero-padded), decoded."""
+    g = np.random.default_rng(100 + M)
+    a = nm.round_bf16(g.standard_normal((M, 64)) * np.exp2(g.integers(-4, 5, (1, 64))))
+    got = mlp._col_operand(a, "mxfp8")
+    codes, scales = nm.quantize_mxfp8_segments_t(a, [0, M])          # [64, Mpad]
+    deq = nm.dequantize_mxfp8(codes, scales, axis=-1)[:, :M].T
+    np.testing.assert_array_equal(got, deq)
+    np.testing.assert_array_equal(got, nm.fake_quant_mxfp8_segments(a, [0, M]))
+    # bf16 leaves the operand alone
+    np.testing.assert_array_equal(mlp._col_operand(a, "bf16"), a)
+
+
+def test_mxfp8_backward_wgrad_uses_segmented_operands():
+    """dW of the MXFP8 backward equals the product of the whole layer's column-wise segmented
+    operands (every expert's rows a segment of the permuted token axis)."""
+    inp = tiny(T=40, H=32, I=32, E=3, k=2, seed=23)
+    idx = inp.topk_idx.numpy()
+    fw = mlp.forward(inp.x, idx, inp.topk_prob, inp.w1, inp.w2, "mxfp8", "bf16")
+    bw = mlp.backward(fw, inp.x, inp.dy, inp.w1, inp.w2)
+    off = fw.perm.offsets
+    tok = fw.perm.token_of_row
+    xs = nm.round_bf16(mlp.f64(inp.x)[tok])
+    dz = nm.round_bf16(mlp.f64(inp.dy)[tok])
+    hs = nm.round_bf16(fw.h)
+    dgu_q = nm.fake_quant_mxfp8_segments(bw.dgu, off)
+    x_q = nm.fake_quant_mxfp8_segments(xs, off)
+    dz_q = nm.fake_quant_mxfp8_segments(dz, off)
+    h_q = nm.fake_quant_mxfp8_segments(hs, off)
+    for e in range(3):
+        lo, hi = int(off[e]), int(off[e + 1])
+        np.testing.assert_allclose(bw.dw1[e], dgu_q[lo:hi].T @ x_q[lo:hi], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(bw.dw2[e], dz_q[lo:hi].T @ h_q[lo:hi], rtol=1e-12, atol=1e-14)
