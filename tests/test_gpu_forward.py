@@ -158,7 +158,9 @@ def test_fused_h_quantizer_bytes(name, cfg, counts):
     oc, _ = nm.quantize_mxfp8(ref.h, axis=1)
     flips = int(np.count_nonzero(oc != codes))
     log(f"  bytes equal; h fp32 vs fp64 err {err:.2e}; codes differing from Q(fp64 h): {flips} of {codes.size}")
-    assert err < 1e-5
+    # fp32 accumulation and the hardware exp / reciprocal against fp64: ~1e-5 relative here; a wrong
+    # side output would be off by O(1)
+    assert err < 1e-3
 
 
 @gpu
