@@ -59,10 +59,10 @@ def test_fullsize_forward(ci, experts, prec):
     assert err < tol
 
 
-def _finegrained_sample(idx, E, T, extra=320, seed=0):
+def _finegrained_sample(idx, E, T, total=512, seed=0):
     """Tokens whose outputs are compared for the 64-expert layer: for every expert, the tokens of
     the first row of its segment, of the first row of its last 256-row tile and of its last row
-    (rows in a segment ascend with the token index), plus `extra` random tokens."""
+    (rows in a segment ascend with the token index), topped up with random tokens to `total`."""
     ref = oracle_permute(idx, E)
     toks = set()
     for e in range(E):
@@ -74,7 +74,7 @@ def _finegrained_sample(idx, E, T, extra=320, seed=0):
             toks.add(int(ref.token_of_row[r]))
     g = np.random.default_rng(seed)
     rest = np.setdiff1d(np.arange(T), np.array(sorted(toks)))
-    toks.update(int(t) for t in g.choice(rest, size=extra, replace=False))
+    toks.update(int(t) for t in g.choice(rest, size=max(0, total - len(toks)), replace=False))
     return sorted(toks)
 
 
