@@ -185,6 +185,34 @@ moe_status moe_permute(const void* x, int x_dtype, int64_t T, int64_t H,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same outputs, bit for bit, with no workspace
+ * argument.  Its index scratch (error flag, per-block expert counts and
+ * bases) is a fixed device array of MOE_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends; nothing is
+ * allocated by this call (no hipMalloc, no library allocation).
+ *
+ * Arguments as moe_permute, without workspace / workspace_bytes, plus
+ * error_flag: optional device int32 that receives the bad-expert-id flag (0
+ * or 1); NULL leaves it in the shared scratch only.
+ * Limit: moe_permute_workspace_size(T, k, E) <= MOE_NOALLOC_SCRATCH_BYTES
+ * (e.g. T <= 130752 tokens at E = 256, T <= 520k at E = 64), else
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  `stream` must belong to
+ * the current device (else MOE_ERR_INVALID_ARG).
+ * Every call on one GPU shares that GPU's scratch: calls that overlap in time
+ * on one GPU (different streams, or host threads) race and must be
+ * serialized by the caller.  Each call writes every scratch word it reads, so
+ * nothing needs clearing between calls.
+ * ------------------------------------------------------------------------ */
+#define MOE_NOALLOC_SCRATCH_BYTES (4u << 20)
+moe_status moe_permute_noalloc(const void* x, int x_dtype, int64_t T, int64_t H,
+                               const int32_t* topk_idx, const float* topk_prob, int k, int E,
+                               int perm_dtype, void* x_perm, uint8_t* x_perm_scales,
+                               int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                               int32_t* src_index, float* prob_perm, int32_t* error_flag, void* stream);
+
+/* ------------------------------------------------------------------------
  * moe_route_topk -- the top-k router ahead of the permutation (page "BioNeMo
  * Uses Grouped Kernels and MXFP8", Figure 1: each token goes to k experts
  * whose outputs are combined with the routing weights).

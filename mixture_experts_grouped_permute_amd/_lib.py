@@ -28,8 +28,9 @@ EXPORTS = (
     "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
     "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop", "fp8_tensor_quantize_workspace",
-    "fp8_tensor_quantize", "mxfp8_quantize_weights",
+    "fp8_tensor_quantize", "mxfp8_quantize_weights", "moe_permute_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 4 << 20    # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -104,6 +105,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_permute.restype = ctypes.c_int
     lib.moe_permute.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_permute_noalloc.restype = ctypes.c_int
+    lib.moe_permute_noalloc.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _vp, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
     lib.moe_grouped_mlp_fwd_workspace.restype = ctypes.c_size_t
     lib.moe_grouped_mlp_fwd_workspace.argtypes = [ctypes.POINTER(FwdArgs)]
     lib.moe_grouped_mlp_fwd.restype = ctypes.c_int
@@ -314,6 +318,41 @@ def moe_permute(x: Optional[torch.Tensor], topk_idx: torch.Tensor, topk_prob: Op
     _check(st, "moe_permute")
     out["workspace"] = ws
     return out
+
+
+def moe_permute_noalloc(x: Optional[torch.Tensor], topk_idx: torch.Tensor, topk_prob: Optional[torch.Tensor],
+                        E: int, perm_dtype: str = "bf16", out: Optional[dict] = None):
+    """moe_permute through the entry point that allocates nothing (its index scratch is the
+    library's fixed device array).  `out`: optional dict of preallocated output tensors with
+    moe_permute's keys plus "error_flag" (int32 [1]); missing ones are allocated here, by torch,
+    before the call.  Returns the dict."""
+    lib = load()
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    _check_routing(topk_idx, topk_prob, dev)
+    R = T * k
+    res = dict(out) if out is not None else {}
+    for key, t in _perm_outputs(T, k, E, dev, topk_prob is not None).items():
+        res.setdefault(key, t)
+    res.setdefault("error_flag", torch.zeros(1, dtype=torch.int32, device=dev))
+    H = 0
+    pd = _compute(perm_dtype)
+    if x is not None:
+        H = x.shape[1]
+        if pd == MOE_BF16:
+            res.setdefault("x_perm", torch.empty((R, H), dtype=torch.bfloat16, device=dev))
+        else:
+            res.setdefault("x_perm", torch.empty((R, H), dtype=torch.uint8, device=dev))
+            res.setdefault("x_perm_scales", torch.empty((R, H // 32), dtype=torch.uint8, device=dev))
+    res.setdefault("x_perm", None)
+    res.setdefault("x_perm_scales", None)
+    st = lib.moe_permute_noalloc(_ptr(x), _io(x) if x is not None else MOE_BF16, T, H, _ptr(topk_idx),
+                                 _ptr(topk_prob), k, E, pd, _ptr(res["x_perm"]), _ptr(res["x_perm_scales"]),
+                                 _ptr(res["split_sizes"]), _ptr(res["offsets"]), _ptr(res["row_id_map"]),
+                                 _ptr(res["src_index"]), _ptr(res["prob_perm"]), _ptr(res["error_flag"]),
+                                 _stream(dev))
+    _check(st, "moe_permute_noalloc")
+    return res
 
 
 def moe_route_topk(logits: torch.Tensor, k: int):

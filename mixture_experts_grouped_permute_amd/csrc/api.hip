@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe.h"
 #include "common.h"
 #include "kernels.h"
@@ -331,6 +333,43 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   return MOE_OK;
 }
 
+// Host-side checks of a permutation call (nothing enqueued).
+moe_status check_permute(const void* x, int x_dtype, int64_t T, int64_t H, const int32_t* topk_idx,
+                         const float* topk_prob, int k, int E, int perm_dtype, const void* x_perm,
+                         const uint8_t* x_perm_scales, const int32_t* split_sizes, const int32_t* offsets,
+                         const int32_t* row_id_map, const int32_t* src_index, const float* prob_perm) {
+  moe_status s = check_common(T, x_perm ? H : 1, E, k);
+  if (s != MOE_OK) return s;
+  MOE_CHECK(topk_idx && split_sizes && offsets && row_id_map && src_index, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(!prob_perm || topk_prob, MOE_ERR_INVALID_ARG);
+  MOE_CHECK(perm_dtype == MOE_BF16 || perm_dtype == MOE_MXFP8_E4M3, MOE_ERR_INVALID_ARG);
+  if (x_perm) {
+    MOE_CHECK(x && io_ok(x_dtype), MOE_ERR_INVALID_ARG);
+    MOE_CHECK(H % 32 == 0, MOE_ERR_UNSUPPORTED);
+    if (perm_dtype == MOE_MXFP8_E4M3) MOE_CHECK(x_perm_scales != nullptr, MOE_ERR_INVALID_ARG);
+  }
+  return MOE_OK;
+}
+
+// The permutation's launches with the index scratch carved from `ws` (error_flag: where the
+// bad-id flag goes instead of the scratch's first word, or nullptr).
+moe_status permute_launch(const void* x, int x_dtype, int64_t T, int64_t H, const int32_t* topk_idx,
+                          const float* topk_prob, int k, int E, int perm_dtype, void* x_perm,
+                          uint8_t* x_perm_scales, int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
+                          int32_t* src_index, float* prob_perm, void* ws, int32_t* error_flag, hipStream_t st) {
+  Carver c(ws);
+  PermWs w = carve_perm(c, T, E);
+  if (error_flag) w.err = error_flag;
+  HIP_TRY(launch_permute_indices(topk_idx, topk_prob, T, k, E, split_sizes, offsets, row_id_map, src_index,
+                                 prob_perm, w.err, w.block_counts, w.block_base, st));
+  if (x_perm)
+    HIP_TRY(launch_permute_rows(x, x_dtype == MOE_F32, T, H, k, row_id_map, x_perm, x_perm_scales,
+                                perm_dtype == MOE_MXFP8_E4M3, st));
+  return MOE_OK;
+}
+
+constexpr int kMaxDevices = 64;
+
 }  // namespace
 
 extern "C" {
@@ -416,27 +455,61 @@ moe_status moe_permute(const void* x, int x_dtype, int64_t T, int64_t H, const i
                        uint8_t* x_perm_scales, int32_t* split_sizes, int32_t* offsets, int32_t* row_id_map,
                        int32_t* src_index, float* prob_perm, void* workspace, size_t workspace_bytes,
                        void* stream) {
-  moe_status s = check_common(T, x_perm ? H : 1, E, k);
+  moe_status s = check_permute(x, x_dtype, T, H, topk_idx, topk_prob, k, E, perm_dtype, x_perm, x_perm_scales,
+                               split_sizes, offsets, row_id_map, src_index, prob_perm);
   if (s != MOE_OK) return s;
-  MOE_CHECK(topk_idx && split_sizes && offsets && row_id_map && src_index, MOE_ERR_INVALID_ARG);
-  MOE_CHECK(!prob_perm || topk_prob, MOE_ERR_INVALID_ARG);
-  MOE_CHECK(perm_dtype == MOE_BF16 || perm_dtype == MOE_MXFP8_E4M3, MOE_ERR_INVALID_ARG);
-  if (x_perm) {
-    MOE_CHECK(x && io_ok(x_dtype), MOE_ERR_INVALID_ARG);
-    MOE_CHECK(H % 32 == 0, MOE_ERR_UNSUPPORTED);
-    if (perm_dtype == MOE_MXFP8_E4M3) MOE_CHECK(x_perm_scales != nullptr, MOE_ERR_INVALID_ARG);
-  }
   const size_t need = moe_permute_workspace_size(T, k, E);
   MOE_CHECK(workspace && workspace_bytes >= need, MOE_ERR_WORKSPACE);
+  return permute_launch(x, x_dtype, T, H, topk_idx, topk_prob, k, E, perm_dtype, x_perm, x_perm_scales,
+                        split_sizes, offsets, row_id_map, src_index, prob_perm, workspace, nullptr,
+                        reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- the allocation-free permutation: its index scratch (the error flag, per-block expert
+// counts and bases) is this file-scope device array instead of a workspace.  Every GPU the
+// library runs on holds its own copy until the process ends; host code never passes the array's
+// name to a kernel (on the host it only stands in for the symbol) but the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (nullptr on failure).
+void* scratch_ptr(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+moe_status moe_permute_noalloc(const void* x, int x_dtype, int64_t T, int64_t H, const int32_t* topk_idx,
+                               const float* topk_prob, int k, int E, int perm_dtype, void* x_perm,
+                               uint8_t* x_perm_scales, int32_t* split_sizes, int32_t* offsets,
+                               int32_t* row_id_map, int32_t* src_index, float* prob_perm, int32_t* error_flag,
+                               void* stream) {
+  moe_status s = check_permute(x, x_dtype, T, H, topk_idx, topk_prob, k, E, perm_dtype, x_perm, x_perm_scales,
+                               split_sizes, offsets, row_id_map, src_index, prob_perm);
+  if (s != MOE_OK) return s;
+  // the scratch holds a fixed number of bytes: larger index problems are refused up front
+  MOE_CHECK(moe_permute_workspace_size(T, k, E) <= (size_t)MOE_NOALLOC_SCRATCH_BYTES, MOE_ERR_UNSUPPORTED);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  Carver c(workspace);
-  PermWs w = carve_perm(c, T, E);
-  HIP_TRY(launch_permute_indices(topk_idx, topk_prob, T, k, E, split_sizes, offsets, row_id_map, src_index,
-                                 prob_perm, w.err, w.block_counts, w.block_base, st));
-  if (x_perm)
-    HIP_TRY(launch_permute_rows(x, x_dtype == MOE_F32, T, H, k, row_id_map, x_perm, x_perm_scales,
-                                perm_dtype == MOE_MXFP8_E4M3, st));
-  return MOE_OK;
+  int dev = -1, sdev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (st) {
+    HIP_TRY(hipStreamGetDevice(st, &sdev));
+    MOE_CHECK(sdev == dev, MOE_ERR_INVALID_ARG);   // the stream must belong to the current device
+  }
+  void* ws = scratch_ptr(dev);
+  MOE_CHECK(ws != nullptr, MOE_ERR_HIP);
+  return permute_launch(x, x_dtype, T, H, topk_idx, topk_prob, k, E, perm_dtype, x_perm, x_perm_scales,
+                        split_sizes, offsets, row_id_map, src_index, prob_perm, ws, error_flag, st);
 }
 
 moe_status moe_route_topk(const void* logits, int logits_dtype, int64_t T, int E, int k, int32_t* topk_idx,

@@ -248,3 +248,19 @@ def test_bwd_cached_transposed_weight_validation(lib):
     assert lib.moe_grouped_mlp_bwd(ctypes.byref(args(w1tq=0x2000)), None) == MOE_ERR_INVALID_ARG
     bf = args(compute=1, w1tq=0x2000, w1ts=0x2000, w2tq=0x2000, w2ts=0x2000)
     assert lib.moe_grouped_mlp_bwd(ctypes.byref(bf), None) == MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_permute_limit_on_host(lib):
+    """moe_permute_noalloc refuses problems beyond its fixed scratch before any HIP call."""
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_UNSUPPORTED, MOE_ERR_INVALID_ARG, NOALLOC_SCRATCH_BYTES
+    lib.moe_permute_workspace_size.restype = ctypes.c_size_t
+    lib.moe_permute_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+    assert lib.moe_permute_workspace_size(130752, 2, 256) <= NOALLOC_SCRATCH_BYTES
+    assert lib.moe_permute_workspace_size(130753, 2, 256) > NOALLOC_SCRATCH_BYTES
+    f = lib.moe_permute_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int, ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 9
+    p = 0x1000
+    assert f(None, 1, 130753, 0, p, None, 2, 256, 1, None, None, p, p, p, p, None, None, None) == MOE_ERR_UNSUPPORTED
+    assert f(None, 1, 16, 0, p, None, 5, 4, 1, None, None, p, p, p, p, None, None, None) == MOE_ERR_INVALID_ARG
