@@ -64,8 +64,17 @@ def _traffic(kernel_key):
     return ent.get("bytes_per_launch")
 
 
-def _time_ex(lib, hip, call_ex, nph, steps, warmup):
-    """Run call_ex(events) warmup + steps times; returns (host ms/step, mean phase ms)."""
+def _stats(xs):
+    """median, p10 and p90 of a list of floats (nearest-rank)."""
+    ys = sorted(xs)
+    pick = lambda q: ys[min(len(ys) - 1, max(0, int(round(q * (len(ys) - 1)))))]
+    return {"median": round(pick(0.5), 4), "p10": round(pick(0.1), 4), "p90": round(pick(0.9), 4)}
+
+
+def _time_ex(lib, hip, call_ex, nph, steps, warmup, flush=None):
+    """Run call_ex(events) warmup + steps times.  Returns (host ms/step, per-step list of phase ms,
+    per-step GPU ms from the first to the last event).  flush(): run before every timed step (outside
+    its events, on the same stream) to evict the caches; the host time then includes it."""
     import torch
     ev = []
     for _ in range(steps * (nph + 1)):
@@ -77,24 +86,37 @@ def _time_ex(lib, hip, call_ex, nph, steps, warmup):
     for _ in range(warmup):
         call_ex(None)
     torch.cuda.synchronize()
-    _log(f"timing {steps} steps")
+    _log(f"timing {steps} steps" + (" (cold caches)" if flush else ""))
     t0 = time.perf_counter()
     for s in range(steps):
+        if flush is not None:
+            flush()
         call_ex(arrays[s])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     f = ctypes.c_float()
-    sums = [0.0] * nph
+    per_step, step_ms = [], []
     for s in range(steps):
+        row = []
         for i in range(nph):
             hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(arrays[s][i]), ctypes.c_void_p(arrays[s][i + 1]))
-            sums[i] += f.value
+            row.append(f.value)
+        per_step.append(row)
+        hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(arrays[s][0]), ctypes.c_void_p(arrays[s][nph]))
+        step_ms.append(f.value)
     for e in ev:
         hip.hipEventDestroy(ctypes.c_void_p(e))
-    return (t1 - t0) * 1e3 / steps, [x / steps for x in sums]
+    return (t1 - t0) * 1e3 / steps, per_step, step_ms
 
 
-def run_gpu(cfg, steps, warmup, backward=False, cached=False):
+def _flusher():
+    """A 1 GiB write between timed steps: more than the 256 MB Infinity Cache and the L2s."""
+    import torch
+    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    return lambda: buf.fill_(1.0)
+
+
+def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0):
     import torch
     import mixture_experts_grouped_permute_amd as m
     from mixture_experts_grouped_permute_amd import _lib as L
@@ -152,10 +174,21 @@ def run_gpu(cfg, steps, warmup, backward=False, cached=False):
 
         def call(evs):
             L._check(lib.moe_grouped_mlp_bwd_ex(ctypes.byref(a), stream, evs), "bwd")
-    ms, ph = _time_ex(lib, hip, call, nph, steps, warmup)
-    split = perm["split_sizes"].cpu().tolist()
+    ms, per_step, step_ms = _time_ex(lib, hip, call, nph, steps, warmup)
+    mean = [sum(r[i] for r in per_step) / len(per_step) for i in range(nph)]
+    res = {"ms_per_step": ms, "phase_ms": dict(zip(names, mean)),
+           "stats": {"step_gpu_ms": _stats(step_ms),
+                     "phase_ms": {n: _stats([r[i] for r in per_step]) for i, n in enumerate(names)}}}
+    if cold_steps:
+        fl = _flusher()
+        _, cold_ph, cold_step = _time_ex(lib, hip, call, nph, cold_steps, 1, flush=fl)
+        del fl
+        res["cold"] = {"step_gpu_ms": _stats(cold_step),
+                       "phase_ms": {n: _stats([r[i] for r in cold_ph]) for i, n in enumerate(names)}}
+    res["split_sizes"] = perm["split_sizes"].cpu().tolist()
+    res["inputs"] = inp
     del keep
-    return {"ms_per_step": ms, "phase_ms": dict(zip(names, ph)), "split_sizes": split, "inputs": inp}
+    return res
 
 
 def gemm_roofline(cfg, phase_ms, phase, flops, kernel):
@@ -174,38 +207,97 @@ def fc1_roofline(cfg, phase_ms):
                          "fwd_gemm_kernel (FC1 gate-up + ScaledSwiGLU*prob)")
 
 
-def fwd_leg(cfg, steps, warmup):
-    r = run_gpu(cfg, steps, warmup)
-    ms = r["ms_per_step"]
-    ph = r["phase_ms"]
-    hbm = {}
+def mem_bytes(cfg, split_sizes):
+    """Algorithmic bytes per launch of the forward's memory-bound phases: read-once inputs plus
+    written outputs plus index metadata."""
     R, H, I, E = cfg.R, cfg.H, cfg.I, cfg.E
     esz = 4 if cfg.x_dtype == "f32" else 2
     op = 1 + 1 / 32 if cfg.precision == "mxfp8" else 2
     if cfg.precision == "fp8":
         # bf16 rows written, then read by the amax and the quantize pass, codes written
         op = 2 + 2 + 2 + 1
-    # algorithmic bytes: read X once, write T*k permuted operand rows (+ index metadata)
-    hbm["permute_rows"] = (cfg.T * H * esz + R * H * op) / (ph["permute_rows"] * 1e-3) / 1e9
+    b = {"permute_rows": cfg.T * H * esz + R * H * op + R * 4}
     zsz = 2 if cfg.x_dtype == "bf16" else 4
-    hbm["combine"] = (R * H * zsz + cfg.T * H * esz + R * 4) / (ph["combine"] * 1e-3) / 1e9
+    b["combine"] = R * H * zsz + cfg.T * H * esz + R * 4
     if cfg.precision == "mxfp8":
-        nz = sum(1 for c in r["split_sizes"] if c > 0)
-        hbm["quant_w1"] = nz * 2 * I * H * (2 + 1 + 1 / 32) / (ph["quant_w1"] * 1e-3) / 1e9
-        hbm["quant_w2"] = nz * H * I * (2 + 1 + 1 / 32) / (ph["quant_w2"] * 1e-3) / 1e9
+        nz = sum(1 for c in split_sizes if c > 0)
+        b["quant_w1"] = nz * 2 * I * H * (2 + 1 + 1 / 32)
+        b["quant_w2"] = nz * H * I * (2 + 1 + 1 / 32)
     if cfg.precision == "fp8":
         # two passes over every bf16 weight (amax, then quantize) and the codes written
-        hbm["quant_w1"] = E * 2 * I * H * (2 + 2 + 1) / (ph["quant_w1"] * 1e-3) / 1e9
-        hbm["quant_w2"] = E * H * I * (2 + 2 + 1) / (ph["quant_w2"] * 1e-3) / 1e9
-    return r, {
+        b["quant_w1"] = E * 2 * I * H * (2 + 2 + 1)
+        b["quant_w2"] = E * H * I * (2 + 2 + 1)
+    return b
+
+
+def fwd_leg(cfg, steps, warmup, cold_steps=5, copy_ceiling=None):
+    r = run_gpu(cfg, steps, warmup, cold_steps=cold_steps)
+    ms = r["ms_per_step"]
+    ph = r["phase_ms"]
+    R, H, I = cfg.R, cfg.H, cfg.I
+    mb = mem_bytes(cfg, r["split_sizes"])
+    hbm = {k_: v / (ph[k_] * 1e-3) / 1e9 for k_, v in mb.items()}
+    memory = {}
+    for k_, v in mb.items():
+        warm = r["stats"]["phase_ms"][k_]["median"]
+        ent = {"bytes_per_launch": int(v), "warm_median_ms": warm, "warm_GBs": round(v / (warm * 1e-3) / 1e9, 1),
+               "frac_of_8TBs_warm": round(v / (warm * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)}
+        if "cold" in r:
+            cold = r["cold"]["phase_ms"][k_]["median"]
+            ent.update({"cold_median_ms": cold, "cold_GBs": round(v / (cold * 1e-3) / 1e9, 1),
+                        "frac_of_8TBs_cold": round(v / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
+        if copy_ceiling:
+            ent["frac_of_copy_warm"] = round(ent["warm_GBs"] / copy_ceiling, 3)
+        memory[k_] = ent
+    out = {
         "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
         "tflops": round(cfg.fwd_flops() / (ms * 1e-3) / 1e12, 1),
         "roofline": fc1_roofline(cfg, ph),
         "fc2_tflops": round(2.0 * R * H * I / (ph["fc2_down"] * 1e-3) / 1e12, 1),
         "hbm_GBs": {k_: round(v, 1) for k_, v in hbm.items()},
+        "memory_kernels": memory,
         "phase_ms": {k_: round(v, 4) for k_, v in ph.items()},
+        "stats": r["stats"],
         "split_sizes": r["split_sizes"],
     }
+    if "cold" in r:
+        out["cold"] = r["cold"]
+    return r, out
+
+
+def copy_leg(reps=10):
+    """The practical HBM ceiling on this GPU: device-to-device copies (read + write), a read-only
+    pass and a write-only fill of 512 MiB and 2 GiB, warm (back to back) and cold (a 1 GiB flush
+    before each), HIP-event timed, median over reps.  GB/s count every byte read and written."""
+    import torch
+    fl = _flusher()
+    res = {}
+    for mib in (512, 2048):
+        n = mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        b = torch.empty_like(a)
+        kinds = {"copy": (lambda: b.copy_(a), 2 * n * 4), "read": (lambda: a.sum(), n * 4),
+                 "write": (lambda: b.fill_(2.0), n * 4)}
+        for kind, (f, nbytes) in kinds.items():
+            for cold in (False, True):
+                f()
+                torch.cuda.synchronize()
+                ts = []
+                for _ in range(reps):
+                    if cold:
+                        fl()
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    f()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1))
+                med = _stats(ts)["median"]
+                res[f"{kind}_{mib}MiB_{'cold' if cold else 'warm'}_GBs"] = round(nbytes / (med * 1e-3) / 1e9, 1)
+        del a, b
+    del fl
+    torch.cuda.empty_cache()
+    return res
 
 
 def bwd_leg(cfg, steps, warmup):
@@ -224,6 +316,7 @@ def bwd_leg(cfg, steps, warmup):
         "roofline": gemm_roofline(cfg, ph, dom, gem[dom], f"bwd_gemm_kernel ({dom})"),
         "gemm_tflops": {k_: round(v / (ph[k_] * 1e-3) / 1e12, 1) for k_, v in gem.items()},
         "phase_ms": {k_: round(v, 4) for k_, v in ph.items()},
+        "stats": r["stats"],
     }
 
 
@@ -338,6 +431,16 @@ def cpu_baseline(inp, cfg, tokens, min_seconds=12.0, max_passes=8):
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
         threads = 1
+    cores = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     xs = inp.x[:tokens]
     idx = inp.topk_idx[:tokens].numpy()
     pr = inp.topk_prob[:tokens]
@@ -347,10 +450,11 @@ def cpu_baseline(inp, cfg, tokens, min_seconds=12.0, max_passes=8):
         mlp.forward(xs, idx, pr, inp.w1, inp.w2, cfg.precision, cfg.x_dtype)
         dt += time.perf_counter() - t0
         passes += 1
-    return {"value": round(passes * tokens / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(passes * tokens / dt, 2), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "cpu_model": model, "blas_threads": int(threads),
             "sample": f"{passes} passes over the first {tokens} of {cfg.T} tokens of the same workload, all "
-                      f"{cfg.E} experts' full weights (fp64 numpy per-expert loop, {threads} BLAS threads), "
-                      f"{dt:.1f} s in total"}
+                      f"{cfg.E} experts' full weights (fp64 numpy per-expert loop, {threads} BLAS threads on "
+                      f"{cores} cores available to the process), {dt:.1f} s in total"}
 
 
 def main():
@@ -362,8 +466,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--legs", default="bf16,mxfp8,mxfp8_finegrained,fp8,backward,backward_mxfp8,router,loop",
-                    help="comma list of bf16, mxfp8, mxfp8_finegrained, fp8, backward, backward_mxfp8, router, "
+    ap.add_argument("--legs", default="copy,bf16,mxfp8,mxfp8_finegrained,fp8,backward,backward_mxfp8,router,loop",
+                    help="comma list of copy, bf16, mxfp8, mxfp8_finegrained, fp8, backward, backward_mxfp8, router, "
                          "loop (bf16 always runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
@@ -384,8 +488,13 @@ def main():
         sys.exit(2)
     from moe_inputs import get_config
 
+    copy = None
+    if "copy" in legs:
+        _log("timing the copy ceiling")
+        copy = copy_leg()
+    ceiling = copy["copy_2048MiB_warm_GBs"] if copy else None
     cfg = get_config(2)
-    r, leg = fwd_leg(cfg, args.steps, args.warmup)
+    r, leg = fwd_leg(cfg, args.steps, args.warmup, copy_ceiling=ceiling)
     ms = leg["ms_per_step"]
     line = {
         "metric": METRIC, "value": leg["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -396,8 +505,11 @@ def main():
                    "T": cfg.T, "H": cfg.H, "I": cfg.I, "E": cfg.E, "top_k": cfg.k, "parallelism": "none (1 GPU)"},
         "tflops": leg["tflops"], "roofline": leg["roofline"],
         "fc2_tflops": leg["fc2_tflops"], "hbm_GBs": leg["hbm_GBs"],
-        "phase_ms": leg["phase_ms"], "split_sizes": leg["split_sizes"],
+        "phase_ms": leg["phase_ms"], "stats": leg["stats"], "cold": leg.get("cold"),
+        "memory_kernels": leg["memory_kernels"], "split_sizes": leg["split_sizes"],
     }
+    if copy:
+        line["copy_ceiling"] = copy
     if not args.no_cpu_baseline:
         _log(f"timing the CPU oracle on {args.cpu_tokens} tokens")
         line["cpu_baseline"] = cpu_baseline(r["inputs"], cfg, args.cpu_tokens)
@@ -409,7 +521,7 @@ def main():
                 continue
             torch.cuda.empty_cache()
             c = get_config(ci)
-            rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2))
+            rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2), copy_ceiling=ceiling)
             del rr
             torch.cuda.empty_cache()
             rc = run_gpu(c, max(2, args.steps // 2), max(1, args.warmup // 2), cached=True)
@@ -424,7 +536,7 @@ def main():
         if "fp8" in legs:
             torch.cuda.empty_cache()
             c = get_config(3).with_(precision="fp8")
-            rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2))
+            rr, lg = fwd_leg(c, max(2, args.steps // 2), max(1, args.warmup // 2), copy_ceiling=ceiling)
             del rr
             torch.cuda.empty_cache()
             rc = run_gpu(c, max(2, args.steps // 2), max(1, args.warmup // 2), cached=True)

@@ -760,9 +760,11 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
     return !events || hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) == hipSuccess;
   };
 
-  // dz = bf16(dy) gathered into expert order
+  // dz = bf16(dy) gathered into expert order.  MXFP8 with bf16 dy needs dz only as the two
+  // quantized operands, which are made from dy directly (below): no gather.
+  const bool dz_direct = mx && !io_f32;
   MOE_CHECK(mark(0), MOE_ERR_HIP);
-  HIP_TRY(launch_gather_rows(a->dy, io_f32, R, H, k, a->src_index, a->offsets, E, p.dz, st));
+  if (!dz_direct) HIP_TRY(launch_gather_rows(a->dy, io_f32, R, H, k, a->src_index, a->offsets, E, p.dz, st));
   MOE_CHECK(mark(1), MOE_ERR_HIP);
 
   // ---- FC2 dgrad with the ScaledSwiGLU backward epilogue -> dgu, dprob partials
@@ -775,7 +777,9 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   d2.dprob_part = p.dprob_part;
   d2.I = I;
   if (mx) {
-    HIP_TRY(launch_mx_quant_rows(p.dz, false, R, H, p.dzq, p.dzs, st));
+    // dz along H: each token's dy row quantized once and written to its k permuted rows
+    if (dz_direct) HIP_TRY(launch_permute_rows(a->dy, false, T, H, k, a->row_id_map, p.dzq, p.dzs, true, st));
+    else HIP_TRY(launch_mx_quant_rows(p.dz, false, R, H, p.dzq, p.dzs, st));
     // W2_e^T along H for every expert with tokens, one launch (unless cached by the caller)
     if (!a->w2tq) HIP_TRY(launch_mx_quant_weights_t(a->w2, E, H, I, p.w2tq, p.w2ts, a->split_sizes, st));
     d2.a = p.dzq; d2.lda = H; d2.a_scales = p.dzs; d2.ldas = H / 32;
@@ -796,7 +800,11 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   w2.out_f32 = dw_f32;
   if (mx) {
     const int64_t Rp = p.rows_pad;
-    HIP_TRY(launch_mx_quant_cols(p.dz, false, R, H, a->offsets, E, Rp, p.dzT, p.dzTs, st, 128));
+    // dz along tokens, per expert segment (dy rows through src_index when dz was not gathered)
+    if (dz_direct)
+      HIP_TRY(launch_mx_quant_cols(a->dy, false, R, H, a->offsets, E, Rp, p.dzT, p.dzTs, st, 128, a->src_index, k));
+    else
+      HIP_TRY(launch_mx_quant_cols(p.dz, false, R, H, a->offsets, E, Rp, p.dzT, p.dzTs, st, 128));
     HIP_TRY(launch_mx_quant_cols(a->saved_h, false, R, I, a->offsets, E, Rp, p.hT, p.hTs, st, 128));
     w2.a = p.dzT; w2.lda = Rp; w2.a_scales = p.dzTs; w2.ldas = Rp / 32;
     w2.b = p.hT; w2.ldb = Rp; w2.b_scales = p.hTs; w2.ldbs = Rp / 32;

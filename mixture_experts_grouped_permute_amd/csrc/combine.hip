@@ -83,16 +83,27 @@ __global__ __launch_bounds__(256) void gather_kernel(const void* __restrict__ x,
   if (r >= R || r >= offsets[E]) return;
   const int64_t t = src_index[r] / k;
   uint16_t* dst = reinterpret_cast<uint16_t*>(out) + r * H;
-  for (int64_t c = (int64_t)lane * 8; c < H; c += 512) {
-    u32x4 w;
-    if (kF32) {
-      const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * H + c);
-      const float4 a = s4[0], b = s4[1];
-      w = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
-    } else {
-      w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + t * H + c);
+  // four 512-column chunks loaded before any is stored: several loads in flight per lane
+  constexpr int kBatch = 4;
+  for (int64_t c0 = (int64_t)lane * 8; c0 < H; c0 += 512 * kBatch) {
+    u32x4 w[kBatch];
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t c = c0 + 512 * b;
+      if (c >= H) continue;
+      if (kF32) {
+        const float4* s4 = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * H + c);
+        const float4 a = s4[0], d = s4[1];
+        w[b] = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w), pack_bf16x2(d.x, d.y), pack_bf16x2(d.z, d.w)};
+      } else {
+        w[b] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + t * H + c);
+      }
     }
-    *reinterpret_cast<u32x4*>(dst + c) = w;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t c = c0 + 512 * b;
+      if (c < H) *reinterpret_cast<u32x4*>(dst + c) = w[b];
+    }
   }
 }
 

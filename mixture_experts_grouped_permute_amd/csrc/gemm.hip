@@ -80,13 +80,15 @@ struct FwdItem {
   int t, tile, part, e, mt, nt, row0, mrows, u0, u1;
 };
 
-// kDeep (K of at least two stages; MXFP8 also needs K % 512 == 0, so 16-byte scale rows): the stage
-// barrier sits inside the stage and stage loads are issued two stages ahead (mma_stage_mx_deep,
-// mma_stage_bf16_deep).
+// kDeep (K of at least two stages): the stage barrier sits inside the stage and stage loads are
+// issued two stages ahead (mma_stage_mx_deep, mma_stage_bf16_deep).  MXFP8 scale rows of a whole
+// number of 16-byte groups (K % 512 == 0) load a group with one 16-byte load per row; kSc4 (MXFP8
+// deep with other K, e.g. the 44-byte rows of K = 1408) takes the four-lane word form instead, fixed
+// at compile time because no branch may sit among the MFMAs.
 // kPt (with kMx): per-tensor-scaled FP8 -- unit block scales, the per-expert dequantization in
 // the epilogue, and FC1's h written as bf16 (a separate instance, so the MXFP8 epilogue keeps
 // its own code)
-template <bool kMx, bool kFc1, bool kOutF32, bool kDeep, bool kPt = false>
+template <bool kMx, bool kFc1, bool kOutF32, bool kDeep, bool kPt = false, bool kSc4 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void fwd_gemm_kernel(const FwdKArgs p) {
   // 2 pipeline stages, then the MXFP8 scales of groups of 4 stages (2 x 8 KB), then the routing
@@ -191,7 +193,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   //   * otherwise (the scale rows of K = 1408 are 44 bytes): four lanes per row, reading its
   //     consecutive words, which the load merges into one request; load j < 4 of wave w covers
   //     rows 64 w + 16 j + L / 4, lane L's word landing at slot L of a 256-byte block.
-  const bool sc16 = kDeep || (kscale_row & 15u) == 0;
+  const bool sc16 = kDeep ? !kSc4 : (kscale_row & 15u) == 0;
   uint32_t as_vo[4] = {0, 0, 0, 0}, bs_vo[4] = {0, 0, 0, 0};
   if constexpr (kMx) {
 #pragma unroll
@@ -213,8 +215,8 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     dma16(d.vb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q], (uint32_t)kt * kRowBytes);
   };
   // the scales of stage group g (stages 4 g .. 4 g + 3) of the item described by d into buffer sb
-  // (called at a stage's top, outside its MFMAs, except in the deep pipeline, which takes the
-  // 16-byte form only: no branch may sit among the MFMAs)
+  // (called at a stage's top, outside its MFMAs, except in the deep pipeline, where the form is
+  // fixed at compile time: no branch may sit among the MFMAs)
   auto dma_s = [&](const Desc& d, int sb, int g) {
     if constexpr (kMx) {
       const uint32_t ss = lds_sc + (uint32_t)sb * (uint32_t)kScBuf;
@@ -595,6 +597,7 @@ hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st) {
   if (pt && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (pt) fwd_gemm_kernel<true, true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (mx && g.K >= 256 && g.K % 512 == 0) fwd_gemm_kernel<true, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+  else if (mx && g.K >= 256) fwd_gemm_kernel<true, true, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else if (mx) fwd_gemm_kernel<true, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
   else if (g.K >= 128) fwd_gemm_kernel<false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
   else fwd_gemm_kernel<false, true, false, false><<<kGemmGrid, 256, 0, st>>>(k);
@@ -609,37 +612,39 @@ hipError_t launch_fc2(const FwdGemm& g, bool mx, hipStream_t st) {
   const bool split = g.part != nullptr && kU / kMinSplitUnits >= 2;
   // pass 1 (or the only pass): the output-dtype instance
   k.split = split ? 1 : 0;
-  // K of at least two 128-byte stages (and 16-byte scale rows for MXFP8) takes the deep pipeline
-  // (split parts have at least kMinSplitUnits stages)
-  const bool deep = mx ? (g.K >= 256 && g.K % 512 == 0) : g.K >= 128;
+  // K of at least two 128-byte stages takes the deep pipeline (split parts have at least
+  // kMinSplitUnits stages); MXFP8 scale rows that are not whole 16-byte groups take its kSc4 form
+  const bool deep = mx ? g.K >= 256 : g.K >= 128;
+  const bool sc4 = mx && g.K % 512 != 0;
   const bool pt = mx && g.pt_s_a != nullptr;
-  if (pt) {
-    if (g.out_f32 && deep) fwd_gemm_kernel<true, false, true, true, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else if (g.out_f32) fwd_gemm_kernel<true, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else if (deep) fwd_gemm_kernel<true, false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else fwd_gemm_kernel<true, false, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
-  } else if (g.out_f32) {
-    if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
-    else if (deep) fwd_gemm_kernel<false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
-  } else {
-    if (mx && deep) fwd_gemm_kernel<true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else if (mx) fwd_gemm_kernel<true, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
-    else if (deep) fwd_gemm_kernel<false, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
-    else fwd_gemm_kernel<false, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
-  }
-  hipError_t err = hipGetLastError();
+  // the per-tensor FP8 instances keep the deep pipeline to 16-byte scale rows
+  const bool pdeep = deep && !sc4;
+  auto launch = [&](bool out_f32) {
+    if (pt) {
+      if (out_f32 && pdeep) fwd_gemm_kernel<true, false, true, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (out_f32) fwd_gemm_kernel<true, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (pdeep) fwd_gemm_kernel<true, false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else fwd_gemm_kernel<true, false, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+    } else if (out_f32) {
+      if (mx && deep && sc4) fwd_gemm_kernel<true, false, true, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (deep) fwd_gemm_kernel<false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
+    } else {
+      if (mx && deep && sc4) fwd_gemm_kernel<true, false, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (mx && deep) fwd_gemm_kernel<true, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (mx) fwd_gemm_kernel<true, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+      else if (deep) fwd_gemm_kernel<false, false, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else fwd_gemm_kernel<false, false, false, false><<<kGemmGrid, 256, 0, st>>>(k);
+    }
+    return hipGetLastError();
+  };
+  hipError_t err = launch(g.out_f32);
   if (err != hipSuccess || !split) return err;
   // pass 2: the split parts (whether there are any is decided on the device), then the fixup
   k.split = 2;
-  if (pt && deep) fwd_gemm_kernel<true, false, true, true, true><<<kGemmGrid, 256, 0, st>>>(k);
-  else if (pt) fwd_gemm_kernel<true, false, true, false, true><<<kGemmGrid, 256, 0, st>>>(k);
-  else if (mx && deep) fwd_gemm_kernel<true, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
-  else if (mx) fwd_gemm_kernel<true, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
-  else if (deep) fwd_gemm_kernel<false, false, true, true><<<kGemmGrid, 256, 0, st>>>(k);
-  else fwd_gemm_kernel<false, false, true, false><<<kGemmGrid, 256, 0, st>>>(k);
-  err = hipGetLastError();
+  err = launch(true);
   if (err != hipSuccess) return err;
   const dim3 fgrid(kGemmGrid, kBM / 32);
   if (g.out_f32) fc2_fixup_kernel<true><<<fgrid, 256, 0, st>>>(k, kU);

@@ -43,9 +43,12 @@ hipError_t launch_mx_quant_weights_t(const void* const* w, int E, int64_t rows, 
 // Column-wise (blocks along rows, restarted per segment, transposed output); see mxfp8_quantize axis 1.
 // seg_align: segments are padded to a multiple of seg_align rows (32 for the C ABI; 128 when the
 // result feeds the variable-K wgrad GEMM, whose K steps are 128 values).
+// src_index != nullptr: segmented row r is row src_index[r] / src_k of x (x holds token rows; rows is
+// the number of segmented rows).
 hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t cols,
                                 const int32_t* group_offsets, int num_groups, int64_t rows_pad, uint8_t* q,
-                                uint8_t* scales, hipStream_t st, int seg_align = 32);
+                                uint8_t* scales, hipStream_t st, int seg_align = 32,
+                                const int32_t* src_index = nullptr, int src_k = 1);
 
 // Per-tensor FP8 (one fp32 scale per tensor): the row segments [offsets[g], offsets[g+1]) of x
 // [rows, cols] (offsets == nullptr: one segment of all rows), or each of E bf16 weight matrices

@@ -156,58 +156,71 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
 // ---------------------------------------------------------------------------
 // K4: copy each token row once from X and write it to its k permuted rows,
 // rounding to bf16 or quantizing to MXFP8 on the way.  One wave per token;
-// a lane owns 8 consecutive values per step (4 lanes per MXFP8 block).
+// a lane owns 8 consecutive values per 512-column chunk (4 lanes per MXFP8
+// block), and loads kBatch chunks before it converts and stores any, so each
+// lane keeps several 16-byte loads in flight.
 // ---------------------------------------------------------------------------
 template <bool kInF32, bool kMx>
 __global__ __launch_bounds__(256) void perm_rows_kernel(const void* __restrict__ x, int64_t T, int64_t H, int k,
                                                           const int32_t* __restrict__ row_id_map,
                                                           void* __restrict__ out, uint8_t* __restrict__ out_scales) {
+  constexpr int kBatch = 4;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   int rows[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) rows[j] = j < k ? row_id_map[t * k + j] : -1;
-  for (int64_t c0 = 0; c0 < H; c0 += 512) {
-    int64_t c = c0 + lane * 8;
-    if (c >= H) break;   // H % 32 == 0 keeps every MXFP8 block's 4 lanes together
-    float v[8];
-    if (kInF32) {
-      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * H + c);
-      float4 a = src[0], b = src[1];
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-      u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + t * H + c);
+  for (int64_t c0 = 0; c0 < H; c0 += 512 * kBatch) {
+    float v[kBatch][8];
+    // H % 32 == 0 keeps every MXFP8 block's 4 lanes together (all in or all past the end)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
-        v[2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t c = c0 + 512 * b + lane * 8;
+      if (c >= H) continue;
+      if (kInF32) {
+        const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + t * H + c);
+        const float4 a = src[0], d = src[1];
+        v[b][0] = a.x; v[b][1] = a.y; v[b][2] = a.z; v[b][3] = a.w;
+        v[b][4] = d.x; v[b][5] = d.y; v[b][6] = d.z; v[b][7] = d.w;
+      } else {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + t * H + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[b][2 * i] = bf16_to_f32((uint16_t)(w[i] & 0xFFFF));
+          v[b][2 * i + 1] = bf16_to_f32((uint16_t)(w[i] >> 16));
+        }
       }
     }
-    if (!kMx) {
-      u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
+    for (int b = 0; b < kBatch; ++b) {
+      const int64_t c = c0 + 512 * b + lane * 8;
+      if (c >= H) continue;
+      if (!kMx) {
+        u32x4 o;
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j >= k || rows[j] < 0) continue;
-        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)rows[j] * H + c) = o;
-      }
-    } else {
-      float am = 0.f;
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(v[b][2 * i], v[b][2 * i + 1]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[i]));
-      am = wave_xor_max(am, 1);
-      am = wave_xor_max(am, 2);
-      int s = mx_shared_exp(am);
-      u32x2 o;
-      o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
-      o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j >= k || rows[j] < 0) continue;
+          *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + (int64_t)rows[j] * H + c) = o;
+        }
+      } else {
+        float am = 0.f;
 #pragma unroll
-      for (int j = 0; j < kMaxTopK; ++j) {
-        if (j >= k || rows[j] < 0) continue;
-        *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(out) + (int64_t)rows[j] * H + c) = o;
-        if ((lane & 3) == 0) out_scales[(int64_t)rows[j] * (H / 32) + c / 32] = (uint8_t)(s + 127);
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(v[b][i]));
+        am = wave_xor_max(am, 1);
+        am = wave_xor_max(am, 2);
+        const int s = mx_shared_exp(am);
+        u32x2 o;
+        o[0] = mx_pack4(v[b][0], v[b][1], v[b][2], v[b][3], s);
+        o[1] = mx_pack4(v[b][4], v[b][5], v[b][6], v[b][7], s);
+#pragma unroll
+        for (int j = 0; j < kMaxTopK; ++j) {
+          if (j >= k || rows[j] < 0) continue;
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(out) + (int64_t)rows[j] * H + c) = o;
+          if ((lane & 3) == 0) out_scales[(int64_t)rows[j] * (H / 32) + c / 32] = (uint8_t)(s + 127);
+        }
       }
     }
   }

@@ -126,12 +126,16 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
 // kernel-argument table; matrices with skip[e] == 0 are left alone), each a single segment with
 // rows % 32 == 0, matrix e's output at q + e * cols * rows_pad and scales + e * cols * rows_pad / 32.
 constexpr int kColRows = 128;   // padded rows per workgroup
+//
+// src_index (optional): row r of the segmented matrix is row src_index[r] / src_k of x (the
+// permuted rows of a token-major x, e.g. the gradient rows of the backward read straight from dY).
 template <bool kF32, bool kTab = false>
 __global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void* __restrict__ x, int64_t rows,
                                                         int64_t cols, const int32_t* __restrict__ goff,
                                                         int num_groups, int64_t rows_pad, uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ scales, int seg_align,
-                                                        const int32_t* __restrict__ skip) {
+                                                        const int32_t* __restrict__ skip,
+                                                        const int32_t* __restrict__ src_index, int src_k) {
   if constexpr (kTab) {
     const int e = blockIdx.z;
     if (skip && skip[e] == 0) return;
@@ -205,6 +209,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void
       const int64_t sr = s_off[lo] + (pr - s_pad[lo]);
       const int64_t end = lo + 1 < num_groups ? min(s_off[lo + 1], (int)rows) : s_off[num_groups];
       if (sr < end && sr < rows) src = (int)sr;
+      if (src >= 0 && src_index) src = src_index[src] / src_k;
     }
     s_src[t] = src;
   }
@@ -416,16 +421,16 @@ hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, in
 
 hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t cols, const int32_t* group_offsets,
                                 int num_groups, int64_t rows_pad, uint8_t* q, uint8_t* scales, hipStream_t st,
-                                int seg_align) {
+                                int seg_align, const int32_t* src_index, int src_k) {
   dim3 grid((unsigned)((rows_pad + kColRows - 1) / kColRows), (unsigned)((cols + 63) / 64));
   if (grid.x == 0) return hipSuccess;
   WTab tab{};
   if (x_f32)
     mx_cols_kernel<true><<<grid, 256, 0, st>>>(tab, x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
-                                               seg_align, nullptr);
+                                               seg_align, nullptr, src_index, src_k);
   else
     mx_cols_kernel<false><<<grid, 256, 0, st>>>(tab, x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
-                                                seg_align, nullptr);
+                                                seg_align, nullptr, src_index, src_k);
   return hipGetLastError();
 }
 
@@ -436,7 +441,7 @@ hipError_t launch_mx_quant_weights_t(const void* const* w, int E, int64_t rows, 
   dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + 63) / 64), (unsigned)E);
   if (grid.x == 0) return hipSuccess;
   mx_cols_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, rows, cols, nullptr, 1, rows, q, scales, 32,
-                                                    skip_if_empty);
+                                                    skip_if_empty, nullptr, 1);
   return hipGetLastError();
 }
 
