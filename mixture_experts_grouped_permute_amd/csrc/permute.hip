@@ -171,6 +171,10 @@ __global__ __launch_bounds__(256) void perm_rows_kernel(const void* __restrict__
   int rows[kMaxTopK];
 #pragma unroll
   for (int j = 0; j < kMaxTopK; ++j) rows[j] = j < k ? row_id_map[t * k + j] : -1;
+  // MXFP8 scale bytes: with H % 128 == 0 (and a 4-byte aligned scale array) every 16-lane group
+  // covers 4 whole blocks and their 4 bytes are 4-byte aligned, so the group's first lane stores
+  // them as one word; otherwise one byte per block
+  const bool pack = ((H / 32) & 3) == 0 && ((reinterpret_cast<uintptr_t>(out_scales) & 3u) == 0);
   for (int64_t c0 = 0; c0 < H; c0 += 512 * kBatch) {
     float v[kBatch][8];
     // H % 32 == 0 keeps every MXFP8 block's 4 lanes together (all in or all past the end)
@@ -215,11 +219,24 @@ __global__ __launch_bounds__(256) void perm_rows_kernel(const void* __restrict__
         u32x2 o;
         o[0] = mx_pack4(v[b][0], v[b][1], v[b][2], v[b][3], s);
         o[1] = mx_pack4(v[b][4], v[b][5], v[b][6], v[b][7], s);
+        // the scale bytes of the 16-lane group's 4 blocks (lanes 16 w + 4 i hold block 4 w + i);
+        // the group is wholly in range here when pack holds
+        uint32_t word = 0;
+        if (pack) {
+          const int g16 = lane & ~15;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) word |= ((uint32_t)(__shfl(s, g16 + 4 * i, 64) + 127) & 0xFFu) << (8 * i);
+        }
 #pragma unroll
         for (int j = 0; j < kMaxTopK; ++j) {
           if (j >= k || rows[j] < 0) continue;
           *reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(out) + (int64_t)rows[j] * H + c) = o;
-          if ((lane & 3) == 0) out_scales[(int64_t)rows[j] * (H / 32) + c / 32] = (uint8_t)(s + 127);
+          uint8_t* sc = out_scales + (int64_t)rows[j] * (H / 32) + c / 32;
+          if (pack) {
+            if ((lane & 15) == 0) *reinterpret_cast<uint32_t*>(sc) = word;
+          } else if ((lane & 3) == 0) {
+            *sc = (uint8_t)(s + 127);
+          }
         }
       }
     }

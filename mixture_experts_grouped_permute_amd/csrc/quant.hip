@@ -53,7 +53,19 @@ __global__ __launch_bounds__(256) void mx_rows_kernel(const void* __restrict__ x
     o[0] = mx_pack4(v[0], v[1], v[2], v[3], s);
     o[1] = mx_pack4(v[4], v[5], v[6], v[7], s);
     *reinterpret_cast<u32x2*>(q + off) = o;
-    if ((threadIdx.x & 3) == 0) scales[off / 32] = (uint8_t)(s + 127);
+    // scale bytes: the blocks of 16 consecutive groups are 4 consecutive bytes, 4-byte aligned in
+    // an aligned array (gi of the group's first lane is a multiple of 16); a group wholly in range
+    // stores them as one word from its first lane, the last partial group one byte per block
+    const int64_t g0 = gi & ~(int64_t)15;
+    if (g0 + 16 <= groups && (reinterpret_cast<uintptr_t>(scales) & 3u) == 0) {
+      const int l16 = (int)(threadIdx.x & 63) & ~15;
+      uint32_t word = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) word |= ((uint32_t)(__shfl(s, l16 + 4 * i, 64) + 127) & 0xFFu) << (8 * i);
+      if ((threadIdx.x & 15) == 0) *reinterpret_cast<uint32_t*>(scales + off / 32) = word;
+    } else if ((threadIdx.x & 3) == 0) {
+      scales[off / 32] = (uint8_t)(s + 127);
+    }
   }
 }
 

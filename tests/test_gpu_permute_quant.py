@@ -18,6 +18,9 @@ ROUTINGS = [
     ("one-expert", cfg_small(T=257, H=64, I=128, E=1, k=1), None),
     ("all-to-one", cfg_small(T=513, H=64, I=128, E=4, k=1), [0, 0, 513, 0]),
     ("tiny-T1", cfg_small(T=1, H=64, I=128, E=4, k=2), None),
+    # H not a multiple of 512 (a partial last chunk), with whole 128-column scale words, and with not
+    ("h384", cfg_small(T=200, H=384, I=128, E=4, k=2), None),
+    ("h160", cfg_small(T=200, H=160, I=128, E=4, k=2), None),
 ]
 
 
@@ -87,10 +90,13 @@ def _quant_inputs():
 
 @gpu
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_mxfp8_quantize_rowwise_bit_exact(dtype):
+# rows x cols / 8 lane groups: a multiple of 16 (scale bytes stored as words), or not (the last
+# partial 16-lane group stores bytes)
+@pytest.mark.parametrize("shape", [(300, 256), (7, 96), (1, 32)])
+def test_mxfp8_quantize_rowwise_bit_exact(dtype, shape):
     m = need_gpu()
-    log(f"mxfp8_quantize axis0 {dtype}")
-    a = torch.from_numpy(_quant_inputs()).to(dtype)
+    log(f"mxfp8_quantize axis0 {dtype} {shape}")
+    a = torch.from_numpy(_quant_inputs()[:shape[0], :shape[1]].copy()).to(dtype)
     q, s = m.mxfp8_quantize(a.cuda(), axis=0)
     rc, rs = nm.quantize_mxfp8(a.to(torch.float64).numpy(), axis=1)
     np.testing.assert_array_equal(q.cpu().numpy(), rc)
