@@ -471,7 +471,31 @@ def main():
                          "loop (bf16 always runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
+    ap.add_argument("--lib-gemm-probe", action="store_true",
+                    help="only time torch.matmul on the gate-up projection's shape as one dense bf16 GEMM "
+                         "(M = T*k = 8192, K = 4096, N = 2*14336), a reference for the MFMA counters")
     args = ap.parse_args()
+    if args.lib_gemm_probe:
+        import torch
+        g = torch.Generator(device="cuda:0").manual_seed(0)
+        a = torch.randn(8192, 4096, device="cuda:0", generator=g).to(torch.bfloat16)
+        b = (torch.randn(4096, 28672, device="cuda:0", generator=g) * 0.02).to(torch.bfloat16)
+        for _ in range(3):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.matmul(a, b)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        med = _stats(ts)["median"]
+        flops = 2.0 * 8192 * 4096 * 28672
+        print(json.dumps({"lib_gemm_probe": "torch.matmul bf16 8192x4096 @ 4096x28672", "median_ms": med,
+                          "tflops": round(flops / (med * 1e-3) / 1e12, 1)}), flush=True)
+        return
     if args.copy_probe:
         import torch
         src = torch.empty(args.copy_probe // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
