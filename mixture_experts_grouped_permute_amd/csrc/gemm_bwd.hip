@@ -69,18 +69,24 @@ struct BwdItem {
   int64_t koff;
 };
 
-template <int kRole, bool kMx, bool kOutF32>
+// kDeep (MXFP8 dgrad, K of at least two stages): the forward's deep MXFP8 pipeline -- the stage
+// barrier between the two MX substeps, stage loads issued two stages ahead, and the E8M0 bytes of
+// four stages loaded together (one 16-byte load per row: K % 512 == 0 for both dgrads).
+template <int kRole, bool kMx, bool kOutF32, bool kDeep = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_gemm_kernel(const BwdKArgs p) {
   constexpr bool kWg = kRole == kRoleWgrad;
   constexpr bool kAMN = kWg && !kMx;   // bf16 wgrad: A is token-major
   constexpr bool kBMN = !kMx;          // bf16: B is N-contiguous (weights in dgrad, activations in wgrad)
   constexpr bool kD2 = kRole == kRoleDgradFc2;
-  // two stages of A + B (64 KB each), the MXFP8 scale words (2 x 2 KB), and for the FC2 dgrad the
-  // routing probabilities of the tile's rows (2 x 1 KB, by work item) and the per-row dprob
-  // partials of the two wave columns (2 x 1 KB)
+  static_assert(!kDeep || (kMx && kRole != kRoleWgrad), "deep pipeline: MXFP8 dgrad only");
+  // two stages of A + B (64 KB each), the MXFP8 scales (2 x 2 KB of one word per row per stage, or
+  // in the deep pipeline 2 x 8 KB of 16 bytes per row per group of four stages), and for the FC2
+  // dgrad the routing probabilities of the tile's rows (2 x 1 KB, by work item) and the per-row
+  // dprob partials of the two wave columns (2 x 1 KB)
   constexpr int kScOff = 2 * kStageBytes;
-  constexpr int kXOff = kScOff + (kMx ? 2 * 2048 : 0);
+  constexpr int kScBuf = kDeep ? 8192 : 2048;
+  constexpr int kXOff = kScOff + (kMx ? 2 * kScBuf : 0);
   __shared__ __attribute__((aligned(16))) uint8_t smem[kXOff + (kD2 ? 4096 : 16)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -219,7 +225,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     bs_vo = (uint32_t)(r * p.ldbs);
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
-  const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * 256u);
+  const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * (kDeep ? 1024u : 256u));
   auto dma_a = [&](const Desc& d, int b, int kt, int q) {
     dma16(d.va, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q] + (uint32_t)kt * a_step, 0);
   };
@@ -227,10 +233,21 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     dma16(d.vb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q] + (uint32_t)kt * b_step, 0);
   };
   auto dma_s = [&](const Desc& d, int b, int kt) {
-    if constexpr (kMx) {
+    if constexpr (kMx && !kDeep) {
       const uint32_t ss = lds_sc + (uint32_t)b * 2048u;
       dma4(d.vas, ss, as_vo + (uint32_t)kt * 4u, 0);
       dma4(d.vbs, ss + 1024u, bs_vo + (uint32_t)kt * 4u, 0);
+    }
+  };
+  // deep pipeline: the scales of stage group g (stages 4 g .. 4 g + 3) into scale buffer sb, row r's
+  // 16 bytes at r * 16 (A rows, then B rows at 4096); predicated by the descriptor (off: no memory
+  // read, zeros written to the buffer, which no pending stage uses)
+  auto dma_sg = [&](const Desc& d, bool on, int sb, int g) {
+    if constexpr (kDeep) {
+      const i32x4 z = make_vsharp(p.a, 0);
+      const uint32_t ss = lds_sc + (uint32_t)sb * (uint32_t)kScBuf;
+      dma16(on ? d.vas : z, ss, as_vo, (uint32_t)g * 16u);
+      dma16(on ? d.vbs : z, ss + 4096u, bs_vo, (uint32_t)g * 16u);
     }
   };
 
@@ -240,6 +257,22 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   descs(cur, dc);
   int par = 0;             // buffer of the current item's first stage
   bool issued = false;     // the current item's first stage was loaded by the previous item
+  int sbc = 0, sbn = 0;    // deep pipeline: scale buffers of the current and the next stage
+  if constexpr (kDeep) {
+    // the first item's first two stages (every dgrad item has at least two)
+    if (cur.t < hi) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { dma_a(dc, 0, cur.u0, q); dma_b(dc, 0, cur.u0, q); }
+      dma_sg(dc, true, 0, cur.u0 >> 2);
+      wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) { dma_a(dc, 1, cur.u0 + 1, q); dma_b(dc, 1, cur.u0 + 1, q); }
+      const bool ng = ((cur.u0 + 1) & 3) == 0;
+      sbn = ng ? 1 : 0;
+      dma_sg(dc, ng, 1, (cur.u0 + 1) >> 2);
+    }
+  }
   for (int round = 0; cur.t < hi; ++round) {
     decode(round + 1, nxt);
     descs(nxt, dn);
@@ -248,6 +281,39 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const float pr = tid < cur.mrows ? p.prob_perm[cur.row0 + tid] : 0.f;
       reinterpret_cast<float*>(smem + kXOff)[ipar * 256 + tid] = pr;
     }
+    TileCore<kMx, false> core;
+    core.zero();
+    if constexpr (kDeep) {
+      // as the forward's deep MXFP8 loop: stage s in buffer (par + s) & 1, the loads of the stage
+      // after next (this item's, or the next item's first two) issued during stage s's second
+      // substep into the buffer stage s just freed; a new scale group goes to the scale buffer
+      // the next stage does not use
+      const int n = cur.kT;
+      StepFrag<true> f0;
+      read_first<true, false, false, false, 16>(f0, smem + par * kStageBytes,
+                                                smem + kScOff + sbc * kScBuf + (cur.u0 & 3) * 4, wm, wn, lane);
+#pragma unroll 1
+      for (int s = 0; s < n; ++s) {
+        const int kt = cur.u0 + s, b = (par + s) & 1, bn = b ^ 1;
+        const int kn = s + 1 < n ? kt + 1 : nxt.u0;
+        const bool in2 = s + 2 < n;
+        const Desc& dt = in2 ? dc : dn;
+        const int k2 = in2 ? kt + 2 : nxt.u0 + (s + 2 - n);
+        const bool ng = (!in2 && s + 2 == n) || (k2 & 3) == 0;
+        const int sbd = ng ? (sbn ^ 1) : sbn;
+        auto sync = [&]() {
+          wait_vmcnt<0>();
+          __syncthreads();
+        };
+        mma_stage_mx_deep<false>(core, f0, smem + b * kStageBytes, smem + kScOff + sbc * kScBuf + (kt & 3) * 4,
+                                 smem + bn * kStageBytes, smem + kScOff + sbn * kScBuf + (kn & 3) * 4, wm, wn, lane,
+                                 [&](int q) { dma_a(dt, b, k2, q); }, [&](int q) { dma_b(dt, b, k2, q); },
+                                 [&]() { dma_sg(dt, ng, sbn ^ 1, k2 >> 2); }, sync);
+        sbc = sbn;
+        sbn = sbd;
+      }
+      par = (par + n) & 1;
+    } else {
     if (!issued && cur.kT > 0) {
 #pragma unroll
       for (int q = 0; q < 8; ++q) { dma_a(dc, par, cur.u0, q); dma_b(dc, par, cur.u0, q); }
@@ -255,8 +321,6 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     }
     // the last stage loads the next item's first one, if it has any stage
     const bool chain = nxt.t < hi && nxt.kT > 0;
-    TileCore<kMx, false> core;
-    core.zero();
 #pragma unroll 1
     for (int s = 0; s < cur.kT; ++s) {
       const int b = (par + s) & 1;
@@ -276,6 +340,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     }
     issued = cur.kT > 0 && chain;
     par = (par + cur.kT) & 1;
+    }
 
     // ---- epilogue straight from the accumulators: acc[i][j][4 q + c] of lane l is output row
     // wm*128 + 32 i + l % 32 of the tile and column wn*128 + 32 j + 8 q + 4 (l / 32) + c.  Loads and
@@ -417,6 +482,15 @@ void bwd_gemm_kernel(const BwdKArgs p) {
 
 template <int kRole, bool kMx>
 hipError_t launch_role(const BwdKArgs& k, bool out_f32, hipStream_t st) {
+  // MXFP8 dgrad whose scale rows are whole 16-byte groups (K % 512 == 0, so at least four stages of
+  // 128 values): the deep pipeline; other K keep the loop with one scale word per row per stage
+  if constexpr (kMx && kRole != kRoleWgrad) {
+    if (k.K >= 256 && k.K % 512 == 0) {
+      if (out_f32) bwd_gemm_kernel<kRole, kMx, true, true><<<kGemmGrid, 256, 0, st>>>(k);
+      else bwd_gemm_kernel<kRole, kMx, false, true><<<kGemmGrid, 256, 0, st>>>(k);
+      return hipGetLastError();
+    }
+  }
   if (out_f32) bwd_gemm_kernel<kRole, kMx, true><<<kGemmGrid, 256, 0, st>>>(k);
   else bwd_gemm_kernel<kRole, kMx, false><<<kGemmGrid, 256, 0, st>>>(k);
   return hipGetLastError();

@@ -23,6 +23,12 @@ CASES = [
     ("split-k-dgrad", cfg_small(T=600, H=256, I=2048, E=4, k=2), None),
     ("finegrained-e64-k8", get_config(5).with_(T=512, H=256, I=256, precision="bf16"), None),
     ("zipf-zero-expert", get_config(3).with_(T=1024, H=256, I=384, precision="bf16"), None),
+    # MXFP8 dgrads in the deep pipeline (K % 512 == 0): FC2 dgrad K = H = 512 (one scale group),
+    # FC1 dgrad K = 2I = 1536 (three groups), an empty expert first
+    ("deep-mx-dgrad", cfg_small(T=700, H=512, I=768, E=4, k=2), [0, 500, 699, 201]),
+    # FC1 dgrad K = 4608 (36 stages) split in 2 parts: the second part starts at stage 18, inside
+    # a scale group
+    ("deep-mx-split-odd", cfg_small(T=640, H=1024, I=2304, E=3, k=2), None),
 ]
 
 
