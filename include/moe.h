@@ -88,7 +88,9 @@ int moe_abi_version(void);
  *          prefix sum of the padded segment sizes and rows_pad =
  *          ceil(rows/32)*32 + 32*num_groups (an upper bound; the caller
  *          allocates it).
- *          Padding codes are 0x00.  cols % 32 == 0.  Offsets outside [0, rows]
+ *          Padding codes are 0x00; the columns past the last segment, up to
+ *          rows_pad, are written as padding too (codes 0x00, scale bytes
+ *          0x00).  cols % 32 == 0.  Offsets outside [0, rows]
  *          or decreasing are clamped on the device (the result is then not
  *          meaningful, but no access leaves the buffers described here).
  * Element rule: s = floor(log2(amax)) - 8 clamped to [-127, 127] (amax = 0

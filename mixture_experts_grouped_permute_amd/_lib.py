@@ -244,8 +244,8 @@ def mxfp8_quantize(x: torch.Tensor, axis: int = 0, group_offsets: Optional[torch
     else:
         G = group_offsets.numel() - 1
         rp = (rows + 31) // 32 * 32 + 32 * G
-        q = torch.zeros((cols, rp), dtype=torch.uint8, device=dev)
-        s = torch.zeros((cols, rp // 32), dtype=torch.uint8, device=dev)
+        q = torch.empty((cols, rp), dtype=torch.uint8, device=dev)      # every byte is written
+        s = torch.empty((cols, rp // 32), dtype=torch.uint8, device=dev)
         st = lib.mxfp8_quantize(_ptr(x), _io(x), rows, cols, 1, _ptr(group_offsets), G, _ptr(q), _ptr(s),
                                 _stream(dev))
     _check(st, "mxfp8_quantize")

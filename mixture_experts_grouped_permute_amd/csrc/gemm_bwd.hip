@@ -65,13 +65,18 @@ __device__ __forceinline__ const uint8_t* bwd_table(int e) {
 // One work item of the backward kernel: a 256 x 256 output tile and its K extent.
 struct BwdItem {
   int t, e, mt, nt, row0, mrows, ncols, kT, Me;
+  int kz;                   // stages with data: loads of stages kz .. kT-1 read zeros (deep wgrad)
   int part, u0;             // K part of a split tile (-1: whole K) and its first stage
   int64_t koff;
 };
 
-// kDeep (MXFP8 dgrad, K of at least two stages): the forward's deep MXFP8 pipeline -- the stage
-// barrier between the two MX substeps, stage loads issued two stages ahead, and the E8M0 bytes of
-// four stages loaded together (one 16-byte load per row: K % 512 == 0 for both dgrads).
+// kDeep (MXFP8): the forward's deep MXFP8 pipeline -- the stage barrier between the two MX
+// substeps, stage loads issued two stages ahead, and the E8M0 bytes of four stages loaded together.
+//   * dgrad (K % 512 == 0): one 16-byte scale load per row per group of four stages;
+//   * wgrad: an expert's token segment starts at a multiple of 128 tokens, so its scale bytes start
+//     4-byte aligned, and four lanes read a row's four words of a group (merged into one request).
+//     Every item runs at least two stages, as the pipeline needs: the stages past an expert's
+//     tokens (an expert with at most 128 tokens, or none) load zeros, which add nothing.
 template <int kRole, bool kMx, bool kOutF32, bool kDeep = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_gemm_kernel(const BwdKArgs p) {
@@ -79,7 +84,8 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   constexpr bool kAMN = kWg && !kMx;   // bf16 wgrad: A is token-major
   constexpr bool kBMN = !kMx;          // bf16: B is N-contiguous (weights in dgrad, activations in wgrad)
   constexpr bool kD2 = kRole == kRoleDgradFc2;
-  static_assert(!kDeep || (kMx && kRole != kRoleWgrad), "deep pipeline: MXFP8 dgrad only");
+  static_assert(!kDeep || kMx, "deep pipeline: MXFP8 only");
+  constexpr bool kSc4 = kDeep && kWg;   // four-lane word form of the scale group loads
   // two stages of A + B (64 KB each), the MXFP8 scales (2 x 2 KB of one word per row per stage, or
   // in the deep pipeline 2 x 8 KB of 16 bytes per row per group of four stages), and for the FC2
   // dgrad the routing probabilities of the tile's rows (2 x 1 KB, by work item) and the per-row
@@ -109,6 +115,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   auto decode = [&](int round, BwdItem& it) {
     it.t = lo + round * G + xcd * per + slot;
     it.kT = 0;
+    it.kz = 0;
     it.u0 = 0;
     it.part = -1;
     if (it.t >= hi) return;
@@ -122,6 +129,8 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
       it.koff = kMx ? __builtin_amdgcn_readfirstlane(sched.tile[it.e]) : __builtin_amdgcn_readfirstlane(sched.off[it.e]);
       it.kT = (it.Me + kKStep - 1) / kKStep;
+      it.kz = it.kT;
+      if (kDeep && it.kT < 2) it.kT = 2;
       it.row0 = it.mt * kBM;
       it.mrows = (int)min((int64_t)kBM, p.M - it.row0);
     } else {
@@ -140,6 +149,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       it.koff = 0;
       it.u0 = it.part < 0 ? 0 : it.part * kU / S;
       it.kT = (it.part < 0 ? kU : (it.part + 1) * kU / S) - it.u0;
+      it.kz = it.u0 + it.kT;
     }
     it.ncols = (int)min((int64_t)kBN, p.N - (int64_t)it.nt * kBN);
   };
@@ -169,7 +179,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     if constexpr (kAMN) {            // bf16 wgrad: A^T = token-major rows [tok][M]
       a_base_off = it.koff * p.lda + m0w * 2; a_range = (uint32_t)max((int64_t)0, it.Me * p.lda - m0w * 2);
     } else if constexpr (kWg) {      // MXFP8 wgrad: A^T quantized [M][Rpad], segment at koff
-      a_base_off = m0w * p.lda + it.koff; a_range = (uint32_t)(it.mrows * p.lda);
+      a_base_off = m0w * p.lda + it.koff; a_range = (uint32_t)(it.mrows * p.lda - it.koff);
     } else {
       a_base_off = (int64_t)it.row0 * p.lda; a_range = (uint32_t)(it.mrows * p.lda);
     }
@@ -180,7 +190,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
         bbase = bwd_table(it.e); b_base_off = n0 * 2; b_range = (uint32_t)(p.K * p.ldb - n0 * 2);
       }
     } else if constexpr (kWg) {      // MXFP8 wgrad: B^T quantized [N][Rpad]
-      bbase = p.b; b_base_off = n0 * p.ldb + it.koff; b_range = (uint32_t)(it.ncols * p.ldb);
+      bbase = p.b; b_base_off = n0 * p.ldb + it.koff; b_range = (uint32_t)(it.ncols * p.ldb - it.koff);
     } else {                         // MXFP8 dgrad: W^T quantized [N][K] per expert
       bbase = p.b + (int64_t)it.e * p.b_stride; b_base_off = n0 * p.ldb; b_range = (uint32_t)(it.ncols * p.ldb);
     }
@@ -188,8 +198,10 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     d.vb = make_vsharp(bbase + b_base_off, b_range);
     if constexpr (kMx) {
       if constexpr (kWg) {
-        d.vas = make_vsharp(p.as + m0w * p.ldas + it.koff / 32, (uint32_t)(it.mrows * p.ldas));
-        d.vbs = make_vsharp(p.bs + n0 * p.ldbs + it.koff / 32, (uint32_t)(it.ncols * p.ldbs));
+        // ranges end at the scale arrays' ends: a group of scale bytes read past the last segment
+        // (padding scales up to rows_pad) reads zeros beyond it
+        d.vas = make_vsharp(p.as + m0w * p.ldas + it.koff / 32, (uint32_t)(it.mrows * p.ldas - it.koff / 32));
+        d.vbs = make_vsharp(p.bs + n0 * p.ldbs + it.koff / 32, (uint32_t)(it.ncols * p.ldbs - it.koff / 32));
       } else {
         d.vas = make_vsharp(p.as + (int64_t)it.row0 * p.ldas, (uint32_t)(it.mrows * p.ldas));
         d.vbs = make_vsharp(p.bs + (int64_t)it.e * p.bs_stride + n0 * p.ldbs, (uint32_t)(it.ncols * p.ldbs));
@@ -219,18 +231,30 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   const uint32_t a_step = kAMN ? (uint32_t)(64 * p.lda) : (uint32_t)kRowBytes;
   const uint32_t b_step = kBMN ? (uint32_t)(64 * p.ldb) : (uint32_t)kRowBytes;
   uint32_t as_vo = 0, bs_vo = 0;
+  uint32_t as4[4] = {0, 0, 0, 0}, bs4[4] = {0, 0, 0, 0};   // deep: scale group offsets
   if constexpr (kMx) {
     const int r = wave * 64 + lane;
     as_vo = (uint32_t)(r * p.ldas);
     bs_vo = (uint32_t)(r * p.ldbs);
+    // group loads: row r's 16 bytes at r * 16 of the buffer; in the four-lane form load j of wave w
+    // covers rows 64 w + 16 j + L / 4, lane L's word landing at slot L of a 256-byte block
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r4 = kSc4 ? wave * 64 + j * 16 + (lane >> 2) : r;
+      const uint32_t w4 = kSc4 ? (uint32_t)(lane & 3) * 4u : 0u;
+      as4[j] = (uint32_t)(r4 * p.ldas) + w4;
+      bs4[j] = (uint32_t)(r4 * p.ldbs) + w4;
+    }
   }
+  const i32x4 zdesc = make_vsharp(p.a, 0);   // zero range: loads read no memory and deliver zeros
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
   const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * (kDeep ? 1024u : 256u));
-  auto dma_a = [&](const Desc& d, int b, int kt, int q) {
-    dma16(d.va, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q] + (uint32_t)kt * a_step, 0);
+  auto dma_a = [&](const Desc& d, int b, int kt, int q, bool on = true) {
+    dma16(on ? d.va : zdesc, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q] + (uint32_t)kt * a_step, 0);
   };
-  auto dma_b = [&](const Desc& d, int b, int kt, int q) {
-    dma16(d.vb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q] + (uint32_t)kt * b_step, 0);
+  auto dma_b = [&](const Desc& d, int b, int kt, int q, bool on = true) {
+    dma16(on ? d.vb : zdesc, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u,
+          b_vo[q] + (uint32_t)kt * b_step, 0);
   };
   auto dma_s = [&](const Desc& d, int b, int kt) {
     if constexpr (kMx && !kDeep) {
@@ -244,10 +268,17 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   // read, zeros written to the buffer, which no pending stage uses)
   auto dma_sg = [&](const Desc& d, bool on, int sb, int g) {
     if constexpr (kDeep) {
-      const i32x4 z = make_vsharp(p.a, 0);
       const uint32_t ss = lds_sc + (uint32_t)sb * (uint32_t)kScBuf;
-      dma16(on ? d.vas : z, ss, as_vo, (uint32_t)g * 16u);
-      dma16(on ? d.vbs : z, ss + 4096u, bs_vo, (uint32_t)g * 16u);
+      if constexpr (!kSc4) {
+        dma16(on ? d.vas : zdesc, ss, as4[0], (uint32_t)g * 16u);
+        dma16(on ? d.vbs : zdesc, ss + 4096u, bs4[0], (uint32_t)g * 16u);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dma4(on ? d.vas : zdesc, ss + (uint32_t)j * 256u, as4[j], (uint32_t)g * 16u);
+          dma4(on ? d.vbs : zdesc, ss + 4096u + (uint32_t)j * 256u, bs4[j], (uint32_t)g * 16u);
+        }
+      }
     }
   };
 
@@ -259,15 +290,16 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   bool issued = false;     // the current item's first stage was loaded by the previous item
   int sbc = 0, sbn = 0;    // deep pipeline: scale buffers of the current and the next stage
   if constexpr (kDeep) {
-    // the first item's first two stages (every dgrad item has at least two)
+    // the first item's first two stages (every item has at least two)
     if (cur.t < hi) {
+      const bool on0 = cur.u0 < cur.kz, on1 = cur.u0 + 1 < cur.kz;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) { dma_a(dc, 0, cur.u0, q); dma_b(dc, 0, cur.u0, q); }
+      for (int q = 0; q < 8; ++q) { dma_a(dc, 0, cur.u0, q, on0); dma_b(dc, 0, cur.u0, q, on0); }
       dma_sg(dc, true, 0, cur.u0 >> 2);
       wait_vmcnt<0>();
       __syncthreads();
 #pragma unroll
-      for (int q = 0; q < 8; ++q) { dma_a(dc, 1, cur.u0 + 1, q); dma_b(dc, 1, cur.u0 + 1, q); }
+      for (int q = 0; q < 8; ++q) { dma_a(dc, 1, cur.u0 + 1, q, on1); dma_b(dc, 1, cur.u0 + 1, q, on1); }
       const bool ng = ((cur.u0 + 1) & 3) == 0;
       sbn = ng ? 1 : 0;
       dma_sg(dc, ng, 1, (cur.u0 + 1) >> 2);
@@ -301,13 +333,14 @@ void bwd_gemm_kernel(const BwdKArgs p) {
         const int k2 = in2 ? kt + 2 : nxt.u0 + (s + 2 - n);
         const bool ng = (!in2 && s + 2 == n) || (k2 & 3) == 0;
         const int sbd = ng ? (sbn ^ 1) : sbn;
+        const bool on = !kWg || k2 < (in2 ? cur.kz : nxt.kz);   // the stage holds data (wgrad)
         auto sync = [&]() {
           wait_vmcnt<0>();
           __syncthreads();
         };
         mma_stage_mx_deep<false>(core, f0, smem + b * kStageBytes, smem + kScOff + sbc * kScBuf + (kt & 3) * 4,
                                  smem + bn * kStageBytes, smem + kScOff + sbn * kScBuf + (kn & 3) * 4, wm, wn, lane,
-                                 [&](int q) { dma_a(dt, b, k2, q); }, [&](int q) { dma_b(dt, b, k2, q); },
+                                 [&](int q) { dma_a(dt, b, k2, q, on); }, [&](int q) { dma_b(dt, b, k2, q, on); },
                                  [&]() { dma_sg(dt, ng, sbn ^ 1, k2 >> 2); }, sync);
         sbc = sbn;
         sbn = sbd;
@@ -482,10 +515,11 @@ void bwd_gemm_kernel(const BwdKArgs p) {
 
 template <int kRole, bool kMx>
 hipError_t launch_role(const BwdKArgs& k, bool out_f32, hipStream_t st) {
-  // MXFP8 dgrad whose scale rows are whole 16-byte groups (K % 512 == 0, so at least four stages of
-  // 128 values): the deep pipeline; other K keep the loop with one scale word per row per stage
-  if constexpr (kMx && kRole != kRoleWgrad) {
-    if (k.K >= 256 && k.K % 512 == 0) {
+  // MXFP8 wgrad, and MXFP8 dgrad whose scale rows are whole 16-byte groups (K % 512 == 0, so at
+  // least four stages of 128 values): the deep pipeline; other K keep the loop with one scale word
+  // per row per stage
+  if constexpr (kMx) {
+    if (kRole == kRoleWgrad || k.K % 512 == 0) {
       if (out_f32) bwd_gemm_kernel<kRole, kMx, true, true><<<kGemmGrid, 256, 0, st>>>(k);
       else bwd_gemm_kernel<kRole, kMx, false, true><<<kGemmGrid, 256, 0, st>>>(k);
       return hipGetLastError();

@@ -208,7 +208,10 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void
   __syncthreads();
   const int64_t p0 = (int64_t)blockIdx.x * kColRows;   // first padded row of this workgroup
   const int64_t ptotal = s_pad[num_groups];
-  if (p0 >= ptotal) return;                             // uniform: nothing of this slab is written
+  // padded rows past the last segment, up to rows_pad, are written as padding too (codes 0, scale
+  // bytes 0): a reader may then take a whole group of scale bytes past its segment's end and find
+  // finite scales there
+  if (p0 >= rows_pad) return;                           // uniform
   if (t < kColRows) {
     const int64_t pr = p0 + t;
     int src = -1;
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void
   __shared__ __attribute__((aligned(16))) uint8_t ostage[64][kColRows + 16];
   const int64_t c = c0 + lane;
   const int64_t pblk = p0 + 32 * wave;                  // padded row of this lane's block
-  const bool valid = c < cols && pblk < ptotal && pblk + 32 <= rows_pad;
+  const bool valid = c < cols && pblk + 32 <= rows_pad;
   float v[32];
   float am = 0.f;
 #pragma unroll
@@ -280,7 +283,7 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void
     const int lc = id >> 3, pc = id & 7;
     const int64_t cc = c0 + lc;
     const int64_t pb = p0 + 32 * (pc >> 1);
-    if (cc < cols && pb < ptotal && pb + 32 <= rows_pad)
+    if (cc < cols && pb + 32 <= rows_pad)
       *reinterpret_cast<u32x4*>(q + cc * rows_pad + p0 + 16 * pc) =
           *reinterpret_cast<const u32x4*>(&ostage[lc][16 * pc]);
   }
