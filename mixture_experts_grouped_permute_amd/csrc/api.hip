@@ -183,10 +183,10 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   if (any_saved && a->compute == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;   // forward only
   if ((a->h_codes != nullptr) != (a->h_scales != nullptr)) return MOE_ERR_INVALID_ARG;
   if (a->h_codes && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
-  // 32-bit buffer ranges inside the GEMMs
-  const int64_t R = a->T * a->k;
-  const int64_t widest = a->H > 2 * a->I ? a->H : 2 * a->I;
-  if (R * widest * 2 >= (int64_t)UINT32_MAX || 2 * a->I * a->H * 2 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  // 32-bit buffer ranges inside the GEMMs: every descriptor spans one 256-row tile of an
+  // activation or one expert's weight matrix, so the limit is on an expert's weights (in bf16),
+  // not on the number of tokens
+  if (2 * a->I * a->H * 2 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -256,12 +256,14 @@ moe_status validate_bwd(const moe_mlp_bwd_args* a) {
   if (any_wt && (!all_wt || a->compute != MOE_MXFP8_E4M3)) return MOE_ERR_INVALID_ARG;
   for (int e = 0; e < a->E; ++e)
     if (!a->w1[e] || !a->w2[e] || !a->dw1[e] || !a->dw2[e]) return MOE_ERR_INVALID_ARG;
+  // 32-bit buffer ranges inside the GEMMs: per tile of an activation (the BF16 wgrad's token
+  // segments get one descriptor per 64-token stage), per expert of the weights and of dW in fp32,
+  // and, for the MXFP8 wgrad, per 256 rows of the token-contiguous operands
   const int64_t R = a->T * a->k;
-  const int64_t widest = a->H > 2 * a->I ? a->H : 2 * a->I;
-  if (R * widest * 2 >= (int64_t)UINT32_MAX || 2 * a->I * a->H * 4 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+  if (2 * a->I * a->H * 4 >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   if (a->compute == MOE_MXFP8_E4M3) {
     const int64_t Rp = (R + 127) / 128 * 128 + 128 * (int64_t)a->E;
-    if (widest * Rp >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (256 * Rp >= (int64_t)UINT32_MAX) return MOE_ERR_UNSUPPORTED;
   }
   return MOE_OK;
 }

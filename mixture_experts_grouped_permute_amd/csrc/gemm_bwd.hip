@@ -160,13 +160,23 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   //     pairs j = 4 (8w + q) + L / 16, slot s = L % 16 holding (row parity, chunk) = s ^ hs(j).
   //   MN-major operand (bf16, K rows of 256 contiguous columns): 64 K rows x 512 bytes in the
   //     mnswz layout; load q of wave w fills rows 2 (8w + q) + L / 32, physical chunk L % 32.
-  //     The K row advance is carried in the per-lane offset so that rows past the end of the
-  //     operand (a ragged token segment in wgrad) fall outside the descriptor and read zero.
+  //     In dgrad the K row advance is carried in the per-lane offset.  In wgrad (the token-major
+  //     activations, whose token segment may span more than 4 GB) each stage gets descriptors
+  //     based at its first token row, ending at the segment's end: rows past a ragged segment read
+  //     zero, and no offset leaves 32 bits.
   //   MXFP8 operands are K-major, with one 4-byte E8M0 word per row per stage.
   // Invalid items and items without K stages get zero-range descriptors: their loads touch no
   // memory.
-  struct Desc { i32x4 va, vb, vas, vbs; };
+  struct Desc {
+    i32x4 va, vb, vas, vbs;
+    const uint8_t *pa, *pb;   // BF16 wgrad: operand bases of the item's first token row
+    int64_t ea, eb;           // and the bytes from there to the segment's end
+  };
   auto descs = [&](const BwdItem& it, Desc& d) {
+    d.pa = p.a;
+    d.pb = p.a;
+    d.ea = 0;
+    d.eb = 0;
     if (it.t >= hi || it.kT == 0) {
       d.va = make_vsharp(p.a, 0); d.vb = d.va; d.vas = d.va; d.vbs = d.va;
       return;
@@ -193,6 +203,14 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       bbase = p.b; b_base_off = n0 * p.ldb + it.koff; b_range = (uint32_t)(it.ncols * p.ldb - it.koff);
     } else {                         // MXFP8 dgrad: W^T quantized [N][K] per expert
       bbase = p.b + (int64_t)it.e * p.b_stride; b_base_off = n0 * p.ldb; b_range = (uint32_t)(it.ncols * p.ldb);
+    }
+    if constexpr (kWg && !kMx) {
+      d.pa = p.a + a_base_off;
+      d.ea = max((int64_t)0, it.Me * p.lda - m0w * 2);
+      d.pb = bbase + b_base_off;
+      d.eb = max((int64_t)0, it.Me * p.ldb - n0 * 2);
+      a_range = 0;
+      b_range = 0;
     }
     d.va = make_vsharp(p.a + a_base_off, a_range);
     d.vb = make_vsharp(bbase + b_base_off, b_range);
@@ -249,12 +267,32 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   const i32x4 zdesc = make_vsharp(p.a, 0);   // zero range: loads read no memory and deliver zeros
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
   const uint32_t lds_sc = __builtin_amdgcn_readfirstlane(lds_addr(smem + kScOff) + (uint32_t)wave * (kDeep ? 1024u : 256u));
+  // BF16 wgrad: descriptors of stage kt, based at its first token row (64 rows per stage), the
+  // range clipped to the segment's end (and to 32 bits)
+  auto stage_vs = [&](const uint8_t* base, int64_t ext, int kt, int64_t ld) -> i32x4 {
+    const int64_t o = (int64_t)kt * 64 * ld;
+    const int64_t r = ext - o;
+    return make_vsharp(base + o, (uint32_t)(r <= 0 ? 0 : (r > (int64_t)0xFFFFFFFF ? (int64_t)0xFFFFFFFF : r)));
+  };
+  i32x4 sva = zdesc, svb = zdesc;
+  // q runs 0..7 in order within a stage (unrolled), so the stage's descriptors are formed at q == 0
   auto dma_a = [&](const Desc& d, int b, int kt, int q, bool on = true) {
-    dma16(on ? d.va : zdesc, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q] + (uint32_t)kt * a_step, 0);
+    if constexpr (kWg && !kMx) {
+      if (q == 0) sva = stage_vs(d.pa, d.ea, kt, p.lda);
+      dma16(sva, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u, a_vo[q], 0);
+    } else {
+      dma16(on ? d.va : zdesc, lds0 + (uint32_t)b * (uint32_t)kStageBytes + q * 1024u,
+            a_vo[q] + (uint32_t)kt * a_step, 0);
+    }
   };
   auto dma_b = [&](const Desc& d, int b, int kt, int q, bool on = true) {
-    dma16(on ? d.vb : zdesc, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u,
-          b_vo[q] + (uint32_t)kt * b_step, 0);
+    if constexpr (kWg && !kMx) {
+      if (q == 0) svb = stage_vs(d.pb, d.eb, kt, p.ldb);
+      dma16(svb, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u, b_vo[q], 0);
+    } else {
+      dma16(on ? d.vb : zdesc, lds0 + (uint32_t)b * (uint32_t)kStageBytes + kTileBytes + q * 1024u,
+            b_vo[q] + (uint32_t)kt * b_step, 0);
+    }
   };
   auto dma_s = [&](const Desc& d, int b, int kt) {
     if constexpr (kMx && !kDeep) {
