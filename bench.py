@@ -163,7 +163,10 @@ def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0):
         _, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision,
                                        save_for_backward=True)
         perm = ctx["perm"]
-        a, outs, keep = L._bwd_args(d.dy, ctx, d.w1, d.w2, torch.float32)
+        wqt = None
+        if cached:   # W1, W2 quantized along the backward's K once, outside the timed region
+            wqt = m.quantize_weights(d.w1, d.w2, cfg.precision, transposed=True)
+        a, outs, keep = L._bwd_args(d.dy, ctx, d.w1, d.w2, torch.float32, w_quant_t=wqt)
         need = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(a))
         if need == 0:
             raise RuntimeError("argument validation failed")
@@ -300,8 +303,8 @@ def copy_leg(reps=10):
     return res
 
 
-def bwd_leg(cfg, steps, warmup):
-    r = run_gpu(cfg, steps, warmup, backward=True)
+def bwd_leg(cfg, steps, warmup, cached=False):
+    r = run_gpu(cfg, steps, warmup, backward=True, cached=cached)
     ms = r["ms_per_step"]
     ph = r["phase_ms"]
     R, H, I = cfg.R, cfg.H, cfg.I
@@ -586,6 +589,13 @@ def main():
         torch.cuda.empty_cache()
         line["backward_mxfp8"] = bwd_leg(get_config(4).with_(precision="mxfp8"), max(2, args.steps // 2),
                                          max(1, args.warmup // 2))
+        # the same with W1, W2 quantized along the backward's K once (e.g. once per optimizer step
+        # under gradient accumulation) and passed in
+        torch.cuda.empty_cache()
+        rc = bwd_leg(get_config(4).with_(precision="mxfp8"), max(2, args.steps // 2), max(1, args.warmup // 2),
+                     cached=True)
+        line["backward_mxfp8"]["cached_weights"] = {"ms_per_step": rc["ms_per_step"], "value": rc["value"],
+                                                    "phase_ms": rc["phase_ms"]}
     print(json.dumps(line), flush=True)
 
 

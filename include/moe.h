@@ -384,6 +384,22 @@ const char* moe_fwd_phase_name(int i);   /* NULL when out of range */
  * mxfp8_quantize_weights(w2, E, H, I, axis 1).  Without them the backward
  * quantizes them itself on every call (one launch per weight table, experts
  * without tokens skipped).
+ * Under MXFP8 the FC2 dgrad epilogue quantizes dgu itself (page "BioNeMo Uses
+ * Grouped Kernels and MXFP8", Fusing precision conversion and expert
+ * computation, Figure 4: the precision conversion fused into the expert
+ * computation), from its bf16 values, both ways: row-wise along 2I for the
+ * FC1 dgrad and along each expert's tokens for the FC1 wgrad; the bf16 dgu
+ * itself is not written.  The optional debug outputs (MXFP8 only; all five or
+ * none, else MOE_ERR_INVALID_ARG) receive, in the caller's buffers:
+ *   dgu_bf16      [R, 2I] bf16, the values that are quantized;
+ *   dgu_codes     [R, 2I] E4M3 and dgu_scales [R, 2I/32] E8M0 (row-wise);
+ *   dgu_t_codes   [2I, rows_pad] E4M3 and dgu_t_scales [2I, rows_pad/32] E8M0,
+ *                 transposed, with rows_pad = ceil(R/128)*128 + 128*E: expert
+ *                 e's tokens at columns [P_e, P_e + M_e) where P_e is the sum of
+ *                 the earlier experts' counts each rounded up to 128; 32-token
+ *                 blocks restart at P_e, the columns up to the next multiple of
+ *                 128 are padding (codes 0), and the scale bytes past the last
+ *                 padded segment are 0.  Other columns are not written.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t T, H, I;
@@ -412,6 +428,11 @@ typedef struct {
   const uint8_t* w1ts;          /* [E, H, 2I/32] E8M0 */
   const uint8_t* w2tq;          /* [E, I, H]     E4M3 */
   const uint8_t* w2ts;          /* [E, I, H/32]  E8M0 */
+  uint16_t* dgu_bf16;           /* [R, 2I] bf16, or NULL (ABI version 5; MXFP8 debug) */
+  uint8_t* dgu_codes;           /* [R, 2I]        E4M3 */
+  uint8_t* dgu_scales;          /* [R, 2I/32]     E8M0 */
+  uint8_t* dgu_t_codes;         /* [2I, rows_pad] E4M3 */
+  uint8_t* dgu_t_scales;        /* [2I, rows_pad/32] E8M0 */
 } moe_mlp_bwd_args;
 
 size_t moe_grouped_mlp_bwd_workspace(const moe_mlp_bwd_args* a);

@@ -72,6 +72,7 @@ class BwdArgs(ctypes.Structure):
         ("dw1", ctypes.POINTER(_vp)), ("dw2", ctypes.POINTER(_vp)),
         ("workspace", _vp), ("workspace_bytes", ctypes.c_size_t),
         ("w1tq", _vp), ("w1ts", _vp), ("w2tq", _vp), ("w2ts", _vp),
+        ("dgu_bf16", _vp), ("dgu_codes", _vp), ("dgu_scales", _vp), ("dgu_t_codes", _vp), ("dgu_t_scales", _vp),
     ]
 
 
@@ -601,15 +602,26 @@ def _bwd_args(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32, w_qua
 
 
 def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32,
-                        workspace: Optional[torch.Tensor] = None, w_quant_t=None):
+                        workspace: Optional[torch.Tensor] = None, w_quant_t=None, debug: Optional[dict] = None):
     """Backward of moe_grouped_mlp_fwd (needs save_for_backward=True).
     w_quant_t: optional quantize_weights(w1, w2, "mxfp8", transposed=True) output (MXFP8): the
     per-call quantization of the transposed weights is skipped.
+    debug: optional dict (MXFP8): filled with the FC2 dgrad epilogue's dgu in bf16 ("dgu_bf16"
+    [R, 2I]) and its two quantizations ("dgu_codes", "dgu_scales" row-wise; "dgu_t_codes",
+    "dgu_t_scales" along tokens, [2I, rows_pad] with rows_pad = ceil(R/128)*128 + 128 E).
     Returns (dx [T,H], dprob [T,k] f32, dw1 [E,2I,H], dw2 [E,H,I])."""
     lib = load()
     dev = dy.device
     a, outs, keep = _bwd_args(dy, ctx, w1, w2, dw_dtype, w_quant_t)
     dx, dprob, dw1, dw2 = outs
+    if debug is not None:
+        R, I2, E = int(a.T) * int(a.k), 2 * int(a.I), int(a.E)
+        rp = (R + 127) // 128 * 128 + 128 * E
+        u8 = lambda *shape: torch.zeros(shape, dtype=torch.uint8, device=dev)
+        debug.update(dgu_bf16=torch.zeros((R, I2), dtype=torch.bfloat16, device=dev), dgu_codes=u8(R, I2),
+                     dgu_scales=u8(R, I2 // 32), dgu_t_codes=u8(I2, rp), dgu_t_scales=u8(I2, rp // 32))
+        for name in ("dgu_bf16", "dgu_codes", "dgu_scales", "dgu_t_codes", "dgu_t_scales"):
+            setattr(a, name, debug[name].data_ptr())
     need = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(a))
     if need == 0:
         _check(lib.moe_grouped_mlp_bwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_bwd")

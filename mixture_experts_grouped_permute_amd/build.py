@@ -26,6 +26,9 @@ FLAGS = [
     "-Wno-unused-result", "-Wno-inline-asm",
     # packed-fp32 instructions are never generated (they are not trusted on this hardware)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # full unrolling of the epilogue loops that index the accumulators with the loop counter (a loop
+    # left rolled would move the accumulators to scratch memory)
+    "-mllvm", "-pragma-unroll-threshold=200000",
     f"-I{os.path.join(ROOT, 'include')}",
 ]
 

@@ -208,12 +208,14 @@ BwdPlan plan_bwd(const moe_mlp_bwd_args* a, void* ws) {
   Carver c(ws);
   const int64_t R = a->T * a->k, H = a->H, I = a->I;
   const int E = a->E;
+  const bool mx = a->compute == MOE_MXFP8_E4M3;
   p.dz = reinterpret_cast<uint16_t*>(c.take((size_t)(R * H * 2)));
-  p.dgu = reinterpret_cast<uint16_t*>(c.take((size_t)(R * 2 * I * 2)));
+  // MXFP8: the FC2 dgrad epilogue quantizes dgu itself; bf16 dgu only into the caller's debug buffer
+  p.dgu = mx ? a->dgu_bf16 : reinterpret_cast<uint16_t*>(c.take((size_t)(R * 2 * I * 2)));
   p.dprob_part = reinterpret_cast<float*>(c.take((size_t)(R * bwd_dprob_parts(I) * 4)));
   p.dx_perm = c.take((size_t)(R * H) * io_size(a->io_dtype));
   p.part = reinterpret_cast<float*>(c.take(kFc2PartBytes));
-  if (a->compute == MOE_MXFP8_E4M3) {
+  if (mx) {
     const int64_t Rp = (R + 127) / 128 * 128 + 128 * (int64_t)E;
     p.rows_pad = Rp;
     auto take8 = [&](int64_t n) { return reinterpret_cast<uint8_t*>(c.take((size_t)n)); };
@@ -225,13 +227,21 @@ BwdPlan plan_bwd(const moe_mlp_bwd_args* a, void* ws) {
     }
     p.dzT = take8(H * Rp); p.dzTs = take8(H * Rp / 32);
     p.hT = take8(I * Rp); p.hTs = take8(I * Rp / 32);
-    p.dguq = take8(R * 2 * I); p.dgus = take8(R * 2 * I / 32);
+    if (a->dgu_codes) {
+      p.dguq = a->dgu_codes; p.dgus = a->dgu_scales;
+    } else {
+      p.dguq = take8(R * 2 * I); p.dgus = take8(R * 2 * I / 32);
+    }
     if (a->w1tq) {
       p.w1tq = const_cast<uint8_t*>(a->w1tq); p.w1ts = const_cast<uint8_t*>(a->w1ts);
     } else {
       p.w1tq = take8((int64_t)E * H * 2 * I); p.w1ts = take8((int64_t)E * H * 2 * I / 32);
     }
-    p.dguT = take8(2 * I * Rp); p.dguTs = take8(2 * I * Rp / 32);
+    if (a->dgu_t_codes) {
+      p.dguT = a->dgu_t_codes; p.dguTs = a->dgu_t_scales;
+    } else {
+      p.dguT = take8(2 * I * Rp); p.dguTs = take8(2 * I * Rp / 32);
+    }
     p.xT = take8(H * Rp); p.xTs = take8(H * Rp / 32);
   }
   p.bytes = c.used;
@@ -254,6 +264,9 @@ moe_status validate_bwd(const moe_mlp_bwd_args* a) {
   const bool any_wt = a->w1tq || a->w1ts || a->w2tq || a->w2ts;
   const bool all_wt = a->w1tq && a->w1ts && a->w2tq && a->w2ts;
   if (any_wt && (!all_wt || a->compute != MOE_MXFP8_E4M3)) return MOE_ERR_INVALID_ARG;
+  const bool any_dbg = a->dgu_bf16 || a->dgu_codes || a->dgu_scales || a->dgu_t_codes || a->dgu_t_scales;
+  const bool all_dbg = a->dgu_bf16 && a->dgu_codes && a->dgu_scales && a->dgu_t_codes && a->dgu_t_scales;
+  if (any_dbg && (!all_dbg || a->compute != MOE_MXFP8_E4M3)) return MOE_ERR_INVALID_ARG;
   for (int e = 0; e < a->E; ++e)
     if (!a->w1[e] || !a->w2[e] || !a->dw1[e] || !a->dw2[e]) return MOE_ERR_INVALID_ARG;
   // 32-bit buffer ranges inside the GEMMs: per tile of an activation (the BF16 wgrad's token
@@ -376,7 +389,7 @@ constexpr int kMaxDevices = 64;
 
 extern "C" {
 
-int moe_abi_version(void) { return 4; }
+int moe_abi_version(void) { return 5; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -779,6 +792,11 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   d2.dprob_part = p.dprob_part;
   d2.I = I;
   if (mx) {
+    d2.dgu_q = p.dguq; d2.dgu_s = p.dgus;
+    d2.dgu_tq = p.dguT; d2.dgu_ts = p.dguTs;
+    d2.rows_pad = p.rows_pad;
+  }
+  if (mx) {
     // dz along H: each token's dy row quantized once and written to its k permuted rows
     if (dz_direct) HIP_TRY(launch_permute_rows(a->dy, false, T, H, k, a->row_id_map, p.dzq, p.dzs, true, st));
     else HIP_TRY(launch_mx_quant_rows(p.dz, false, R, H, p.dzq, p.dzs, st));
@@ -793,6 +811,8 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   }
   MOE_CHECK(mark(2), MOE_ERR_HIP);
   HIP_TRY(launch_bwd_dgrad_fc2(d2, mx, st));
+  // the token-axis scale bytes past the last padded segment: a wgrad scale-group load may read them
+  if (mx) HIP_TRY(launch_scale_tail_zero(p.dguTs, 2 * I, p.rows_pad / 32, a->split_sizes, E, st));
   MOE_CHECK(mark(3), MOE_ERR_HIP);
 
   // ---- FC2 wgrad: dW2_e = dz_e^T h_e
@@ -824,7 +844,7 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   d1.N = H; d1.K = 2 * I; d1.E = E; d1.split_sizes = a->split_sizes;
   d1.out = p.dx_perm; d1.out_f32 = io_f32; d1.part = p.part;
   if (mx) {
-    HIP_TRY(launch_mx_quant_rows(p.dgu, false, R, 2 * I, p.dguq, p.dgus, st));
+    // dgu along 2I: quantized by the FC2 dgrad epilogue
     // W1_e^T along 2I for every expert with tokens, one launch (unless cached by the caller)
     if (!a->w1tq) HIP_TRY(launch_mx_quant_weights_t(a->w1, E, 2 * I, H, p.w1tq, p.w1ts, a->split_sizes, st));
     d1.a = p.dguq; d1.lda = 2 * I; d1.a_scales = p.dgus; d1.ldas = 2 * I / 32;
@@ -845,7 +865,7 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   w1.out_f32 = dw_f32;
   if (mx) {
     const int64_t Rp = p.rows_pad;
-    HIP_TRY(launch_mx_quant_cols(p.dgu, false, R, 2 * I, a->offsets, E, Rp, p.dguT, p.dguTs, st, 128));
+    // dgu along tokens: quantized by the FC2 dgrad epilogue
     HIP_TRY(launch_mx_quant_cols(a->saved_x_perm, false, R, H, a->offsets, E, Rp, p.xT, p.xTs, st, 128));
     w1.a = p.dguT; w1.lda = Rp; w1.a_scales = p.dguTs; w1.ldas = Rp / 32;
     w1.b = p.xT; w1.ldb = Rp; w1.b_scales = p.xTs; w1.ldbs = Rp / 32;

@@ -430,7 +430,7 @@ void fwd_gemm_kernel(const FwdKArgs p) {
             float am = 0.f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
-            am = fmaxf(am, __shfl_xor(am, 32, 64));
+            am = max_xor32(am);
             const int sx = mx_shared_exp(am);
             uint32_t cq[4];
 #pragma unroll

@@ -48,6 +48,9 @@ struct BwdKArgs {
   uint8_t* out;             // FC1 dgrad: dx_perm [R, N]
   float* part;              // FC1 dgrad split parts: kGemmGrid x 64K floats
   int split;                // FC1 dgrad: 0 every tile; 1 tiles before the split ones; 2 the split parts
+  uint8_t *dgu_q, *dgu_s;   // MXFP8 FC2 dgrad: dGU quantized along 2I, [R, 2I] + [R, 2I / 32]
+  uint8_t *dgu_tq, *dgu_ts; // and along tokens, [2I, rows_pad] + [2I, rows_pad / 32]
+  int64_t rows_pad;
   const uint8_t* tab[kMaxExperts];   // BF16 dgrad: W_e; wgrad: dW_e
 };
 
@@ -65,6 +68,7 @@ __device__ __forceinline__ const uint8_t* bwd_table(int e) {
 // One work item of the backward kernel: a 256 x 256 output tile and its K extent.
 struct BwdItem {
   int t, e, mt, nt, row0, mrows, ncols, kT, Me;
+  int poff;                 // MXFP8 FC2 dgrad: the expert's first column in the token-padded layout
   int kz;                   // stages with data: loads of stages kz .. kT-1 read zeros (deep wgrad)
   int part, u0;             // K part of a split tile (-1: whole K) and its first stage
   int64_t koff;
@@ -93,7 +97,11 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   constexpr int kScOff = 2 * kStageBytes;
   constexpr int kScBuf = kDeep ? 8192 : 2048;
   constexpr int kXOff = kScOff + (kMx ? 2 * kScBuf : 0);
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kXOff + (kD2 ? 4096 : 16)];
+  // MXFP8 FC2 dgrad: a 32 x 32 bf16 block per wave (2 KB each) for the transposes of the
+  // token-axis quantization
+  constexpr bool kQ = kD2 && kMx;
+  constexpr int kTOff = kXOff + 4096;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXOff + (kD2 ? 4096 : 16) + (kQ ? 4 * 2048 : 0)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -141,6 +149,11 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       }
       it.e = __builtin_amdgcn_readfirstlane(find_expert(sched, E, tile));
       it.Me = __builtin_amdgcn_readfirstlane(sched.cnt[it.e]);
+      if constexpr (kQ) {
+        int po = 0;
+        for (int e2 = 0; e2 < it.e; ++e2) po += (sched.cnt[e2] + 127) / 128 * 128;
+        it.poff = __builtin_amdgcn_readfirstlane(po);
+      }
       const int nMe = (it.Me + kBM - 1) / kBM;
       const int local = tile - __builtin_amdgcn_readfirstlane(sched.tile[it.e]);
       tile_coords(local, nMe, p.nN, it.mt, it.nt);
@@ -451,6 +464,89 @@ void bwd_gemm_kernel(const BwdKArgs p) {
           ul[bf][pp] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rgu, o + I32 * 2u, 0, 0));
         }
       };
+      // MXFP8: dGU quantized here, from its bf16 values (the operand the unfused path would quantize),
+      // by the OCP rule of the row-wise quantizer:
+      //   * along 2I (FC1 dgrad's K): a row's 32-column block lies in lanes l and l ^ 32, 16
+      //     values each -- codes go out 8 bytes per run, the scale byte from the lane holding the
+      //     block's first columns;
+      //   * along the expert's tokens (FC1 wgrad's K), into the transposed layout whose segments
+      //     are padded to 128 tokens: the wave writes the bf16 block to its LDS slot row by row and
+      //     reads it back with transposing reads, lane l getting column l % 32 at rows
+      //     16 (l / 32) + [0, 16); the column's 32-row block lies in lanes l and l ^ 32.  Blocks
+      //     past the segment's padded end are left alone (they belong to the next segment); rows
+      //     past the expert's tokens inside it are zero.
+      [[maybe_unused]] const uint32_t I2 = 2u * I32;
+      // (the row-wise outputs' descriptors end at the tile's last row; null-based with no range in BF16)
+      [[maybe_unused]] const rsrc_t rq = make_rsrc(kQ ? p.dgu_q + (int64_t)cur.row0 * 2 * I : nullptr, kQ ? mr * I2 : 0u);
+      [[maybe_unused]] const rsrc_t rqs =
+          make_rsrc(kQ ? p.dgu_s + (int64_t)cur.row0 * (2 * I / 32) : nullptr, kQ ? mr * (I2 / 32) : 0u);
+      // one 32-column block of dG (half 0) or dU (half 1): w0 / w1 its runs pp = 0 / 1.  The scale
+      // bytes are collected into words, so that they leave as 4-byte stores: a row's bytes of the
+      // wave's 4 column blocks (rword, byte j), and a column's bytes of the wave's 4 row blocks
+      // (cword, byte i) -- both 4-byte aligned, as I % 128 == 0 and segments start at multiples of 128.
+      auto quant_half = [&](const u32x4 w0, const u32x4 w1, int half, int i, int j, uint32_t& rword,
+                            uint32_t& cword) {
+        const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
+        const int srel = cur.mt * kBM + wm * 128 + i * 32;                   // block's first segment row
+        const bool tv = srel < (cur.Me + 127) / 128 * 128;                   // wave-uniform
+        uint8_t* lt = smem + kTOff + wave * 2048;
+        const int G4 = elane >> 4, sl = elane & 15;
+        const uint32_t rd = (uint32_t)(16 * (G4 >> 1) + sl / 4) * 64u + (uint32_t)(16 * (G4 & 1) + 4 * (sl & 3)) * 2u;
+        {
+          const uint32_t colg = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);   // dGU column
+          float v[16];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            v[2 * x] = bf16_to_f32((uint16_t)(w0[x] & 0xFFFF));
+            v[2 * x + 1] = bf16_to_f32((uint16_t)(w0[x] >> 16));
+            v[8 + 2 * x] = bf16_to_f32((uint16_t)(w1[x] & 0xFFFF));
+            v[8 + 2 * x + 1] = bf16_to_f32((uint16_t)(w1[x] >> 16));
+          }
+          float am = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
+          am = max_xor32(am);
+          const int sx = mx_shared_exp(am);
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const u32x2 c{mx_pack4(v[8 * pp], v[8 * pp + 1], v[8 * pp + 2], v[8 * pp + 3], sx),
+                          mx_pack4(v[8 * pp + 4], v[8 * pp + 5], v[8 * pp + 6], v[8 * pp + 7], sx)};
+            __builtin_amdgcn_raw_buffer_store_b64(c, rq, m * I2 + colg + 16u * pp + 8u * (uint32_t)(elane >> 5), 0, 0);
+          }
+          rword |= (uint32_t)(sx + 127) << (8 * j);
+          if (tv) {
+            *reinterpret_cast<u32x4*>(lt + r32 * 64 + (8 * (elane >> 5)) * 2) = w0;
+            *reinterpret_cast<u32x4*>(lt + r32 * 64 + (16 + 8 * (elane >> 5)) * 2) = w1;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
+            const auto base = (__attribute__((address_space(3))) uint8_t*)(lt);
+            float t[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + rd + q * 256u));
+#pragma unroll
+              for (int x = 0; x < 4; ++x) t[4 * q + x] = (float)r[x];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            float at = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) at = fmaxf(at, fabsf(t[r]));
+            at = max_xor32(at);
+            const int st = mx_shared_exp(at);
+            const u32x4 c{mx_pack4(t[0], t[1], t[2], t[3], st), mx_pack4(t[4], t[5], t[6], t[7], st),
+                          mx_pack4(t[8], t[9], t[10], t[11], st), mx_pack4(t[12], t[13], t[14], t[15], st)};
+            // through descriptors over the block's 32 transposed rows: a split_sizes array that does
+            // not match rows_pad cannot take the stores outside the buffers
+            const uint32_t rp = (uint32_t)p.rows_pad, prow = (uint32_t)(cur.poff + srel);
+            const rsrc_t rt = make_rsrc(p.dgu_tq + (int64_t)colg * p.rows_pad, 32u * rp);
+            __builtin_amdgcn_raw_buffer_store_b128(c, rt, (uint32_t)(elane & 31) * rp + prow + 16u * (uint32_t)(elane >> 5),
+                                                   0, 0);
+            cword |= (uint32_t)(st + 127) << (8 * i);
+          }
+        }
+      };
+      [[maybe_unused]] uint32_t rsw[2] = {0u, 0u};                    // row scale words (current i)
+      [[maybe_unused]] uint32_t csw[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};   // column ones, by j
       float part[4] = {0.f, 0.f, 0.f, 0.f};
       load(0, 0);
 #pragma unroll
@@ -472,6 +568,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
               dh[8 * pp + c] = __builtin_bit_cast(float, (uint32_t)r[0]);
               dh[8 * pp + 4 + c] = __builtin_bit_cast(float, (uint32_t)r[1]);
             }
+          u32x4 gb[2], ub[2];   // dG, dU in bf16: 8 consecutive columns 16 pp + 8 hh + [0, 8) each
 #pragma unroll
           for (int pp = 0; pp < 2; ++pp) {
             float dgv[8], duv[8];
@@ -488,16 +585,52 @@ void bwd_gemm_kernel(const BwdKArgs p) {
               duv[x] = da * sl;
               dgv[x] = da * uu * (sg * (1.0f + g * (1.0f - sg)));
             }
-            const uint32_t o = boff(blk, pp);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3]),
-                                                         pack_bf16x2(dgv[4], dgv[5]), pack_bf16x2(dgv[6], dgv[7])},
-                                                   rdg, o, 0, 0);
-            __builtin_amdgcn_raw_buffer_store_b128(u32x4{pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3]),
-                                                         pack_bf16x2(duv[4], duv[5]), pack_bf16x2(duv[6], duv[7])},
-                                                   rdg, o + I32 * 2u, 0, 0);
+            gb[pp] = u32x4{pack_bf16x2(dgv[0], dgv[1]), pack_bf16x2(dgv[2], dgv[3]), pack_bf16x2(dgv[4], dgv[5]),
+                           pack_bf16x2(dgv[6], dgv[7])};
+            ub[pp] = u32x4{pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3]), pack_bf16x2(duv[4], duv[5]),
+                           pack_bf16x2(duv[6], duv[7])};
+            if (!kQ || p.dgu) {
+              const uint32_t o = boff(blk, pp);
+              __builtin_amdgcn_raw_buffer_store_b128(gb[pp], rdg, o, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(ub[pp], rdg, o + I32 * 2u, 0, 0);
+            }
+          }
+          if constexpr (kQ) {
+            quant_half(gb[0], gb[1], 0, i, j, rsw[0], csw[j][0]);
+            quant_half(ub[0], ub[1], 1, i, j, rsw[1], csw[j][1]);
+            if (j == 3) {
+              // the row's scale words of the wave's 4 column blocks, dG then dU
+              const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
+#pragma unroll
+              for (int half = 0; half < 2; ++half) {
+                const uint32_t cb = ((half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128)) / 32;
+                const uint32_t so = (elane >> 5) == 0 ? m * (I2 / 32) + cb : 0xFFFFFFF0u;
+                __builtin_amdgcn_raw_buffer_store_b32(rsw[half], rqs, so, 0, 0);
+                rsw[half] = 0;
+              }
+            }
           }
         }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (kQ) {
+        // a column's scale words of the wave's 4 row blocks: the wave's 128 rows lie wholly inside
+        // the expert's 128-padded segment or wholly past it
+        const int srel = cur.mt * kBM + wm * 128;
+        if (srel < (cur.Me + 127) / 128 * 128) {
+          const uint32_t rp = (uint32_t)p.rows_pad, prow = (uint32_t)(cur.poff + srel);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if (n0 + wn * 128 + j * 32 >= I) continue;   // wave-uniform
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+              const uint32_t colg = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);
+              const rsrc_t rts = make_rsrc(p.dgu_ts + (int64_t)colg * (p.rows_pad / 32), 32u * (rp / 32));
+              const uint32_t tso = (elane >> 5) == 0 ? (uint32_t)(elane & 31) * (rp / 32) + prow / 32 : 0xFFFFFFF0u;
+              __builtin_amdgcn_raw_buffer_store_b32(csw[j][half], rts, tso, 0, 0);
+            }
+          }
+        }
       }
       // per-row partial over the tile's 256 columns: the lane pair (l, l ^ 32) holds a row's 128
       // columns of this wave, the two waves of a row block the two halves -- fixed-order sums
@@ -591,6 +724,11 @@ BwdKArgs base_args(const BwdGemm& g) {
   k.gu = g.gu;
   k.prob_perm = g.prob_perm;
   k.dgu = g.dgu;
+  k.dgu_q = g.dgu_q;
+  k.dgu_s = g.dgu_s;
+  k.dgu_tq = g.dgu_tq;
+  k.dgu_ts = g.dgu_ts;
+  k.rows_pad = g.rows_pad;
   k.dprob_part = g.dprob_part;
   k.I = g.I;
   k.out = reinterpret_cast<uint8_t*>(g.out);
@@ -628,5 +766,31 @@ hipError_t launch_bwd_wgrad(const BwdGemm& g, bool mx, hipStream_t st) {
 }
 
 int bwd_dprob_parts(int64_t I) { return (int)((I + kBN - 1) / kBN); }
+
+namespace {
+// Row r's scale bytes from the end of the last 128-padded segment to ld: zero.  Every workgroup
+// recomputes that end from split_sizes.
+__global__ __launch_bounds__(256) void scale_tail_zero_kernel(uint8_t* __restrict__ scales, int64_t rows, int64_t ld,
+                                                              const int32_t* __restrict__ split_sizes, int E) {
+  __shared__ int s_end;
+  if (threadIdx.x == 0) {
+    int64_t pt = 0;
+    for (int e = 0; e < E; ++e) pt += ((int64_t)max(split_sizes[e], 0) + 127) / 128 * 128;
+    s_end = (int)min(pt / 32, ld);
+  }
+  __syncthreads();
+  const int64_t b0 = s_end, n = ld - b0;
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x)
+    for (int64_t c = threadIdx.x; c < n; c += 256) scales[r * ld + b0 + c] = 0;
+}
+}  // namespace
+
+hipError_t launch_scale_tail_zero(uint8_t* scales, int64_t rows, int64_t ld, const int32_t* split_sizes, int E,
+                                  hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const unsigned g = (unsigned)(rows < 4096 ? rows : 4096);
+  scale_tail_zero_kernel<<<g, 256, 0, st>>>(scales, rows, ld, split_sizes, E);
+  return hipGetLastError();
+}
 
 }  // namespace moe

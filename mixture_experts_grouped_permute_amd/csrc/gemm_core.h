@@ -468,6 +468,15 @@ __device__ __forceinline__ void swap_runs8(const uint32_t (&c)[4], u32x2 (&o)[2]
   }
 }
 
+// max(v, v of lane l ^ 32) by v_permlane32_swap (a VALU exchange of the wave's halves, no LDS round
+// trip): swapping a register with itself leaves each lane its own value in one result and its
+// partner's in the other.
+__device__ __forceinline__ float max_xor32(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 // Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
 // allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
 // and spills.

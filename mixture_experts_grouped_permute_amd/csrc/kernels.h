@@ -138,9 +138,14 @@ struct BwdGemm {
   const int32_t* split_sizes;
   const uint16_t* gu;
   const float* prob_perm;
-  uint16_t* dgu;
+  uint16_t* dgu;            // bf16 dGU (BF16; MXFP8 only when asked for, as a debug output)
   float* dprob_part;
   int64_t I;
+  // MXFP8 FC2 dgrad: dGU quantized in the epilogue, along 2I (row-wise, [R, 2I] + [R, 2I/32]) and
+  // along each expert's tokens (transposed [2I, rows_pad] + [2I, rows_pad/32], segments padded to
+  // 128 tokens)
+  uint8_t *dgu_q, *dgu_s, *dgu_tq, *dgu_ts;
+  int64_t rows_pad;
   void* out;
   bool out_f32;
   float* part;              // FC1 dgrad: split-tile partials (kFc2PartBytes), or null for no split
@@ -148,6 +153,9 @@ struct BwdGemm {
 hipError_t launch_bwd_dgrad_fc2(const BwdGemm& g, bool mx, hipStream_t st);
 hipError_t launch_bwd_dgrad_fc1(const BwdGemm& g, bool mx, hipStream_t st);
 hipError_t launch_bwd_wgrad(const BwdGemm& g, bool mx, hipStream_t st);
+// zero the scale bytes of the transposed operand past its last 128-padded segment ([rows, ld])
+hipError_t launch_scale_tail_zero(uint8_t* scales, int64_t rows, int64_t ld, const int32_t* split_sizes, int E,
+                                  hipStream_t st);
 int bwd_dprob_parts(int64_t I);
 
 }  // namespace moe

@@ -52,7 +52,7 @@ def test_binding_lists_every_declared_symbol():
 
 
 def test_version_status_and_phase_names(lib):
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     lib.moe_status_string.restype = ctypes.c_char_p
     for s in range(5):
         assert lib.moe_status_string(s)
@@ -248,6 +248,38 @@ def test_bwd_cached_transposed_weight_validation(lib):
     assert lib.moe_grouped_mlp_bwd(ctypes.byref(args(w1tq=0x2000)), None) == MOE_ERR_INVALID_ARG
     bf = args(compute=1, w1tq=0x2000, w1ts=0x2000, w2tq=0x2000, w2ts=0x2000)
     assert lib.moe_grouped_mlp_bwd(ctypes.byref(bf), None) == MOE_ERR_INVALID_ARG
+
+
+def test_bwd_fused_dgu_debug_validation(lib):
+    """ABI 5: the MXFP8 backward quantizes dGU in the FC2 dgrad epilogue and keeps no bf16 dGU in its
+    workspace; the five debug outputs go all together, MXFP8 only, and replace workspace buffers."""
+    from mixture_experts_grouped_permute_amd._lib import BwdArgs, MOE_ERR_INVALID_ARG
+    E, T, k, H, I = 8, 4096, 2, 4096, 14336
+    R = T * k
+    tab = (ctypes.c_void_p * E)(*([0x1000] * E))
+
+    def args(**kw):
+        a = BwdArgs(T=T, H=H, I=I, E=E, k=k, compute=2, io_dtype=1, dw_dtype=0, dy=0x1000, w1=tab, w2=tab,
+                    split_sizes=0x1000, offsets=0x1000, row_id_map=0x1000, src_index=0x1000, prob_perm=0x1000,
+                    saved_x_perm=0x1000, saved_gu=0x1000, saved_h=0x1000, dx=0x1000, dprob=0x1000, dw1=tab, dw2=tab)
+        for k_, v in kw.items():
+            setattr(a, k_, v)
+        return a
+
+    lib.moe_grouped_mlp_bwd_workspace.restype = ctypes.c_size_t
+    dbg = dict(dgu_bf16=0x2000, dgu_codes=0x2000, dgu_scales=0x2000, dgu_t_codes=0x2000, dgu_t_scales=0x2000)
+    mx = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(args()))
+    bf = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(args(compute=1)))
+    with_dbg = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(args(**dbg)))
+    rp = (R + 127) // 128 * 128 + 128 * E
+    # the debug buffers replace the two quantized copies of dGU (row-wise and along tokens)
+    assert 0 < with_dbg < mx and mx - with_dbg >= R * 2 * I + 2 * I * rp
+    # bf16 dGU lives in the BF16 workspace only
+    assert bf > 0
+    for name in dbg:
+        one = {name: 0x2000}
+        assert lib.moe_grouped_mlp_bwd(ctypes.byref(args(**one)), None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_grouped_mlp_bwd(ctypes.byref(args(compute=1, **dbg)), None) == MOE_ERR_INVALID_ARG
 
 
 def test_noalloc_permute_limit_on_host(lib):

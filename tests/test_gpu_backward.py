@@ -11,6 +11,7 @@ from gpu_util import BF16_TOL, MXFP8_TOL, cfg_small, gpu, log, need_gpu, to_np
 from moe_inputs import get_config, make_inputs
 from moe_inputs.generate import routing_with_counts
 from oracle import mlp
+from oracle import numerics as nm
 
 CASES = [
     ("cfg1-tiny-f32io", get_config(1), None),
@@ -118,3 +119,52 @@ def test_forward_flag_survives_backward():
     m.moe_grouped_mlp_bwd(d.dy, ctx, d.w1, d.w2)
     assert m.moe_read_device_error(ctx_bad["error_flag"]) == 1
     assert m.moe_read_device_error(ctx["error_flag"]) == 0
+
+
+def _check_fused_dgu(dbg, offsets, I, log_name):
+    """The FC2 dgrad epilogue's MXFP8 dGU against the oracle's quantizer applied to the kernel's own
+    bf16 dGU: row-wise along 2I, and along each expert's tokens in the 128-padded transposed layout
+    (the 32-padded oracle layout, each segment moved to its 128-aligned start, zeros up to it), with
+    the scale bytes past the last segment zero."""
+    dgu = dbg["dgu_bf16"].cpu().to(torch.float64).numpy()
+    rc, rs = nm.quantize_mxfp8(dgu, axis=1)
+    np.testing.assert_array_equal(dbg["dgu_codes"].cpu().numpy(), rc)
+    np.testing.assert_array_equal(dbg["dgu_scales"].cpu().numpy(), rs)
+    tc, ts = nm.quantize_mxfp8_segments_t(dgu, offsets)
+    gq, gs = dbg["dgu_t_codes"].cpu().numpy(), dbg["dgu_t_scales"].cpu().numpy()
+    p32 = p128 = 0
+    for e in range(len(offsets) - 1):
+        me = int(offsets[e + 1] - offsets[e])
+        n32, n128 = (me + 31) // 32 * 32, (me + 127) // 128 * 128
+        np.testing.assert_array_equal(gq[:, p128:p128 + n32], tc[:, p32:p32 + n32], err_msg=f"codes e={e}")
+        np.testing.assert_array_equal(gs[:, p128 // 32:(p128 + n32) // 32], ts[:, p32 // 32:(p32 + n32) // 32],
+                                      err_msg=f"scales e={e}")
+        assert not gq[:, p128 + n32:p128 + n128].any() and not gs[:, (p128 + n32) // 32:(p128 + n128) // 32].any()
+        p32 += n32
+        p128 += n128
+    assert not gs[:, p128 // 32:].any()
+    log(f"  {log_name}: fused dGU quantizer bytes equal (rows {dgu.shape[0]}, 2I {2 * I}, segment end {p128})")
+
+
+@gpu
+@pytest.mark.parametrize("name,cfg,counts", [c for c in CASES if c[1].H % 128 == 0 and c[1].I % 128 == 0],
+                         ids=[c[0] for c in CASES if c[1].H % 128 == 0 and c[1].I % 128 == 0])
+def test_fused_dgu_quantizer_bytes(name, cfg, counts):
+    """MXFP8: the dGU bytes the FC2 dgrad epilogue writes for both FC1 GEMMs are bit-exact against
+    the oracle's OCP quantizer of the epilogue's own bf16 dGU; that bf16 dGU is within the MXFP8
+    tolerance of the oracle's."""
+    m = need_gpu()
+    log(f"fused dGU quantizer {name} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k}")
+    inp = _inputs(cfg, counts)
+    d = inp.to("cuda")
+    out, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", save_for_backward=True)
+    dbg = {}
+    m.moe_grouped_mlp_bwd(d.dy, ctx, d.w1, d.w2, debug=dbg)
+    torch.cuda.synchronize()
+    offsets = ctx["perm"]["offsets"].cpu().numpy()
+    _check_fused_dgu(dbg, offsets, cfg.I, name)
+    fw = mlp.forward(inp.x, inp.topk_idx.numpy(), inp.topk_prob, inp.w1, inp.w2, "mxfp8", cfg.x_dtype)
+    bw = mlp.backward(fw, inp.x, inp.dy, inp.w1, inp.w2)
+    err = mlp.normwise_rel_err(dbg["dgu_bf16"].cpu().to(torch.float64).numpy(), bw.dgu)
+    log(f"  dgu vs oracle {err:.2e}")
+    assert err < MXFP8_TOL
