@@ -116,7 +116,7 @@ def _flusher():
     return lambda: buf.fill_(1.0)
 
 
-def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0):
+def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0, per_call_wt=False):
     import torch
     import mixture_experts_grouped_permute_amd as m
     from mixture_experts_grouped_permute_amd import _lib as L
@@ -160,13 +160,34 @@ def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0):
         def call(evs):
             L._check(lib.moe_grouped_mlp_fwd_ex(ctypes.byref(a), stream, evs), "fwd")
     else:
+        # MXFP8 training: by default the forward quantizes the weights along the backward's K too
+        # (one read of the bf16 masters for both); per_call_wt: the backward quantizes them itself
+        qfb = (not per_call_wt) if cfg.precision == "mxfp8" else None
         _, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision,
-                                       save_for_backward=True)
+                                       save_for_backward=True, quantize_for_backward=qfb)
         perm = ctx["perm"]
-        wqt = None
-        if cached:   # W1, W2 quantized along the backward's K once, outside the timed region
-            wqt = m.quantize_weights(d.w1, d.w2, cfg.precision, transposed=True)
-        a, outs, keep = L._bwd_args(d.dy, ctx, d.w1, d.w2, torch.float32, w_quant_t=wqt)
+        # the forward as a training step runs it (saving for the backward), timed the same way
+        fout = torch.empty((T, H), dtype=d.x.dtype, device=dev)
+        fa, fkeep, _, _ = L._fwd_args(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, cfg.precision, fout, perm,
+                                      ctx["saved"])
+        if ctx.get("w_quant_t") is not None:
+            fa.w1tq_out, fa.w1ts_out, fa.w2tq_out, fa.w2ts_out = (t.data_ptr() for t in ctx["w_quant_t"])
+        fneed = lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(fa))
+        if fneed == 0:
+            raise RuntimeError("argument validation failed")
+        fws = torch.empty(fneed, dtype=torch.uint8, device=dev)
+        fa.workspace, fa.workspace_bytes = fws.data_ptr(), fws.numel()
+        fnph = lib.moe_fwd_phase_count()
+        fnames = [lib.moe_fwd_phase_name(i).decode() for i in range(fnph)]
+
+        def fcall(evs):
+            L._check(lib.moe_grouped_mlp_fwd_ex(ctypes.byref(fa), stream, evs), "fwd")
+        _log("timing the forward that saves for the backward")
+        fms, fper, _ = _time_ex(lib, hip, fcall, fnph, steps, warmup)
+        fwd_save = {"ms_per_step": fms,
+                    "phase_ms": {n: sum(r[i] for r in fper) / len(fper) for i, n in enumerate(fnames)}}
+        del fws, fkeep
+        a, outs, keep = L._bwd_args(d.dy, ctx, d.w1, d.w2, torch.float32)
         need = lib.moe_grouped_mlp_bwd_workspace(ctypes.byref(a))
         if need == 0:
             raise RuntimeError("argument validation failed")
@@ -190,6 +211,8 @@ def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0):
                        "phase_ms": {n: _stats([r[i] for r in cold_ph]) for i, n in enumerate(names)}}
     res["split_sizes"] = perm["split_sizes"].cpu().tolist()
     res["inputs"] = inp
+    if backward:
+        res["fwd_save"] = fwd_save
     del keep
     return res
 
@@ -303,8 +326,8 @@ def copy_leg(reps=10):
     return res
 
 
-def bwd_leg(cfg, steps, warmup, cached=False):
-    r = run_gpu(cfg, steps, warmup, backward=True, cached=cached)
+def bwd_leg(cfg, steps, warmup, per_call_wt=False):
+    r = run_gpu(cfg, steps, warmup, backward=True, per_call_wt=per_call_wt)
     ms = r["ms_per_step"]
     ph = r["phase_ms"]
     R, H, I = cfg.R, cfg.H, cfg.I
@@ -320,6 +343,12 @@ def bwd_leg(cfg, steps, warmup, cached=False):
         "gemm_tflops": {k_: round(v / (ph[k_] * 1e-3) / 1e12, 1) for k_, v in gem.items()},
         "phase_ms": {k_: round(v, 4) for k_, v in ph.items()},
         "stats": r["stats"],
+        # the forward of the same training step (saving for the backward; under MXFP8 it also
+        # quantizes the weights along the backward's K) and the step's total
+        "forward_with_save_ms": round(r["fwd_save"]["ms_per_step"], 4),
+        "forward_with_save_phase_ms": {k_: round(v, 4) for k_, v in r["fwd_save"]["phase_ms"].items()},
+        "train_step_ms": round(r["fwd_save"]["ms_per_step"] + ms, 4),
+        "train_step_tokens_per_s": round(cfg.T / ((r["fwd_save"]["ms_per_step"] + ms) * 1e-3), 1),
     }
 
 
@@ -589,13 +618,13 @@ def main():
         torch.cuda.empty_cache()
         line["backward_mxfp8"] = bwd_leg(get_config(4).with_(precision="mxfp8"), max(2, args.steps // 2),
                                          max(1, args.warmup // 2))
-        # the same with W1, W2 quantized along the backward's K once (e.g. once per optimizer step
-        # under gradient accumulation) and passed in
+        # the same step with the backward quantizing W1, W2 along its K itself (the forward quantizing
+        # only its own copy)
         torch.cuda.empty_cache()
         rc = bwd_leg(get_config(4).with_(precision="mxfp8"), max(2, args.steps // 2), max(1, args.warmup // 2),
-                     cached=True)
-        line["backward_mxfp8"]["cached_weights"] = {"ms_per_step": rc["ms_per_step"], "value": rc["value"],
-                                                    "phase_ms": rc["phase_ms"]}
+                     per_call_wt=True)
+        line["backward_mxfp8"]["per_call_weights"] = {
+            k_: rc[k_] for k_ in ("ms_per_step", "value", "phase_ms", "forward_with_save_ms", "train_step_ms")}
     print(json.dumps(line), flush=True)
 
 

@@ -305,6 +305,16 @@ moe_status moe_route_permute(const void* logits, int logits_dtype, const void* x
  * silu(g) * u * p in fp32 exactly as it computed it, before rounding it to
  * bf16 or quantizing it -- the input of the fused quantizer, so that its
  * bytes can be checked against mxfp8_quantize's rule.  NULL in production.
+ * w1tq_out, w1ts_out, w2tq_out, w2ts_out: optional (ABI version 6; MXFP8
+ * compute with per-call weight quantization only -- not with w1q..w2s --
+ * all four or none, else MOE_ERR_INVALID_ARG): caller buffers [E, H, 2I],
+ * [E, H, 2I/32], [E, I, H], [E, I, H/32] that receive the weights quantized
+ * along the backward's K as well, the very bytes mxfp8_quantize_weights
+ * (axis 1) gives and moe_grouped_mlp_bwd's w1tq..w2ts take: the per-call
+ * quantization then reads each bf16 weight once for both orientations (page
+ * "How BioNeMo cuts overhead", How MXFP8 reduces memory use: the masters are
+ * converted for each low-precision GEMM, forward and backward).  Experts
+ * without tokens are skipped, as in the forward's own copy.
  * ------------------------------------------------------------------------ */
 typedef struct {
   int64_t T, H, I;
@@ -337,6 +347,10 @@ typedef struct {
   uint8_t* h_codes;             /* [R, I]    E4M3, or NULL (ABI version 4) */
   uint8_t* h_scales;            /* [R, I/32] E8M0 */
   float* h_f32;                 /* [R, I]    fp32, or NULL (ABI version 4) */
+  uint8_t* w1tq_out;            /* [E, H, 2I]    E4M3, or NULL (ABI version 6) */
+  uint8_t* w1ts_out;            /* [E, H, 2I/32] E8M0 */
+  uint8_t* w2tq_out;            /* [E, I, H]     E4M3 */
+  uint8_t* w2ts_out;            /* [E, I, H/32]  E8M0 */
 } moe_mlp_fwd_args;
 
 size_t moe_grouped_mlp_fwd_workspace(const moe_mlp_fwd_args* a);
@@ -457,7 +471,8 @@ const char* moe_bwd_phase_name(int i);   /* NULL when out of range */
  * (the caller obtains them, e.g. from a previous permutation; they must equal
  * the counts the device computes, which is the caller's responsibility; their
  * sum must be T*k).  Results equal moe_grouped_mlp_fwd's up to fp32
- * accumulation order.
+ * accumulation order.  The transposed-weight outputs (w1tq_out ..) are not
+ * offered here (MOE_ERR_UNSUPPORTED).
  * ------------------------------------------------------------------------ */
 moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* split_sizes_host, void* stream);
 

@@ -57,6 +57,7 @@ class FwdArgs(ctypes.Structure):
         ("w1q", _vp), ("w1s", _vp), ("w2q", _vp), ("w2s", _vp),
         ("w1_scale", _vp), ("w2_scale", _vp),
         ("error_flag", _vp), ("h_codes", _vp), ("h_scales", _vp), ("h_f32", _vp),
+        ("w1tq_out", _vp), ("w1ts_out", _vp), ("w2tq_out", _vp), ("w2ts_out", _vp),
     ]
 
 
@@ -480,11 +481,14 @@ def quantize_weights(w1, w2, compute: str = "mxfp8", transposed: bool = False):
 
 def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torch.Tensor, w1, w2,
                         compute: str = "bf16", save_for_backward: bool = False, workspace: Optional[torch.Tensor] = None,
-                        w_quant=None, debug_h: bool = False):
+                        w_quant=None, debug_h: bool = False, quantize_for_backward: Optional[bool] = None):
     """Grouped expert MLP forward.  w1: [E,2I,H] tensor or E tensors [2I,H] (bf16);
     w2: [E,H,I] or E tensors [H,I].  compute: "bf16", "mxfp8" or "fp8" (per-tensor scales,
     forward only).  w_quant: optional quantize_weights(w1, w2, compute) output ("mxfp8" or
     "fp8"): the per-call weight quantization is skipped.
+    quantize_for_backward (MXFP8 with save_for_backward and per-call weight quantization; the
+    default there): the same read of the bf16 weights also quantizes them along the backward's K,
+    into ctx["w_quant_t"], which moe_grouped_mlp_bwd then uses.
     debug_h: also return, in ctx["debug"], h in fp32 as FC1's epilogue computed it ("h_f32",
     [R, I], permuted rows) and, under MXFP8, the E4M3 codes and E8M0 scales its fused quantizer
     wrote ("h_codes" [R, I], "h_scales" [R, I/32]).
@@ -517,6 +521,16 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
             debug["h_codes"] = torch.empty((R, I), dtype=torch.uint8, device=dev)
             debug["h_scales"] = torch.empty((R, I // 32), dtype=torch.uint8, device=dev)
             a.h_codes, a.h_scales = debug["h_codes"].data_ptr(), debug["h_scales"].data_ptr()
+    wqt = None
+    if quantize_for_backward is None:
+        quantize_for_backward = save_for_backward and compute == "mxfp8" and w_quant is None
+    if quantize_for_backward:
+        if not (save_for_backward and compute == "mxfp8" and w_quant is None):
+            raise ValueError("quantize_for_backward needs save_for_backward, mxfp8 and per-call weights")
+        u8 = lambda *shape: torch.empty(shape, dtype=torch.uint8, device=dev)
+        Hh = x.shape[1]
+        wqt = (u8(E, Hh, 2 * I), u8(E, Hh, 2 * I // 32), u8(E, I, Hh), u8(E, I, Hh // 32))
+        a.w1tq_out, a.w1ts_out, a.w2tq_out, a.w2ts_out = (t.data_ptr() for t in wqt)
     if w_quant is not None:
         for t in w_quant:
             if t.device != dev:
@@ -534,7 +548,7 @@ def moe_grouped_mlp_fwd(x: torch.Tensor, topk_idx: torch.Tensor, topk_prob: torc
     a.workspace, a.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(lib.moe_grouped_mlp_fwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_fwd")
     ctx = {"perm": perm, "saved": saved, "compute": compute, "E": E, "I": I, "error_flag": flag,
-           "workspace": ws, "_keep": keep}
+           "workspace": ws, "_keep": keep, "w_quant_t": wqt}
     if debug is not None:
         ctx["debug"] = debug
     return out, ctx
@@ -594,6 +608,8 @@ def _bwd_args(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.float32, w_qua
     a.saved_x_perm, a.saved_gu, a.saved_h = _ptr(saved["x_perm"]), _ptr(saved["gu"]), _ptr(saved["h"])
     a.dx, a.dprob = _ptr(dx), _ptr(dprob)
     a.dw1, a.dw2 = dw1t, dw2t
+    if w_quant_t is None:
+        w_quant_t = ctx.get("w_quant_t")   # quantized by the forward, if it was asked to
     if w_quant_t is not None:
         for t in w_quant_t:
             _need(t, torch.uint8, dev, "cached transposed weights")

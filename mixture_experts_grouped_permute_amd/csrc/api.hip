@@ -182,6 +182,9 @@ moe_status validate_fwd(const moe_mlp_fwd_args* a) {
   if (any_saved && !all_saved) return MOE_ERR_INVALID_ARG;
   if (any_saved && a->compute == MOE_FP8_E4M3) return MOE_ERR_UNSUPPORTED;   // forward only
   if ((a->h_codes != nullptr) != (a->h_scales != nullptr)) return MOE_ERR_INVALID_ARG;
+  const bool any_wt = a->w1tq_out || a->w1ts_out || a->w2tq_out || a->w2ts_out;
+  const bool all_wt = a->w1tq_out && a->w1ts_out && a->w2tq_out && a->w2ts_out;
+  if (any_wt && (!all_wt || a->compute != MOE_MXFP8_E4M3 || any_q)) return MOE_ERR_INVALID_ARG;
   if (a->h_codes && a->compute != MOE_MXFP8_E4M3) return MOE_ERR_INVALID_ARG;
   // 32-bit buffer ranges inside the GEMMs: every descriptor spans one 256-row tile of an
   // activation or one expert's weight matrix, so the limit is on an expert's weights (in bf16),
@@ -389,7 +392,7 @@ constexpr int kMaxDevices = 64;
 
 extern "C" {
 
-int moe_abi_version(void) { return 5; }
+int moe_abi_version(void) { return 6; }
 
 const char* moe_status_string(int status) {
   switch (status) {
@@ -608,9 +611,17 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
     if (a->saved_x_perm)
       HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, a->saved_x_perm, nullptr, false, st));
     MOE_CHECK(mark(2), MOE_ERR_HIP);
-    if (!a->w1q) HIP_TRY(launch_mx_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.w1s, a->split_sizes, st));
+    // per-call weight quantization; with the backward's transposed copies requested, one read of
+    // each bf16 weight gives both
+    if (!a->w1q && a->w1tq_out)
+      HIP_TRY(launch_mx_quant_weights_t(a->w1, E, 2 * I, H, a->w1tq_out, a->w1ts_out, a->split_sizes, st, p.w1q, p.w1s));
+    else if (!a->w1q)
+      HIP_TRY(launch_mx_quant_weights(a->w1, E, 2 * I, H, p.w1q, p.w1s, a->split_sizes, st));
     MOE_CHECK(mark(3), MOE_ERR_HIP);
-    if (!a->w1q) HIP_TRY(launch_mx_quant_weights(a->w2, E, H, I, p.w2q, p.w2s, a->split_sizes, st));
+    if (!a->w1q && a->w2tq_out)
+      HIP_TRY(launch_mx_quant_weights_t(a->w2, E, H, I, a->w2tq_out, a->w2ts_out, a->split_sizes, st, p.w2q, p.w2s));
+    else if (!a->w1q)
+      HIP_TRY(launch_mx_quant_weights(a->w2, E, H, I, p.w2q, p.w2s, a->split_sizes, st));
   } else {
     HIP_TRY(launch_permute_rows(a->x, x_f32, T, H, k, a->row_id_map, p.x_op, nullptr, false, st));
     MOE_CHECK(mark(2), MOE_ERR_HIP);
@@ -667,6 +678,7 @@ moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* sp
   if (s != MOE_OK) return s;
   MOE_CHECK(split_sizes_host != nullptr, MOE_ERR_INVALID_ARG);
   MOE_CHECK(a->compute != MOE_FP8_E4M3, MOE_ERR_UNSUPPORTED);
+  MOE_CHECK(!a->w1tq_out, MOE_ERR_UNSUPPORTED);   // the baseline quantizes the forward's copy only
   int64_t sum = 0;
   for (int e = 0; e < a->E; ++e) {
     MOE_CHECK(split_sizes_host[e] >= 0, MOE_ERR_INVALID_ARG);

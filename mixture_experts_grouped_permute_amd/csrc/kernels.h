@@ -38,8 +38,11 @@ hipError_t launch_mx_quant_weights(const void* const* w, int E, int64_t rows, in
 // Column-wise MXFP8 of E bf16 weight matrices [rows, cols] (rows % 32 == 0) of a host pointer table
 // in one launch, transposed: matrix e's codes [cols, rows] at q + e * cols * rows, its scales
 // [cols, rows / 32] at scales + e * cols * rows / 32; skip_if_empty as launch_mx_quant_weights.
+// With q_rows / s_rows the same read also gives the row-wise codes [rows, cols] and scales
+// [rows, cols / 32] of every matrix (launch_mx_quant_weights' output), for cols % 32 == 0.
 hipError_t launch_mx_quant_weights_t(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
-                                     uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st);
+                                     uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st,
+                                     uint8_t* q_rows = nullptr, uint8_t* s_rows = nullptr);
 // Column-wise (blocks along rows, restarted per segment, transposed output); see mxfp8_quantize axis 1.
 // seg_align: segments are padded to a multiple of seg_align rows (32 for the C ABI; 128 when the
 // result feeds the variable-K wgrad GEMM, whose K steps are 128 values).

@@ -133,36 +133,17 @@ __global__ __launch_bounds__(256) void mx_weights_kernel(const WTab tab, int64_t
 //     scale byte, and puts its 32 codes in an LDS staging area [column][padded row];
 //   * the staged codes go out as 16-byte pieces with consecutive lanes along one output row, so
 //     a store instruction writes 8 whole 128-byte stretches of the transposed output.
-//
-// kTab: a table of E weight matrices instead of one x (blockIdx.z = matrix e, read from the
-// kernel-argument table; matrices with skip[e] == 0 are left alone), each a single segment with
-// rows % 32 == 0, matrix e's output at q + e * cols * rows_pad and scales + e * cols * rows_pad / 32.
 constexpr int kColRows = 128;   // padded rows per workgroup
 //
 // src_index (optional): row r of the segmented matrix is row src_index[r] / src_k of x (the
 // permuted rows of a token-major x, e.g. the gradient rows of the backward read straight from dY).
-template <bool kF32, bool kTab = false>
-__global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void* __restrict__ x, int64_t rows,
-                                                        int64_t cols, const int32_t* __restrict__ goff,
-                                                        int num_groups, int64_t rows_pad, uint8_t* __restrict__ q,
+
+template <bool kF32>
+__global__ __launch_bounds__(256) void mx_cols_kernel(const void* __restrict__ x, int64_t rows, int64_t cols,
+                                                        const int32_t* __restrict__ goff, int num_groups,
+                                                        int64_t rows_pad, uint8_t* __restrict__ q,
                                                         uint8_t* __restrict__ scales, int seg_align,
-                                                        const int32_t* __restrict__ skip,
                                                         const int32_t* __restrict__ src_index, int src_k) {
-  if constexpr (kTab) {
-    const int e = blockIdx.z;
-    if (skip && skip[e] == 0) return;
-#if defined(__HIP_DEVICE_COMPILE__)
-    x = reinterpret_cast<const uint16_t* const*>(
-        reinterpret_cast<const char*>(__builtin_amdgcn_kernarg_segment_ptr()))[e];
-#else
-    x = tab.w[e];
-#endif
-    q += (int64_t)e * cols * rows_pad;
-    scales += (int64_t)e * cols * (rows_pad / 32);
-  } else {
-    (void)tab;
-    (void)skip;
-  }
   __shared__ int s_pad[kMaxExperts + 1];
   __shared__ int s_off[kMaxExperts + 1];
   using TT = typename std::conditional<kF32, float, uint16_t>::type;
@@ -230,25 +211,42 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void
   }
   __syncthreads();
   const int64_t c0 = (int64_t)blockIdx.y * 64;
-  // the tile, in chunks of 8 values
+  // the tile, in chunks of 8 values: all four loads are issued before any is used (a chunk with no
+  // source reads x's first chunk unconditionally and is replaced by zeros, so that no branch
+  // separates the loads); rows == 0 leaves every chunk without a source
+  if (rows > 0) {
+    [[maybe_unused]] float v[4][8];
+    [[maybe_unused]] u32x4 wr[4];
+    bool ok[4];
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int id = t + 256 * it;                        // 1024 chunks: 128 rows x 8 chunks of 8 columns
-    const int rr = id >> 3, ck = id & 7;
-    const int64_t col = c0 + 8 * ck;
-    const int src = s_src[rr];
-    if constexpr (kF32) {
-      float v[8];
+    for (int it = 0; it < 4; ++it) {
+      const int id = t + 256 * it;                      // 1024 chunks: 128 rows x 8 chunks of 8 columns
+      const int rr = id >> 3, ck = id & 7;
+      const int64_t col = c0 + 8 * ck;
+      const int src = s_src[rr];
+      ok[it] = src >= 0 && col < cols;
+      const int64_t off = ok[it] ? (int64_t)src * cols + col : 0;
+      if constexpr (kF32) load8(x, true, off, v[it]);
+      else wr[it] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + off);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = 0.f;
-      if (src >= 0 && col < cols) load8(x, true, (int64_t)src * cols + col, v);
+    for (int it = 0; it < 4; ++it) {
+      const int id = t + 256 * it;
+      const int rr = id >> 3, ck = id & 7;
+      if constexpr (kF32) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) tile[rr][8 * ck + e] = v[e];
-    } else {
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (src >= 0 && col < cols)
-        w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(x) + (int64_t)src * cols + col);
-      *reinterpret_cast<u32x4*>(&tile[rr][8 * ck]) = w;
+        for (int e = 0; e < 8; ++e) tile[rr][8 * ck + e] = ok[it] ? v[it][e] : 0.f;
+      } else {
+        *reinterpret_cast<u32x4*>(&tile[rr][8 * ck]) = ok[it] ? wr[it] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int id = t + 256 * it;
+      const int rr = id >> 3, ck = id & 7;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tile[rr][8 * ck + e] = 0;
     }
   }
   __syncthreads();
@@ -286,6 +284,142 @@ __global__ __launch_bounds__(256) void mx_cols_kernel(const WTab tab, const void
     if (cc < cols && pb + 32 <= rows_pad)
       *reinterpret_cast<u32x4*>(q + cc * rows_pad + p0 + 16 * pc) =
           *reinterpret_cast<const u32x4*>(&ostage[lc][16 * pc]);
+  }
+}
+
+// Weight tables quantized column-wise into the transposed layout (the backward's dgrad operands:
+// blocks of 32 along the rows of each matrix), and with kRows also row-wise (the forward's: blocks
+// of 32 along the columns, mx_weights_kernel's layout and rule), from one read of the bf16 weights.
+// A workgroup takes a 128 x 128 tile of matrix blockIdx.z (rows % 32 == 0, cols % 32 == 0;
+// matrices with skip[e] == 0 are left alone):
+//   * the tile is loaded with 16-byte loads, 16 lanes per 256-byte row, and kept in LDS as bf16
+//     (rows padded by 16 bytes, so that the row-wise reads below hit distinct banks);
+//   * row-wise: thread t takes row t / 2, columns 64 (t % 2) + [0, 64) -- two blocks, 64 code bytes
+//     and 2 scale bytes, so the two threads of a row write its whole 128-byte stretch;
+//   * column-wise: thread t takes column t % 128, rows 64 (t / 128) + [0, 64) -- two blocks along
+//     the rows; their codes go to an LDS staging area [column][row] (rows padded by 16 bytes),
+//     from which consecutive lanes store a column's 128 bytes of the transposed output, 8 whole
+//     128-byte stretches per store instruction; the two scale bytes go out as one 2-byte word.
+// Matrix e's outputs: qt + e * cols * rows [cols, rows], st + e * cols * rows / 32 [cols, rows / 32],
+// qr + e * rows * cols [rows, cols], sr + e * rows * cols / 32 [rows, cols / 32].
+constexpr int kWT = 128;
+template <bool kRows>
+__global__ __launch_bounds__(256) void mx_wt_kernel(const WTab tab, int64_t rows, int64_t cols, uint8_t* __restrict__ qt,
+                                                    uint8_t* __restrict__ st, uint8_t* __restrict__ qr,
+                                                    uint8_t* __restrict__ sr, const int32_t* __restrict__ skip) {
+  const int e = blockIdx.z;
+  if (skip && skip[e] == 0) return;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint16_t* x = reinterpret_cast<const uint16_t* const*>(
+      reinterpret_cast<const char*>(__builtin_amdgcn_kernarg_segment_ptr()))[e];
+#else
+  const uint16_t* x = tab.w[e];
+#endif
+  qt += (int64_t)e * cols * rows;
+  st += (int64_t)e * cols * (rows / 32);
+  if constexpr (kRows) {
+    qr += (int64_t)e * rows * cols;
+    sr += (int64_t)e * rows * (cols / 32);
+  }
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kWT][kWT + 8];
+  __shared__ __attribute__((aligned(16))) uint8_t ostage[kWT][kWT + 16];
+  const int t = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * kWT, c0 = (int64_t)blockIdx.y * kWT;
+  {
+    // all eight loads before any is used: a chunk past the matrix reads its first chunk
+    // unconditionally and is replaced by zeros, so that no branch separates the loads
+    u32x4 w[8];
+    bool ok[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int id = t + 256 * it;                     // 128 rows x 16 chunks of 8 values
+      const int rr = id >> 4, ck = id & 15;
+      const int64_t row = r0 + rr, col = c0 + 8 * ck;
+      ok[it] = row < rows && col < cols;
+      w[it] = *reinterpret_cast<const u32x4*>(x + (ok[it] ? row * cols + col : 0));
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int id = t + 256 * it;
+      const int rr = id >> 4, ck = id & 15;
+      *reinterpret_cast<u32x4*>(&tile[rr][8 * ck]) = ok[it] ? w[it] : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();
+  // 32 values -> their scale byte and 32 codes (two 16-byte words)
+  auto quant32 = [](const float (&v)[32], u32x4& o0, u32x4& o1) -> uint8_t {
+    float am = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+    const int sx = mx_shared_exp(am);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o0[i] = mx_pack4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3], sx);
+      o1[i] = mx_pack4(v[16 + 4 * i], v[16 + 4 * i + 1], v[16 + 4 * i + 2], v[16 + 4 * i + 3], sx);
+    }
+    return (uint8_t)(sx + 127);
+  };
+  if constexpr (kRows) {
+    const int rr = t >> 1, hb = t & 1;
+    const int64_t row = r0 + rr;
+    if (row < rows) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int64_t cb = c0 + 64 * hb + 32 * b;
+        if (cb >= cols) continue;
+        float v[32];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 u = *reinterpret_cast<const u32x4*>(&tile[rr][64 * hb + 32 * b + 8 * k]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[8 * k + 2 * i] = bf16_to_f32((uint16_t)(u[i] & 0xFFFF));
+            v[8 * k + 2 * i + 1] = bf16_to_f32((uint16_t)(u[i] >> 16));
+          }
+        }
+        u32x4 o0, o1;
+        const uint8_t sb = quant32(v, o0, o1);
+        uint8_t* d = qr + row * cols + cb;
+        *reinterpret_cast<u32x4*>(d) = o0;
+        *reinterpret_cast<u32x4*>(d + 16) = o1;
+        sr[row * (cols / 32) + cb / 32] = sb;
+      }
+    }
+  }
+  {
+    const int cl = t & 127, rb = 64 * (t >> 7);
+    const int64_t col = c0 + cl;
+    uint32_t sw = 0;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float v[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) v[r] = bf16_to_f32(tile[rb + 32 * b + r][cl]);
+      u32x4 o0, o1;
+      sw |= (uint32_t)quant32(v, o0, o1) << (8 * b);
+      *reinterpret_cast<u32x4*>(&ostage[cl][rb + 32 * b]) = o0;
+      *reinterpret_cast<u32x4*>(&ostage[cl][rb + 32 * b + 16]) = o1;
+    }
+    // rows % 32 == 0: both blocks are in or past the matrix together only when rows - row0 >= 64
+    const int64_t row = r0 + rb;
+    if (col < cols && row < rows) {
+      uint8_t* sp = st + col * (rows / 32) + row / 32;
+      if (row + 64 <= rows && ((rows / 32) & 1) == 0) {
+        *reinterpret_cast<uint16_t*>(sp) = (uint16_t)sw;   // 2-byte aligned: row / 32 and rows / 32 even
+      } else {
+        sp[0] = (uint8_t)sw;
+        if (row + 64 <= rows) sp[1] = (uint8_t)(sw >> 8);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int id = t + 256 * it;                     // 128 columns x 8 pieces of 16 rows
+      const int lc = id >> 3, pc = id & 7;
+      const int64_t cc = c0 + lc, rr = r0 + 16 * pc;
+      if (cc < cols && rr < rows)
+        *reinterpret_cast<u32x4*>(qt + cc * rows + rr) = *reinterpret_cast<const u32x4*>(&ostage[lc][16 * pc]);
+    }
   }
 }
 
@@ -439,24 +573,26 @@ hipError_t launch_mx_quant_cols(const void* x, bool x_f32, int64_t rows, int64_t
                                 int seg_align, const int32_t* src_index, int src_k) {
   dim3 grid((unsigned)((rows_pad + kColRows - 1) / kColRows), (unsigned)((cols + 63) / 64));
   if (grid.x == 0) return hipSuccess;
-  WTab tab{};
   if (x_f32)
-    mx_cols_kernel<true><<<grid, 256, 0, st>>>(tab, x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
-                                               seg_align, nullptr, src_index, src_k);
+    mx_cols_kernel<true><<<grid, 256, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                               seg_align, src_index, src_k);
   else
-    mx_cols_kernel<false><<<grid, 256, 0, st>>>(tab, x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
-                                                seg_align, nullptr, src_index, src_k);
+    mx_cols_kernel<false><<<grid, 256, 0, st>>>(x, rows, cols, group_offsets, num_groups, rows_pad, q, scales,
+                                                seg_align, src_index, src_k);
   return hipGetLastError();
 }
 
 hipError_t launch_mx_quant_weights_t(const void* const* w, int E, int64_t rows, int64_t cols, uint8_t* q,
-                                     uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st) {
+                                     uint8_t* scales, const int32_t* skip_if_empty, hipStream_t st, uint8_t* q_rows,
+                                     uint8_t* s_rows) {
   WTab tab{};
   for (int e = 0; e < E; ++e) tab.w[e] = reinterpret_cast<const uint16_t*>(w[e]);
-  dim3 grid((unsigned)((rows + kColRows - 1) / kColRows), (unsigned)((cols + 63) / 64), (unsigned)E);
-  if (grid.x == 0) return hipSuccess;
-  mx_cols_kernel<false, true><<<grid, 256, 0, st>>>(tab, nullptr, rows, cols, nullptr, 1, rows, q, scales, 32,
-                                                    skip_if_empty, nullptr, 1);
+  const dim3 grid((unsigned)((rows + kWT - 1) / kWT), (unsigned)((cols + kWT - 1) / kWT), (unsigned)E);
+  if (grid.x == 0 || grid.y == 0 || E == 0) return hipSuccess;
+  if (q_rows)
+    mx_wt_kernel<true><<<grid, 256, 0, st>>>(tab, rows, cols, q, scales, q_rows, s_rows, skip_if_empty);
+  else
+    mx_wt_kernel<false><<<grid, 256, 0, st>>>(tab, rows, cols, q, scales, nullptr, nullptr, skip_if_empty);
   return hipGetLastError();
 }
 

@@ -52,7 +52,7 @@ def test_binding_lists_every_declared_symbol():
 
 
 def test_version_status_and_phase_names(lib):
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     lib.moe_status_string.restype = ctypes.c_char_p
     for s in range(5):
         assert lib.moe_status_string(s)
@@ -280,6 +280,33 @@ def test_bwd_fused_dgu_debug_validation(lib):
         one = {name: 0x2000}
         assert lib.moe_grouped_mlp_bwd(ctypes.byref(args(**one)), None) == MOE_ERR_INVALID_ARG
     assert lib.moe_grouped_mlp_bwd(ctypes.byref(args(compute=1, **dbg)), None) == MOE_ERR_INVALID_ARG
+
+
+def test_fwd_transposed_weight_output_validation(lib):
+    """ABI 6: the forward's optional transposed-weight outputs go all four together, MXFP8 with
+    per-call weight quantization only; the per-expert loop does not offer them."""
+    from mixture_experts_grouped_permute_amd._lib import FwdArgs, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED
+    E = 8
+    tab = (ctypes.c_void_p * E)(*([0x1000] * E))
+
+    def args(**kw):
+        a = FwdArgs(T=4096, H=4096, I=14336, E=E, k=2, compute=2, io_dtype=1, x=0x1000, topk_idx=0x1000,
+                    topk_prob=0x1000, w1=tab, w2=tab, out=0x1000, split_sizes=0x1000, offsets=0x1000,
+                    row_id_map=0x1000, src_index=0x1000, prob_perm=0x1000)
+        for k_, v in kw.items():
+            setattr(a, k_, v)
+        return a
+
+    lib.moe_grouped_mlp_fwd_workspace.restype = ctypes.c_size_t
+    wt = dict(w1tq_out=0x2000, w1ts_out=0x2000, w2tq_out=0x2000, w2ts_out=0x2000)
+    assert lib.moe_grouped_mlp_fwd_workspace(ctypes.byref(args(**wt))) > 0
+    for name in wt:
+        assert lib.moe_grouped_mlp_fwd(ctypes.byref(args(**{name: 0x2000})), None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(args(compute=1, **wt)), None) == MOE_ERR_INVALID_ARG
+    cached = dict(w1q=0x3000, w1s=0x3000, w2q=0x3000, w2s=0x3000)
+    assert lib.moe_grouped_mlp_fwd(ctypes.byref(args(**wt, **cached)), None) == MOE_ERR_INVALID_ARG
+    counts = (ctypes.c_int32 * E)(*([1024] * E))
+    assert lib.moe_grouped_mlp_fwd_loop(ctypes.byref(args(**wt)), counts, None) == MOE_ERR_UNSUPPORTED
 
 
 def test_noalloc_permute_limit_on_host(lib):

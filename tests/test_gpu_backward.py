@@ -168,3 +168,31 @@ def test_fused_dgu_quantizer_bytes(name, cfg, counts):
     err = mlp.normwise_rel_err(dbg["dgu_bf16"].cpu().to(torch.float64).numpy(), bw.dgu)
     log(f"  dgu vs oracle {err:.2e}")
     assert err < MXFP8_TOL
+
+
+@gpu
+@pytest.mark.parametrize("name,cfg,counts", [CASES[2], CASES[7]], ids=[CASES[2][0], CASES[7][0]])
+def test_forward_quantizes_weights_for_backward(name, cfg, counts):
+    """MXFP8 training: the forward's one read of the bf16 weights for both orientations gives the
+    same forward output, bit for bit, and the same transposed bytes as mxfp8_quantize_weights (axis
+    1) for every expert with tokens; the backward that takes them equals the one that quantizes per
+    call, bit for bit."""
+    m = need_gpu()
+    log(f"forward quantizes W^T for the backward: {name}")
+    inp = _inputs(cfg, counts)
+    d = inp.to("cuda")
+    out1, ctx1 = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", save_for_backward=True)
+    out0, ctx0 = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", save_for_backward=True,
+                                       quantize_for_backward=False)
+    assert ctx1["w_quant_t"] is not None and ctx0["w_quant_t"] is None
+    g1 = m.moe_grouped_mlp_bwd(d.dy, ctx1, d.w1, d.w2)
+    g0 = m.moe_grouped_mlp_bwd(d.dy, ctx0, d.w1, d.w2)
+    ref = m.quantize_weights(d.w1, d.w2, "mxfp8", transposed=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out0.view(torch.int16))
+    split = ctx1["perm"]["split_sizes"].cpu().numpy()
+    for t_fwd, t_ref in zip(ctx1["w_quant_t"], ref):
+        for e in np.nonzero(split > 0)[0]:
+            assert torch.equal(t_fwd[e], t_ref[e]), e
+    for a_, b_ in zip(g1, g0):
+        assert torch.equal(a_, b_)

@@ -195,7 +195,7 @@ def test_weight_quantizer_tables():
     m = need_gpu()
     log("weight quantizer tables")
     g = np.random.default_rng(31)
-    E, rows, cols = 5, 320, 192
+    E, rows, cols = 5, 352, 192
     w = torch.from_numpy(g.standard_normal((E, rows, cols)).astype(np.float32) * 0.02).to(torch.bfloat16)
     w[2, 5:37] = 0.0          # all-zero blocks along both axes
     w[3] *= 1e-30             # subnormal-range values (bf16 keeps the fp32 exponent range)

@@ -208,6 +208,39 @@ def test_fullsize_fused_h_quantizer_bytes():
 @gpu
 @slow
 @pytest.mark.timeout(900)
+def test_fullsize_fused_dgu_quantizer_bytes():
+    """The FC2 dgrad epilogue's fused MXFP8 quantizer of dGU at the full Mixtral backward (T=8192,
+    H=4096, I=14336, E=8 top-2), byte for byte against the oracle's quantizer on the kernel's bf16
+    dGU, for the rows of the first and the last expert: row-wise along 2I, and along the tokens of
+    each of the two segments in the 128-padded transposed layout."""
+    m = need_gpu()
+    cfg = get_config(4)
+    log("full-size fused dGU quantizer: generating inputs")
+    inp = make_inputs(cfg)
+    d = inp.to("cuda")
+    out, ctx = m.moe_grouped_mlp_fwd(d.x, d.topk_idx, d.topk_prob, d.w1, d.w2, "mxfp8", save_for_backward=True)
+    dbg = {}
+    m.moe_grouped_mlp_bwd(d.dy, ctx, d.w1, d.w2, debug=dbg)
+    torch.cuda.synchronize()
+    off = ctx["perm"]["offsets"].cpu().numpy().astype(np.int64)
+    pad = np.concatenate([[0], np.cumsum((np.diff(off) + 127) // 128 * 128)])
+    for e in (0, cfg.E - 1):
+        lo, hi = int(off[e]), int(off[e + 1])
+        g = dbg["dgu_bf16"][lo:hi].cpu().to(torch.float64).numpy()
+        rc, rs = nm.quantize_mxfp8(g, axis=1)
+        np.testing.assert_array_equal(dbg["dgu_codes"][lo:hi].cpu().numpy(), rc)
+        np.testing.assert_array_equal(dbg["dgu_scales"][lo:hi].cpu().numpy(), rs)
+        tc, ts = nm.quantize_mxfp8_segments_t(g, np.array([0, hi - lo]))
+        n32 = tc.shape[1]
+        p0 = int(pad[e])
+        np.testing.assert_array_equal(dbg["dgu_t_codes"][:, p0:p0 + n32].cpu().numpy(), tc)
+        np.testing.assert_array_equal(dbg["dgu_t_scales"][:, p0 // 32:(p0 + n32) // 32].cpu().numpy(), ts)
+        log(f"  expert {e}: {hi - lo} rows x {2 * cfg.I}, both layouts equal")
+
+
+@gpu
+@slow
+@pytest.mark.timeout(900)
 def test_fullsize_fp8_tensor_bytes():
     """The per-tensor FP8 quantizer over the bf16 permuted rows of the MXFP8 workload, one
     tensor per expert segment (the empty expert included): codes and scales byte for byte."""
