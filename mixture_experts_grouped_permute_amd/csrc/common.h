@@ -101,21 +101,63 @@ __host__ __device__ inline uint32_t mx_e4m3_code(float v, int s) {
 }
 
 // 4-byte pack of the codes of v[0..3] with exponent s.
-// Device: q = v * 2^-s is exact (|q| < 2^9; anything that underflows fp32 rounds to a signed
-// zero in E4M3 anyway), clamping q to +-448 is exactly the saturation rule, and gfx950's
-// v_cvt_pk_fp8_f32 then rounds to the nearest E4M3FN value, ties to even, keeping the sign of
-// zero -- the same code as mx_e4m3_code, at two values per instruction.
+// Device: the magnitudes are clamped to 448 * 2^s (exact: 448 = 1.75 * 2^8; with the scaling this
+// is exactly the saturation rule), and gfx950's scaled conversion v_cvt_scalef32_pk_fp8_f32 divides
+// by 2^s -- exact, a power of two -- and rounds to the nearest E4M3FN value, ties to even, keeping
+// the sign of zero: the same code as mx_e4m3_code, two values per instruction.  The scale operand
+// is 2^s as an fp32 bit pattern (s = -127 gives exponent field 0, which the conversion reads as
+// 2^-127 like an E8M0 byte).  Without the clamp the conversion would give NaN past 448.
 __host__ __device__ inline uint32_t mx_pack4(float a, float b, float c, float d, int s) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const float m = __builtin_bit_cast(float, (uint32_t)(127 - s) << 23);   // 2^-s, s in [-127, 119]
-  auto q = [m](float v) { return __builtin_amdgcn_fmed3f(v * m, -448.0f, 448.0f); };
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(a), q(b), 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(q(c), q(d), w, true);
-  return (uint32_t)w;
+  typedef short short2_t __attribute__((ext_vector_type(2)));
+  const float sc = __builtin_bit_cast(float, (uint32_t)(127 + s) << 23);                 // s in [-127, 119]
+  const float lim = __builtin_bit_cast(float, ((uint32_t)(135 + s) << 23) | 0x600000u);   // 448 * 2^s
+  auto q = [lim](float v) { return __builtin_amdgcn_fmed3f(v, -lim, lim); };
+  short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32((short2_t){0, 0}, q(a), q(b), sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, q(c), q(d), sc, true);
+  return __builtin_bit_cast(uint32_t, r);
 #else
   return mx_e4m3_code(a, s) | (mx_e4m3_code(b, s) << 8) | (mx_e4m3_code(c, s) << 16) |
          (mx_e4m3_code(d, s) << 24);
 #endif
+}
+
+// The same for four bf16 values packed two per word (w01 = values 0, 1; w23 = values 2, 3), without
+// unpacking: the clamp of the magnitudes is an unsigned 16-bit min on the bit patterns (for
+// non-negative bf16 values the integer order is the numeric order), and the conversion reads bf16.
+__device__ inline uint32_t mx_pack4_bf16(uint32_t w01, uint32_t w23, int s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef short short2_t __attribute__((ext_vector_type(2)));
+  typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const float sc = __builtin_bit_cast(float, (uint32_t)(127 + s) << 23);
+  const uint32_t l16 = ((uint32_t)(135 + s) << 7) | 0x60u;                               // 448 * 2^s in bf16
+  const ushort2_t lim = __builtin_bit_cast(ushort2_t, l16 | (l16 << 16));
+  auto clamp = [lim](uint32_t w) {
+    const ushort2_t m = __builtin_elementwise_min(__builtin_bit_cast(ushort2_t, w & 0x7FFF7FFFu), lim);
+    return __builtin_bit_cast(bf16x2_t, __builtin_bit_cast(uint32_t, m) | (w & 0x80008000u));
+  };
+  short2_t r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16((short2_t){0, 0}, clamp(w01), sc, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, clamp(w23), sc, true);
+  return __builtin_bit_cast(uint32_t, r);
+#else
+  (void)w01;
+  (void)w23;
+  (void)s;
+  return 0;
+#endif
+}
+
+// The largest magnitude of the 2 n bf16 values packed in w[0..n-1], as an fp32 (bit patterns of
+// non-negative bf16 values order as the values do).
+template <int n>
+__device__ inline float bf16_amax(const uint32_t* w) {
+  typedef unsigned short ushort2_t __attribute__((ext_vector_type(2)));
+  ushort2_t m = __builtin_bit_cast(ushort2_t, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < n; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2_t, w[i] & 0x7FFF7FFFu));
+  const uint32_t h = m[0] > m[1] ? m[0] : m[1];
+  return __builtin_bit_cast(float, h << 16);
 }
 
 // ---------------------------------------------------------------------------

@@ -494,25 +494,13 @@ void bwd_gemm_kernel(const BwdKArgs p) {
         const uint32_t rd = (uint32_t)(16 * (G4 >> 1) + sl / 4) * 64u + (uint32_t)(16 * (G4 & 1) + 4 * (sl & 3)) * 2u;
         {
           const uint32_t colg = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);   // dGU column
-          float v[16];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            v[2 * x] = bf16_to_f32((uint16_t)(w0[x] & 0xFFFF));
-            v[2 * x + 1] = bf16_to_f32((uint16_t)(w0[x] >> 16));
-            v[8 + 2 * x] = bf16_to_f32((uint16_t)(w1[x] & 0xFFFF));
-            v[8 + 2 * x + 1] = bf16_to_f32((uint16_t)(w1[x] >> 16));
-          }
-          float am = 0.f;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(v[r]));
-          am = max_xor32(am);
-          const int sx = mx_shared_exp(am);
-#pragma unroll
-          for (int pp = 0; pp < 2; ++pp) {
-            const u32x2 c{mx_pack4(v[8 * pp], v[8 * pp + 1], v[8 * pp + 2], v[8 * pp + 3], sx),
-                          mx_pack4(v[8 * pp + 4], v[8 * pp + 5], v[8 * pp + 6], v[8 * pp + 7], sx)};
-            __builtin_amdgcn_raw_buffer_store_b64(c, rq, m * I2 + colg + 16u * pp + 8u * (uint32_t)(elane >> 5), 0, 0);
-          }
+          // the bf16 values stay packed: amax on the bit patterns, codes by the scaled conversion
+          const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+          const int sx = mx_shared_exp(max_xor32(bf16_amax<8>(wv)));
+          const u32x2 c0{mx_pack4_bf16(w0[0], w0[1], sx), mx_pack4_bf16(w0[2], w0[3], sx)};
+          const u32x2 c1{mx_pack4_bf16(w1[0], w1[1], sx), mx_pack4_bf16(w1[2], w1[3], sx)};
+          __builtin_amdgcn_raw_buffer_store_b64(c0, rq, m * I2 + colg + 8u * (uint32_t)(elane >> 5), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b64(c1, rq, m * I2 + colg + 16u + 8u * (uint32_t)(elane >> 5), 0, 0);
           rword |= (uint32_t)(sx + 127) << (8 * j);
           if (tv) {
             *reinterpret_cast<u32x4*>(lt + r32 * 64 + (8 * (elane >> 5)) * 2) = w0;
@@ -520,21 +508,18 @@ void bwd_gemm_kernel(const BwdKArgs p) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
             const auto base = (__attribute__((address_space(3))) uint8_t*)(lt);
-            float t[16];
+            uint32_t tw[8];   // rows 16 (l / 32) + [0, 16) of column l % 32, two bf16 per word
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + rd + q * 256u));
-#pragma unroll
-              for (int x = 0; x < 4; ++x) t[4 * q + x] = (float)r[x];
+              const u32x2 rw = __builtin_bit_cast(u32x2, r);
+              tw[2 * q] = rw[0];
+              tw[2 * q + 1] = rw[1];
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            float at = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) at = fmaxf(at, fabsf(t[r]));
-            at = max_xor32(at);
-            const int st = mx_shared_exp(at);
-            const u32x4 c{mx_pack4(t[0], t[1], t[2], t[3], st), mx_pack4(t[4], t[5], t[6], t[7], st),
-                          mx_pack4(t[8], t[9], t[10], t[11], st), mx_pack4(t[12], t[13], t[14], t[15], st)};
+            const int st = mx_shared_exp(max_xor32(bf16_amax<8>(tw)));
+            const u32x4 c{mx_pack4_bf16(tw[0], tw[1], st), mx_pack4_bf16(tw[2], tw[3], st),
+                          mx_pack4_bf16(tw[4], tw[5], st), mx_pack4_bf16(tw[6], tw[7], st)};
             // through descriptors over the block's 32 transposed rows: a split_sizes array that does
             // not match rows_pad cannot take the stores outside the buffers
             const uint32_t rp = (uint32_t)p.rows_pad, prow = (uint32_t)(cur.poff + srel);
