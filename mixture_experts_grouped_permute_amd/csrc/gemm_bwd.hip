@@ -101,7 +101,15 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   // token-axis quantization
   constexpr bool kQ = kD2 && kMx;
   constexpr int kTOff = kXOff + 4096;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kXOff + (kD2 ? 4096 : 16) + (kQ ? 4 * 2048 : 0)];
+  // BF16 FC2 dgrad: a 32 x 128-byte staging slot per wave (4 KB each) for full-line dG / dU stores
+  constexpr bool kStage = kD2 && !kMx;
+  constexpr int kSOff = kXOff + 4096;
+  // fp32 outputs (the weight gradients, the split parts of the FC1 dgrad): a 16 x 128-byte slot per
+  // wave (2 KB each) for full-line stores
+  constexpr bool kStageF = kOutF32 && !kD2;
+  constexpr int kFOff = kXOff + 16;
+  __shared__ __attribute__((aligned(16)))
+  uint8_t smem[kXOff + (kD2 ? 4096 : 16) + (kQ ? 4 * 2048 : 0) + (kStage ? 4 * 4096 : 0) + (kStageF ? 4 * 2048 : 0)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -532,6 +540,36 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       };
       [[maybe_unused]] uint32_t rsw[2] = {0u, 0u};                    // row scale words (current i)
       [[maybe_unused]] uint32_t csw[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};   // column ones, by j
+      // BF16: dG (then dU) of the two column blocks j, j + 1 of a row block, staged row by row in the
+      // wave's slot (16-byte chunk c of row r at chunk c ^ (r & 7): conflict-free reads, 2-way
+      // writes) and stored 8 whole 128-byte rows per instruction -- the direct stores wrote 32-byte
+      // pieces of 32 rows each, and their partial lines cost the write path several times their
+      // bytes.  e / o: the even / odd block's runs pp = 0, 1; colbyte: the pair's first column in the
+      // dGU row, in bytes.
+      [[maybe_unused]] auto flush_pair = [&](const u32x4 (&e)[2], const u32x4 (&o)[2], uint32_t colbyte, int i) {
+        uint8_t* sl = smem + kSOff + wave * 4096;
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int pp = 0; pp < 2; ++pp) {
+            const uint32_t c = (uint32_t)(jj * 4 + 2 * pp + (elane >> 5));
+            *reinterpret_cast<u32x4*>(sl + r32 * 128 + ((c ^ (uint32_t)(r32 & 7)) << 4)) = jj ? o[pp] : e[pp];
+          }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        u32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = 8 * q + (elane >> 3), ch = elane & 7;
+          v[q] = *reinterpret_cast<const u32x4*>(sl + row * 128 + ((ch ^ (row & 7)) << 4));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot is free for the next pair
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t m = (uint32_t)(wm * 128 + i * 32 + 8 * q + (elane >> 3));
+          __builtin_amdgcn_raw_buffer_store_b128(v[q], rdg, 2u * m * I32 * 2u + colbyte + (uint32_t)(elane & 7) * 16u, 0, 0);
+        }
+      };
+      [[maybe_unused]] u32x4 gk[2], uk[2];   // BF16: the even block's dG, dU, kept for its pair
       float part[4] = {0.f, 0.f, 0.f, 0.f};
       load(0, 0);
 #pragma unroll
@@ -574,10 +612,19 @@ void bwd_gemm_kernel(const BwdKArgs p) {
                            pack_bf16x2(dgv[6], dgv[7])};
             ub[pp] = u32x4{pack_bf16x2(duv[0], duv[1]), pack_bf16x2(duv[2], duv[3]), pack_bf16x2(duv[4], duv[5]),
                            pack_bf16x2(duv[6], duv[7])};
-            if (!kQ || p.dgu) {
+            if (kQ && p.dgu) {   // MXFP8 debug output: the bf16 dGU, stored directly
               const uint32_t o = boff(blk, pp);
               __builtin_amdgcn_raw_buffer_store_b128(gb[pp], rdg, o, 0, 0);
               __builtin_amdgcn_raw_buffer_store_b128(ub[pp], rdg, o + I32 * 2u, 0, 0);
+            }
+          }
+          if constexpr (kStage) {
+            if ((j & 1) == 0) {
+              gk[0] = gb[0]; gk[1] = gb[1]; uk[0] = ub[0]; uk[1] = ub[1];
+            } else {
+              const uint32_t c0 = (uint32_t)n0 + (uint32_t)(wn * 128 + (j - 1) * 32);   // the pair's first column
+              flush_pair(gk, gb, c0 * 2u, i);
+              flush_pair(uk, ub, (I32 + c0) * 2u, i);
             }
           }
           if constexpr (kQ) {
@@ -647,10 +694,34 @@ void bwd_gemm_kernel(const BwdKArgs p) {
           float a[16];
           agpr_read16(core.acc[i][j], a);
           if constexpr (kOutF32) {
-            const uint32_t e0 = m * N32 + col + (uint32_t)ch;
+            // a block row is 128 bytes of fp32: staged 16 rows at a time in the wave's slot (16-byte
+            // chunk c of row r at chunk c ^ (r & 7)) and stored 8 whole rows per instruction, instead
+            // of 32-byte pieces of 32 rows per instruction
+            uint8_t* sl = smem + kFOff + wave * 2048;
+            const uint32_t cb = (uint32_t)(elane >> 5);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              __builtin_amdgcn_raw_buffer_store_b128(f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, ro, (e0 + 8u * q) * 4u, 0, 0);
+            for (int h = 0; h < 2; ++h) {
+              if ((r32 >> 4) == h) {
+                const uint32_t rr = (uint32_t)(r32 & 15);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  *reinterpret_cast<f32x4*>(sl + rr * 128 + (((2u * q + cb) ^ (rr & 7u)) << 4)) =
+                      f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+              }
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+              f32x4 v[2];
+#pragma unroll
+              for (int t2 = 0; t2 < 2; ++t2) {
+                const uint32_t rr = (uint32_t)(8 * t2 + (elane >> 3)), c = (uint32_t)(elane & 7);
+                v[t2] = *reinterpret_cast<const f32x4*>(sl + rr * 128 + ((c ^ (rr & 7u)) << 4));
+              }
+              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot is free again
+#pragma unroll
+              for (int t2 = 0; t2 < 2; ++t2) {
+                const uint32_t mm = (uint32_t)(wm * 128 + i * 32 + 16 * h + 8 * t2 + (elane >> 3));
+                __builtin_amdgcn_raw_buffer_store_b128(v[t2], ro, (mm * N32 + col) * 4u + (uint32_t)(elane & 7) * 16u, 0, 0);
+              }
+            }
           } else {
             // bf16 in the lane-paired layout: 8 consecutive columns 16 pp + 8 hh + [0, 8) per lane
             const uint32_t e8 = m * N32 + col + 2u * (uint32_t)ch;
