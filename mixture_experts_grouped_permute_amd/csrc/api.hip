@@ -592,7 +592,7 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
   MOE_CHECK(a->workspace && a->workspace_bytes >= need, MOE_ERR_WORKSPACE);
   FwdPlan p = plan_fwd(a, a->workspace);
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  const int64_t T = a->T, H = a->H, I = a->I, R = T * a->k;
+  const int64_t T = a->T, H = a->H, I = a->I;
   const int E = a->E, k = a->k;
   const bool mx = a->compute == MOE_MXFP8_E4M3;
   const bool x_f32 = a->io_dtype == MOE_F32;

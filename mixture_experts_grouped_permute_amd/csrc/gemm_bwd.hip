@@ -513,7 +513,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
           if (tv) {
             *reinterpret_cast<u32x4*>(lt + r32 * 64 + (8 * (elane >> 5)) * 2) = w0;
             *reinterpret_cast<u32x4*>(lt + r32 * 64 + (16 + 8 * (elane >> 5)) * 2) = w1;
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("" ::: "memory");   // in-order LDS within the wave: no counter wait
             typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
             const auto base = (__attribute__((address_space(3))) uint8_t*)(lt);
             uint32_t tw[8];   // rows 16 (l / 32) + [0, 16) of column l % 32, two bf16 per word
@@ -524,7 +524,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
               tw[2 * q] = rw[0];
               tw[2 * q + 1] = rw[1];
             }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("" ::: "memory");
             const int st = mx_shared_exp(max_xor32(bf16_amax<8>(tw)));
             const u32x4 c{mx_pack4_bf16(tw[0], tw[1], st), mx_pack4_bf16(tw[2], tw[3], st),
                           mx_pack4_bf16(tw[4], tw[5], st), mx_pack4_bf16(tw[6], tw[7], st)};
@@ -555,14 +555,17 @@ void bwd_gemm_kernel(const BwdKArgs p) {
             const uint32_t c = (uint32_t)(jj * 4 + 2 * pp + (elane >> 5));
             *reinterpret_cast<u32x4*>(sl + r32 * 128 + ((c ^ (uint32_t)(r32 & 7)) << 4)) = jj ? o[pp] : e[pp];
           }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        // the LDS unit runs one wave's operations in issue order: the reads below see these writes,
+        // and the next pair's writes cannot overtake them, so no counter wait is needed -- the
+        // empty asm only keeps the compiler from moving LDS accesses across it
+        asm volatile("" ::: "memory");
         u32x4 v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int row = 8 * q + (elane >> 3), ch = elane & 7;
           v[q] = *reinterpret_cast<const u32x4*>(sl + row * 128 + ((ch ^ (row & 7)) << 4));
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot is free for the next pair
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const uint32_t m = (uint32_t)(wm * 128 + i * 32 + 8 * q + (elane >> 3));
@@ -684,6 +687,12 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const rsrc_t ro = sp ? make_rsrc(p.part + (size_t)(cur.t - full) * 65536, 65536u * 4u)
                            : make_rsrc(obase + r0 * p.N * es, (uint32_t)cur.mrows * N32 * es);
       const int64_t cbase = sp ? 0 : n0;                             // tile's first column in the destination
+      // fp32: the previous block's staged rows (t: rows 8 t + l / 8 of the block), not yet stored;
+      // weight gradients are written once and never re-read here: non-temporal stores
+      [[maybe_unused]] f32x4 pend[4];
+      [[maybe_unused]] uint32_t pend_off = 0;
+      [[maybe_unused]] bool npend = false;
+      constexpr int kStoreAux = kWg ? 2 : 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
@@ -696,9 +705,12 @@ void bwd_gemm_kernel(const BwdKArgs p) {
           if constexpr (kOutF32) {
             // a block row is 128 bytes of fp32: staged 16 rows at a time in the wave's slot (16-byte
             // chunk c of row r at chunk c ^ (r & 7)) and stored 8 whole rows per instruction, instead
-            // of 32-byte pieces of 32 rows per instruction
+            // of 32-byte pieces of 32 rows per instruction.  The LDS unit runs one wave's operations
+            // in issue order, so both halves go through the one slot with no counter wait, and the
+            // global stores of a block are issued after the next block's LDS round trip (pend).
             uint8_t* sl = smem + kFOff + wave * 2048;
             const uint32_t cb = (uint32_t)(elane >> 5);
+            f32x4 v[4];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
               if ((r32 >> 4) == h) {
@@ -708,20 +720,22 @@ void bwd_gemm_kernel(const BwdKArgs p) {
                   *reinterpret_cast<f32x4*>(sl + rr * 128 + (((2u * q + cb) ^ (rr & 7u)) << 4)) =
                       f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
               }
-              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-              f32x4 v[2];
+              asm volatile("" ::: "memory");
 #pragma unroll
               for (int t2 = 0; t2 < 2; ++t2) {
                 const uint32_t rr = (uint32_t)(8 * t2 + (elane >> 3)), c = (uint32_t)(elane & 7);
-                v[t2] = *reinterpret_cast<const f32x4*>(sl + rr * 128 + ((c ^ (rr & 7u)) << 4));
+                v[2 * h + t2] = *reinterpret_cast<const f32x4*>(sl + rr * 128 + ((c ^ (rr & 7u)) << 4));
               }
-              asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the slot is free again
-#pragma unroll
-              for (int t2 = 0; t2 < 2; ++t2) {
-                const uint32_t mm = (uint32_t)(wm * 128 + i * 32 + 16 * h + 8 * t2 + (elane >> 3));
-                __builtin_amdgcn_raw_buffer_store_b128(v[t2], ro, (mm * N32 + col) * 4u + (uint32_t)(elane & 7) * 16u, 0, 0);
-              }
+              asm volatile("" ::: "memory");
             }
+            if (npend) {
+#pragma unroll
+              for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * N32 * 4u, 0, kStoreAux);
+            }
+            npend = true;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) pend[t] = v[t];
+            pend_off = ((uint32_t)(wm * 128 + i * 32 + (elane >> 3)) * N32 + col) * 4u + (uint32_t)(elane & 7) * 16u;
           } else {
             // bf16 in the lane-paired layout: 8 consecutive columns 16 pp + 8 hh + [0, 8) per lane
             const uint32_t e8 = m * N32 + col + 2u * (uint32_t)ch;
@@ -731,6 +745,12 @@ void bwd_gemm_kernel(const BwdKArgs p) {
             for (int pp = 0; pp < 2; ++pp) __builtin_amdgcn_raw_buffer_store_b128(oa[pp], ro, (e8 + 16u * pp) * 2u, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (kOutF32) {
+        if (npend) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * N32 * 4u, 0, kStoreAux);
         }
       }
     }

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(const int32_t* __rest
                                                              float* __restrict__ prob_perm) {
   __shared__ int run[kMaxExperts];
   __shared__ int wcnt[4][kMaxExperts];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
   for (int e = tid; e < E; e += 256) run[e] = block_base[(int64_t)blockIdx.x * E + e];
   const int chunk = kPermTokens * k;
   int64_t base = (int64_t)blockIdx.x * chunk;
