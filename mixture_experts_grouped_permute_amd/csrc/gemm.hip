@@ -96,7 +96,9 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   constexpr int kScOff = 2 * kStageBytes;
   constexpr int kScBuf = 8192;
   constexpr int kPrOff = kScOff + (kMx ? 2 * kScBuf : 0);
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kPrOff + (kFc1 ? 2 * 1024 : 16)];
+  // FC2: a 2 KB slot per wave for the epilogue's full-line stores
+  constexpr int kFOff = kPrOff + 16;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kPrOff + (kFc1 ? 2 * 1024 : 16 + 4 * 2048)];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -472,36 +474,63 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       // first column of the tile in the destination (0 for a part slot)
       const uint32_t c0 = (kOutF32 && cur.part >= 0) ? 0u : (uint32_t)cur.nt * kBN;
       const float dq = (kMx && kPt) ? (1.0f / p.pt_s_a[cur.e]) * (1.0f / p.pt_s_b[cur.e]) : 1.0f;
+      // A row of a 32 x 32 fp32 block, or of a pair of bf16 blocks j = 2 jp, 2 jp + 1, is 128 bytes,
+      // which lanes l and l + 32 hold as 16-byte chunks 2 q + l / 32: it goes through the wave's
+      // LDS slot (stage_rows32) and out 8 whole rows per store, each unit's stores issued after the
+      // next unit's LDS round trip.  A unit past N (a ragged last N tile; N is a multiple of 64)
+      // gets offsets past the descriptor's range, so its stores are dropped.
+      constexpr uint32_t kEsz = kOutF32 ? 4u : 2u;
+      constexpr int kUnits = kOutF32 ? 16 : 8;
+      uint8_t* sl = smem + kFOff + wave * 2048;
+      u32x4 pend[4];               // the previous unit's rows 8 t + l / 8, t < 4
+      uint32_t pend_off = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = wm * 128 + i * 32 + r32;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t tc = (uint32_t)(wn * 128 + j * 32);           // column of the block within the tile
-          if ((uint32_t)cur.nt * kBN + tc >= N32) continue;            // wave-uniform
+      for (int u = 0; u < kUnits; ++u) {
+        const int i = kOutF32 ? u >> 2 : u >> 1;
+        const int j0 = kOutF32 ? (u & 3) : 2 * (u & 1);   // the unit's first block
+        uint32_t lo[8], hi[8];
+        if constexpr (kOutF32) {
           float a[16];
-          agpr_read16(core.acc[i][j], a);
+          agpr_read16(core.acc[i][j0], a);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            lo[k] = __builtin_bit_cast(uint32_t, a[k] * dq);
+            hi[k] = __builtin_bit_cast(uint32_t, a[8 + k] * dq);
+          }
+        } else {
+          float a0[16], a1[16];
+          agpr_read16(core.acc[i][j0], a0);
+          agpr_read16(core.acc[i][j0 + 1], a1);
           if constexpr (kMx && kPt) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) a[r] *= dq;
+            for (int r = 0; r < 16; ++r) { a0[r] *= dq; a1[r] *= dq; }
           }
-          const uint32_t e0 = (uint32_t)m * ld + c0 + tc + (uint32_t)ch;
-          if constexpr (kOutF32) {
-            // fp32 runs already give 32 contiguous bytes per row (lanes l and l ^ 32)
+          u32x4 e[2], o[2];   // the lane-paired bf16 runs: chunks 2 pp + l / 32 of each block's 64 bytes
+          pack_bf16_runs8(a0, e);
+          pack_bf16_runs8(a1, o);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              __builtin_amdgcn_raw_buffer_store_b128(f32x4{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]}, ro, (e0 + 8u * q) * 4u, 0, 0);
-          } else {
-            // bf16 in the lane-paired layout: 8 consecutive columns 16 pp + 8 hh + [0, 8) per lane
-            const uint32_t e8 = (uint32_t)m * ld + c0 + tc + 2u * (uint32_t)ch;
-            u32x4 oa[2];
-            pack_bf16_runs8(a, oa);
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) __builtin_amdgcn_raw_buffer_store_b128(oa[pp], ro, (e8 + 16u * pp) * 2u, 0, 0);
+          for (int k = 0; k < 4; ++k) {
+            lo[k] = e[0][k];
+            lo[4 + k] = e[1][k];
+            hi[k] = o[0][k];
+            hi[4 + k] = o[1][k];
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
+        u32x4 v[4];
+        stage_rows32(sl, lo, hi, elane, v);
+        if (u > 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * ld * kEsz, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pend[t] = v[t];
+        const uint32_t tc = (uint32_t)(wn * 128 + j0 * 32);            // column of the unit within the tile
+        const bool ok = (uint32_t)cur.nt * kBN + tc < N32;
+        pend_off = ok ? ((uint32_t)(wm * 128 + i * 32 + (elane >> 3)) * ld + c0 + tc) * kEsz + ((uint32_t)elane & 7u) * 16u
+                      : 0x80000000u;
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * ld * kEsz, 0, 0);
     }
     cur = nxt;
     dc = dn;

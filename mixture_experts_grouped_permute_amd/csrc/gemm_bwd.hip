@@ -104,9 +104,9 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   // BF16 FC2 dgrad: a 32 x 128-byte staging slot per wave (4 KB each) for full-line dG / dU stores
   constexpr bool kStage = kD2 && !kMx;
   constexpr int kSOff = kXOff + 4096;
-  // fp32 outputs (the weight gradients, the split parts of the FC1 dgrad): a 16 x 128-byte slot per
-  // wave (2 KB each) for full-line stores
-  constexpr bool kStageF = kOutF32 && !kD2;
+  // the other roles' outputs (weight gradients, FC1 dgrad and its split parts): a 16 x 128-byte
+  // slot per wave (2 KB each) for full-line stores
+  constexpr bool kStageF = !kD2;
   constexpr int kFOff = kXOff + 16;
   __shared__ __attribute__((aligned(16)))
   uint8_t smem[kXOff + (kD2 ? 4096 : 16) + (kQ ? 4 * 2048 : 0) + (kStage ? 4 * 4096 : 0) + (kStageF ? 4 * 2048 : 0)];
@@ -687,87 +687,60 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const rsrc_t ro = sp ? make_rsrc(p.part + (size_t)(cur.t - full) * 65536, 65536u * 4u)
                            : make_rsrc(obase + r0 * p.N * es, (uint32_t)cur.mrows * N32 * es);
       const int64_t cbase = sp ? 0 : n0;                             // tile's first column in the destination
-      if constexpr (kOutF32) {
-        // fp32: a block row is 128 bytes, staged 16 rows at a time in the wave's 2 KB slot (16-byte
-        // chunk c of row r at chunk c ^ (r & 7)) and stored 8 whole rows per instruction, instead of
-        // 32-byte pieces of 32 rows per instruction.  Lane l holds chunks 2 q + l / 32 (q < 4) of row
-        // l % 32; a permlane16 swap trades chunks q = 2, 3 of rows 0-15 for chunks q = 0, 1 of rows
-        // 16-31, so each half of the block is written by all 64 lanes with two stores.  The LDS unit
-        // runs one wave's operations in issue order: both halves use the one slot with no counter
-        // wait, and a block's global stores are issued after the next block's LDS round trip.
-        uint8_t* sl = smem + kFOff + wave * 2048;
-        const uint32_t cb = (uint32_t)(elane >> 5), hi = (uint32_t)(r32 >> 4), rr = (uint32_t)(r32 & 15);
-        uint32_t wofs[2], rofs[2];
+      // A row of a 32 x 32 fp32 block, or of a pair of bf16 blocks j = 2 jp, 2 jp + 1, is 128 bytes,
+      // which lanes l and l + 32 hold as 16-byte chunks 2 q + l / 32: it goes through the wave's
+      // LDS slot (stage_rows32) and out 8 whole rows per store, each unit's stores issued after the
+      // next unit's LDS round trip.  A unit past N (a ragged last N tile; N is a multiple of 64)
+      // gets offsets past the descriptor's range, so its stores are dropped.  Weight gradients are
+      // written once and never re-read here: non-temporal stores.
+      constexpr int kStoreAux = kWg ? 2 : 0;
+      constexpr int kUnits = kOutF32 ? 16 : 8;
+      uint8_t* sl = smem + kFOff + wave * 2048;
+      u32x4 pend[4];               // the previous unit's rows 8 t + l / 8, t < 4
+      uint32_t pend_off = 0;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          wofs[t] = rr * 128u + (((2u * ((uint32_t)t + 2u * hi) + cb) ^ (rr & 7u)) << 4);
-          const uint32_t row = 8u * (uint32_t)t + (uint32_t)(elane >> 3);
-          rofs[t] = row * 128u + ((((uint32_t)elane & 7u) ^ (row & 7u)) << 4);
-        }
-        // weight gradients are written once and never re-read here: non-temporal stores
-        constexpr int kStoreAux = kWg ? 2 : 0;
-        f32x4 pend[4];              // the previous block's rows 8 t + l / 8, t < 4
-        uint32_t pend_off = 0;
-#pragma unroll
-        for (int blk = 0; blk < 16; ++blk) {
-          const int i = blk >> 2, j = blk & 3;
+      for (int u = 0; u < kUnits; ++u) {
+        const int i = kOutF32 ? u >> 2 : u >> 1;
+        const int j0 = kOutF32 ? (u & 3) : 2 * (u & 1);   // the unit's first block
+        uint32_t lo[8], hi[8];
+        if constexpr (kOutF32) {
           float a[16];
-          agpr_read16(core.acc[i][j], a);
-          uint32_t P[8], Q[8];      // chunks q = 0, 1 and q = 2, 3
+          agpr_read16(core.acc[i][j0], a);
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
-            const auto sw = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a[k]),
-                                                             __builtin_bit_cast(uint32_t, a[8 + k]), false, false);
-            P[k] = sw[0];
-            Q[k] = sw[1];
+            lo[k] = __builtin_bit_cast(uint32_t, a[k]);
+            hi[k] = __builtin_bit_cast(uint32_t, a[8 + k]);
           }
-          f32x4 v[4];
+        } else {
+          float a0[16], a1[16];
+          agpr_read16(core.acc[i][j0], a0);
+          agpr_read16(core.acc[i][j0 + 1], a1);
+          u32x4 e[2], o[2];   // the lane-paired bf16 runs: chunks 2 pp + l / 32 of each block's 64 bytes
+          pack_bf16_runs8(a0, e);
+          pack_bf16_runs8(a1, o);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t* d = h ? Q : P;
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-              *reinterpret_cast<u32x4*>(sl + wofs[t]) = u32x4{d[4 * t], d[4 * t + 1], d[4 * t + 2], d[4 * t + 3]};
-            asm volatile("" ::: "memory");
-#pragma unroll
-            for (int t = 0; t < 2; ++t) v[2 * h + t] = *reinterpret_cast<const f32x4*>(sl + rofs[t]);
-            asm volatile("" ::: "memory");
-          }
-          if (blk > 0) {
-#pragma unroll
-            for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * N32 * 4u, 0, kStoreAux);
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) pend[t] = v[t];
-          // a column block past N (a ragged last N tile) gets an offset past the descriptor's range:
-          // its stores are dropped
-          const bool ok = (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32) < (uint32_t)p.N;
-          const uint32_t col = (uint32_t)cbase + (uint32_t)(wn * 128 + j * 32);
-          pend_off = ok ? ((uint32_t)(wm * 128 + i * 32 + (elane >> 3)) * N32 + col) * 4u + ((uint32_t)elane & 7u) * 16u
-                        : 0x80000000u;
-        }
-#pragma unroll
-        for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * N32 * 4u, 0, kStoreAux);
-      } else {
-        // bf16 in the lane-paired layout: 8 consecutive columns 16 pp + 8 hh + [0, 8) per lane
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if ((uint32_t)n0 + (uint32_t)(wn * 128 + j * 32) >= (uint32_t)p.N) continue;   // wave-uniform
-            const uint32_t col = (uint32_t)cbase + (uint32_t)(wn * 128 + j * 32);          // in the destination
-            float a[16];
-            agpr_read16(core.acc[i][j], a);
-            const uint32_t e8 = m * N32 + col + 2u * (uint32_t)ch;
-            u32x4 oa[2];
-            pack_bf16_runs8(a, oa);
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) __builtin_amdgcn_raw_buffer_store_b128(oa[pp], ro, (e8 + 16u * pp) * 2u, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
+          for (int k = 0; k < 4; ++k) {
+            lo[k] = e[0][k];
+            lo[4 + k] = e[1][k];
+            hi[k] = o[0][k];
+            hi[4 + k] = o[1][k];
           }
         }
+        u32x4 v[4];
+        stage_rows32(sl, lo, hi, elane, v);
+        if (u > 0) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * N32 * es, 0, kStoreAux);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) pend[t] = v[t];
+        const uint32_t tc = (uint32_t)(wn * 128 + j0 * 32);            // column of the unit within the tile
+        const bool ok = (uint32_t)n0 + tc < (uint32_t)p.N;
+        pend_off = ok ? ((uint32_t)(wm * 128 + i * 32 + (elane >> 3)) * N32 + (uint32_t)cbase + tc) * es + ((uint32_t)elane & 7u) * 16u
+                      : 0x80000000u;
       }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * N32 * es, 0, kStoreAux);
     }
     cur = nxt;
     dc = dn;

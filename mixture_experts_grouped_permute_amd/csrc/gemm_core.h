@@ -477,6 +477,43 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
+// A 32-row x 128-byte output block held one row per lane pair: lane l holds 16-byte chunks
+// 2 q + l / 32 (q < 4) of row l % 32, as lo (q = 0, 1) and hi (q = 2, 3), four words per chunk.
+// The block passes through a 2 KB LDS slot 16 rows at a time and comes back as out[t] = chunk
+// l % 8 of row 8 t + l / 8, ready for stores of 8 whole 128-byte rows per instruction (the
+// lane-pair layout itself stores 32-byte pieces of 32 rows, and partial lines cost the write path
+// several times their bytes).  A permlane16 swap first trades the hi chunks of rows 0-15 for the
+// lo chunks of rows 16-31, so each half is written by all 64 lanes in two instructions.  Chunk c
+// of slot row r sits at chunk c ^ (r & 7): conflict-free writes and reads.  The LDS unit runs
+// one wave's operations in issue order, so the reads see the writes and the next writes cannot
+// overtake the reads without any counter wait; the empty asm statements only keep the compiler
+// from moving LDS accesses across them.
+__device__ __forceinline__ void stage_rows32(uint8_t* slot, uint32_t (&lo)[8], uint32_t (&hi)[8], int lane,
+                                             u32x4 (&out)[4]) {
+  const uint32_t r32 = (uint32_t)lane & 31u, cb = (uint32_t)lane >> 5, h16 = r32 >> 4, rr = r32 & 15u;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const auto sw = __builtin_amdgcn_permlane16_swap(lo[k], hi[k], false, false);
+    lo[k] = sw[0];
+    hi[k] = sw[1];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t* d = h ? hi : lo;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      *reinterpret_cast<u32x4*>(slot + rr * 128u + (((2u * ((uint32_t)t + 2u * h16) + cb) ^ (rr & 7u)) << 4)) =
+          u32x4{d[4 * t], d[4 * t + 1], d[4 * t + 2], d[4 * t + 3]};
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t row = 8u * (uint32_t)t + ((uint32_t)lane >> 3);
+      out[2 * h + t] = *reinterpret_cast<const u32x4*>(slot + row * 128u + ((((uint32_t)lane & 7u) ^ (row & 7u)) << 4));
+    }
+    asm volatile("" ::: "memory");
+  }
+}
+
 // Copy of an accumulator out of its AGPR at this point of the program.  Without it the register
 // allocator copies all 256 accumulators to VGPRs where the main loop ends, which does not fit
 // and spills.
