@@ -351,7 +351,10 @@ __device__ __forceinline__ void mma_stage(TileCore<kMx, kFc1>& core, const uint8
   }
 }
 
-// The substep-0 fragments of the stage in sA / sS.
+// The substep-0 fragments of the stage in sA / sS, ahead of a deep stage loop.  The MXFP8 scale
+// values leave as opaque 32-bit values: were they byte loads on both edges into the loop, the
+// compiler would carry them as bytes and re-extend them at the top of every stage, waiting there
+// for every LDS read in flight.
 template <bool kMx, bool kFc1, bool kAMN, bool kBMN, int kScRow>
 __device__ __forceinline__ void read_first(StepFrag<kMx>& f0, const uint8_t* sA, const uint8_t* sS, int wm, int wn,
                                            int lane) {
@@ -359,6 +362,10 @@ __device__ __forceinline__ void read_first(StepFrag<kMx>& f0, const uint8_t* sA,
   for (int e = 0; e < 8; ++e) {
     read_elem<kMx, kFc1, kAMN, kBMN, kScRow>(f0, sA, sS, 0, e, wm, wn, lane);
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (kMx) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(f0.sa[i]), "+v"(f0.sb[i]));
   }
 }
 
