@@ -492,51 +492,54 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       // bytes are collected into words, so that they leave as 4-byte stores: a row's bytes of the
       // wave's 4 column blocks (rword, byte j), and a column's bytes of the wave's 4 row blocks
       // (cword, byte i) -- both 4-byte aligned, as I % 128 == 0 and segments start at multiples of 128.
-      auto quant_half = [&](const u32x4 w0, const u32x4 w1, int half, int i, int j, uint32_t& rword,
-                            uint32_t& cword) {
+      // Along 2I (quant_rows): codes and scale straight from the lane's runs.
+      auto quant_rows = [&](const u32x4 w0, const u32x4 w1, int half, int i, int j, uint32_t& rword) {
         const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
-        const int srel = cur.mt * kBM + wm * 128 + i * 32;                   // block's first segment row
-        const bool tv = srel < (cur.Me + 127) / 128 * 128;                   // wave-uniform
+        const uint32_t colg = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);   // dGU column
+        // the bf16 values stay packed: amax on the bit patterns, codes by the scaled conversion
+        const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+        const int sx = mx_shared_exp(max_xor32(bf16_amax<8>(wv)));
+        const u32x2 c0{mx_pack4_bf16(w0[0], w0[1], sx), mx_pack4_bf16(w0[2], w0[3], sx)};
+        const u32x2 c1{mx_pack4_bf16(w1[0], w1[1], sx), mx_pack4_bf16(w1[2], w1[3], sx)};
+        __builtin_amdgcn_raw_buffer_store_b64(c0, rq, m * I2 + colg + 8u * (uint32_t)(elane >> 5), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(c1, rq, m * I2 + colg + 16u + 8u * (uint32_t)(elane >> 5), 0, 0);
+        rword |= (uint32_t)(sx + 127) << (8 * j);
+      };
+      // Along the tokens: the block goes through the wave's 2 KB slot (row r at r * 64 bytes) and
+      // comes back by transposing reads (tcols_read), which the row-wise work of both halves then
+      // hides; tcols_quant encodes lane l's column l % 32, rows 16 (l / 32) + [0, 16).  The LDS unit
+      // runs one wave's operations in issue order, so the second half's writes to the slot cannot
+      // overtake the first half's reads.
+      const uint32_t trd = (uint32_t)(16 * ((elane >> 4) >> 1) + (elane & 15) / 4) * 64u +
+                           (uint32_t)(16 * ((elane >> 4) & 1) + 4 * (elane & 3)) * 2u;
+      auto tcols_read = [&](const u32x4 w0, const u32x4 w1, uint32_t (&tw)[8]) {
         uint8_t* lt = smem + kTOff + wave * 2048;
-        const int G4 = elane >> 4, sl = elane & 15;
-        const uint32_t rd = (uint32_t)(16 * (G4 >> 1) + sl / 4) * 64u + (uint32_t)(16 * (G4 & 1) + 4 * (sl & 3)) * 2u;
-        {
-          const uint32_t colg = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);   // dGU column
-          // the bf16 values stay packed: amax on the bit patterns, codes by the scaled conversion
-          const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-          const int sx = mx_shared_exp(max_xor32(bf16_amax<8>(wv)));
-          const u32x2 c0{mx_pack4_bf16(w0[0], w0[1], sx), mx_pack4_bf16(w0[2], w0[3], sx)};
-          const u32x2 c1{mx_pack4_bf16(w1[0], w1[1], sx), mx_pack4_bf16(w1[2], w1[3], sx)};
-          __builtin_amdgcn_raw_buffer_store_b64(c0, rq, m * I2 + colg + 8u * (uint32_t)(elane >> 5), 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(c1, rq, m * I2 + colg + 16u + 8u * (uint32_t)(elane >> 5), 0, 0);
-          rword |= (uint32_t)(sx + 127) << (8 * j);
-          if (tv) {
-            *reinterpret_cast<u32x4*>(lt + r32 * 64 + (8 * (elane >> 5)) * 2) = w0;
-            *reinterpret_cast<u32x4*>(lt + r32 * 64 + (16 + 8 * (elane >> 5)) * 2) = w1;
-            asm volatile("" ::: "memory");   // in-order LDS within the wave: no counter wait
-            typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
-            const auto base = (__attribute__((address_space(3))) uint8_t*)(lt);
-            uint32_t tw[8];   // rows 16 (l / 32) + [0, 16) of column l % 32, two bf16 per word
+        *reinterpret_cast<u32x4*>(lt + r32 * 64 + (8 * (elane >> 5)) * 2) = w0;
+        *reinterpret_cast<u32x4*>(lt + r32 * 64 + (16 + 8 * (elane >> 5)) * 2) = w1;
+        asm volatile("" ::: "memory");
+        typedef __attribute__((address_space(3))) bf16x4_t lds_v4;
+        const auto base = (__attribute__((address_space(3))) uint8_t*)(lt);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + rd + q * 256u));
-              const u32x2 rw = __builtin_bit_cast(u32x2, r);
-              tw[2 * q] = rw[0];
-              tw[2 * q + 1] = rw[1];
-            }
-            asm volatile("" ::: "memory");
-            const int st = mx_shared_exp(max_xor32(bf16_amax<8>(tw)));
-            const u32x4 c{mx_pack4_bf16(tw[0], tw[1], st), mx_pack4_bf16(tw[2], tw[3], st),
-                          mx_pack4_bf16(tw[4], tw[5], st), mx_pack4_bf16(tw[6], tw[7], st)};
-            // through descriptors over the block's 32 transposed rows: a split_sizes array that does
-            // not match rows_pad cannot take the stores outside the buffers
-            const uint32_t rp = (uint32_t)p.rows_pad, prow = (uint32_t)(cur.poff + srel);
-            const rsrc_t rt = make_rsrc(p.dgu_tq + (int64_t)colg * p.rows_pad, 32u * rp);
-            __builtin_amdgcn_raw_buffer_store_b128(c, rt, (uint32_t)(elane & 31) * rp + prow + 16u * (uint32_t)(elane >> 5),
-                                                   0, 0);
-            cword |= (uint32_t)(st + 127) << (8 * i);
-          }
+        for (int q = 0; q < 4; ++q) {
+          const bf16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_v4*)(base + trd + q * 256u));
+          const u32x2 rw = __builtin_bit_cast(u32x2, r);
+          tw[2 * q] = rw[0];
+          tw[2 * q + 1] = rw[1];
         }
+        asm volatile("" ::: "memory");
+      };
+      auto tcols_quant = [&](const uint32_t (&tw)[8], int half, int i, int j, uint32_t& cword) {
+        const int srel = cur.mt * kBM + wm * 128 + i * 32;                   // block's first segment row
+        const uint32_t colg = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);
+        const int st = mx_shared_exp(max_xor32(bf16_amax<8>(tw)));
+        const u32x4 c{mx_pack4_bf16(tw[0], tw[1], st), mx_pack4_bf16(tw[2], tw[3], st),
+                      mx_pack4_bf16(tw[4], tw[5], st), mx_pack4_bf16(tw[6], tw[7], st)};
+        // through descriptors over the block's 32 transposed rows: a split_sizes array that does
+        // not match rows_pad cannot take the stores outside the buffers
+        const uint32_t rp = (uint32_t)p.rows_pad, prow = (uint32_t)(cur.poff + srel);
+        const rsrc_t rt = make_rsrc(p.dgu_tq + (int64_t)colg * p.rows_pad, 32u * rp);
+        __builtin_amdgcn_raw_buffer_store_b128(c, rt, (uint32_t)(elane & 31) * rp + prow + 16u * (uint32_t)(elane >> 5), 0, 0);
+        cword |= (uint32_t)(st + 127) << (8 * i);
       };
       [[maybe_unused]] uint32_t rsw[2] = {0u, 0u};                    // row scale words (current i)
       [[maybe_unused]] uint32_t csw[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};   // column ones, by j
@@ -631,8 +634,21 @@ void bwd_gemm_kernel(const BwdKArgs p) {
             }
           }
           if constexpr (kQ) {
-            quant_half(gb[0], gb[1], 0, i, j, rsw[0], csw[j][0]);
-            quant_half(ub[0], ub[1], 1, i, j, rsw[1], csw[j][1]);
+            // blocks past the segment's padded end get no token-axis codes (they belong to the next
+            // segment); rows past the expert's tokens inside it are zero
+            const int srel = cur.mt * kBM + wm * 128 + i * 32;
+            if (srel < (cur.Me + 127) / 128 * 128) {                    // wave-uniform
+              uint32_t twg[8], twu[8];
+              tcols_read(gb[0], gb[1], twg);
+              quant_rows(gb[0], gb[1], 0, i, j, rsw[0]);
+              tcols_read(ub[0], ub[1], twu);
+              quant_rows(ub[0], ub[1], 1, i, j, rsw[1]);
+              tcols_quant(twg, 0, i, j, csw[j][0]);
+              tcols_quant(twu, 1, i, j, csw[j][1]);
+            } else {
+              quant_rows(gb[0], gb[1], 0, i, j, rsw[0]);
+              quant_rows(ub[0], ub[1], 1, i, j, rsw[1]);
+            }
             if (j == 3) {
               // the row's scale words of the wave's 4 column blocks, dG then dU
               const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
@@ -646,7 +662,6 @@ void bwd_gemm_kernel(const BwdKArgs p) {
             }
           }
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (kQ) {
         // a column's scale words of the wave's 4 row blocks: the wave's 128 rows lie wholly inside
