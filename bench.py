@@ -209,6 +209,18 @@ def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0, per_
         del fl
         res["cold"] = {"step_gpu_ms": _stats(cold_step),
                        "phase_ms": {n: _stats([r[i] for r in cold_ph]) for i, n in enumerate(names)}}
+    # the grouped GEMMs' per-wave cycle split (main loops vs epilogues, shader clock), from one more
+    # call outside the timed region with the library's diagnostic counters on
+    tbuf = m.tile_stats_new(dev)
+    m.set_tile_stats(tbuf)
+    try:
+        if backward:
+            fcall(None)
+        call(None)
+        torch.cuda.synchronize()
+    finally:
+        m.set_tile_stats(None)
+    res["tile_cycles"] = m.tile_stats_summary(tbuf)
     res["split_sizes"] = perm["split_sizes"].cpu().tolist()
     res["inputs"] = inp
     if backward:
@@ -285,6 +297,7 @@ def fwd_leg(cfg, steps, warmup, cold_steps=5, copy_ceiling=None):
         "phase_ms": {k_: round(v, 4) for k_, v in ph.items()},
         "stats": r["stats"],
         "split_sizes": r["split_sizes"],
+        "tile_cycles": r["tile_cycles"],
     }
     if "cold" in r:
         out["cold"] = r["cold"]
@@ -349,6 +362,7 @@ def bwd_leg(cfg, steps, warmup, per_call_wt=False):
         "forward_with_save_phase_ms": {k_: round(v, 4) for k_, v in r["fwd_save"]["phase_ms"].items()},
         "train_step_ms": round(r["fwd_save"]["ms_per_step"] + ms, 4),
         "train_step_tokens_per_s": round(cfg.T / ((r["fwd_save"]["ms_per_step"] + ms) * 1e-3), 1),
+        "tile_cycles": r["tile_cycles"],
     }
 
 
@@ -563,6 +577,7 @@ def main():
         "fc2_tflops": leg["fc2_tflops"], "hbm_GBs": leg["hbm_GBs"],
         "phase_ms": leg["phase_ms"], "stats": leg["stats"], "cold": leg.get("cold"),
         "memory_kernels": leg["memory_kernels"], "split_sizes": leg["split_sizes"],
+        "tile_cycles": leg["tile_cycles"],
     }
     if copy:
         line["copy_ceiling"] = copy

@@ -482,6 +482,22 @@ moe_status moe_grouped_mlp_fwd_loop(const moe_mlp_fwd_args* a, const int32_t* sp
  * rewrites the flag).  Returns -1 if the HIP calls fail. */
 int moe_read_device_error(void* workspace, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Diagnostic for callers measuring the grouped GEMMs, not for production.
+ * moe_set_tile_stats(buf, bytes) with a device buffer of at least
+ * moe_tile_stats_bytes() bytes makes every later grouped-GEMM launch of
+ * moe_grouped_mlp_fwd / _bwd (and their _ex forms; not the per-expert loop)
+ * record, per wave, shader-clock cycle counts (s_memtime) into its slot of
+ * buf; NULL turns it off (the default).  Slots, each 256 workgroups x 4 waves
+ * x 4 uint32 words {main-loop cycles, epilogue cycles, work items, 0x7153}:
+ * 0 FC1, 1 FC2 (main pass), 2 FC2 dgrad, 3 FC2 wgrad, 4 FC1 dgrad (main
+ * pass), 5 FC1 wgrad.  A launch rewrites its slot; words of waves with no work
+ * item are still written.  Outputs are unchanged.  The setting is process-wide
+ * and not synchronized: set it while no call is being made.
+ * MOE_ERR_INVALID_ARG if buf is not NULL and bytes is too small. */
+size_t moe_tile_stats_bytes(void);
+moe_status moe_set_tile_stats(uint32_t* device_buf, size_t bytes);
+
 /* Human-readable name of a status code. */
 const char* moe_status_string(int status);
 

@@ -28,7 +28,8 @@ EXPORTS = (
     "moe_grouped_mlp_bwd", "moe_read_device_error", "moe_grouped_mlp_fwd_ex", "moe_fwd_phase_count",
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
     "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop", "fp8_tensor_quantize_workspace",
-    "fp8_tensor_quantize", "mxfp8_quantize_weights", "moe_permute_noalloc",
+    "fp8_tensor_quantize", "mxfp8_quantize_weights", "moe_permute_noalloc", "moe_tile_stats_bytes",
+    "moe_set_tile_stats",
 )
 NOALLOC_SCRATCH_BYTES = 4 << 20    # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -130,6 +131,10 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_bwd_phase_name.argtypes = [ctypes.c_int]
     lib.moe_read_device_error.restype = ctypes.c_int
     lib.moe_read_device_error.argtypes = [_vp, _vp]
+    lib.moe_tile_stats_bytes.restype = ctypes.c_size_t
+    lib.moe_tile_stats_bytes.argtypes = []
+    lib.moe_set_tile_stats.restype = ctypes.c_int
+    lib.moe_set_tile_stats.argtypes = [_vp, ctypes.c_size_t]
     lib.moe_grouped_mlp_fwd_loop.restype = ctypes.c_int
     lib.moe_grouped_mlp_fwd_loop.argtypes = [ctypes.POINTER(FwdArgs), ctypes.POINTER(_i32), _vp]
     lib.moe_route_topk.restype = ctypes.c_int
@@ -646,6 +651,47 @@ def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.floa
     _check(lib.moe_grouped_mlp_bwd(ctypes.byref(a), _stream(dev)), "moe_grouped_mlp_bwd")
     del keep
     return dx, dprob, dw1, dw2
+
+
+TILE_STAT_SLOTS = ("fc1", "fc2", "dgrad_fc2", "wgrad_fc2", "dgrad_fc1", "wgrad_fc1")
+
+
+def set_tile_stats(buf: Optional[torch.Tensor]) -> None:
+    """Diagnostic: record per-wave GEMM cycle counts into `buf` (an int32 device tensor of at least
+    moe_tile_stats_bytes() bytes) on later calls, or stop (None).  Process-wide; see moe.h."""
+    lib = load()
+    if buf is None:
+        _check(lib.moe_set_tile_stats(None, 0), "moe_set_tile_stats")
+        return
+    if buf.dtype != torch.int32 or not buf.is_cuda or not buf.is_contiguous():
+        raise TypeError("tile stats buffer must be a contiguous int32 device tensor")
+    _check(lib.moe_set_tile_stats(_ptr(buf), buf.numel() * 4), "moe_set_tile_stats")
+
+
+def tile_stats_new(device) -> torch.Tensor:
+    """A zeroed buffer for set_tile_stats."""
+    return torch.zeros(load().moe_tile_stats_bytes() // 4, dtype=torch.int32, device=device)
+
+
+def tile_stats_summary(buf: torch.Tensor) -> dict:
+    """Per GEMM slot recorded in `buf`: work items per wave (min, max), mean main-loop and epilogue
+    cycles per item, and the slowest wave's total cycles."""
+    import numpy as np
+    w = buf.view(len(TILE_STAT_SLOTS), -1, 4).cpu().numpy().astype(np.uint32).astype(np.float64)
+    out = {}
+    for k, name in enumerate(TILE_STAT_SLOTS):
+        v = w[k]
+        if not (v[:, 3] == 0x7153).all():
+            continue
+        items = v[:, 2]
+        n = max(items.sum(), 1.0)
+        out[name] = {"items_per_wave": [int(items.min()), int(items.max())],
+                     "main_cycles_per_item": round(v[:, 0].sum() / n),
+                     "epilogue_cycles_per_item": round(v[:, 1].sum() / n),
+                     "epilogue_frac": round(v[:, 1].sum() / max(v[:, 0].sum() + v[:, 1].sum(), 1.0), 4),
+                     "max_wave_cycles": int((v[:, 0] + v[:, 1]).max()),
+                     "mean_wave_cycles": round((v[:, 0] + v[:, 1]).mean())}
+    return out
 
 
 def moe_read_device_error(flag: torch.Tensor) -> int:

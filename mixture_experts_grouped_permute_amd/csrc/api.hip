@@ -322,6 +322,7 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   g1.pt_s_b = p.sw1;
   g1.pt_amax_out = p.h_amax;
   g1.h_f32 = a->h_f32;
+  g1.tstat = tile_stat_slot(kStatFc1);
   HIP_TRY(launch_fc1(g1, true, st));
   HIP_TRY(launch_pt_quant(p.h_bf, false, R, I, a->offsets, E, reinterpret_cast<uint8_t*>(p.h_op), p.sh, nullptr,
                           p.pt_part, st, p.h_amax));
@@ -343,6 +344,7 @@ moe_status fwd_fp8_tail(const moe_mlp_fwd_args* a, const FwdPlan& p, hipStream_t
   g2.out_f32 = x_f32;
   g2.pt_s_a = p.sh;
   g2.pt_s_b = p.sw2;
+  g2.tstat = tile_stat_slot(kStatFc2);
   HIP_TRY(launch_fc2(g2, true, st));
   MOE_CHECK(mark(6), MOE_ERR_HIP);
 
@@ -388,7 +390,14 @@ moe_status permute_launch(const void* x, int x_dtype, int64_t T, int64_t H, cons
 
 constexpr int kMaxDevices = 64;
 
+// diagnostic per-wave cycle counts of the grouped GEMMs (moe_set_tile_stats), or null
+uint32_t* g_tile_stats = nullptr;
+
 }  // namespace
+
+uint32_t* moe::tile_stat_slot(int slot) {
+  return g_tile_stats ? g_tile_stats + (size_t)slot * kTileStatLaunchWords : nullptr;
+}
 
 extern "C" {
 
@@ -647,6 +656,7 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
   g1.save_gu = reinterpret_cast<uint16_t*>(a->saved_gu);
   g1.save_h = mx ? reinterpret_cast<uint16_t*>(a->saved_h) : nullptr;
   g1.h_f32 = a->h_f32;
+  g1.tstat = tile_stat_slot(kStatFc1);
   HIP_TRY(launch_fc1(g1, mx, st));
   MOE_CHECK(mark(5), MOE_ERR_HIP);
 
@@ -665,6 +675,7 @@ moe_status moe_grouped_mlp_fwd_ex(const moe_mlp_fwd_args* a, void* stream, void*
   g2.out = p.z;
   g2.part = p.part;
   g2.out_f32 = x_f32;
+  g2.tstat = tile_stat_slot(kStatFc2);
   HIP_TRY(launch_fc2(g2, mx, st));
   MOE_CHECK(mark(6), MOE_ERR_HIP);
 
@@ -822,6 +833,7 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
     d2.tab = a->w2; d2.ldb = I * 2;
   }
   MOE_CHECK(mark(2), MOE_ERR_HIP);
+  d2.tstat = tile_stat_slot(kStatDgradFc2);
   HIP_TRY(launch_bwd_dgrad_fc2(d2, mx, st));
   // the token-axis scale bytes past the last padded segment: a wgrad scale-group load may read them
   if (mx) HIP_TRY(launch_scale_tail_zero(p.dguTs, 2 * I, p.rows_pad / 32, a->split_sizes, E, st));
@@ -848,6 +860,7 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
     w2.b = a->saved_h; w2.ldb = I * 2;
   }
   MOE_CHECK(mark(4), MOE_ERR_HIP);
+  w2.tstat = tile_stat_slot(kStatWgradFc2);
   HIP_TRY(launch_bwd_wgrad(w2, mx, st));
   MOE_CHECK(mark(5), MOE_ERR_HIP);
 
@@ -867,6 +880,7 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
     d1.tab = a->w1; d1.ldb = H * 2;
   }
   MOE_CHECK(mark(6), MOE_ERR_HIP);
+  d1.tstat = tile_stat_slot(kStatDgradFc1);
   HIP_TRY(launch_bwd_dgrad_fc1(d1, mx, st));
   MOE_CHECK(mark(7), MOE_ERR_HIP);
 
@@ -887,6 +901,7 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
     w1.b = a->saved_x_perm; w1.ldb = H * 2;
   }
   MOE_CHECK(mark(8), MOE_ERR_HIP);
+  w1.tstat = tile_stat_slot(kStatWgradFc1);
   HIP_TRY(launch_bwd_wgrad(w1, mx, st));
   MOE_CHECK(mark(9), MOE_ERR_HIP);
 
@@ -894,6 +909,14 @@ moe_status moe_grouped_mlp_bwd_ex(const moe_mlp_bwd_args* a, void* stream, void*
   HIP_TRY(launch_combine(p.dx_perm, io_f32, T, H, k, a->row_id_map, a->dx, io_f32, st));
   HIP_TRY(launch_dprob_reduce(p.dprob_part, R, parts, a->row_id_map, T, k, a->dprob, st));
   MOE_CHECK(mark(10), MOE_ERR_HIP);
+  return MOE_OK;
+}
+
+size_t moe_tile_stats_bytes(void) { return (size_t)kStatSlots * kTileStatLaunchWords * sizeof(uint32_t); }
+
+moe_status moe_set_tile_stats(uint32_t* device_buf, size_t bytes) {
+  if (device_buf && bytes < moe_tile_stats_bytes()) return MOE_ERR_INVALID_ARG;
+  g_tile_stats = device_buf;
   return MOE_OK;
 }
 

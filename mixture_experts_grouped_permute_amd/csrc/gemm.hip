@@ -59,6 +59,7 @@ struct FwdKArgs {
   const float* pt_s_b;
   uint32_t* pt_amax_out;     // per-tensor FP8, FC1: per expert max |bf16 h| (float bits, atomic max)
   float* h_f32;              // FC1: h in fp32 as the epilogue computes it, before rounding, or null
+  uint32_t* tstat;           // per-wave cycle counts (diagnostic), or null
   const uint8_t* w[kMaxExperts];
 };
 
@@ -271,7 +272,12 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     }
   }
 
+  // diagnostic (p.tstat): shader-clock cycles of the main loops and of the epilogues of this wave
+  const bool tst = p.tstat != nullptr;
+  uint64_t tc_main = 0, tc_epi = 0, tc_t = 0;
+  uint32_t n_items = 0;
   for (int round = 0; cur.t < hi; ++round) {
+    if (tst) tc_t = __builtin_amdgcn_s_memtime();
     decode(round + 1, nxt);
     descs(nxt, dn);
     const int ipar = round & 1;                          // probability buffer of this item
@@ -349,6 +355,11 @@ void fwd_gemm_kernel(const FwdKArgs p) {
     par = (par + n) & 1;
     spar = (spar + glast - g0 + 1) & 1;
 
+    if (tst) {
+      const uint64_t t = __builtin_amdgcn_s_memtime();
+      tc_main += t - tc_t;
+      tc_t = t;
+    }
     // ---- epilogue straight from the accumulators.  acc[i][j][4 q + c] of lane l is token row
     // wm*128 + 32 i + l % 32 of the tile and output column (weight block j) + 8 q + 4 (l / 32) + c.
     // Stores go through buffer descriptors that end at the tile's last row, so the rows of a
@@ -532,10 +543,21 @@ void fwd_gemm_kernel(const FwdKArgs p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * ld * kEsz, 0, 0);
     }
+    if (tst) {
+      tc_epi += __builtin_amdgcn_s_memtime() - tc_t;
+      ++n_items;
+    }
     cur = nxt;
     dc = dn;
   }
   wait_vmcnt<0>();
+  if (tst && lane == 0 && p.split != 2) {   // (a split-parts pass leaves the main pass's counts)
+    uint32_t* o = p.tstat + ((size_t)blockIdx.x * 4 + wave) * kTileStatWords;
+    o[0] = (uint32_t)tc_main;
+    o[1] = (uint32_t)tc_epi;
+    o[2] = n_items;
+    o[3] = kTileStatTag;
+  }
 }
 
 // Finishes the split tiles of an FC2 launch: the S row-major [256][256] fp32 partials of tile
@@ -613,6 +635,7 @@ FwdKArgs make_fwd_args(const FwdGemm& g, bool mx, bool fc1) {
   k.pt_s_b = g.pt_s_b;
   k.pt_amax_out = g.pt_amax_out;
   k.h_f32 = g.h_f32;
+  k.tstat = g.tstat;
   if (!mx)
     for (int e = 0; e < g.E; ++e) k.w[e] = reinterpret_cast<const uint8_t*>(g.w_tab[e]);
   return k;

@@ -47,6 +47,7 @@ struct BwdKArgs {
   int64_t I;
   uint8_t* out;             // FC1 dgrad: dx_perm [R, N]
   float* part;              // FC1 dgrad split parts: kGemmGrid x 64K floats
+  uint32_t* tstat;          // per-wave cycle counts (diagnostic), or null
   int split;                // FC1 dgrad: 0 every tile; 1 tiles before the split ones; 2 the split parts
   uint8_t *dgu_q, *dgu_s;   // MXFP8 FC2 dgrad: dGU quantized along 2I, [R, 2I] + [R, 2I / 32]
   uint8_t *dgu_tq, *dgu_ts; // and along tokens, [2I, rows_pad] + [2I, rows_pad / 32]
@@ -364,7 +365,12 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       dma_sg(dc, ng, 1, (cur.u0 + 1) >> 2);
     }
   }
+  // diagnostic (p.tstat): shader-clock cycles of the main loops and of the epilogues of this wave
+  const bool tst = p.tstat != nullptr;
+  uint64_t tc_main = 0, tc_epi = 0, tc_t = 0;
+  uint32_t n_items = 0;
   for (int round = 0; cur.t < hi; ++round) {
+    if (tst) tc_t = __builtin_amdgcn_s_memtime();
     decode(round + 1, nxt);
     descs(nxt, dn);
     const int ipar = round & 1;
@@ -434,6 +440,11 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     par = (par + cur.kT) & 1;
     }
 
+    if (tst) {
+      const uint64_t t = __builtin_amdgcn_s_memtime();
+      tc_main += t - tc_t;
+      tc_t = t;
+    }
     // ---- epilogue straight from the accumulators: acc[i][j][4 q + c] of lane l is output row
     // wm*128 + 32 i + l % 32 of the tile and column wn*128 + 32 j + 8 q + 4 (l / 32) + c.  Loads and
     // stores go through buffer descriptors that end at the tile's last valid row.
@@ -757,10 +768,21 @@ void bwd_gemm_kernel(const BwdKArgs p) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(pend[t], ro, pend_off + t * 8u * N32 * es, 0, kStoreAux);
     }
+    if (tst) {
+      tc_epi += __builtin_amdgcn_s_memtime() - tc_t;
+      ++n_items;
+    }
     cur = nxt;
     dc = dn;
   }
   wait_vmcnt<0>();
+  if (tst && lane == 0 && !(kRole == kRoleDgradFc1 && p.split == 2)) {   // (split parts: the main pass's)
+    uint32_t* o = p.tstat + ((size_t)blockIdx.x * 4 + wave) * kTileStatWords;
+    o[0] = (uint32_t)tc_main;
+    o[1] = (uint32_t)tc_epi;
+    o[2] = n_items;
+    o[3] = kTileStatTag;
+  }
 }
 
 template <int kRole, bool kMx>
@@ -811,6 +833,7 @@ BwdKArgs base_args(const BwdGemm& g) {
   k.dprob_part = g.dprob_part;
   k.I = g.I;
   k.out = reinterpret_cast<uint8_t*>(g.out);
+  k.tstat = g.tstat;
   if (g.tab)
     for (int e = 0; e < g.E; ++e) k.tab[e] = reinterpret_cast<const uint8_t*>(g.tab[e]);
   return k;

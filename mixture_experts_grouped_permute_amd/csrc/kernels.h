@@ -111,7 +111,19 @@ struct FwdGemm {
   // FC1: optional fp32 copy of h = silu(g) u p [R, I] as the epilogue computes it, before it is
   // rounded to bf16 or quantized (the input of the fused quantizer); nullptr: not written
   float* h_f32;
+  // diagnostic: kGemmGrid x 4 waves x kTileStatWords words of per-wave cycle counts (null: off)
+  uint32_t* tstat = nullptr;
 };
+// Per-wave cycle counts of a grouped GEMM launch (diagnostic, moe_set_tile_stats): words
+// {main-loop cycles, epilogue cycles, work items, kTileStatTag} per wave of each workgroup.
+constexpr int kTileStatWords = 4;
+constexpr uint32_t kTileStatTag = 0x7153u;
+constexpr size_t kTileStatLaunchWords = (size_t)kGemmGrid * 4 * kTileStatWords;
+// Slots of the launches that record them.
+enum : int { kStatFc1 = 0, kStatFc2, kStatDgradFc2, kStatWgradFc2, kStatDgradFc1, kStatWgradFc1, kStatSlots };
+// The caller's diagnostic buffer (kStatSlots x kTileStatLaunchWords words), or null.
+uint32_t* tile_stat_slot(int slot);
+
 // Workspace of the FC2 split-tile partials (bytes).
 constexpr size_t kFc2PartBytes = (size_t)kGemmGrid * 65536 * sizeof(float);
 hipError_t launch_fc1(const FwdGemm& g, bool mx, hipStream_t st);
@@ -152,6 +164,7 @@ struct BwdGemm {
   void* out;
   bool out_f32;
   float* part;              // FC1 dgrad: split-tile partials (kFc2PartBytes), or null for no split
+  uint32_t* tstat = nullptr;  // diagnostic per-wave cycle counts (kTileStatLaunchWords words), or null
 };
 hipError_t launch_bwd_dgrad_fc2(const BwdGemm& g, bool mx, hipStream_t st);
 hipError_t launch_bwd_dgrad_fc1(const BwdGemm& g, bool mx, hipStream_t st);

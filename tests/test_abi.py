@@ -323,3 +323,16 @@ def test_noalloc_permute_limit_on_host(lib):
     p = 0x1000
     assert f(None, 1, 130753, 0, p, None, 2, 256, 1, None, None, p, p, p, p, None, None, None) == MOE_ERR_UNSUPPORTED
     assert f(None, 1, 16, 0, p, None, 5, 4, 1, None, None, p, p, p, p, None, None, None) == MOE_ERR_INVALID_ARG
+
+
+def test_tile_stats_diagnostic_on_host(lib):
+    """moe_set_tile_stats: 6 GEMM slots of 256 x 4 waves x 4 words; a short buffer is refused
+    before anything is recorded, and NULL (off) is always accepted."""
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG, TILE_STAT_SLOTS
+    lib.moe_tile_stats_bytes.restype = ctypes.c_size_t
+    lib.moe_set_tile_stats.restype = ctypes.c_int
+    lib.moe_set_tile_stats.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    need = lib.moe_tile_stats_bytes()
+    assert need == len(TILE_STAT_SLOTS) * 256 * 4 * 4 * 4
+    assert lib.moe_set_tile_stats(0x1000, need - 4) == MOE_ERR_INVALID_ARG
+    assert lib.moe_set_tile_stats(None, 0) == 0
