@@ -503,17 +503,22 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       // bytes are collected into words, so that they leave as 4-byte stores: a row's bytes of the
       // wave's 4 column blocks (rword, byte j), and a column's bytes of the wave's 4 row blocks
       // (cword, byte i) -- both 4-byte aligned, as I % 128 == 0 and segments start at multiples of 128.
-      // Along 2I (quant_rows): codes and scale straight from the lane's runs.
-      auto quant_rows = [&](const u32x4 w0, const u32x4 w1, int half, int i, int j, uint32_t& rword) {
-        const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
-        const uint32_t colg = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128 + j * 32);   // dGU column
+      // Along 2I (quant_rows): codes and scale from the lane's runs.  The codes of run pp (8 bytes,
+      // columns 16 pp + 8 hh) are traded with lane l ^ 32 (v_permlane32_swap) so that the lane holds
+      // the block row's 16-byte chunk hh; the 4 blocks of a row block then leave through the LDS
+      // slot as whole 128-byte rows per half (stage_rows32), instead of 16-byte pieces of 32 rows.
+      auto quant_rows = [&](const u32x4 w0, const u32x4 w1, int j, uint32_t& rword, u32x4& chunk) {
         // the bf16 values stay packed: amax on the bit patterns, codes by the scaled conversion
         const uint32_t wv[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
         const int sx = mx_shared_exp(max_xor32(bf16_amax<8>(wv)));
-        const u32x2 c0{mx_pack4_bf16(w0[0], w0[1], sx), mx_pack4_bf16(w0[2], w0[3], sx)};
-        const u32x2 c1{mx_pack4_bf16(w1[0], w1[1], sx), mx_pack4_bf16(w1[2], w1[3], sx)};
-        __builtin_amdgcn_raw_buffer_store_b64(c0, rq, m * I2 + colg + 8u * (uint32_t)(elane >> 5), 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(c1, rq, m * I2 + colg + 16u + 8u * (uint32_t)(elane >> 5), 0, 0);
+        const uint32_t c0[2] = {mx_pack4_bf16(w0[0], w0[1], sx), mx_pack4_bf16(w0[2], w0[3], sx)};
+        const uint32_t c1[2] = {mx_pack4_bf16(w1[0], w1[1], sx), mx_pack4_bf16(w1[2], w1[3], sx)};
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(c0[k], c1[k], false, false);
+          chunk[k] = sw[0];
+          chunk[2 + k] = sw[1];
+        }
         rword |= (uint32_t)(sx + 127) << (8 * j);
       };
       // Along the tokens: the block goes through the wave's 2 KB slot (row r at r * 64 bytes) and
@@ -553,6 +558,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
         cword |= (uint32_t)(st + 127) << (8 * i);
       };
       [[maybe_unused]] uint32_t rsw[2] = {0u, 0u};                    // row scale words (current i)
+      [[maybe_unused]] u32x4 rcode[2][4];                             // row codes (current i), by half, j
       [[maybe_unused]] uint32_t csw[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};   // column ones, by j
       // BF16: dG (then dU) of the two column blocks j, j + 1 of a row block, staged row by row in the
       // wave's slot (16-byte chunk c of row r at chunk c ^ (r & 7): conflict-free reads, 2-way
@@ -651,22 +657,38 @@ void bwd_gemm_kernel(const BwdKArgs p) {
             if (srel < (cur.Me + 127) / 128 * 128) {                    // wave-uniform
               uint32_t twg[8], twu[8];
               tcols_read(gb[0], gb[1], twg);
-              quant_rows(gb[0], gb[1], 0, i, j, rsw[0]);
+              quant_rows(gb[0], gb[1], j, rsw[0], rcode[0][j]);
               tcols_read(ub[0], ub[1], twu);
-              quant_rows(ub[0], ub[1], 1, i, j, rsw[1]);
+              quant_rows(ub[0], ub[1], j, rsw[1], rcode[1][j]);
               tcols_quant(twg, 0, i, j, csw[j][0]);
               tcols_quant(twu, 1, i, j, csw[j][1]);
             } else {
-              quant_rows(gb[0], gb[1], 0, i, j, rsw[0]);
-              quant_rows(ub[0], ub[1], 1, i, j, rsw[1]);
+              quant_rows(gb[0], gb[1], j, rsw[0], rcode[0][j]);
+              quant_rows(ub[0], ub[1], j, rsw[1], rcode[1][j]);
             }
             if (j == 3) {
-              // the row's scale words of the wave's 4 column blocks, dG then dU
+              // the row block's codes of the wave's 4 column blocks (128 bytes per row and half), and
+              // the rows' scale words, dG then dU (I % 128 == 0: the 4 blocks are all valid)
               const uint32_t m = (uint32_t)(wm * 128 + i * 32 + r32);
 #pragma unroll
               for (int half = 0; half < 2; ++half) {
-                const uint32_t cb = ((half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128)) / 32;
-                const uint32_t so = (elane >> 5) == 0 ? m * (I2 / 32) + cb : 0xFFFFFFF0u;
+                uint32_t lo[8], hi[8];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                  lo[k] = rcode[half][0][k];
+                  lo[4 + k] = rcode[half][1][k];
+                  hi[k] = rcode[half][2][k];
+                  hi[4 + k] = rcode[half][3][k];
+                }
+                u32x4 v[4];
+                stage_rows32(smem + kTOff + wave * 2048, lo, hi, elane, v);
+                const uint32_t c0 = (half ? I32 : 0u) + (uint32_t)n0 + (uint32_t)(wn * 128);
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                  const uint32_t mm = (uint32_t)(wm * 128 + i * 32 + 8 * t + (elane >> 3));
+                  __builtin_amdgcn_raw_buffer_store_b128(v[t], rq, mm * I2 + c0 + ((uint32_t)elane & 7u) * 16u, 0, 0);
+                }
+                const uint32_t so = (elane >> 5) == 0 ? m * (I2 / 32) + c0 / 32 : 0xFFFFFFF0u;
                 __builtin_amdgcn_raw_buffer_store_b32(rsw[half], rqs, so, 0, 0);
                 rsw[half] = 0;
               }
