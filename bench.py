@@ -116,6 +116,9 @@ def _flusher():
     return lambda: buf.fill_(1.0)
 
 
+TILE_STATS = True   # bench.py --no-tile-stats turns it off
+
+
 def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0, per_call_wt=False):
     import torch
     import mixture_experts_grouped_permute_amd as m
@@ -211,16 +214,18 @@ def run_gpu(cfg, steps, warmup, backward=False, cached=False, cold_steps=0, per_
                        "phase_ms": {n: _stats([r[i] for r in cold_ph]) for i, n in enumerate(names)}}
     # the grouped GEMMs' per-wave cycle split (main loops vs epilogues, shader clock), from one more
     # call outside the timed region with the library's diagnostic counters on
-    tbuf = m.tile_stats_new(dev)
-    m.set_tile_stats(tbuf)
-    try:
-        if backward:
-            fcall(None)
-        call(None)
-        torch.cuda.synchronize()
-    finally:
-        m.set_tile_stats(None)
-    res["tile_cycles"] = m.tile_stats_summary(tbuf)
+    res["tile_cycles"] = None
+    if TILE_STATS:
+        tbuf = m.tile_stats_new(dev)
+        m.set_tile_stats(tbuf)
+        try:
+            if backward:
+                fcall(None)
+            call(None)
+            torch.cuda.synchronize()
+        finally:
+            m.set_tile_stats(None)
+        res["tile_cycles"] = m.tile_stats_summary(tbuf)
     res["split_sizes"] = perm["split_sizes"].cpu().tolist()
     res["inputs"] = inp
     if backward:
@@ -511,6 +516,8 @@ def main():
     ap.add_argument("--no-mxfp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-tile-stats", action="store_true",
+                    help="skip the untimed call with the GEMM cycle counters on (keeps profiler pass counts)")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--legs", default="copy,bf16,mxfp8,mxfp8_finegrained,fp8,backward,backward_mxfp8,router,loop",
                     help="comma list of copy, bf16, mxfp8, mxfp8_finegrained, fp8, backward, backward_mxfp8, router, "
@@ -521,6 +528,8 @@ def main():
                     help="only time torch.matmul on the gate-up projection's shape as one dense bf16 GEMM "
                          "(M = T*k = 8192, K = 4096, N = 2*14336), a reference for the MFMA counters")
     args = ap.parse_args()
+    global TILE_STATS
+    TILE_STATS = not args.no_tile_stats
     if args.lib_gemm_probe:
         import torch
         g = torch.Generator(device="cuda:0").manual_seed(0)
