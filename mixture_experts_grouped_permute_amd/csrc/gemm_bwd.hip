@@ -16,8 +16,9 @@
 // (ds_read_b64_tr_b16), which delivers the MFMA's K-major operand layout.
 // MXFP8 operands arrive already quantized along each GEMM's K in K-major
 // layout.  The main loop is the forward's interleaved stage schedule, the last
-// stage of a tile loads the first stage of the next one, and the epilogues
-// store straight from the accumulators.
+// stage of a tile loads the first stage of the next one, and the epilogues read
+// the accumulators block by block and store whole 128-byte rows through a small
+// LDS slot per wave (stage_rows32).
 #include "gemm_core.h"
 
 namespace moe {
