@@ -97,9 +97,9 @@ void fwd_gemm_kernel(const FwdKArgs p) {
   constexpr int kScOff = 2 * kStageBytes;
   constexpr int kScBuf = 8192;
   constexpr int kPrOff = kScOff + (kMx ? 2 * kScBuf : 0);
-  // FC2: a 2 KB slot per wave for the epilogue's full-line stores
-  constexpr int kFOff = kPrOff + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kPrOff + (kFc1 ? 2 * 1024 : 16 + 4 * 2048)];
+  // a 2 KB slot per wave for the epilogue's full-line stores
+  constexpr int kFOff = kPrOff + (kFc1 ? 2 * 1024 : 16);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kFOff + 4 * 2048];
   __shared__ Sched sched;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -387,14 +387,38 @@ void fwd_gemm_kernel(const FwdKArgs p) {
       const float dq = pt ? (1.0f / p.pt_s_a[cur.e]) * (1.0f / p.pt_s_b[cur.e]) : 1.0f;
       float hmax = 0.f;   // per-tensor FP8: the largest |h| of the wave's blocks (rows past the tile's
                           // end are zero: zero A rows and probability)
+      // bf16 outputs (h, the saved g / u, the saved h): the wave's two 32-column blocks of a row
+      // block make 128 bytes per row, which leave through the wave's LDS slot as whole rows
+      // (stage_rows32) once the second block is done; kept[.] holds the first block's runs
+      uint8_t* sl = smem + kFOff + wave * 2048;
+      const uint32_t cw = (uint32_t)cur.nt * 128u + (uint32_t)(wn * 64);   // the wave's first h column
+      auto stage_pair = [&](const u32x4 (&e)[2], const u32x4 (&o)[2], const rsrc_t& rs, uint32_t row_bytes,
+                            uint32_t col_byte, int i) {
+        uint32_t lo[8], hi[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          lo[k] = e[0][k];
+          lo[4 + k] = e[1][k];
+          hi[k] = o[0][k];
+          hi[4 + k] = o[1][k];
+        }
+        u32x4 v[4];
+        stage_rows32(sl, lo, hi, elane, v);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t mm = (uint32_t)(wm * 128 + i * 32 + 8 * t + (elane >> 3));
+          __builtin_amdgcn_raw_buffer_store_b128(v[t], rs, mm * row_bytes + col_byte + ((uint32_t)elane & 7u) * 16u, 0, 0);
+        }
+      };
+      u32x4 kg[2], ku[2], kh[2];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = wm * 128 + i * 32 + r32;
         const float pr = prs[m];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
-          const uint32_t col = (uint32_t)cur.nt * 128u + (uint32_t)(wn * 64 + jj * 32);   // h column of the block
-          if (col >= I32) continue;                                                         // wave-uniform
+          const uint32_t col = cw + (uint32_t)(jj * 32);                                     // h column of the block
+          if (cw >= I32) continue;                 // wave-uniform; I % 64 == 0: both blocks or neither
           float g[16], u[16];
           agpr_read16(core.acc[i][jj], g);
           agpr_read16(core.acc[i][jj + 2], u);
@@ -402,18 +426,18 @@ void fwd_gemm_kernel(const FwdKArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) { g[r] *= dq; u[r] *= dq; }
           }
-          // stores go out in the lane-paired layout (pack_bf16_runs8 / swap_runs8): the lane's 8
-          // consecutive columns 16 pp + 8 hh + [0, 8) of the block
+          // the lane-paired layout (pack_bf16_runs8 / swap_runs8): the lane's 8 consecutive columns
+          // 16 pp + 8 hh + [0, 8) of the block
           const uint32_t e8 = (uint32_t)m * I32 + col + 2u * (uint32_t)ch;                  // element of h
           if (p.save_gu) {
             u32x4 og[2], ou[2];
             pack_bf16_runs8(g, og);
             pack_bf16_runs8(u, ou);
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp) {
-              const uint32_t o = (2 * (uint32_t)m * I32 + col + 2u * (uint32_t)ch + 16u * pp) * 2u;
-              __builtin_amdgcn_raw_buffer_store_b128(og[pp], rg, o, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b128(ou[pp], rg, o + I32 * 2u, 0, 0);
+            if (jj == 0) {
+              kg[0] = og[0]; kg[1] = og[1]; ku[0] = ou[0]; ku[1] = ou[1];
+            } else {
+              stage_pair(kg, og, rg, I32 * 4u, cw * 2u, i);
+              stage_pair(ku, ou, rg, I32 * 4u, (I32 + cw) * 2u, i);
             }
           }
           float v[16];
@@ -434,9 +458,11 @@ void fwd_gemm_kernel(const FwdKArgs p) {
           if (!kMx || pt || p.save_h) {
             u32x4 oh[2];
             pack_bf16_runs8(v, oh);
-#pragma unroll
-            for (int pp = 0; pp < 2; ++pp)
-              __builtin_amdgcn_raw_buffer_store_b128(oh[pp], kMx ? rh : ro, (e8 + 16u * pp) * 2u, 0, 0);
+            if (jj == 0) {
+              kh[0] = oh[0]; kh[1] = oh[1];
+            } else {
+              stage_pair(kh, oh, kMx ? rh : ro, I32 * 2u, cw * 2u, i);
+            }
           }
           if constexpr (kMx && !pt) {
             // the 32-column block of this row is split between lanes l and l ^ 32
