@@ -118,6 +118,31 @@ def test_forward_split_last_round(compute):
     assert err < tol
 
 
+@gpu
+@pytest.mark.parametrize("compute", ["bf16", "mxfp8"])
+def test_forward_split_last_round_short_k(compute):
+    """Short K with a nearly empty last round (the 64-expert layer's FC2 shape): K = I = 1408 is
+    11 MXFP8 stages (its E8M0 rows are not whole 16-byte groups, the four-lane scale loads) or
+    22 BF16 ones, and 130 M-blocks x 2 N-tiles = 260 tiles leave 4 for the last round, which
+    runs unsplit (K is too short for parts of kMinSplitUnits stages).  Experts 3 and 7 (the
+    last tiles are expert 7's; the routing pairs them) are compared."""
+    m = need_gpu()
+    counts = [4096] * 6 + [4100, 4100]                    # 16 x 6 + 17 x 2 = 130 M-blocks
+    cfg = cfg_small(T=sum(counts) // 2, H=512, I=1408, E=8, k=2)
+    log(f"fwd short-K split-tail {compute} T={cfg.T} H={cfg.H} I={cfg.I}")
+    inp = _inputs(cfg, counts)
+    out, ctx = _run(m, inp, compute)
+    idx = inp.topk_idx.numpy()
+    experts = (3, 7)
+    rows = np.all(np.isin(idx, experts), axis=1)
+    assert rows.sum() >= 1024
+    ref = mlp.forward(inp.x, idx, inp.topk_prob, inp.w1, inp.w2, compute, cfg.x_dtype, experts=experts)
+    err = mlp.normwise_rel_err(to_np(out)[rows], ref.out[rows])
+    tol = BF16_TOL if compute == "bf16" else MXFP8_TOL
+    log(f"  {rows.sum()} tokens, normwise err {err:.3e} (tol {tol})")
+    assert err < tol
+
+
 def _fused_h_check(m, inp):
     """Forward with the FC1 epilogue's debug outputs: the E4M3 codes and E8M0 scales its fused
     quantizer wrote must be the oracle quantizer's bytes for the kernel's own fp32 h (one
