@@ -408,7 +408,8 @@ const char* moe_fwd_phase_name(int i);   /* NULL when out of range */
  *   dgu_bf16      [R, 2I] bf16, the values that are quantized;
  *   dgu_codes     [R, 2I] E4M3 and dgu_scales [R, 2I/32] E8M0 (row-wise);
  *   dgu_t_codes   [2I, rows_pad] E4M3 and dgu_t_scales [2I, rows_pad/32] E8M0,
- *                 transposed, with rows_pad = ceil(R/128)*128 + 128*E: expert
+ *                 transposed, with rows_pad = ceil(R/128)*128 + 128*E rounded
+ *                 up to a multiple of 512 (ABI version 7; 6: not rounded): expert
  *                 e's tokens at columns [P_e, P_e + M_e) where P_e is the sum of
  *                 the earlier experts' counts each rounded up to 128; 32-token
  *                 blocks restart at P_e, the columns up to the next multiple of

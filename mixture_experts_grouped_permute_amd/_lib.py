@@ -629,7 +629,8 @@ def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.floa
     per-call quantization of the transposed weights is skipped.
     debug: optional dict (MXFP8): filled with the FC2 dgrad epilogue's dgu in bf16 ("dgu_bf16"
     [R, 2I]) and its two quantizations ("dgu_codes", "dgu_scales" row-wise; "dgu_t_codes",
-    "dgu_t_scales" along tokens, [2I, rows_pad] with rows_pad = ceil(R/128)*128 + 128 E).
+    "dgu_t_scales" along tokens, [2I, rows_pad] with rows_pad = ceil(R/128)*128 + 128 E rounded up to
+    a multiple of 512).
     Returns (dx [T,H], dprob [T,k] f32, dw1 [E,2I,H], dw2 [E,H,I])."""
     lib = load()
     dev = dy.device
@@ -637,7 +638,7 @@ def moe_grouped_mlp_bwd(dy: torch.Tensor, ctx: dict, w1, w2, dw_dtype=torch.floa
     dx, dprob, dw1, dw2 = outs
     if debug is not None:
         R, I2, E = int(a.T) * int(a.k), 2 * int(a.I), int(a.E)
-        rp = (R + 127) // 128 * 128 + 128 * E
+        rp = ((R + 127) // 128 * 128 + 128 * E + 511) // 512 * 512
         u8 = lambda *shape: torch.zeros(shape, dtype=torch.uint8, device=dev)
         debug.update(dgu_bf16=torch.zeros((R, I2), dtype=torch.bfloat16, device=dev), dgu_codes=u8(R, I2),
                      dgu_scales=u8(R, I2 // 32), dgu_t_codes=u8(I2, rp), dgu_t_scales=u8(I2, rp // 32))

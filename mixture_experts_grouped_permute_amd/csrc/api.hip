@@ -219,7 +219,9 @@ BwdPlan plan_bwd(const moe_mlp_bwd_args* a, void* ws) {
   p.dx_perm = c.take((size_t)(R * H) * io_size(a->io_dtype));
   p.part = reinterpret_cast<float*>(c.take(kFc2PartBytes));
   if (mx) {
-    const int64_t Rp = (R + 127) / 128 * 128 + 128 * (int64_t)E;
+    // the token-padded layout's rows: every segment padded to 128 tokens, the row length to 512
+    // (whole 16-byte E8M0 groups per row for the weight gradients' scale loads)
+    const int64_t Rp = ((R + 127) / 128 * 128 + 128 * (int64_t)E + 511) / 512 * 512;
     p.rows_pad = Rp;
     auto take8 = [&](int64_t n) { return reinterpret_cast<uint8_t*>(c.take((size_t)n)); };
     p.dzq = take8(R * H); p.dzs = take8(R * H / 32);
@@ -401,7 +403,7 @@ uint32_t* moe::tile_stat_slot(int slot) {
 
 extern "C" {
 
-int moe_abi_version(void) { return 6; }
+int moe_abi_version(void) { return 7; }
 
 const char* moe_status_string(int status) {
   switch (status) {

@@ -73,16 +73,19 @@ struct BwdItem {
   int poff;                 // MXFP8 FC2 dgrad: the expert's first column in the token-padded layout
   int kz;                   // stages with data: loads of stages kz .. kT-1 read zeros (deep wgrad)
   int part, u0;             // K part of a split tile (-1: whole K) and its first stage
+  int gs;                   // deep MXFP8 wgrad: stage of the item's first stage within its 16-byte scale group
   int64_t koff;
 };
 
 // kDeep (MXFP8): the forward's deep MXFP8 pipeline -- the stage barrier between the two MX
 // substeps, stage loads issued two stages ahead, and the E8M0 bytes of four stages loaded together.
-//   * dgrad (K % 512 == 0): one 16-byte scale load per row per group of four stages;
-//   * wgrad: an expert's token segment starts at a multiple of 128 tokens, so its scale bytes start
-//     4-byte aligned, and four lanes read a row's four words of a group (merged into one request).
-//     Every item runs at least two stages, as the pipeline needs: the stages past an expert's
-//     tokens (an expert with at most 128 tokens, or none) load zeros, which add nothing.
+//   * one 16-byte scale load per row per group of four stages.  In dgrad (K % 512 == 0) the groups
+//     start at K = 0.  In wgrad the groups are the token-padded layout's own 512-token (16-byte)
+//     ones -- its row length is a multiple of 512 -- and an expert's segment, which starts at a
+//     multiple of 128 tokens, enters its first group at stage gs = (start / 128) % 4; the bytes of
+//     a group outside the segment belong to its neighbours and are never read back.
+//     Every wgrad item runs at least two stages, as the pipeline needs: the stages past an
+//     expert's tokens (an expert with at most 128 tokens, or none) load zeros, which add nothing.
 template <int kRole, bool kMx, bool kOutF32, bool kDeep = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_gemm_kernel(const BwdKArgs p) {
@@ -91,7 +94,6 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   constexpr bool kBMN = !kMx;          // bf16: B is N-contiguous (weights in dgrad, activations in wgrad)
   constexpr bool kD2 = kRole == kRoleDgradFc2;
   static_assert(!kDeep || kMx, "deep pipeline: MXFP8 only");
-  constexpr bool kSc4 = kDeep && kWg;   // four-lane word form of the scale group loads
   // two stages of A + B (64 KB each), the MXFP8 scales (2 x 2 KB of one word per row per stage, or
   // in the deep pipeline 2 x 8 KB of 16 bytes per row per group of four stages), and for the FC2
   // dgrad the routing probabilities of the tile's rows (2 x 1 KB, by work item) and the per-row
@@ -135,6 +137,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     it.kT = 0;
     it.kz = 0;
     it.u0 = 0;
+    it.gs = 0;
     it.part = -1;
     if (it.t >= hi) return;
     if constexpr (kWg) {
@@ -148,6 +151,7 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       it.koff = kMx ? __builtin_amdgcn_readfirstlane(sched.tile[it.e]) : __builtin_amdgcn_readfirstlane(sched.off[it.e]);
       it.kT = (it.Me + kKStep - 1) / kKStep;
       it.kz = it.kT;
+      if (kDeep) it.gs = (int)((it.koff / 128) & 3);
       if (kDeep && it.kT < 2) it.kT = 2;
       it.row0 = it.mt * kBM;
       it.mrows = (int)min((int64_t)kBM, p.M - it.row0);
@@ -241,8 +245,11 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       if constexpr (kWg) {
         // ranges end at the scale arrays' ends: a group of scale bytes read past the last segment
         // (padding scales up to rows_pad) reads zeros beyond it
-        d.vas = make_vsharp(p.as + m0w * p.ldas + it.koff / 32, (uint32_t)(it.mrows * p.ldas - it.koff / 32));
-        d.vbs = make_vsharp(p.bs + n0 * p.ldbs + it.koff / 32, (uint32_t)(it.ncols * p.ldbs - it.koff / 32));
+        // based at the 16-byte group holding the segment's first scale bytes (the deep pipeline's
+        // groups are the layout's own)
+        const int64_t s0 = kDeep ? it.koff / 32 - 4 * it.gs : it.koff / 32;
+        d.vas = make_vsharp(p.as + m0w * p.ldas + s0, (uint32_t)(it.mrows * p.ldas - s0));
+        d.vbs = make_vsharp(p.bs + n0 * p.ldbs + s0, (uint32_t)(it.ncols * p.ldbs - s0));
       } else {
         d.vas = make_vsharp(p.as + (int64_t)it.row0 * p.ldas, (uint32_t)(it.mrows * p.ldas));
         d.vbs = make_vsharp(p.bs + (int64_t)it.e * p.bs_stride + n0 * p.ldbs, (uint32_t)(it.ncols * p.ldbs));
@@ -272,20 +279,14 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   const uint32_t a_step = kAMN ? (uint32_t)(64 * p.lda) : (uint32_t)kRowBytes;
   const uint32_t b_step = kBMN ? (uint32_t)(64 * p.ldb) : (uint32_t)kRowBytes;
   uint32_t as_vo = 0, bs_vo = 0;
-  uint32_t as4[4] = {0, 0, 0, 0}, bs4[4] = {0, 0, 0, 0};   // deep: scale group offsets
+  uint32_t as4[1] = {0}, bs4[1] = {0};   // deep: scale group offsets
   if constexpr (kMx) {
     const int r = wave * 64 + lane;
     as_vo = (uint32_t)(r * p.ldas);
     bs_vo = (uint32_t)(r * p.ldbs);
-    // group loads: row r's 16 bytes at r * 16 of the buffer; in the four-lane form load j of wave w
-    // covers rows 64 w + 16 j + L / 4, lane L's word landing at slot L of a 256-byte block
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r4 = kSc4 ? wave * 64 + j * 16 + (lane >> 2) : r;
-      const uint32_t w4 = kSc4 ? (uint32_t)(lane & 3) * 4u : 0u;
-      as4[j] = (uint32_t)(r4 * p.ldas) + w4;
-      bs4[j] = (uint32_t)(r4 * p.ldbs) + w4;
-    }
+    // group loads: row r's 16 bytes at r * 16 of the buffer
+    as4[0] = (uint32_t)(r * p.ldas);
+    bs4[0] = (uint32_t)(r * p.ldbs);
   }
   const i32x4 zdesc = make_vsharp(p.a, 0);   // zero range: loads read no memory and deliver zeros
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(smem) + (uint32_t)(wave * 8) * 1024u);
@@ -330,16 +331,8 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   auto dma_sg = [&](const Desc& d, bool on, int sb, int g) {
     if constexpr (kDeep) {
       const uint32_t ss = lds_sc + (uint32_t)sb * (uint32_t)kScBuf;
-      if constexpr (!kSc4) {
-        dma16(on ? d.vas : zdesc, ss, as4[0], (uint32_t)g * 16u);
-        dma16(on ? d.vbs : zdesc, ss + 4096u, bs4[0], (uint32_t)g * 16u);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dma4(on ? d.vas : zdesc, ss + (uint32_t)j * 256u, as4[j], (uint32_t)g * 16u);
-          dma4(on ? d.vbs : zdesc, ss + 4096u + (uint32_t)j * 256u, bs4[j], (uint32_t)g * 16u);
-        }
-      }
+      dma16(on ? d.vas : zdesc, ss, as4[0], (uint32_t)g * 16u);
+      dma16(on ? d.vbs : zdesc, ss + 4096u, bs4[0], (uint32_t)g * 16u);
     }
   };
 
@@ -356,14 +349,14 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const bool on0 = cur.u0 < cur.kz, on1 = cur.u0 + 1 < cur.kz;
 #pragma unroll
       for (int q = 0; q < 8; ++q) { dma_a(dc, 0, cur.u0, q, on0); dma_b(dc, 0, cur.u0, q, on0); }
-      dma_sg(dc, true, 0, cur.u0 >> 2);
+      dma_sg(dc, true, 0, (cur.u0 + cur.gs) >> 2);
       wait_vmcnt<0>();
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < 8; ++q) { dma_a(dc, 1, cur.u0 + 1, q, on1); dma_b(dc, 1, cur.u0 + 1, q, on1); }
-      const bool ng = ((cur.u0 + 1) & 3) == 0;
+      const bool ng = ((cur.u0 + 1 + cur.gs) & 3) == 0;
       sbn = ng ? 1 : 0;
-      dma_sg(dc, ng, 1, (cur.u0 + 1) >> 2);
+      dma_sg(dc, ng, 1, (cur.u0 + 1 + cur.gs) >> 2);
     }
   }
   // diagnostic (p.tstat): shader-clock cycles of the main loops and of the epilogues of this wave
@@ -389,7 +382,8 @@ void bwd_gemm_kernel(const BwdKArgs p) {
       const int n = cur.kT;
       StepFrag<true> f0;
       read_first<true, false, false, false, 16>(f0, smem + par * kStageBytes,
-                                                smem + kScOff + sbc * kScBuf + (cur.u0 & 3) * 4, wm, wn, lane);
+                                                smem + kScOff + sbc * kScBuf + ((cur.u0 + cur.gs) & 3) * 4, wm, wn,
+                                                lane);
 #pragma unroll 1
       for (int s = 0; s < n; ++s) {
         const int kt = cur.u0 + s, b = (par + s) & 1, bn = b ^ 1;
@@ -397,17 +391,19 @@ void bwd_gemm_kernel(const BwdKArgs p) {
         const bool in2 = s + 2 < n;
         const Desc& dt = in2 ? dc : dn;
         const int k2 = in2 ? kt + 2 : nxt.u0 + (s + 2 - n);
-        const bool ng = (!in2 && s + 2 == n) || (k2 & 3) == 0;
+        // stage positions within the 16-byte scale groups (shifted by each item's gs)
+        const int gt = kt + cur.gs, gn = kn + (s + 1 < n ? cur.gs : nxt.gs), g2 = k2 + (in2 ? cur.gs : nxt.gs);
+        const bool ng = (!in2 && s + 2 == n) || (g2 & 3) == 0;
         const int sbd = ng ? (sbn ^ 1) : sbn;
         const bool on = !kWg || k2 < (in2 ? cur.kz : nxt.kz);   // the stage holds data (wgrad)
         auto sync = [&]() {
           wait_vmcnt<0>();
           __syncthreads();
         };
-        mma_stage_mx_deep<false>(core, f0, smem + b * kStageBytes, smem + kScOff + sbc * kScBuf + (kt & 3) * 4,
-                                 smem + bn * kStageBytes, smem + kScOff + sbn * kScBuf + (kn & 3) * 4, wm, wn, lane,
+        mma_stage_mx_deep<false>(core, f0, smem + b * kStageBytes, smem + kScOff + sbc * kScBuf + (gt & 3) * 4,
+                                 smem + bn * kStageBytes, smem + kScOff + sbn * kScBuf + (gn & 3) * 4, wm, wn, lane,
                                  [&](int q) { dma_a(dt, b, k2, q, on); }, [&](int q) { dma_b(dt, b, k2, q, on); },
-                                 [&]() { dma_sg(dt, ng, sbn ^ 1, k2 >> 2); }, sync);
+                                 [&]() { dma_sg(dt, ng, sbn ^ 1, g2 >> 2); }, sync);
         sbc = sbn;
         sbn = sbd;
       }
