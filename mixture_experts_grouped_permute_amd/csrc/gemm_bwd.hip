@@ -119,6 +119,25 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   const int wm = wave >> 1, wn = wave & 1;
   const int E = p.E;
   build_sched(sched, p.split_sizes, E, p.nN, kWg ? (kMx ? p.pad : 1) : 0);
+  // wgrad: every expert has the same nM x nN tiles, of K = its token count.  The tile space takes
+  // the experts in decreasing K (ties by index), and a round's 256 consecutive tiles are dealt to
+  // the workgroups forwards in even rounds and backwards in odd ones, so that a workgroup's long
+  // tiles of one round meet short ones of the next -- with skewed routing, a plain deal leaves
+  // some workgroups a sum of K well above the mean (64-expert FC2 wgrad: slowest wave 1.3-1.4x
+  // the mean).  Each round's tiles still go to the XCDs 32 consecutive ones at a time.
+  __shared__ int16_t worder[kWg ? kMaxExperts : 1];
+  if constexpr (kWg) {
+    if (tid < E) {
+      const int c = sched.cnt[tid];
+      int rank = 0;
+      for (int e2 = 0; e2 < E; ++e2) {
+        const int c2 = sched.cnt[e2];
+        rank += (c2 > c || (c2 == c && e2 < tid)) ? 1 : 0;
+      }
+      worder[rank] = (int16_t)tid;
+    }
+    __syncthreads();
+  }
   const int total = kWg ? E * p.nM * p.nN : __builtin_amdgcn_readfirstlane(sched.tile[E]);
   const int G = gridDim.x, per = G >> 3, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   constexpr int kKStep = kMx ? 128 : 64;                  // K values per LDS stage
@@ -133,7 +152,8 @@ void bwd_gemm_kernel(const BwdKArgs p) {
   const int hi = p.split == 0 ? total : (p.split == 1 ? full : (S > 1 ? full + (total - full) * S : full));
 
   auto decode = [&](int round, BwdItem& it) {
-    it.t = lo + round * G + xcd * per + slot;
+    const int pos = xcd * per + slot;
+    it.t = lo + round * G + ((kWg && (round & 1)) ? G - 1 - pos : pos);
     it.kT = 0;
     it.kz = 0;
     it.u0 = 0;
@@ -142,8 +162,9 @@ void bwd_gemm_kernel(const BwdKArgs p) {
     if (it.t >= hi) return;
     if constexpr (kWg) {
       const int pe = p.nM * p.nN;
-      it.e = it.t / pe;
-      const int local = it.t - it.e * pe;
+      const int rank = it.t / pe;
+      it.e = __builtin_amdgcn_readfirstlane((int)worder[rank]);
+      const int local = it.t - rank * pe;
       // groups of 4 M-tiles when an expert's dW has few of them (FC2's H / 256 = 16): measured
       // 10 % faster for that wgrad than groups of 8, the same for FC1's 2I / 256 = 112
       tile_coords(local, p.nM, p.nN, it.mt, it.nt, p.nM <= 16 ? 4 : kGroupM);
