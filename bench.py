@@ -527,6 +527,9 @@ def main():
     ap.add_argument("--lib-gemm-probe", action="store_true",
                     help="only time torch.matmul on the gate-up projection's shape as one dense bf16 GEMM "
                          "(M = T*k = 8192, K = 4096, N = 2*14336), a reference for the MFMA counters")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only run the library's MFMA issue-rate probe (moe_mfma_probe): cycles per MFMA of "
+                         "the bf16 and the E4M3 MFMA-scale instruction on all 1024 SIMDs, and the clock")
     args = ap.parse_args()
     global TILE_STATS
     TILE_STATS = not args.no_tile_stats
@@ -550,6 +553,11 @@ def main():
         flops = 2.0 * 8192 * 4096 * 28672
         print(json.dumps({"lib_gemm_probe": "torch.matmul bf16 8192x4096 @ 4096x28672", "median_ms": med,
                           "tflops": round(flops / (med * 1e-3) / 1e12, 1)}), flush=True)
+        return
+    if args.mfma_probe:
+        import mixture_experts_grouped_permute_amd as m
+        for kind in (2, 0, 1):
+            print(json.dumps({"mfma_probe": m.mfma_probe(kind)}), flush=True)
         return
     if args.copy_probe:
         import torch

@@ -499,6 +499,23 @@ int moe_read_device_error(void* workspace, void* stream);
 size_t moe_tile_stats_bytes(void);
 moe_status moe_set_tile_stats(uint32_t* device_buf, size_t bytes);
 
+/* ------------------------------------------------------------------------
+ * Diagnostic, not for production: the matrix-core issue-rate ceiling that the
+ * grouped GEMMs' main loops are measured against.  moe_mfma_probe launches
+ * moe_probe_workgroups() (256) workgroups of 4 waves on `stream`; every wave
+ * issues `iters` rounds of 16 MFMAs into 16 independent 32 x 32 fp32
+ * accumulators (the GEMM tiles' instruction and accumulator count), operands
+ * in registers, no memory traffic.  kind: 0 MFMA-scale 32x32x64 E4M3 with
+ * per-lane E8M0 scale registers, 1 the same with constant scales, 2 MFMA
+ * 32x32x16 bf16.  cycles (device, 1024 uint64 = workgroups x 4 waves) receives
+ * each wave's shader-clock cycles (s_memtime) of its MFMA loop; sink (device,
+ * 256 x 256 floats) receives the accumulator sums, so that nothing is folded
+ * away.  Both buffers belong to the caller.  Asynchronous: time it with events
+ * on `stream`.  MOE_ERR_INVALID_ARG for kind outside [0, 2], iters outside
+ * [1, 2^20] or a NULL buffer; MOE_ERR_HIP if the launch fails. */
+int moe_probe_workgroups(void);
+moe_status moe_mfma_probe(int kind, int iters, float* sink, uint64_t* cycles, void* stream);
+
 /* Human-readable name of a status code. */
 const char* moe_status_string(int status);
 

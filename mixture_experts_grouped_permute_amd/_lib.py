@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
     "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop", "fp8_tensor_quantize_workspace",
     "fp8_tensor_quantize", "mxfp8_quantize_weights", "moe_permute_noalloc", "moe_tile_stats_bytes",
-    "moe_set_tile_stats",
+    "moe_set_tile_stats", "moe_probe_workgroups", "moe_mfma_probe",
 )
 NOALLOC_SCRATCH_BYTES = 4 << 20    # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -131,6 +131,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_bwd_phase_name.argtypes = [ctypes.c_int]
     lib.moe_read_device_error.restype = ctypes.c_int
     lib.moe_read_device_error.argtypes = [_vp, _vp]
+    lib.moe_probe_workgroups.restype = ctypes.c_int
+    lib.moe_mfma_probe.restype = ctypes.c_int
+    lib.moe_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]
     lib.moe_tile_stats_bytes.restype = ctypes.c_size_t
     lib.moe_tile_stats_bytes.argtypes = []
     lib.moe_set_tile_stats.restype = ctypes.c_int
@@ -693,6 +696,38 @@ def tile_stats_summary(buf: torch.Tensor) -> dict:
                      "max_wave_cycles": int((v[:, 0] + v[:, 1]).max()),
                      "mean_wave_cycles": round((v[:, 0] + v[:, 1]).mean())}
     return out
+
+
+MFMA_PROBE_KINDS = ("mfma_scale_32x32x64_e4m3", "mfma_scale_32x32x64_e4m3_const_scales", "mfma_32x32x16_bf16")
+
+
+def mfma_probe(kind: int, iters: int = 2000, device="cuda:0", reps: int = 3) -> dict:
+    """Diagnostic: back-to-back MFMA issue cost on every SIMD (moe_mfma_probe).  Returns the mean
+    and max shader-clock cycles per MFMA over the 1024 waves, the launch time (median of `reps`
+    event-timed launches after one warm-up), the clock that implies, and the dense rate."""
+    lib = load()
+    dev = torch.device(device)
+    G = lib.moe_probe_workgroups()
+    sink = torch.empty(G * 256, dtype=torch.float32, device=dev)
+    cyc = torch.zeros(G * 4, dtype=torch.int64, device=dev)
+    ms = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _check(lib.moe_mfma_probe(kind, iters, _ptr(sink), _ptr(cyc), _stream(dev)), "moe_mfma_probe")
+        e1.record()
+        torch.cuda.synchronize(dev)
+        if r:
+            ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    t = ms[len(ms) // 2]
+    c = cyc.cpu().double()
+    per = c / (16.0 * iters)
+    flop = (32 * 32 * 16 * 2) if kind == 2 else (32 * 32 * 64 * 2)
+    return {"kind": MFMA_PROBE_KINDS[kind], "iters": iters, "waves": G * 4,
+            "cycles_per_mfma_mean": round(float(per.mean()), 2), "cycles_per_mfma_max": round(float(per.max()), 2),
+            "launch_ms": round(t, 4), "clock_ghz": round(float(c.mean()) / (t * 1e6), 3),
+            "tflops": round(flop * 16.0 * iters * G * 4 / (t * 1e-3) / 1e12, 1)}
 
 
 def moe_read_device_error(flag: torch.Tensor) -> int:

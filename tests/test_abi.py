@@ -336,3 +336,18 @@ def test_tile_stats_diagnostic_on_host(lib):
     assert need == len(TILE_STAT_SLOTS) * 256 * 4 * 4 * 4
     assert lib.moe_set_tile_stats(0x1000, need - 4) == MOE_ERR_INVALID_ARG
     assert lib.moe_set_tile_stats(None, 0) == 0
+
+
+def test_mfma_probe_rejects_bad_arguments_on_host(lib):
+    """moe_mfma_probe: bad kind, iteration count or buffer is refused before any launch."""
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG
+    lib.moe_probe_workgroups.restype = ctypes.c_int
+    lib.moe_mfma_probe.restype = ctypes.c_int
+    lib.moe_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.moe_probe_workgroups() == 256
+    assert lib.moe_mfma_probe(3, 10, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(-1, 10, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(0, 0, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(0, (1 << 20) + 1, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(2, 10, None, 0x1000, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(2, 10, 0x1000, None, None) == MOE_ERR_INVALID_ARG
