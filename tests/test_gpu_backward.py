@@ -30,6 +30,11 @@ CASES = [
     # FC1 dgrad K = 4608 (36 stages) split in 2 parts: the second part starts at stage 18, inside
     # a scale group
     ("deep-mx-split-odd", cfg_small(T=640, H=1024, I=2304, E=3, k=2), None),
+    # several rounds of tiles in every GEMM under skewed routing with an empty expert: the weight
+    # gradients' largest-expert-first, snake-dealt rounds (4 and 2 rounds), FC1 in 2 rounds, and
+    # token segments starting at every 128-row offset modulo 512 (the MXFP8 scale-group shift)
+    ("multiround-skew", cfg_small(T=1024, H=1024, I=2048, E=16, k=2),
+     [600, 0, 300, 250, 200, 150, 120, 100, 80, 70, 60, 50, 30, 20, 10, 8]),
 ]
 
 

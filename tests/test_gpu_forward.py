@@ -31,6 +31,11 @@ CASES = [
     ("mixed-depth", cfg_small(T=300, H=64, I=128, E=4, k=2), None),
     # MXFP8 FC1 with K = 384: three stages but 12-byte scale rows (scale words read per lane)
     ("mx-row-scales", cfg_small(T=300, H=384, I=256, E=4, k=2), None),
+    # several rounds of tiles in every GEMM under skewed routing with an empty expert: the weight
+    # gradients' largest-expert-first, snake-dealt rounds (4 and 2 rounds), FC1 in 2 rounds, and
+    # token segments starting at every 128-row offset modulo 512 (the MXFP8 scale-group shift)
+    ("multiround-skew", cfg_small(T=1024, H=1024, I=2048, E=16, k=2),
+     [600, 0, 300, 250, 200, 150, 120, 100, 80, 70, 60, 50, 30, 20, 10, 8]),
 ]
 
 
