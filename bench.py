@@ -290,7 +290,9 @@ def fwd_leg(cfg, steps, warmup, cold_steps=5, copy_ceiling=None):
             ent.update({"cold_median_ms": cold, "cold_GBs": round(v / (cold * 1e-3) / 1e9, 1),
                         "frac_of_8TBs_cold": round(v / (cold * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)})
         if copy_ceiling:
-            ent["frac_of_copy_warm"] = round(ent["warm_GBs"] / copy_ceiling, 3)
+            ent["frac_of_copy_warm"] = round(ent["warm_GBs"] / copy_ceiling[0], 3)
+            if copy_ceiling[1]:
+                ent["frac_of_copy64_warm"] = round(ent["warm_GBs"] / copy_ceiling[1], 3)
         memory[k_] = ent
     out = {
         "value": round(cfg.T / (ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms, 4),
@@ -311,12 +313,13 @@ def fwd_leg(cfg, steps, warmup, cold_steps=5, copy_ceiling=None):
 
 def copy_leg(reps=10):
     """The practical HBM ceiling on this GPU: device-to-device copies (read + write), a read-only
-    pass and a write-only fill of 512 MiB and 2 GiB, warm (back to back) and cold (a 1 GiB flush
-    before each), HIP-event timed, median over reps.  GB/s count every byte read and written."""
+    pass and a write-only fill of 64 MiB, 512 MiB and 2 GiB (64 MiB: a copy moving about as many
+    bytes as one permute or combine launch), warm (back to back) and cold (a 1 GiB flush before
+    each), HIP-event timed, median over reps.  GB/s count every byte read and written."""
     import torch
     fl = _flusher()
     res = {}
-    for mib in (512, 2048):
+    for mib in (64, 512, 2048):
         n = mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda:0")
         b = torch.empty_like(a)
@@ -579,7 +582,7 @@ def main():
     if "copy" in legs:
         _log("timing the copy ceiling")
         copy = copy_leg()
-    ceiling = copy["copy_2048MiB_warm_GBs"] if copy else None
+    ceiling = (copy["copy_2048MiB_warm_GBs"], copy["copy_64MiB_warm_GBs"]) if copy else None
     cfg = get_config(2)
     r, leg = fwd_leg(cfg, args.steps, args.warmup, copy_ceiling=ceiling)
     ms = leg["ms_per_step"]
