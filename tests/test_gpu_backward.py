@@ -35,6 +35,10 @@ CASES = [
     # token segments starting at every 128-row offset modulo 512 (the MXFP8 scale-group shift)
     ("multiround-skew", cfg_small(T=1024, H=1024, I=2048, E=16, k=2),
      [600, 0, 300, 250, 200, 150, 120, 100, 80, 70, 60, 50, 30, 20, 10, 8]),
+    # one token routed to every expert (k = E): every expert holds a single row
+    ("one-token-all-experts", cfg_small(T=1, H=128, I=128, E=8, k=8), None),
+    # the largest expert count with few tokens: 256 experts of a few rows each, 25 of them empty
+    ("e256-sparse", cfg_small(T=64, H=128, I=256, E=256, k=8), None),
 ]
 
 
