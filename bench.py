@@ -559,7 +559,7 @@ def main():
         return
     if args.mfma_probe:
         import mixture_experts_grouped_permute_amd as m
-        for kind in (2, 0, 1):
+        for kind in (2, 3, 0, 4, 1):
             print(json.dumps({"mfma_probe": m.mfma_probe(kind)}), flush=True)
         return
     if args.copy_probe:

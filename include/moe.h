@@ -507,11 +507,14 @@ moe_status moe_set_tile_stats(uint32_t* device_buf, size_t bytes);
  * accumulators (the GEMM tiles' instruction and accumulator count), operands
  * in registers, no memory traffic.  kind: 0 MFMA-scale 32x32x64 E4M3 with
  * per-lane E8M0 scale registers, 1 the same with constant scales, 2 MFMA
- * 32x32x16 bf16.  cycles (device, 1024 uint64 = workgroups x 4 waves) receives
+ * 32x32x16 bf16 -- one operand pair, few distinct values; 3 (bf16) and 4
+ * (E4M3, scale registers) cycle through 4 A and 4 B fragments of
+ * pseudo-random values as a GEMM tile does, so that the operands change with
+ * every MFMA.  cycles (device, 1024 uint64 = workgroups x 4 waves) receives
  * each wave's shader-clock cycles (s_memtime) of its MFMA loop; sink (device,
  * 256 x 256 floats) receives the accumulator sums, so that nothing is folded
  * away.  Both buffers belong to the caller.  Asynchronous: time it with events
- * on `stream`.  MOE_ERR_INVALID_ARG for kind outside [0, 2], iters outside
+ * on `stream`.  MOE_ERR_INVALID_ARG for kind outside [0, 4], iters outside
  * [1, 2^20] or a NULL buffer; MOE_ERR_HIP if the launch fails. */
 int moe_probe_workgroups(void);
 moe_status moe_mfma_probe(int kind, int iters, float* sink, uint64_t* cycles, void* stream);

@@ -698,7 +698,8 @@ def tile_stats_summary(buf: torch.Tensor) -> dict:
     return out
 
 
-MFMA_PROBE_KINDS = ("mfma_scale_32x32x64_e4m3", "mfma_scale_32x32x64_e4m3_const_scales", "mfma_32x32x16_bf16")
+MFMA_PROBE_KINDS = ("mfma_scale_32x32x64_e4m3", "mfma_scale_32x32x64_e4m3_const_scales", "mfma_32x32x16_bf16",
+                    "mfma_32x32x16_bf16_random_4x4_fragments", "mfma_scale_32x32x64_e4m3_random_4x4_fragments")
 
 
 def mfma_probe(kind: int, iters: int = 2000, device="cuda:0", reps: int = 3) -> dict:
@@ -723,7 +724,7 @@ def mfma_probe(kind: int, iters: int = 2000, device="cuda:0", reps: int = 3) -> 
     t = ms[len(ms) // 2]
     c = cyc.cpu().double()
     per = c / (16.0 * iters)
-    flop = (32 * 32 * 16 * 2) if kind == 2 else (32 * 32 * 64 * 2)
+    flop = (32 * 32 * 16 * 2) if kind in (2, 3) else (32 * 32 * 64 * 2)
     return {"kind": MFMA_PROBE_KINDS[kind], "iters": iters, "waves": G * 4,
             "cycles_per_mfma_mean": round(float(per.mean()), 2), "cycles_per_mfma_max": round(float(per.max()), 2),
             "launch_ms": round(t, 4), "clock_ghz": round(float(c.mean()) / (t * 1e6), 3),

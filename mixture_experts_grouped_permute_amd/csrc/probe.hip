@@ -18,8 +18,24 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8p __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8p __attribute__((ext_vector_type(8)));
 
+// Pseudo-random operand bits: Knuth's multiplicative hash of the counter (2^32 / golden ratio),
+// then two of Marsaglia's xorshift32 steps (shifts 13, 17, 5).
+__device__ __forceinline__ uint32_t probe_hash(uint32_t x) {
+  x *= 0x9E3779B9u;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    x ^= x << 13;
+    x ^= x >> 17;
+    x ^= x << 5;
+  }
+  return x;
+}
+
 // kKind: 0 MFMA-scale 32x32x64 E4M3 with per-lane E8M0 scale registers (the MXFP8 GEMMs), 1 the
-// same with constant scales, 2 MFMA 32x32x16 bf16 (the BF16 GEMMs)
+// same with constant scales, 2 MFMA 32x32x16 bf16 (the BF16 GEMMs) -- one operand pair for all
+// 16 MFMAs, a few distinct values; 3 (bf16) and 4 (E4M3 with scale registers): the GEMM tiles'
+// pattern, 4 A and 4 B fragments of pseudo-random values, MFMA q of a round multiplying A q / 4 by
+// B q % 4, so that the operands change from one MFMA to the next as in the GEMMs
 template <int kKind>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mfma_probe_kernel(float* sink, uint64_t* cycles, int iters) {
@@ -42,6 +58,32 @@ void mfma_probe_kernel(float* sink, uint64_t* cycles, int iters) {
   int sa = 127, sb = 127 + (tid & 1);
   // opaque to the compiler, so the loop cannot be folded
   asm volatile("" : "+v"(a), "+v"(b), "+v"(sa), "+v"(sb), "+v"(ab), "+v"(bb));
+  // kinds 3 and 4: pseudo-random fragments; bf16 values of either sign with exponents 2^-7 .. 2^7
+  // and random mantissas, E4M3 bytes of either sign with exponent fields 0 .. 14 (no NaN code)
+  bf16x8p fa[4], fb[4];
+  i32x8p ga[4], gb[4];
+  int gsa[4], gsb[4];
+  if constexpr (kKind >= 3) {
+    const uint32_t seed = (uint32_t)(blockIdx.x * 256 + tid) * 64u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint32_t ha = probe_hash(seed + (uint32_t)(i * 16 + r)), hb = probe_hash(seed + (uint32_t)(i * 16 + 8 + r));
+        if constexpr (kKind == 3) {
+          fa[i][r] = __builtin_bit_cast(__bf16, (uint16_t)((ha & 0x807Fu) | ((120u + (ha >> 16) % 15u) << 7)));
+          fb[i][r] = __builtin_bit_cast(__bf16, (uint16_t)((hb & 0x807Fu) | ((120u + (hb >> 16) % 15u) << 7)));
+        } else {
+          ga[i][r] = (int)(ha & 0xF7F7F7F7u);
+          gb[i][r] = (int)(hb & 0xF7F7F7F7u);
+        }
+      }
+      gsa[i] = 120 + (int)(probe_hash(seed + 100u + (uint32_t)i) & 7u);
+      gsb[i] = 120 + (int)(probe_hash(seed + 200u + (uint32_t)i) & 7u);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(fa[i]), "+v"(fb[i]), "+v"(ga[i]), "+v"(gb[i]), "+v"(gsa[i]), "+v"(gsb[i]));
+  }
   const uint64_t t0 = __builtin_amdgcn_s_memtime();
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
@@ -50,8 +92,13 @@ void mfma_probe_kernel(float* sink, uint64_t* cycles, int iters) {
         acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[q], 0, 0, 0, sa, 0, sb);
       else if constexpr (kKind == 1)
         acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[q], 0, 0, 0, 127, 0, 127);
-      else
+      else if constexpr (kKind == 2)
         acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, bb, acc[q], 0, 0, 0);
+      else if constexpr (kKind == 3)
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[q & 3], fa[q >> 2], acc[q], 0, 0, 0);
+      else
+        acc[q] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[q & 3], ga[q >> 2], acc[q], 0, 0, 0, gsb[q & 3], 0,
+                                                                 gsa[q >> 2]);
     }
   }
   const uint64_t t1 = __builtin_amdgcn_s_memtime();
@@ -71,12 +118,14 @@ extern "C" {
 int moe_probe_workgroups(void) { return 256; }
 
 moe_status moe_mfma_probe(int kind, int iters, float* sink, uint64_t* cycles, void* stream) {
-  if (kind < 0 || kind > 2 || iters <= 0 || iters > (1 << 20) || !sink || !cycles) return MOE_ERR_INVALID_ARG;
+  if (kind < 0 || kind > 4 || iters <= 0 || iters > (1 << 20) || !sink || !cycles) return MOE_ERR_INVALID_ARG;
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   const dim3 grid(256), block(256);
   if (kind == 0) hipLaunchKernelGGL(mfma_probe_kernel<0>, grid, block, 0, st, sink, cycles, iters);
   else if (kind == 1) hipLaunchKernelGGL(mfma_probe_kernel<1>, grid, block, 0, st, sink, cycles, iters);
-  else hipLaunchKernelGGL(mfma_probe_kernel<2>, grid, block, 0, st, sink, cycles, iters);
+  else if (kind == 2) hipLaunchKernelGGL(mfma_probe_kernel<2>, grid, block, 0, st, sink, cycles, iters);
+  else if (kind == 3) hipLaunchKernelGGL(mfma_probe_kernel<3>, grid, block, 0, st, sink, cycles, iters);
+  else hipLaunchKernelGGL(mfma_probe_kernel<4>, grid, block, 0, st, sink, cycles, iters);
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

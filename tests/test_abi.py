@@ -345,7 +345,7 @@ def test_mfma_probe_rejects_bad_arguments_on_host(lib):
     lib.moe_mfma_probe.restype = ctypes.c_int
     lib.moe_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     assert lib.moe_probe_workgroups() == 256
-    assert lib.moe_mfma_probe(3, 10, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_mfma_probe(5, 10, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_probe(-1, 10, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_probe(0, 0, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_probe(0, (1 << 20) + 1, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG

@@ -9,7 +9,7 @@ import mixture_experts_grouped_permute_amd as m
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("kind,cycles", [(2, 32.0), (0, 64.0), (1, 64.0)])
+@pytest.mark.parametrize("kind,cycles", [(2, 32.0), (3, 32.0), (0, 64.0), (1, 64.0), (4, 64.0)])
 def test_mfma_probe_issue_cost(kind, cycles):
     r = m.mfma_probe(kind, iters=200, reps=1)
     assert r["waves"] == 1024
