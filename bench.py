@@ -522,9 +522,10 @@ def main():
     ap.add_argument("--no-tile-stats", action="store_true",
                     help="skip the untimed call with the GEMM cycle counters on (keeps profiler pass counts)")
     ap.add_argument("--cpu-tokens", type=int, default=4096)
-    ap.add_argument("--legs", default="copy,bf16,mxfp8,mxfp8_finegrained,fp8,backward,backward_mxfp8,router,loop",
+    ap.add_argument("--legs", default="copy,bf16,mxfp8,mxfp8_finegrained,fp8,backward,backward_mxfp8,router,loop,"
+                                      "mfma_probe",
                     help="comma list of copy, bf16, mxfp8, mxfp8_finegrained, fp8, backward, backward_mxfp8, router, "
-                         "loop (bf16 always runs)")
+                         "loop, mfma_probe (bf16 always runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES, 5 times (counter calibration)")
     ap.add_argument("--lib-gemm-probe", action="store_true",
@@ -660,7 +661,25 @@ def main():
                      per_call_wt=True)
         line["backward_mxfp8"]["per_call_weights"] = {
             k_: rc[k_] for k_ in ("ms_per_step", "value", "phase_ms", "forward_with_save_ms", "train_step_ms")}
+    if "mfma_probe" in legs:
+        # after every timed region: the matrix cores' own rate with GEMM-like random operands, beside
+        # the published peak of each roofline (bf16 for peak 2500, E4M3 otherwise)
+        annotate_rooflines(line)
     print(json.dumps(line), flush=True)
+
+
+def annotate_rooflines(line):
+    """Add the library MFMA probe's random-operand ceiling (kinds 3 and 4: 4 A x 4 B pseudo-random
+    fragments, no memory traffic) to every roofline object of the line, with achieved / ceiling."""
+    import mixture_experts_grouped_permute_amd as m
+    ceil = {2500.0: m.mfma_probe(3, iters=1000)["tflops"], 5000.0: m.mfma_probe(4, iters=1000)["tflops"]}
+    objs = [line.get("roofline")] + [v.get("roofline") for v in line.values() if isinstance(v, dict)]
+    for rf in objs:
+        if not rf or rf.get("unit") != "TFLOP/s" or rf.get("peak") not in ceil:
+            continue
+        c = ceil[rf["peak"]]
+        rf["mfma_probe_ceiling"] = c
+        rf["frac_of_mfma_probe"] = round(rf["achieved"] / c, 4)
 
 
 if __name__ == "__main__":
