@@ -534,6 +534,8 @@ def main():
     ap.add_argument("--mfma-probe", action="store_true",
                     help="only run the library's MFMA issue-rate probe (moe_mfma_probe): cycles per MFMA of "
                          "the bf16 and the E4M3 MFMA-scale instruction on all 1024 SIMDs, and the clock")
+    ap.add_argument("--load-probe", action="store_true",
+                    help="only run the library's LDS fill-rate probe (moe_load_probe) on its four access patterns")
     args = ap.parse_args()
     global TILE_STATS
     TILE_STATS = not args.no_tile_stats
@@ -557,6 +559,13 @@ def main():
         flops = 2.0 * 8192 * 4096 * 28672
         print(json.dumps({"lib_gemm_probe": "torch.matmul bf16 8192x4096 @ 4096x28672", "median_ms": med,
                           "tflops": round(flops / (med * 1e-3) / 1e12, 1)}), flush=True)
+        return
+    if args.load_probe:
+        import torch
+        import mixture_experts_grouped_permute_amd as m
+        buf = torch.zeros(m.load().moe_load_probe_bytes(), dtype=torch.uint8, device="cuda:0")
+        for pat in range(4):
+            print(json.dumps({"load_probe": m.load_probe(pat, buf=buf)}), flush=True)
         return
     if args.mfma_probe:
         import mixture_experts_grouped_permute_amd as m

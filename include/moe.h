@@ -519,6 +519,24 @@ moe_status moe_set_tile_stats(uint32_t* device_buf, size_t bytes);
 int moe_probe_workgroups(void);
 moe_status moe_mfma_probe(int kind, int iters, float* sink, uint64_t* cycles, void* stream);
 
+/* Diagnostic, not for production: the rate at which the GEMMs' direct-to-LDS
+ * loads fill LDS.  moe_load_probe launches 256 workgroups (one per CU) on
+ * `stream`; each loads 64 KB per stage into LDS (16-byte lanes, the GEMMs'
+ * load instruction), two stages in flight, a barrier per stage, for `stages`
+ * stages, from the region of its XCD (workgroup b on XCD b % 8) in `buf`.
+ * pattern: 0 every workgroup its own 64 KB chunks of a 2 MB region (L2
+ * resident); 1 the same over 64 MB (streamed from HBM); 2 eight workgroups
+ * per XCD sharing each chunk at the same stage (64 MB); 3 that sharing with
+ * the GEMM operands' access, 512 rows of 4 KB of which each stage reads one
+ * 128-byte slice per row.  buf (device, caller-owned, at least
+ * moe_load_probe_bytes() = 512 MiB; its contents are never used) is only
+ * read; cycles (device, 256 uint64) receives each workgroup's shader-clock
+ * cycles.  MOE_ERR_INVALID_ARG for a pattern outside [0, 3], stages outside
+ * [1, 65536], a NULL pointer or a short buffer; MOE_ERR_HIP if the launch
+ * fails. */
+size_t moe_load_probe_bytes(void);
+moe_status moe_load_probe(int pattern, int stages, const void* buf, size_t bytes, uint64_t* cycles, void* stream);
+
 /* Human-readable name of a status code. */
 const char* moe_status_string(int status);
 

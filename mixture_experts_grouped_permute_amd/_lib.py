@@ -29,7 +29,7 @@ EXPORTS = (
     "moe_fwd_phase_name", "moe_grouped_mlp_bwd_ex", "moe_bwd_phase_count", "moe_bwd_phase_name",
     "moe_route_topk", "moe_route_permute", "moe_grouped_mlp_fwd_loop", "fp8_tensor_quantize_workspace",
     "fp8_tensor_quantize", "mxfp8_quantize_weights", "moe_permute_noalloc", "moe_tile_stats_bytes",
-    "moe_set_tile_stats", "moe_probe_workgroups", "moe_mfma_probe",
+    "moe_set_tile_stats", "moe_probe_workgroups", "moe_mfma_probe", "moe_load_probe_bytes", "moe_load_probe",
 )
 NOALLOC_SCRATCH_BYTES = 4 << 20    # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -134,6 +134,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
     lib.moe_probe_workgroups.restype = ctypes.c_int
     lib.moe_mfma_probe.restype = ctypes.c_int
     lib.moe_mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, _vp, _vp, _vp]
+    lib.moe_load_probe_bytes.restype = ctypes.c_size_t
+    lib.moe_load_probe.restype = ctypes.c_int
+    lib.moe_load_probe.argtypes = [ctypes.c_int, ctypes.c_int, _vp, ctypes.c_size_t, _vp, _vp]
     lib.moe_tile_stats_bytes.restype = ctypes.c_size_t
     lib.moe_tile_stats_bytes.argtypes = []
     lib.moe_set_tile_stats.restype = ctypes.c_int
@@ -729,6 +732,39 @@ def mfma_probe(kind: int, iters: int = 2000, device="cuda:0", reps: int = 3) -> 
             "cycles_per_mfma_mean": round(float(per.mean()), 2), "cycles_per_mfma_max": round(float(per.max()), 2),
             "launch_ms": round(t, 4), "clock_ghz": round(float(c.mean()) / (t * 1e6), 3),
             "tflops": round(flop * 16.0 * iters * G * 4 / (t * 1e-3) / 1e12, 1)}
+
+
+LOAD_PROBE_PATTERNS = ("own_chunks_l2_resident", "own_chunks_streamed", "8_sharers_lockstep_streamed",
+                       "8_sharers_gemm_rows_streamed")
+
+
+def load_probe(pattern: int, stages: int = 512, device="cuda:0", reps: int = 3, buf: Optional[torch.Tensor] = None) -> dict:
+    """Diagnostic: the LDS fill rate of the GEMMs' direct-to-LDS loads (moe_load_probe).  Returns the
+    launch time (median of `reps` event-timed launches after one warm-up), the bytes per cycle and
+    per CU (mean over the 256 workgroups' shader-clock cycles), and the aggregate rate into LDS."""
+    lib = load()
+    dev = torch.device(device)
+    need = lib.moe_load_probe_bytes()
+    if buf is None:
+        buf = torch.zeros(need, dtype=torch.uint8, device=dev)
+    if buf.numel() < need or not buf.is_cuda:
+        raise TypeError(f"load probe buffer must be a device tensor of at least {need} bytes")
+    cyc = torch.zeros(256, dtype=torch.int64, device=dev)
+    ms = []
+    for r in range(reps + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        _check(lib.moe_load_probe(pattern, stages, _ptr(buf), buf.numel(), _ptr(cyc), _stream(dev)), "moe_load_probe")
+        e1.record()
+        torch.cuda.synchronize(dev)
+        if r:
+            ms.append(e0.elapsed_time(e1))
+    ms.sort()
+    t = ms[len(ms) // 2]
+    c = float(cyc.cpu().double().mean())
+    return {"pattern": LOAD_PROBE_PATTERNS[pattern], "stages": stages, "launch_ms": round(t, 4),
+            "bytes_per_cycle_per_cu": round(65536.0 * stages / c, 1), "cycles_per_64KB_stage": round(c / stages),
+            "TBs_into_lds": round(256 * 65536.0 * stages / (t * 1e-3) / 1e12, 2)}
 
 
 def moe_read_device_error(flag: torch.Tensor) -> int:

@@ -111,9 +111,83 @@ void mfma_probe_kernel(float* sink, uint64_t* cycles, int iters) {
   if ((tid & 63) == 0) cycles[blockIdx.x * 4 + (tid >> 6)] = t1 - t0;
 }
 
+// LDS fill-rate probe: each of 256 workgroups (one per CU) loads 64 KB per stage straight into
+// LDS with the GEMMs' direct-to-LDS loads (16 bytes per lane, 1 KB per wave and instruction, 16
+// instructions per wave and stage), two stages in flight, a barrier per stage, nothing else.  XCD
+// x (workgroup b: x = b % 8, slot j = b / 8) reads the region [x * region, (x + 1) * region) of the
+// buffer; stage s of slot j, with sharer group g = j % 4 and sharer m = j / 4, reads
+//   pattern 0, 1: the 64 KB chunk (s + 7 j) mod (region / 64 KB) -- every workgroup its own data
+//     (pattern 0 on a 2 MB region that stays in L2, pattern 1 on 64 MB that streams from HBM);
+//   pattern 2: chunk (4 s + g) mod ... -- 8 workgroups share each chunk in lockstep (64 MB);
+//   pattern 3: the GEMM operands' access with the same sharing: 512 rows of 4 KB, row block
+//     (4 (s / 32) + g) mod (region / 2 MB), 128-byte slice s mod 32 of each row (64 MB).
+__device__ __forceinline__ void probe_lds_load16(const int32_t (&vs)[4], uint32_t lds, uint32_t voff) {
+  const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(l), "v"(voff), "s"(*reinterpret_cast<const int32_t __attribute__((ext_vector_type(4)))*>(vs))
+               : "memory", "m0");
+}
+
+template <int kPattern>
+__global__ __launch_bounds__(256) void load_probe_kernel(const uint8_t* base, uint32_t region, int stages,
+                                                         uint64_t* cycles) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * 65536];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t xcd = blockIdx.x & 7u, slot = blockIdx.x >> 3;
+  const uint32_t g = slot & 3u;
+  const uint64_t a = reinterpret_cast<uint64_t>(base + (size_t)xcd * region);
+  int32_t vs[4];
+  vs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  vs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
+  vs[2] = __builtin_amdgcn_readfirstlane((int)region);
+  vs[3] = 0x00020000;
+  const uint32_t nchunk = region / 65536u, nblock = region / (512u * 4096u);
+  const uint32_t lbase = __builtin_amdgcn_readfirstlane((uint32_t)(size_t)(__attribute__((address_space(3))) void*)lds);
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int s = 0; s < stages; ++s) {
+    const uint32_t b = (uint32_t)s & 1u;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      uint32_t off;
+      if constexpr (kPattern == 3) {
+        const uint32_t rb = ((uint32_t)s / 32u * 4u + g) % nblock;
+        const uint32_t row = (uint32_t)wave * 128u + (uint32_t)q * 8u + (uint32_t)(lane >> 3);
+        off = rb * 512u * 4096u + row * 4096u + ((uint32_t)s % 32u) * 128u + (uint32_t)(lane & 7) * 16u;
+      } else {
+        const uint32_t chunk = kPattern == 2 ? ((uint32_t)s * 4u + g) % nchunk : ((uint32_t)s + slot * 7u) % nchunk;
+        off = chunk * 65536u + (uint32_t)wave * 16384u + (uint32_t)q * 1024u + (uint32_t)lane * 16u;
+      }
+      probe_lds_load16(vs, lbase + b * 65536u + (uint32_t)wave * 16384u + (uint32_t)q * 1024u, off);
+    }
+    __builtin_amdgcn_s_waitcnt((16 & 0xF) | ((16 >> 4) << 14) | (0x7 << 4) | (0xF << 8));   // vmcnt(16)
+    __syncthreads();
+  }
+  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));                                        // vmcnt(0)
+  __syncthreads();
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (tid == 0) cycles[blockIdx.x] = t1 - t0;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t moe_load_probe_bytes(void) { return (size_t)8 * 64 * 1048576; }
+
+moe_status moe_load_probe(int pattern, int stages, const void* buf, size_t bytes, uint64_t* cycles, void* stream) {
+  if (pattern < 0 || pattern > 3 || stages <= 0 || stages > (1 << 16) || !buf || !cycles ||
+      bytes < moe_load_probe_bytes())
+    return MOE_ERR_INVALID_ARG;
+  const uint32_t region = pattern == 0 ? 2u * 1048576u : 64u * 1048576u;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const uint8_t* b = static_cast<const uint8_t*>(buf);
+  if (pattern == 0) hipLaunchKernelGGL(load_probe_kernel<0>, dim3(256), dim3(256), 0, st, b, region, stages, cycles);
+  else if (pattern == 1) hipLaunchKernelGGL(load_probe_kernel<1>, dim3(256), dim3(256), 0, st, b, region, stages, cycles);
+  else if (pattern == 2) hipLaunchKernelGGL(load_probe_kernel<2>, dim3(256), dim3(256), 0, st, b, region, stages, cycles);
+  else hipLaunchKernelGGL(load_probe_kernel<3>, dim3(256), dim3(256), 0, st, b, region, stages, cycles);
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
 
 int moe_probe_workgroups(void) { return 256; }
 

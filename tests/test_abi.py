@@ -351,3 +351,23 @@ def test_mfma_probe_rejects_bad_arguments_on_host(lib):
     assert lib.moe_mfma_probe(0, (1 << 20) + 1, 0x1000, 0x1000, None) == MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_probe(2, 10, None, 0x1000, None) == MOE_ERR_INVALID_ARG
     assert lib.moe_mfma_probe(2, 10, 0x1000, None, None) == MOE_ERR_INVALID_ARG
+
+
+def test_load_probe_rejects_bad_arguments_on_host(lib):
+    """moe_load_probe: bad pattern, stage count, pointer or a short buffer is refused before any
+    launch."""
+    from mixture_experts_grouped_permute_amd._lib import MOE_ERR_INVALID_ARG
+    lib.moe_load_probe_bytes.restype = ctypes.c_size_t
+    lib.moe_load_probe.restype = ctypes.c_int
+    lib.moe_load_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    need = lib.moe_load_probe_bytes()
+    assert need == 512 << 20
+    p = 0x1000
+    assert lib.moe_load_probe(4, 16, p, need, p, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_load_probe(-1, 16, p, need, p, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_load_probe(0, 0, p, need, p, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_load_probe(0, (1 << 16) + 1, p, need, p, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_load_probe(0, 16, None, need, p, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_load_probe(0, 16, p, need - 1, p, None) == MOE_ERR_INVALID_ARG
+    assert lib.moe_load_probe(0, 16, p, need, None, None) == MOE_ERR_INVALID_ARG

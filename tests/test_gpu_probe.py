@@ -16,3 +16,13 @@ def test_mfma_probe_issue_cost(kind, cycles):
     assert cycles * 0.95 <= r["cycles_per_mfma_mean"] <= cycles * 1.5, r
     assert r["cycles_per_mfma_max"] <= cycles * 2.0, r
     assert 0.5 < r["clock_ghz"] < 3.0, r
+
+
+def test_load_probe_patterns():
+    """moe_load_probe: every pattern fills LDS at a plausible rate, and L2-resident data fills it
+    faster than data streamed from HBM."""
+    buf = torch.zeros(m.load().moe_load_probe_bytes(), dtype=torch.uint8, device="cuda:0")
+    r = [m.load_probe(p, stages=256, reps=1, buf=buf) for p in range(4)]
+    for x in r:
+        assert 1.0 < x["bytes_per_cycle_per_cu"] < 256.0, x
+    assert r[0]["bytes_per_cycle_per_cu"] > r[1]["bytes_per_cycle_per_cu"], r
