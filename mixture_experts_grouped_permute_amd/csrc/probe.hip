@@ -17,6 +17,7 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8p __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8p __attribute__((ext_vector_type(8)));
+typedef int32_t i32x4p __attribute__((ext_vector_type(4)));   // a buffer descriptor, 4 SGPRs
 
 // Pseudo-random operand bits: Knuth's multiplicative hash of the counter (2^32 / golden ratio),
 // then two of Marsaglia's xorshift32 steps (shifts 13, 17, 5).
@@ -121,12 +122,9 @@ void mfma_probe_kernel(float* sink, uint64_t* cycles, int iters) {
 //   pattern 2: chunk (4 s + g) mod ... -- 8 workgroups share each chunk in lockstep (64 MB);
 //   pattern 3: the GEMM operands' access with the same sharing: 512 rows of 4 KB, row block
 //     (4 (s / 32) + g) mod (region / 2 MB), 128-byte slice s mod 32 of each row (64 MB).
-__device__ __forceinline__ void probe_lds_load16(const int32_t (&vs)[4], uint32_t lds, uint32_t voff) {
+__device__ __forceinline__ void probe_lds_load16(const i32x4p& vs, uint32_t lds, uint32_t voff) {
   const uint32_t l = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :
-               : "s"(l), "v"(voff), "s"(*reinterpret_cast<const int32_t __attribute__((ext_vector_type(4)))*>(vs))
-               : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" : : "s"(l), "v"(voff), "s"(vs) : "memory", "m0");
 }
 
 template <int kPattern>
@@ -137,7 +135,7 @@ __global__ __launch_bounds__(256) void load_probe_kernel(const uint8_t* base, ui
   const uint32_t xcd = blockIdx.x & 7u, slot = blockIdx.x >> 3;
   const uint32_t g = slot & 3u;
   const uint64_t a = reinterpret_cast<uint64_t>(base + (size_t)xcd * region);
-  int32_t vs[4];
+  i32x4p vs;
   vs[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
   vs[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32));
   vs[2] = __builtin_amdgcn_readfirstlane((int)region);
