@@ -120,6 +120,100 @@ __global__ __launch_bounds__(256) void dprob_kernel(const float* __restrict__ pa
   dprob[p] = s;
 }
 
+// The same sum with k fixed at compile time: each pass issues the loads of all k source rows before
+// the first add, instead of a load-and-wait per row behind the runtime row loop's branches (which
+// made k round trips per pass).  A row slot holding no row (-1), or a column past H, loads row 0,
+// column 0 and is left out of the sum by a select, so every slot's result is the runtime loop's.
+template <bool kInF32, bool kOutF32, int kK>
+__global__ __launch_bounds__(256) void combine_k_kernel(const void* __restrict__ z, int64_t T, int64_t H,
+                                                          const int32_t* __restrict__ row_id_map,
+                                                          void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int rows[kK];
+#pragma unroll
+  for (int j = 0; j < kK; ++j) rows[j] = row_id_map[t * kK + j];
+  constexpr int kU = kInF32 ? 1 : 2;
+  for (int64_t c0 = (int64_t)lane * 8; c0 < H; c0 += 512 * kU) {
+    bool ok[kK][kU];
+    u32x4 w[kK][kU][kInF32 ? 2 : 1];
+#pragma unroll
+    for (int j = 0; j < kK; ++j)
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int64_t c = c0 + 512 * u;
+        ok[j][u] = rows[j] >= 0 && c < H;
+        const int64_t o = ok[j][u] ? (int64_t)rows[j] * H + c : 0;
+        if constexpr (kInF32) {
+          const u32x4* s = reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(z) + o);
+          w[j][u][0] = s[0];
+          w[j][u][1] = s[1];
+        } else {
+          w[j][u][0] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(z) + o);
+        }
+      }
+    float acc[kU][8];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kK; ++j)
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        float v[8];
+        if constexpr (kInF32) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // (a vector element copied out first: bit-casting the element expression in place
+            // read element 0)
+            const uint32_t lo = w[j][u][0][i], hi = w[j][u][1][i];
+            v[i] = __builtin_bit_cast(float, lo);
+            v[4 + i] = __builtin_bit_cast(float, hi);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[2 * i] = bf16_to_f32((uint16_t)(w[j][u][0][i] & 0xFFFF));
+            v[2 * i + 1] = bf16_to_f32((uint16_t)(w[j][u][0][i] >> 16));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] = ok[j][u] ? acc[u][i] + v[i] : acc[u][i];
+      }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t c = c0 + 512 * u;
+      if (c >= H) continue;
+      const int64_t o = t * H + c;
+      if (kOutF32) {
+        float4* d = reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + o);
+        d[0] = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+        d[1] = make_float4(acc[u][4], acc[u][5], acc[u][6], acc[u][7]);
+      } else {
+        u32x4 wo;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wo[i] = pack_bf16x2(acc[u][2 * i], acc[u][2 * i + 1]);
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(out) + o) = wo;
+      }
+    }
+  }
+}
+
+template <bool kInF32, bool kOutF32>
+void launch_combine_t(dim3 grid, const void* z, int64_t T, int64_t H, int k, const int32_t* row_id_map, void* out,
+                      hipStream_t st) {
+  switch (k) {
+    case 1: combine_k_kernel<kInF32, kOutF32, 1><<<grid, 256, 0, st>>>(z, T, H, row_id_map, out); break;
+    case 2: combine_k_kernel<kInF32, kOutF32, 2><<<grid, 256, 0, st>>>(z, T, H, row_id_map, out); break;
+    case 4: combine_k_kernel<kInF32, kOutF32, 4><<<grid, 256, 0, st>>>(z, T, H, row_id_map, out); break;
+    case 6: combine_k_kernel<kInF32, kOutF32, 6><<<grid, 256, 0, st>>>(z, T, H, row_id_map, out); break;
+    case 8: combine_k_kernel<kInF32, kOutF32, 8><<<grid, 256, 0, st>>>(z, T, H, row_id_map, out); break;
+    default: combine_kernel<kInF32, kOutF32><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out); break;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_combine(const void* z, bool z_f32, int64_t T, int64_t H, int k, const int32_t* row_id_map,
@@ -127,11 +221,11 @@ hipError_t launch_combine(const void* z, bool z_f32, int64_t T, int64_t H, int k
   dim3 grid((unsigned)((T + 3) / 4));
   if (T == 0) return hipSuccess;
   if (z_f32) {
-    if (out_f32) combine_kernel<true, true><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
-    else combine_kernel<true, false><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
+    if (out_f32) launch_combine_t<true, true>(grid, z, T, H, k, row_id_map, out, st);
+    else launch_combine_t<true, false>(grid, z, T, H, k, row_id_map, out, st);
   } else {
-    if (out_f32) combine_kernel<false, true><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
-    else combine_kernel<false, false><<<grid, 256, 0, st>>>(z, T, H, k, row_id_map, out);
+    if (out_f32) launch_combine_t<false, true>(grid, z, T, H, k, row_id_map, out, st);
+    else launch_combine_t<false, false>(grid, z, T, H, k, row_id_map, out, st);
   }
   return hipGetLastError();
 }
