@@ -42,9 +42,12 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t* __restric
 
 // ---------------------------------------------------------------------------
 // K2: split_sizes, offsets and the per-(block, expert) base rows.  One workgroup of 1024
-// threads: expert e's column of block counts is cut into S = 1024 / E slices, thread (e, s)
-// sums its slice, an exclusive prefix over the slices gives each slice's base, and the thread
-// then writes the running base of every block in its slice.
+// threads: expert e's column of block counts is cut into S = 1024 / E slices and thread
+// (e, s), e fastest so that a slice's threads read each block's row of counts contiguously,
+// sums its slice.  Laid out expert-major (position e * S + s), the exclusive prefix sum of the
+// slice sums is at once expert e's first row plus the rows of its earlier slices, so one
+// block-wide scan gives every slice's base; the thread then writes the running base of every
+// block in its slice.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restrict__ block_counts,
                                                            const int32_t* __restrict__ block_bad, int nb, int E,
@@ -53,49 +56,79 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(const int32_t* __restri
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ block_base) {
   __shared__ int slice_sum[1024];
-  __shared__ int tot[kMaxExperts];
-  __shared__ int off[kMaxExperts + 1];
-  __shared__ int bad;
-  const int tid = threadIdx.x;
+  __shared__ int slice_base[1024];
+  __shared__ int wave_base[16];
+  __shared__ int total, bad;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int S = 1024 / E;                 // >= 4 slices per expert (E <= 256)
-  const int e = tid / S, sl = tid % S;
-  const bool act = e < E;
+  const int e = tid % E, sl = tid / E;
+  const bool act = sl < S;                // exactly the threads tid < E * S
   const int per = (nb + S - 1) / S;
   const int b0 = min(nb, sl * per), b1 = min(nb, b0 + per);
   if (tid == 0) bad = 0;
+  // a slice's counts in batches of 8 blocks, all 8 loads issued before the first add (a block past
+  // the slice reads the slice's last one and adds 0)
+  auto count_at = [&](int b) { return block_counts[(int64_t)b * E + e]; };
   int s = 0;
   if (act)
-    for (int b = b0; b < b1; ++b) s += block_counts[(int64_t)b * E + e];
-  slice_sum[tid] = s;
+    for (int b = b0; b < b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = count_at(min(b + u, b1 - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += b + u < b1 ? v[u] : 0;
+    }
+  // (e, sl) -> e * S + sl maps the active threads onto [0, E * S); the positions above hold 0
+  slice_sum[act ? e * S + sl : tid] = act ? s : 0;
   int bd = 0;
   for (int b = tid; b < nb; b += 1024) bd |= block_bad[b];
   __syncthreads();
   if (bd) atomicOr(&bad, 1);
-  int pre = 0;
-  if (act) {
-    for (int q = 0; q < sl; ++q) pre += slice_sum[e * S + q];
-    if (sl == S - 1) tot[e] = pre + s;
+  // block-wide exclusive scan of slice_sum: within each wave, then over the 16 wave totals
+  const int x = slice_sum[tid];
+  int inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(inc, d, 64);
+    if (lane >= d) inc += y;
+  }
+  if (lane == 63) wave_base[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < 16 ? wave_base[lane] : 0;
+    int wi = w;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int y = __shfl_up(wi, d, 64);
+      if (lane >= d) wi += y;
+    }
+    if (lane < 16) wave_base[lane] = wi - w;   // each lane rewrites only the entry it read
   }
   __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < E; ++i) { off[i] = run; run += tot[i]; }
-    off[E] = run;
-  }
+  slice_base[tid] = wave_base[wave] + inc - x;
+  if (tid == 1023) total = wave_base[wave] + inc;
   __syncthreads();
   if (act) {
     if (sl == 0) {
-      split_sizes[e] = tot[e];
-      offsets[e] = off[e];
+      const int first = slice_base[e * S];
+      split_sizes[e] = (e + 1 < E ? slice_base[(e + 1) * S] : total) - first;
+      offsets[e] = first;
     }
-    int run = off[e] + pre;
-    for (int b = b0; b < b1; ++b) {
-      block_base[(int64_t)b * E + e] = run;
-      run += block_counts[(int64_t)b * E + e];
+    int run = slice_base[e * S + sl];
+    for (int b = b0; b < b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = count_at(min(b + u, b1 - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (b + u < b1) {
+          block_base[(int64_t)(b + u) * E + e] = run;
+          run += v[u];
+        }
     }
   }
   if (tid == 0) {
-    offsets[E] = off[E];
+    offsets[E] = total;
     err_flag[0] = bad;   // the flag describes this call only
   }
 }
