@@ -21,6 +21,13 @@ ROUTINGS = [
     # H not a multiple of 512 (a partial last chunk), with whole 128-column scale words, and with not
     ("h384", cfg_small(T=200, H=384, I=128, E=4, k=2), None),
     ("h160", cfg_small(T=200, H=160, I=128, E=4, k=2), None),
+    # the count scan's slicing: 1024 / E slices per expert over the 64-token blocks, with a
+    # slice length that is not a whole number of 8-block batches (24 experts, 469 blocks: 12
+    # per slice), 64 blocks per slice (256 experts), and more slices than blocks with E * S
+    # short of 1024 (3 experts: 341 slices, 79 blocks)
+    ("scan-e24-469-blocks", cfg_small(T=30000, H=64, I=128, E=24, k=6), None),
+    ("scan-e256-256-blocks", cfg_small(T=16384, H=64, I=128, E=256, k=8), None),
+    ("scan-e3-79-blocks", cfg_small(T=5000, H=64, I=128, E=3, k=2), None),
 ]
 
 
