@@ -40,6 +40,10 @@ CASES = [
     ("odd-k3", 999, 5, 3, "ties", torch.bfloat16),
     ("ties-e16-k4", 2048, 16, 4, "ties", torch.float32),
     ("zipf-masked-expert", 1111, 8, 2, "zipf", torch.float32),
+    # many 64-token blocks, so the permutation's count scan slices each expert's column of the
+    # router's block counts over several blocks (256 experts: 256 blocks; 24 experts: 469)
+    ("e256-k8-256-blocks", 16384, 256, 8, "normal", torch.float32),
+    ("e24-k6-469-blocks", 30000, 24, 6, "normal", torch.bfloat16),
 ]
 
 
@@ -61,7 +65,8 @@ def test_route_topk_matches_oracle(case):
 
 @gpu
 @pytest.mark.parametrize("perm_dtype", ["bf16", "mxfp8"])
-@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[4], CASES[6]], ids=["mixtral", "finegrained", "odd-k3", "zipf"])
+@pytest.mark.parametrize("case", [CASES[0], CASES[1], CASES[4], CASES[6], CASES[7], CASES[8]],
+                         ids=["mixtral", "finegrained", "odd-k3", "zipf", "e256-256-blocks", "e24-469-blocks"])
 def test_route_permute_matches_oracle(case, perm_dtype):
     m = need_gpu()
     name, T, E, k, kind, dtype = case
