@@ -197,7 +197,9 @@ template <bool kInF32, bool kMx>
 __global__ __launch_bounds__(256) void perm_rows_kernel(const void* __restrict__ x, int64_t T, int64_t H, int k,
                                                           const int32_t* __restrict__ row_id_map,
                                                           void* __restrict__ out, uint8_t* __restrict__ out_scales) {
-  constexpr int kBatch = 4;
+  // 8 chunks in flight (a 4096-wide bf16 row at once) for the plain copy; the MXFP8 path's extra
+  // registers make 4 the faster choice there
+  constexpr int kBatch = kMx ? 4 : 8;
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
